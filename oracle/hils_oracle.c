@@ -1,0 +1,279 @@
+/*
+ * HiLS-Attention forward pass: plain fp64 CPU oracle.
+ *
+ * TEST INFRASTRUCTURE ONLY (see hils_oracle.h).  Every function follows the
+ * steps in the order the pages give them; comments cite the page and section.
+ * Plain loops in double precision, libm exp/log, the C library's qsort as the
+ * sorting step.  No blocking, fusion or reordering.
+ *
+ * Readings taken where the pages are silent (each is listed in the design
+ * notes of the repository):
+ *   - the landmark softmax and the intra-chunk softmax use the same scale
+ *     1/sqrt(d) as the chunk score;
+ *   - a landmark query attends the S keys of its own chunk only;
+ *   - query i scores the complete past chunks c < floor(i/S); its own chunk
+ *     floor(i/S) is always attended with a causal mask and takes its exact
+ *     log-sum-exp as its score; the own chunk is not part of the top-K budget;
+ *   - with fewer than K past chunks, all of them are selected;
+ *   - ties in the chunk score go to the lower chunk index;
+ *   - Q-Cal: q^ = q + U_h (D_h q) scores chunks; the raw q attends.
+ */
+#include "hils_oracle.h"
+
+#include <math.h>
+#include <stdlib.h>
+#include <string.h>
+
+static double ld(const void* p, int dt, int64_t i) {
+  if (dt == HR_F64) return ((const double*)p)[i];
+  if (dt == HR_F32) return (double)((const float*)p)[i];
+  /* bf16: the upper half of an IEEE float */
+  uint32_t x = (uint32_t)((const uint16_t*)p)[i] << 16;
+  float f;
+  memcpy(&f, &x, 4);
+  return (double)f;
+}
+
+/*
+ * Landmark compression (aitrends.kr, "Key contributions" first item and
+ * "Methodology"; "Technical details"): the landmark query of chunk c attends
+ * the chunk's S keys; the attention weights a_j give the compressed key
+ * k'_c = sum_j a_j k_j and the entropy bias b'_c = -sum_j a_j log a_j.
+ */
+void hr_compress(const hr_shape* s, const void* k, int kdt, const void* lmk, int ldt, double* kc,
+                 double* bc) {
+  const int B = s->B, Hl = s->Hl, Hkv = s->Hkv, d = s->d, S = s->S, N = s->N;
+  const int C = N / S;
+  const double tau = 1.0 / sqrt((double)d);
+  const int lm_per_kv = Hl / Hkv;
+#pragma omp parallel for collapse(3) schedule(static)
+  for (int b = 0; b < B; ++b)
+    for (int l = 0; l < Hl; ++l)
+      for (int c = 0; c < C; ++c) {
+        const int kvh = l / lm_per_kv;
+        const int64_t lbase = (((int64_t)b * Hl + l) * C + c) * d;
+        const int64_t kbase = (((int64_t)b * Hkv + kvh) * N + (int64_t)c * S) * d;
+        double* z = (double*)malloc(sizeof(double) * S);
+        double m = -INFINITY;
+        for (int j = 0; j < S; ++j) {
+          double acc = 0.0;
+          for (int e = 0; e < d; ++e) acc += ld(lmk, ldt, lbase + e) * ld(k, kdt, kbase + (int64_t)j * d + e);
+          z[j] = tau * acc;
+          if (z[j] > m) m = z[j];
+        }
+        double Z = 0.0;
+        for (int j = 0; j < S; ++j) Z += exp(z[j] - m);
+        double* out = kc + lbase;
+        for (int e = 0; e < d; ++e) out[e] = 0.0;
+        double ent = 0.0;
+        for (int j = 0; j < S; ++j) {
+          double a = exp(z[j] - m) / Z;
+          for (int e = 0; e < d; ++e) out[e] += a * ld(k, kdt, kbase + (int64_t)j * d + e);
+          if (a > 0.0) ent -= a * log(a);
+        }
+        bc[((int64_t)b * Hl + l) * C + c] = ent;
+        free(z);
+      }
+}
+
+/*
+ * Q-Cal (aitrends.kr, "Methodology": a low-rank down/up projection of the
+ * query q_i gives q^_i, used only to calibrate the chunk-level score).
+ * D_h is [r, d], U_h is [d, r].
+ */
+void hr_qcal(const hr_shape* s, int h, const double* q, const void* D, const void* U, int wdt,
+             double* qhat) {
+  const int d = s->d, r = s->r;
+  for (int e = 0; e < d; ++e) qhat[e] = q[e];
+  if (r <= 0 || !D || !U) return;
+  double* t = (double*)malloc(sizeof(double) * r);
+  for (int a = 0; a < r; ++a) {
+    double acc = 0.0;
+    for (int e = 0; e < d; ++e) acc += ld(D, wdt, ((int64_t)h * r + a) * d + e) * q[e];
+    t[a] = acc;
+  }
+  for (int e = 0; e < d; ++e) {
+    double acc = 0.0;
+    for (int a = 0; a < r; ++a) acc += ld(U, wdt, ((int64_t)h * d + e) * r + a) * t[a];
+    qhat[e] += acc;
+  }
+  free(t);
+}
+
+/* softmax attention of q over keys [j0, j1) of one KV head: o (normalised) and the LSE */
+static double attend_range(const hr_shape* s, const double* q, const void* k, const void* v, int kvdt,
+                           int64_t kvbase_row, int j0, int j1, double* o) {
+  const int d = s->d;
+  const double tau = 1.0 / sqrt((double)d);
+  const int n = j1 - j0;
+  double* t = (double*)malloc(sizeof(double) * (n > 0 ? n : 1));
+  double m = -INFINITY;
+  for (int j = 0; j < n; ++j) {
+    double acc = 0.0;
+    const int64_t kb = (kvbase_row + j0 + j) * d;
+    for (int e = 0; e < d; ++e) acc += q[e] * ld(k, kvdt, kb + e);
+    t[j] = tau * acc;
+    if (t[j] > m) m = t[j];
+  }
+  double l = 0.0;
+  for (int j = 0; j < n; ++j) l += exp(t[j] - m);
+  for (int e = 0; e < d; ++e) o[e] = 0.0;
+  for (int j = 0; j < n; ++j) {
+    double p = exp(t[j] - m) / l;
+    const int64_t vb = (kvbase_row + j0 + j) * d;
+    for (int e = 0; e < d; ++e) o[e] += p * ld(v, kvdt, vb + e);
+  }
+  free(t);
+  return m + log(l);
+}
+
+/*
+ * Chunk score (aitrends.kr, "Methodology", the formula with its worked
+ * example): s_ic = q^_i . k'_c / sqrt(d) + b'_c.  In HR_EXACT mode the score
+ * is the exact log-sum-exp of the chunk, log sum_j exp(q_i . k_j / sqrt(d)),
+ * the quantity the surrogate linearises ("Technical details").
+ */
+int hr_row_scores(const hr_shape* s, int mode, int b, int h, int pos, const void* qrow, int qdt,
+                  const void* k, int kvdt, const double* kc, const double* bc, const void* D,
+                  const void* U, int wdt, double* out) {
+  const int d = s->d, S = s->S, C = s->N / s->S;
+  const double tau = 1.0 / sqrt((double)d);
+  int P = pos / S;
+  if (P > C) P = C;
+  double* q = (double*)malloc(sizeof(double) * d);
+  double* qh = (double*)malloc(sizeof(double) * d);
+  for (int e = 0; e < d; ++e) q[e] = ld(qrow, qdt, e);
+  if (mode == HR_EXACT) {
+    const int kvh = h / (s->Hq / s->Hkv);
+    const int64_t row0 = ((int64_t)b * s->Hkv + kvh) * s->N;
+    double* tmp = (double*)malloc(sizeof(double) * d);
+    for (int c = 0; c < P; ++c) out[c] = attend_range(s, q, k, k, kvdt, row0, c * S, c * S + S, tmp);
+    free(tmp);
+  } else {
+    hr_qcal(s, h, q, D, U, wdt, qh);
+    const int lm = h / (s->Hq / s->Hl);
+    for (int c = 0; c < P; ++c) {
+      const double* kp = kc + (((int64_t)b * s->Hl + lm) * C + c) * d;
+      double acc = 0.0;
+      for (int e = 0; e < d; ++e) acc += qh[e] * kp[e];
+      out[c] = tau * acc + bc[((int64_t)b * s->Hl + lm) * C + c];
+    }
+  }
+  free(q);
+  free(qh);
+  return P;
+}
+
+typedef struct {
+  double score;
+  int32_t idx;
+} cand;
+
+/* order: higher score first; equal scores -> lower chunk index first */
+static int by_score_desc(const void* x, const void* y) {
+  const cand* a = (const cand*)x;
+  const cand* b = (const cand*)y;
+  if (a->score > b->score) return -1;
+  if (a->score < b->score) return 1;
+  return (a->idx > b->idx) - (a->idx < b->idx);
+}
+
+static int by_idx_asc(const void* x, const void* y) {
+  const cand* a = (const cand*)x;
+  const cand* b = (const cand*)y;
+  return (a->idx > b->idx) - (a->idx < b->idx);
+}
+
+/*
+ * One query through the hierarchical factorisation (hotpaper.ai abstract;
+ * aitrends.kr "Methodology" calculation flow and "Key contributions"
+ * second item; ai-papers.net "How HiLS Attention works", Fig. 1):
+ *   1. score every complete past chunk with the surrogate, keep the top K;
+ *   2. attend independently inside each selected chunk (intra-chunk softmax);
+ *   3. the own, partial chunk is attended causally; its score is its exact LSE;
+ *   4. fuse the per-chunk outputs with a softmax over the chunk scores.
+ */
+void hr_attend(const hr_shape* s, int mode, int64_t nrows, const int32_t* row_b,
+               const int32_t* row_h, const int32_t* row_pos, const void* qrows, int qdt,
+               const void* k, const void* v, int kvdt, const double* kc, const double* bc,
+               const void* D, const void* U, int wdt, const int32_t* sel_in, double* o,
+               int32_t* sel_idx, double* sel_score, double* gap, double* lse_own, int32_t* nsel) {
+  const int d = s->d, S = s->S, K = s->K, C = s->N / s->S;
+#pragma omp parallel for schedule(dynamic, 1)
+  for (int64_t n = 0; n < nrows; ++n) {
+    const int b = row_b[n], h = row_h[n], pos = row_pos[n];
+    const int kvh = h / (s->Hq / s->Hkv);
+    const int64_t row0 = ((int64_t)b * s->Hkv + kvh) * s->N;
+    int P = pos / S;
+    if (P > C) P = C;
+    const void* qn = (const char*)qrows + (size_t)n * d * (qdt == HR_F64 ? 8 : qdt == HR_F32 ? 4 : 2);
+
+    /* step 1: scores of all past chunks and the top-K */
+    double* sc = (double*)malloc(sizeof(double) * (P > 0 ? P : 1));
+    hr_row_scores(s, mode == HR_EXACT ? HR_EXACT : HR_LANDMARK, b, h, pos, qn, qdt, k, kvdt, kc, bc, D,
+                  U, wdt, sc);
+    cand* cs = (cand*)malloc(sizeof(cand) * (P > 0 ? P : 1));
+    for (int c = 0; c < P; ++c) {
+      cs[c].score = sc[c];
+      cs[c].idx = c;
+    }
+    int ns = 0;
+    double g = INFINITY;
+    if (mode == HR_GIVEN) {
+      cand* chosen = (cand*)malloc(sizeof(cand) * (K > 0 ? K : 1));
+      for (int t = 0; t < K; ++t) {
+        int c = sel_in[n * K + t];
+        if (c >= 0 && c < P) {
+          chosen[ns].idx = c;
+          chosen[ns].score = sc[c];
+          ++ns;
+        }
+      }
+      memcpy(cs, chosen, sizeof(cand) * ns);
+      free(chosen);
+    } else {
+      qsort(cs, P, sizeof(cand), by_score_desc);
+      ns = P < K ? P : K;
+      if (P > K) g = cs[K - 1].score - cs[K].score;
+    }
+    qsort(cs, ns, sizeof(cand), by_idx_asc);
+
+    /* steps 2-4 */
+    double* q = (double*)malloc(sizeof(double) * d);
+    for (int e = 0; e < d; ++e) q[e] = ld(qn, qdt, e);
+    double* oc = (double*)malloc(sizeof(double) * d * (ns + 1));
+    double* sig = (double*)malloc(sizeof(double) * (ns + 1));
+    for (int t = 0; t < ns; ++t) {
+      const int c = cs[t].idx;
+      attend_range(s, q, k, v, kvdt, row0, c * S, c * S + S, oc + (int64_t)t * d);
+      sig[t] = cs[t].score;
+    }
+    const int own = pos / S;
+    const double lse = attend_range(s, q, k, v, kvdt, row0, own * S, pos + 1, oc + (int64_t)ns * d);
+    sig[ns] = lse;
+    double M = -INFINITY;
+    for (int t = 0; t <= ns; ++t)
+      if (sig[t] > M) M = sig[t];
+    double Zs = 0.0;
+    for (int t = 0; t <= ns; ++t) Zs += exp(sig[t] - M);
+    double* on = o + n * d;
+    for (int e = 0; e < d; ++e) on[e] = 0.0;
+    for (int t = 0; t <= ns; ++t) {
+      const double w = exp(sig[t] - M) / Zs;
+      for (int e = 0; e < d; ++e) on[e] += w * oc[(int64_t)t * d + e];
+    }
+
+    if (sel_idx)
+      for (int t = 0; t < K; ++t) sel_idx[n * K + t] = t < ns ? cs[t].idx : -1;
+    if (sel_score)
+      for (int t = 0; t < K; ++t) sel_score[n * K + t] = t < ns ? cs[t].score : -INFINITY;
+    if (gap) gap[n] = g;
+    if (lse_own) lse_own[n] = lse;
+    if (nsel) nsel[n] = ns;
+    free(sc);
+    free(cs);
+    free(q);
+    free(oc);
+    free(sig);
+  }
+}
