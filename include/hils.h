@@ -1,0 +1,141 @@
+/*
+ * hils.h — C ABI of the HiLS-Attention forward pass on AMD Instinct MI355X (gfx950).
+ *
+ * HiLS ("Hierarchical Landmark Sparse") attention, from "Hierarchical Sparse
+ * Attention Done Right: Toward Infinite Context Modeling" (arXiv 2607.02980):
+ *   (1) a landmark query per chunk of S keys gives softmax weights a_j over the
+ *       chunk; k'_c = sum_j a_j k_j and b'_c = -sum_j a_j log a_j
+ *       (aitrends.kr article, "Key contributions" and "Methodology");
+ *   (2) query i scores every complete past chunk c < floor(i/S) with
+ *       s_ic = q^_i . k'_c / sqrt(d) + b'_c (q^ = Q-Cal-calibrated query) and keeps
+ *       the top K; ties go to the lower chunk index ("Methodology", the formula
+ *       and its worked example);
+ *   (3) the query attends each selected chunk with an independent softmax, and
+ *       its own partial chunk causally; the own chunk's score is its exact
+ *       log-sum-exp (hotpaper.ai abstract; "Methodology" calculation flow);
+ *   (4) the per-chunk outputs are fused with a softmax over the chunk scores
+ *       (abstract; aitrends.kr "Key contributions", hierarchical softmax).
+ *
+ * Conventions shared by every call:
+ *   - Every pointer argument is a DEVICE pointer allocated by the caller, except
+ *     `dims`, which is a host pointer.  The library allocates no memory and keeps
+ *     no pointer after a call returns.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the default stream).  All
+ *     work is enqueued asynchronously on it; no call synchronises.
+ *   - Every call validates all arguments before enqueuing anything; on a non-OK
+ *     return nothing was enqueued (except HILS_E_HIP, returned when a launch
+ *     failed).  hils_last_error() then holds a message (thread-local).
+ *   - Layouts are dense row-major ("head-major", as torch SDPA):
+ *       q, o       [B, Hq, N, d]        (decode: [B, Hq, d])
+ *       k, v       [B, Hkv, N, d]       (decode: the KV cache, N = capacity)
+ *       lmk_q      [B, Hlmk, C, d]      landmark queries, C = floor(N / S)
+ *       kc         [B, Hlmk, C, d]      fp32, compressed keys k'
+ *       bc         [B, Hlmk, C]         fp32, entropy biases b'
+ *       qcal_D     [Hq, r, d]           Q-Cal down projection (r = qcal_rank)
+ *       qcal_U     [Hq, d, r]           Q-Cal up projection
+ *       sel_idx    [B, Hq, N, K] int32  selected chunk ids (decode: [B, Hq, K])
+ *       sel_score  [B, Hq, N, K] fp32   their scores s_ic
+ *     Query head h uses KV head h / (Hq / Hkv) and landmark head h / (Hq / Hlmk).
+ *   - Selection lists are in rank order: best score first, equal scores by
+ *     ascending chunk id.  Rows with fewer than K past chunks select all of them
+ *     and pad with id -1 and score -inf.
+ *   - q, k, v, o, lmk_q, qcal_D, qcal_U all have the element type `io`;
+ *     kc, bc and sel_score are always fp32.
+ */
+#ifndef HILS_H
+#define HILS_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum { HILS_F32 = 0, HILS_BF16 = 1 } hils_dtype_t;
+
+enum {
+  HILS_OK = 0,
+  HILS_E_INVAL = -1,       /* a required pointer is NULL or a size is inconsistent      */
+  HILS_E_UNSUPPORTED = -2, /* legal but not implemented (d, S, K, dtype, head layout)    */
+  HILS_E_WORKSPACE = -3,   /* ws_bytes < hils_workspace_bytes(dims, op)                  */
+  HILS_E_HIP = -4          /* a HIP launch failed; the runtime's message is kept         */
+};
+
+/* op codes of hils_workspace_bytes */
+enum { HILS_OP_COMPRESS = 0, HILS_OP_SCORE_TOPK = 1, HILS_OP_PREFILL = 2, HILS_OP_DECODE = 3 };
+
+typedef struct {
+  int32_t B;         /* batch (sequences)                                              */
+  int32_t Hq;        /* query heads                                                    */
+  int32_t Hkv;       /* KV heads; Hq % Hkv == 0                                        */
+  int32_t Hlmk;      /* landmark heads; this build requires Hlmk == Hq                  */
+  int32_t d;         /* head dimension: 64 or 128                                      */
+  int32_t S;         /* chunk size: 64                                                 */
+  int32_t K;         /* top-K chunks per query: 1 <= K <= 32                            */
+  int32_t N;         /* prefill: tokens; decode: KV-cache capacity (row stride of k/v) */
+  int32_t qcal_rank; /* Q-Cal rank r, 0 <= r <= 32 (0: no Q-Cal, q^ = q)                */
+  int32_t io;        /* hils_dtype_t of q, k, v, o, lmk_q, qcal_D, qcal_U              */
+} hils_dims_t;
+
+/* Bytes of device workspace the call `op` needs for these dims (0 if none).
+ * Returns (size_t)-1 if dims is invalid or unsupported. */
+size_t hils_workspace_bytes(const hils_dims_t* dims, int op);
+
+/*
+ * Landmark compression, step (1), of chunks c_begin <= c < c_end of every
+ * (batch, landmark head):  z_j = lmk_q[b,l,c] . k[b, l/(Hlmk/Hkv), c*S + j] / sqrt(d),
+ * a = softmax_j(z), kc[b,l,c] = sum_j a_j k_j, bc[b,l,c] = -sum_j a_j log a_j.
+ * Chunks outside [c_begin, c_end) are left untouched, so a decode cache can be
+ * extended one completed chunk at a time.  0 <= c_begin <= c_end <= floor(N/S);
+ * an empty range does nothing and then k, lmk_q, kc and bc may be NULL.
+ * Needs no workspace.
+ */
+int hils_landmark_compress(const hils_dims_t* dims, const void* k, const void* lmk_q, int32_t c_begin,
+                           int32_t c_end, float* kc, float* bc, void* stream);
+
+/*
+ * Chunk scoring and top-K, step (2), for all N prefill queries:
+ * s_ic = q^_i . kc[c] / sqrt(d) + bc[c] for c < floor(i/S), q^ = q + U_h (D_h q)
+ * when qcal_rank > 0 (qcal_D/qcal_U may be NULL only if qcal_rank == 0).
+ * Writes sel_idx and sel_score [B,Hq,N,K] (rank order, padded).
+ */
+int hils_chunk_score_topk(const hils_dims_t* dims, const void* q, const void* qcal_D, const void* qcal_U,
+                          const float* kc, const float* bc, int32_t* sel_idx, float* sel_score, void* ws,
+                          size_t ws_bytes, void* stream);
+
+/*
+ * The whole prefill forward pass, steps (1)-(4), for all N queries of every
+ * (batch, query head); writes o [B,Hq,N,d].
+ *   lmk_q != NULL: landmark compression runs first in the same call and writes
+ *                  kc/bc (which may then be NULL: the workspace holds them);
+ *   lmk_q == NULL: kc/bc are inputs (precomputed by hils_landmark_compress).
+ * When N < S there is no complete chunk and lmk_q, kc and bc may all be NULL.
+ * sel_idx_out/sel_score_out (nullable) receive the selection of step (2).
+ */
+int hils_attn_prefill(const hils_dims_t* dims, const void* q, const void* k, const void* v, const void* lmk_q,
+                      float* kc, float* bc, const void* qcal_D, const void* qcal_U, int32_t* sel_idx_out,
+                      float* sel_score_out, void* o, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * One decode step: for every sequence b and query head h, the single query
+ * q[b,h] at position seq_lens[b]-1 runs steps (2)-(4) against the KV cache
+ * (k_cache/v_cache [B,Hkv,N,d], N = capacity).  seq_lens [B] int32 lives on the
+ * device and counts the cached tokens including the current one
+ * (1 <= seq_lens[b] <= N; the caller appends the new token's k/v first).
+ * kc/bc [B,Hlmk,floor(N/S),d] must hold the compressed keys of every complete
+ * chunk c < floor((seq_lens[b]-1)/S) (see hils_landmark_compress).
+ * Writes o [B,Hq,d]; sel_idx_out (nullable) [B,Hq,K].
+ */
+int hils_attn_decode(const hils_dims_t* dims, const void* q, const void* k_cache, const void* v_cache,
+                     const int32_t* seq_lens, const float* kc, const float* bc, const void* qcal_D,
+                     const void* qcal_U, int32_t* sel_idx_out, void* o, void* ws, size_t ws_bytes,
+                     void* stream);
+
+/* Message of the last non-OK return on this thread ("" if none). */
+const char* hils_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* HILS_H */

@@ -1,0 +1,196 @@
+// The C ABI of include/hils.h: argument validation, workspace layout and
+// dispatch to the kernel launchers.  Nothing is enqueued unless every argument
+// is valid.
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include "../../include/hils.h"
+#include "kernels.h"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+int fail(int code, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof g_err, fmt, ap);
+  va_end(ap);
+  return code;
+}
+
+int hip_fail(hipError_t e, const char* where) {
+  return fail(HILS_E_HIP, "%s: %s", where, hipGetErrorString(e));
+}
+
+constexpr size_t kAlign = 256;
+size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+// Validates dims; on success fills g.  Returns HILS_OK or an error code.
+int check_dims(const hils_dims_t* dims, hils::Geom& g) {
+  if (!dims) return fail(HILS_E_INVAL, "dims is NULL");
+  const hils_dims_t& s = *dims;
+  if (s.B < 1 || s.Hq < 1 || s.Hkv < 1 || s.Hlmk < 1 || s.N < 1)
+    return fail(HILS_E_INVAL, "B, Hq, Hkv, Hlmk and N must be >= 1 (B=%d Hq=%d Hkv=%d Hlmk=%d N=%d)", s.B, s.Hq,
+                s.Hkv, s.Hlmk, s.N);
+  if (s.Hq % s.Hkv != 0) return fail(HILS_E_INVAL, "Hq (%d) must be a multiple of Hkv (%d)", s.Hq, s.Hkv);
+  if (s.Hq % s.Hlmk != 0 || s.Hlmk % s.Hkv != 0)
+    return fail(HILS_E_INVAL, "need Hq %% Hlmk == 0 and Hlmk %% Hkv == 0 (Hq=%d Hlmk=%d Hkv=%d)", s.Hq, s.Hlmk, s.Hkv);
+  if (s.K < 1) return fail(HILS_E_INVAL, "K must be >= 1 (K=%d)", s.K);
+  if (s.qcal_rank < 0) return fail(HILS_E_INVAL, "qcal_rank must be >= 0 (%d)", s.qcal_rank);
+  if (s.d < 1 || s.S < 1) return fail(HILS_E_INVAL, "d and S must be >= 1 (d=%d S=%d)", s.d, s.S);
+  if (s.io != HILS_F32 && s.io != HILS_BF16) return fail(HILS_E_UNSUPPORTED, "io dtype %d not supported", s.io);
+  if (s.Hlmk != s.Hq) return fail(HILS_E_UNSUPPORTED, "this build needs Hlmk == Hq (got Hlmk=%d Hq=%d)", s.Hlmk, s.Hq);
+  if (s.d != 64 && s.d != 128) return fail(HILS_E_UNSUPPORTED, "head dim %d not supported (64 or 128)", s.d);
+  if (s.S != 64) return fail(HILS_E_UNSUPPORTED, "chunk size %d not supported (64)", s.S);
+  if (s.K > 32) return fail(HILS_E_UNSUPPORTED, "K=%d not supported (K <= 32)", s.K);
+  if (s.qcal_rank > 32) return fail(HILS_E_UNSUPPORTED, "qcal_rank=%d not supported (<= 32)", s.qcal_rank);
+  g = hils::Geom{s.B, s.Hq, s.Hkv, s.Hlmk, s.d, s.S, s.K, s.N, s.qcal_rank, s.io};
+  return HILS_OK;
+}
+
+// Prefill-only limits: (row, slot) pair ids are 32-bit and the bucket histograms
+// hold at most 16384 chunks.
+int check_prefill(const hils::Geom& g) {
+  if ((int64_t)g.B * g.Hq * (int64_t)g.N * g.K >= ((int64_t)1 << 32))
+    return fail(HILS_E_UNSUPPORTED, "prefill needs B*Hq*N*K < 2^32");
+  if (g.C() > 16384) return fail(HILS_E_UNSUPPORTED, "prefill needs N/S <= 16384 (N=%d)", g.N);
+  return HILS_OK;
+}
+
+// prefill workspace: [kc | bc | sel_idx | sel_score | attend workspace]
+struct PrefillWs {
+  size_t kc, bc, sel_idx, sel_score, attend, total;
+};
+PrefillWs prefill_ws(const hils::Geom& g) {
+  PrefillWs w;
+  const size_t C = (size_t)g.C(), rows = (size_t)g.B * g.Hq * g.N;
+  size_t off = 0;
+  w.kc = off;
+  off += align_up((size_t)g.B * g.Hl * C * g.d * 4);
+  w.bc = off;
+  off += align_up((size_t)g.B * g.Hl * C * 4);
+  w.sel_idx = off;
+  off += align_up(rows * g.K * 4);
+  w.sel_score = off;
+  off += align_up(rows * g.K * 4);
+  w.attend = off;
+  off += align_up(hils::attend_workspace_bytes(g));
+  w.total = off;
+  return w;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* hils_last_error(void) { return g_err; }
+
+size_t hils_workspace_bytes(const hils_dims_t* dims, int op) {
+  hils::Geom g;
+  if (check_dims(dims, g) != HILS_OK) return (size_t)-1;
+  switch (op) {
+    case HILS_OP_COMPRESS:
+    case HILS_OP_SCORE_TOPK:
+      return 0;
+    case HILS_OP_PREFILL:
+      if (check_prefill(g) != HILS_OK) return (size_t)-1;
+      return prefill_ws(g).total;
+    case HILS_OP_DECODE:
+      return hils::decode_workspace_bytes(g);
+    default:
+      fail(HILS_E_INVAL, "unknown op %d", op);
+      return (size_t)-1;
+  }
+}
+
+int hils_landmark_compress(const hils_dims_t* dims, const void* k, const void* lmk_q, int32_t c_begin,
+                           int32_t c_end, float* kc, float* bc, void* stream) {
+  hils::Geom g;
+  int rc = check_dims(dims, g);
+  if (rc) return rc;
+  if (c_begin < 0 || c_end < c_begin || c_end > g.C())
+    return fail(HILS_E_INVAL, "need 0 <= c_begin <= c_end <= N/S (c_begin=%d c_end=%d N/S=%d)", c_begin, c_end, g.C());
+  if (c_end == c_begin) {  // nothing to compress: the arrays may be empty (NULL)
+    g_err[0] = 0;
+    return HILS_OK;
+  }
+  if (!k || !lmk_q || !kc || !bc) return fail(HILS_E_INVAL, "k, lmk_q, kc and bc must be non-NULL");
+  hipError_t e = hils::launch_compress(g.io, k, lmk_q, kc, bc, g.B, g.Hkv, g.Hl, g.N, g.d, c_begin, c_end,
+                                       (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "hils_landmark_compress");
+  g_err[0] = 0;
+  return HILS_OK;
+}
+
+int hils_chunk_score_topk(const hils_dims_t* dims, const void* q, const void* qcal_D, const void* qcal_U,
+                          const float* kc, const float* bc, int32_t* sel_idx, float* sel_score, void* ws,
+                          size_t ws_bytes, void* stream) {
+  (void)ws;
+  (void)ws_bytes;
+  hils::Geom g;
+  int rc = check_dims(dims, g);
+  if (rc) return rc;
+  if (!q || !kc || !bc || !sel_idx || !sel_score)
+    return fail(HILS_E_INVAL, "q, kc, bc, sel_idx and sel_score must be non-NULL");
+  if (g.r > 0 && (!qcal_D || !qcal_U)) return fail(HILS_E_INVAL, "qcal_rank > 0 needs qcal_D and qcal_U");
+  hipError_t e = hils::launch_score_topk(g, q, qcal_D, qcal_U, kc, bc, sel_idx, sel_score, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "hils_chunk_score_topk");
+  g_err[0] = 0;
+  return HILS_OK;
+}
+
+int hils_attn_prefill(const hils_dims_t* dims, const void* q, const void* k, const void* v, const void* lmk_q,
+                      float* kc, float* bc, const void* qcal_D, const void* qcal_U, int32_t* sel_idx_out,
+                      float* sel_score_out, void* o, void* ws, size_t ws_bytes, void* stream) {
+  hils::Geom g;
+  int rc = check_dims(dims, g);
+  if (rc) return rc;
+  if ((rc = check_prefill(g))) return rc;
+  if (!q || !k || !v || !o) return fail(HILS_E_INVAL, "q, k, v and o must be non-NULL");
+  if (g.C() > 0 && !lmk_q && (!kc || !bc)) return fail(HILS_E_INVAL, "without lmk_q, kc and bc are required inputs");
+  if (g.r > 0 && (!qcal_D || !qcal_U)) return fail(HILS_E_INVAL, "qcal_rank > 0 needs qcal_D and qcal_U");
+  const PrefillWs w = prefill_ws(g);
+  if (!ws && w.total > 0) return fail(HILS_E_WORKSPACE, "workspace is NULL (%zu bytes needed)", w.total);
+  if (ws_bytes < w.total) return fail(HILS_E_WORKSPACE, "workspace too small: %zu < %zu", ws_bytes, w.total);
+  char* base = (char*)ws;
+  float* kcp = kc ? kc : (float*)(base + w.kc);
+  float* bcp = bc ? bc : (float*)(base + w.bc);
+  int32_t* sel = sel_idx_out ? sel_idx_out : (int32_t*)(base + w.sel_idx);
+  float* scr = sel_score_out ? sel_score_out : (float*)(base + w.sel_score);
+  hipStream_t st = (hipStream_t)stream;
+  hipError_t e;
+  if (lmk_q && g.C() > 0) {
+    e = hils::launch_compress(g.io, k, lmk_q, kcp, bcp, g.B, g.Hkv, g.Hl, g.N, g.d, 0, g.C(), st);
+    if (e != hipSuccess) return hip_fail(e, "hils_attn_prefill (compress)");
+  }
+  e = hils::launch_score_topk(g, q, qcal_D, qcal_U, kcp, bcp, sel, scr, st);
+  if (e != hipSuccess) return hip_fail(e, "hils_attn_prefill (score/top-K)");
+  e = hils::launch_prefill_attend(g, q, k, v, sel, scr, o, base + w.attend, w.total - w.attend, st);
+  if (e != hipSuccess) return hip_fail(e, "hils_attn_prefill (attend)");
+  g_err[0] = 0;
+  return HILS_OK;
+}
+
+int hils_attn_decode(const hils_dims_t* dims, const void* q, const void* k_cache, const void* v_cache,
+                     const int32_t* seq_lens, const float* kc, const float* bc, const void* qcal_D,
+                     const void* qcal_U, int32_t* sel_idx_out, void* o, void* ws, size_t ws_bytes,
+                     void* stream) {
+  hils::Geom g;
+  int rc = check_dims(dims, g);
+  if (rc) return rc;
+  if (!q || !k_cache || !v_cache || !seq_lens || !kc || !bc || !o)
+    return fail(HILS_E_INVAL, "q, k_cache, v_cache, seq_lens, kc, bc and o must be non-NULL");
+  if (g.r > 0 && (!qcal_D || !qcal_U)) return fail(HILS_E_INVAL, "qcal_rank > 0 needs qcal_D and qcal_U");
+  const size_t need = hils::decode_workspace_bytes(g);
+  if (!ws && need > 0) return fail(HILS_E_WORKSPACE, "workspace is NULL (%zu bytes needed)", need);
+  if (ws_bytes < need) return fail(HILS_E_WORKSPACE, "workspace too small: %zu < %zu", ws_bytes, need);
+  hipError_t e = hils::launch_decode(g, q, k_cache, v_cache, seq_lens, kc, bc, qcal_D, qcal_U, sel_idx_out, o, ws,
+                                     ws_bytes, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "hils_attn_decode");
+  g_err[0] = 0;
+  return HILS_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,183 @@
+"""Thin Python binding of libhils.so (include/hils.h).
+
+Argument marshalling only: every step of the HiLS forward pass runs in the HIP
+kernels of the library.  torch supplies device memory and the current stream.
+There is no fallback: if the library is missing or a call fails, an exception
+is raised.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libhils.so")
+
+F32, BF16 = 0, 1
+OP_COMPRESS, OP_SCORE_TOPK, OP_PREFILL, OP_DECODE = 0, 1, 2, 3
+OK, E_INVAL, E_UNSUPPORTED, E_WORKSPACE, E_HIP = 0, -1, -2, -3, -4
+
+SYMBOLS = ("hils_workspace_bytes", "hils_landmark_compress", "hils_chunk_score_topk", "hils_attn_prefill",
+           "hils_attn_decode", "hils_last_error")
+
+
+class Dims(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int32) for n in ("B", "Hq", "Hkv", "Hlmk", "d", "S", "K", "N", "qcal_rank", "io")]
+
+    def __repr__(self):
+        return "Dims(%s)" % ", ".join("%s=%d" % (n, getattr(self, n)) for n, _ in self._fields_)
+
+
+class HilsError(RuntimeError):
+    def __init__(self, code, msg):
+        super().__init__("%s (code %d)" % (msg, code))
+        self.code = code
+
+
+_lib = None
+
+
+def load():
+    """Load libhils.so (built in-tree by __graft_entry__.build())."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError("libhils.so is not built (%s); run __graft_entry__.build()" % LIB_PATH)
+        lib = ctypes.CDLL(LIB_PATH)
+        vp, i32, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t
+        dp = ctypes.POINTER(Dims)
+        lib.hils_workspace_bytes.argtypes = [dp, ctypes.c_int]
+        lib.hils_workspace_bytes.restype = sz
+        lib.hils_landmark_compress.argtypes = [dp, vp, vp, i32, i32, vp, vp, vp]
+        lib.hils_chunk_score_topk.argtypes = [dp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+        lib.hils_attn_prefill.argtypes = [dp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+        lib.hils_attn_decode.argtypes = [dp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+        for f in ("hils_landmark_compress", "hils_chunk_score_topk", "hils_attn_prefill", "hils_attn_decode"):
+            getattr(lib, f).restype = ctypes.c_int
+        lib.hils_last_error.argtypes = []
+        lib.hils_last_error.restype = ctypes.c_char_p
+        _lib = lib
+    return _lib
+
+
+def dims(B, Hq, Hkv, d, N, K, S=64, qcal_rank=0, io=BF16, Hlmk=None) -> Dims:
+    return Dims(B, Hq, Hkv, Hq if Hlmk is None else Hlmk, d, S, K, N, qcal_rank, io)
+
+
+def _check(rc):
+    if rc != OK:
+        raise HilsError(rc, load().hils_last_error().decode())
+
+
+def _p(t):
+    return None if t is None else t.data_ptr()
+
+
+def _stream():
+    return torch.cuda.current_stream().cuda_stream
+
+
+def _io(t) -> int:
+    if t.dtype == torch.bfloat16:
+        return BF16
+    if t.dtype == torch.float32:
+        return F32
+    raise TypeError("io tensors must be bfloat16 or float32, got %s" % t.dtype)
+
+
+def _req(t, name, shape=None, dtype=None):
+    if t is None:
+        raise ValueError("%s is required" % name)
+    if not t.is_cuda or not t.is_contiguous():
+        raise ValueError("%s must be a contiguous CUDA tensor" % name)
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError("%s has shape %s, expected %s" % (name, tuple(t.shape), tuple(shape)))
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError("%s has dtype %s, expected %s" % (name, t.dtype, dtype))
+    return t
+
+
+def workspace_bytes(dm: Dims, op: int) -> int:
+    n = load().hils_workspace_bytes(ctypes.byref(dm), op)
+    if n == ctypes.c_size_t(-1).value:
+        raise HilsError(E_INVAL, load().hils_last_error().decode())
+    return n
+
+
+def workspace(dm: Dims, op: int, device="cuda") -> torch.Tensor:
+    return torch.empty(max(1, workspace_bytes(dm, op)), dtype=torch.uint8, device=device)
+
+
+def landmark_compress(dm: Dims, k, lmk_q, kc, bc, c_begin=0, c_end=None):
+    C = dm.N // dm.S
+    c_end = C if c_end is None else c_end
+    dt = torch.float32 if dm.io == F32 else torch.bfloat16
+    _req(k, "k", (dm.B, dm.Hkv, dm.N, dm.d), dt)
+    _req(lmk_q, "lmk_q", (dm.B, dm.Hlmk, C, dm.d), dt)
+    _req(kc, "kc", (dm.B, dm.Hlmk, C, dm.d), torch.float32)
+    _req(bc, "bc", (dm.B, dm.Hlmk, C), torch.float32)
+    _check(load().hils_landmark_compress(ctypes.byref(dm), _p(k), _p(lmk_q), c_begin, c_end, _p(kc), _p(bc),
+                                         _stream()))
+
+
+def chunk_score_topk(dm: Dims, q, kc, bc, sel_idx, sel_score, qcal_D=None, qcal_U=None, ws=None):
+    C = dm.N // dm.S
+    dt = torch.float32 if dm.io == F32 else torch.bfloat16
+    _req(q, "q", (dm.B, dm.Hq, dm.N, dm.d), dt)
+    _req(kc, "kc", (dm.B, dm.Hlmk, C, dm.d), torch.float32)
+    _req(bc, "bc", (dm.B, dm.Hlmk, C), torch.float32)
+    _req(sel_idx, "sel_idx", (dm.B, dm.Hq, dm.N, dm.K), torch.int32)
+    _req(sel_score, "sel_score", (dm.B, dm.Hq, dm.N, dm.K), torch.float32)
+    if dm.qcal_rank > 0:
+        _req(qcal_D, "qcal_D", (dm.Hq, dm.qcal_rank, dm.d), dt)
+        _req(qcal_U, "qcal_U", (dm.Hq, dm.d, dm.qcal_rank), dt)
+    nws = ws.numel() if ws is not None else 0
+    _check(load().hils_chunk_score_topk(ctypes.byref(dm), _p(q), _p(qcal_D), _p(qcal_U), _p(kc), _p(bc), _p(sel_idx),
+                                        _p(sel_score), _p(ws), nws, _stream()))
+
+
+def attn_prefill(dm: Dims, q, k, v, o, ws, lmk_q=None, kc=None, bc=None, qcal_D=None, qcal_U=None, sel_idx=None,
+                 sel_score=None):
+    C = dm.N // dm.S
+    dt = torch.float32 if dm.io == F32 else torch.bfloat16
+    _req(q, "q", (dm.B, dm.Hq, dm.N, dm.d), dt)
+    _req(k, "k", (dm.B, dm.Hkv, dm.N, dm.d), dt)
+    _req(v, "v", (dm.B, dm.Hkv, dm.N, dm.d), dt)
+    _req(o, "o", (dm.B, dm.Hq, dm.N, dm.d), dt)
+    _req(ws, "ws", dtype=torch.uint8)
+    if lmk_q is not None:
+        _req(lmk_q, "lmk_q", (dm.B, dm.Hlmk, C, dm.d), dt)
+    if kc is not None:
+        _req(kc, "kc", (dm.B, dm.Hlmk, C, dm.d), torch.float32)
+        _req(bc, "bc", (dm.B, dm.Hlmk, C), torch.float32)
+    if dm.qcal_rank > 0:
+        _req(qcal_D, "qcal_D", (dm.Hq, dm.qcal_rank, dm.d), dt)
+        _req(qcal_U, "qcal_U", (dm.Hq, dm.d, dm.qcal_rank), dt)
+    if sel_idx is not None:
+        _req(sel_idx, "sel_idx", (dm.B, dm.Hq, dm.N, dm.K), torch.int32)
+    if sel_score is not None:
+        _req(sel_score, "sel_score", (dm.B, dm.Hq, dm.N, dm.K), torch.float32)
+    _check(load().hils_attn_prefill(ctypes.byref(dm), _p(q), _p(k), _p(v), _p(lmk_q), _p(kc), _p(bc), _p(qcal_D),
+                                    _p(qcal_U), _p(sel_idx), _p(sel_score), _p(o), _p(ws), ws.numel(), _stream()))
+
+
+def attn_decode(dm: Dims, q, k_cache, v_cache, seq_lens, kc, bc, o, ws, qcal_D=None, qcal_U=None, sel_idx=None):
+    C = dm.N // dm.S
+    dt = torch.float32 if dm.io == F32 else torch.bfloat16
+    _req(q, "q", (dm.B, dm.Hq, dm.d), dt)
+    _req(k_cache, "k_cache", (dm.B, dm.Hkv, dm.N, dm.d), dt)
+    _req(v_cache, "v_cache", (dm.B, dm.Hkv, dm.N, dm.d), dt)
+    _req(seq_lens, "seq_lens", (dm.B,), torch.int32)
+    _req(kc, "kc", (dm.B, dm.Hlmk, C, dm.d), torch.float32)
+    _req(bc, "bc", (dm.B, dm.Hlmk, C), torch.float32)
+    _req(o, "o", (dm.B, dm.Hq, dm.d), dt)
+    _req(ws, "ws", dtype=torch.uint8)
+    if dm.qcal_rank > 0:
+        _req(qcal_D, "qcal_D", (dm.Hq, dm.qcal_rank, dm.d), dt)
+        _req(qcal_U, "qcal_U", (dm.Hq, dm.d, dm.qcal_rank), dt)
+    if sel_idx is not None:
+        _req(sel_idx, "sel_idx", (dm.B, dm.Hq, dm.K), torch.int32)
+    _check(load().hils_attn_decode(ctypes.byref(dm), _p(q), _p(k_cache), _p(v_cache), _p(seq_lens), _p(kc), _p(bc),
+                                   _p(qcal_D), _p(qcal_U), _p(sel_idx), _p(o), _p(ws), ws.numel(), _stream()))

@@ -172,6 +172,8 @@ WORKLOADS = {
 def scaled(w: Workload, **kw) -> Workload:
     """A copy of w with some fields replaced (for smaller test shapes)."""
     import dataclasses
+    if "Hq" in kw and "Hlmk" not in kw:
+        kw["Hlmk"] = 0          # one landmark head per query head again
     return dataclasses.replace(w, **kw)
 
 

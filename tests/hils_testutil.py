@@ -1,0 +1,151 @@
+"""Shared helpers of the GPU parity tests: upload synthetic inputs, run the C ABI
+through the binding, compute the oracle on the same bits, and compare.
+
+Parity bar:
+  * selected chunk ids bit-exact for every query whose oracle K-th/(K+1)-th
+    score gap exceeds 1e-4;
+  * near-tie queries (gap <= 1e-4): the GPU set must be a valid top-K within
+    1e-4 of the oracle scores, and its output is compared with the oracle run on
+    the GPU's own selection;
+  * outputs: max |diff| <= 1e-2 and mean |diff| <= 1e-3 for bf16 I/O (fp32
+    accumulation), <= 1e-5 for fp32 I/O.
+"""
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+import oracle
+import synth
+from long_context_chunk_amd import hils
+
+GAP = 1e-4
+TOL = {synth.BF16: (1e-2, 1e-3), synth.F32: (1e-5, 1e-5)}
+
+
+def upload(a: np.ndarray, io: int) -> torch.Tensor:
+    if io == synth.BF16 and a.dtype == np.uint16:
+        return torch.from_numpy(a.view(np.int16)).cuda().view(torch.bfloat16)
+    return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+
+def download_f32(t: torch.Tensor) -> np.ndarray:
+    return t.float().cpu().numpy()
+
+
+def dims_of(w: synth.Workload) -> hils.Dims:
+    return hils.dims(w.B, w.Hq, w.Hkv, w.d, w.N, w.K, S=w.S, qcal_rank=w.qcal_rank, io=w.io, Hlmk=w.Hlmk)
+
+
+def shape_of(w: synth.Workload) -> oracle.Shape:
+    return oracle.shape(w.B, w.Hq, w.Hkv, w.d, w.N, S=w.S, K=w.K, Hl=w.Hlmk, r=w.qcal_rank)
+
+
+def gpu_compress(w, x):
+    dm = dims_of(w)
+    k = upload(x["k"], w.io)
+    lmk = upload(x["lmk"], w.io)
+    kc = torch.empty((w.B, w.Hlmk, w.C, w.d), dtype=torch.float32, device="cuda")
+    bc = torch.empty((w.B, w.Hlmk, w.C), dtype=torch.float32, device="cuda")
+    hils.landmark_compress(dm, k, lmk, kc, bc)
+    torch.cuda.synchronize()
+    return kc, bc
+
+
+def gpu_prefill(w, x, fused=True, kc=None, bc=None):
+    """Full prefill through hils_attn_prefill.  Returns numpy outputs."""
+    dm = dims_of(w)
+    q, k, v = upload(x["q"], w.io), upload(x["k"], w.io), upload(x["v"], w.io)
+    dt = q.dtype
+    o = torch.empty_like(q)
+    sel = torch.empty((w.B, w.Hq, w.N, w.K), dtype=torch.int32, device="cuda")
+    scr = torch.empty((w.B, w.Hq, w.N, w.K), dtype=torch.float32, device="cuda")
+    ws = hils.workspace(dm, hils.OP_PREFILL)
+    D = upload(x["D"], w.io) if w.qcal_rank else None
+    U = upload(x["U"], w.io) if w.qcal_rank else None
+    if fused:
+        kc = torch.empty((w.B, w.Hlmk, w.C, w.d), dtype=torch.float32, device="cuda")
+        bc = torch.empty((w.B, w.Hlmk, w.C), dtype=torch.float32, device="cuda")
+        hils.attn_prefill(dm, q, k, v, o, ws, lmk_q=upload(x["lmk"], w.io), kc=kc, bc=bc, qcal_D=D, qcal_U=U,
+                          sel_idx=sel, sel_score=scr)
+    else:
+        hils.attn_prefill(dm, q, k, v, o, ws, kc=kc, bc=bc, qcal_D=D, qcal_U=U, sel_idx=sel, sel_score=scr)
+    torch.cuda.synchronize()
+    assert o.dtype == dt
+    out = {"o": download_f32(o), "sel_idx": sel.cpu().numpy(), "sel_score": scr.cpu().numpy(),
+           "kc": kc.cpu().numpy(), "bc": bc.cpu().numpy()}
+    del ws
+    return out
+
+
+def oracle_compress(w, x):
+    return oracle.compress(shape_of(w), x["k"], x["lmk"])
+
+
+def oracle_rows(w, x, kc, bc, rows):
+    return oracle.prefill_rows(shape_of(w), x["q"], x["k"], x["v"], kc, bc, rows, D=x.get("D"), U=x.get("U"))
+
+
+def check_selection_and_output(w, x, kc_o, bc_o, rows, ref, gpu_sel, gpu_score, gpu_o, label=""):
+    """Compare the GPU's selection/output on `rows` with the oracle result `ref`.
+
+    gpu_sel / gpu_score: [n, K] in rank order; gpu_o: [n, d] (fp32 view of the io output).
+    Returns a summary dict.
+    """
+    s = shape_of(w)
+    n = len(rows)
+    max_tol, mean_tol = TOL[w.io]
+    exact_rows = 0
+    tie_rows = []
+    diffs = np.zeros((n, w.d))
+    for t in range(n):
+        ns = ref["nsel"][t]
+        o_sel = np.sort(ref["sel_idx"][t][:ns])
+        g_sel = gpu_sel[t]
+        g_valid = g_sel[g_sel >= 0]
+        assert len(g_valid) == ns, "%s row %s: %d selected, oracle %d" % (label, rows[t], len(g_valid), ns)
+        assert np.all(g_sel[ns:] == -1)
+        assert len(np.unique(g_valid)) == ns
+        if ref["gap"][t] > GAP:
+            assert np.array_equal(np.sort(g_valid), o_sel), "%s row %s: selection differs (gap %.3g)\n gpu %s\n ora %s" % (
+                label, rows[t], ref["gap"][t], np.sort(g_valid), o_sel)
+            exact_rows += 1
+            diffs[t] = gpu_o[t] - ref["o"][t]
+            if gpu_score is not None:  # rank order and scores
+                order = np.argsort(-ref["sel_score"][t][:ns], kind="stable")
+                np.testing.assert_allclose(gpu_score[t][:ns], ref["sel_score"][t][:ns][order], rtol=0, atol=2e-5)
+        else:
+            tie_rows.append(t)
+            b, h, i = rows[t]
+            allsc = oracle.row_scores(s, b, h, i, x["q"][b, h, i], kc=kc_o, bc=bc_o, D=x.get("D"), U=x.get("U"))
+            chosen = np.zeros(len(allsc), bool)
+            chosen[g_valid] = True
+            if chosen.any() and (~chosen).any():
+                assert allsc[chosen].min() >= allsc[~chosen].max() - GAP, "%s row %s: invalid near-tie set" % (label, rows[t])
+            r2 = oracle.attend(s, [b], [h], [i], x["q"][b, h, i][None], x["k"], x["v"], kc_o, bc_o, D=x.get("D"),
+                               U=x.get("U"), sel_in=g_sel[None])
+            diffs[t] = gpu_o[t] - r2["o"][0]
+    ad = np.abs(diffs)
+    assert ad.max() <= max_tol, "%s: max |diff| %.3g > %.3g" % (label, ad.max(), max_tol)
+    assert ad.mean() <= mean_tol, "%s: mean |diff| %.3g > %.3g" % (label, ad.mean(), mean_tol)
+    return {"rows": n, "exact_rows": exact_rows, "near_tie_rows": len(tie_rows), "max_abs": float(ad.max()),
+            "mean_abs": float(ad.mean())}
+
+
+def gpu_decode(w, x, kc=None, bc=None):
+    dm = dims_of(w)
+    k, v = upload(x["k"], w.io), upload(x["v"], w.io)
+    if kc is None:
+        kc = torch.empty((w.B, w.Hlmk, w.C, w.d), dtype=torch.float32, device="cuda")
+        bc = torch.empty((w.B, w.Hlmk, w.C), dtype=torch.float32, device="cuda")
+        hils.landmark_compress(dm, k, upload(x["lmk"], w.io), kc, bc)
+    q = upload(x["q"], w.io)
+    lens = torch.from_numpy(x["seq_lens"]).cuda()
+    o = torch.empty_like(q)
+    sel = torch.empty((w.B, w.Hq, w.K), dtype=torch.int32, device="cuda")
+    ws = hils.workspace(dm, hils.OP_DECODE)
+    D = upload(x["D"], w.io) if w.qcal_rank else None
+    U = upload(x["U"], w.io) if w.qcal_rank else None
+    hils.attn_decode(dm, q, k, v, lens, kc, bc, o, ws, qcal_D=D, qcal_U=U, sel_idx=sel)
+    torch.cuda.synchronize()
+    return {"o": download_f32(o), "sel_idx": sel.cpu().numpy(), "kc": kc, "bc": bc}

@@ -1,0 +1,118 @@
+"""Host-side checks of the C ABI (no GPU needed): the library loads and exports
+every symbol include/hils.h declares, the header compiles as C99, and argument
+validation returns the documented error codes without touching the device."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+from long_context_chunk_amd import hils
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "hils.h")
+
+
+def _declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(hils_[a-z_]+)\s*\(", src)))
+
+
+def test_header_compiles_as_c99():
+    subprocess.check_call(["gcc", "-std=c99", "-Wall", "-Werror", "-fsyntax-only", "-x", "c", HEADER])
+
+
+def test_library_exports_every_declared_symbol():
+    lib = hils.load()
+    names = _declared_functions()
+    assert set(names) == set(hils.SYMBOLS), names
+    for n in names:
+        assert hasattr(lib, n), n
+    out = subprocess.check_output(["nm", "-D", "--defined-only", hils.LIB_PATH], text=True)
+    for n in names:
+        assert re.search(r"\bT %s\b" % n, out), n
+
+
+def _rc(fn, *args):
+    return fn(*args)
+
+
+def test_workspace_bytes():
+    d = hils.dims(1, 32, 8, 128, 262144, 32, qcal_rank=32)
+    n = hils.workspace_bytes(d, hils.OP_PREFILL)
+    # the fp16 per-pair partial outputs dominate: B*Hq*N*K*d*2 bytes
+    assert n >= 1 * 32 * 262144 * 32 * 128 * 2
+    assert hils.workspace_bytes(d, hils.OP_COMPRESS) == 0
+    assert hils.workspace_bytes(d, hils.OP_SCORE_TOPK) == 0
+    dd = hils.dims(8, 32, 8, 128, 524288, 32)
+    assert 0 < hils.workspace_bytes(dd, hils.OP_DECODE) < 64 << 20
+    with pytest.raises(hils.HilsError):
+        hils.workspace_bytes(dd, hils.OP_PREFILL)   # 32-bit pair ids: B*Hq*N*K >= 2^32
+    with pytest.raises(hils.HilsError):
+        hils.workspace_bytes(d, 7)
+
+
+@pytest.mark.parametrize("field,value,code", [
+    ("d", 96, hils.E_UNSUPPORTED), ("S", 32, hils.E_UNSUPPORTED), ("K", 0, hils.E_INVAL), ("K", 33, hils.E_UNSUPPORTED),
+    ("Hkv", 3, hils.E_INVAL), ("Hlmk", 8, hils.E_UNSUPPORTED), ("B", 0, hils.E_INVAL), ("N", 0, hils.E_INVAL),
+    ("io", 5, hils.E_UNSUPPORTED), ("qcal_rank", -1, hils.E_INVAL), ("qcal_rank", 64, hils.E_UNSUPPORTED),
+])
+def test_invalid_dims_rejected(field, value, code):
+    lib = hils.load()
+    d = hils.dims(1, 16, 4, 64, 1024, 16)
+    setattr(d, field, value)
+    fake = ctypes.c_void_p(0x1000)  # never dereferenced: validation fails first
+    rc = lib.hils_landmark_compress(ctypes.byref(d), fake, fake, 0, 1, fake, fake, None)
+    assert rc == code, (rc, lib.hils_last_error())
+    assert lib.hils_last_error()
+    rc = lib.hils_attn_prefill(ctypes.byref(d), fake, fake, fake, None, fake, fake, None, None, None, None, fake,
+                               fake, 1 << 40, None)
+    assert rc == code
+
+
+def test_null_pointers_and_ranges_rejected():
+    lib = hils.load()
+    d = hils.dims(1, 16, 4, 64, 1024, 16)
+    fake = ctypes.c_void_p(0x1000)
+    assert lib.hils_landmark_compress(None, fake, fake, 0, 1, fake, fake, None) == hils.E_INVAL
+    assert lib.hils_landmark_compress(ctypes.byref(d), None, fake, 0, 1, fake, fake, None) == hils.E_INVAL
+    assert lib.hils_landmark_compress(ctypes.byref(d), fake, fake, 5, 4, fake, fake, None) == hils.E_INVAL
+    assert lib.hils_landmark_compress(ctypes.byref(d), fake, fake, 0, 17, fake, fake, None) == hils.E_INVAL
+    assert lib.hils_chunk_score_topk(ctypes.byref(d), fake, None, None, fake, fake, None, fake, None, 0,
+                                     None) == hils.E_INVAL
+    # prefill without landmark queries needs kc/bc
+    assert lib.hils_attn_prefill(ctypes.byref(d), fake, fake, fake, None, None, None, None, None, None, None, fake,
+                                 fake, 1 << 40, None) == hils.E_INVAL
+    # Q-Cal rank without matrices
+    dq = hils.dims(1, 16, 4, 64, 1024, 16, qcal_rank=8)
+    assert lib.hils_attn_prefill(ctypes.byref(dq), fake, fake, fake, fake, fake, fake, None, None, None, None, fake,
+                                 fake, 1 << 40, None) == hils.E_INVAL
+    assert lib.hils_attn_decode(ctypes.byref(d), fake, fake, fake, None, fake, fake, None, None, None, fake, fake,
+                                1 << 30, None) == hils.E_INVAL
+
+
+def test_workspace_too_small_rejected():
+    lib = hils.load()
+    d = hils.dims(1, 16, 4, 64, 1024, 16)
+    fake = ctypes.c_void_p(0x1000)
+    need = hils.workspace_bytes(d, hils.OP_PREFILL)
+    rc = lib.hils_attn_prefill(ctypes.byref(d), fake, fake, fake, fake, fake, fake, None, None, None, None, fake, fake,
+                               need - 1, None)
+    assert rc == hils.E_WORKSPACE
+    assert b"too small" in lib.hils_last_error()
+    need = hils.workspace_bytes(d, hils.OP_DECODE)
+    rc = lib.hils_attn_decode(ctypes.byref(d), fake, fake, fake, fake, fake, fake, None, None, None, fake, fake,
+                              need - 1, None)
+    assert rc == hils.E_WORKSPACE
+
+
+def test_product_path_does_not_import_oracle():
+    """The library binding and package never reference the oracle."""
+    pkg = os.path.join(ROOT, "long_context_chunk_amd")
+    for dirpath, _, files in os.walk(pkg):
+        for f in files:
+            if f.endswith((".py", ".hip", ".h", ".cpp")):
+                txt = open(os.path.join(dirpath, f)).read()
+                assert "import oracle" not in txt and "hils_oracle" not in txt and "from oracle" not in txt, f

@@ -1,0 +1,235 @@
+"""GPU parity of the HIP path against the fp64 oracle at sizes the oracle
+finishes in seconds (several tiles, ragged tails, degenerate cases).
+
+All calls go through the C ABI (libhils.so) via the Python binding.
+"""
+import math
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from hils_testutil import (TOL, check_selection_and_output, dims_of, gpu_compress, gpu_decode, gpu_prefill,
+                           oracle_compress, oracle_rows, shape_of, upload)
+from long_context_chunk_amd import hils
+
+pytestmark = pytest.mark.gpu
+
+SEED = synth.BASE_SEED
+
+
+def _say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+# small workloads: (name, Workload)
+SMALL = [
+    ("tiny_f32", synth.WORKLOADS["tiny_f32"]),
+    ("bf16_d64_ragged", synth.scaled(synth.WORKLOADS["prefill_8k"], N=2000)),
+    ("bf16_d128_qcal_ragged", synth.scaled(synth.WORKLOADS["prefill_256k_qcal"], N=1500, Hq=8, Hkv=2, K=8)),
+    ("f32_d128_qcal", synth.Workload("f32_d128_qcal", B=2, Hq=4, Hkv=2, d=128, N=777, K=5, io=synth.F32,
+                                     qcal_rank=16)),
+    ("bf16_d64_B2_K32", synth.Workload("bf16_d64_B2_K32", B=2, Hq=4, Hkv=1, d=64, N=3000, K=32)),
+]
+
+
+@pytest.mark.parametrize("name,w", SMALL, ids=[n for n, _ in SMALL])
+def test_compress(name, w):
+    _say("compress", name)
+    x = synth.make_inputs(w, SEED)
+    kc, bc = gpu_compress(w, x)
+    kc_o, bc_o = oracle_compress(w, x)
+    kc, bc = kc.cpu().numpy(), bc.cpu().numpy()
+    np.testing.assert_allclose(kc, kc_o, rtol=0, atol=1e-5 * max(1.0, np.abs(kc_o).max()))
+    np.testing.assert_allclose(bc, bc_o, rtol=0, atol=1e-5)
+
+
+def test_compress_range_leaves_other_chunks():
+    w = synth.scaled(synth.WORKLOADS["prefill_8k"], N=1024, Hq=4, Hkv=2)
+    x = synth.make_inputs(w, SEED + 1)
+    dm = dims_of(w)
+    k, lmk = upload(x["k"], w.io), upload(x["lmk"], w.io)
+    kc = torch.full((w.B, w.Hq, w.C, w.d), 7.0, device="cuda")
+    bc = torch.full((w.B, w.Hq, w.C), 7.0, device="cuda")
+    hils.landmark_compress(dm, k, lmk, kc, bc, 3, 9)
+    torch.cuda.synchronize()
+    kc_o, bc_o = oracle_compress(w, x)
+    kc, bc = kc.cpu().numpy(), bc.cpu().numpy()
+    assert np.all(kc[:, :, :3] == 7.0) and np.all(kc[:, :, 9:] == 7.0) and np.all(bc[:, :, 9:] == 7.0)
+    np.testing.assert_allclose(kc[:, :, 3:9], kc_o[:, :, 3:9], atol=1e-5 * np.abs(kc_o).max())
+    np.testing.assert_allclose(bc[:, :, 3:9], bc_o[:, :, 3:9], atol=1e-5)
+
+
+@pytest.mark.parametrize("name,w", SMALL, ids=[n for n, _ in SMALL])
+def test_score_topk_on_oracle_landmarks(name, w):
+    """Staged: the GPU scores the oracle's k'/b' (rounded to fp32)."""
+    _say("score_topk", name)
+    x = synth.make_inputs(w, SEED)
+    kc_o, bc_o = oracle_compress(w, x)
+    dm = dims_of(w)
+    q = upload(x["q"], w.io)
+    kc = torch.from_numpy(kc_o.astype(np.float32)).cuda()
+    bc = torch.from_numpy(bc_o.astype(np.float32)).cuda()
+    sel = torch.empty((w.B, w.Hq, w.N, w.K), dtype=torch.int32, device="cuda")
+    scr = torch.empty((w.B, w.Hq, w.N, w.K), dtype=torch.float32, device="cuda")
+    D = upload(x["D"], w.io) if w.qcal_rank else None
+    U = upload(x["U"], w.io) if w.qcal_rank else None
+    hils.chunk_score_topk(dm, q, kc, bc, sel, scr, qcal_D=D, qcal_U=U)
+    torch.cuda.synchronize()
+    sel, scr = sel.cpu().numpy(), scr.cpu().numpy()
+    rows = [(b, h, i) for b in range(w.B) for h in range(w.Hq) for i in range(w.N)]
+    ref = oracle_rows(w, x, kc_o.astype(np.float32).astype(np.float64), bc_o.astype(np.float32).astype(np.float64),
+                      rows)
+    mism = 0
+    for t, (b, h, i) in enumerate(rows):
+        ns = ref["nsel"][t]
+        g = sel[b, h, i]
+        assert np.all(g[ns:] == -1) and np.all(np.isneginf(scr[b, h, i][ns:]))
+        if ref["gap"][t] > 1e-4:
+            if not np.array_equal(np.sort(g[:ns]), np.sort(ref["sel_idx"][t][:ns])):
+                mism += 1
+        # rank order: scores non-increasing
+        assert np.all(np.diff(scr[b, h, i][:ns]) <= 0)
+    assert mism == 0, "%d rows with gap > 1e-4 select different chunks" % mism
+
+
+@pytest.mark.parametrize("name,w", SMALL, ids=[n for n, _ in SMALL])
+def test_prefill_end_to_end(name, w):
+    _say("prefill", name)
+    x = synth.make_inputs(w, SEED)
+    g = gpu_prefill(w, x, fused=True)
+    kc_o, bc_o = oracle_compress(w, x)
+    rows = [(b, h, i) for b in range(w.B) for h in range(w.Hq) for i in range(w.N)]
+    ref = oracle_rows(w, x, kc_o, bc_o, rows)
+    rr = np.asarray(rows)
+    summ = check_selection_and_output(w, x, kc_o, bc_o, rows, ref, g["sel_idx"][rr[:, 0], rr[:, 1], rr[:, 2]],
+                                      g["sel_score"][rr[:, 0], rr[:, 1], rr[:, 2]],
+                                      g["o"][rr[:, 0], rr[:, 1], rr[:, 2]], label=name)
+    _say(name, summ)
+
+
+def test_prefill_unfused_matches_fused():
+    w = SMALL[1][1]
+    x = synth.make_inputs(w, SEED + 2)
+    a = gpu_prefill(w, x, fused=True)
+    kc = torch.from_numpy(a["kc"]).cuda()
+    bc = torch.from_numpy(a["bc"]).cuda()
+    b = gpu_prefill(w, x, fused=False, kc=kc, bc=bc)
+    np.testing.assert_array_equal(a["sel_idx"], b["sel_idx"])
+    np.testing.assert_array_equal(a["o"], b["o"])
+
+
+def test_prefill_deterministic():
+    w = SMALL[2][1]
+    x = synth.make_inputs(w, SEED + 3)
+    a = gpu_prefill(w, x)
+    b = gpu_prefill(w, x)
+    np.testing.assert_array_equal(a["sel_idx"], b["sel_idx"])
+    np.testing.assert_array_equal(a["sel_score"], b["sel_score"])
+    np.testing.assert_array_equal(a["o"], b["o"])
+
+
+@pytest.mark.parametrize("N", [1, 17, 64, 65, 128, 129])
+def test_prefill_short_sequences(N):
+    """Sequences shorter than a few chunks: no or one past chunk, partial own chunk."""
+    w = synth.Workload("short", B=1, Hq=2, Hkv=1, d=64, N=N, K=3)
+    x = synth.make_inputs(w, SEED + N)
+    g = gpu_prefill(w, x)
+    kc_o, bc_o = oracle_compress(w, x)
+    rows = [(0, h, i) for h in range(2) for i in range(N)]
+    ref = oracle_rows(w, x, kc_o, bc_o, rows)
+    rr = np.asarray(rows)
+    check_selection_and_output(w, x, kc_o, bc_o, rows, ref, g["sel_idx"][rr[:, 0], rr[:, 1], rr[:, 2]],
+                               g["sel_score"][rr[:, 0], rr[:, 1], rr[:, 2]], g["o"][rr[:, 0], rr[:, 1], rr[:, 2]],
+                               label="N=%d" % N)
+
+
+def _dense_causal_rows(q, k, v, tau):
+    qt = torch.from_numpy(q.astype(np.float64))[None, None]
+    kt = torch.from_numpy(k.astype(np.float64))[None, None]
+    vt = torch.from_numpy(v.astype(np.float64))[None, None]
+    return torch.nn.functional.scaled_dot_product_attention(qt, kt, vt, is_causal=True, scale=tau)[0, 0].numpy()
+
+
+@pytest.mark.parametrize("io", [synth.F32, synth.BF16])
+def test_dense_reduction_chunk_constant_keys(io):
+    """Chunk-constant keys and K >= number of chunks: HiLS equals dense causal attention."""
+    d, S, C = 64, 64, 20
+    N = C * S + 30
+    rng = np.random.default_rng(5)
+    kappa = rng.standard_normal((C + 1, d)).astype(np.float32)
+    k = np.repeat(kappa, S, axis=0)[:N]
+    v = rng.standard_normal((N, d)).astype(np.float32)
+    q = rng.standard_normal((N, d)).astype(np.float32)
+    lmk = rng.standard_normal((C, d)).astype(np.float32)
+    if io == synth.BF16:
+        to = lambda a: torch.from_numpy(a).to(torch.bfloat16)
+        k, v, q, lmk = [to(a).float().numpy() for a in (k, v, q, lmk)]
+    w = synth.Workload("dense", B=1, Hq=1, Hkv=1, d=d, N=N, K=32, io=io, planted=False)
+    dm = dims_of(w)
+    dev = lambda a: torch.from_numpy(a.reshape(1, 1, *a.shape)).cuda().to(torch.float32 if io == synth.F32
+                                                                          else torch.bfloat16)
+    qt, kt, vt, lt = dev(q), dev(k), dev(v), dev(lmk)
+    o = torch.empty_like(qt)
+    ws = hils.workspace(dm, hils.OP_PREFILL)
+    hils.attn_prefill(dm, qt, kt, vt, o, ws, lmk_q=lt)
+    torch.cuda.synchronize()
+    ref = _dense_causal_rows(q, k, v, 1 / math.sqrt(d))
+    diff = np.abs(o.float().cpu().numpy()[0, 0] - ref)
+    mx, mean = TOL[io]
+    assert diff.max() <= mx and diff.mean() <= mean, (diff.max(), diff.mean())
+
+
+DECODE_SMALL = [
+    ("bf16_d128", synth.Workload("dec_bf16_d128", B=5, Hq=8, Hkv=2, d=128, N=4096, K=8, decode=True,
+                                 seq_lens=[1, 64, 65, 1000, 4096], needle_frac=0.05)),
+    ("bf16_d64_qcal", synth.Workload("dec_bf16_d64_qcal", B=3, Hq=4, Hkv=4, d=64, N=3000, K=16, decode=True,
+                                     seq_lens=[2999, 3000, 640], qcal_rank=8, planted_seqs=1)),
+    ("f32_d64", synth.Workload("dec_f32_d64", B=2, Hq=2, Hkv=1, d=64, N=2048, K=4, io=synth.F32, decode=True,
+                               seq_lens=[2048, 1111], planted=False)),
+]
+
+
+@pytest.mark.parametrize("name,w", DECODE_SMALL, ids=[n for n, _ in DECODE_SMALL])
+def test_decode(name, w):
+    _say("decode", name)
+    x = synth.make_inputs(w, SEED)
+    g = gpu_decode(w, x)
+    kc_o, bc_o = oracle_compress(w, x)
+    s = shape_of(w)
+    rows_b = [b for b in range(w.B) for h in range(w.Hq)]
+    rows_h = [h for b in range(w.B) for h in range(w.Hq)]
+    pos = [int(x["seq_lens"][b]) - 1 for b in rows_b]
+    qrows = x["q"].reshape(w.B * w.Hq, w.d)
+    ref = oracle.attend(s, rows_b, rows_h, pos, qrows, x["k"], x["v"], kc_o, bc_o, D=x.get("D"), U=x.get("U"))
+    xx = dict(x)
+
+    class QView:  # check_selection_and_output indexes q as [b, h, i]
+
+        def __getitem__(self, key):
+            b, h, i = key
+            return x["q"][b, h]
+    xx["q"] = QView()
+    rows = list(zip(rows_b, rows_h, pos))
+    summ = check_selection_and_output(w, xx, kc_o, bc_o, rows, ref, g["sel_idx"].reshape(-1, w.K), None,
+                                      g["o"].reshape(-1, w.d), label=name)
+    _say(name, summ)
+
+
+def test_decode_matches_prefill_row():
+    """A decode step at cache length L reproduces prefill row L-1 (same kernels' inputs)."""
+    L = 1000
+    w = synth.Workload("pre", B=1, Hq=4, Hkv=2, d=128, N=L, K=8)
+    x = synth.make_inputs(w, SEED + 9)
+    pre = gpu_prefill(w, x)
+    wd = synth.Workload("dec", B=1, Hq=4, Hkv=2, d=128, N=L, K=8, decode=True, seq_lens=[L])
+    xd = {"k": x["k"], "v": x["v"], "lmk": x["lmk"], "q": np.ascontiguousarray(x["q"][:, :, L - 1]),
+          "seq_lens": np.asarray([L], np.int32)}
+    dec = gpu_decode(wd, xd, kc=torch.from_numpy(pre["kc"]).cuda(), bc=torch.from_numpy(pre["bc"]).cuda())
+    for h in range(4):
+        assert set(dec["sel_idx"][0, h]) == set(pre["sel_idx"][0, h, L - 1])
+    np.testing.assert_allclose(dec["o"][0], pre["o"][0, :, L - 1], rtol=0, atol=1e-2)
