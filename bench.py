@@ -1,0 +1,367 @@
+"""Benchmark of the HiLS-Attention forward pass on one MI355X.
+
+One step = one full prefill pass of a 7B-like attention layer at 256K context
+(B=1, 32 query / 8 KV heads, d=128, S=64, K=32, bf16 I/O, Q-Cal rank 32,
+landmark compression in the same call): compression, Q-Cal, chunk scoring +
+top-K, intra-chunk attention and fusion, all through hils_attn_prefill.
+Inputs are synthetic (seeded, with the planted-direction retrieval structure)
+and resident in HBM before timing starts.
+
+Also reported on the same line:
+  * decode: one decode step of 8 sequences against a 512K-token KV cache
+    (32/8 heads, d=128, K=32), microseconds per step, with its roofline;
+  * roofline of the dominant prefill kernel from HIP-event stage times;
+  * cpu_baseline: the fp64 oracle on a bounded sample of the same workload;
+  * dense: torch SDPA causal attention on the same q/k/v (the pages compare
+    against full attention).
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-decode] [--no-cpu] [--no-dense]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "HiLS prefill tokens/s and decode us/step at 128K-512K ctx; % MFMA/HBM peak"
+PEAK_BF16_TFLOPS = 2516.6   # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def upload(a, io):
+    import torch
+    import synth
+    if io == synth.BF16:
+        return torch.from_numpy(a.view(np.int16)).cuda().view(torch.bfloat16)
+    return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+
+def prefill_counts(w):
+    """Algorithmic work of one prefill pass (2 flops per MAC, exp/log not counted)."""
+    S, d, K, C, N = w.S, w.d, w.K, w.C, w.N
+    rows_per_head = 0
+    score_macs = 0
+    intra_macs = 0
+    pairs = 0
+    for p in range((N + S - 1) // S):            # query chunk p holds rows p*S .. p*S+S-1
+        nrow = min(S, N - p * S)
+        P = min(p, C)
+        n = min(K, P)
+        score_macs += nrow * P * d
+        pairs += nrow * n
+        own = sum(i + 1 for i in range(nrow))    # causal own-chunk keys
+        intra_macs += 2 * d * (nrow * n * S + own)
+        rows_per_head += nrow
+    H = w.B * w.Hq
+    return {
+        "compress_flops": 4.0 * S * d * w.B * w.Hlmk * C,
+        "qcal_flops": 4.0 * w.qcal_rank * d * H * rows_per_head,
+        "score_flops": 2.0 * score_macs * H,
+        "intra_flops": 2.0 * intra_macs * H,
+        "pairs": pairs * H,
+    }
+
+
+def stage_roofline(w, cnt, stage_ms, io_bytes=2):
+    """Algorithmic bytes / flops per launch of each prefill stage and its roofline fraction."""
+    d, S = w.d, w.S
+    nbk = w.B * w.Hkv * w.C
+    out = {}
+    # compression: read K and the landmark queries once, write k' (fp32) and b'
+    comp_bytes = (w.B * w.Hkv * w.C * S * d * io_bytes + w.B * w.Hlmk * w.C * d * io_bytes
+                  + w.B * w.Hlmk * w.C * (d + 1) * 4)
+    # chunk attention: per (query, chunk) pair the gathered query row, its pair id and its
+    # fp16 partial output; per bucket one K/V chunk tile
+    ca_bytes = cnt["pairs"] * (d * io_bytes + 4 + d * 2) + nbk * 2 * S * d * io_bytes
+    ca_flops = cnt["pairs"] * 4.0 * S * d
+    st_flops = cnt["score_flops"] + cnt["qcal_flops"]
+    for name, kind, amount in (("compress", "hbm", comp_bytes), ("score_topk", "mfma", st_flops),
+                               ("chunk_attend", "hbm", ca_bytes)):
+        ms = stage_ms[name]
+        if kind == "hbm":
+            ach = amount / (ms * 1e-3) / 1e9
+            out[name] = {"bound": "hbm", "achieved": ach, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                         "frac": ach / PEAK_HBM_GBS, "algorithmic_bytes": amount, "ms": ms}
+        else:
+            ach = amount / (ms * 1e-3) / 1e12
+            out[name] = {"bound": "mfma", "achieved": ach, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                         "frac": ach / PEAK_BF16_TFLOPS, "algorithmic_flops": amount, "ms": ms}
+    out["chunk_attend"]["mfma_frac_algorithmic"] = ca_flops / (stage_ms["chunk_attend"] * 1e-3) / 1e12 / PEAK_BF16_TFLOPS
+    return out
+
+
+def run_prefill(w, steps, warmup, seed):
+    import torch
+    import synth
+    from long_context_chunk_amd import hils
+    t0 = time.time()
+    x = synth.make_inputs(w, seed)
+    log("prefill inputs generated in %.1fs" % (time.time() - t0))
+    dm = hils.dims(w.B, w.Hq, w.Hkv, w.d, w.N, w.K, S=w.S, qcal_rank=w.qcal_rank, io=w.io)
+    q, k, v, lmk = (upload(x[n], w.io) for n in ("q", "k", "v", "lmk"))
+    D = upload(x["D"], w.io) if w.qcal_rank else None
+    U = upload(x["U"], w.io) if w.qcal_rank else None
+    host = x
+    o = torch.empty_like(q)
+    kc = torch.empty((w.B, w.Hlmk, w.C, w.d), dtype=torch.float32, device="cuda")
+    bc = torch.empty((w.B, w.Hlmk, w.C), dtype=torch.float32, device="cuda")
+    sel = torch.empty((w.B, w.Hq, w.N, w.K), dtype=torch.int32, device="cuda")
+    scr = torch.empty((w.B, w.Hq, w.N, w.K), dtype=torch.float32, device="cuda")
+    ws = hils.workspace(dm, hils.OP_PREFILL)
+    log("prefill workspace %.1f GiB" % (ws.numel() / 2**30))
+
+    def step():
+        hils.attn_prefill(dm, q, k, v, o, ws, lmk_q=lmk, kc=kc, bc=bc, qcal_D=D, qcal_U=U, sel_idx=sel,
+                          sel_score=scr)
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(steps):
+        step()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    log("prefill: %.3f ms/step" % ms)
+    # per-stage times (HIP events recorded by the library on the launch stream)
+    stages = {s: 0.0 for s in hils.STAGES}
+    nrep = max(1, min(steps, 5))
+    for _ in range(nrep):
+        r = hils.attn_prefill(dm, q, k, v, o, ws, lmk_q=lmk, kc=kc, bc=bc, qcal_D=D, qcal_U=U, sel_idx=sel,
+                              sel_score=scr, timed=True)
+        for s_ in stages:
+            stages[s_] += r[s_] / nrep
+    log("stages (ms): " + ", ".join("%s %.3f" % kv for kv in stages.items()))
+    return {"ms": ms, "stages": stages, "tensors": (q, k, v, o, sel, kc, bc), "host": host, "ws": ws}
+
+
+def sampled_parity(w, res, nrows=64, seed=7):
+    """Oracle check of a few random rows of the benchmarked output (same launch configuration)."""
+    import oracle
+    x = res["host"]
+    q, k, v, o, sel, kc, bc = res["tensors"]
+    rng = np.random.default_rng(seed)
+    rows = [(0, int(rng.integers(w.Hq)), int(rng.integers(w.N))) for _ in range(nrows)]
+    s = oracle.shape(w.B, w.Hq, w.Hkv, w.d, w.N, S=w.S, K=w.K, r=w.qcal_rank)
+    # landmarks of the needed heads only
+    heads = sorted({h for _, h, _ in rows})
+    kc_o = np.zeros((w.B, w.Hq, w.C, w.d))
+    bc_o = np.zeros((w.B, w.Hq, w.C))
+    for h in heads:
+        s1 = oracle.shape(1, 1, 1, w.d, w.N, S=w.S, K=w.K)
+        kvh = h // (w.Hq // w.Hkv)
+        a, b = oracle.compress(s1, np.ascontiguousarray(x["k"][0:1, kvh:kvh + 1]),
+                               np.ascontiguousarray(x["lmk"][0:1, h:h + 1]))
+        kc_o[0, h], bc_o[0, h] = a[0, 0], b[0, 0]
+    ref = oracle.prefill_rows(s, x["q"], x["k"], x["v"], kc_o, bc_o, rows, D=x.get("D"), U=x.get("U"))
+    og = o.float()
+    worst, exact, ties = 0.0, 0, 0
+    for t, (b, h, i) in enumerate(rows):
+        g_sel = sel[b, h, i].cpu().numpy()
+        if ref["gap"][t] > 1e-4:
+            exact += int(set(g_sel[g_sel >= 0]) == set(ref["sel_idx"][t][:ref["nsel"][t]]))
+            worst = max(worst, float(np.abs(og[b, h, i].cpu().numpy() - ref["o"][t]).max()))
+        else:
+            ties += 1
+    return {"rows": nrows, "selection_exact": exact, "near_tie_rows": ties, "max_abs_diff": worst}
+
+
+def cpu_baseline(w, res, target_s=15.0):
+    """The fp64 oracle on the host cores: all-chunk compression + a uniform sample of query rows."""
+    import oracle
+    x = res["host"]
+    s = oracle.shape(w.B, w.Hq, w.Hkv, w.d, w.N, S=w.S, K=w.K, r=w.qcal_rank)
+    cores = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
+    t0 = time.time()
+    kc_o, bc_o = oracle.compress(s, x["k"], x["lmk"])
+    t_comp = time.time() - t0
+    rng = np.random.default_rng(11)
+    total_rows = w.B * w.Hq * w.N
+    n = 256
+    t_rows, done = 0.0, 0
+    while t_rows < target_s - t_comp and done < total_rows:
+        rows = [(int(rng.integers(w.B)), int(rng.integers(w.Hq)), int(rng.integers(w.N))) for _ in range(n)]
+        t1 = time.time()
+        oracle.prefill_rows(s, x["q"], x["k"], x["v"], kc_o, bc_o, rows, D=x.get("D"), U=x.get("U"))
+        t_rows += time.time() - t1
+        done += n
+        n *= 2
+    t_full = t_comp + t_rows * total_rows / done
+    return {"value": w.B * w.N / t_full, "unit": "tokens/s", "cores": cores, "kind": "oracle",
+            "sample": "landmark compression of all %d chunks x %d heads (%.1fs) + %d of %d query rows drawn "
+                      "uniformly (%.1fs), scaled to the full layer" % (w.C, w.Hlmk, t_comp, done, total_rows, t_rows)}
+
+
+def dense_baseline(res, w, reps=2):
+    """torch SDPA causal attention (flash / memory-efficient kernels only) on the same q/k/v."""
+    import torch
+    from torch.nn.attention import SDPBackend, sdpa_kernel
+    q, k, v = res["tensors"][:3]
+    G = w.Hq // w.Hkv
+    k2 = k.repeat_interleave(G, dim=1).contiguous()
+    v2 = v.repeat_interleave(G, dim=1).contiguous()
+    f = torch.nn.functional.scaled_dot_product_attention
+    with torch.no_grad(), sdpa_kernel([SDPBackend.FLASH_ATTENTION, SDPBackend.EFFICIENT_ATTENTION]):
+        f(q, k2, v2, is_causal=True)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            f(q, k2, v2, is_causal=True)
+        e1.record()
+        torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    del k2, v2
+    return {"impl": "torch SDPA causal, flash/mem-efficient backend, KV heads repeated to Hq", "ms": ms,
+            "tokens_per_s": w.B * w.N / (ms * 1e-3)}
+
+
+def run_decode(wd, steps, warmup, seed):
+    import torch
+    import synth
+    from long_context_chunk_amd import hils
+    t0 = time.time()
+    x = synth.make_inputs(wd, seed)
+    log("decode inputs generated in %.1fs" % (time.time() - t0))
+    dm = hils.dims(wd.B, wd.Hq, wd.Hkv, wd.d, wd.N, wd.K, S=wd.S, qcal_rank=wd.qcal_rank, io=wd.io)
+    kcache, vcache, lmk = (upload(x[n], wd.io) for n in ("k", "v", "lmk"))
+    del x["k"], x["v"]
+    q = upload(x["q"], wd.io)
+    lens = torch.from_numpy(x["seq_lens"]).cuda()
+    kc = torch.empty((wd.B, wd.Hlmk, wd.C, wd.d), dtype=torch.float32, device="cuda")
+    bc = torch.empty((wd.B, wd.Hlmk, wd.C), dtype=torch.float32, device="cuda")
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    hils.landmark_compress(dm, kcache, lmk, kc, bc)
+    e1.record()
+    torch.cuda.synchronize()
+    comp_ms = e0.elapsed_time(e1)
+    o = torch.empty_like(q)
+    sel = torch.empty((wd.B, wd.Hq, wd.K), dtype=torch.int32, device="cuda")
+    ws = hils.workspace(dm, hils.OP_DECODE)
+    flush = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
+    for _ in range(warmup):
+        hils.attn_decode(dm, q, kcache, vcache, lens, kc, bc, o, ws, sel_idx=sel)
+    torch.cuda.synchronize()
+    tot, stages = 0.0, {s: 0.0 for s in hils.DECODE_STAGES}
+    for _ in range(steps):
+        flush.fill_(1)   # evict k' and the KV chunks from the 256 MB Infinity Cache (untimed)
+        r = hils.attn_decode(dm, q, kcache, vcache, lens, kc, bc, o, ws, sel_idx=sel, timed=True)
+        for s_ in stages:
+            stages[s_] += r[s_] / steps
+    us = sum(stages.values()) * 1e3
+    # algorithmic bytes per step: q, o; k' and b' of every past chunk; the K/V rows of the
+    # union of selected chunks per (sequence, KV head) plus the own chunk
+    seln = sel.cpu().numpy()
+    G = wd.Hq // wd.Hkv
+    kv_bytes = 0
+    for b in range(wd.B):
+        L = int(x["seq_lens"][b])
+        P = min(wd.C, (L - 1) // wd.S)
+        for g in range(wd.Hkv):
+            u = set(seln[b, g * G:(g + 1) * G].ravel().tolist()) - {-1}
+            kv_bytes += (len(u) * wd.S + (L - (L - 1) // wd.S * wd.S)) * wd.d * 2 * 2
+    Ps = [min(wd.C, (int(L) - 1) // wd.S) for L in x["seq_lens"]]
+    scan_bytes = sum(P * wd.Hlmk * (wd.d + 1) * 4 for P in Ps)
+    total_bytes = scan_bytes + kv_bytes + 2 * 2 * wd.B * wd.Hq * wd.d
+    step_gbs = total_bytes / (us * 1e-6) / 1e9
+    scan_gbs = scan_bytes / (stages["scan"] * 1e-3) / 1e9
+    log("decode: %.1f us/step (stages ms %s)" % (us, stages))
+    dense_kv = sum(int(L) for L in x["seq_lens"]) * wd.Hkv * wd.d * 2 * 2
+    return {
+        "workload": wd.name, "B": wd.B, "Hq": wd.Hq, "Hkv": wd.Hkv, "d": wd.d, "ctx": int(max(x["seq_lens"])),
+        "K": wd.K, "us_per_step": us, "stages_us": {k_: v_ * 1e3 for k_, v_ in stages.items()},
+        "one_off_compress_ms": comp_ms,
+        "roofline": {"bound": "hbm", "achieved": scan_gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                     "frac": scan_gbs / PEAK_HBM_GBS, "kernel": "decode_scan", "traffic": None},
+        "step_hbm": {"algorithmic_bytes": total_bytes, "achieved_GBs": step_gbs, "frac": step_gbs / PEAK_HBM_GBS,
+                     "kv_union_bytes": kv_bytes, "kprime_bytes": scan_bytes},
+        "dense_kv_bytes": dense_kv, "dense_us_at_hbm_peak": dense_kv / (PEAK_HBM_GBS * 1e9) * 1e6,
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--workload", default="prefill_256k_qcal")
+    ap.add_argument("--decode-workload", default="decode_512k")
+    ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--no-dense", action="store_true")
+    ap.add_argument("--no-parity", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: the HiLS path here runs on a single MI355X "
+              "(no sharding or collectives); run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    import synth
+    from long_context_chunk_amd import hils
+    hils.load()
+    assert torch.cuda.is_available()
+    w = synth.WORKLOADS[args.workload]
+    seed = synth.BASE_SEED + 5
+    res = run_prefill(w, args.steps, args.warmup, seed)
+    cnt = prefill_counts(w)
+    roof = stage_roofline(w, cnt, res["stages"])
+    dom = max(("compress", "score_topk", "chunk_attend"), key=lambda s_: res["stages"][s_])
+    total_flops = cnt["compress_flops"] + cnt["qcal_flops"] + cnt["score_flops"] + cnt["intra_flops"]
+    line = {
+        "metric": METRIC,
+        "value": w.B * w.N / (res["ms"] * 1e-3),
+        "unit": "tokens/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": res["ms"],
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic (seeded counter-based generator; planted-direction needle chunks and queries)",
+        "config": {"workload": w.name, "B": w.B, "Hq": w.Hq, "Hkv": w.Hkv, "d": w.d, "seq_len": w.N, "S": w.S,
+                   "K": w.K, "qcal_rank": w.qcal_rank, "compression": "in the same call"},
+        "roofline": dict(roof[dom], kernel=dom, traffic=None),
+        "stages_ms": res["stages"],
+        "stage_rooflines": roof,
+        "algorithmic_tflops_per_step": total_flops / 1e12,
+        "mfma_frac_whole_step": total_flops / (res["ms"] * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
+    }
+    if not args.no_parity:
+        t0 = time.time()
+        line["sampled_parity"] = sampled_parity(w, res)
+        log("sampled parity %s (%.1fs)" % (line["sampled_parity"], time.time() - t0))
+    if not args.no_dense:
+        try:
+            dn = dense_baseline(res, w)
+            dn["hils_speedup"] = dn["ms"] / res["ms"]
+            line["dense"] = dn
+            log("dense SDPA: %.1f ms" % dn["ms"])
+        except Exception as ex:  # report, never hide
+            line["dense"] = {"error": repr(ex)}
+    if not args.no_cpu:
+        t0 = time.time()
+        line["cpu_baseline"] = cpu_baseline(w, res)
+        log("cpu baseline done in %.1fs" % (time.time() - t0))
+    else:
+        line["cpu_baseline"] = None
+    res.clear()
+    torch.cuda.empty_cache()
+    if not args.no_decode:
+        wd = synth.WORKLOADS[args.decode_workload]
+        line["decode"] = run_decode(wd, max(args.steps, 20), args.warmup, seed + 1)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -21,7 +21,8 @@
  *     `dims`, which is a host pointer.  The library allocates no memory and keeps
  *     no pointer after a call returns.
  *   - `stream` is a hipStream_t passed as void* (NULL = the default stream).  All
- *     work is enqueued asynchronously on it; no call synchronises.
+ *     work is enqueued asynchronously on it; no call synchronises (except the
+ *     measurement variant hils_attn_prefill_timed).
  *   - Every call validates all arguments before enqueuing anything; on a non-OK
  *     return nothing was enqueued (except HILS_E_HIP, returned when a launch
  *     failed).  hils_last_error() then holds a message (thread-local).
@@ -118,6 +119,19 @@ int hils_attn_prefill(const hils_dims_t* dims, const void* q, const void* k, con
                       float* sel_score_out, void* o, void* ws, size_t ws_bytes, void* stream);
 
 /*
+ * hils_attn_prefill for measurement: the same work, plus the GPU time of each
+ * stage in milliseconds, taken with HIP events on `stream`, in stage_ms[5]
+ * (a HOST array): [0] landmark compression (0 if lmk_q == NULL), [1] scoring and
+ * top-K, [2] bucketing of (query, chunk) pairs, [3] intra-chunk attention of
+ * the selected chunks, [4] own-chunk attention and fusion.  Unlike every other
+ * call it synchronises with the stream before returning.
+ */
+int hils_attn_prefill_timed(const hils_dims_t* dims, const void* q, const void* k, const void* v, const void* lmk_q,
+                            float* kc, float* bc, const void* qcal_D, const void* qcal_U, int32_t* sel_idx_out,
+                            float* sel_score_out, void* o, void* ws, size_t ws_bytes, void* stream,
+                            float* stage_ms);
+
+/*
  * One decode step: for every sequence b and query head h, the single query
  * q[b,h] at position seq_lens[b]-1 runs steps (2)-(4) against the KV cache
  * (k_cache/v_cache [B,Hkv,N,d], N = capacity).  seq_lens [B] int32 lives on the
@@ -131,6 +145,17 @@ int hils_attn_decode(const hils_dims_t* dims, const void* q, const void* k_cache
                      const int32_t* seq_lens, const float* kc, const float* bc, const void* qcal_D,
                      const void* qcal_U, int32_t* sel_idx_out, void* o, void* ws, size_t ws_bytes,
                      void* stream);
+
+/*
+ * hils_attn_decode for measurement: the same work, plus the GPU time of each
+ * stage in milliseconds (HIP events on `stream`) in stage_ms[4] (a HOST array):
+ * [0] chunk scoring scan, [1] top-K, [2] chunk gather-attention, [3] fusion.
+ * Synchronises with the stream before returning.
+ */
+int hils_attn_decode_timed(const hils_dims_t* dims, const void* q, const void* k_cache, const void* v_cache,
+                           const int32_t* seq_lens, const float* kc, const float* bc, const void* qcal_D,
+                           const void* qcal_U, int32_t* sel_idx_out, void* o, void* ws, size_t ws_bytes,
+                           void* stream, float* stage_ms);
 
 /* Message of the last non-OK return on this thread ("" if none). */
 const char* hils_last_error(void);

@@ -141,9 +141,14 @@ int hils_chunk_score_topk(const hils_dims_t* dims, const void* q, const void* qc
   return HILS_OK;
 }
 
-int hils_attn_prefill(const hils_dims_t* dims, const void* q, const void* k, const void* v, const void* lmk_q,
-                      float* kc, float* bc, const void* qcal_D, const void* qcal_U, int32_t* sel_idx_out,
-                      float* sel_score_out, void* o, void* ws, size_t ws_bytes, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// hils_attn_prefill with optional stage timing (stage_ms: 5 host floats, or NULL)
+int run_prefill(const hils_dims_t* dims, const void* q, const void* k, const void* v, const void* lmk_q, float* kc,
+                float* bc, const void* qcal_D, const void* qcal_U, int32_t* sel_idx_out, float* sel_score_out, void* o,
+                void* ws, size_t ws_bytes, void* stream, float* stage_ms) {
   hils::Geom g;
   int rc = check_dims(dims, g);
   if (rc) return rc;
@@ -160,37 +165,99 @@ int hils_attn_prefill(const hils_dims_t* dims, const void* q, const void* k, con
   int32_t* sel = sel_idx_out ? sel_idx_out : (int32_t*)(base + w.sel_idx);
   float* scr = sel_score_out ? sel_score_out : (float*)(base + w.sel_score);
   hipStream_t st = (hipStream_t)stream;
-  hipError_t e;
-  if (lmk_q && g.C() > 0) {
-    e = hils::launch_compress(g.io, k, lmk_q, kcp, bcp, g.B, g.Hkv, g.Hl, g.N, g.d, 0, g.C(), st);
-    if (e != hipSuccess) return hip_fail(e, "hils_attn_prefill (compress)");
+  hipEvent_t ev[6] = {};
+  hipError_t e = hipSuccess;
+  if (stage_ms) {
+    for (int i = 0; i < 6 && e == hipSuccess; ++i) e = hipEventCreate(&ev[i]);
+    if (e == hipSuccess) e = hipEventRecord(ev[0], st);
   }
-  e = hils::launch_score_topk(g, q, qcal_D, qcal_U, kcp, bcp, sel, scr, st);
-  if (e != hipSuccess) return hip_fail(e, "hils_attn_prefill (score/top-K)");
-  e = hils::launch_prefill_attend(g, q, k, v, sel, scr, o, base + w.attend, w.total - w.attend, st);
-  if (e != hipSuccess) return hip_fail(e, "hils_attn_prefill (attend)");
+  if (e == hipSuccess && lmk_q && g.C() > 0) {
+    e = hils::launch_compress(g.io, k, lmk_q, kcp, bcp, g.B, g.Hkv, g.Hl, g.N, g.d, 0, g.C(), st);
+  }
+  if (e == hipSuccess && stage_ms) e = hipEventRecord(ev[1], st);
+  if (e == hipSuccess) e = hils::launch_score_topk(g, q, qcal_D, qcal_U, kcp, bcp, sel, scr, st);
+  if (e == hipSuccess && stage_ms) e = hipEventRecord(ev[2], st);
+  if (e == hipSuccess)
+    e = hils::launch_prefill_attend(g, q, k, v, sel, scr, o, base + w.attend, w.total - w.attend, st,
+                                    stage_ms ? ev + 3 : nullptr);
+  if (stage_ms) {
+    if (e == hipSuccess) e = hipEventSynchronize(ev[5]);
+    for (int i = 0; i < 5 && e == hipSuccess; ++i) e = hipEventElapsedTime(&stage_ms[i], ev[i], ev[i + 1]);
+    for (int i = 0; i < 6; ++i)
+      if (ev[i]) hipEventDestroy(ev[i]);
+  }
+  if (e != hipSuccess) return hip_fail(e, "hils_attn_prefill");
   g_err[0] = 0;
   return HILS_OK;
+}
+
+int run_decode(const hils_dims_t* dims, const void* q, const void* k_cache, const void* v_cache,
+               const int32_t* seq_lens, const float* kc, const float* bc, const void* qcal_D, const void* qcal_U,
+               int32_t* sel_idx_out, void* o, void* ws, size_t ws_bytes, void* stream, float* stage_ms) {
+  hils::Geom g;
+  int rc = check_dims(dims, g);
+  if (rc) return rc;
+  if (!q || !k_cache || !v_cache || !seq_lens || !o)
+    return fail(HILS_E_INVAL, "q, k_cache, v_cache, seq_lens and o must be non-NULL");
+  if (g.C() > 0 && (!kc || !bc)) return fail(HILS_E_INVAL, "kc and bc must be non-NULL");
+  if (g.r > 0 && (!qcal_D || !qcal_U)) return fail(HILS_E_INVAL, "qcal_rank > 0 needs qcal_D and qcal_U");
+  const size_t need = hils::decode_workspace_bytes(g);
+  if (!ws && need > 0) return fail(HILS_E_WORKSPACE, "workspace is NULL (%zu bytes needed)", need);
+  if (ws_bytes < need) return fail(HILS_E_WORKSPACE, "workspace too small: %zu < %zu", ws_bytes, need);
+  hipStream_t st = (hipStream_t)stream;
+  hipEvent_t ev[5] = {};
+  hipError_t e = hipSuccess;
+  if (stage_ms)
+    for (int i = 0; i < 5 && e == hipSuccess; ++i) e = hipEventCreate(&ev[i]);
+  if (e == hipSuccess)
+    e = hils::launch_decode(g, q, k_cache, v_cache, seq_lens, kc, bc, qcal_D, qcal_U, sel_idx_out, o, ws, ws_bytes,
+                            st, stage_ms ? ev : nullptr);
+  if (stage_ms) {
+    if (e == hipSuccess) e = hipEventSynchronize(ev[4]);
+    for (int i = 0; i < 4 && e == hipSuccess; ++i) e = hipEventElapsedTime(&stage_ms[i], ev[i], ev[i + 1]);
+    for (int i = 0; i < 5; ++i)
+      if (ev[i]) hipEventDestroy(ev[i]);
+  }
+  if (e != hipSuccess) return hip_fail(e, "hils_attn_decode");
+  g_err[0] = 0;
+  return HILS_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int hils_attn_prefill(const hils_dims_t* dims, const void* q, const void* k, const void* v, const void* lmk_q,
+                      float* kc, float* bc, const void* qcal_D, const void* qcal_U, int32_t* sel_idx_out,
+                      float* sel_score_out, void* o, void* ws, size_t ws_bytes, void* stream) {
+  return run_prefill(dims, q, k, v, lmk_q, kc, bc, qcal_D, qcal_U, sel_idx_out, sel_score_out, o, ws, ws_bytes, stream,
+                     nullptr);
+}
+
+int hils_attn_prefill_timed(const hils_dims_t* dims, const void* q, const void* k, const void* v, const void* lmk_q,
+                            float* kc, float* bc, const void* qcal_D, const void* qcal_U, int32_t* sel_idx_out,
+                            float* sel_score_out, void* o, void* ws, size_t ws_bytes, void* stream,
+                            float* stage_ms) {
+  if (!stage_ms) return fail(HILS_E_INVAL, "stage_ms must be non-NULL");
+  return run_prefill(dims, q, k, v, lmk_q, kc, bc, qcal_D, qcal_U, sel_idx_out, sel_score_out, o, ws, ws_bytes, stream,
+                     stage_ms);
 }
 
 int hils_attn_decode(const hils_dims_t* dims, const void* q, const void* k_cache, const void* v_cache,
                      const int32_t* seq_lens, const float* kc, const float* bc, const void* qcal_D,
                      const void* qcal_U, int32_t* sel_idx_out, void* o, void* ws, size_t ws_bytes,
                      void* stream) {
-  hils::Geom g;
-  int rc = check_dims(dims, g);
-  if (rc) return rc;
-  if (!q || !k_cache || !v_cache || !seq_lens || !kc || !bc || !o)
-    return fail(HILS_E_INVAL, "q, k_cache, v_cache, seq_lens, kc, bc and o must be non-NULL");
-  if (g.r > 0 && (!qcal_D || !qcal_U)) return fail(HILS_E_INVAL, "qcal_rank > 0 needs qcal_D and qcal_U");
-  const size_t need = hils::decode_workspace_bytes(g);
-  if (!ws && need > 0) return fail(HILS_E_WORKSPACE, "workspace is NULL (%zu bytes needed)", need);
-  if (ws_bytes < need) return fail(HILS_E_WORKSPACE, "workspace too small: %zu < %zu", ws_bytes, need);
-  hipError_t e = hils::launch_decode(g, q, k_cache, v_cache, seq_lens, kc, bc, qcal_D, qcal_U, sel_idx_out, o, ws,
-                                     ws_bytes, (hipStream_t)stream);
-  if (e != hipSuccess) return hip_fail(e, "hils_attn_decode");
-  g_err[0] = 0;
-  return HILS_OK;
+  return run_decode(dims, q, k_cache, v_cache, seq_lens, kc, bc, qcal_D, qcal_U, sel_idx_out, o, ws, ws_bytes, stream,
+                    nullptr);
+}
+
+int hils_attn_decode_timed(const hils_dims_t* dims, const void* q, const void* k_cache, const void* v_cache,
+                           const int32_t* seq_lens, const float* kc, const float* bc, const void* qcal_D,
+                           const void* qcal_U, int32_t* sel_idx_out, void* o, void* ws, size_t ws_bytes,
+                           void* stream, float* stage_ms) {
+  if (!stage_ms) return fail(HILS_E_INVAL, "stage_ms must be non-NULL");
+  return run_decode(dims, q, k_cache, v_cache, seq_lens, kc, bc, qcal_D, qcal_U, sel_idx_out, o, ws, ws_bytes, stream,
+                    stage_ms);
 }
 
 }  // extern "C"

@@ -445,7 +445,7 @@ __global__ void __launch_bounds__(256) fuse_own(const IO* __restrict__ q, const 
 // ------------------------------------------------------------------ launcher
 template <typename IO, int D>
 static hipError_t launch_attend_t(const Geom& g, const void* q, const void* k, const void* v, const int32_t* sel,
-                                  const float* scr, void* o, char* ws, hipStream_t st) {
+                                  const float* scr, void* o, char* ws, hipStream_t st, hipEvent_t* ev) {
   const AttendWs w = attend_ws(g);
   uint32_t* counts = (uint32_t*)(ws + w.counts);
   uint32_t* cursor = (uint32_t*)(ws + w.cursor);
@@ -465,6 +465,7 @@ static hipError_t launch_attend_t(const Geom& g, const void* q, const void* k, c
     hipLaunchKernelGGL(bucket_count, dim3(ngrp * spg), dim3(256), 0, st, sel, counts, group_len, spg, C);
     hipLaunchKernelGGL(bucket_scan, dim3(1), dim3(1024), 0, st, counts, boff, toff, nbk);
     hipLaunchKernelGGL(bucket_scatter, dim3(ngrp * spg), dim3(256), 0, st, sel, boff, cursor, pairs, group_len, spg, C);
+    if (ev) hipEventRecord(ev[0], st);
     // tiles <= total pairs / AT_ROWS + number of buckets (host bound, exact count read on the device)
     // rows of query chunk p (64 of them, fewer in the tail) select min(K, p, C) chunks each
     int64_t pairs_total = 0;
@@ -476,23 +477,29 @@ static hipError_t launch_attend_t(const Geom& g, const void* q, const void* k, c
     if (pairs_total > 0)
       hipLaunchKernelGGL((chunk_attend<IO, D>), dim3(grid), dim3(256), 0, st, (const IO*)q, (const IO*)k, (const IO*)v,
                          pairs, boff, toff, partial, g.Hkv, g.N, C, g.K, nbk, grid_items);
+    if (ev) hipEventRecord(ev[1], st);
+  } else if (ev) {
+    hipEventRecord(ev[0], st);
+    hipEventRecord(ev[1], st);
   }
   const int NQC = (g.N + 63) / 64;
   hipLaunchKernelGGL((fuse_own<IO, D>), dim3(g.B * g.Hq * NQC), dim3(256), 0, st, (const IO*)q, (const IO*)k,
                      (const IO*)v, sel, scr, (const void*)partial, (IO*)o, g.Hq, g.Hkv, g.N, g.K, NQC);
+  if (ev) hipEventRecord(ev[2], st);
   return hipGetLastError();
 }
 
 hipError_t launch_prefill_attend(const Geom& g, const void* q, const void* k, const void* v, const int32_t* sel_idx,
-                                 const float* sel_score, void* o, void* ws, size_t ws_bytes, hipStream_t st) {
+                                 const float* sel_score, void* o, void* ws, size_t ws_bytes, hipStream_t st,
+                                 hipEvent_t* ev) {
   if (ws_bytes < attend_workspace_bytes(g)) return hipErrorInvalidValue;
   if (g.C() > MAX_C) return hipErrorNotSupported;
   char* w = (char*)ws;
   if (g.io == 0)
-    return g.d == 64 ? launch_attend_t<float, 64>(g, q, k, v, sel_idx, sel_score, o, w, st)
-                     : launch_attend_t<float, 128>(g, q, k, v, sel_idx, sel_score, o, w, st);
-  return g.d == 64 ? launch_attend_t<bf16_t, 64>(g, q, k, v, sel_idx, sel_score, o, w, st)
-                   : launch_attend_t<bf16_t, 128>(g, q, k, v, sel_idx, sel_score, o, w, st);
+    return g.d == 64 ? launch_attend_t<float, 64>(g, q, k, v, sel_idx, sel_score, o, w, st, ev)
+                     : launch_attend_t<float, 128>(g, q, k, v, sel_idx, sel_score, o, w, st, ev);
+  return g.d == 64 ? launch_attend_t<bf16_t, 64>(g, q, k, v, sel_idx, sel_score, o, w, st, ev)
+                   : launch_attend_t<bf16_t, 128>(g, q, k, v, sel_idx, sel_score, o, w, st, ev);
 }
 
 }  // namespace hils

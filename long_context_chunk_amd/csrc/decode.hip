@@ -301,7 +301,8 @@ __global__ void __launch_bounds__(128) decode_combine(const float* __restrict__ 
 template <typename IO, int D>
 static hipError_t launch_decode_t(const Geom& g, const void* q, const void* kcache, const void* vcache,
                                   const int32_t* seq_lens, const float* kc, const float* bc, const void* Dw,
-                                  const void* Uw, int32_t* sel_user, void* o, char* ws, hipStream_t st) {
+                                  const void* Uw, int32_t* sel_user, void* o, char* ws, hipStream_t st,
+                                  hipEvent_t* ev) {
   const DecodeWs w = decode_ws(g);
   float* scores = (float*)(ws + w.scores);
   int32_t* sel_i = (int32_t*)(ws + w.sel_i);
@@ -311,27 +312,32 @@ static hipError_t launch_decode_t(const Geom& g, const void* q, const void* kcac
   float* sig = (float*)(ws + w.sig);
   const int C = g.C(), BH = g.B * g.Hq;
   const int nsplit = (C + DS_CHUNKS - 1) / DS_CHUNKS;
+  if (ev) hipEventRecord(ev[0], st);
   if (nsplit > 0)
     hipLaunchKernelGGL((decode_scan<IO, D>), dim3(BH * nsplit), dim3(256), 0, st, (const IO*)q, (const IO*)Dw,
                        (const IO*)Uw, kc, bc, seq_lens, scores, g.Hq, C, g.r, nsplit);
+  if (ev) hipEventRecord(ev[1], st);
   hipLaunchKernelGGL(decode_topk<0>, dim3(BH), dim3(256), 0, st, scores, seq_lens, sel_i, sel_s, nsel, sel_user, g.Hq,
                      C, g.K);
+  if (ev) hipEventRecord(ev[2], st);
   hipLaunchKernelGGL((decode_attend<IO, D>), dim3(BH * (g.K + 1)), dim3(256), 0, st, (const IO*)q, (const IO*)kcache,
                      (const IO*)vcache, seq_lens, sel_i, sel_s, nsel, part, sig, g.Hq, g.Hkv, g.N, g.K);
+  if (ev) hipEventRecord(ev[3], st);
   hipLaunchKernelGGL((decode_combine<IO, D>), dim3(BH), dim3(128), 0, st, part, sig, nsel, (IO*)o, g.K);
+  if (ev) hipEventRecord(ev[4], st);
   return hipGetLastError();
 }
 
 hipError_t launch_decode(const Geom& g, const void* q, const void* kcache, const void* vcache, const int32_t* seq_lens,
                          const float* kc, const float* bc, const void* Dw, const void* Uw, int32_t* sel_idx_out,
-                         void* o, void* ws, size_t ws_bytes, hipStream_t st) {
+                         void* o, void* ws, size_t ws_bytes, hipStream_t st, hipEvent_t* ev) {
   if (ws_bytes < decode_workspace_bytes(g)) return hipErrorInvalidValue;
   char* w = (char*)ws;
   if (g.io == 0)
-    return g.d == 64 ? launch_decode_t<float, 64>(g, q, kcache, vcache, seq_lens, kc, bc, Dw, Uw, sel_idx_out, o, w, st)
-                     : launch_decode_t<float, 128>(g, q, kcache, vcache, seq_lens, kc, bc, Dw, Uw, sel_idx_out, o, w, st);
-  return g.d == 64 ? launch_decode_t<bf16_t, 64>(g, q, kcache, vcache, seq_lens, kc, bc, Dw, Uw, sel_idx_out, o, w, st)
-                   : launch_decode_t<bf16_t, 128>(g, q, kcache, vcache, seq_lens, kc, bc, Dw, Uw, sel_idx_out, o, w, st);
+    return g.d == 64 ? launch_decode_t<float, 64>(g, q, kcache, vcache, seq_lens, kc, bc, Dw, Uw, sel_idx_out, o, w, st, ev)
+                     : launch_decode_t<float, 128>(g, q, kcache, vcache, seq_lens, kc, bc, Dw, Uw, sel_idx_out, o, w, st, ev);
+  return g.d == 64 ? launch_decode_t<bf16_t, 64>(g, q, kcache, vcache, seq_lens, kc, bc, Dw, Uw, sel_idx_out, o, w, st, ev)
+                   : launch_decode_t<bf16_t, 128>(g, q, kcache, vcache, seq_lens, kc, bc, Dw, Uw, sel_idx_out, o, w, st, ev);
 }
 
 }  // namespace hils

@@ -22,13 +22,16 @@ hipError_t launch_score_topk(const Geom& g, const void* q, const void* D, const 
 
 // Intra-chunk attention and fusion for prefill, given the selection.
 size_t attend_workspace_bytes(const Geom& g);
+// ev (nullable): three events recorded after bucketing, chunk attention and fusion.
 hipError_t launch_prefill_attend(const Geom& g, const void* q, const void* k, const void* v, const int32_t* sel_idx,
-                                 const float* sel_score, void* o, void* ws, size_t ws_bytes, hipStream_t st);
+                                 const float* sel_score, void* o, void* ws, size_t ws_bytes, hipStream_t st,
+                                 hipEvent_t* ev = nullptr);
 
 // One decode step.
 size_t decode_workspace_bytes(const Geom& g);
+// ev (nullable): five events recorded before the scan and after each of its four kernels.
 hipError_t launch_decode(const Geom& g, const void* q, const void* kcache, const void* vcache, const int32_t* seq_lens,
                          const float* kc, const float* bc, const void* D, const void* U, int32_t* sel_idx_out,
-                         void* o, void* ws, size_t ws_bytes, hipStream_t st);
+                         void* o, void* ws, size_t ws_bytes, hipStream_t st, hipEvent_t* ev = nullptr);
 
 }  // namespace hils

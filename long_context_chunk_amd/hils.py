@@ -20,7 +20,9 @@ OP_COMPRESS, OP_SCORE_TOPK, OP_PREFILL, OP_DECODE = 0, 1, 2, 3
 OK, E_INVAL, E_UNSUPPORTED, E_WORKSPACE, E_HIP = 0, -1, -2, -3, -4
 
 SYMBOLS = ("hils_workspace_bytes", "hils_landmark_compress", "hils_chunk_score_topk", "hils_attn_prefill",
-           "hils_attn_decode", "hils_last_error")
+           "hils_attn_prefill_timed", "hils_attn_decode", "hils_attn_decode_timed", "hils_last_error")
+STAGES = ("compress", "score_topk", "bucket", "chunk_attend", "own_fuse")
+DECODE_STAGES = ("scan", "topk", "attend", "combine")
 
 
 class Dims(ctypes.Structure):
@@ -53,8 +55,13 @@ def load():
         lib.hils_landmark_compress.argtypes = [dp, vp, vp, i32, i32, vp, vp, vp]
         lib.hils_chunk_score_topk.argtypes = [dp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
         lib.hils_attn_prefill.argtypes = [dp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+        lib.hils_attn_prefill_timed.argtypes = [dp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp,
+                                                ctypes.POINTER(ctypes.c_float)]
         lib.hils_attn_decode.argtypes = [dp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
-        for f in ("hils_landmark_compress", "hils_chunk_score_topk", "hils_attn_prefill", "hils_attn_decode"):
+        lib.hils_attn_decode_timed.argtypes = [dp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp,
+                                               ctypes.POINTER(ctypes.c_float)]
+        for f in ("hils_landmark_compress", "hils_chunk_score_topk", "hils_attn_prefill", "hils_attn_prefill_timed",
+                  "hils_attn_decode", "hils_attn_decode_timed"):
             getattr(lib, f).restype = ctypes.c_int
         lib.hils_last_error.argtypes = []
         lib.hils_last_error.restype = ctypes.c_char_p
@@ -139,7 +146,8 @@ def chunk_score_topk(dm: Dims, q, kc, bc, sel_idx, sel_score, qcal_D=None, qcal_
 
 
 def attn_prefill(dm: Dims, q, k, v, o, ws, lmk_q=None, kc=None, bc=None, qcal_D=None, qcal_U=None, sel_idx=None,
-                 sel_score=None):
+                 sel_score=None, timed=False):
+    """hils_attn_prefill (timed=True: hils_attn_prefill_timed, returns {stage: ms})."""
     C = dm.N // dm.S
     dt = torch.float32 if dm.io == F32 else torch.bfloat16
     _req(q, "q", (dm.B, dm.Hq, dm.N, dm.d), dt)
@@ -159,11 +167,18 @@ def attn_prefill(dm: Dims, q, k, v, o, ws, lmk_q=None, kc=None, bc=None, qcal_D=
         _req(sel_idx, "sel_idx", (dm.B, dm.Hq, dm.N, dm.K), torch.int32)
     if sel_score is not None:
         _req(sel_score, "sel_score", (dm.B, dm.Hq, dm.N, dm.K), torch.float32)
-    _check(load().hils_attn_prefill(ctypes.byref(dm), _p(q), _p(k), _p(v), _p(lmk_q), _p(kc), _p(bc), _p(qcal_D),
-                                    _p(qcal_U), _p(sel_idx), _p(sel_score), _p(o), _p(ws), ws.numel(), _stream()))
+    args = (ctypes.byref(dm), _p(q), _p(k), _p(v), _p(lmk_q), _p(kc), _p(bc), _p(qcal_D), _p(qcal_U), _p(sel_idx),
+            _p(sel_score), _p(o), _p(ws), ws.numel(), _stream())
+    if timed:
+        ms = (ctypes.c_float * 5)()
+        _check(load().hils_attn_prefill_timed(*args, ms))
+        return dict(zip(STAGES, [float(x) for x in ms]))
+    _check(load().hils_attn_prefill(*args))
 
 
-def attn_decode(dm: Dims, q, k_cache, v_cache, seq_lens, kc, bc, o, ws, qcal_D=None, qcal_U=None, sel_idx=None):
+def attn_decode(dm: Dims, q, k_cache, v_cache, seq_lens, kc, bc, o, ws, qcal_D=None, qcal_U=None, sel_idx=None,
+                timed=False):
+    """hils_attn_decode (timed=True: hils_attn_decode_timed, returns {stage: ms})."""
     C = dm.N // dm.S
     dt = torch.float32 if dm.io == F32 else torch.bfloat16
     _req(q, "q", (dm.B, dm.Hq, dm.d), dt)
@@ -179,5 +194,10 @@ def attn_decode(dm: Dims, q, k_cache, v_cache, seq_lens, kc, bc, o, ws, qcal_D=N
         _req(qcal_U, "qcal_U", (dm.Hq, dm.d, dm.qcal_rank), dt)
     if sel_idx is not None:
         _req(sel_idx, "sel_idx", (dm.B, dm.Hq, dm.K), torch.int32)
-    _check(load().hils_attn_decode(ctypes.byref(dm), _p(q), _p(k_cache), _p(v_cache), _p(seq_lens), _p(kc), _p(bc),
-                                   _p(qcal_D), _p(qcal_U), _p(sel_idx), _p(o), _p(ws), ws.numel(), _stream()))
+    args = (ctypes.byref(dm), _p(q), _p(k_cache), _p(v_cache), _p(seq_lens), _p(kc), _p(bc), _p(qcal_D), _p(qcal_U),
+            _p(sel_idx), _p(o), _p(ws), ws.numel(), _stream())
+    if timed:
+        ms = (ctypes.c_float * 4)()
+        _check(load().hils_attn_decode_timed(*args, ms))
+        return dict(zip(DECODE_STAGES, [float(x) for x in ms]))
+    _check(load().hils_attn_decode(*args))
