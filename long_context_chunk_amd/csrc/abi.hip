@@ -98,6 +98,10 @@ size_t hils_workspace_bytes(const hils_dims_t* dims, int op) {
       if (check_prefill(g) != HILS_OK) return (size_t)-1;
       return prefill_ws(g).total;
     case HILS_OP_DECODE:
+      if (g.C() > 16384) {
+        fail(HILS_E_UNSUPPORTED, "decode needs N/S <= 16384 (N=%d)", g.N);
+        return (size_t)-1;
+      }
       return hils::decode_workspace_bytes(g);
     default:
       fail(HILS_E_INVAL, "unknown op %d", op);
@@ -200,6 +204,7 @@ int run_decode(const hils_dims_t* dims, const void* q, const void* k_cache, cons
   if (!q || !k_cache || !v_cache || !seq_lens || !o)
     return fail(HILS_E_INVAL, "q, k_cache, v_cache, seq_lens and o must be non-NULL");
   if (g.C() > 0 && (!kc || !bc)) return fail(HILS_E_INVAL, "kc and bc must be non-NULL");
+  if (g.C() > 16384) return fail(HILS_E_UNSUPPORTED, "decode needs N/S <= 16384 (N=%d)", g.N);
   if (g.r > 0 && (!qcal_D || !qcal_U)) return fail(HILS_E_INVAL, "qcal_rank > 0 needs qcal_D and qcal_U");
   const size_t need = hils::decode_workspace_bytes(g);
   if (!ws && need > 0) return fail(HILS_E_WORKSPACE, "workspace is NULL (%zu bytes needed)", need);

@@ -166,33 +166,41 @@ struct KVTile {
   uint16_t vt[NT][D * LDV];
 };
 
+// Coalesced staging: each thread moves 8 consecutive elements of a key row and a value row.
 template <typename IO, int D, int NT>
 HILS_DEV void stage_kv(KVTile<IO, D, NT>& tile, const IO* __restrict__ k, const IO* __restrict__ v, int64_t row0,
-                       int nvalid) {
+                       int nvalid, int tid, int nthreads) {
   constexpr int LDK = KVTile<IO, D, NT>::LDK, LDV = KVTile<IO, D, NT>::LDV;
-  for (int i = threadIdx.x * 4; i < 64 * D; i += 256 * 4) {
+  for (int i = tid * 8; i < 64 * D; i += nthreads * 8) {
     const int key = i / D, e = i % D;
-    float kx[4], vx[4];
-    const bool ok = key < nvalid;
+    float kx[8], vx[8];
+    if (key < nvalid) {
+      const int64_t off = (row0 + key) * D + e;
+      io_traits<IO>::load4(k, off, *reinterpret_cast<float(*)[4]>(kx));
+      io_traits<IO>::load4(k, off + 4, *reinterpret_cast<float(*)[4]>(kx + 4));
+      io_traits<IO>::load4(v, off, *reinterpret_cast<float(*)[4]>(vx));
+      io_traits<IO>::load4(v, off + 4, *reinterpret_cast<float(*)[4]>(vx + 4));
+    } else {
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      kx[u] = ok ? io_traits<IO>::load(k, (row0 + key) * D + e + u) : 0.f;
-      vx[u] = ok ? io_traits<IO>::load(v, (row0 + key) * D + e + u) : 0.f;
+      for (int u = 0; u < 8; ++u) kx[u] = vx[u] = 0.f;
     }
-    uint16_t ks[4][NT], vs[4][NT];
+    uint16_t ks[8][NT], vs[8][NT];
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
+    for (int u = 0; u < 8; ++u) {
       split_bf16<NT>(kx[u], ks[u]);
       split_bf16<NT>(vx[u], vs[u]);
     }
 #pragma unroll
     for (int j = 0; j < NT; ++j) {
-      u32x2_t pk;
-      pk.x = (uint32_t)ks[0][j] | ((uint32_t)ks[1][j] << 16);
-      pk.y = (uint32_t)ks[2][j] | ((uint32_t)ks[3][j] << 16);
-      *reinterpret_cast<u32x2_t*>(&tile.k[j][key * LDK + e]) = pk;
 #pragma unroll
-      for (int u = 0; u < 4; ++u) tile.vt[j][(e + u) * LDV + key] = vs[u][j];
+      for (int h = 0; h < 2; ++h) {
+        u32x2_t pk;
+        pk.x = (uint32_t)ks[4 * h][j] | ((uint32_t)ks[4 * h + 1][j] << 16);
+        pk.y = (uint32_t)ks[4 * h + 2][j] | ((uint32_t)ks[4 * h + 3][j] << 16);
+        *reinterpret_cast<u32x2_t*>(&tile.k[j][key * LDK + e + 4 * h]) = pk;
+      }
+#pragma unroll
+      for (int u = 0; u < 8; ++u) tile.vt[j][(e + u) * LDV + key] = vs[u][j];
     }
   }
 }
@@ -244,7 +252,7 @@ HILS_DEV void wave_chunk_attention(const KVTile<IO, D, NT>& tile, const bf16x8_t
   for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
     for (int rr = 0; rr < 16; ++rr) {
-      const float p = (m == -INFINITY) ? 0.f : expf(s[tt][rr] - m);
+      const float p = (m == -INFINITY) ? 0.f : __expf(s[tt][rr] - m);
       s[tt][rr] = p;
       l += p;
     }
@@ -282,18 +290,25 @@ HILS_DEV void wave_chunk_attention(const KVTile<IO, D, NT>& tile, const bf16x8_t
   l_out = l;
 }
 
-// Loads query row `qrow_off` (element offset of the row) as NT-term B operands.
+// Loads query row `qrow_off` (element offset of the row) from global memory as NT-term B operands.
 template <typename IO, int D, int NT>
 HILS_DEV void load_q_operand(const IO* __restrict__ q, int64_t qrow_off, bool ok, bf16x8_t (&qb)[NT][D / 16]) {
   const int hf = (threadIdx.x & 63) >> 5;
 #pragma unroll
   for (int ks = 0; ks < D / 16; ++ks) {
+    float x[8];
+    if (ok) {
+      io_traits<IO>::load4(q, qrow_off + kperm(ks, hf, 0), *reinterpret_cast<float(*)[4]>(x));
+      io_traits<IO>::load4(q, qrow_off + kperm(ks, hf, 4), *reinterpret_cast<float(*)[4]>(x + 4));
+    } else {
+#pragma unroll
+      for (int m = 0; m < 8; ++m) x[m] = 0.f;
+    }
     uint16_t t[NT][8];
 #pragma unroll
     for (int m = 0; m < 8; ++m) {
-      const float x = ok ? io_traits<IO>::load(q, qrow_off + kperm(ks, hf, m)) : 0.f;
       uint16_t s[NT];
-      split_bf16<NT>(x, s);
+      split_bf16<NT>(x[m], s);
 #pragma unroll
       for (int j = 0; j < NT; ++j) t[j][m] = s[j];
     }
@@ -302,27 +317,40 @@ HILS_DEV void load_q_operand(const IO* __restrict__ q, int64_t qrow_off, bool ok
   }
 }
 
+// bf16 query row already staged in LDS (row stride LDQ elements) as the B operand.
+template <int D>
+HILS_DEV void lds_q_operand(const uint16_t* rowp, bf16x8_t (&qb)[1][D / 16]) {
+  const int hf = (threadIdx.x & 63) >> 5;
+#pragma unroll
+  for (int ks = 0; ks < D / 16; ++ks) qb[0][ks] = lds_kop(rowp, ks, hf);
+}
+
 template <typename IO>
 struct partial_t {
   using type = uint16_t;  // fp16 bits
-  static constexpr int bytes = 2;
 };
 template <>
 struct partial_t<float> {
   using type = float;
-  static constexpr int bytes = 4;
 };
 
 // ------------------------------------------------------------- chunk_attend
+// bf16 I/O: gathered query rows and the per-pair outputs go through LDS so that
+// global loads and stores move whole rows (16 bytes per lane, rows contiguous).
 template <typename IO, int D>
-__global__ void __launch_bounds__(256) chunk_attend(const IO* __restrict__ q, const IO* __restrict__ k,
-                                                    const IO* __restrict__ v, const uint32_t* __restrict__ pairs,
-                                                    const uint32_t* __restrict__ boff, const uint32_t* __restrict__ toff,
-                                                    void* __restrict__ partial_v, int Hkv, int N, int C, int K,
-                                                    int nbk, int grid_items) {
+__global__ void __launch_bounds__(256, 2) chunk_attend(const IO* __restrict__ q, const IO* __restrict__ k,
+                                                       const IO* __restrict__ v, const uint32_t* __restrict__ pairs,
+                                                       const uint32_t* __restrict__ boff,
+                                                       const uint32_t* __restrict__ toff, void* __restrict__ partial_v,
+                                                       int Hkv, int N, int C, int K, int nbk, int grid_items) {
   constexpr int NT = io_traits<IO>::terms;
+  constexpr bool STAGE = NT == 1;
+  constexpr int LDQ = D + 8;  // bf16 row stride of the staged rows (16-byte aligned rows)
+  constexpr int SEGS = D / 8; // 16-byte segments per bf16 row
   using PT = typename partial_t<IO>::type;
   __shared__ KVTile<IO, D, NT> tile;
+  __shared__ uint16_t qs[STAGE ? AT_ROWS * LDQ : 8];
+  __shared__ uint32_t pid[AT_ROWS];
   const int tix = remap_xcd(blockIdx.x, grid_items);
   const uint32_t ntiles = toff[nbk];
   if (tix >= grid_items || (uint32_t)tix >= ntiles) return;
@@ -338,61 +366,152 @@ __global__ void __launch_bounds__(256) chunk_attend(const IO* __restrict__ q, co
   const uint32_t first = ((uint32_t)tix - toff[bk]) * AT_ROWS;
   const int c = bk % C, kvh = (bk / C) % Hkv, b = bk / (C * Hkv);
   const int64_t row0 = ((int64_t)b * Hkv + kvh) * N + (int64_t)c * 64;
-  stage_kv<IO, D, NT>(tile, k, v, row0, 64);
-
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, hf = lane >> 5;
-  const uint32_t p = first + 32 * w + (lane & 31);
-  const bool ok = p < count;
-  const uint32_t e_pair = ok ? pairs[boff[bk] + p] : 0;
-  const int64_t qrow = e_pair / (uint32_t)K;  // (b*Hq + h)*N + i
-  bf16x8_t qb[NT][D / 16];
-  load_q_operand<IO, D, NT>(q, qrow * D, ok, qb);
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, hf = lane >> 5;
+  if (tid < AT_ROWS) {
+    const uint32_t p = first + tid;
+    pid[tid] = p < count ? pairs[boff[bk] + p] : 0xffffffffu;
+  }
+  stage_kv<IO, D, NT>(tile, k, v, row0, 64, tid, 256);
   __syncthreads();
+  if constexpr (STAGE) {  // gather the query rows, whole rows per 16-byte lane group
+    for (int i = tid; i < AT_ROWS * SEGS; i += 256) {
+      const int r = i / SEGS, sg = i % SEGS;
+      const uint32_t e = pid[r];
+      u32x4_t val = {0u, 0u, 0u, 0u};
+      if (e != 0xffffffffu) val = *reinterpret_cast<const u32x4_t*>(q + (int64_t)(e / (uint32_t)K) * D + 8 * sg);
+      *reinterpret_cast<u32x4_t*>(&qs[r * LDQ + 8 * sg]) = val;
+    }
+    __syncthreads();
+  }
+  const int rl = 32 * w + (lane & 31);
+  const uint32_t e_pair = pid[rl];
+  const bool ok = e_pair != 0xffffffffu;
+  bf16x8_t qb[NT][D / 16];
+  if constexpr (STAGE)
+    lds_q_operand<D>(&qs[rl * LDQ], *reinterpret_cast<bf16x8_t(*)[1][D / 16]>(&qb));
+  else
+    load_q_operand<IO, D, NT>(q, (int64_t)(ok ? e_pair / (uint32_t)K : 0) * D, ok, qb);
   f32x16_t o[D / 32];
   float m, l;
   wave_chunk_attention<IO, D, NT>(tile, qb, 64, o, m, l);
-  if (ok) {
-    const float inv = 1.0f / l;
+  const float inv = 1.0f / l;
+  if constexpr (STAGE) {
+    // normalised output (fp16) into this wave's own staged rows, then whole-row stores
+#pragma unroll
+    for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+      for (int g4 = 0; g4 < 4; ++g4) {
+        const int e = 32 * dt + 8 * g4 + 4 * hf;
+        u32x2_t pk;
+        pk.x = (uint32_t)f32_to_f16(o[dt][4 * g4 + 0] * inv) | ((uint32_t)f32_to_f16(o[dt][4 * g4 + 1] * inv) << 16);
+        pk.y = (uint32_t)f32_to_f16(o[dt][4 * g4 + 2] * inv) | ((uint32_t)f32_to_f16(o[dt][4 * g4 + 3] * inv) << 16);
+        *reinterpret_cast<u32x2_t*>(&qs[rl * LDQ + e]) = pk;
+      }
+    __syncthreads();
+    uint16_t* dst = reinterpret_cast<uint16_t*>(partial_v);
+    for (int i = lane; i < 32 * SEGS; i += 64) {
+      const int r = 32 * w + i / SEGS, sg = i % SEGS;
+      const uint32_t e = pid[r];
+      if (e != 0xffffffffu)
+        *reinterpret_cast<u32x4_t*>(dst + (int64_t)e * D + 8 * sg) = *reinterpret_cast<const u32x4_t*>(&qs[r * LDQ + 8 * sg]);
+    }
+  } else if (ok) {
     PT* dst = reinterpret_cast<PT*>(partial_v) + (int64_t)e_pair * D;
 #pragma unroll
     for (int dt = 0; dt < D / 32; ++dt)
 #pragma unroll
       for (int g4 = 0; g4 < 4; ++g4) {
         const int e = 32 * dt + 8 * g4 + 4 * hf;
-        if constexpr (sizeof(PT) == 2) {
-          u32x2_t pk;
-          pk.x = (uint32_t)f32_to_f16(o[dt][4 * g4 + 0] * inv) | ((uint32_t)f32_to_f16(o[dt][4 * g4 + 1] * inv) << 16);
-          pk.y = (uint32_t)f32_to_f16(o[dt][4 * g4 + 2] * inv) | ((uint32_t)f32_to_f16(o[dt][4 * g4 + 3] * inv) << 16);
-          *reinterpret_cast<u32x2_t*>(dst + e) = pk;
-        } else {
-          *reinterpret_cast<float4*>(dst + e) = make_float4(o[dt][4 * g4] * inv, o[dt][4 * g4 + 1] * inv,
-                                                            o[dt][4 * g4 + 2] * inv, o[dt][4 * g4 + 3] * inv);
-        }
+        *reinterpret_cast<float4*>(dst + e) = make_float4(o[dt][4 * g4] * inv, o[dt][4 * g4 + 1] * inv,
+                                                          o[dt][4 * g4 + 2] * inv, o[dt][4 * g4 + 3] * inv);
       }
   }
 }
 
 // ---------------------------------------------------------------- fuse_own
-// One workgroup per (b, h, query chunk qc): rows qc*64 .. qc*64+63.
+// One workgroup (8 waves) per (b, h, query chunk qc): rows qc*64 .. qc*64+63.
+//   waves 0-1: the own chunk on the MFMA (causal), normalised o_own and LSE_own -> LDS;
+//   waves 2-7: meanwhile, per row, the selected chunks' outputs weighted by
+//              exp(s_c - max s) with 16-byte loads of whole partial rows (registers);
+//   then waves 2-7 combine both parts with the softmax over all chunk scores.
+constexpr int FU_WAVES = 6;                    // fusion waves
+constexpr int FU_ROWS = (64 + FU_WAVES - 1) / FU_WAVES;
+
 template <typename IO, int D>
-__global__ void __launch_bounds__(256) fuse_own(const IO* __restrict__ q, const IO* __restrict__ k,
+__global__ void __launch_bounds__(512) fuse_own(const IO* __restrict__ q, const IO* __restrict__ k,
                                                 const IO* __restrict__ v, const int32_t* __restrict__ sel_idx,
                                                 const float* __restrict__ sel_score, const void* __restrict__ partial_v,
                                                 IO* __restrict__ o, int Hq, int Hkv, int N, int K, int NQC) {
   constexpr int NT = io_traits<IO>::terms;
   using PT = typename partial_t<IO>::type;
+  constexpr int EPL = 16 / sizeof(PT);   // partial elements per 16-byte load
+  constexpr int LPS = D / EPL;           // lanes per partial row
+  constexpr int SPL = 64 / LPS;          // partial rows per wave-wide load
   __shared__ KVTile<IO, D, NT> tile;
-  __shared__ float own[64][D + 1];
+  __shared__ float own[64][D + 4];
   __shared__ float lse[64];
   const int qc = blockIdx.x % NQC, bh = blockIdx.x / NQC;
   const int h = bh % Hq, b = bh / Hq;
   const int kvh = h / (Hq / Hkv);
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, hf = lane >> 5;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, hf = lane >> 5;
   const int key0 = qc * 64;
   const int nkeys = min(64, N - key0);
-  stage_kv<IO, D, NT>(tile, k, v, ((int64_t)b * Hkv + kvh) * N + key0, nkeys);
+  float sacc[FU_ROWS][EPL];
+  float msel[FU_ROWS], zsel[FU_ROWS];
+  if (w < 2) {
+    stage_kv<IO, D, NT>(tile, k, v, ((int64_t)b * Hkv + kvh) * N + key0, nkeys, tid, 128);
+  } else {
+    const int f = w - 2;
+    const int slot = lane / LPS, dpos = (lane % LPS) * EPL;
+#pragma unroll
+    for (int u = 0; u < FU_ROWS; ++u) {
+      const int rl = f + FU_WAVES * u;
+      const int i = key0 + rl;
+#pragma unroll
+      for (int x = 0; x < EPL; ++x) sacc[u][x] = 0.f;
+      msel[u] = -INFINITY;
+      zsel[u] = 0.f;
+      if (rl < 64 && i < N) {
+        const int64_t row = (int64_t)bh * N + i;
+        const float sc = lane < K ? sel_score[row * K + lane] : -INFINITY;
+        const int ci = lane < K ? sel_idx[row * K + lane] : -1;
+        const float sv = ci >= 0 ? sc : -INFINITY;
+        const float M = wave_max(sv);
+        const float wt = ci >= 0 ? __expf(sv - M) : 0.f;
+        zsel[u] = wave_sum(wt);
+        msel[u] = M;
+        const int nsel = __popcll(__ballot(ci >= 0));
+        const PT* src = reinterpret_cast<const PT*>(partial_v) + row * K * D;
+        for (int t0 = 0; t0 < nsel; t0 += SPL) {
+          const int t = t0 + slot;
+          const float wtt = __shfl(wt, t < 64 ? t : 0);
+          if (t < nsel) {
+            const u32x4_t raw = *reinterpret_cast<const u32x4_t*>(src + (int64_t)t * D + dpos);
+            if constexpr (sizeof(PT) == 2) {
+              const uint32_t wd[4] = {raw.x, raw.y, raw.z, raw.w};
+#pragma unroll
+              for (int x = 0; x < 4; ++x) {
+                sacc[u][2 * x] = fmaf(wtt, f16_to_f32((uint16_t)(wd[x] & 0xffffu)), sacc[u][2 * x]);
+                sacc[u][2 * x + 1] = fmaf(wtt, f16_to_f32((uint16_t)(wd[x] >> 16)), sacc[u][2 * x + 1]);
+              }
+            } else {
+              sacc[u][0] = fmaf(wtt, __uint_as_float(raw.x), sacc[u][0]);
+              sacc[u][1] = fmaf(wtt, __uint_as_float(raw.y), sacc[u][1]);
+              sacc[u][2] = fmaf(wtt, __uint_as_float(raw.z), sacc[u][2]);
+              sacc[u][3] = fmaf(wtt, __uint_as_float(raw.w), sacc[u][3]);
+            }
+          }
+        }
+        // sum the slot groups: lanes with the same dpos
+#pragma unroll
+        for (int st = LPS; st < 64; st <<= 1)
+#pragma unroll
+          for (int x = 0; x < EPL; ++x) sacc[u][x] += __shfl_xor(sacc[u][x], st);
+      }
+    }
+  }
   __syncthreads();
-  if (w < 2) {  // own chunk on the MFMA: wave w takes rows 32w .. 32w+31 of the chunk
+  if (w < 2) {  // own chunk: wave w takes rows 32w .. 32w+31 of the chunk
     const int rl = 32 * w + (lane & 31);
     const int i = key0 + rl;
     const bool ok = i < N;
@@ -405,40 +524,40 @@ __global__ void __launch_bounds__(256) fuse_own(const IO* __restrict__ q, const 
 #pragma unroll
     for (int dt = 0; dt < D / 32; ++dt)
 #pragma unroll
-      for (int rr = 0; rr < 16; ++rr) own[rl][32 * dt + acc_row(rr, hf)] = oa[dt][rr] * inv;
+      for (int g4 = 0; g4 < 4; ++g4)
+        *reinterpret_cast<float4*>(&own[rl][32 * dt + 8 * g4 + 4 * hf]) =
+            make_float4(oa[dt][4 * g4] * inv, oa[dt][4 * g4 + 1] * inv, oa[dt][4 * g4 + 2] * inv, oa[dt][4 * g4 + 3] * inv);
     if (hf == 0) lse[rl] = m + logf(l);
   }
   __syncthreads();
-  // fusion: wave w handles rows w, w+4, ...; lane owns head dims lane, lane+64
-  for (int rl = w; rl < 64; rl += 4) {
-    const int i = key0 + rl;
-    if (i >= N) break;
-    const int64_t row = (int64_t)bh * N + i;
-    const float sc = lane < K ? sel_score[row * K + lane] : -INFINITY;
-    const int ci = lane < K ? sel_idx[row * K + lane] : -1;
-    const float lo = lse[rl];
-    const float M = fmaxf(wave_max(ci >= 0 ? sc : -INFINITY), lo);
-    const float wt = ci >= 0 ? expf(sc - M) : 0.f;
-    const float wo = expf(lo - M);
-    const float Z = wave_sum(wt) + wo;
-    const int nsel = __popcll(__ballot(ci >= 0));
-    float acc0 = wo * own[rl][lane];
-    float acc1 = (D > 64) ? wo * own[rl][lane + 64] : 0.f;
-    const PT* src = reinterpret_cast<const PT*>(partial_v) + row * K * D;
-    for (int t = 0; t < nsel; ++t) {
-      const float wtt = __shfl(wt, t);
-      const PT* ps = src + (int64_t)t * D;
-      if constexpr (sizeof(PT) == 2) {
-        acc0 = fmaf(wtt, f16_to_f32(ps[lane]), acc0);
-        if (D > 64) acc1 = fmaf(wtt, f16_to_f32(ps[lane + 64]), acc1);
-      } else {
-        acc0 = fmaf(wtt, ps[lane], acc0);
-        if (D > 64) acc1 = fmaf(wtt, ps[lane + 64], acc1);
+  if (w >= 2 && lane < LPS) {
+    const int f = w - 2;
+    const int dpos = lane * EPL;
+#pragma unroll
+    for (int u = 0; u < FU_ROWS; ++u) {
+      const int rl = f + FU_WAVES * u;
+      const int i = key0 + rl;
+      if (rl < 64 && i < N) {
+        const int64_t row = (int64_t)bh * N + i;
+        const float lo = lse[rl];
+        const float M = fmaxf(msel[u], lo);
+        const float a = __expf(msel[u] - M), bo = __expf(lo - M);
+        const float inv = 1.0f / (zsel[u] * a + bo);
+        float r[EPL];
+#pragma unroll
+        for (int x = 0; x < EPL; ++x) r[x] = (sacc[u][x] * a + own[rl][dpos + x] * bo) * inv;
+        if constexpr (sizeof(IO) == 2) {
+          u32x4_t pk;
+          pk.x = (uint32_t)f32_to_bf16(r[0]) | ((uint32_t)f32_to_bf16(r[1]) << 16);
+          pk.y = (uint32_t)f32_to_bf16(r[2]) | ((uint32_t)f32_to_bf16(r[3]) << 16);
+          pk.z = (uint32_t)f32_to_bf16(r[4]) | ((uint32_t)f32_to_bf16(r[5]) << 16);
+          pk.w = (uint32_t)f32_to_bf16(r[6]) | ((uint32_t)f32_to_bf16(r[7]) << 16);
+          *reinterpret_cast<u32x4_t*>(o + row * D + dpos) = pk;
+        } else {
+          *reinterpret_cast<float4*>(reinterpret_cast<float*>(o) + row * D + dpos) = make_float4(r[0], r[1], r[2], r[3]);
+        }
       }
     }
-    const float inv = 1.0f / Z;
-    io_traits<IO>::store(o, row * D + lane, acc0 * inv);
-    if (D > 64) io_traits<IO>::store(o, row * D + lane + 64, acc1 * inv);
   }
 }
 
@@ -457,7 +576,9 @@ static hipError_t launch_attend_t(const Geom& g, const void* q, const void* k, c
   const int nbk = g.B * g.Hkv * C;
   // zero counts and cursors (contiguous) with a kernel: no memset nodes in captured streams
   const int64_t nz = (int64_t)(w.boff - w.counts) / 4;
-  hipLaunchKernelGGL(zero_u32, dim3((unsigned)std::min<int64_t>((nz + 255) / 256, 4096)), dim3(256), 0, st, counts, nz);
+  if (nz > 0)
+    hipLaunchKernelGGL(zero_u32, dim3((unsigned)std::min<int64_t>((nz + 255) / 256, 4096)), dim3(256), 0, st, counts,
+                       nz);
   if (nbk > 0) {
     const int64_t group_len = (int64_t)g.G() * g.N * g.K;
     const int spg = (int)((group_len + HIST_SLICE - 1) / HIST_SLICE);
@@ -483,7 +604,7 @@ static hipError_t launch_attend_t(const Geom& g, const void* q, const void* k, c
     hipEventRecord(ev[1], st);
   }
   const int NQC = (g.N + 63) / 64;
-  hipLaunchKernelGGL((fuse_own<IO, D>), dim3(g.B * g.Hq * NQC), dim3(256), 0, st, (const IO*)q, (const IO*)k,
+  hipLaunchKernelGGL((fuse_own<IO, D>), dim3(g.B * g.Hq * NQC), dim3(512), 0, st, (const IO*)q, (const IO*)k,
                      (const IO*)v, sel, scr, (const void*)partial, (IO*)o, g.Hq, g.Hkv, g.N, g.K, NQC);
   if (ev) hipEventRecord(ev[2], st);
   return hipGetLastError();

@@ -113,45 +113,65 @@ __global__ void __launch_bounds__(256) decode_scan(const IO* __restrict__ q, con
   }
 }
 
-// exact top-K of the P scores of one (b, h); output in rank order
-template <int DUMMY>
+// exact top-K of the P scores of one (b, h); output in rank order.  The scores
+// are staged in LDS once; four 8-bit radix passes on the ordered score bits find
+// the K-th best value, then ties at that value are taken by ascending chunk id.
+constexpr int TK_MAXC = 16384;  // largest chunk count decode_topk stages in LDS
+
 __global__ void __launch_bounds__(256) decode_topk(const float* __restrict__ scores, const int32_t* __restrict__ seq_lens,
                                                    int32_t* __restrict__ sel_i, float* __restrict__ sel_s,
                                                    int32_t* __restrict__ nsel_out, int32_t* __restrict__ sel_user,
                                                    int Hq, int C, int K) {
+  __shared__ uint32_t ov[TK_MAXC];
   __shared__ uint32_t hist[256];
   __shared__ uint32_t sh_prefix, sh_need;
   __shared__ uint32_t cnt_gt[256], cnt_eq[256];
   __shared__ uint64_t picked[32];
   const int bh = blockIdx.x, b = bh / Hq;
-  const int t = threadIdx.x;
+  const int t = threadIdx.x, lane = t & 63, w = t >> 6;
   const int L = seq_lens[b];
   const int P = min(C, (L - 1) / 64);
   const int n = min(K, P);
   const float* sb = scores + (int64_t)bh * C;
+  for (int c = t; c < P; c += 256) ov[c] = order_f32(sb[c]);
   const int per = (P + 255) / 256;
   const int beg = min(P, t * per), end = min(P, beg + per);
   uint32_t prefix = 0, mask = 0;
   uint32_t need = (uint32_t)n;
+  __syncthreads();
   if (n > 0) {
     for (int pass = 0; pass < 4; ++pass) {
       const int shift = 24 - 8 * pass;
       hist[t] = 0;
       __syncthreads();
-      for (int c = beg; c < end; ++c) {
-        const uint32_t o = order_f32(sb[c]);
+      for (int c = t; c < P; c += 256) {
+        const uint32_t o = ov[c];
         if ((o & mask) == prefix) atomicAdd(&hist[(o >> shift) & 255u], 1u);
       }
       __syncthreads();
-      if (t == 0) {
-        uint32_t cum = 0;
-        int dg = 255;
-        for (; dg > 0; --dg) {
-          if (cum + hist[dg] >= need) break;
-          cum += hist[dg];
+      if (w == 0) {
+        // lane owns digits 4*lane .. 4*lane+3; suffix sums from the top digit down
+        const uint32_t h0 = hist[4 * lane], h1 = hist[4 * lane + 1], h2 = hist[4 * lane + 2], h3 = hist[4 * lane + 3];
+        const uint32_t mine = h0 + h1 + h2 + h3;
+        // inclusive suffix scan over lanes of `mine`; `above` = count of digits > 4*lane+3
+        uint32_t suf = mine;
+        for (int o = 1; o < 64; o <<= 1) {
+          const uint32_t x = __shfl_down(suf, o);
+          if (lane + o < 64) suf += x;
         }
-        sh_prefix = prefix | ((uint32_t)dg << shift);
-        sh_need = need - cum;
+        const uint32_t above = suf - mine;
+        // the digit d with (count > d) < need <= (count >= d)
+        const uint32_t c3 = above + h3, c2 = c3 + h2, c1 = c2 + h1, c0 = c1 + h0;
+        int dg = -1;
+        uint32_t cum = 0;
+        if (above < need && c3 >= need) { dg = 4 * lane + 3; cum = above; }
+        else if (c3 < need && c2 >= need) { dg = 4 * lane + 2; cum = c3; }
+        else if (c2 < need && c1 >= need) { dg = 4 * lane + 1; cum = c2; }
+        else if (c1 < need && c0 >= need) { dg = 4 * lane; cum = c1; }
+        if (dg >= 0) {
+          sh_prefix = prefix | ((uint32_t)dg << shift);
+          sh_need = need - cum;
+        }
       }
       __syncthreads();
       prefix = sh_prefix;
@@ -163,7 +183,7 @@ __global__ void __launch_bounds__(256) decode_topk(const float* __restrict__ sco
   // prefix = ordered bits of the K-th best score; `need` of the elements equal to it are taken (lowest ids)
   uint32_t gt = 0, eq = 0;
   for (int c = beg; c < end; ++c) {
-    const uint32_t o = order_f32(sb[c]);
+    const uint32_t o = ov[c];
     gt += o > prefix;
     eq += o == prefix;
   }
@@ -177,17 +197,16 @@ __global__ void __launch_bounds__(256) decode_topk(const float* __restrict__ sco
     cnt_eq[t] += e;
     __syncthreads();
   }
-  if (n > 0) {
+  if (n > 0 && (gt | eq)) {
     uint32_t pos_gt = cnt_gt[t] - gt;   // exclusive prefix
     uint32_t rank_eq = cnt_eq[t] - eq;
     const uint32_t ngt = cnt_gt[255];
     for (int c = beg; c < end; ++c) {
-      const float s = sb[c];
-      const uint32_t o = order_f32(s);
+      const uint32_t o = ov[c];
       if (o > prefix) {
-        picked[pos_gt++] = make_key(s, c);
+        picked[pos_gt++] = make_key(unorder_f32(o), c);
       } else if (o == prefix) {
-        if (rank_eq < need) picked[ngt + rank_eq] = make_key(s, c);
+        if (rank_eq < need) picked[ngt + rank_eq] = make_key(unorder_f32(o), c);
         ++rank_eq;
       }
     }
@@ -219,10 +238,12 @@ __global__ void __launch_bounds__(256) decode_attend(const IO* __restrict__ q, c
                                                      const int32_t* __restrict__ sel_i, const float* __restrict__ sel_s,
                                                      const int32_t* __restrict__ nsel, float* __restrict__ part,
                                                      float* __restrict__ sig, int Hq, int Hkv, int N, int K) {
+  constexpr int NG = 256 / (D / 4);  // key groups for the value pass (4 head dims per thread)
+  constexpr int KPG = 64 / NG;
   __shared__ float qs[D];
   __shared__ float z[64];
-  __shared__ float red[8];
-  __shared__ float acc2[256 / D][D];
+  __shared__ float ml[2];
+  __shared__ float red[NG][D];
   const int slot = blockIdx.x % (K + 1), bh = blockIdx.x / (K + 1);
   const int b = bh / Hq, h = bh % Hq, kvh = h / (Hq / Hkv);
   const int t = threadIdx.x, lane = t & 63, w = t >> 6;
@@ -240,44 +261,59 @@ __global__ void __launch_bounds__(256) decode_attend(const IO* __restrict__ q, c
   __syncthreads();
   const int64_t row0 = ((int64_t)b * Hkv + kvh) * N + (int64_t)c * 64;
   const float tau = 1.0f / sqrtf((float)D);
-  // logits: 4 threads per key, each a quarter of the head dim
-  {
+  {  // logits: 4 threads per key, each a quarter of the head dim (vector loads)
     const int key = t >> 2, qd = t & 3;
     float s = 0.f;
     if (key < nk) {
-      const IO* kr = kcache + (row0 + key) * D + qd * (D / 4);
-#pragma unroll 8
-      for (int e = 0; e < D / 4; ++e) s = fmaf(qs[qd * (D / 4) + e], io_traits<IO>::load(kr, e), s);
+      const int64_t base = (row0 + key) * D + qd * (D / 4);
+#pragma unroll
+      for (int e = 0; e < D / 4; e += 4) {
+        float x[4];
+        io_traits<IO>::load4(kcache, base + e, x);
+#pragma unroll
+        for (int u = 0; u < 4; ++u) s = fmaf(qs[qd * (D / 4) + e + u], x[u], s);
+      }
     }
     s += __shfl_xor(s, 1);
     s += __shfl_xor(s, 2);
     if (qd == 0) z[key] = key < nk ? s * tau : -INFINITY;
   }
   __syncthreads();
-  float m = -INFINITY;
-  for (int j = 0; j < 64; ++j) m = fmaxf(m, z[j]);
-  float l = 0.f;
-  for (int j = 0; j < 64; ++j) l += (z[j] == -INFINITY) ? 0.f : expf(z[j] - m);
-  // output: thread (e = t % D, key group t / D)
-  {
-    constexpr int NG = 256 / D, KPG = 64 / NG;
-    const int e = t % D, kg = t / D;
-    float a = 0.f;
-    for (int j = kg * KPG; j < (kg + 1) * KPG; ++j)
-      if (j < nk) a = fmaf(expf(z[j] - m), io_traits<IO>::load(vcache, (row0 + j) * D + e), a);
-    acc2[kg][e] = a;
-    __syncthreads();
-    if (t < D) {
-      float o = 0.f;
-#pragma unroll
-      for (int g2 = 0; g2 < NG; ++g2) o += acc2[g2][t];
-      part[((int64_t)bh * (K + 1) + slot) * D + t] = o / l;
+  if (w == 0) {
+    const float zz = z[lane];
+    const float m = wave_max(zz);
+    const float p = zz == -INFINITY ? 0.f : __expf(zz - m);
+    const float l = wave_sum(p);
+    z[lane] = p;
+    if (lane == 0) {
+      ml[0] = m;
+      ml[1] = l;
     }
-    if (t == 0) sig[(int64_t)bh * (K + 1) + slot] = slot == K ? m + logf(l) : sel_s[(int64_t)bh * K + slot];
   }
-  (void)lane;
-  (void)w;
-  (void)red;
+  __syncthreads();
+  {  // values: thread (4 head dims, key group)
+    const int e4 = (t % (D / 4)) * 4, kg = t / (D / 4);
+    float a[4] = {0.f, 0.f, 0.f, 0.f};
+    for (int j = kg * KPG; j < (kg + 1) * KPG; ++j) {
+      if (j < nk) {
+        float x[4];
+        io_traits<IO>::load4(vcache, (row0 + j) * D + e4, x);
+        const float pj = z[j];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) a[u] = fmaf(pj, x[u], a[u]);
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) red[kg][e4 + u] = a[u];
+  }
+  __syncthreads();
+  if (t < D) {
+    float o = 0.f;
+#pragma unroll
+    for (int g2 = 0; g2 < NG; ++g2) o += red[g2][t];
+    part[((int64_t)bh * (K + 1) + slot) * D + t] = o / ml[1];
+  }
+  if (t == 0) sig[(int64_t)bh * (K + 1) + slot] = slot == K ? ml[0] + logf(ml[1]) : sel_s[(int64_t)bh * K + slot];
 }
 
 template <typename IO, int D>
@@ -317,7 +353,7 @@ static hipError_t launch_decode_t(const Geom& g, const void* q, const void* kcac
     hipLaunchKernelGGL((decode_scan<IO, D>), dim3(BH * nsplit), dim3(256), 0, st, (const IO*)q, (const IO*)Dw,
                        (const IO*)Uw, kc, bc, seq_lens, scores, g.Hq, C, g.r, nsplit);
   if (ev) hipEventRecord(ev[1], st);
-  hipLaunchKernelGGL(decode_topk<0>, dim3(BH), dim3(256), 0, st, scores, seq_lens, sel_i, sel_s, nsel, sel_user, g.Hq,
+  hipLaunchKernelGGL(decode_topk, dim3(BH), dim3(256), 0, st, scores, seq_lens, sel_i, sel_s, nsel, sel_user, g.Hq,
                      C, g.K);
   if (ev) hipEventRecord(ev[2], st);
   hipLaunchKernelGGL((decode_attend<IO, D>), dim3(BH * (g.K + 1)), dim3(256), 0, st, (const IO*)q, (const IO*)kcache,

@@ -43,12 +43,27 @@ struct io_traits<float> {
   static constexpr int terms = 3;  // bf16 terms needed to carry an fp32 value exactly
   static __device__ __forceinline__ float load(const float* p, int64_t i) { return p[i]; }
   static __device__ __forceinline__ void store(float* p, int64_t i, float v) { p[i] = v; }
+  // four consecutive elements; i must be a multiple of 4
+  static __device__ __forceinline__ void load4(const float* p, int64_t i, float (&v)[4]) {
+    const float4 x = *reinterpret_cast<const float4*>(p + i);
+    v[0] = x.x;
+    v[1] = x.y;
+    v[2] = x.z;
+    v[3] = x.w;
+  }
 };
 template <>
 struct io_traits<bf16_t> {
   static constexpr int terms = 1;
   static __device__ __forceinline__ float load(const bf16_t* p, int64_t i) { return bf16_to_f32(p[i].bits); }
   static __device__ __forceinline__ void store(bf16_t* p, int64_t i, float v) { p[i].bits = f32_to_bf16(v); }
+  static __device__ __forceinline__ void load4(const bf16_t* p, int64_t i, float (&v)[4]) {
+    const u32x2_t x = *reinterpret_cast<const u32x2_t*>(p + i);
+    v[0] = __uint_as_float(x.x << 16);
+    v[1] = __uint_as_float(x.x & 0xffff0000u);
+    v[2] = __uint_as_float(x.y << 16);
+    v[3] = __uint_as_float(x.y & 0xffff0000u);
+  }
 };
 
 // Split x into NT bf16 terms whose sum carries x to ~8*NT mantissa bits

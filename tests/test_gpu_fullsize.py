@@ -1,0 +1,111 @@
+"""GPU parity at the full workload sizes, in the launch configuration the
+benchmark times: oracle comparison on sampled queries, plus whole-array
+properties of the selection that hold at any size."""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from hils_testutil import TOL, check_selection_and_output, dims_of, gpu_decode, shape_of, upload
+from long_context_chunk_amd import hils
+
+pytestmark = pytest.mark.gpu
+SEED = synth.BASE_SEED + 5   # the benchmark's seed
+
+
+def _say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def _run_prefill(w, x):
+    dm = dims_of(w)
+    q, k, v, lmk = (upload(x[n], w.io) for n in ("q", "k", "v", "lmk"))
+    D = upload(x["D"], w.io) if w.qcal_rank else None
+    U = upload(x["U"], w.io) if w.qcal_rank else None
+    o = torch.empty_like(q)
+    kc = torch.empty((w.B, w.Hlmk, w.C, w.d), dtype=torch.float32, device="cuda")
+    bc = torch.empty((w.B, w.Hlmk, w.C), dtype=torch.float32, device="cuda")
+    sel = torch.empty((w.B, w.Hq, w.N, w.K), dtype=torch.int32, device="cuda")
+    scr = torch.empty((w.B, w.Hq, w.N, w.K), dtype=torch.float32, device="cuda")
+    ws = hils.workspace(dm, hils.OP_PREFILL)
+    hils.attn_prefill(dm, q, k, v, o, ws, lmk_q=lmk, kc=kc, bc=bc, qcal_D=D, qcal_U=U, sel_idx=sel, sel_score=scr)
+    torch.cuda.synchronize()
+    del ws, q, k, v, lmk
+    torch.cuda.empty_cache()
+    return o, sel, scr, kc, bc
+
+
+def _selection_properties(w, sel, scr):
+    """Every row: exactly min(K, P_i) distinct ids, all < P_i, padded with -1/-inf, scores non-increasing."""
+    s = sel.cpu().numpy().reshape(-1, w.N, w.K)
+    sc = scr.cpu().numpy().reshape(-1, w.N, w.K)
+    P = np.minimum(np.arange(w.N) // w.S, w.C)
+    n = np.minimum(P, w.K)
+    valid = s >= 0
+    assert np.array_equal(valid.sum(-1), np.broadcast_to(n, valid.shape[:2]))
+    slot = np.arange(w.K)
+    assert np.array_equal(valid, np.broadcast_to(slot[None, None, :] < n[None, :, None], valid.shape))
+    assert np.all(np.where(valid, s, -1) < P[None, :, None])
+    ss = np.sort(np.where(valid, s, -1 - slot[None, None, :]), axis=-1)
+    assert np.all(np.diff(ss, axis=-1) != 0), "duplicate chunk ids in a row"
+    assert np.all(np.isneginf(sc[~valid]))
+    d = np.diff(np.where(valid, sc, -np.inf), axis=-1)
+    assert np.all((d <= 0) | np.isnan(d)), "scores not in rank order"
+
+
+@pytest.mark.parametrize("name,nrows", [("prefill_8k", None), ("prefill_128k", 3000), ("prefill_256k_qcal", 768)])
+def test_prefill_full_size(name, nrows):
+    w = synth.WORKLOADS[name]
+    _say("full-size prefill", name)
+    x = synth.make_inputs(w, SEED)
+    o, sel, scr, kc, bc = _run_prefill(w, x)
+    _selection_properties(w, sel, scr)
+    assert torch.isfinite(o.float()).all()
+    if nrows is None:
+        rows = [(0, h, i) for h in range(w.Hq) for i in range(w.N)]
+    else:
+        rng = np.random.default_rng(3)
+        rows = sorted({(0, int(rng.integers(w.Hq)), int(rng.integers(w.N))) for _ in range(nrows)})
+        rows += [(0, h, w.N - 1) for h in range(w.Hq)]            # the longest rows
+        rows += [(0, h, i) for h in (0, w.Hq - 1) for i in range(60, 70)]  # first chunk boundary
+    kc_o, bc_o = oracle.compress(shape_of(w), x["k"], x["lmk"])
+    ref = oracle.prefill_rows(shape_of(w), x["q"], x["k"], x["v"], kc_o, bc_o, rows, D=x.get("D"), U=x.get("U"))
+    rr = np.asarray(rows)
+    sel_h = sel[0].cpu().numpy()
+    scr_h = scr[0].cpu().numpy()
+    o_h = o[0].float().cpu().numpy()
+    summ = check_selection_and_output(w, x, kc_o, bc_o, rows, ref, sel_h[rr[:, 1], rr[:, 2]], scr_h[rr[:, 1], rr[:, 2]],
+                                      o_h[rr[:, 1], rr[:, 2]], label=name)
+    _say(name, summ)
+    # compressed keys of every chunk
+    np.testing.assert_allclose(kc.cpu().numpy(), kc_o, rtol=0, atol=1e-5 * max(1.0, np.abs(kc_o).max()))
+    np.testing.assert_allclose(bc.cpu().numpy(), bc_o, rtol=0, atol=1e-5)
+
+
+def test_decode_full_size():
+    w = synth.WORKLOADS["decode_512k"]
+    _say("full-size decode", w.name)
+    x = synth.make_inputs(w, SEED + 1)
+    g = gpu_decode(w, x)
+    kc_g = g["kc"].cpu().numpy()
+    rows_b = [b for b in range(w.B) for h in range(w.Hq)]
+    rows_h = [h for b in range(w.B) for h in range(w.Hq)]
+    pos = [int(x["seq_lens"][b]) - 1 for b in rows_b]
+    s = shape_of(w)
+    kc_o, bc_o = oracle.compress(s, x["k"], x["lmk"])
+    np.testing.assert_allclose(kc_g, kc_o, rtol=0, atol=1e-5 * max(1.0, np.abs(kc_o).max()))
+    ref = oracle.attend(s, rows_b, rows_h, pos, x["q"].reshape(-1, w.d), x["k"], x["v"], kc_o, bc_o)
+
+    class QView:
+        def __getitem__(self, key):
+            b, h, i = key
+            return x["q"][b, h]
+    xx = dict(x)
+    xx["q"] = QView()
+    summ = check_selection_and_output(w, xx, kc_o, bc_o, list(zip(rows_b, rows_h, pos)), ref,
+                                      g["sel_idx"].reshape(-1, w.K), None, g["o"].reshape(-1, w.d), label=w.name)
+    _say(w.name, summ)
