@@ -99,7 +99,8 @@ int hils_landmark_compress(const hils_dims_t* dims, const void* k, const void* l
  * Chunk scoring and top-K, step (2), for all N prefill queries:
  * s_ic = q^_i . kc[c] / sqrt(d) + bc[c] for c < floor(i/S), q^ = q + U_h (D_h q)
  * when qcal_rank > 0 (qcal_D/qcal_U may be NULL only if qcal_rank == 0).
- * Writes sel_idx and sel_score [B,Hq,N,K] (rank order, padded).
+ * Writes sel_idx and sel_score [B,Hq,N,K] (rank order, padded).  Needs a
+ * workspace of hils_workspace_bytes(dims, HILS_OP_SCORE_TOPK) bytes.
  */
 int hils_chunk_score_topk(const hils_dims_t* dims, const void* q, const void* qcal_D, const void* qcal_U,
                           const float* kc, const float* bc, int32_t* sel_idx, float* sel_score, void* ws,

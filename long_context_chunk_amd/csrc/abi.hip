@@ -59,9 +59,9 @@ int check_prefill(const hils::Geom& g) {
   return HILS_OK;
 }
 
-// prefill workspace: [kc | bc | sel_idx | sel_score | attend workspace]
+// prefill workspace: [kc | bc | sel_idx | sel_score | score workspace | attend workspace]
 struct PrefillWs {
-  size_t kc, bc, sel_idx, sel_score, attend, total;
+  size_t kc, bc, sel_idx, sel_score, score, attend, total;
 };
 PrefillWs prefill_ws(const hils::Geom& g) {
   PrefillWs w;
@@ -75,6 +75,8 @@ PrefillWs prefill_ws(const hils::Geom& g) {
   off += align_up(rows * g.K * 4);
   w.sel_score = off;
   off += align_up(rows * g.K * 4);
+  w.score = off;
+  off += align_up(hils::score_workspace_bytes(g));
   w.attend = off;
   off += align_up(hils::attend_workspace_bytes(g));
   w.total = off;
@@ -92,8 +94,9 @@ size_t hils_workspace_bytes(const hils_dims_t* dims, int op) {
   if (check_dims(dims, g) != HILS_OK) return (size_t)-1;
   switch (op) {
     case HILS_OP_COMPRESS:
-    case HILS_OP_SCORE_TOPK:
       return 0;
+    case HILS_OP_SCORE_TOPK:
+      return hils::score_workspace_bytes(g);
     case HILS_OP_PREFILL:
       if (check_prefill(g) != HILS_OK) return (size_t)-1;
       return prefill_ws(g).total;
@@ -131,15 +134,18 @@ int hils_landmark_compress(const hils_dims_t* dims, const void* k, const void* l
 int hils_chunk_score_topk(const hils_dims_t* dims, const void* q, const void* qcal_D, const void* qcal_U,
                           const float* kc, const float* bc, int32_t* sel_idx, float* sel_score, void* ws,
                           size_t ws_bytes, void* stream) {
-  (void)ws;
-  (void)ws_bytes;
   hils::Geom g;
   int rc = check_dims(dims, g);
   if (rc) return rc;
-  if (!q || !kc || !bc || !sel_idx || !sel_score)
-    return fail(HILS_E_INVAL, "q, kc, bc, sel_idx and sel_score must be non-NULL");
+  if (g.C() > 16384) return fail(HILS_E_UNSUPPORTED, "scoring needs N/S <= 16384 (N=%d)", g.N);
+  if (!q || !sel_idx || !sel_score) return fail(HILS_E_INVAL, "q, sel_idx and sel_score must be non-NULL");
+  if (g.C() > 0 && (!kc || !bc)) return fail(HILS_E_INVAL, "kc and bc must be non-NULL");
   if (g.r > 0 && (!qcal_D || !qcal_U)) return fail(HILS_E_INVAL, "qcal_rank > 0 needs qcal_D and qcal_U");
-  hipError_t e = hils::launch_score_topk(g, q, qcal_D, qcal_U, kc, bc, sel_idx, sel_score, (hipStream_t)stream);
+  const size_t need = hils::score_workspace_bytes(g);
+  if (!ws && need > 0) return fail(HILS_E_WORKSPACE, "workspace is NULL (%zu bytes needed)", need);
+  if (ws_bytes < need) return fail(HILS_E_WORKSPACE, "workspace too small: %zu < %zu", ws_bytes, need);
+  hipError_t e = hils::launch_score_topk(g, q, qcal_D, qcal_U, kc, bc, sel_idx, sel_score, ws, ws_bytes,
+                                         (hipStream_t)stream);
   if (e != hipSuccess) return hip_fail(e, "hils_chunk_score_topk");
   g_err[0] = 0;
   return HILS_OK;
@@ -179,7 +185,8 @@ int run_prefill(const hils_dims_t* dims, const void* q, const void* k, const voi
     e = hils::launch_compress(g.io, k, lmk_q, kcp, bcp, g.B, g.Hkv, g.Hl, g.N, g.d, 0, g.C(), st);
   }
   if (e == hipSuccess && stage_ms) e = hipEventRecord(ev[1], st);
-  if (e == hipSuccess) e = hils::launch_score_topk(g, q, qcal_D, qcal_U, kcp, bcp, sel, scr, st);
+  if (e == hipSuccess)
+    e = hils::launch_score_topk(g, q, qcal_D, qcal_U, kcp, bcp, sel, scr, base + w.score, w.attend - w.score, st);
   if (e == hipSuccess && stage_ms) e = hipEventRecord(ev[2], st);
   if (e == hipSuccess)
     e = hils::launch_prefill_attend(g, q, k, v, sel, scr, o, base + w.attend, w.total - w.attend, st,

@@ -17,8 +17,10 @@ hipError_t launch_compress(int io, const void* k, const void* lmk, float* kc, fl
                            int N, int d, int c_begin, int c_end, hipStream_t st);
 
 // Chunk scores and per-row top-K for all N queries of every (b, h).
+size_t score_workspace_bytes(const Geom& g);
 hipError_t launch_score_topk(const Geom& g, const void* q, const void* D, const void* U, const float* kc,
-                             const float* bc, int32_t* sel_idx, float* sel_score, hipStream_t st);
+                             const float* bc, int32_t* sel_idx, float* sel_score, void* ws, size_t ws_bytes,
+                             hipStream_t st);
 
 // Intra-chunk attention and fusion for prefill, given the selection.
 size_t attend_workspace_bytes(const Geom& g);

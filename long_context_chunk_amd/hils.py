@@ -140,7 +140,9 @@ def chunk_score_topk(dm: Dims, q, kc, bc, sel_idx, sel_score, qcal_D=None, qcal_
     if dm.qcal_rank > 0:
         _req(qcal_D, "qcal_D", (dm.Hq, dm.qcal_rank, dm.d), dt)
         _req(qcal_U, "qcal_U", (dm.Hq, dm.d, dm.qcal_rank), dt)
-    nws = ws.numel() if ws is not None else 0
+    if ws is None:
+        ws = workspace(dm, OP_SCORE_TOPK)
+    nws = ws.numel()
     _check(load().hils_chunk_score_topk(ctypes.byref(dm), _p(q), _p(qcal_D), _p(qcal_U), _p(kc), _p(bc), _p(sel_idx),
                                         _p(sel_score), _p(ws), nws, _stream()))
 
