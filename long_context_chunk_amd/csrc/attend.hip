@@ -13,14 +13,16 @@
 // (query row, selected chunk) pair is bucketed by (batch, KV head, chunk); each
 // workgroup loads one chunk's K/V tile into LDS once and runs full 32-row MFMA
 // tiles of gathered query rows against it.  Per pair it writes the normalised
-// chunk output o_ic (fp16 for bf16 I/O, fp32 for fp32 I/O) to a slot of its row;
-// a per-query-chunk pass then computes the own chunk on the MFMA and fuses.
+// chunk output o_ic (fp16 for bf16 I/O, fp32 for fp32 I/O) to a slot of its row
+// (K + 1 slots per row); a per-query-chunk pass writes the own chunk's output to
+// the last slot, and a streaming pass fuses the slots.
 //
 //   bucket_count  : LDS-privatised histogram of the selections per bucket
 //   bucket_scan   : exclusive scans -> bucket offsets and tile offsets
 //   bucket_scatter: pair ids (= linear index into sel_idx) grouped by bucket
 //   chunk_attend  : gathered-row MFMA attention per (bucket, 128-row tile)
-//   fuse_own      : own-chunk MFMA attention + softmax fusion -> o
+//   own_attend    : causal own-chunk MFMA attention -> slot K and LSE_own
+//   fuse          : softmax over {s_ic} U {LSE_own}, weighted sum of the slots -> o
 #include <algorithm>
 
 #include "hils_common.h"
@@ -33,7 +35,7 @@ constexpr int HIST_SLICE = 1 << 18; // selection entries per bucket_count / buck
 constexpr int MAX_C = 16384;        // largest chunk count the LDS histograms hold
 
 struct AttendWs {
-  size_t counts, cursor, boff, toff, pairs, partial, total;
+  size_t counts, cursor, boff, toff, pairs, partial, lse, total;
 };
 
 static size_t al(size_t x) { return (x + 255) / 256 * 256; }
@@ -53,8 +55,12 @@ static AttendWs attend_ws(const Geom& g) {
   off += al((nbk + 1) * 4);
   w.pairs = off;
   off += al(ent * 4);
+  // per row K + 1 output slots: the selected chunks' in selection order, then the own chunk
+  const size_t rows = (size_t)g.B * g.Hq * g.N;
   w.partial = off;
-  off += al(ent * g.d * (g.io == 0 ? 4 : 2));
+  off += al(rows * (g.K + 1) * g.d * (g.io == 0 ? 4 : 2));
+  w.lse = off;
+  off += al(rows * 4);
   w.total = off;
   return w;
 }
@@ -413,10 +419,11 @@ __global__ void __launch_bounds__(256, 2) chunk_attend(const IO* __restrict__ q,
       const int r = 32 * w + i / SEGS, sg = i % SEGS;
       const uint32_t e = pid[r];
       if (e != 0xffffffffu)
-        *reinterpret_cast<u32x4_t*>(dst + (int64_t)e * D + 8 * sg) = *reinterpret_cast<const u32x4_t*>(&qs[r * LDQ + 8 * sg]);
+        *reinterpret_cast<u32x4_t*>(dst + ((int64_t)e + e / (uint32_t)K) * D + 8 * sg) =
+            *reinterpret_cast<const u32x4_t*>(&qs[r * LDQ + 8 * sg]);
     }
   } else if (ok) {
-    PT* dst = reinterpret_cast<PT*>(partial_v) + (int64_t)e_pair * D;
+    PT* dst = reinterpret_cast<PT*>(partial_v) + ((int64_t)e_pair + e_pair / (uint32_t)K) * D;
 #pragma unroll
     for (int dt = 0; dt < D / 32; ++dt)
 #pragma unroll
@@ -428,133 +435,146 @@ __global__ void __launch_bounds__(256, 2) chunk_attend(const IO* __restrict__ q,
   }
 }
 
-// ---------------------------------------------------------------- fuse_own
-// One workgroup (8 waves) per (b, h, query chunk qc): rows qc*64 .. qc*64+63.
-//   waves 0-1: the own chunk on the MFMA (causal), normalised o_own and LSE_own -> LDS;
-//   waves 2-7: meanwhile, per row, the selected chunks' outputs weighted by
-//              exp(s_c - max s) with 16-byte loads of whole partial rows (registers);
-//   then waves 2-7 combine both parts with the softmax over all chunk scores.
-constexpr int FU_WAVES = 6;                    // fusion waves
-constexpr int FU_ROWS = (64 + FU_WAVES - 1) / FU_WAVES;
-
+// ---------------------------------------------------------------- own_attend
+// One workgroup (2 waves) per (b, h, query chunk qc): rows qc*64 .. qc*64+63 attend
+// their own chunk causally on the MFMA; the normalised output goes to output slot K
+// of the row and its log-sum-exp to lse[row].
 template <typename IO, int D>
-__global__ void __launch_bounds__(512) fuse_own(const IO* __restrict__ q, const IO* __restrict__ k,
-                                                const IO* __restrict__ v, const int32_t* __restrict__ sel_idx,
-                                                const float* __restrict__ sel_score, const void* __restrict__ partial_v,
-                                                IO* __restrict__ o, int Hq, int Hkv, int N, int K, int NQC) {
+__global__ void __launch_bounds__(128) own_attend(const IO* __restrict__ q, const IO* __restrict__ k,
+                                                  const IO* __restrict__ v, void* __restrict__ partial_v,
+                                                  float* __restrict__ lse, int Hq, int Hkv, int N, int K, int NQC) {
   constexpr int NT = io_traits<IO>::terms;
   using PT = typename partial_t<IO>::type;
-  constexpr int EPL = 16 / sizeof(PT);   // partial elements per 16-byte load
-  constexpr int LPS = D / EPL;           // lanes per partial row
-  constexpr int SPL = 64 / LPS;          // partial rows per wave-wide load
   __shared__ KVTile<IO, D, NT> tile;
-  __shared__ float own[64][D + 4];
-  __shared__ float lse[64];
   const int qc = blockIdx.x % NQC, bh = blockIdx.x / NQC;
   const int h = bh % Hq, b = bh / Hq;
   const int kvh = h / (Hq / Hkv);
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, hf = lane >> 5;
   const int key0 = qc * 64;
   const int nkeys = min(64, N - key0);
-  float sacc[FU_ROWS][EPL];
-  float msel[FU_ROWS], zsel[FU_ROWS];
-  if (w < 2) {
-    stage_kv<IO, D, NT>(tile, k, v, ((int64_t)b * Hkv + kvh) * N + key0, nkeys, tid, 128);
-  } else {
-    const int f = w - 2;
-    const int slot = lane / LPS, dpos = (lane % LPS) * EPL;
+  stage_kv<IO, D, NT>(tile, k, v, ((int64_t)b * Hkv + kvh) * N + key0, nkeys, tid, 128);
+  const int rl = 32 * w + (lane & 31);
+  const int i = key0 + rl;
+  const bool ok = i < N;
+  bf16x8_t qb[NT][D / 16];
+  load_q_operand<IO, D, NT>(q, ((int64_t)bh * N + (ok ? i : 0)) * D, ok, qb);
+  __syncthreads();
+  f32x16_t oa[D / 32];
+  float m, l;
+  wave_chunk_attention<IO, D, NT>(tile, qb, rl + 1, oa, m, l);  // causal: keys 0..rl
+  if (!ok) return;
+  const int64_t row = (int64_t)bh * N + i;
+  const float inv = 1.0f / l;
+  PT* dst = reinterpret_cast<PT*>(partial_v) + (row * (K + 1) + K) * D;
 #pragma unroll
-    for (int u = 0; u < FU_ROWS; ++u) {
-      const int rl = f + FU_WAVES * u;
-      const int i = key0 + rl;
+  for (int dt = 0; dt < D / 32; ++dt)
 #pragma unroll
-      for (int x = 0; x < EPL; ++x) sacc[u][x] = 0.f;
-      msel[u] = -INFINITY;
-      zsel[u] = 0.f;
-      if (rl < 64 && i < N) {
-        const int64_t row = (int64_t)bh * N + i;
-        const float sc = lane < K ? sel_score[row * K + lane] : -INFINITY;
-        const int ci = lane < K ? sel_idx[row * K + lane] : -1;
-        const float sv = ci >= 0 ? sc : -INFINITY;
-        const float M = wave_max(sv);
-        const float wt = ci >= 0 ? __expf(sv - M) : 0.f;
-        zsel[u] = wave_sum(wt);
-        msel[u] = M;
-        const int nsel = __popcll(__ballot(ci >= 0));
-        const PT* src = reinterpret_cast<const PT*>(partial_v) + row * K * D;
-        for (int t0 = 0; t0 < nsel; t0 += SPL) {
-          const int t = t0 + slot;
-          const float wtt = __shfl(wt, t < 64 ? t : 0);
-          if (t < nsel) {
-            const u32x4_t raw = *reinterpret_cast<const u32x4_t*>(src + (int64_t)t * D + dpos);
-            if constexpr (sizeof(PT) == 2) {
-              const uint32_t wd[4] = {raw.x, raw.y, raw.z, raw.w};
-#pragma unroll
-              for (int x = 0; x < 4; ++x) {
-                sacc[u][2 * x] = fmaf(wtt, f16_to_f32((uint16_t)(wd[x] & 0xffffu)), sacc[u][2 * x]);
-                sacc[u][2 * x + 1] = fmaf(wtt, f16_to_f32((uint16_t)(wd[x] >> 16)), sacc[u][2 * x + 1]);
-              }
-            } else {
-              sacc[u][0] = fmaf(wtt, __uint_as_float(raw.x), sacc[u][0]);
-              sacc[u][1] = fmaf(wtt, __uint_as_float(raw.y), sacc[u][1]);
-              sacc[u][2] = fmaf(wtt, __uint_as_float(raw.z), sacc[u][2]);
-              sacc[u][3] = fmaf(wtt, __uint_as_float(raw.w), sacc[u][3]);
-            }
-          }
-        }
-        // sum the slot groups: lanes with the same dpos
-#pragma unroll
-        for (int st = LPS; st < 64; st <<= 1)
-#pragma unroll
-          for (int x = 0; x < EPL; ++x) sacc[u][x] += __shfl_xor(sacc[u][x], st);
+    for (int g4 = 0; g4 < 4; ++g4) {
+      const int e = 32 * dt + 8 * g4 + 4 * hf;
+      if constexpr (sizeof(PT) == 2) {
+        u32x2_t pk;
+        pk.x = (uint32_t)f32_to_f16(oa[dt][4 * g4 + 0] * inv) | ((uint32_t)f32_to_f16(oa[dt][4 * g4 + 1] * inv) << 16);
+        pk.y = (uint32_t)f32_to_f16(oa[dt][4 * g4 + 2] * inv) | ((uint32_t)f32_to_f16(oa[dt][4 * g4 + 3] * inv) << 16);
+        *reinterpret_cast<u32x2_t*>(dst + e) = pk;
+      } else {
+        *reinterpret_cast<float4*>(dst + e) = make_float4(oa[dt][4 * g4] * inv, oa[dt][4 * g4 + 1] * inv,
+                                                          oa[dt][4 * g4 + 2] * inv, oa[dt][4 * g4 + 3] * inv);
       }
     }
-  }
-  __syncthreads();
-  if (w < 2) {  // own chunk: wave w takes rows 32w .. 32w+31 of the chunk
-    const int rl = 32 * w + (lane & 31);
-    const int i = key0 + rl;
-    const bool ok = i < N;
-    bf16x8_t qb[NT][D / 16];
-    load_q_operand<IO, D, NT>(q, ((int64_t)bh * N + (ok ? i : 0)) * D, ok, qb);
-    f32x16_t oa[D / 32];
-    float m, l;
-    wave_chunk_attention<IO, D, NT>(tile, qb, rl + 1, oa, m, l);  // causal: keys 0..rl
-    const float inv = 1.0f / l;
+  if (hf == 0) lse[row] = m + logf(l);
+}
+
+// ---------------------------------------------------------------------- fuse
+// o_i = sum over the row's chunk outputs (selected chunks, then its own chunk) weighted
+// by the softmax of their scores (the selected chunks' s_ic, the own chunk's LSE).  The
+// number of selected chunks is min(K, past chunks), so every load of a row is issued at
+// once; each wave works on two rows at a time.  16-byte loads of whole output rows.
+constexpr int FZ_ROWS = 16;  // rows per wave
+
+template <typename IO, int D>
+__global__ void __launch_bounds__(256) fuse(const float* __restrict__ sel_score, const float* __restrict__ lse,
+                                            const void* __restrict__ partial_v, IO* __restrict__ o, int N, int C,
+                                            int K, int64_t rows) {
+  using PT = typename partial_t<IO>::type;
+  constexpr int EPL = 16 / sizeof(PT);   // partial elements per 16-byte load
+  constexpr int LPS = D / EPL;           // lanes per output row
+  constexpr int SPL = 64 / LPS;          // output rows per wave-wide load
+  constexpr int NSEG = (32 + 1 + SPL - 1) / SPL;  // loads per lane for up to 32 + 1 slots
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int slot = lane / LPS, dpos = (lane % LPS) * EPL;
+  const int64_t row0 = ((int64_t)blockIdx.x * 4 + w) * FZ_ROWS;
+  const PT* part = reinterpret_cast<const PT*>(partial_v);
+  for (int u = 0; u < FZ_ROWS; u += 2) {
+    u32x4_t raw[2][NSEG];
+    float sc[2];
+    int nsel[2];
+    bool live[2];
 #pragma unroll
-    for (int dt = 0; dt < D / 32; ++dt)
+    for (int v2 = 0; v2 < 2; ++v2) {  // issue every load of both rows first
+      const int64_t row = row0 + u + v2;
+      live[v2] = row < rows;
+      const int i = live[v2] ? (int)(row % N) : 0;
+      const int ns = min(K, min(C, i / 64));
+      nsel[v2] = ns;
+      sc[v2] = -INFINITY;
+      if (live[v2]) {
+        if (lane < ns) sc[v2] = sel_score[row * K + lane];
+        else if (lane == ns) sc[v2] = lse[row];
+      }
 #pragma unroll
-      for (int g4 = 0; g4 < 4; ++g4)
-        *reinterpret_cast<float4*>(&own[rl][32 * dt + 8 * g4 + 4 * hf]) =
-            make_float4(oa[dt][4 * g4] * inv, oa[dt][4 * g4 + 1] * inv, oa[dt][4 * g4 + 2] * inv, oa[dt][4 * g4 + 3] * inv);
-    if (hf == 0) lse[rl] = m + logf(l);
-  }
-  __syncthreads();
-  if (w >= 2 && lane < LPS) {
-    const int f = w - 2;
-    const int dpos = lane * EPL;
+      for (int sg = 0; sg < NSEG; ++sg) {
+        const int t = sg * SPL + slot;           // logical slot: 0..ns-1 selected, ns = own
+        const int phys = t < ns ? t : K;
+        raw[v2][sg] = (live[v2] && t <= ns)
+                          ? *reinterpret_cast<const u32x4_t*>(part + (row * (K + 1) + phys) * D + dpos)
+                          : u32x4_t{0u, 0u, 0u, 0u};
+      }
+    }
 #pragma unroll
-    for (int u = 0; u < FU_ROWS; ++u) {
-      const int rl = f + FU_WAVES * u;
-      const int i = key0 + rl;
-      if (rl < 64 && i < N) {
-        const int64_t row = (int64_t)bh * N + i;
-        const float lo = lse[rl];
-        const float M = fmaxf(msel[u], lo);
-        const float a = __expf(msel[u] - M), bo = __expf(lo - M);
-        const float inv = 1.0f / (zsel[u] * a + bo);
-        float r[EPL];
+    for (int v2 = 0; v2 < 2; ++v2) {
+      if (!live[v2]) continue;
+      const int64_t row = row0 + u + v2;
+      const float M = wave_max(sc[v2]);
+      const float wt = sc[v2] == -INFINITY ? 0.f : __expf(sc[v2] - M);
+      const float inv = 1.0f / wave_sum(wt);
+      float acc[EPL];
 #pragma unroll
-        for (int x = 0; x < EPL; ++x) r[x] = (sacc[u][x] * a + own[rl][dpos + x] * bo) * inv;
+      for (int x = 0; x < EPL; ++x) acc[x] = 0.f;
+#pragma unroll
+      for (int sg = 0; sg < NSEG; ++sg) {
+        const int t = sg * SPL + slot;
+        const float wtt = __shfl(wt, t < 64 ? t : 0) * (t <= nsel[v2] ? 1.f : 0.f);
+        const u32x4_t rw = raw[v2][sg];
+        if constexpr (sizeof(PT) == 2) {
+          const uint32_t wd[4] = {rw.x, rw.y, rw.z, rw.w};
+#pragma unroll
+          for (int x = 0; x < 4; ++x) {
+            acc[2 * x] = fmaf(wtt, f16_to_f32((uint16_t)(wd[x] & 0xffffu)), acc[2 * x]);
+            acc[2 * x + 1] = fmaf(wtt, f16_to_f32((uint16_t)(wd[x] >> 16)), acc[2 * x + 1]);
+          }
+        } else {
+          acc[0] = fmaf(wtt, __uint_as_float(rw.x), acc[0]);
+          acc[1] = fmaf(wtt, __uint_as_float(rw.y), acc[1]);
+          acc[2] = fmaf(wtt, __uint_as_float(rw.z), acc[2]);
+          acc[3] = fmaf(wtt, __uint_as_float(rw.w), acc[3]);
+        }
+      }
+      // sum the slot groups (lanes with the same dpos)
+#pragma unroll
+      for (int st = LPS; st < 64; st <<= 1)
+#pragma unroll
+        for (int x = 0; x < EPL; ++x) acc[x] += __shfl_xor(acc[x], st);
+      if (lane < LPS) {
         if constexpr (sizeof(IO) == 2) {
           u32x4_t pk;
-          pk.x = (uint32_t)f32_to_bf16(r[0]) | ((uint32_t)f32_to_bf16(r[1]) << 16);
-          pk.y = (uint32_t)f32_to_bf16(r[2]) | ((uint32_t)f32_to_bf16(r[3]) << 16);
-          pk.z = (uint32_t)f32_to_bf16(r[4]) | ((uint32_t)f32_to_bf16(r[5]) << 16);
-          pk.w = (uint32_t)f32_to_bf16(r[6]) | ((uint32_t)f32_to_bf16(r[7]) << 16);
+          pk.x = (uint32_t)f32_to_bf16(acc[0] * inv) | ((uint32_t)f32_to_bf16(acc[1] * inv) << 16);
+          pk.y = (uint32_t)f32_to_bf16(acc[2] * inv) | ((uint32_t)f32_to_bf16(acc[3] * inv) << 16);
+          pk.z = (uint32_t)f32_to_bf16(acc[4] * inv) | ((uint32_t)f32_to_bf16(acc[5] * inv) << 16);
+          pk.w = (uint32_t)f32_to_bf16(acc[6] * inv) | ((uint32_t)f32_to_bf16(acc[7] * inv) << 16);
           *reinterpret_cast<u32x4_t*>(o + row * D + dpos) = pk;
         } else {
-          *reinterpret_cast<float4*>(reinterpret_cast<float*>(o) + row * D + dpos) = make_float4(r[0], r[1], r[2], r[3]);
+          *reinterpret_cast<float4*>(reinterpret_cast<float*>(o) + row * D + dpos) =
+              make_float4(acc[0] * inv, acc[1] * inv, acc[2] * inv, acc[3] * inv);
         }
       }
     }
@@ -604,8 +624,13 @@ static hipError_t launch_attend_t(const Geom& g, const void* q, const void* k, c
     hipEventRecord(ev[1], st);
   }
   const int NQC = (g.N + 63) / 64;
-  hipLaunchKernelGGL((fuse_own<IO, D>), dim3(g.B * g.Hq * NQC), dim3(512), 0, st, (const IO*)q, (const IO*)k,
-                     (const IO*)v, sel, scr, (const void*)partial, (IO*)o, g.Hq, g.Hkv, g.N, g.K, NQC);
+  float* lse = (float*)(ws + w.lse);
+  hipLaunchKernelGGL((own_attend<IO, D>), dim3(g.B * g.Hq * NQC), dim3(128), 0, st, (const IO*)q, (const IO*)k,
+                     (const IO*)v, partial, lse, g.Hq, g.Hkv, g.N, g.K, NQC);
+  const int64_t rows = (int64_t)g.B * g.Hq * g.N;
+  const int64_t nwg = (rows + 4 * FZ_ROWS - 1) / (4 * FZ_ROWS);
+  hipLaunchKernelGGL((fuse<IO, D>), dim3((unsigned)nwg), dim3(256), 0, st, scr, (const float*)lse,
+                     (const void*)partial, (IO*)o, g.N, C, g.K, rows);
   if (ev) hipEventRecord(ev[2], st);
   return hipGetLastError();
 }
