@@ -1,33 +1,31 @@
-// Chunk scoring and streaming top-K for prefill queries.
+// Chunk scoring and top-K for prefill queries.
 //
 //   s_ic = q^_i . k'_c / sqrt(d) + b'_c   for every complete past chunk c < floor(i/S)
 //   q^_i = q_i + U_h (D_h q_i)             (Q-Cal; q^ = q without it)
 // keep the K best (ties -> lower chunk id).  (aitrends.kr article,
 // "Methodology": the score formula, the calculation flow and the Q-Cal module.)
 //
-// Design (gfx950):
-//   * One workgroup = 128 consecutive queries of one (batch, head); wave w owns 32
-//     of them as the M dimension of v_mfma_f32_32x32x16_bf16 and the chunks are the
-//     N dimension, so accumulator register r of a lane holds one chunk's score for
-//     a query row, and the 32 lanes of each half-wave cover 32 chunks of one row.
-//   * k' tiles of 64 chunks are staged through LDS (double-buffered, the next tile
-//     prefetched into registers while the current one is on the MFMA) and shared
-//     by the four waves.  k' (fp32) is split into bf16 terms (hi + lo, or three
-//     terms for fp32 I/O) and q^ likewise, so the bf16 MFMA reproduces the fp32
-//     dot product to ~2^-17 relative: index parity needs score errors far below
-//     1e-4, which a single bf16 rounding of k' does not give.
-//   * Q-Cal runs on the same MFMA (T = D q, then U T), chained through the
-//     accumulator layout without any cross-lane movement.
-//   * Chunk order: each block scans its past chunks in descending order of b'
-//     (the query-independent part of the score), from a per-head sort, so that
-//     the running K-th best rises early and few later chunks still qualify.
-//     k' is split into bf16 planes once per call, so staging a tile is a copy.
-//   * Top-K: every row keeps its exact running top K sorted across the 32 lanes
-//     of its half-wave (lane j = j-th best) in registers, plus an unsorted
-//     32-slot candidate buffer.  New scores are tested against the row's K-th
-//     best with one compare; passing ones are appended to the buffer with one
-//     lane permute; a full buffer is bitonic-sorted and merged into the list
-//     (DPP and swizzle lane exchanges, no LDS traffic).
+// Two passes over the past chunks, both on v_mfma_f32_32x32x16_bf16: one workgroup
+// = 128 consecutive queries of one (batch, head), wave w owns 32 of them as the M
+// dimension, the chunks are the N dimension (accumulator register r of a lane holds
+// one chunk's score for one query row; the 32 lanes of a half-wave cover 32 chunks of
+// one row), and k' tiles of 64 chunks are staged through LDS for the four waves.
+//
+//   1. score_threshold: one bf16 product per score, bf16(q^/sqrt(d)) . bf16(k'_c),
+//      with b'_c and an error allowance e_i |k'_c| folded into one extra MFMA k-step,
+//      so every value is at most the fp32-accurate score of pass 2.  Each lane keeps
+//      the two largest values of its column of chunks; the K-th largest of these 64
+//      values of distinct chunks is a threshold theta_i that the row's K-th best
+//      score can not be below.
+//   2. score_topk_kernel: the scores to ~2^-17 relative (k' split into bf16 hi + lo
+//      terms, q^ too when it is not exactly bf16), tested against the row's running
+//      K-th best, which starts at theta_i, so only about K candidates per row reach
+//      the selection.  Candidates are appended to a 31-slot buffer per row (one lane
+//      permute); a full buffer is bitonic-sorted and merged into the row's sorted
+//      list (lane exchanges by DPP and swizzle).
+//   k' is rewritten once per call into bf16 term planes whose 16-element k-blocks are
+//   stored in MFMA operand order, so staging is a copy and an operand is one 16-byte
+//   LDS read.
 #include <algorithm>
 
 #include "hils_common.h"
@@ -108,11 +106,13 @@ HILS_DEV void merge_into(float& ls, int& li, float ns, int nc, int j, int K) {
 
 HILS_DEV float readlane_f(float v, int l) { return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), l)); }
 
-// the K-th best (score, chunk) of each half's list, broadcast to its lanes
-HILS_DEV void kth(float ls, int li, int hf, int K, float& ts, int& ti) {
+// the K-th best (score, chunk) of each half's list, broadcast to its lanes; the
+// score is raised to the row's threshold th while the list holds fewer than K
+// entries (every list entry is >= th, so a full list's K-th best is too)
+HILS_DEV void kth(float ls, int li, int hf, int K, float th, float& ts, int& ti) {
   const float t0 = readlane_f(ls, K - 1), t1 = readlane_f(ls, 32 + K - 1);
   const int i0 = __builtin_amdgcn_readlane(li, K - 1), i1 = __builtin_amdgcn_readlane(li, 32 + K - 1);
-  ts = hf ? t1 : t0;
+  ts = fmaxf(hf ? t1 : t0, th);
   ti = hf ? i1 : i0;
 }
 
@@ -134,35 +134,336 @@ HILS_DEV void append(float& bs, int& bi, int& f0, int& f1, float s, int c, bool 
 }
 
 // merge the buffer into the list and empty it; refresh the K-th best
-HILS_DEV void flush(float& ls, int& li, float& bs, int& bi, int& f0, int& f1, float& ts, int& ti, int j, int hf,
-                    int K) {
+HILS_DEV void flush(float& ls, int& li, float& bs, int& bi, int& f0, int& f1, float th, float& ts, int& ti, int j,
+                    int hf, int K) {
   const bool v = j < (hf ? f1 : f0);
   merge_into(ls, li, v ? bs : -INFINITY, v ? bi : 0x7fffffff, j, K);
   f0 = f1 = 0;
-  kth(ls, li, hf, K, ts, ti);
+  kth(ls, li, hf, K, th, ts, ti);
 }
 
+// float-only compare-exchange with lane j ^ X: keep the larger of the pair if keep_max
+template <int X>
+HILS_DEV float cxf(float s, int j, bool keep_max) {
+  const float p = __int_as_float(xlane<X>(__float_as_int(s), j));
+  return keep_max ? fmaxf(s, p) : fminf(s, p);
+}
+
+// bitonic sort of one float per lane, descending, within each 32-lane half
+HILS_DEV float sort32f(float s, int j) {
+#define HILS_STAGE(K_, X_) s = cxf<X_>(s, j, ((j & X_) == 0) == (((j & K_) == 0) || K_ == 32));
+  HILS_STAGE(2, 1)
+  HILS_STAGE(4, 2) HILS_STAGE(4, 1)
+  HILS_STAGE(8, 4) HILS_STAGE(8, 2) HILS_STAGE(8, 1)
+  HILS_STAGE(16, 8) HILS_STAGE(16, 4) HILS_STAGE(16, 2) HILS_STAGE(16, 1)
+  HILS_STAGE(32, 16) HILS_STAGE(32, 8) HILS_STAGE(32, 4) HILS_STAGE(32, 2) HILS_STAGE(32, 1)
+#undef HILS_STAGE
+  return s;
+}
+
+// the K-th largest of the 64 values {a, b} of each 32-lane half, broadcast to its lanes
+HILS_DEV float kth_of_pairs(float a, float b, int j, int hf, int K) {
+  a = sort32f(a, j);
+  b = sort32f(b, j);
+  a = fmaxf(a, __int_as_float(xlane<31>(__float_as_int(b), j)));  // the 32 largest, bitonic
+  a = cxf<16>(a, j, (j & 16) == 0);
+  a = cxf<8>(a, j, (j & 8) == 0);
+  a = cxf<4>(a, j, (j & 4) == 0);
+  a = cxf<2>(a, j, (j & 2) == 0);
+  a = cxf<1>(a, j, (j & 1) == 0);
+  const float t0 = readlane_f(a, K - 1), t1 = readlane_f(a, 32 + K - 1);
+  return hf ? t1 : t0;
+}
+
+// bf16 bits of the smallest bf16 >= x (x >= 0), clamped to the largest finite bf16
+HILS_DEV uint16_t bf16_up(float x) {
+  if (!(x < 3.38e38f)) return 0x7f7f;
+  uint16_t b = f32_to_bf16(x);
+  if (bf16_to_f32(b) < x) ++b;
+  return b;
+}
+
+// q^ = q + U_h (D_h q) of this lane's row (zero when !row_ok), delivered one MFMA
+// k-step at a time in the A-operand layout: sink(ks, v) gets v[m] = q^[kperm(ks, hf, m)].
+// Q-Cal runs on the MFMA (T = D q, then U T), chained through the accumulator layout.
+template <typename IO, int D, bool QCAL, typename Sink>
+HILS_DEV void qhat_rows(const IO* __restrict__ q, const IO* __restrict__ Dw, const IO* __restrict__ Uw, int hh, int r,
+                        int64_t qrow, bool row_ok, int lane, Sink&& sink) {
+  constexpr int NKS = D / 16;
+  constexpr int NIO = io_traits<IO>::terms;
+  const int hf = lane >> 5;
+  auto load8 = [&](int ks, float(&v)[8]) {
+    float a4[4], b4[4];
+    if (row_ok) {
+      io_traits<IO>::load4(q, qrow + kperm(ks, hf, 0), a4);
+      io_traits<IO>::load4(q, qrow + kperm(ks, hf, 4), b4);
+    } else {
+#pragma unroll
+      for (int m = 0; m < 4; ++m) a4[m] = b4[m] = 0.f;
+    }
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+      v[m] = a4[m];
+      v[4 + m] = b4[m];
+    }
+  };
+  if constexpr (!QCAL) {
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) {
+      float v[8];
+      load8(ks, v);
+      sink(ks, v);
+    }
+  } else {
+    // raw q terms (exact: NIO bf16 terms carry an io value exactly), as B operands
+    bf16x8_t qr[NIO][NKS];
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) {
+      float v[8];
+      load8(ks, v);
+      uint16_t t[NIO][8];
+#pragma unroll
+      for (int m = 0; m < 8; ++m) {
+        uint16_t sp[NIO];
+        split_bf16<NIO>(v[m], sp);
+#pragma unroll
+        for (int j = 0; j < NIO; ++j) t[j][m] = sp[j];
+      }
+#pragma unroll
+      for (int j = 0; j < NIO; ++j) qr[j][ks] = pack8(t[j]);
+    }
+    // T^T[a][row] = sum_e D[a][e] q[row][e]   (a < r; rows a >= r are zero)
+    f32x16_t T = zero16();
+    const int a_row = lane & 31;
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) {
+      uint16_t dt[NIO][8];
+#pragma unroll
+      for (int m = 0; m < 8; ++m) {
+        const float x = a_row < r ? io_traits<IO>::load(Dw, ((int64_t)hh * r + a_row) * D + kperm(ks, hf, m)) : 0.f;
+        uint16_t sp[NIO];
+        split_bf16<NIO>(x, sp);
+#pragma unroll
+        for (int j = 0; j < NIO; ++j) dt[j][m] = sp[j];
+      }
+#pragma unroll
+      for (int i = 0; i < NIO; ++i)
+#pragma unroll
+        for (int j = 0; j < NIO; ++j)
+          if (i + j < NIO) T = mfma32(pack8(dt[i]), qr[j][ks], T);
+    }
+    // T as the B operand of U T: accumulator register 8*ks2 + m -> k-step ks2, element m
+    constexpr int NT = NIO == 1 ? 2 : 3;
+    bf16x8_t tb[NT][2];
+#pragma unroll
+    for (int ks2 = 0; ks2 < 2; ++ks2) {
+      uint16_t t[NT][8];
+#pragma unroll
+      for (int m = 0; m < 8; ++m) {
+        uint16_t sp[NT];
+        split_bf16<NT>(T[8 * ks2 + m], sp);
+#pragma unroll
+        for (int j = 0; j < NT; ++j) t[j][m] = sp[j];
+      }
+#pragma unroll
+      for (int j = 0; j < NT; ++j) tb[j][ks2] = pack8(t[j]);
+    }
+    constexpr int NP = NIO > NT ? NIO : NT;
+#pragma unroll
+    for (int dt2 = 0; dt2 < D / 32; ++dt2) {
+      f32x16_t Q = zero16();
+      const int e = 32 * dt2 + (lane & 31);
+#pragma unroll
+      for (int ks2 = 0; ks2 < 2; ++ks2) {
+        uint16_t ut[NIO][8];
+#pragma unroll
+        for (int m = 0; m < 8; ++m) {
+          const int a = kperm(ks2, hf, m);
+          const float x = a < r ? io_traits<IO>::load(Uw, ((int64_t)hh * D + e) * r + a) : 0.f;
+          uint16_t sp[NIO];
+          split_bf16<NIO>(x, sp);
+#pragma unroll
+          for (int j = 0; j < NIO; ++j) ut[j][m] = sp[j];
+        }
+#pragma unroll
+        for (int i = 0; i < NIO; ++i)
+#pragma unroll
+          for (int j = 0; j < NT; ++j)
+            if (i + j < NP) Q = mfma32(pack8(ut[i]), tb[j][ks2], Q);
+      }
+      // register rr of this tile is head dim 32*dt2 + acc_row(rr, hf) = k-step 2*dt2 + rr/8, element rr%8
+#pragma unroll
+      for (int half = 0; half < 2; ++half) {
+        const int ks = 2 * dt2 + half;
+        float v[8];
+        load8(ks, v);  // reload the raw q slice (cheaper than keeping it live)
+#pragma unroll
+        for (int m = 0; m < 8; ++m) v[m] += Q[8 * half + m];
+        sink(ks, v);
+      }
+    }
+  }
+}
+
+// ------------------------------------------------------------- threshold pass
+// Error allowance of the one-product scores: with u = 2^-8 (bf16 rounding),
+// |bf(x) bf(y) - x y| <= (2u + u^2) |x y|, so over the head dimension the product
+// error is at most (2u + u^2) |tau q^| |k'| (Cauchy-Schwarz); TH_REL exceeds 2u + u^2
+// by enough to cover pass 2's own ~2^-16 relative error and fp32 accumulation, and
+// TH_ABS covers the two-term split of b'.
+constexpr float TH_REL = 0.008f;
+constexpr float TH_ABS = 1.0f / 4096.0f;   // bf16 0x3980
+constexpr int TH_EXT = 16;                  // elements of the extension k-step
+
+template <typename IO, int D, bool QCAL>
+__global__ void __launch_bounds__(256, 3) score_threshold(const IO* __restrict__ q, const IO* __restrict__ Dw,
+                                                          const IO* __restrict__ Uw, const uint16_t* __restrict__ t1,
+                                                          float* __restrict__ theta, int H, int N, int C, int K, int r,
+                                                          int NB, int items) {
+  constexpr int NKS = D / 16;
+  constexpr int DE = D + TH_EXT;      // bf16 elements of a chunk row
+  constexpr int LDT = DE + 8;         // LDS row stride (16-byte pad: conflict-free 16-byte reads)
+  constexpr int SEGS = DE / 8;
+  constexpr int NSEG = ST_TILE * SEGS;
+  constexpr int PL = (NSEG + 255) / 256;
+  __shared__ __align__(16) uint16_t kt[2][ST_TILE * LDT];
+
+  const int item = remap_xcd(blockIdx.x, items);
+  if (item >= items) return;
+  const int bh = item / NB;
+  const int rb = NB - 1 - (item % NB);  // heavier (later) row blocks first
+  const int hh = bh % H;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int n = lane & 31, hf = lane >> 5;
+  const int r0 = rb * ST_ROWS;
+  const int row = r0 + 32 * w + n;
+  const bool row_ok = row < N;
+  const int last = min(r0 + ST_ROWS, N) - 1;
+  const int Pmax = min(C, last / 64);
+  const int Pmin = min(C, r0 / 64);
+  const float tau = 1.0f / sqrtf((float)D);
+  const int64_t qrow = ((int64_t)bh * N + (row_ok ? row : 0)) * D;
+
+  // A operands: bf16(tau q^), then the extension step [1, 1, -1, -e_i] against the
+  // chunk's [b'_hi, b'_lo, TH_ABS, |k'_c| rounded up], e_i = TH_REL |tau q^_i| rounded up
+  bf16x8_t qa[NKS + 1];
+  float ss = 0.f;
+  qhat_rows<IO, D, QCAL>(q, Dw, Uw, hh, r, qrow, row_ok, lane, [&](int ks, const float(&v)[8]) {
+    uint16_t t[8];
+#pragma unroll
+    for (int m = 0; m < 8; ++m) {
+      const float x = v[m] * tau;
+      ss = fmaf(x, x, ss);
+      t[m] = f32_to_bf16(x);
+    }
+    qa[ks] = pack8(t);
+  });
+  ss += __shfl_xor(ss, 32);
+  {
+    uint16_t t[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+    if (hf == 0) {
+      t[0] = t[1] = 0x3f80;
+      t[2] = 0xbf80;
+      t[3] = (uint16_t)(bf16_up(TH_REL * sqrtf(ss)) | 0x8000u);
+    }
+    qa[NKS] = pack8(t);
+  }
+
+  const uint16_t* src = t1 + (int64_t)bh * C * DE;
+  u32x4_t pf[PL];
+  auto load_tile = [&](int t) {
+#pragma unroll
+    for (int u = 0; u < PL; ++u) {
+      const int it = tid + 256 * u;
+      const int e = it / SEGS, sg = it % SEGS;
+      const int c = t * ST_TILE + e;
+      pf[u] = (it < NSEG && c < Pmax) ? *reinterpret_cast<const u32x4_t*>(src + (int64_t)c * DE + 8 * sg)
+                                      : u32x4_t{0u, 0u, 0u, 0u};
+    }
+  };
+  auto store_tile = [&](int buf) {
+#pragma unroll
+    for (int u = 0; u < PL; ++u) {
+      const int it = tid + 256 * u;
+      if (it < NSEG) {
+        const int e = it / SEGS, sg = it % SEGS;
+        *reinterpret_cast<u32x4_t*>(&kt[buf][e * LDT + 8 * sg]) = pf[u];
+      }
+    }
+  };
+
+  // each lane: the two largest values of its column of chunks, for 2 rows per register
+  float m1[16], m2[16];
+#pragma unroll
+  for (int rr = 0; rr < 16; ++rr) m1[rr] = m2[rr] = -INFINITY;
+  const int ntiles = (Pmax + ST_TILE - 1) / ST_TILE;
+  if (ntiles > 0) {
+    load_tile(0);
+    store_tile(0);
+  }
+  __syncthreads();
+  for (int t = 0; t < ntiles; ++t) {
+    const int buf = t & 1;
+    const bool more = t + 1 < ntiles;
+    if (more) load_tile(t + 1);
+    const bool masked = (t + 1) * ST_TILE > Pmin;  // chunks >= Pmin are not past chunks of every row
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt) {
+      if (t * ST_TILE + 32 * tt >= Pmax) break;
+      const int ch = 32 * tt + n;
+      f32x16_t acc = zero16();
+#pragma unroll
+      for (int ks = 0; ks <= NKS; ++ks) {
+        const bf16x8_t bk = *reinterpret_cast<const bf16x8_t*>(&kt[buf][ch * LDT + 16 * ks + 8 * hf]);
+        acc = mfma32(qa[ks], bk, acc);
+      }
+      if (masked) {
+        const int c = t * ST_TILE + ch;
+#pragma unroll
+        for (int rr = 0; rr < 16; ++rr) {
+          const int rw = r0 + 32 * w + acc_row(rr, hf);
+          const int prow = rw < N ? min(C, rw / 64) : 0;
+          if (c >= prow) acc[rr] = -INFINITY;
+        }
+      }
+#pragma unroll
+      for (int rr = 0; rr < 16; ++rr) {
+        const float v = acc[rr];
+        m2[rr] = fmaxf(m2[rr], fminf(m1[rr], v));
+        m1[rr] = fmaxf(m1[rr], v);
+      }
+    }
+    if (more) store_tile(buf ^ 1);
+    __syncthreads();
+  }
+#pragma unroll
+  for (int rr = 0; rr < 16; ++rr) {
+    const float th = kth_of_pairs(m1[rr], m2[rr], n, hf, K);
+    const int rw = r0 + 32 * w + acc_row(rr, hf);
+    if (n == 0 && rw < N) theta[(int64_t)bh * N + rw] = th;
+  }
+}
+
+
+// ------------------------------------------------------------- selection pass
 template <typename IO, int D, int NQ, int NK, bool QCAL>
 __global__ void __launch_bounds__(256, 2) score_topk_kernel(const IO* __restrict__ q, const IO* __restrict__ Dw,
                                                              const IO* __restrict__ Uw,
                                                              const uint16_t* __restrict__ planes,
                                                              const float* __restrict__ bc,
-                                                             const int32_t* __restrict__ order,
+                                                             const float* __restrict__ theta,
                                                              int32_t* __restrict__ sel_idx,
                                                              float* __restrict__ sel_score, int H, int N, int C, int K,
                                                              int r, int NB, int items) {
-  constexpr int LDK = D + 4;            // padded bf16 row stride of the k' tile planes
+  constexpr int LDK = D + 8;            // LDS row stride of the k' tile planes (16-byte pad)
   constexpr int NKS = D / 16;           // MFMA k-steps over the head dimension
-  constexpr int NIO = io_traits<IO>::terms;
   constexpr int SEGS = D / 8;           // 16-byte segments of a plane row
   constexpr int PH = ST_TILE / 2 * NK * SEGS / 256;  // 16-byte prefetch loads per thread per half tile
-  __shared__ uint16_t kt[NK][ST_TILE * LDK];   // the current tile; its two halves are refilled in turn
+  __shared__ __align__(16) uint16_t kt[NK][ST_TILE * LDK];   // the current tile; its halves are refilled in turn
   __shared__ float bt[ST_TILE];
-  __shared__ int ct[ST_TILE];
-  __shared__ int wsum[4];
   __shared__ float lsl[4][16][64];              // per-row sorted lists (see below)
   __shared__ int lil[4][16][64];
-  extern __shared__ uint16_t lst[];    // this block's past chunks in scan order (C entries)
+  __shared__ float thl[4][16][2];               // per-row thresholds from the first pass
 
   const int item = remap_xcd(blockIdx.x, items);
   if (item >= items) return;
@@ -176,192 +477,51 @@ __global__ void __launch_bounds__(256, 2) score_topk_kernel(const IO* __restrict
   const bool row_ok = row < N;
   const int last = min(r0 + ST_ROWS, N) - 1;
   const int Pmax = min(C, last / 64);
+  const int Pmin = min(C, r0 / 64);
   const float tau = 1.0f / sqrtf((float)D);
   const int64_t qrow = ((int64_t)bh * N + (row_ok ? row : 0)) * D;
 
-  // ---- the query's A operands (k-permuted head-dim slices), split into bf16 terms
+  // ---- the query's A operands, q^ split into NQ bf16 terms
   bf16x8_t qb[NQ][NKS];
-  {
-    float qf[NKS][8];
+  qhat_rows<IO, D, QCAL>(q, Dw, Uw, hh, r, qrow, row_ok, lane, [&](int ks, const float(&v)[8]) {
+    uint16_t t[NQ][8];
 #pragma unroll
-    for (int ks = 0; ks < NKS; ++ks) {
-      float a4[4], b4[4];
-      if (row_ok) {
-        io_traits<IO>::load4(q, qrow + kperm(ks, hf, 0), a4);
-        io_traits<IO>::load4(q, qrow + kperm(ks, hf, 4), b4);
-      } else {
+    for (int m = 0; m < 8; ++m) {
+      uint16_t sp[NQ];
+      split_bf16<NQ>(v[m], sp);
 #pragma unroll
-        for (int m = 0; m < 4; ++m) a4[m] = b4[m] = 0.f;
-      }
-#pragma unroll
-      for (int m = 0; m < 4; ++m) {
-        qf[ks][m] = a4[m];
-        qf[ks][4 + m] = b4[m];
-      }
+      for (int j = 0; j < NQ; ++j) t[j][m] = sp[j];
     }
-    if constexpr (!QCAL) {
 #pragma unroll
-      for (int ks = 0; ks < NKS; ++ks) {
-        uint16_t t[NQ][8];
-#pragma unroll
-        for (int m = 0; m < 8; ++m) {
-          uint16_t sp[NQ];
-          split_bf16<NQ>(qf[ks][m], sp);
-#pragma unroll
-          for (int j = 0; j < NQ; ++j) t[j][m] = sp[j];
-        }
-#pragma unroll
-        for (int j = 0; j < NQ; ++j) qb[j][ks] = pack8(t[j]);
-      }
-    } else {
-      // raw q terms (exact: NIO bf16 terms carry an io value exactly), as B operands
-      bf16x8_t qr[NIO][NKS];
-#pragma unroll
-      for (int ks = 0; ks < NKS; ++ks) {
-        uint16_t t[NIO][8];
-#pragma unroll
-        for (int m = 0; m < 8; ++m) {
-          uint16_t sp[NIO];
-          split_bf16<NIO>(qf[ks][m], sp);
-#pragma unroll
-          for (int j = 0; j < NIO; ++j) t[j][m] = sp[j];
-        }
-#pragma unroll
-        for (int j = 0; j < NIO; ++j) qr[j][ks] = pack8(t[j]);
-      }
-      // T^T[a][row] = sum_e D[a][e] q[row][e]   (a < r; rows a >= r are zero)
-      f32x16_t T = zero16();
-      const int a_row = lane & 31;
-#pragma unroll
-      for (int ks = 0; ks < NKS; ++ks) {
-        uint16_t dt[NIO][8];
-#pragma unroll
-        for (int m = 0; m < 8; ++m) {
-          const float x = a_row < r ? io_traits<IO>::load(Dw, ((int64_t)hh * r + a_row) * D + kperm(ks, hf, m)) : 0.f;
-          uint16_t sp[NIO];
-          split_bf16<NIO>(x, sp);
-#pragma unroll
-          for (int j = 0; j < NIO; ++j) dt[j][m] = sp[j];
-        }
-#pragma unroll
-        for (int i = 0; i < NIO; ++i)
-#pragma unroll
-          for (int j = 0; j < NIO; ++j)
-            if (i + j < NIO) T = mfma32(pack8(dt[i]), qr[j][ks], T);
-      }
-      // T as the B operand of U T: accumulator register 8*ks2 + m -> k-step ks2, element m
-      constexpr int NT = NIO == 1 ? 2 : 3;
-      bf16x8_t tb[NT][2];
-#pragma unroll
-      for (int ks2 = 0; ks2 < 2; ++ks2) {
-        uint16_t t[NT][8];
-#pragma unroll
-        for (int m = 0; m < 8; ++m) {
-          uint16_t sp[NT];
-          split_bf16<NT>(T[8 * ks2 + m], sp);
-#pragma unroll
-          for (int j = 0; j < NT; ++j) t[j][m] = sp[j];
-        }
-#pragma unroll
-        for (int j = 0; j < NT; ++j) tb[j][ks2] = pack8(t[j]);
-      }
-      constexpr int NP = NIO > NT ? NIO : NT;
-#pragma unroll
-      for (int dt2 = 0; dt2 < D / 32; ++dt2) {
-        f32x16_t Q = zero16();
-        const int e = 32 * dt2 + (lane & 31);
-#pragma unroll
-        for (int ks2 = 0; ks2 < 2; ++ks2) {
-          uint16_t ut[NIO][8];
-#pragma unroll
-          for (int m = 0; m < 8; ++m) {
-            const int a = kperm(ks2, hf, m);
-            const float x = a < r ? io_traits<IO>::load(Uw, ((int64_t)hh * D + e) * r + a) : 0.f;
-            uint16_t sp[NIO];
-            split_bf16<NIO>(x, sp);
-#pragma unroll
-            for (int j = 0; j < NIO; ++j) ut[j][m] = sp[j];
-          }
-#pragma unroll
-          for (int i = 0; i < NIO; ++i)
-#pragma unroll
-            for (int j = 0; j < NT; ++j)
-              if (i + j < NP) Q = mfma32(pack8(ut[i]), tb[j][ks2], Q);
-        }
-        // register rr of this tile is head dim 32*dt2 + acc_row(rr, hf) = k-step 2*dt2 + rr/8, element rr%8
-#pragma unroll
-        for (int half = 0; half < 2; ++half) {
-          const int ks = 2 * dt2 + half;
-          uint16_t t[NQ][8];
-          float a4[4], b4[4];  // reload the raw q slice (cheaper than keeping it live)
-          if (row_ok) {
-            io_traits<IO>::load4(q, qrow + kperm(ks, hf, 0), a4);
-            io_traits<IO>::load4(q, qrow + kperm(ks, hf, 4), b4);
-          } else {
-#pragma unroll
-            for (int m = 0; m < 4; ++m) a4[m] = b4[m] = 0.f;
-          }
-#pragma unroll
-          for (int m = 0; m < 8; ++m) {
-            const float qh = (m < 4 ? a4[m] : b4[m - 4]) + Q[8 * half + m];
-            uint16_t sp[NQ];
-            split_bf16<NQ>(qh, sp);
-#pragma unroll
-            for (int j = 0; j < NQ; ++j) t[j][m] = sp[j];
-          }
-#pragma unroll
-          for (int j = 0; j < NQ; ++j) qb[j][ks] = pack8(t[j]);
-        }
-      }
-    }
-  }
-
-  // ---- scan order: past chunks c < Pmin (valid for every row of the block) by descending
-  // b', then the chunks Pmin .. Pmax-1 that only the later rows of the block see.
-  const int Pmin = min(C, r0 / 64);
-  {
-    const int32_t* ord = order + (int64_t)bh * C;
-    int base = 0;
-    for (int i0 = 0; i0 < C; i0 += 256) {
-      const int i = i0 + tid;
-      const int c = i < C ? ord[i] : C;
-      const bool v = c < Pmin;
-      const uint64_t bm = __ballot(v);
-      const int pre = (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(bm >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)bm, 0u));
-      if (lane == 0) wsum[w] = __popcll(bm);
-      __syncthreads();
-      int off = base;
-      for (int x = 0; x < w; ++x) off += wsum[x];
-      if (v) lst[off + pre] = (uint16_t)c;
-      base += wsum[0] + wsum[1] + wsum[2] + wsum[3];
-      __syncthreads();
-    }
-    for (int x = tid; x < Pmax - Pmin; x += 256) lst[Pmin + x] = (uint16_t)(Pmin + x);
-    __syncthreads();
-  }
+    for (int j = 0; j < NQ; ++j) qb[j][ks] = pack8(t[j]);
+  });
 
   // ---- per-row top-K state: register rr holds rows acc_row(rr, 0) (lanes 0..31) and
   // acc_row(rr, 1) (lanes 32..63) of this wave.  Lane j of a half holds buffer slot j
   // (bs, bi) of its row in registers; the row's sorted list (lane j = j-th best) lives
-  // in LDS (lsl, lil) and is only touched when a buffer is merged.  ts = K-th best score.
+  // in LDS (lsl, lil) and is only touched when a buffer is merged.  ts = the K-th best
+  // score so far, never below the row's threshold.
   float bs[16], ts[16];
   int bi[16], ff[16];  // ff: wave-uniform buffer fills, lanes 0..31 in bits 0..7, lanes 32..63 in bits 8..15
 #pragma unroll
   for (int rr = 0; rr < 16; ++rr) {
-    bs[rr] = ts[rr] = -INFINITY;
+    const int rw = r0 + 32 * w + acc_row(rr, hf);
+    const float th = rw < N ? theta[(int64_t)bh * N + rw] : -INFINITY;
+    ts[rr] = th;
+    bs[rr] = -INFINITY;
     bi[rr] = 0x7fffffff;
     ff[rr] = 0;
     lsl[w][rr][lane] = -INFINITY;
     lil[w][rr][lane] = 0x7fffffff;
+    if (n == 0) thl[w][rr][hf] = th;
   }
 
   const int64_t PL = (int64_t)(items / NB) * C * D;    // elements per plane: B*H*C*D
   const float* bcb = bc + (int64_t)bh * C;
   const int ntiles = (Pmax + ST_TILE - 1) / ST_TILE;
   // The next tile is prefetched in two halves of 32 chunks: loads issued before each
-  // 32-chunk MFMA column tile, written to the other LDS buffer after it.
+  // 32-chunk MFMA column tile, written over that half after it.
   u32x4_t pf[PH];
-  int pcid = 0;
   float pb = 0.f;
   auto prefetch = [&](int t, int part) {
 #pragma unroll
@@ -370,15 +530,13 @@ __global__ void __launch_bounds__(256, 2) score_topk_kernel(const IO* __restrict
       const int e = 32 * part + it / (NK * SEGS);
       const int rem = it % (NK * SEGS);
       const int pl = rem / SEGS, sg = rem % SEGS;
-      const int idx = t * ST_TILE + e;
-      const int cid = idx < Pmax ? (int)lst[idx] : -1;
-      pf[u] = cid >= 0 ? *reinterpret_cast<const u32x4_t*>(planes + pl * PL + ((int64_t)bh * C + cid) * D + 8 * sg)
+      const int c = t * ST_TILE + e;
+      pf[u] = c < Pmax ? *reinterpret_cast<const u32x4_t*>(planes + pl * PL + ((int64_t)bh * C + c) * D + 8 * sg)
                        : u32x4_t{0u, 0u, 0u, 0u};
     }
     if (tid < 32) {
-      const int idx = t * ST_TILE + 32 * part + tid;
-      pcid = idx < Pmax ? (int)lst[idx] : 0x7fffffff;
-      pb = idx < Pmax ? bcb[pcid] : 0.f;
+      const int c = t * ST_TILE + 32 * part + tid;
+      pb = c < Pmax ? bcb[c] : 0.f;
     }
   };
   // merge row-register rr's buffer into its LDS list; refresh ts
@@ -386,7 +544,7 @@ __global__ void __launch_bounds__(256, 2) score_topk_kernel(const IO* __restrict
     float ls = lsl[w][rr][lane];
     int li = lil[w][rr][lane];
     int bf0 = bff & 0xff, bf1 = bff >> 8;
-    flush(ls, li, b_s, b_i, bf0, bf1, t_s, t_i, n, hf, K);
+    flush(ls, li, b_s, b_i, bf0, bf1, thl[w][rr][hf], t_s, t_i, n, hf, K);
     bff = 0;
     lsl[w][rr][lane] = ls;
     lil[w][rr][lane] = li;
@@ -398,14 +556,9 @@ __global__ void __launch_bounds__(256, 2) score_topk_kernel(const IO* __restrict
       const int e = 32 * part + it / (NK * SEGS);
       const int rem = it % (NK * SEGS);
       const int pl = rem / SEGS, sg = rem % SEGS;
-      uint16_t* dstp = &kt[pl][e * LDK + 8 * sg];
-      *reinterpret_cast<u32x2_t*>(dstp) = u32x2_t{pf[u].x, pf[u].y};
-      *reinterpret_cast<u32x2_t*>(dstp + 4) = u32x2_t{pf[u].z, pf[u].w};
+      *reinterpret_cast<u32x4_t*>(&kt[pl][e * LDK + 8 * sg]) = pf[u];
     }
-    if (tid < 32) {
-      ct[32 * part + tid] = pcid;
-      bt[32 * part + tid] = pb;
-    }
+    if (tid < 32) bt[32 * part + tid] = pb;
   };
 
   if (ntiles > 0) {
@@ -415,66 +568,66 @@ __global__ void __launch_bounds__(256, 2) score_topk_kernel(const IO* __restrict
     commit(1);
   }
   __syncthreads();
-  // Half tile tt of the next tile is loaded into registers before the MFMA of half tt and
+  // Half tt of the next tile is loaded into registers before the MFMA of half tt and
   // written over half tt after a barrier; half tt is only read by column tile tt.
   for (int t = 0; t < ntiles; ++t) {
     const bool more = t + 1 < ntiles;
-    const bool masked = (t + 1) * ST_TILE > Pmin;  // entries beyond Pmin are not valid for every row
+    const bool masked = (t + 1) * ST_TILE > Pmin;  // chunks >= Pmin are not past chunks of every row
 #pragma unroll
     for (int tt = 0; tt < 2; ++tt) {
       if (more) prefetch(t + 1, tt);
-      f32x16_t acc = zero16();
-      const int ch = 32 * tt + (lane & 31);
+      if (t * ST_TILE + 32 * tt < Pmax) {
+        f32x16_t acc = zero16();
+        const int ch = 32 * tt + n;
 #pragma unroll
-      for (int ks = 0; ks < NKS; ++ks) {
+        for (int ks = 0; ks < NKS; ++ks) {
 #pragma unroll
-        for (int j = 0; j < NK; ++j) {
-          const uint16_t* kr = &kt[j][ch * LDK + 16 * ks + 4 * hf];
-          const bf16x8_t bk = pack8(*reinterpret_cast<const u32x2_t*>(kr), *reinterpret_cast<const u32x2_t*>(kr + 8));
+          for (int j = 0; j < NK; ++j) {
+            const bf16x8_t bk = *reinterpret_cast<const bf16x8_t*>(&kt[j][ch * LDK + 16 * ks + 8 * hf]);
 #pragma unroll
-          for (int i = 0; i < NQ; ++i)
-            if (i + j < (NQ > NK ? NQ : NK)) acc = mfma32(qb[i][ks], bk, acc);
-        }
-      }
-      const int c = ct[ch];
-      const float bprime = bt[ch];
-      // filter against each row's K-th best; append the survivors; overflowing
-      // buffers are handled after the pass (one copy of the merge code)
-      auto score_of = [&](float a, int rr) {
-        float s = fmaf(a, tau, bprime);
-        if (masked) {
-          const int rw = r0 + 32 * w + acc_row(rr, hf);
-          const int prow = rw < N ? min(C, rw / 64) : 0;
-          if (c >= prow) s = __builtin_nanf("");
-        }
-        return s;
-      };
-      uint32_t ovf = 0;
-#pragma unroll
-      for (int rr = 0; rr < 16; ++rr) {
-        const float s = score_of(acc[rr], rr);
-        bool pass = s > ts[rr];  // NaN never passes
-        if (__ballot(s == ts[rr])) {
-          const int ti = lil[w][rr][32 * hf + K - 1];
-          pass = pass || (s == ts[rr] && c < ti);
-        }
-        const uint64_t mk = __ballot(pass);
-        if (mk) {
-          int a0 = ff[rr] & 0xff, a1 = ff[rr] >> 8;
-          if (a0 + __popc((uint32_t)mk) > ST_BUF || a1 + __popc((uint32_t)(mk >> 32)) > ST_BUF) {
-            ovf |= 1u << rr;
-          } else {
-            append(bs[rr], bi[rr], a0, a1, s, c, pass, mk, n, hf);
-            ff[rr] = a0 | (a1 << 8);
+            for (int i = 0; i < NQ; ++i)
+              if (i + j < (NQ > NK ? NQ : NK)) acc = mfma32(qb[i][ks], bk, acc);
           }
         }
-      }
-      while (ovf) {
-        const int rr = __builtin_ctz(ovf);
-        ovf &= ovf - 1;
-        float wb, wt, wa;
-        int wj, wf;
-        switch (rr) {
+        const int c = t * ST_TILE + ch;
+        const float bprime = bt[ch];
+        // filter against each row's K-th best; append the survivors; overflowing
+        // buffers are handled after the pass (one copy of the merge code)
+        auto score_of = [&](float a, int rr) {
+          float s = fmaf(a, tau, bprime);
+          if (masked) {
+            const int rw = r0 + 32 * w + acc_row(rr, hf);
+            const int prow = rw < N ? min(C, rw / 64) : 0;
+            if (c >= prow) s = __builtin_nanf("");
+          }
+          return s;
+        };
+        uint32_t ovf = 0;
+#pragma unroll
+        for (int rr = 0; rr < 16; ++rr) {
+          const float s = score_of(acc[rr], rr);
+          bool pass = s > ts[rr];  // NaN never passes
+          if (__ballot(s == ts[rr])) {
+            const int ti = lil[w][rr][32 * hf + K - 1];
+            pass = pass || (s == ts[rr] && c < ti);
+          }
+          const uint64_t mk = __ballot(pass);
+          if (mk) {
+            int a0 = ff[rr] & 0xff, a1 = ff[rr] >> 8;
+            if (a0 + __popc((uint32_t)mk) > ST_BUF || a1 + __popc((uint32_t)(mk >> 32)) > ST_BUF) {
+              ovf |= 1u << rr;
+            } else {
+              append(bs[rr], bi[rr], a0, a1, s, c, pass, mk, n, hf);
+              ff[rr] = a0 | (a1 << 8);
+            }
+          }
+        }
+        while (ovf) {
+          const int rr = __builtin_ctz(ovf);
+          ovf &= ovf - 1;
+          float wb, wt, wa;
+          int wj, wf;
+          switch (rr) {
 #define HILS_PICK(R) \
   case R:            \
     wb = bs[R];      \
@@ -483,33 +636,33 @@ __global__ void __launch_bounds__(256, 2) score_topk_kernel(const IO* __restrict
     wt = ts[R];      \
     wa = acc[R];     \
     break;
-          HILS_PICK(0) HILS_PICK(1) HILS_PICK(2) HILS_PICK(3) HILS_PICK(4) HILS_PICK(5) HILS_PICK(6) HILS_PICK(7)
-          HILS_PICK(8) HILS_PICK(9) HILS_PICK(10) HILS_PICK(11) HILS_PICK(12) HILS_PICK(13) HILS_PICK(14)
-          HILS_PICK(15)
+            HILS_PICK(0) HILS_PICK(1) HILS_PICK(2) HILS_PICK(3) HILS_PICK(4) HILS_PICK(5) HILS_PICK(6) HILS_PICK(7)
+            HILS_PICK(8) HILS_PICK(9) HILS_PICK(10) HILS_PICK(11) HILS_PICK(12) HILS_PICK(13) HILS_PICK(14)
+            HILS_PICK(15)
 #undef HILS_PICK
-          default:
-            wb = wt = wa = 0.f;
-            wj = wf = 0;
-        }
-        const float ws = score_of(wa, rr);
-        int wti;
-        flush_rr(rr, wb, wj, wf, wt, wti);
-        const bool pass = better(ws, c, wt, wti);
-        const uint64_t mk = __ballot(pass);
-        int m0 = __popc((uint32_t)mk), m1 = __popc((uint32_t)(mk >> 32));
-        if ((m0 > m1 ? m0 : m1) > ST_BUF) {  // more than a buffer of new candidates: merge them directly
-          float ls = lsl[w][rr][lane];
-          int li = lil[w][rr][lane];
-          merge_into(ls, li, pass ? ws : -INFINITY, pass ? c : 0x7fffffff, n, K);
-          kth(ls, li, hf, K, wt, wti);
-          lsl[w][rr][lane] = ls;
-          lil[w][rr][lane] = li;
-        } else if (mk) {
-          int a0 = 0, a1 = 0;
-          append(wb, wj, a0, a1, ws, c, pass, mk, n, hf);
-          wf = a0 | (a1 << 8);
-        }
-        switch (rr) {
+            default:
+              wb = wt = wa = 0.f;
+              wj = wf = 0;
+          }
+          const float ws = score_of(wa, rr);
+          int wti;
+          flush_rr(rr, wb, wj, wf, wt, wti);
+          const bool pass = better(ws, c, wt, wti);
+          const uint64_t mk = __ballot(pass);
+          int m0 = __popc((uint32_t)mk), m1 = __popc((uint32_t)(mk >> 32));
+          if ((m0 > m1 ? m0 : m1) > ST_BUF) {  // more than a buffer of new candidates: merge them directly
+            float ls = lsl[w][rr][lane];
+            int li = lil[w][rr][lane];
+            merge_into(ls, li, pass ? ws : -INFINITY, pass ? c : 0x7fffffff, n, K);
+            kth(ls, li, hf, K, thl[w][rr][hf], wt, wti);
+            lsl[w][rr][lane] = ls;
+            lil[w][rr][lane] = li;
+          } else if (mk) {
+            int a0 = 0, a1 = 0;
+            append(wb, wj, a0, a1, ws, c, pass, mk, n, hf);
+            wf = a0 | (a1 << 8);
+          }
+          switch (rr) {
 #define HILS_PUT(R) \
   case R:           \
     bs[R] = wb;     \
@@ -517,11 +670,12 @@ __global__ void __launch_bounds__(256, 2) score_topk_kernel(const IO* __restrict
     ff[R] = wf;     \
     ts[R] = wt;     \
     break;
-          HILS_PUT(0) HILS_PUT(1) HILS_PUT(2) HILS_PUT(3) HILS_PUT(4) HILS_PUT(5) HILS_PUT(6) HILS_PUT(7)
-          HILS_PUT(8) HILS_PUT(9) HILS_PUT(10) HILS_PUT(11) HILS_PUT(12) HILS_PUT(13) HILS_PUT(14) HILS_PUT(15)
+            HILS_PUT(0) HILS_PUT(1) HILS_PUT(2) HILS_PUT(3) HILS_PUT(4) HILS_PUT(5) HILS_PUT(6) HILS_PUT(7)
+            HILS_PUT(8) HILS_PUT(9) HILS_PUT(10) HILS_PUT(11) HILS_PUT(12) HILS_PUT(13) HILS_PUT(14) HILS_PUT(15)
 #undef HILS_PUT
-          default:
-            break;
+            default:
+              break;
+          }
         }
       }
       __syncthreads();  // every wave is done with half tt of this tile
@@ -547,115 +701,149 @@ __global__ void __launch_bounds__(256, 2) score_topk_kernel(const IO* __restrict
   }
 }
 
-// ---------------------------------------------------------------- helpers kernels
-// k' (fp32) -> NK bf16 planes: plane j holds term j of every element (same layout as k')
-template <int NK>
-__global__ void __launch_bounds__(256) split_kprime(const float* __restrict__ kc, uint16_t* __restrict__ planes,
-                                                    int64_t n) {
-  for (int64_t i = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4; i < n; i += (int64_t)gridDim.x * 256 * 4) {
-    const float4 v = *reinterpret_cast<const float4*>(kc + i);
-    uint16_t s0[NK], s1[NK], s2[NK], s3[NK];
-    split_bf16<NK>(v.x, s0);
-    split_bf16<NK>(v.y, s1);
-    split_bf16<NK>(v.z, s2);
-    split_bf16<NK>(v.w, s3);
+// ---------------------------------------------------------------- k' preparation
+// k' (fp32) -> (a) NK bf16 term planes (plane j holds term j of every element) for the
+// selection pass and (b) the threshold pass's rows: bf16(k') followed by the extension
+// [b'_hi, b'_lo, TH_ABS, |k'_c| rounded up, 0 ...].  Both hold each 16-element k-block in
+// MFMA operand order: position 16 ks + 8 h + m holds element kperm(ks, h, m).
+template <int D, int NK>
+__global__ void __launch_bounds__(256) prep_kprime(const float* __restrict__ kc, const float* __restrict__ bc,
+                                                   uint16_t* __restrict__ planes, uint16_t* __restrict__ t1,
+                                                   int64_t rows) {
+  constexpr int SPR = D / 8;        // 16-byte segments (threads) per chunk row
+  constexpr int RPB = 256 / SPR;    // chunk rows per workgroup pass
+  constexpr int DE = D + TH_EXT;
+  const int tid = threadIdx.x;
+  const int sg = tid % SPR, ks = sg >> 1, h = sg & 1;
+  const int64_t n = rows * D;
+  for (int64_t base = (int64_t)blockIdx.x * RPB; base < rows; base += (int64_t)gridDim.x * RPB) {
+    const int64_t rw = base + tid / SPR;
+    const bool ok = rw < rows;
+    float x[8];
+    if (ok) {
+      const float4 a = *reinterpret_cast<const float4*>(kc + rw * D + kperm(ks, h, 0));
+      const float4 b = *reinterpret_cast<const float4*>(kc + rw * D + kperm(ks, h, 4));
+      x[0] = a.x, x[1] = a.y, x[2] = a.z, x[3] = a.w, x[4] = b.x, x[5] = b.y, x[6] = b.z, x[7] = b.w;
+    } else {
 #pragma unroll
-    for (int j = 0; j < NK; ++j) {
-      u32x2_t pk;
-      pk.x = (uint32_t)s0[j] | ((uint32_t)s1[j] << 16);
-      pk.y = (uint32_t)s2[j] | ((uint32_t)s3[j] << 16);
-      *reinterpret_cast<u32x2_t*>(planes + j * n + i) = pk;
+      for (int m = 0; m < 8; ++m) x[m] = 0.f;
     }
-  }
-}
-
-// per (b, h): chunk ids ordered by descending b' (ties: lower id first); bitonic sort in LDS
-__global__ void __launch_bounds__(1024) sort_bprime(const float* __restrict__ bc, int32_t* __restrict__ order, int C,
-                                                    int Cp2) {
-  extern __shared__ uint64_t keys[];
-  const int bh = blockIdx.x, t = threadIdx.x;
-  for (int i = t; i < Cp2; i += 1024) keys[i] = i < C ? make_key(bc[(int64_t)bh * C + i], i) : 0ull;
-  __syncthreads();
-  for (int k = 2; k <= Cp2; k <<= 1) {
-    for (int jj = k >> 1; jj > 0; jj >>= 1) {
-      for (int i = t; i < Cp2; i += 1024) {
-        const int l = i ^ jj;
-        if (l > i) {
-          const uint64_t a = keys[i], b = keys[l];
-          const bool desc = (i & k) == 0;
-          if (desc ? a < b : a > b) {
-            keys[i] = b;
-            keys[l] = a;
-          }
+    float s2 = 0.f;
+#pragma unroll
+    for (int m = 0; m < 8; ++m) s2 = fmaf(x[m], x[m], s2);
+#pragma unroll
+    for (int o = 1; o < SPR; o <<= 1) s2 += __shfl_xor(s2, o);
+    uint16_t tm[NK][8];
+#pragma unroll
+    for (int m = 0; m < 8; ++m) {
+      uint16_t sp[NK];
+      split_bf16<NK>(x[m], sp);
+#pragma unroll
+      for (int j = 0; j < NK; ++j) tm[j][m] = sp[j];
+    }
+    if (ok) {
+#pragma unroll
+      for (int j = 0; j < NK; ++j)
+        *reinterpret_cast<bf16x8_t*>(planes + j * n + rw * D + 8 * sg) = pack8(tm[j]);
+      uint16_t* o1 = t1 + rw * DE;
+      *reinterpret_cast<bf16x8_t*>(o1 + 8 * sg) = pack8(tm[0]);
+      if (sg < 2) {
+        uint16_t e[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+        if (sg == 0) {
+          uint16_t sp[2];
+          split_bf16<2>(bc[rw], sp);
+          e[0] = sp[0];
+          e[1] = sp[1];
+          e[2] = 0x3980;  // TH_ABS = 2^-12
+          e[3] = bf16_up(sqrtf(s2));
         }
+        *reinterpret_cast<bf16x8_t*>(o1 + D + 8 * sg) = pack8(e);
       }
-      __syncthreads();
     }
   }
-  for (int i = t; i < C; i += 1024) order[(int64_t)bh * C + i] = key_chunk(keys[i]);
 }
 
 static size_t al3(size_t x) { return (x + 255) / 256 * 256; }
 static int nk_of(const Geom& g) { return g.io == 0 ? 3 : 2; }
 
-size_t score_workspace_bytes(const Geom& g) {
-  const size_t n = (size_t)g.B * g.Hq * g.C() * g.d;
-  return al3((size_t)nk_of(g) * n * 2) + al3((size_t)g.B * g.Hq * g.C() * 4);
+struct ScoreWs {
+  size_t planes, t1, theta, total;
+};
+static ScoreWs score_ws(const Geom& g) {
+  const size_t rows = (size_t)g.B * g.Hq * g.C();
+  ScoreWs w;
+  size_t off = 0;
+  w.planes = off;
+  off += al3((size_t)nk_of(g) * rows * g.d * 2);
+  w.t1 = off;
+  off += al3(rows * (g.d + TH_EXT) * 2);
+  w.theta = off;
+  off += al3((size_t)g.B * g.Hq * g.N * 4);
+  w.total = off;
+  return w;
 }
+
+size_t score_workspace_bytes(const Geom& g) { return score_ws(g).total; }
 
 template <typename IO, int D, int NQ, int NK, bool QCAL>
 static void launch_st(const Geom& g, const void* q, const void* Dw, const void* Uw, const uint16_t* planes,
-                      const float* bc, const int32_t* order, int32_t* si, float* ss, hipStream_t st) {
+                      const uint16_t* t1, float* theta, const float* bc, int32_t* si, float* ss, hipStream_t st) {
   const int NB = (g.N + ST_ROWS - 1) / ST_ROWS;
   const int items = g.B * g.Hq * NB;
   const int grid = ((items + 7) / 8) * 8;
-  const size_t dyn = ((size_t)g.C() * 2 + 15) / 16 * 16 + 16;
-  auto kern = score_topk_kernel<IO, D, NQ, NK, QCAL>;
-  hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)dyn);
-  hipLaunchKernelGGL(kern, dim3(grid), dim3(256), dyn, st, (const IO*)q, (const IO*)Dw, (const IO*)Uw, planes, bc,
-                     order, si, ss, g.Hq, g.N, g.C(), g.K, g.r, NB, items);
+  hipLaunchKernelGGL((score_threshold<IO, D, QCAL>), dim3(grid), dim3(256), 0, st, (const IO*)q, (const IO*)Dw,
+                     (const IO*)Uw, t1, theta, g.Hq, g.N, g.C(), g.K, g.r, NB, items);
+  hipLaunchKernelGGL((score_topk_kernel<IO, D, NQ, NK, QCAL>), dim3(grid), dim3(256), 0, st, (const IO*)q,
+                     (const IO*)Dw, (const IO*)Uw, planes, bc, (const float*)theta, si, ss, g.Hq, g.N, g.C(), g.K,
+                     g.r, NB, items);
 }
 
 template <typename IO, int D>
 static void launch_st_d(const Geom& g, const void* q, const void* Dw, const void* Uw, const uint16_t* planes,
-                        const float* bc, const int32_t* order, int32_t* si, float* ss, hipStream_t st) {
+                        const uint16_t* t1, float* theta, const float* bc, int32_t* si, float* ss, hipStream_t st) {
   constexpr bool F32 = io_traits<IO>::terms == 3;
   if (g.r > 0)
-    launch_st<IO, D, F32 ? 3 : 2, F32 ? 3 : 2, true>(g, q, Dw, Uw, planes, bc, order, si, ss, st);
+    launch_st<IO, D, F32 ? 3 : 2, F32 ? 3 : 2, true>(g, q, Dw, Uw, planes, t1, theta, bc, si, ss, st);
   else
-    launch_st<IO, D, F32 ? 3 : 1, F32 ? 3 : 2, false>(g, q, Dw, Uw, planes, bc, order, si, ss, st);
+    launch_st<IO, D, F32 ? 3 : 1, F32 ? 3 : 2, false>(g, q, Dw, Uw, planes, t1, theta, bc, si, ss, st);
+}
+
+template <int D>
+static void launch_prep(const Geom& g, const float* kc, const float* bc, uint16_t* planes, uint16_t* t1,
+                        hipStream_t st) {
+  const int64_t rows = (int64_t)g.B * g.Hq * g.C();
+  const int64_t rpb = 256 / (D / 8);
+  const unsigned gs = (unsigned)std::min<int64_t>((rows + rpb - 1) / rpb, 16384);
+  if (nk_of(g) == 3)
+    hipLaunchKernelGGL((prep_kprime<D, 3>), dim3(gs), dim3(256), 0, st, kc, bc, planes, t1, rows);
+  else
+    hipLaunchKernelGGL((prep_kprime<D, 2>), dim3(gs), dim3(256), 0, st, kc, bc, planes, t1, rows);
 }
 
 hipError_t launch_score_topk(const Geom& g, const void* q, const void* Dw, const void* Uw, const float* kc,
                              const float* bc, int32_t* sel_idx, float* sel_score, void* ws, size_t ws_bytes,
                              hipStream_t st) {
   if (ws_bytes < score_workspace_bytes(g)) return hipErrorInvalidValue;
-  const int C = g.C();
-  const int64_t n = (int64_t)g.B * g.Hq * C * g.d;
-  uint16_t* planes = (uint16_t*)ws;
-  int32_t* order = (int32_t*)((char*)ws + al3((size_t)nk_of(g) * n * 2));
-  if (C > 0) {
-    const unsigned gs = (unsigned)std::min<int64_t>((n / 4 + 255) / 256, 8192);
-    if (nk_of(g) == 3)
-      hipLaunchKernelGGL(split_kprime<3>, dim3(gs), dim3(256), 0, st, kc, planes, n);
+  const ScoreWs w = score_ws(g);
+  uint16_t* planes = (uint16_t*)((char*)ws + w.planes);
+  uint16_t* t1 = (uint16_t*)((char*)ws + w.t1);
+  float* theta = (float*)((char*)ws + w.theta);
+  if (g.C() > 0) {
+    if (g.d == 64)
+      launch_prep<64>(g, kc, bc, planes, t1, st);
     else
-      hipLaunchKernelGGL(split_kprime<2>, dim3(gs), dim3(256), 0, st, kc, planes, n);
-    int Cp2 = 1;
-    while (Cp2 < C) Cp2 <<= 1;
-    const size_t dyn = (size_t)Cp2 * 8;
-    hipFuncSetAttribute((const void*)sort_bprime, hipFuncAttributeMaxDynamicSharedMemorySize, (int)dyn);
-    hipLaunchKernelGGL(sort_bprime, dim3(g.B * g.Hq), dim3(1024), dyn, st, bc, order, C, Cp2);
+      launch_prep<128>(g, kc, bc, planes, t1, st);
   }
   if (g.io == 0) {
     if (g.d == 64)
-      launch_st_d<float, 64>(g, q, Dw, Uw, planes, bc, order, sel_idx, sel_score, st);
+      launch_st_d<float, 64>(g, q, Dw, Uw, planes, t1, theta, bc, sel_idx, sel_score, st);
     else
-      launch_st_d<float, 128>(g, q, Dw, Uw, planes, bc, order, sel_idx, sel_score, st);
+      launch_st_d<float, 128>(g, q, Dw, Uw, planes, t1, theta, bc, sel_idx, sel_score, st);
   } else {
     if (g.d == 64)
-      launch_st_d<bf16_t, 64>(g, q, Dw, Uw, planes, bc, order, sel_idx, sel_score, st);
+      launch_st_d<bf16_t, 64>(g, q, Dw, Uw, planes, t1, theta, bc, sel_idx, sel_score, st);
     else
-      launch_st_d<bf16_t, 128>(g, q, Dw, Uw, planes, bc, order, sel_idx, sel_score, st);
+      launch_st_d<bf16_t, 128>(g, q, Dw, Uw, planes, t1, theta, bc, sel_idx, sel_score, st);
   }
   return hipGetLastError();
 }
