@@ -27,6 +27,7 @@
 //   stored in MFMA operand order, so staging is a copy and an operand is one 16-byte
 //   LDS read.
 #include <algorithm>
+#include <type_traits>
 
 #include "hils_common.h"
 #include "kernels.h"
@@ -146,7 +147,7 @@ HILS_DEV void flush(float& ls, int& li, float& bs, int& bi, int& f0, int& f1, fl
 template <int X>
 HILS_DEV float cxf(float s, int j, bool keep_max) {
   const float p = __int_as_float(xlane<X>(__float_as_int(s), j));
-  return keep_max ? fmaxf(s, p) : fminf(s, p);
+  return (p > s) == keep_max ? p : s;
 }
 
 // bitonic sort of one float per lane, descending, within each 32-lane half
@@ -165,7 +166,7 @@ HILS_DEV float sort32f(float s, int j) {
 HILS_DEV float kth_of_pairs(float a, float b, int j, int hf, int K) {
   a = sort32f(a, j);
   b = sort32f(b, j);
-  a = fmaxf(a, __int_as_float(xlane<31>(__float_as_int(b), j)));  // the 32 largest, bitonic
+  a = __builtin_amdgcn_fmed3f(a, __int_as_float(xlane<31>(__float_as_int(b), j)), INFINITY);  // the 32 largest, bitonic
   a = cxf<16>(a, j, (j & 16) == 0);
   a = cxf<8>(a, j, (j & 8) == 0);
   a = cxf<4>(a, j, (j & 4) == 0);
@@ -238,11 +239,22 @@ HILS_DEV void qhat_rows(const IO* __restrict__ q, const IO* __restrict__ Dw, con
 #pragma unroll
     for (int ks = 0; ks < NKS; ++ks) {
       uint16_t dt[NIO][8];
+      float dv[8];
+      {
+        float a4[4], b4[4];
+        const int64_t drow = ((int64_t)hh * r + min(a_row, r - 1)) * D;  // clamped: no divergent loads
+        io_traits<IO>::load4(Dw, drow + kperm(ks, hf, 0), a4);
+        io_traits<IO>::load4(Dw, drow + kperm(ks, hf, 4), b4);
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+          dv[m] = a_row < r ? a4[m] : 0.f;
+          dv[4 + m] = a_row < r ? b4[m] : 0.f;
+        }
+      }
 #pragma unroll
       for (int m = 0; m < 8; ++m) {
-        const float x = a_row < r ? io_traits<IO>::load(Dw, ((int64_t)hh * r + a_row) * D + kperm(ks, hf, m)) : 0.f;
         uint16_t sp[NIO];
-        split_bf16<NIO>(x, sp);
+        split_bf16<NIO>(dv[m], sp);
 #pragma unroll
         for (int j = 0; j < NIO; ++j) dt[j][m] = sp[j];
       }
@@ -276,10 +288,28 @@ HILS_DEV void qhat_rows(const IO* __restrict__ q, const IO* __restrict__ Dw, con
 #pragma unroll
       for (int ks2 = 0; ks2 < 2; ++ks2) {
         uint16_t ut[NIO][8];
+        float uv[8];
+        const int64_t urow = ((int64_t)hh * D + e) * r;
+        if ((r & 3) == 0) {  // 4-aligned rows: two vector loads
+          float a4[4], b4[4];
+          io_traits<IO>::load4(Uw, urow + min(kperm(ks2, hf, 0), r - 4), a4);
+          io_traits<IO>::load4(Uw, urow + min(kperm(ks2, hf, 4), r - 4), b4);
+#pragma unroll
+          for (int m = 0; m < 4; ++m) {
+            uv[m] = kperm(ks2, hf, m) < r ? a4[m] : 0.f;
+            uv[4 + m] = kperm(ks2, hf, 4 + m) < r ? b4[m] : 0.f;
+          }
+        } else {
+#pragma unroll
+          for (int m = 0; m < 8; ++m) {
+            const int a = kperm(ks2, hf, m);
+            const float x = io_traits<IO>::load(Uw, urow + min(a, r - 1));
+            uv[m] = a < r ? x : 0.f;
+          }
+        }
 #pragma unroll
         for (int m = 0; m < 8; ++m) {
-          const int a = kperm(ks2, hf, m);
-          const float x = a < r ? io_traits<IO>::load(Uw, ((int64_t)hh * D + e) * r + a) : 0.f;
+          const float x = uv[m];
           uint16_t sp[NIO];
           split_bf16<NIO>(x, sp);
 #pragma unroll
@@ -316,7 +346,7 @@ constexpr float TH_ABS = 1.0f / 4096.0f;   // bf16 0x3980
 constexpr int TH_EXT = 16;                  // elements of the extension k-step
 
 template <typename IO, int D, bool QCAL>
-__global__ void __launch_bounds__(256, 3) score_threshold(const IO* __restrict__ q, const IO* __restrict__ Dw,
+__global__ void __launch_bounds__(256, 2) score_threshold(const IO* __restrict__ q, const IO* __restrict__ Dw,
                                                           const IO* __restrict__ Uw, const uint16_t* __restrict__ t1,
                                                           float* __restrict__ theta, int H, int N, int C, int K, int r,
                                                           int NB, int items) {
@@ -326,7 +356,10 @@ __global__ void __launch_bounds__(256, 3) score_threshold(const IO* __restrict__
   constexpr int SEGS = DE / 8;
   constexpr int NSEG = ST_TILE * SEGS;
   constexpr int PL = (NSEG + 255) / 256;
-  __shared__ __align__(16) uint16_t kt[2][ST_TILE * LDT];
+  constexpr int TILE_BYTES = 2 * ST_TILE * LDT * 2;
+  constexpr int TOP2_BYTES = 4 * 16 * 2 * 64 * 4;  // per wave, register, top-2 slot, lane
+  __shared__ __align__(16) unsigned char smem[TILE_BYTES > TOP2_BYTES ? TILE_BYTES : TOP2_BYTES];
+  uint16_t(*kt)[ST_TILE * LDT] = reinterpret_cast<uint16_t(*)[ST_TILE * LDT]>(smem);
 
   const int item = remap_xcd(blockIdx.x, items);
   if (item >= items) return;
@@ -417,28 +450,40 @@ __global__ void __launch_bounds__(256, 3) score_threshold(const IO* __restrict__
         const bf16x8_t bk = *reinterpret_cast<const bf16x8_t*>(&kt[buf][ch * LDT + 16 * ks + 8 * hf]);
         acc = mfma32(qa[ks], bk, acc);
       }
-      if (masked) {
+      // top two per lane (m1 >= m2): m2 = median(m1, m2, v), m1 = median(m1, v, +inf)
+      if (!masked) {
+#pragma unroll
+        for (int rr = 0; rr < 16; ++rr) {
+          m2[rr] = __builtin_amdgcn_fmed3f(m1[rr], m2[rr], acc[rr]);
+          m1[rr] = __builtin_amdgcn_fmed3f(m1[rr], acc[rr], INFINITY);
+        }
+      } else {
         const int c = t * ST_TILE + ch;
 #pragma unroll
         for (int rr = 0; rr < 16; ++rr) {
           const int rw = r0 + 32 * w + acc_row(rr, hf);
           const int prow = rw < N ? min(C, rw / 64) : 0;
-          if (c >= prow) acc[rr] = -INFINITY;
+          const float v = c >= prow ? -INFINITY : acc[rr];
+          m2[rr] = __builtin_amdgcn_fmed3f(m1[rr], m2[rr], v);
+          m1[rr] = __builtin_amdgcn_fmed3f(m1[rr], v, INFINITY);
         }
-      }
-#pragma unroll
-      for (int rr = 0; rr < 16; ++rr) {
-        const float v = acc[rr];
-        m2[rr] = fmaxf(m2[rr], fminf(m1[rr], v));
-        m1[rr] = fmaxf(m1[rr], v);
       }
     }
     if (more) store_tile(buf ^ 1);
     __syncthreads();
   }
+  // theta per row: park the top-two values in LDS (the tiles are no longer read) and
+  // reduce one register row-pair at a time
+  float* mm = reinterpret_cast<float*>(smem) + w * (16 * 2 * 64);
 #pragma unroll
   for (int rr = 0; rr < 16; ++rr) {
-    const float th = kth_of_pairs(m1[rr], m2[rr], n, hf, K);
+    mm[(2 * rr) * 64 + lane] = m1[rr];
+    mm[(2 * rr + 1) * 64 + lane] = m2[rr];
+  }
+  __builtin_amdgcn_wave_barrier();
+#pragma unroll 1
+  for (int rr = 0; rr < 16; ++rr) {
+    const float th = kth_of_pairs(mm[(2 * rr) * 64 + lane], mm[(2 * rr + 1) * 64 + lane], n, hf, K);
     const int rw = r0 + 32 * w + acc_row(rr, hf);
     if (n == 0 && rw < N) theta[(int64_t)bh * N + rw] = th;
   }
@@ -446,6 +491,8 @@ __global__ void __launch_bounds__(256, 3) score_threshold(const IO* __restrict__
 
 
 // ------------------------------------------------------------- selection pass
+constexpr int SEL_CAP = 56;  // candidate slots per row in LDS
+
 template <typename IO, int D, int NQ, int NK, bool QCAL>
 __global__ void __launch_bounds__(256, 2) score_topk_kernel(const IO* __restrict__ q, const IO* __restrict__ Dw,
                                                              const IO* __restrict__ Uw,
@@ -461,9 +508,11 @@ __global__ void __launch_bounds__(256, 2) score_topk_kernel(const IO* __restrict
   constexpr int PH = ST_TILE / 2 * NK * SEGS / 256;  // 16-byte prefetch loads per thread per half tile
   __shared__ __align__(16) uint16_t kt[NK][ST_TILE * LDK];   // the current tile; its halves are refilled in turn
   __shared__ float bt[ST_TILE];
-  __shared__ float lsl[4][16][64];              // per-row sorted lists (see below)
-  __shared__ int lil[4][16][64];
-  __shared__ float thl[4][16][2];               // per-row thresholds from the first pass
+  // per-row candidates (score, chunk); the last 256 entries are per-lane sinks for
+  // the stores of lanes whose score did not pass
+  __shared__ float cs[ST_ROWS * SEL_CAP + 256];
+  __shared__ uint16_t ci[ST_ROWS * SEL_CAP + 256];
+  __shared__ int fls[4][16][2];
 
   const int item = remap_xcd(blockIdx.x, items);
   if (item >= items) return;
@@ -496,25 +545,54 @@ __global__ void __launch_bounds__(256, 2) score_topk_kernel(const IO* __restrict
     for (int j = 0; j < NQ; ++j) qb[j][ks] = pack8(t[j]);
   });
 
-  // ---- per-row top-K state: register rr holds rows acc_row(rr, 0) (lanes 0..31) and
-  // acc_row(rr, 1) (lanes 32..63) of this wave.  Lane j of a half holds buffer slot j
-  // (bs, bi) of its row in registers; the row's sorted list (lane j = j-th best) lives
-  // in LDS (lsl, lil) and is only touched when a buffer is merged.  ts = the K-th best
-  // score so far, never below the row's threshold.
-  float bs[16], ts[16];
-  int bi[16], ff[16];  // ff: wave-uniform buffer fills, lanes 0..31 in bits 0..7, lanes 32..63 in bits 8..15
+  // ---- per-row state: register rr holds rows acc_row(rr, 0) (lanes 0..31) and
+  // acc_row(rr, 1) (lanes 32..63) of this wave.  ts = the row's running threshold
+  // (starts at theta_i; raised to the K-th best when its list is compacted); f0 / f1
+  // = wave-uniform candidate counts of the two rows.  A score s >= ts is appended to
+  // the row's LDS list; a list that would overflow is sorted, cut to its best K and
+  // merged with the new candidates (settle).
+  float ts[16];
+  int ff[16];  // fills: row of lanes 0..31 in bits 0..7, row of lanes 32..63 in bits 8..15
+  const int row_base = (32 * w + 4 * hf) * SEL_CAP;  // + acc_row(rr, 0) * SEL_CAP: this lane's row of register rr
+  const int sink = ST_ROWS * SEL_CAP + tid;
 #pragma unroll
   for (int rr = 0; rr < 16; ++rr) {
     const int rw = r0 + 32 * w + acc_row(rr, hf);
-    const float th = rw < N ? theta[(int64_t)bh * N + rw] : -INFINITY;
-    ts[rr] = th;
-    bs[rr] = -INFINITY;
-    bi[rr] = 0x7fffffff;
+    ts[rr] = rw < N ? theta[(int64_t)bh * N + rw] : -INFINITY;
     ff[rr] = 0;
-    lsl[w][rr][lane] = -INFINITY;
-    lil[w][rr][lane] = 0x7fffffff;
-    if (n == 0) thl[w][rr][hf] = th;
   }
+
+  // Sort the candidates of row-register rr (each half its own row; fa / fb entries),
+  // keep the best K (lane j = j-th best), merge (ns, nc) into them and write the result
+  // back as the list's first entries.  Raises t_s to the K-th best; updates fa / fb.
+  auto settle = [&](int rr, float& t_s, int& fa, int& fb, float ns, int nc, bool merge_new, float& ls, int& li) {
+    const int base = (32 * w + acc_row(rr, hf)) * SEL_CAP;
+    const int fill = hf ? fb : fa;
+    float xs = -INFINITY, ys = -INFINITY;
+    int xi = 0x7fffffff, yi = 0x7fffffff;
+    if (n < fill) {
+      xs = cs[base + n];
+      xi = ci[base + n];
+    }
+    if (n + 32 < fill) {
+      ys = cs[base + n + 32];
+      yi = ci[base + n + 32];
+    }
+    sort32(xs, xi, n);
+    merge_into(xs, xi, ys, yi, n, K);
+    if (merge_new) merge_into(xs, xi, ns, nc, n, K);
+    if (n < K) {
+      cs[base + n] = xs;
+      ci[base + n] = (uint16_t)xi;
+    }
+    const uint64_t vm = __ballot(xi != 0x7fffffff);
+    fa = __popc((uint32_t)vm);
+    fb = __popc((uint32_t)(vm >> 32));
+    const float k0 = readlane_f(xs, K - 1), k1 = readlane_f(xs, 32 + K - 1);
+    t_s = fmaxf(t_s, hf ? k1 : k0);  // -inf (fewer than K) keeps the threshold
+    ls = xs;
+    li = xi;
+  };
 
   const int64_t PL = (int64_t)(items / NB) * C * D;    // elements per plane: B*H*C*D
   const float* bcb = bc + (int64_t)bh * C;
@@ -538,16 +616,6 @@ __global__ void __launch_bounds__(256, 2) score_topk_kernel(const IO* __restrict
       const int c = t * ST_TILE + 32 * part + tid;
       pb = c < Pmax ? bcb[c] : 0.f;
     }
-  };
-  // merge row-register rr's buffer into its LDS list; refresh ts
-  auto flush_rr = [&](int rr, float& b_s, int& b_i, int& bff, float& t_s, int& t_i) {
-    float ls = lsl[w][rr][lane];
-    int li = lil[w][rr][lane];
-    int bf0 = bff & 0xff, bf1 = bff >> 8;
-    flush(ls, li, b_s, b_i, bf0, bf1, thl[w][rr][hf], t_s, t_i, n, hf, K);
-    bff = 0;
-    lsl[w][rr][lane] = ls;
-    lil[w][rr][lane] = li;
   };
   auto commit = [&](int part) {
 #pragma unroll
@@ -573,7 +641,7 @@ __global__ void __launch_bounds__(256, 2) score_topk_kernel(const IO* __restrict
   for (int t = 0; t < ntiles; ++t) {
     const bool more = t + 1 < ntiles;
     const bool masked = (t + 1) * ST_TILE > Pmin;  // chunks >= Pmin are not past chunks of every row
-#pragma unroll
+#pragma unroll 1
     for (int tt = 0; tt < 2; ++tt) {
       if (more) prefetch(t + 1, tt);
       if (t * ST_TILE + 32 * tt < Pmax) {
@@ -591,8 +659,6 @@ __global__ void __launch_bounds__(256, 2) score_topk_kernel(const IO* __restrict
         }
         const int c = t * ST_TILE + ch;
         const float bprime = bt[ch];
-        // filter against each row's K-th best; append the survivors; overflowing
-        // buffers are handled after the pass (one copy of the merge code)
         auto score_of = [&](float a, int rr) {
           float s = fmaf(a, tau, bprime);
           if (masked) {
@@ -602,73 +668,72 @@ __global__ void __launch_bounds__(256, 2) score_topk_kernel(const IO* __restrict
           }
           return s;
         };
+        // filter against each row's threshold and append the survivors (branch-free
+        // within the wave: lanes that did not pass store to their sink slot)
         uint32_t ovf = 0;
+        auto filter = [&](auto masked_tag) {
+          constexpr bool MASKED = decltype(masked_tag)::value;
 #pragma unroll
-        for (int rr = 0; rr < 16; ++rr) {
-          const float s = score_of(acc[rr], rr);
-          bool pass = s > ts[rr];  // NaN never passes
-          if (__ballot(s == ts[rr])) {
-            const int ti = lil[w][rr][32 * hf + K - 1];
-            pass = pass || (s == ts[rr] && c < ti);
-          }
-          const uint64_t mk = __ballot(pass);
-          if (mk) {
-            int a0 = ff[rr] & 0xff, a1 = ff[rr] >> 8;
-            if (a0 + __popc((uint32_t)mk) > ST_BUF || a1 + __popc((uint32_t)(mk >> 32)) > ST_BUF) {
-              ovf |= 1u << rr;
-            } else {
-              append(bs[rr], bi[rr], a0, a1, s, c, pass, mk, n, hf);
-              ff[rr] = a0 | (a1 << 8);
+          for (int rr = 0; rr < 16; ++rr) {
+            float s = fmaf(acc[rr], tau, bprime);
+            if constexpr (MASKED) {
+              const int rw = r0 + 32 * w + acc_row(rr, hf);
+              const int prow = rw < N ? min(C, rw / 64) : 0;
+              if (c >= prow) s = __builtin_nanf("");
+            }
+            const bool pass = s >= ts[rr];  // NaN never passes
+            const uint64_t mk = __ballot(pass);
+            if (mk) {
+              const uint32_t lo = (uint32_t)mk, hi = (uint32_t)(mk >> 32);
+              const int n0 = __popc(lo), n1 = __popc(hi);
+              const int a0 = ff[rr] & 0xff, a1 = ff[rr] >> 8;
+              if (a0 + n0 > SEL_CAP || a1 + n1 > SEL_CAP) {
+                ovf |= 1u << rr;
+              } else {
+                const int rank = (int)__builtin_amdgcn_mbcnt_hi(hi, __builtin_amdgcn_mbcnt_lo(lo, 0u)) - (hf ? n0 : 0);
+                const int pos = pass ? row_base + acc_row(rr, 0) * SEL_CAP + (hf ? a1 : a0) + rank : sink;
+                cs[pos] = s;
+                ci[pos] = (uint16_t)c;
+                ff[rr] = __builtin_amdgcn_readfirstlane(ff[rr] + n0 + (n1 << 8));
+              }
             }
           }
-        }
-        while (ovf) {
+        };
+        if (masked)
+          filter(std::true_type{});
+        else
+          filter(std::false_type{});
+        while (ovf) {  // rare: lists that would overflow
           const int rr = __builtin_ctz(ovf);
           ovf &= ovf - 1;
-          float wb, wt, wa;
-          int wj, wf;
+          float wt, wa;
+          int wa0, wa1;
           switch (rr) {
 #define HILS_PICK(R) \
   case R:            \
-    wb = bs[R];      \
-    wj = bi[R];      \
-    wf = ff[R];      \
     wt = ts[R];      \
     wa = acc[R];     \
+    wa0 = ff[R] & 0xff; \
+    wa1 = ff[R] >> 8;   \
     break;
             HILS_PICK(0) HILS_PICK(1) HILS_PICK(2) HILS_PICK(3) HILS_PICK(4) HILS_PICK(5) HILS_PICK(6) HILS_PICK(7)
             HILS_PICK(8) HILS_PICK(9) HILS_PICK(10) HILS_PICK(11) HILS_PICK(12) HILS_PICK(13) HILS_PICK(14)
             HILS_PICK(15)
 #undef HILS_PICK
             default:
-              wb = wt = wa = 0.f;
-              wj = wf = 0;
+              wt = wa = 0.f;
+              wa0 = wa1 = 0;
           }
           const float ws = score_of(wa, rr);
-          int wti;
-          flush_rr(rr, wb, wj, wf, wt, wti);
-          const bool pass = better(ws, c, wt, wti);
-          const uint64_t mk = __ballot(pass);
-          int m0 = __popc((uint32_t)mk), m1 = __popc((uint32_t)(mk >> 32));
-          if ((m0 > m1 ? m0 : m1) > ST_BUF) {  // more than a buffer of new candidates: merge them directly
-            float ls = lsl[w][rr][lane];
-            int li = lil[w][rr][lane];
-            merge_into(ls, li, pass ? ws : -INFINITY, pass ? c : 0x7fffffff, n, K);
-            kth(ls, li, hf, K, thl[w][rr][hf], wt, wti);
-            lsl[w][rr][lane] = ls;
-            lil[w][rr][lane] = li;
-          } else if (mk) {
-            int a0 = 0, a1 = 0;
-            append(wb, wj, a0, a1, ws, c, pass, mk, n, hf);
-            wf = a0 | (a1 << 8);
-          }
+          const bool pass = ws >= wt;
+          float ls;
+          int li;
+          settle(rr, wt, wa0, wa1, pass ? ws : -INFINITY, pass ? c : 0x7fffffff, true, ls, li);
           switch (rr) {
 #define HILS_PUT(R) \
   case R:           \
-    bs[R] = wb;     \
-    bi[R] = wj;     \
-    ff[R] = wf;     \
     ts[R] = wt;     \
+    ff[R] = wa0 | (wa1 << 8); \
     break;
             HILS_PUT(0) HILS_PUT(1) HILS_PUT(2) HILS_PUT(3) HILS_PUT(4) HILS_PUT(5) HILS_PUT(6) HILS_PUT(7)
             HILS_PUT(8) HILS_PUT(9) HILS_PUT(10) HILS_PUT(11) HILS_PUT(12) HILS_PUT(13) HILS_PUT(14) HILS_PUT(15)
@@ -683,20 +748,26 @@ __global__ void __launch_bounds__(256, 2) score_topk_kernel(const IO* __restrict
     }
   }
 
-  // ---- final merges and output: lane j of each half writes slot j of its row
+  // ---- final selection and output: lane j of each half writes slot j of its row
+  if (lane == 0) {
 #pragma unroll
-  for (int rr = 0; rr < 16; ++rr) {
-    if (ff[rr] != 0) {
-      int tdummy;
-      flush_rr(rr, bs[rr], bi[rr], ff[rr], ts[rr], tdummy);
+    for (int rr = 0; rr < 16; ++rr) {
+      fls[w][rr][0] = ff[rr] & 0xff;
+      fls[w][rr][1] = ff[rr] >> 8;
     }
+  }
+  __builtin_amdgcn_wave_barrier();
+#pragma unroll 1
+  for (int rr = 0; rr < 16; ++rr) {
+    float dummy = -INFINITY, ls;
+    int fa = fls[w][rr][0], fb = fls[w][rr][1], li;
+    settle(rr, dummy, fa, fb, -INFINITY, 0x7fffffff, false, ls, li);
     const int rw = r0 + 32 * w + acc_row(rr, hf);
     if (rw < N && n < K) {
       const int64_t o = ((int64_t)bh * N + rw) * K + n;
-      const int li = lil[w][rr][lane];
       const bool ok = li != 0x7fffffff;
       sel_idx[o] = ok ? li : -1;
-      sel_score[o] = ok ? lsl[w][rr][lane] : -INFINITY;
+      sel_score[o] = ok ? ls : -INFINITY;
     }
   }
 }
