@@ -30,7 +30,9 @@
 
 namespace hils {
 
-constexpr int AT_ROWS = 128;        // gathered rows per chunk_attend workgroup (4 waves x 32)
+constexpr int AT_ROWS = 128;        // gathered rows per chunk_attend tile (4 waves x 32)
+constexpr int AT_TILES = 4;         // tiles per chunk_attend work item (one K/V staging)
+constexpr int ITEM_ROWS = AT_ROWS * AT_TILES;
 constexpr int HIST_SLICE = 1 << 18; // selection entries per bucket_count / bucket_scatter workgroup
 constexpr int MAX_C = 16384;        // largest chunk count the LDS histograms hold
 
@@ -42,7 +44,7 @@ static size_t al(size_t x) { return (x + 255) / 256 * 256; }
 
 static AttendWs attend_ws(const Geom& g) {
   AttendWs w;
-  const size_t nbk = (size_t)g.B * g.Hkv * g.C();
+  const size_t nbk = (size_t)g.B * g.Hq * g.C();
   const size_t ent = (size_t)g.B * g.Hq * g.N * g.K;
   size_t off = 0;
   w.counts = off;
@@ -72,8 +74,8 @@ __global__ void __launch_bounds__(256) zero_u32(uint32_t* p, int64_t n) {
   for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256) p[i] = 0;
 }
 
-// Selection entries of one (b, kv head) group are contiguous in sel_idx:
-// heads kvh*G .. kvh*G+G-1 of batch b, all rows, all K slots.
+// Buckets are (b, h, chunk), numbered head-major; the selection entries of one
+// (b, h) group (all rows, all K slots) are contiguous in sel_idx.
 __global__ void __launch_bounds__(256) bucket_count(const int32_t* __restrict__ sel, uint32_t* __restrict__ counts,
                                                     int64_t group_len, int slices_per_group, int C) {
   __shared__ uint32_t hist[MAX_C];
@@ -92,7 +94,7 @@ __global__ void __launch_bounds__(256) bucket_count(const int32_t* __restrict__ 
 }
 
 // Single workgroup: boff = exclusive scan of counts, toff = exclusive scan of
-// ceil(count / AT_ROWS).  Both get a final total entry.
+// ceil(count / ITEM_ROWS) (work items).  Both get a final total entry.
 __global__ void __launch_bounds__(1024) bucket_scan(const uint32_t* __restrict__ counts, uint32_t* __restrict__ boff,
                                                     uint32_t* __restrict__ toff, int nbk) {
   __shared__ uint32_t sa[1024], sb[1024];
@@ -102,7 +104,7 @@ __global__ void __launch_bounds__(1024) bucket_scan(const uint32_t* __restrict__
   uint32_t a = 0, b = 0;
   for (int i = beg; i < end; ++i) {
     a += counts[i];
-    b += (counts[i] + AT_ROWS - 1) / AT_ROWS;
+    b += (counts[i] + ITEM_ROWS - 1) / ITEM_ROWS;
   }
   sa[t] = a;
   sb[t] = b;
@@ -119,7 +121,7 @@ __global__ void __launch_bounds__(1024) bucket_scan(const uint32_t* __restrict__
     boff[i] = ra;
     toff[i] = rb;
     ra += counts[i];
-    rb += (counts[i] + AT_ROWS - 1) / AT_ROWS;
+    rb += (counts[i] + ITEM_ROWS - 1) / ITEM_ROWS;
   }
   if (t == 1023) {
     boff[nbk] = sa[t];
@@ -341,97 +343,126 @@ struct partial_t<float> {
 };
 
 // ------------------------------------------------------------- chunk_attend
-// bf16 I/O: gathered query rows and the per-pair outputs go through LDS so that
-// global loads and stores move whole rows (16 bytes per lane, rows contiguous).
+// One work item = up to AT_TILES tiles of 128 gathered rows of one bucket (b, h, c):
+// the chunk's K/V tile is staged into LDS once; then each wave runs its own pipeline
+// over its 32 rows of every tile (no further barriers): the query rows of the next
+// tile are loaded into registers (16 bytes per lane, whole rows) while the current
+// tile is on the MFMA, and the normalised outputs leave through the wave's LDS rows
+// as whole-row 16-byte stores.  Work items run in bucket order, head-major, so the
+// rows gathered at any time come from one head and stay cache-resident.
 template <typename IO, int D>
 __global__ void __launch_bounds__(256, 2) chunk_attend(const IO* __restrict__ q, const IO* __restrict__ k,
                                                        const IO* __restrict__ v, const uint32_t* __restrict__ pairs,
                                                        const uint32_t* __restrict__ boff,
                                                        const uint32_t* __restrict__ toff, void* __restrict__ partial_v,
-                                                       int Hkv, int N, int C, int K, int nbk, int grid_items) {
+                                                       int Hq, int Hkv, int N, int C, int K, int nbk) {
   constexpr int NT = io_traits<IO>::terms;
   constexpr bool STAGE = NT == 1;
-  constexpr int LDQ = D + 8;  // bf16 row stride of the staged rows (16-byte aligned rows)
-  constexpr int SEGS = D / 8; // 16-byte segments per bf16 row
+  constexpr int LDQ = D + 8;   // bf16 row stride of the staged rows (16-byte aligned rows)
+  constexpr int SEGS = D / 8;  // 16-byte segments per bf16 row
+  constexpr int RPL = 64 / SEGS;  // rows covered by one wave-wide 16-byte load
+  constexpr int NLD = 32 / RPL;   // loads per lane for the wave's 32 rows
   using PT = typename partial_t<IO>::type;
   __shared__ KVTile<IO, D, NT> tile;
-  __shared__ uint16_t qs[STAGE ? AT_ROWS * LDQ : 8];
-  __shared__ uint32_t pid[AT_ROWS];
-  const int tix = remap_xcd(blockIdx.x, grid_items);
-  const uint32_t ntiles = toff[nbk];
-  if (tix >= grid_items || (uint32_t)tix >= ntiles) return;
-  // bucket = last index with toff[bk] <= tix
+  __shared__ __align__(16) uint16_t qs[STAGE ? AT_ROWS * LDQ : 8];
+  const int item = blockIdx.x;
+  if ((uint32_t)item >= toff[nbk]) return;
+  // bucket = last index with toff[bk] <= item
   int lo = 0, hi = nbk - 1;
   while (lo < hi) {
     const int mid = (lo + hi + 1) >> 1;
-    if (toff[mid] <= (uint32_t)tix) lo = mid;
+    if (toff[mid] <= (uint32_t)item) lo = mid;
     else hi = mid - 1;
   }
   const int bk = lo;
   const uint32_t count = boff[bk + 1] - boff[bk];
-  const uint32_t first = ((uint32_t)tix - toff[bk]) * AT_ROWS;
-  const int c = bk % C, kvh = (bk / C) % Hkv, b = bk / (C * Hkv);
+  const uint32_t first = ((uint32_t)item - toff[bk]) * ITEM_ROWS;
+  const uint32_t nrows = min((uint32_t)ITEM_ROWS, count - first);
+  const uint32_t* pp = pairs + boff[bk] + first;
+  const int c = bk % C, h = (bk / C) % Hq, b = bk / (C * Hq);
+  const int kvh = h / (Hq / Hkv);
   const int64_t row0 = ((int64_t)b * Hkv + kvh) * N + (int64_t)c * 64;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, hf = lane >> 5;
-  if (tid < AT_ROWS) {
-    const uint32_t p = first + tid;
-    pid[tid] = p < count ? pairs[boff[bk] + p] : 0xffffffffu;
-  }
   stage_kv<IO, D, NT>(tile, k, v, row0, 64, tid, 256);
   __syncthreads();
-  if constexpr (STAGE) {  // gather the query rows, whole rows per 16-byte lane group
-    for (int i = tid; i < AT_ROWS * SEGS; i += 256) {
-      const int r = i / SEGS, sg = i % SEGS;
-      const uint32_t e = pid[r];
-      u32x4_t val = {0u, 0u, 0u, 0u};
-      if (e != 0xffffffffu) val = *reinterpret_cast<const u32x4_t*>(q + (int64_t)(e / (uint32_t)K) * D + 8 * sg);
-      *reinterpret_cast<u32x4_t*>(&qs[r * LDQ + 8 * sg]) = val;
-    }
-    __syncthreads();
-  }
+  const int ntile = (int)((nrows + AT_ROWS - 1) / AT_ROWS);
   const int rl = 32 * w + (lane & 31);
-  const uint32_t e_pair = pid[rl];
-  const bool ok = e_pair != 0xffffffffu;
-  bf16x8_t qb[NT][D / 16];
-  if constexpr (STAGE)
-    lds_q_operand<D>(&qs[rl * LDQ], *reinterpret_cast<bf16x8_t(*)[1][D / 16]>(&qb));
-  else
-    load_q_operand<IO, D, NT>(q, (int64_t)(ok ? e_pair / (uint32_t)K : 0) * D, ok, qb);
-  f32x16_t o[D / 32];
-  float m, l;
-  wave_chunk_attention<IO, D, NT>(tile, qb, 64, o, m, l);
-  const float inv = 1.0f / l;
   if constexpr (STAGE) {
-    // normalised output (fp16) into this wave's own staged rows, then whole-row stores
+    uint16_t* myq = &qs[32 * w * LDQ];   // this wave's 32 staged rows
+    const int lr = lane / SEGS, sg = lane % SEGS;
+    u32x4_t qn[NLD];
+    uint32_t pn[NLD], pc[NLD];
+    auto gather = [&](int j) {
 #pragma unroll
-    for (int dt = 0; dt < D / 32; ++dt)
-#pragma unroll
-      for (int g4 = 0; g4 < 4; ++g4) {
-        const int e = 32 * dt + 8 * g4 + 4 * hf;
-        u32x2_t pk;
-        pk.x = (uint32_t)f32_to_f16(o[dt][4 * g4 + 0] * inv) | ((uint32_t)f32_to_f16(o[dt][4 * g4 + 1] * inv) << 16);
-        pk.y = (uint32_t)f32_to_f16(o[dt][4 * g4 + 2] * inv) | ((uint32_t)f32_to_f16(o[dt][4 * g4 + 3] * inv) << 16);
-        *reinterpret_cast<u32x2_t*>(&qs[rl * LDQ + e]) = pk;
+      for (int u = 0; u < NLD; ++u) {
+        const uint32_t r = (uint32_t)(j * AT_ROWS + 32 * w + RPL * u + lr);
+        pn[u] = r < nrows ? pp[r] : 0xffffffffu;
+        qn[u] = pn[u] != 0xffffffffu
+                    ? *reinterpret_cast<const u32x4_t*>(q + (int64_t)(pn[u] / (uint32_t)K) * D + 8 * sg)
+                    : u32x4_t{0u, 0u, 0u, 0u};
       }
-    __syncthreads();
-    uint16_t* dst = reinterpret_cast<uint16_t*>(partial_v);
-    for (int i = lane; i < 32 * SEGS; i += 64) {
-      const int r = 32 * w + i / SEGS, sg = i % SEGS;
-      const uint32_t e = pid[r];
-      if (e != 0xffffffffu)
-        *reinterpret_cast<u32x4_t*>(dst + ((int64_t)e + e / (uint32_t)K) * D + 8 * sg) =
-            *reinterpret_cast<const u32x4_t*>(&qs[r * LDQ + 8 * sg]);
+    };
+    gather(0);
+    for (int j = 0; j < ntile; ++j) {
+#pragma unroll
+      for (int u = 0; u < NLD; ++u) {
+        *reinterpret_cast<u32x4_t*>(&myq[(RPL * u + lr) * LDQ + 8 * sg]) = qn[u];
+        pc[u] = pn[u];
+      }
+      __builtin_amdgcn_wave_barrier();
+      if (j + 1 < ntile) gather(j + 1);
+      bf16x8_t qb[1][D / 16];
+      lds_q_operand<D>(&myq[(lane & 31) * LDQ], qb);
+      f32x16_t o[D / 32];
+      float m, l;
+      wave_chunk_attention<IO, D, NT>(tile, *reinterpret_cast<bf16x8_t(*)[NT][D / 16]>(&qb), 64, o, m, l);
+      const float inv = 1.0f / l;
+      __builtin_amdgcn_wave_barrier();
+      // normalised output (fp16) over this wave's staged rows, then whole-row stores
+#pragma unroll
+      for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+        for (int g4 = 0; g4 < 4; ++g4) {
+          const int e = 32 * dt + 8 * g4 + 4 * hf;
+          u32x2_t pk;
+          pk.x = (uint32_t)f32_to_f16(o[dt][4 * g4 + 0] * inv) | ((uint32_t)f32_to_f16(o[dt][4 * g4 + 1] * inv) << 16);
+          pk.y = (uint32_t)f32_to_f16(o[dt][4 * g4 + 2] * inv) | ((uint32_t)f32_to_f16(o[dt][4 * g4 + 3] * inv) << 16);
+          *reinterpret_cast<u32x2_t*>(&myq[(lane & 31) * LDQ + e]) = pk;
+        }
+      __builtin_amdgcn_wave_barrier();
+      uint16_t* dst = reinterpret_cast<uint16_t*>(partial_v);
+#pragma unroll
+      for (int u = 0; u < NLD; ++u) {
+        const uint32_t e = pc[u];
+        if (e != 0xffffffffu)
+          *reinterpret_cast<u32x4_t*>(dst + ((int64_t)e + e / (uint32_t)K) * D + 8 * sg) =
+              *reinterpret_cast<const u32x4_t*>(&myq[(RPL * u + lr) * LDQ + 8 * sg]);
+      }
+      __builtin_amdgcn_wave_barrier();
     }
-  } else if (ok) {
-    PT* dst = reinterpret_cast<PT*>(partial_v) + ((int64_t)e_pair + e_pair / (uint32_t)K) * D;
+  } else {
+    for (int j = 0; j < ntile; ++j) {
+      const uint32_t r = (uint32_t)(j * AT_ROWS + rl);
+      const uint32_t e_pair = r < nrows ? pp[r] : 0xffffffffu;
+      const bool ok = e_pair != 0xffffffffu;
+      bf16x8_t qb[NT][D / 16];
+      load_q_operand<IO, D, NT>(q, (int64_t)(ok ? e_pair / (uint32_t)K : 0) * D, ok, qb);
+      f32x16_t o[D / 32];
+      float m, l;
+      wave_chunk_attention<IO, D, NT>(tile, qb, 64, o, m, l);
+      const float inv = 1.0f / l;
+      if (ok) {
+        PT* dst = reinterpret_cast<PT*>(partial_v) + ((int64_t)e_pair + e_pair / (uint32_t)K) * D;
 #pragma unroll
-    for (int dt = 0; dt < D / 32; ++dt)
+        for (int dt = 0; dt < D / 32; ++dt)
 #pragma unroll
-      for (int g4 = 0; g4 < 4; ++g4) {
-        const int e = 32 * dt + 8 * g4 + 4 * hf;
-        *reinterpret_cast<float4*>(dst + e) = make_float4(o[dt][4 * g4] * inv, o[dt][4 * g4 + 1] * inv,
-                                                          o[dt][4 * g4 + 2] * inv, o[dt][4 * g4 + 3] * inv);
+          for (int g4 = 0; g4 < 4; ++g4) {
+            const int e = 32 * dt + 8 * g4 + 4 * hf;
+            *reinterpret_cast<float4*>(dst + e) = make_float4(o[dt][4 * g4] * inv, o[dt][4 * g4 + 1] * inv,
+                                                              o[dt][4 * g4 + 2] * inv, o[dt][4 * g4 + 3] * inv);
+          }
       }
+    }
   }
 }
 
@@ -593,31 +624,29 @@ static hipError_t launch_attend_t(const Geom& g, const void* q, const void* k, c
   uint32_t* pairs = (uint32_t*)(ws + w.pairs);
   void* partial = ws + w.partial;
   const int C = g.C();
-  const int nbk = g.B * g.Hkv * C;
+  const int nbk = g.B * g.Hq * C;
   // zero counts and cursors (contiguous) with a kernel: no memset nodes in captured streams
   const int64_t nz = (int64_t)(w.boff - w.counts) / 4;
   if (nz > 0)
     hipLaunchKernelGGL(zero_u32, dim3((unsigned)std::min<int64_t>((nz + 255) / 256, 4096)), dim3(256), 0, st, counts,
                        nz);
   if (nbk > 0) {
-    const int64_t group_len = (int64_t)g.G() * g.N * g.K;
+    const int64_t group_len = (int64_t)g.N * g.K;
     const int spg = (int)((group_len + HIST_SLICE - 1) / HIST_SLICE);
-    const int ngrp = g.B * g.Hkv;
+    const int ngrp = g.B * g.Hq;
     hipLaunchKernelGGL(bucket_count, dim3(ngrp * spg), dim3(256), 0, st, sel, counts, group_len, spg, C);
     hipLaunchKernelGGL(bucket_scan, dim3(1), dim3(1024), 0, st, counts, boff, toff, nbk);
     hipLaunchKernelGGL(bucket_scatter, dim3(ngrp * spg), dim3(256), 0, st, sel, boff, cursor, pairs, group_len, spg, C);
     if (ev) hipEventRecord(ev[0], st);
-    // tiles <= total pairs / AT_ROWS + number of buckets (host bound, exact count read on the device)
+    // work items <= total pairs / ITEM_ROWS + number of buckets (host bound; the exact count is read on the device)
     // rows of query chunk p (64 of them, fewer in the tail) select min(K, p, C) chunks each
     int64_t pairs_total = 0;
     for (int p = 0; p * 64 < g.N; ++p) pairs_total += (int64_t)std::min(64, g.N - p * 64) * std::min(g.K, std::min(C, p));
     pairs_total *= (int64_t)g.B * g.Hq;
-    const int64_t tiles = (pairs_total + AT_ROWS - 1) / AT_ROWS + nbk;
-    const int grid_items = (int)tiles;
-    const int grid = ((grid_items + 7) / 8) * 8;
+    const int64_t items = std::min<int64_t>((pairs_total + ITEM_ROWS - 1) / ITEM_ROWS + nbk, 0x7fffffff);
     if (pairs_total > 0)
-      hipLaunchKernelGGL((chunk_attend<IO, D>), dim3(grid), dim3(256), 0, st, (const IO*)q, (const IO*)k, (const IO*)v,
-                         pairs, boff, toff, partial, g.Hkv, g.N, C, g.K, nbk, grid_items);
+      hipLaunchKernelGGL((chunk_attend<IO, D>), dim3((unsigned)items), dim3(256), 0, st, (const IO*)q, (const IO*)k,
+                         (const IO*)v, pairs, boff, toff, partial, g.Hq, g.Hkv, g.N, C, g.K, nbk);
     if (ev) hipEventRecord(ev[1], st);
   } else if (ev) {
     hipEventRecord(ev[0], st);
