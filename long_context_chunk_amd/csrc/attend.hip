@@ -365,6 +365,8 @@ __global__ void __launch_bounds__(256, 2) chunk_attend(const IO* __restrict__ q,
   using PT = typename partial_t<IO>::type;
   __shared__ KVTile<IO, D, NT> tile;
   __shared__ __align__(16) uint16_t qs[STAGE ? AT_ROWS * LDQ : 8];
+  __shared__ uint32_t ipid[ITEM_ROWS];  // the item's pair ids (linear selection index) ...
+  __shared__ uint32_t irow[ITEM_ROWS];  // ... and their query rows (pair id / K)
   const int item = blockIdx.x;
   if ((uint32_t)item >= toff[nbk]) return;
   // bucket = last index with toff[bk] <= item
@@ -383,6 +385,11 @@ __global__ void __launch_bounds__(256, 2) chunk_attend(const IO* __restrict__ q,
   const int kvh = h / (Hq / Hkv);
   const int64_t row0 = ((int64_t)b * Hkv + kvh) * N + (int64_t)c * 64;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, hf = lane >> 5;
+  for (int r = tid; r < ITEM_ROWS; r += 256) {
+    const uint32_t e = (uint32_t)r < nrows ? pp[r] : 0xffffffffu;
+    ipid[r] = e;
+    irow[r] = e != 0xffffffffu ? e / (uint32_t)K : 0u;
+  }
   stage_kv<IO, D, NT>(tile, k, v, row0, 64, tid, 256);
   __syncthreads();
   const int ntile = (int)((nrows + AT_ROWS - 1) / AT_ROWS);
@@ -391,24 +398,18 @@ __global__ void __launch_bounds__(256, 2) chunk_attend(const IO* __restrict__ q,
     uint16_t* myq = &qs[32 * w * LDQ];   // this wave's 32 staged rows
     const int lr = lane / SEGS, sg = lane % SEGS;
     u32x4_t qn[NLD];
-    uint32_t pn[NLD], pc[NLD];
+    // rows beyond the item load query row 0 (in bounds) and store nothing
     auto gather = [&](int j) {
 #pragma unroll
       for (int u = 0; u < NLD; ++u) {
-        const uint32_t r = (uint32_t)(j * AT_ROWS + 32 * w + RPL * u + lr);
-        pn[u] = r < nrows ? pp[r] : 0xffffffffu;
-        qn[u] = pn[u] != 0xffffffffu
-                    ? *reinterpret_cast<const u32x4_t*>(q + (int64_t)(pn[u] / (uint32_t)K) * D + 8 * sg)
-                    : u32x4_t{0u, 0u, 0u, 0u};
+        const int r = j * AT_ROWS + 32 * w + RPL * u + lr;
+        qn[u] = *reinterpret_cast<const u32x4_t*>(q + (int64_t)irow[r] * D + 8 * sg);
       }
     };
     gather(0);
     for (int j = 0; j < ntile; ++j) {
 #pragma unroll
-      for (int u = 0; u < NLD; ++u) {
-        *reinterpret_cast<u32x4_t*>(&myq[(RPL * u + lr) * LDQ + 8 * sg]) = qn[u];
-        pc[u] = pn[u];
-      }
+      for (int u = 0; u < NLD; ++u) *reinterpret_cast<u32x4_t*>(&myq[(RPL * u + lr) * LDQ + 8 * sg]) = qn[u];
       __builtin_amdgcn_wave_barrier();
       if (j + 1 < ntile) gather(j + 1);
       bf16x8_t qb[1][D / 16];
@@ -433,26 +434,27 @@ __global__ void __launch_bounds__(256, 2) chunk_attend(const IO* __restrict__ q,
       uint16_t* dst = reinterpret_cast<uint16_t*>(partial_v);
 #pragma unroll
       for (int u = 0; u < NLD; ++u) {
-        const uint32_t e = pc[u];
-        if (e != 0xffffffffu)
-          *reinterpret_cast<u32x4_t*>(dst + ((int64_t)e + e / (uint32_t)K) * D + 8 * sg) =
-              *reinterpret_cast<const u32x4_t*>(&myq[(RPL * u + lr) * LDQ + 8 * sg]);
+        const int r = j * AT_ROWS + 32 * w + RPL * u + lr;
+        const uint32_t e = ipid[r];
+        const u32x4_t val = *reinterpret_cast<const u32x4_t*>(&myq[(RPL * u + lr) * LDQ + 8 * sg]);
+        if (e != 0xffffffffu)  // slot (e mod K) of row e / K, K + 1 slots per row
+          *reinterpret_cast<u32x4_t*>(dst + ((int64_t)e + irow[r]) * D + 8 * sg) = val;
       }
       __builtin_amdgcn_wave_barrier();
     }
   } else {
     for (int j = 0; j < ntile; ++j) {
-      const uint32_t r = (uint32_t)(j * AT_ROWS + rl);
-      const uint32_t e_pair = r < nrows ? pp[r] : 0xffffffffu;
+      const int r = j * AT_ROWS + rl;
+      const uint32_t e_pair = ipid[r];
       const bool ok = e_pair != 0xffffffffu;
       bf16x8_t qb[NT][D / 16];
-      load_q_operand<IO, D, NT>(q, (int64_t)(ok ? e_pair / (uint32_t)K : 0) * D, ok, qb);
+      load_q_operand<IO, D, NT>(q, (int64_t)irow[r] * D, ok, qb);
       f32x16_t o[D / 32];
       float m, l;
       wave_chunk_attention<IO, D, NT>(tile, qb, 64, o, m, l);
       const float inv = 1.0f / l;
       if (ok) {
-        PT* dst = reinterpret_cast<PT*>(partial_v) + ((int64_t)e_pair + e_pair / (uint32_t)K) * D;
+        PT* dst = reinterpret_cast<PT*>(partial_v) + ((int64_t)e_pair + irow[r]) * D;
 #pragma unroll
         for (int dt = 0; dt < D / 32; ++dt)
 #pragma unroll
