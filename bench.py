@@ -16,6 +16,7 @@ Also reported on the same line:
     against full attention).
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-decode] [--no-cpu] [--no-dense]
+                       [--no-prefill] [--copy-calibration]
 """
 from __future__ import annotations
 
@@ -74,32 +75,100 @@ def prefill_counts(w):
     }
 
 
-def stage_roofline(w, cnt, stage_ms, io_bytes=2):
-    """Algorithmic bytes / flops per launch of each prefill stage and its roofline fraction."""
-    d, S = w.d, w.S
-    nbk = w.B * w.Hkv * w.C
-    out = {}
-    # compression: read K and the landmark queries once, write k' (fp32) and b'
-    comp_bytes = (w.B * w.Hkv * w.C * S * d * io_bytes + w.B * w.Hlmk * w.C * d * io_bytes
-                  + w.B * w.Hlmk * w.C * (d + 1) * 4)
-    # chunk attention: per (query, chunk) pair the gathered query row, its pair id and its
-    # fp16 partial output; per bucket one K/V chunk tile
-    ca_bytes = cnt["pairs"] * (d * io_bytes + 4 + d * 2) + nbk * 2 * S * d * io_bytes
-    ca_flops = cnt["pairs"] * 4.0 * S * d
-    st_flops = cnt["score_flops"] + cnt["qcal_flops"]
-    for name, kind, amount in (("compress", "hbm", comp_bytes), ("score_topk", "mfma", st_flops),
-                               ("chunk_attend", "hbm", ca_bytes)):
-        ms = stage_ms[name]
-        if kind == "hbm":
-            ach = amount / (ms * 1e-3) / 1e9
-            out[name] = {"bound": "hbm", "achieved": ach, "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                         "frac": ach / PEAK_HBM_GBS, "algorithmic_bytes": amount, "ms": ms}
-        else:
-            ach = amount / (ms * 1e-3) / 1e12
-            out[name] = {"bound": "mfma", "achieved": ach, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                         "frac": ach / PEAK_BF16_TFLOPS, "algorithmic_flops": amount, "ms": ms}
-    out["chunk_attend"]["mfma_frac_algorithmic"] = ca_flops / (stage_ms["chunk_attend"] * 1e-3) / 1e12 / PEAK_BF16_TFLOPS
+# algorithmic work of each prefill kernel: ("hbm", bytes) or ("mfma", flops) per launch
+def kernel_work(w, cnt, io_bytes=2):
+    d, S, K = w.d, w.S, w.K
+    rows = w.B * w.Hq * w.N
+    entries = rows * K
+    return {
+        # K and the landmark queries read once, k' (fp32) and b' written
+        "compress": ("hbm", w.B * w.Hkv * w.C * S * d * io_bytes + w.B * w.Hlmk * w.C * d * io_bytes
+                     + w.B * w.Hlmk * w.C * (d + 1) * 4),
+        # one q^ . k' product per (query, past chunk) + Q-Cal
+        "score_threshold": ("mfma", cnt["score_flops"] + cnt["qcal_flops"]),
+        "score_select": ("mfma", cnt["score_flops"] + cnt["qcal_flops"]),
+        # selection read twice (count, scatter), pair ids written
+        "bucket": ("hbm", entries * 4 * 3),
+        # per (query, chunk) pair: the gathered query row and the fp16 chunk output; each
+        # (batch, KV head, chunk) K/V tile once
+        "chunk_attend": ("hbm", cnt["pairs"] * (d * io_bytes + d * 2) + w.B * w.Hkv * w.C * 2 * S * d * io_bytes),
+        # per row: q, the own chunk's K/V (once per head and chunk), the fp16 output slot and the LSE
+        "own_attend": ("hbm", rows * d * io_bytes + w.B * w.Hq * w.N * d * io_bytes * 2 + rows * (d * 2 + 4)),
+        # per row: its selected chunk outputs + own output (fp16), their scores, the output row
+        "fuse": ("hbm", (cnt["pairs"] + rows) * d * 2 + cnt["pairs"] * 4 + rows * 4 + rows * d * io_bytes),
+    }
+
+
+def roofline_of(kind, amount, ms):
+    if kind == "hbm":
+        ach = amount / (ms * 1e-3) / 1e9
+        return {"bound": "hbm", "achieved": ach, "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": ach / PEAK_HBM_GBS,
+                "algorithmic_bytes": amount, "ms": ms}
+    ach = amount / (ms * 1e-3) / 1e12
+    return {"bound": "mfma", "achieved": ach, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+            "frac": ach / PEAK_BF16_TFLOPS, "algorithmic_flops": amount, "ms": ms}
+
+
+def stage_roofline(w, cnt, stage_ms):
+    work = kernel_work(w, cnt)
+    out = {name: roofline_of(kind, amount, stage_ms[name]) for name, (kind, amount) in work.items()
+           if stage_ms.get(name, 0) > 0}
+    if "chunk_attend" in out:
+        out["chunk_attend"]["mfma_frac_algorithmic"] = (cnt["pairs"] * 4.0 * w.S * w.d / (stage_ms["chunk_attend"] * 1e-3)
+                                                        / 1e12 / PEAK_BF16_TFLOPS)
     return out
+
+
+# kernel (stage) -> the source file whose hash must match the profiled one
+KERNEL_SOURCES = {
+    "compress": "compress.hip", "score_threshold": "score_topk.hip", "score_select": "score_topk.hip",
+    "bucket": "attend.hip", "chunk_attend": "attend.hip", "own_attend": "attend.hip", "fuse": "attend.hip",
+    "decode_scan": "decode.hip", "decode_topk": "decode.hip", "decode_attend": "decode.hip", "decode_combine": "decode.hip",
+}
+
+
+def source_hash(stage):
+    import hashlib
+    src = os.path.join(ROOT, "long_context_chunk_amd", "csrc", KERNEL_SOURCES[stage])
+    h = hashlib.sha256()
+    for f in (src, os.path.join(ROOT, "long_context_chunk_amd", "csrc", "hils_common.h")):
+        h.update(open(f, "rb").read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(stage, workload):
+    """HBM bytes per launch from the committed rocprofv3 counter summary (FETCH_SIZE +
+    WRITE_SIZE, each scaled by the same counter's reading for a plain copy of known size),
+    or None when there is none or the kernel source changed since it was taken."""
+    path = os.path.join(ROOT, "profiles", "traffic_%s.txt" % workload)
+    if not os.path.exists(path):
+        return None
+    vals, kern = {}, {}
+    for line in open(path):
+        t = line.split()
+        if not t or t[0].startswith("#"):
+            continue
+        if t[0] == "kernel" and len(t) >= 8:
+            kern[t[1]] = {"fetch_kib": float(t[3]), "write_kib": float(t[5]), "src": t[7]}
+        elif len(t) == 2:
+            vals[t[0]] = float(t[1])
+    k = kern.get(stage)
+    if k is None or k["src"] != source_hash(stage) or "copy_bytes" not in vals:
+        return None
+    fs = vals["copy_bytes"] / (vals["copy_fetch_kib"] * 1024.0)
+    ws = vals["copy_bytes"] / (vals["copy_write_kib"] * 1024.0)
+    return k["fetch_kib"] * 1024.0 * fs + k["write_kib"] * 1024.0 * ws
+
+
+def copy_calibration(nbytes=2 << 30, reps=3):
+    """A plain device copy of known size, for scaling the FETCH_SIZE / WRITE_SIZE counters."""
+    import torch
+    src = torch.ones(nbytes // 4, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(reps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes": nbytes, "reps": reps}), flush=True)
 
 
 def run_prefill(w, steps, warmup, seed):
@@ -287,7 +356,8 @@ def run_decode(wd, steps, warmup, seed):
         "K": wd.K, "us_per_step": us, "stages_us": {k_: v_ * 1e3 for k_, v_ in stages.items()},
         "one_off_compress_ms": comp_ms,
         "roofline": {"bound": "hbm", "achieved": scan_gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                     "frac": scan_gbs / PEAK_HBM_GBS, "kernel": "decode_scan", "traffic": None},
+                     "frac": scan_gbs / PEAK_HBM_GBS, "kernel": "decode_scan",
+                     "traffic": measured_traffic("decode_scan", wd.name)},
         "step_hbm": {"algorithmic_bytes": total_bytes, "achieved_GBs": step_gbs, "frac": step_gbs / PEAK_HBM_GBS,
                      "kv_union_bytes": kv_bytes, "kprime_bytes": scan_bytes},
         "dense_kv_bytes": dense_kv, "dense_us_at_hbm_peak": dense_kv / (PEAK_HBM_GBS * 1e9) * 1e6,
@@ -305,6 +375,9 @@ def main():
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-dense", action="store_true")
     ap.add_argument("--no-parity", action="store_true")
+    ap.add_argument("--no-prefill", action="store_true", help="decode step only (for profiling it alone)")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain 2 GiB device copy (counter calibration for the traffic figures)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: the HiLS path here runs on a single MI355X "
@@ -313,14 +386,21 @@ def main():
     import torch
     import synth
     from long_context_chunk_amd import hils
+    if args.copy_calibration:
+        copy_calibration()
+        return
     hils.load()
     assert torch.cuda.is_available()
     w = synth.WORKLOADS[args.workload]
     seed = synth.BASE_SEED + 5
+    if args.no_prefill:
+        wd = synth.WORKLOADS[args.decode_workload]
+        print(json.dumps({"decode": run_decode(wd, max(args.steps, 20), args.warmup, seed + 1)}), flush=True)
+        return
     res = run_prefill(w, args.steps, args.warmup, seed)
     cnt = prefill_counts(w)
     roof = stage_roofline(w, cnt, res["stages"])
-    dom = max(("compress", "score_topk", "chunk_attend"), key=lambda s_: res["stages"][s_])
+    dom = max(roof, key=lambda s_: roof[s_]["ms"])
     total_flops = cnt["compress_flops"] + cnt["qcal_flops"] + cnt["score_flops"] + cnt["intra_flops"]
     line = {
         "metric": METRIC,
@@ -331,7 +411,7 @@ def main():
         "data": "synthetic (seeded counter-based generator; planted-direction needle chunks and queries)",
         "config": {"workload": w.name, "B": w.B, "Hq": w.Hq, "Hkv": w.Hkv, "d": w.d, "seq_len": w.N, "S": w.S,
                    "K": w.K, "qcal_rank": w.qcal_rank, "compression": "in the same call"},
-        "roofline": dict(roof[dom], kernel=dom, traffic=None),
+        "roofline": dict(roof[dom], kernel=dom, traffic=measured_traffic(dom, w.name)),
         "stages_ms": res["stages"],
         "stage_rooflines": roof,
         "algorithmic_tflops_per_step": total_flops / 1e12,

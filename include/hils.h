@@ -121,12 +121,15 @@ int hils_attn_prefill(const hils_dims_t* dims, const void* q, const void* k, con
 
 /*
  * hils_attn_prefill for measurement: the same work, plus the GPU time of each
- * stage in milliseconds, taken with HIP events on `stream`, in stage_ms[5]
- * (a HOST array): [0] landmark compression (0 if lmk_q == NULL), [1] scoring and
- * top-K, [2] bucketing of (query, chunk) pairs, [3] intra-chunk attention of
- * the selected chunks, [4] own-chunk attention and fusion.  Unlike every other
- * call it synchronises with the stream before returning.
+ * stage in milliseconds, taken with HIP events on `stream`, in
+ * stage_ms[HILS_PREFILL_STAGES] (a HOST array): [0] landmark compression (0 if
+ * lmk_q == NULL), [1] k' preparation and the threshold pass of the top-K,
+ * [2] scoring and top-K selection, [3] bucketing of (query, chunk) pairs,
+ * [4] intra-chunk attention of the selected chunks, [5] own-chunk attention,
+ * [6] fusion.  Unlike every other call it synchronises with the stream before
+ * returning.
  */
+#define HILS_PREFILL_STAGES 7
 int hils_attn_prefill_timed(const hils_dims_t* dims, const void* q, const void* k, const void* v, const void* lmk_q,
                             float* kc, float* bc, const void* qcal_D, const void* qcal_U, int32_t* sel_idx_out,
                             float* sel_score_out, void* o, void* ws, size_t ws_bytes, void* stream,

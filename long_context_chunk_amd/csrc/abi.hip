@@ -155,7 +155,7 @@ int hils_chunk_score_topk(const hils_dims_t* dims, const void* q, const void* qc
 
 namespace {
 
-// hils_attn_prefill with optional stage timing (stage_ms: 5 host floats, or NULL)
+// hils_attn_prefill with optional stage timing (stage_ms: HILS_PREFILL_STAGES host floats, or NULL)
 int run_prefill(const hils_dims_t* dims, const void* q, const void* k, const void* v, const void* lmk_q, float* kc,
                 float* bc, const void* qcal_D, const void* qcal_U, int32_t* sel_idx_out, float* sel_score_out, void* o,
                 void* ws, size_t ws_bytes, void* stream, float* stage_ms) {
@@ -175,10 +175,11 @@ int run_prefill(const hils_dims_t* dims, const void* q, const void* k, const voi
   int32_t* sel = sel_idx_out ? sel_idx_out : (int32_t*)(base + w.sel_idx);
   float* scr = sel_score_out ? sel_score_out : (float*)(base + w.sel_score);
   hipStream_t st = (hipStream_t)stream;
-  hipEvent_t ev[6] = {};
+  constexpr int NS = HILS_PREFILL_STAGES;
+  hipEvent_t ev[NS + 1] = {};
   hipError_t e = hipSuccess;
   if (stage_ms) {
-    for (int i = 0; i < 6 && e == hipSuccess; ++i) e = hipEventCreate(&ev[i]);
+    for (int i = 0; i <= NS && e == hipSuccess; ++i) e = hipEventCreate(&ev[i]);
     if (e == hipSuccess) e = hipEventRecord(ev[0], st);
   }
   if (e == hipSuccess && lmk_q && g.C() > 0) {
@@ -186,15 +187,15 @@ int run_prefill(const hils_dims_t* dims, const void* q, const void* k, const voi
   }
   if (e == hipSuccess && stage_ms) e = hipEventRecord(ev[1], st);
   if (e == hipSuccess)
-    e = hils::launch_score_topk(g, q, qcal_D, qcal_U, kcp, bcp, sel, scr, base + w.score, w.attend - w.score, st);
-  if (e == hipSuccess && stage_ms) e = hipEventRecord(ev[2], st);
+    e = hils::launch_score_topk(g, q, qcal_D, qcal_U, kcp, bcp, sel, scr, base + w.score, w.attend - w.score, st,
+                                stage_ms ? ev + 2 : nullptr);
   if (e == hipSuccess)
     e = hils::launch_prefill_attend(g, q, k, v, sel, scr, o, base + w.attend, w.total - w.attend, st,
-                                    stage_ms ? ev + 3 : nullptr);
+                                    stage_ms ? ev + 4 : nullptr);
   if (stage_ms) {
-    if (e == hipSuccess) e = hipEventSynchronize(ev[5]);
-    for (int i = 0; i < 5 && e == hipSuccess; ++i) e = hipEventElapsedTime(&stage_ms[i], ev[i], ev[i + 1]);
-    for (int i = 0; i < 6; ++i)
+    if (e == hipSuccess) e = hipEventSynchronize(ev[NS]);
+    for (int i = 0; i < NS && e == hipSuccess; ++i) e = hipEventElapsedTime(&stage_ms[i], ev[i], ev[i + 1]);
+    for (int i = 0; i <= NS; ++i)
       if (ev[i]) hipEventDestroy(ev[i]);
   }
   if (e != hipSuccess) return hip_fail(e, "hils_attn_prefill");

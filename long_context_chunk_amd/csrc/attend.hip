@@ -658,11 +658,12 @@ static hipError_t launch_attend_t(const Geom& g, const void* q, const void* k, c
   float* lse = (float*)(ws + w.lse);
   hipLaunchKernelGGL((own_attend<IO, D>), dim3(g.B * g.Hq * NQC), dim3(128), 0, st, (const IO*)q, (const IO*)k,
                      (const IO*)v, partial, lse, g.Hq, g.Hkv, g.N, g.K, NQC);
+  if (ev) hipEventRecord(ev[2], st);
   const int64_t rows = (int64_t)g.B * g.Hq * g.N;
   const int64_t nwg = (rows + 4 * FZ_ROWS - 1) / (4 * FZ_ROWS);
   hipLaunchKernelGGL((fuse<IO, D>), dim3((unsigned)nwg), dim3(256), 0, st, scr, (const float*)lse,
                      (const void*)partial, (IO*)o, g.N, C, g.K, rows);
-  if (ev) hipEventRecord(ev[2], st);
+  if (ev) hipEventRecord(ev[3], st);
   return hipGetLastError();
 }
 

@@ -18,13 +18,14 @@ hipError_t launch_compress(int io, const void* k, const void* lmk, float* kc, fl
 
 // Chunk scores and per-row top-K for all N queries of every (b, h).
 size_t score_workspace_bytes(const Geom& g);
+// ev (nullable): two events recorded after the threshold pass and after the selection pass.
 hipError_t launch_score_topk(const Geom& g, const void* q, const void* D, const void* U, const float* kc,
                              const float* bc, int32_t* sel_idx, float* sel_score, void* ws, size_t ws_bytes,
-                             hipStream_t st);
+                             hipStream_t st, hipEvent_t* ev = nullptr);
 
 // Intra-chunk attention and fusion for prefill, given the selection.
 size_t attend_workspace_bytes(const Geom& g);
-// ev (nullable): three events recorded after bucketing, chunk attention and fusion.
+// ev (nullable): four events recorded after bucketing, chunk attention, own-chunk attention and fusion.
 hipError_t launch_prefill_attend(const Geom& g, const void* q, const void* k, const void* v, const int32_t* sel_idx,
                                  const float* sel_score, void* o, void* ws, size_t ws_bytes, hipStream_t st,
                                  hipEvent_t* ev = nullptr);

@@ -858,12 +858,14 @@ size_t score_workspace_bytes(const Geom& g) { return score_ws(g).total; }
 
 template <typename IO, int D, int NQ, int NK, bool QCAL>
 static void launch_st(const Geom& g, const void* q, const void* Dw, const void* Uw, const uint16_t* planes,
-                      const uint16_t* t1, float* theta, const float* bc, int32_t* si, float* ss, hipStream_t st) {
+                      const uint16_t* t1, float* theta, const float* bc, int32_t* si, float* ss, hipStream_t st,
+                      hipEvent_t* ev) {
   const int NB = (g.N + ST_ROWS - 1) / ST_ROWS;
   const int items = g.B * g.Hq * NB;
   const int grid = ((items + 7) / 8) * 8;
   hipLaunchKernelGGL((score_threshold<IO, D, QCAL>), dim3(grid), dim3(256), 0, st, (const IO*)q, (const IO*)Dw,
                      (const IO*)Uw, t1, theta, g.Hq, g.N, g.C(), g.K, g.r, NB, items);
+  if (ev) hipEventRecord(ev[0], st);
   hipLaunchKernelGGL((score_topk_kernel<IO, D, NQ, NK, QCAL>), dim3(grid), dim3(256), 0, st, (const IO*)q,
                      (const IO*)Dw, (const IO*)Uw, planes, bc, (const float*)theta, si, ss, g.Hq, g.N, g.C(), g.K,
                      g.r, NB, items);
@@ -871,12 +873,13 @@ static void launch_st(const Geom& g, const void* q, const void* Dw, const void* 
 
 template <typename IO, int D>
 static void launch_st_d(const Geom& g, const void* q, const void* Dw, const void* Uw, const uint16_t* planes,
-                        const uint16_t* t1, float* theta, const float* bc, int32_t* si, float* ss, hipStream_t st) {
+                        const uint16_t* t1, float* theta, const float* bc, int32_t* si, float* ss, hipStream_t st,
+                        hipEvent_t* ev) {
   constexpr bool F32 = io_traits<IO>::terms == 3;
   if (g.r > 0)
-    launch_st<IO, D, F32 ? 3 : 2, F32 ? 3 : 2, true>(g, q, Dw, Uw, planes, t1, theta, bc, si, ss, st);
+    launch_st<IO, D, F32 ? 3 : 2, F32 ? 3 : 2, true>(g, q, Dw, Uw, planes, t1, theta, bc, si, ss, st, ev);
   else
-    launch_st<IO, D, F32 ? 3 : 1, F32 ? 3 : 2, false>(g, q, Dw, Uw, planes, t1, theta, bc, si, ss, st);
+    launch_st<IO, D, F32 ? 3 : 1, F32 ? 3 : 2, false>(g, q, Dw, Uw, planes, t1, theta, bc, si, ss, st, ev);
 }
 
 template <int D>
@@ -893,7 +896,7 @@ static void launch_prep(const Geom& g, const float* kc, const float* bc, uint16_
 
 hipError_t launch_score_topk(const Geom& g, const void* q, const void* Dw, const void* Uw, const float* kc,
                              const float* bc, int32_t* sel_idx, float* sel_score, void* ws, size_t ws_bytes,
-                             hipStream_t st) {
+                             hipStream_t st, hipEvent_t* ev) {
   if (ws_bytes < score_workspace_bytes(g)) return hipErrorInvalidValue;
   const ScoreWs w = score_ws(g);
   uint16_t* planes = (uint16_t*)((char*)ws + w.planes);
@@ -907,15 +910,16 @@ hipError_t launch_score_topk(const Geom& g, const void* q, const void* Dw, const
   }
   if (g.io == 0) {
     if (g.d == 64)
-      launch_st_d<float, 64>(g, q, Dw, Uw, planes, t1, theta, bc, sel_idx, sel_score, st);
+      launch_st_d<float, 64>(g, q, Dw, Uw, planes, t1, theta, bc, sel_idx, sel_score, st, ev);
     else
-      launch_st_d<float, 128>(g, q, Dw, Uw, planes, t1, theta, bc, sel_idx, sel_score, st);
+      launch_st_d<float, 128>(g, q, Dw, Uw, planes, t1, theta, bc, sel_idx, sel_score, st, ev);
   } else {
     if (g.d == 64)
-      launch_st_d<bf16_t, 64>(g, q, Dw, Uw, planes, t1, theta, bc, sel_idx, sel_score, st);
+      launch_st_d<bf16_t, 64>(g, q, Dw, Uw, planes, t1, theta, bc, sel_idx, sel_score, st, ev);
     else
-      launch_st_d<bf16_t, 128>(g, q, Dw, Uw, planes, t1, theta, bc, sel_idx, sel_score, st);
+      launch_st_d<bf16_t, 128>(g, q, Dw, Uw, planes, t1, theta, bc, sel_idx, sel_score, st, ev);
   }
+  if (ev) hipEventRecord(ev[1], st);
   return hipGetLastError();
 }
 

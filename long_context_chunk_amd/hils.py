@@ -21,7 +21,7 @@ OK, E_INVAL, E_UNSUPPORTED, E_WORKSPACE, E_HIP = 0, -1, -2, -3, -4
 
 SYMBOLS = ("hils_workspace_bytes", "hils_landmark_compress", "hils_chunk_score_topk", "hils_attn_prefill",
            "hils_attn_prefill_timed", "hils_attn_decode", "hils_attn_decode_timed", "hils_last_error")
-STAGES = ("compress", "score_topk", "bucket", "chunk_attend", "own_fuse")
+STAGES = ("compress", "score_threshold", "score_select", "bucket", "chunk_attend", "own_attend", "fuse")
 DECODE_STAGES = ("scan", "topk", "attend", "combine")
 
 
@@ -172,7 +172,7 @@ def attn_prefill(dm: Dims, q, k, v, o, ws, lmk_q=None, kc=None, bc=None, qcal_D=
     args = (ctypes.byref(dm), _p(q), _p(k), _p(v), _p(lmk_q), _p(kc), _p(bc), _p(qcal_D), _p(qcal_U), _p(sel_idx),
             _p(sel_score), _p(o), _p(ws), ws.numel(), _stream())
     if timed:
-        ms = (ctypes.c_float * 5)()
+        ms = (ctypes.c_float * len(STAGES))()
         _check(load().hils_attn_prefill_timed(*args, ms))
         return dict(zip(STAGES, [float(x) for x in ms]))
     _check(load().hils_attn_prefill(*args))
