@@ -5,25 +5,26 @@
 // keep the K best (ties -> lower chunk id).  (aitrends.kr article,
 // "Methodology": the score formula, the calculation flow and the Q-Cal module.)
 //
-// Two passes over the past chunks, both on v_mfma_f32_32x32x16_bf16: one workgroup
-// = 128 consecutive queries of one (batch, head), wave w owns 32 of them as the M
-// dimension, the chunks are the N dimension (accumulator register r of a lane holds
-// one chunk's score for one query row; the 32 lanes of a half-wave cover 32 chunks of
-// one row), and k' tiles of 64 chunks are staged through LDS for the four waves.
+// Two passes over the past chunks, both on v_mfma_f32_32x32x16_bf16, one workgroup per
+// 128 consecutive queries of one (batch, head) (32 per wave), with k' tiles staged
+// through LDS and shared by the four waves:
 //
-//   1. score_threshold: one bf16 product per score, bf16(q^/sqrt(d)) . bf16(k'_c),
-//      with b'_c and an error allowance e_i |k'_c| folded into one extra MFMA k-step,
-//      so every value is at most the fp32-accurate score of pass 2.  Each lane keeps
-//      the two largest values of its column of chunks; the K-th largest of these 64
-//      values of distinct chunks is a threshold theta_i that the row's K-th best
-//      score can not be below.
-//   2. score_topk_kernel: the scores to ~2^-17 relative (k' split into bf16 hi + lo
-//      terms, q^ too when it is not exactly bf16), tested against the row's running
-//      K-th best, which starts at theta_i, so only about K candidates per row reach
-//      the selection.  Candidates are appended to a 31-slot buffer per row (one lane
-//      permute); a full buffer is bitonic-sorted and merged into the row's sorted
-//      list (lane exchanges by DPP and swizzle).
-//   k' is rewritten once per call into bf16 term planes whose 16-element k-blocks are
+//   1. score_threshold (queries = M, chunks = N: accumulator register r of a lane holds
+//      one chunk's score for one row; the 32 lanes of a half-wave cover 32 chunks of
+//      that row): one bf16 product per score, bf16(q^/sqrt(d)) . bf16(k'_c), with b'_c
+//      and an error allowance e_i |k'_c| folded into one extra MFMA k-step, so every
+//      value is at most the fp32-accurate score of pass 2.  Each lane keeps the two
+//      largest values of its column of chunks; the K-th largest of these 64 values of
+//      distinct chunks is a threshold theta_i that the row's K-th best score can not
+//      be below.
+//   2. score_topk_kernel (chunks = M, queries = N: each lane owns one row's scores):
+//      the scores to ~2^-17 relative (tau k' split into bf16 hi + lo terms, q^ too
+//      when it is not exactly bf16; b' through an extra k-step), tested against the
+//      row's threshold, which starts at theta_i, so only about K candidates per row
+//      are kept.  Each lane appends its row's candidates to its own half of the row's
+//      LDS list; a full list is sorted by bitonic networks (DPP and swizzle lane
+//      exchanges), cut to the best K and the threshold raised.
+//   k' is rewritten once per call into bf16 term rows whose 16-element k-blocks are
 //   stored in MFMA operand order, so staging is a copy and an operand is one 16-byte
 //   LDS read.
 #include <algorithm>
@@ -36,7 +37,6 @@ namespace hils {
 
 constexpr int ST_ROWS = 128;   // queries per workgroup
 constexpr int ST_TILE = 64;    // chunks per LDS tile
-constexpr int ST_BUF = 31;     // candidate buffer slots per row (slot 31 is a sink)
 
 HILS_DEV bool better(float s1, int c1, float s2, int c2) { return s1 > s2 || (s1 == s2 && c1 < c2); }
 
@@ -106,42 +106,6 @@ HILS_DEV void merge_into(float& ls, int& li, float ns, int nc, int j, int K) {
 }
 
 HILS_DEV float readlane_f(float v, int l) { return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), l)); }
-
-// the K-th best (score, chunk) of each half's list, broadcast to its lanes; the
-// score is raised to the row's threshold th while the list holds fewer than K
-// entries (every list entry is >= th, so a full list's K-th best is too)
-HILS_DEV void kth(float ls, int li, int hf, int K, float th, float& ts, int& ti) {
-  const float t0 = readlane_f(ls, K - 1), t1 = readlane_f(ls, 32 + K - 1);
-  const int i0 = __builtin_amdgcn_readlane(li, K - 1), i1 = __builtin_amdgcn_readlane(li, 32 + K - 1);
-  ts = fmaxf(hf ? t1 : t0, th);
-  ti = hf ? i1 : i0;
-}
-
-// append this lane's candidate (if `pass`) to its half's buffer; mk = ballot(pass);
-// f0 / f1: filled slots of the two halves (wave-uniform)
-HILS_DEV void append(float& bs, int& bi, int& f0, int& f1, float s, int c, bool pass, uint64_t mk, int j, int hf) {
-  const uint32_t lo = (uint32_t)mk, hi = (uint32_t)(mk >> 32);
-  const int m0 = __popc(lo), m1 = __popc(hi);
-  const int fl = hf ? f1 : f0, mown = hf ? m1 : m0;
-  const int rank = hf ? (int)__builtin_amdgcn_mbcnt_hi(hi, 0u) : (int)__builtin_amdgcn_mbcnt_lo(lo, 0u);
-  const int dst = 32 * hf + (pass ? fl + rank : ST_BUF);
-  const int rs = __builtin_amdgcn_ds_permute(dst * 4, __float_as_int(s));
-  const int rc = __builtin_amdgcn_ds_permute(dst * 4, c);
-  const bool neu = j >= fl && j < fl + mown;
-  bs = neu ? __int_as_float(rs) : bs;
-  bi = neu ? rc : bi;
-  f0 += m0;
-  f1 += m1;
-}
-
-// merge the buffer into the list and empty it; refresh the K-th best
-HILS_DEV void flush(float& ls, int& li, float& bs, int& bi, int& f0, int& f1, float th, float& ts, int& ti, int j,
-                    int hf, int K) {
-  const bool v = j < (hf ? f1 : f0);
-  merge_into(ls, li, v ? bs : -INFINITY, v ? bi : 0x7fffffff, j, K);
-  f0 = f1 = 0;
-  kth(ls, li, hf, K, th, ts, ti);
-}
 
 // float-only compare-exchange with lane j ^ X: keep the larger of the pair if keep_max
 template <int X>
@@ -491,28 +455,36 @@ __global__ void __launch_bounds__(256, 2) score_threshold(const IO* __restrict__
 
 
 // ------------------------------------------------------------- selection pass
-constexpr int SEL_CAP = 56;  // candidate slots per row in LDS
+// S^T = k' q^T on the MFMA: k' rows (chunks) are the A operand, the queries the B
+// operand, so accumulator register r of lane l holds the score of chunk
+// acc_row(r, l >> 5) of the 32-chunk tile for query row l & 31.  Each lane therefore
+// owns one row's scores and appends its passing candidates to its own half of the
+// row's list (LDS) with a per-lane fill: no cross-lane bookkeeping per score.
+// tau is folded into the k' planes and b' (three exact bf16 terms) enters through an
+// extra k-step against a constant [1, 1, 1, 0 ...] query operand.
+constexpr int SEL_CT = 32;     // chunks per column tile (single LDS buffer)
+constexpr int SEL_HALF = 32;   // candidate slots per half-row list (plus one spill slot)
+constexpr int P2_EXT = 16;     // extension elements after plane 0: [b'_hi, b'_mid, b'_lo, 0 ...]
 
 template <typename IO, int D, int NQ, int NK, bool QCAL>
 __global__ void __launch_bounds__(256, 2) score_topk_kernel(const IO* __restrict__ q, const IO* __restrict__ Dw,
                                                              const IO* __restrict__ Uw,
-                                                             const uint16_t* __restrict__ planes,
-                                                             const float* __restrict__ bc,
+                                                             const uint16_t* __restrict__ p2,
                                                              const float* __restrict__ theta,
                                                              int32_t* __restrict__ sel_idx,
                                                              float* __restrict__ sel_score, int H, int N, int C, int K,
                                                              int r, int NB, int items) {
-  constexpr int LDK = D + 8;            // LDS row stride of the k' tile planes (16-byte pad)
-  constexpr int NKS = D / 16;           // MFMA k-steps over the head dimension
-  constexpr int SEGS = D / 8;           // 16-byte segments of a plane row
-  constexpr int PH = ST_TILE / 2 * NK * SEGS / 256;  // 16-byte prefetch loads per thread per half tile
-  __shared__ __align__(16) uint16_t kt[NK][ST_TILE * LDK];   // the current tile; its halves are refilled in turn
-  __shared__ float bt[ST_TILE];
-  // per-row candidates (score, chunk); the last 256 entries are per-lane sinks for
-  // the stores of lanes whose score did not pass
-  __shared__ float cs[ST_ROWS * SEL_CAP + 256];
-  __shared__ uint16_t ci[ST_ROWS * SEL_CAP + 256];
-  __shared__ int fls[4][16][2];
+  constexpr int NKS = D / 16;
+  constexpr int DE2 = NK * D + P2_EXT;  // elements of a chunk row: plane 0, extension, planes 1..
+  constexpr int LDR = DE2 + 8;          // LDS row stride (16-byte pad)
+  constexpr int SEGS = DE2 / 8;
+  constexpr int NSEG = SEL_CT * SEGS;
+  constexpr int PL = (NSEG + 255) / 256;
+  constexpr int HSTR = SEL_HALF + 1;    // half-list stride: SEL_HALF slots + a spill slot
+  constexpr int LIST = 2 * HSTR;        // slots per row
+  __shared__ __align__(16) uint16_t kt[SEL_CT * LDR];
+  __shared__ float cs[ST_ROWS * LIST + 256];      // candidate scores; the last 256 are per-lane sinks
+  __shared__ uint16_t ci[ST_ROWS * LIST + 256];   // candidate chunks
 
   const int item = remap_xcd(blockIdx.x, items);
   if (item >= items) return;
@@ -522,15 +494,15 @@ __global__ void __launch_bounds__(256, 2) score_topk_kernel(const IO* __restrict
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int n = lane & 31, hf = lane >> 5;
   const int r0 = rb * ST_ROWS;
-  const int row = r0 + 32 * w + n;       // this lane's row as an MFMA A-operand supplier
+  const int row = r0 + 32 * w + n;       // this lane's query row
   const bool row_ok = row < N;
   const int last = min(r0 + ST_ROWS, N) - 1;
   const int Pmax = min(C, last / 64);
   const int Pmin = min(C, r0 / 64);
-  const float tau = 1.0f / sqrtf((float)D);
+  const int prow = row_ok ? min(C, row / 64) : 0;   // past chunks of this lane's row
   const int64_t qrow = ((int64_t)bh * N + (row_ok ? row : 0)) * D;
 
-  // ---- the query's A operands, q^ split into NQ bf16 terms
+  // ---- the query's B operands: q^ split into NQ bf16 terms, plus the constant extension
   bf16x8_t qb[NQ][NKS];
   qhat_rows<IO, D, QCAL>(q, Dw, Uw, hh, r, qrow, row_ok, lane, [&](int ks, const float(&v)[8]) {
     uint16_t t[NQ][8];
@@ -544,225 +516,176 @@ __global__ void __launch_bounds__(256, 2) score_topk_kernel(const IO* __restrict
 #pragma unroll
     for (int j = 0; j < NQ; ++j) qb[j][ks] = pack8(t[j]);
   });
-
-  // ---- per-row state: register rr holds rows acc_row(rr, 0) (lanes 0..31) and
-  // acc_row(rr, 1) (lanes 32..63) of this wave.  ts = the row's running threshold
-  // (starts at theta_i; raised to the K-th best when its list is compacted); f0 / f1
-  // = wave-uniform candidate counts of the two rows.  A score s >= ts is appended to
-  // the row's LDS list; a list that would overflow is sorted, cut to its best K and
-  // merged with the new candidates (settle).
-  float ts[16];
-  int ff[16];  // fills: row of lanes 0..31 in bits 0..7, row of lanes 32..63 in bits 8..15
-  const int row_base = (32 * w + 4 * hf) * SEL_CAP;  // + acc_row(rr, 0) * SEL_CAP: this lane's row of register rr
-  const int sink = ST_ROWS * SEL_CAP + tid;
-#pragma unroll
-  for (int rr = 0; rr < 16; ++rr) {
-    const int rw = r0 + 32 * w + acc_row(rr, hf);
-    ts[rr] = rw < N ? theta[(int64_t)bh * N + rw] : -INFINITY;
-    ff[rr] = 0;
+  bf16x8_t qext;
+  {
+    uint16_t t[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+    if (hf == 0) t[0] = t[1] = t[2] = 0x3f80;
+    qext = pack8(t);
   }
 
-  // Sort the candidates of row-register rr (each half its own row; fa / fb entries),
-  // keep the best K (lane j = j-th best), merge (ns, nc) into them and write the result
-  // back as the list's first entries.  Raises t_s to the K-th best; updates fa / fb.
-  auto settle = [&](int rr, float& t_s, int& fa, int& fb, float ns, int nc, bool merge_new, float& ls, int& li) {
-    const int base = (32 * w + acc_row(rr, hf)) * SEL_CAP;
-    const int fill = hf ? fb : fa;
+  // ---- per-lane state: the row's threshold (theta, raised when its list is compacted)
+  // and this half's list fill; rows beyond N take +inf and never collect anything
+  float th = row_ok ? theta[(int64_t)bh * N + row] : INFINITY;
+  int fill = 0;
+  const int lrow = 32 * w + n;           // row within the workgroup
+  const int lbase = lrow * LIST + hf * HSTR;
+  const int sink = ST_ROWS * LIST + tid;
+
+  // Sort the lists of rows ra (lanes 0..31) and rb_ (lanes 32..63) of this wave (lane j
+  // holds slot j of each half list), keep the best K (lane j = j-th best), optionally
+  // write them back split over the two half lists, and return the K-th best per half.
+  auto settle2 = [&](int ra, int rb2, bool write_back, float& ls, int& li, int& nvalid) {
+    const int rw = hf ? rb2 : ra;
+    const int f0 = min(__shfl(fill, rw), SEL_HALF), f1 = min(__shfl(fill, 32 + rw), SEL_HALF);  // valid entries
+    const int base = (32 * w + rw) * LIST;
     float xs = -INFINITY, ys = -INFINITY;
     int xi = 0x7fffffff, yi = 0x7fffffff;
-    if (n < fill) {
+    if (n < f0) {
       xs = cs[base + n];
       xi = ci[base + n];
     }
-    if (n + 32 < fill) {
-      ys = cs[base + n + 32];
-      yi = ci[base + n + 32];
+    if (n < f1) {
+      ys = cs[base + HSTR + n];
+      yi = ci[base + HSTR + n];
     }
     sort32(xs, xi, n);
     merge_into(xs, xi, ys, yi, n, K);
-    if (merge_new) merge_into(xs, xi, ns, nc, n, K);
-    if (n < K) {
-      cs[base + n] = xs;
-      ci[base + n] = (uint16_t)xi;
-    }
     const uint64_t vm = __ballot(xi != 0x7fffffff);
-    fa = __popc((uint32_t)vm);
-    fb = __popc((uint32_t)(vm >> 32));
-    const float k0 = readlane_f(xs, K - 1), k1 = readlane_f(xs, 32 + K - 1);
-    t_s = fmaxf(t_s, hf ? k1 : k0);  // -inf (fewer than K) keeps the threshold
+    nvalid = __popc(hf ? (uint32_t)(vm >> 32) : (uint32_t)vm);
+    if (write_back && n < K) {  // best (K+1)/2 to half 0, the rest to half 1
+      const int kh = (K + 1) >> 1;
+      const int slot = n < kh ? n : HSTR + n - kh;
+      cs[base + slot] = xs;
+      ci[base + slot] = (uint16_t)xi;
+    }
     ls = xs;
     li = xi;
   };
 
-  const int64_t PL = (int64_t)(items / NB) * C * D;    // elements per plane: B*H*C*D
-  const float* bcb = bc + (int64_t)bh * C;
-  const int ntiles = (Pmax + ST_TILE - 1) / ST_TILE;
-  // The next tile is prefetched in two halves of 32 chunks: loads issued before each
-  // 32-chunk MFMA column tile, written over that half after it.
-  u32x4_t pf[PH];
-  float pb = 0.f;
-  auto prefetch = [&](int t, int part) {
+  const uint16_t* src = p2 + (int64_t)bh * C * DE2;
+  u32x4_t pf[PL];
+  auto load_tile = [&](int ct) {
 #pragma unroll
-    for (int u = 0; u < PH; ++u) {
+    for (int u = 0; u < PL; ++u) {
       const int it = tid + 256 * u;
-      const int e = 32 * part + it / (NK * SEGS);
-      const int rem = it % (NK * SEGS);
-      const int pl = rem / SEGS, sg = rem % SEGS;
-      const int c = t * ST_TILE + e;
-      pf[u] = c < Pmax ? *reinterpret_cast<const u32x4_t*>(planes + pl * PL + ((int64_t)bh * C + c) * D + 8 * sg)
-                       : u32x4_t{0u, 0u, 0u, 0u};
-    }
-    if (tid < 32) {
-      const int c = t * ST_TILE + 32 * part + tid;
-      pb = c < Pmax ? bcb[c] : 0.f;
+      const int e = it / SEGS, sg = it % SEGS;
+      const int c = ct * SEL_CT + e;
+      pf[u] = (it < NSEG && c < Pmax) ? *reinterpret_cast<const u32x4_t*>(src + (int64_t)c * DE2 + 8 * sg)
+                                      : u32x4_t{0u, 0u, 0u, 0u};
     }
   };
-  auto commit = [&](int part) {
+  auto store_tile = [&]() {
 #pragma unroll
-    for (int u = 0; u < PH; ++u) {
+    for (int u = 0; u < PL; ++u) {
       const int it = tid + 256 * u;
-      const int e = 32 * part + it / (NK * SEGS);
-      const int rem = it % (NK * SEGS);
-      const int pl = rem / SEGS, sg = rem % SEGS;
-      *reinterpret_cast<u32x4_t*>(&kt[pl][e * LDK + 8 * sg]) = pf[u];
+      if (it < NSEG) {
+        const int e = it / SEGS, sg = it % SEGS;
+        *reinterpret_cast<u32x4_t*>(&kt[e * LDR + 8 * sg]) = pf[u];
+      }
     }
-    if (tid < 32) bt[32 * part + tid] = pb;
   };
 
-  if (ntiles > 0) {
-    prefetch(0, 0);
-    commit(0);
-    prefetch(0, 1);
-    commit(1);
+  const int nct = (Pmax + SEL_CT - 1) / SEL_CT;
+  if (nct > 0) {
+    load_tile(0);
+    store_tile();
   }
   __syncthreads();
-  // Half tt of the next tile is loaded into registers before the MFMA of half tt and
-  // written over half tt after a barrier; half tt is only read by column tile tt.
-  for (int t = 0; t < ntiles; ++t) {
-    const bool more = t + 1 < ntiles;
-    const bool masked = (t + 1) * ST_TILE > Pmin;  // chunks >= Pmin are not past chunks of every row
-#pragma unroll 1
-    for (int tt = 0; tt < 2; ++tt) {
-      if (more) prefetch(t + 1, tt);
-      if (t * ST_TILE + 32 * tt < Pmax) {
-        f32x16_t acc = zero16();
-        const int ch = 32 * tt + n;
+  for (int ct = 0; ct < nct; ++ct) {
+    const bool more = ct + 1 < nct;
+    if (more) load_tile(ct + 1);
+    f32x16_t acc = zero16();
+    const uint16_t* krow = &kt[n * LDR];   // A operand row: chunk n of the tile
 #pragma unroll
-        for (int ks = 0; ks < NKS; ++ks) {
+    for (int ks = 0; ks < NKS; ++ks)
 #pragma unroll
-          for (int j = 0; j < NK; ++j) {
-            const bf16x8_t bk = *reinterpret_cast<const bf16x8_t*>(&kt[j][ch * LDK + 16 * ks + 8 * hf]);
+      for (int j = 0; j < NK; ++j) {
+        const bf16x8_t a = *reinterpret_cast<const bf16x8_t*>(krow + j * D + (j ? P2_EXT : 0) + 16 * ks + 8 * hf);
 #pragma unroll
-            for (int i = 0; i < NQ; ++i)
-              if (i + j < (NQ > NK ? NQ : NK)) acc = mfma32(qb[i][ks], bk, acc);
-          }
+        for (int i = 0; i < NQ; ++i)
+          if (i + j < (NQ > NK ? NQ : NK)) acc = mfma32(a, qb[i][ks], acc);
+      }
+    acc = mfma32(*reinterpret_cast<const bf16x8_t*>(krow + D + 8 * hf), qext, acc);  // + b'
+    // candidates: s >= th goes to this lane's half list.  A full list takes further
+    // candidates in its spill slot (lost for now); the row is compacted after the tile
+    // and the lost ones are appended again against the raised threshold.
+    const int cb = ct * SEL_CT + 4 * hf;
+    const bool masked = (ct + 1) * SEL_CT > Pmin;  // chunks >= Pmin are not past chunks of every row
+    const int f_start = fill;
+    const float th_old = th;
+    auto score_at = [&](int rr) {
+      const int c = cb + 8 * (rr >> 2) + (rr & 3);   // chunk acc_row(rr, hf) of the tile
+      float s = acc[rr];
+      if (masked && c >= prow) s = __builtin_nanf("");
+      return s;
+    };
+#pragma unroll
+    for (int rr = 0; rr < 16; ++rr) {
+      const int c = cb + 8 * (rr >> 2) + (rr & 3);
+      const float s = score_at(rr);
+      const bool pass = s >= th;   // NaN never passes
+      const int pos = pass ? lbase + min(fill, SEL_HALF) : sink;
+      cs[pos] = s;
+      ci[pos] = (uint16_t)c;
+      fill += pass ? 1 : 0;
+    }
+    const uint64_t ovf = __ballot(fill > SEL_HALF);
+    if (ovf) {  // rare: compact the rows with a full half list, then re-append what was lost
+      const bool lost = fill > SEL_HALF;
+      uint32_t rows_big = (uint32_t)ovf | (uint32_t)(ovf >> 32);
+      while (rows_big) {
+        const int ra = __builtin_ctz(rows_big);
+        rows_big &= rows_big - 1;
+        int rb2 = ra;
+        const bool two = rows_big != 0;
+        if (two) {
+          rb2 = __builtin_ctz(rows_big);
+          rows_big &= rows_big - 1;
         }
-        const int c = t * ST_TILE + ch;
-        const float bprime = bt[ch];
-        auto score_of = [&](float a, int rr) {
-          float s = fmaf(a, tau, bprime);
-          if (masked) {
-            const int rw = r0 + 32 * w + acc_row(rr, hf);
-            const int prow = rw < N ? min(C, rw / 64) : 0;
-            if (c >= prow) s = __builtin_nanf("");
-          }
-          return s;
-        };
-        // filter against each row's threshold and append the survivors (branch-free
-        // within the wave: lanes that did not pass store to their sink slot)
-        uint32_t ovf = 0;
-        auto filter = [&](auto masked_tag) {
-          constexpr bool MASKED = decltype(masked_tag)::value;
-#pragma unroll
-          for (int rr = 0; rr < 16; ++rr) {
-            float s = fmaf(acc[rr], tau, bprime);
-            if constexpr (MASKED) {
-              const int rw = r0 + 32 * w + acc_row(rr, hf);
-              const int prow = rw < N ? min(C, rw / 64) : 0;
-              if (c >= prow) s = __builtin_nanf("");
-            }
-            const bool pass = s >= ts[rr];  // NaN never passes
-            const uint64_t mk = __ballot(pass);
-            if (mk) {
-              const uint32_t lo = (uint32_t)mk, hi = (uint32_t)(mk >> 32);
-              const int n0 = __popc(lo), n1 = __popc(hi);
-              const int a0 = ff[rr] & 0xff, a1 = ff[rr] >> 8;
-              if (a0 + n0 > SEL_CAP || a1 + n1 > SEL_CAP) {
-                ovf |= 1u << rr;
-              } else {
-                const int rank = (int)__builtin_amdgcn_mbcnt_hi(hi, __builtin_amdgcn_mbcnt_lo(lo, 0u)) - (hf ? n0 : 0);
-                const int pos = pass ? row_base + acc_row(rr, 0) * SEL_CAP + (hf ? a1 : a0) + rank : sink;
-                cs[pos] = s;
-                ci[pos] = (uint16_t)c;
-                ff[rr] = __builtin_amdgcn_readfirstlane(ff[rr] + n0 + (n1 << 8));
-              }
-            }
-          }
-        };
-        if (masked)
-          filter(std::true_type{});
-        else
-          filter(std::false_type{});
-        while (ovf) {  // rare: lists that would overflow
-          const int rr = __builtin_ctz(ovf);
-          ovf &= ovf - 1;
-          float wt, wa;
-          int wa0, wa1;
-          switch (rr) {
-#define HILS_PICK(R) \
-  case R:            \
-    wt = ts[R];      \
-    wa = acc[R];     \
-    wa0 = ff[R] & 0xff; \
-    wa1 = ff[R] >> 8;   \
-    break;
-            HILS_PICK(0) HILS_PICK(1) HILS_PICK(2) HILS_PICK(3) HILS_PICK(4) HILS_PICK(5) HILS_PICK(6) HILS_PICK(7)
-            HILS_PICK(8) HILS_PICK(9) HILS_PICK(10) HILS_PICK(11) HILS_PICK(12) HILS_PICK(13) HILS_PICK(14)
-            HILS_PICK(15)
-#undef HILS_PICK
-            default:
-              wt = wa = 0.f;
-              wa0 = wa1 = 0;
-          }
-          const float ws = score_of(wa, rr);
-          const bool pass = ws >= wt;
-          float ls;
-          int li;
-          settle(rr, wt, wa0, wa1, pass ? ws : -INFINITY, pass ? c : 0x7fffffff, true, ls, li);
-          switch (rr) {
-#define HILS_PUT(R) \
-  case R:           \
-    ts[R] = wt;     \
-    ff[R] = wa0 | (wa1 << 8); \
-    break;
-            HILS_PUT(0) HILS_PUT(1) HILS_PUT(2) HILS_PUT(3) HILS_PUT(4) HILS_PUT(5) HILS_PUT(6) HILS_PUT(7)
-            HILS_PUT(8) HILS_PUT(9) HILS_PUT(10) HILS_PUT(11) HILS_PUT(12) HILS_PUT(13) HILS_PUT(14) HILS_PUT(15)
-#undef HILS_PUT
-            default:
-              break;
-          }
+        float ls;
+        int li, nv;
+        settle2(ra, rb2, true, ls, li, nv);
+        // new fills and thresholds of the two rows (half 0 of the wave did row ra, half 1 row rb2)
+        const int kh = (K + 1) >> 1;
+        const int nva = __shfl(nv, 0), nvb = __shfl(nv, 32);
+        const float ka = readlane_f(ls, K - 1), kb = readlane_f(ls, 32 + K - 1);
+        if (n == ra) {
+          fill = hf ? max(0, nva - kh) : min(nva, kh);
+          th = fmaxf(th, ka);
+        }
+        if (two && n == rb2) {
+          fill = hf ? max(0, nvb - kh) : min(nvb, kh);
+          th = fmaxf(th, kb);
         }
       }
-      __syncthreads();  // every wave is done with half tt of this tile
-      if (more) commit(tt);
+      int running = f_start;
+#pragma unroll
+      for (int rr = 0; rr < 16; ++rr) {
+        const int c = cb + 8 * (rr >> 2) + (rr & 3);
+        const float s = score_at(rr);
+        const bool was = s >= th_old;
+        running += was ? 1 : 0;
+        if (lost && was && running > SEL_HALF && s >= th) {  // at most 16 after a compaction to <= 16
+          cs[lbase + fill] = s;
+          ci[lbase + fill] = (uint16_t)c;
+          ++fill;
+        }
+      }
+    }
+    __syncthreads();  // every wave is done with this tile
+    if (more) {
+      store_tile();
+      __syncthreads();
     }
   }
 
-  // ---- final selection and output: lane j of each half writes slot j of its row
-  if (lane == 0) {
-#pragma unroll
-    for (int rr = 0; rr < 16; ++rr) {
-      fls[w][rr][0] = ff[rr] & 0xff;
-      fls[w][rr][1] = ff[rr] >> 8;
-    }
-  }
-  __builtin_amdgcn_wave_barrier();
+  // ---- final selection and output, two rows per step: lane j of each half writes slot j
 #pragma unroll 1
-  for (int rr = 0; rr < 16; ++rr) {
-    float dummy = -INFINITY, ls;
-    int fa = fls[w][rr][0], fb = fls[w][rr][1], li;
-    settle(rr, dummy, fa, fb, -INFINITY, 0x7fffffff, false, ls, li);
-    const int rw = r0 + 32 * w + acc_row(rr, hf);
+  for (int p = 0; p < 16; ++p) {
+    float ls;
+    int li, nv;
+    settle2(p, p + 16, false, ls, li, nv);
+    const int rw = r0 + 32 * w + (hf ? p + 16 : p);
     if (rw < N && n < K) {
       const int64_t o = ((int64_t)bh * N + rw) * K + n;
       const bool ok = li != 0x7fffffff;
@@ -773,20 +696,22 @@ __global__ void __launch_bounds__(256, 2) score_topk_kernel(const IO* __restrict
 }
 
 // ---------------------------------------------------------------- k' preparation
-// k' (fp32) -> (a) NK bf16 term planes (plane j holds term j of every element) for the
-// selection pass and (b) the threshold pass's rows: bf16(k') followed by the extension
-// [b'_hi, b'_lo, TH_ABS, |k'_c| rounded up, 0 ...].  Both hold each 16-element k-block in
-// MFMA operand order: position 16 ks + 8 h + m holds element kperm(ks, h, m).
+// k' (fp32) -> (a) the selection pass's rows: tau*k' split into NK bf16 term planes with
+// the extension [b'_hi, b'_mid, b'_lo, 0 ...] after plane 0, and (b) the threshold pass's
+// rows: bf16(k') followed by [b'_hi, b'_lo, TH_ABS, |k'_c| rounded up, 0 ...].  Both hold
+// each 16-element k-block in MFMA operand order: position 16 ks + 8 h + m holds element
+// kperm(ks, h, m).
 template <int D, int NK>
 __global__ void __launch_bounds__(256) prep_kprime(const float* __restrict__ kc, const float* __restrict__ bc,
-                                                   uint16_t* __restrict__ planes, uint16_t* __restrict__ t1,
+                                                   uint16_t* __restrict__ p2, uint16_t* __restrict__ t1,
                                                    int64_t rows) {
   constexpr int SPR = D / 8;        // 16-byte segments (threads) per chunk row
   constexpr int RPB = 256 / SPR;    // chunk rows per workgroup pass
   constexpr int DE = D + TH_EXT;
+  constexpr int DE2 = NK * D + P2_EXT;
+  const float tau = 1.0f / sqrtf((float)D);
   const int tid = threadIdx.x;
   const int sg = tid % SPR, ks = sg >> 1, h = sg & 1;
-  const int64_t n = rows * D;
   for (int64_t base = (int64_t)blockIdx.x * RPB; base < rows; base += (int64_t)gridDim.x * RPB) {
     const int64_t rw = base + tid / SPR;
     const bool ok = rw < rows;
@@ -804,31 +729,39 @@ __global__ void __launch_bounds__(256) prep_kprime(const float* __restrict__ kc,
     for (int m = 0; m < 8; ++m) s2 = fmaf(x[m], x[m], s2);
 #pragma unroll
     for (int o = 1; o < SPR; o <<= 1) s2 += __shfl_xor(s2, o);
-    uint16_t tm[NK][8];
+    uint16_t tm[NK][8], hi[8];
 #pragma unroll
     for (int m = 0; m < 8; ++m) {
       uint16_t sp[NK];
-      split_bf16<NK>(x[m], sp);
+      split_bf16<NK>(tau * x[m], sp);
 #pragma unroll
       for (int j = 0; j < NK; ++j) tm[j][m] = sp[j];
+      hi[m] = f32_to_bf16(x[m]);
     }
     if (ok) {
+      uint16_t* o2 = p2 + rw * DE2;
 #pragma unroll
       for (int j = 0; j < NK; ++j)
-        *reinterpret_cast<bf16x8_t*>(planes + j * n + rw * D + 8 * sg) = pack8(tm[j]);
+        *reinterpret_cast<bf16x8_t*>(o2 + j * D + (j ? P2_EXT : 0) + 8 * sg) = pack8(tm[j]);
       uint16_t* o1 = t1 + rw * DE;
-      *reinterpret_cast<bf16x8_t*>(o1 + 8 * sg) = pack8(tm[0]);
+      *reinterpret_cast<bf16x8_t*>(o1 + 8 * sg) = pack8(hi);
       if (sg < 2) {
-        uint16_t e[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+        uint16_t e[8] = {0, 0, 0, 0, 0, 0, 0, 0}, f[8] = {0, 0, 0, 0, 0, 0, 0, 0};
         if (sg == 0) {
-          uint16_t sp[2];
-          split_bf16<2>(bc[rw], sp);
-          e[0] = sp[0];
-          e[1] = sp[1];
+          const float bv = bc[rw];
+          uint16_t sp3[3], sp2[2];
+          split_bf16<3>(bv, sp3);
+          split_bf16<2>(bv, sp2);
+          e[0] = sp2[0];
+          e[1] = sp2[1];
           e[2] = 0x3980;  // TH_ABS = 2^-12
           e[3] = bf16_up(sqrtf(s2));
+          f[0] = sp3[0];
+          f[1] = sp3[1];
+          f[2] = sp3[2];
         }
         *reinterpret_cast<bf16x8_t*>(o1 + D + 8 * sg) = pack8(e);
+        *reinterpret_cast<bf16x8_t*>(o2 + D + 8 * sg) = pack8(f);
       }
     }
   }
@@ -845,7 +778,7 @@ static ScoreWs score_ws(const Geom& g) {
   ScoreWs w;
   size_t off = 0;
   w.planes = off;
-  off += al3((size_t)nk_of(g) * rows * g.d * 2);
+  off += al3(rows * ((size_t)nk_of(g) * g.d + P2_EXT) * 2);
   w.t1 = off;
   off += al3(rows * (g.d + TH_EXT) * 2);
   w.theta = off;
@@ -867,8 +800,8 @@ static void launch_st(const Geom& g, const void* q, const void* Dw, const void* 
                      (const IO*)Uw, t1, theta, g.Hq, g.N, g.C(), g.K, g.r, NB, items);
   if (ev) hipEventRecord(ev[0], st);
   hipLaunchKernelGGL((score_topk_kernel<IO, D, NQ, NK, QCAL>), dim3(grid), dim3(256), 0, st, (const IO*)q,
-                     (const IO*)Dw, (const IO*)Uw, planes, bc, (const float*)theta, si, ss, g.Hq, g.N, g.C(), g.K,
-                     g.r, NB, items);
+                     (const IO*)Dw, (const IO*)Uw, planes, (const float*)theta, si, ss, g.Hq, g.N, g.C(), g.K, g.r,
+                     NB, items);
 }
 
 template <typename IO, int D>
