@@ -438,7 +438,7 @@ __global__ void __launch_bounds__(256, 2) chunk_attend(const IO* __restrict__ q,
         const uint32_t e = ipid[r];
         const u32x4_t val = *reinterpret_cast<const u32x4_t*>(&myq[(RPL * u + lr) * LDQ + 8 * sg]);
         if (e != 0xffffffffu)  // slot (e mod K) of row e / K, K + 1 slots per row
-          *reinterpret_cast<u32x4_t*>(dst + ((int64_t)e + irow[r]) * D + 8 * sg) = val;
+          __builtin_nontemporal_store(val, reinterpret_cast<u32x4_t*>(dst + ((int64_t)e + irow[r]) * D + 8 * sg));
       }
       __builtin_amdgcn_wave_barrier();
     }
@@ -559,7 +559,7 @@ __global__ void __launch_bounds__(256) fuse(const float* __restrict__ sel_score,
         const int t = sg * SPL + slot;           // logical slot: 0..ns-1 selected, ns = own
         const int phys = t < ns ? t : K;
         raw[v2][sg] = (live[v2] && t <= ns)
-                          ? *reinterpret_cast<const u32x4_t*>(part + (row * (K + 1) + phys) * D + dpos)
+                          ? __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(part + (row * (K + 1) + phys) * D + dpos))
                           : u32x4_t{0u, 0u, 0u, 0u};
       }
     }
