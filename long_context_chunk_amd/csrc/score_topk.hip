@@ -38,8 +38,6 @@ namespace hils {
 constexpr int ST_ROWS = 128;   // queries per workgroup
 constexpr int ST_TILE = 64;    // chunks per LDS tile
 
-HILS_DEV bool better(float s1, int c1, float s2, int c2) { return s1 > s2 || (s1 == s2 && c1 < c2); }
-
 template <int CTRL>
 HILS_DEV int dpp(int v) {
   return __builtin_amdgcn_update_dpp(v, v, CTRL, 0xf, 0xf, false);
@@ -63,19 +61,25 @@ HILS_DEV int xlane(int v, int j) {
   }
 }
 
-// compare-exchange with lane j ^ X; keep the better of the pair if kb, else the worse
+// value of lane j ^ X (within each 32-lane half) of a 64-bit key
 template <int X>
-HILS_DEV void cx(float& s, int& c, int j, bool kb) {
-  const float ps = __int_as_float(xlane<X>(__float_as_int(s), j));
-  const int pc = xlane<X>(c, j);
-  const bool take = kb ? better(ps, pc, s, c) : better(s, c, ps, pc);
-  s = take ? ps : s;
-  c = take ? pc : c;
+HILS_DEV uint64_t xlane64(uint64_t v, int j) {
+  const uint32_t lo = (uint32_t)xlane<X>((int)(uint32_t)v, j);
+  const uint32_t hi = (uint32_t)xlane<X>((int)(uint32_t)(v >> 32), j);
+  return ((uint64_t)hi << 32) | lo;
 }
 
-// bitonic sort of one (score, chunk) per lane, best first, within each 32-lane half
-HILS_DEV void sort32(float& s, int& c, int j) {
-#define HILS_STAGE(K_, X_) cx<X_>(s, c, j, ((j & X_) == 0) == (((j & K_) == 0) || K_ == 32));
+// compare-exchange of 64-bit selection keys (make_key: larger = better, ties to the lower
+// chunk; 0 = empty) with lane j ^ X: keep the larger of the pair if kb, else the smaller
+template <int X>
+HILS_DEV void cxk(uint64_t& k, int j, bool kb) {
+  const uint64_t p = xlane64<X>(k, j);
+  k = ((p > k) == kb) ? p : k;
+}
+
+// bitonic sort of one key per lane, best first, within each 32-lane half
+HILS_DEV void sort32k(uint64_t& k, int j) {
+#define HILS_STAGE(K_, X_) cxk<X_>(k, j, ((j & X_) == 0) == (((j & K_) == 0) || K_ == 32));
   HILS_STAGE(2, 1)
   HILS_STAGE(4, 2) HILS_STAGE(4, 1)
   HILS_STAGE(8, 4) HILS_STAGE(8, 2) HILS_STAGE(8, 1)
@@ -84,25 +88,18 @@ HILS_DEV void sort32(float& s, int& c, int j) {
 #undef HILS_STAGE
 }
 
-// merge the unsorted (ns, nc) into the sorted list (ls, li) of each half; keep the best K
-HILS_DEV void merge_into(float& ls, int& li, float ns, int nc, int j, int K) {
-  sort32(ns, nc, j);
-  const float rs = __int_as_float(xlane<31>(__float_as_int(ns), j));  // lane j: the (31-j)-th best new one
-  const int rc = xlane<31>(nc, j);
-  if (better(rs, rc, ls, li)) {
-    ls = rs;
-    li = rc;
-  }
-  // the 32 kept entries form a bitonic sequence: half-cleaners sort it best-first
-  cx<16>(ls, li, j, (j & 16) == 0);
-  cx<8>(ls, li, j, (j & 8) == 0);
-  cx<4>(ls, li, j, (j & 4) == 0);
-  cx<2>(ls, li, j, (j & 2) == 0);
-  cx<1>(ls, li, j, (j & 1) == 0);
-  if (j >= K) {
-    ls = -INFINITY;
-    li = 0x7fffffff;
-  }
+// merge the unsorted keys nk into the sorted list lk of each half; keep the best K
+HILS_DEV void merge_intok(uint64_t& lk, uint64_t nk, int j, int K) {
+  sort32k(nk, j);
+  const uint64_t r = xlane64<31>(nk, j);  // lane j: the (31-j)-th best new key
+  lk = r > lk ? r : lk;
+  // the 32 kept keys form a bitonic sequence: half-cleaners sort it best-first
+  cxk<16>(lk, j, (j & 16) == 0);
+  cxk<8>(lk, j, (j & 8) == 0);
+  cxk<4>(lk, j, (j & 4) == 0);
+  cxk<2>(lk, j, (j & 2) == 0);
+  cxk<1>(lk, j, (j & 1) == 0);
+  if (j >= K) lk = 0;
 }
 
 HILS_DEV float readlane_f(float v, int l) { return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), l)); }
@@ -368,24 +365,23 @@ __global__ void __launch_bounds__(256, 2) score_threshold(const IO* __restrict__
 
   const uint16_t* src = t1 + (int64_t)bh * C * DE;
   u32x4_t pf[PL];
+  // chunks beyond Pmax load chunk Pmax-1 (finite; masked out below); the last partial
+  // group of segments repeats the final segment: no divergent loads
   auto load_tile = [&](int t) {
 #pragma unroll
     for (int u = 0; u < PL; ++u) {
-      const int it = tid + 256 * u;
+      const int it = min(tid + 256 * u, NSEG - 1);
       const int e = it / SEGS, sg = it % SEGS;
-      const int c = t * ST_TILE + e;
-      pf[u] = (it < NSEG && c < Pmax) ? *reinterpret_cast<const u32x4_t*>(src + (int64_t)c * DE + 8 * sg)
-                                      : u32x4_t{0u, 0u, 0u, 0u};
+      const int c = min(t * ST_TILE + e, Pmax - 1);
+      pf[u] = *reinterpret_cast<const u32x4_t*>(src + (int64_t)c * DE + 8 * sg);
     }
   };
   auto store_tile = [&](int buf) {
 #pragma unroll
     for (int u = 0; u < PL; ++u) {
-      const int it = tid + 256 * u;
-      if (it < NSEG) {
-        const int e = it / SEGS, sg = it % SEGS;
-        *reinterpret_cast<u32x4_t*>(&kt[buf][e * LDT + 8 * sg]) = pf[u];
-      }
+      const int it = min(tid + 256 * u, NSEG - 1);
+      const int e = it / SEGS, sg = it % SEGS;
+      *reinterpret_cast<u32x4_t*>(&kt[buf][e * LDT + 8 * sg]) = pf[u];
     }
   };
 
@@ -524,64 +520,58 @@ __global__ void __launch_bounds__(256, 2) score_topk_kernel(const IO* __restrict
   }
 
   // ---- per-lane state: the row's threshold (theta, raised when its list is compacted)
-  // and this half's list fill; rows beyond N take +inf and never collect anything
+  // and this half's list position lf (absolute slot index, lbase + fill); rows beyond
+  // N take +inf and never collect anything
   float th = row_ok ? theta[(int64_t)bh * N + row] : INFINITY;
-  int fill = 0;
   const int lrow = 32 * w + n;           // row within the workgroup
   const int lbase = lrow * LIST + hf * HSTR;
+  const int lcap = lbase + SEL_HALF;     // the spill slot
   const int sink = ST_ROWS * LIST + tid;
+  int lf = lbase;
 
-  // Sort the lists of rows ra (lanes 0..31) and rb_ (lanes 32..63) of this wave (lane j
-  // holds slot j of each half list), keep the best K (lane j = j-th best), optionally
-  // write them back split over the two half lists, and return the K-th best per half.
-  auto settle2 = [&](int ra, int rb2, bool write_back, float& ls, int& li, int& nvalid) {
+  // Sort the lists of rows ra (lanes 0..31) and rb_ (lanes 32..63) of this wave as
+  // selection keys (lane j holds slot j of each half list), keep the best K (lane j =
+  // j-th best) and optionally write them back split over the two half lists.
+  auto settle2 = [&](int ra, int rb2, bool write_back, uint64_t& lk, int& nvalid) {
     const int rw = hf ? rb2 : ra;
-    const int f0 = min(__shfl(fill, rw), SEL_HALF), f1 = min(__shfl(fill, 32 + rw), SEL_HALF);  // valid entries
+    const int myfill = lf - lbase;
+    const int f0 = min(__shfl(myfill, rw), SEL_HALF), f1 = min(__shfl(myfill, 32 + rw), SEL_HALF);
     const int base = (32 * w + rw) * LIST;
-    float xs = -INFINITY, ys = -INFINITY;
-    int xi = 0x7fffffff, yi = 0x7fffffff;
-    if (n < f0) {
-      xs = cs[base + n];
-      xi = ci[base + n];
-    }
-    if (n < f1) {
-      ys = cs[base + HSTR + n];
-      yi = ci[base + HSTR + n];
-    }
-    sort32(xs, xi, n);
-    merge_into(xs, xi, ys, yi, n, K);
-    const uint64_t vm = __ballot(xi != 0x7fffffff);
+    uint64_t x = 0, y = 0;
+    if (n < f0) x = make_key(cs[base + n], ci[base + n]);
+    if (n < f1) y = make_key(cs[base + HSTR + n], ci[base + HSTR + n]);
+    sort32k(x, n);
+    merge_intok(x, y, n, K);
+    const uint64_t vm = __ballot(x != 0);
     nvalid = __popc(hf ? (uint32_t)(vm >> 32) : (uint32_t)vm);
     if (write_back && n < K) {  // best (K+1)/2 to half 0, the rest to half 1
       const int kh = (K + 1) >> 1;
       const int slot = n < kh ? n : HSTR + n - kh;
-      cs[base + slot] = xs;
-      ci[base + slot] = (uint16_t)xi;
+      cs[base + slot] = key_score(x);
+      ci[base + slot] = (uint16_t)key_chunk(x);
     }
-    ls = xs;
-    li = xi;
+    lk = x;
   };
 
   const uint16_t* src = p2 + (int64_t)bh * C * DE2;
   u32x4_t pf[PL];
+  // chunks beyond Pmax load chunk Pmax-1 (finite; masked out below) and the last
+  // partial group of segments repeats the final segment: no divergent loads
   auto load_tile = [&](int ct) {
 #pragma unroll
     for (int u = 0; u < PL; ++u) {
-      const int it = tid + 256 * u;
+      const int it = min(tid + 256 * u, NSEG - 1);
       const int e = it / SEGS, sg = it % SEGS;
-      const int c = ct * SEL_CT + e;
-      pf[u] = (it < NSEG && c < Pmax) ? *reinterpret_cast<const u32x4_t*>(src + (int64_t)c * DE2 + 8 * sg)
-                                      : u32x4_t{0u, 0u, 0u, 0u};
+      const int c = min(ct * SEL_CT + e, Pmax - 1);
+      pf[u] = *reinterpret_cast<const u32x4_t*>(src + (int64_t)c * DE2 + 8 * sg);
     }
   };
   auto store_tile = [&]() {
 #pragma unroll
     for (int u = 0; u < PL; ++u) {
-      const int it = tid + 256 * u;
-      if (it < NSEG) {
-        const int e = it / SEGS, sg = it % SEGS;
-        *reinterpret_cast<u32x4_t*>(&kt[e * LDR + 8 * sg]) = pf[u];
-      }
+      const int it = min(tid + 256 * u, NSEG - 1);
+      const int e = it / SEGS, sg = it % SEGS;
+      *reinterpret_cast<u32x4_t*>(&kt[e * LDR + 8 * sg]) = pf[u];
     }
   };
 
@@ -610,29 +600,49 @@ __global__ void __launch_bounds__(256, 2) score_topk_kernel(const IO* __restrict
     // candidates in its spill slot (lost for now); the row is compacted after the tile
     // and the lost ones are appended again against the raised threshold.
     const int cb = ct * SEL_CT + 4 * hf;
-    const bool masked = (ct + 1) * SEL_CT > Pmin;  // chunks >= Pmin are not past chunks of every row
-    const int f_start = fill;
+    const int lf_start = lf;
     const float th_old = th;
-    auto score_at = [&](int rr) {
-      const int c = cb + 8 * (rr >> 2) + (rr & 3);   // chunk acc_row(rr, hf) of the tile
+    auto score_at = [&](int rr, auto masked_tag) {
       float s = acc[rr];
-      if (masked && c >= prow) s = __builtin_nanf("");
+      if constexpr (decltype(masked_tag)::value) {
+        if (cb + 8 * (rr >> 2) + (rr & 3) >= prow) s = __builtin_nanf("");
+      }
       return s;
     };
+    auto append_all = [&](auto masked_tag) {
 #pragma unroll
-    for (int rr = 0; rr < 16; ++rr) {
-      const int c = cb + 8 * (rr >> 2) + (rr & 3);
-      const float s = score_at(rr);
-      const bool pass = s >= th;   // NaN never passes
-      const int pos = pass ? lbase + min(fill, SEL_HALF) : sink;
-      cs[pos] = s;
-      ci[pos] = (uint16_t)c;
-      fill += pass ? 1 : 0;
-    }
-    const uint64_t ovf = __ballot(fill > SEL_HALF);
+      for (int rr = 0; rr < 16; ++rr) {
+        const float s = score_at(rr, masked_tag);
+        const bool pass = s >= th;   // NaN never passes
+        const int pos = pass ? min(lf, lcap) : sink;
+        cs[pos] = s;
+        ci[pos] = (uint16_t)(cb + 8 * (rr >> 2) + (rr & 3));
+        lf += pass ? 1 : 0;
+      }
+    };
+    auto reappend_lost = [&](auto masked_tag) {
+      int running = lf_start;
+#pragma unroll
+      for (int rr = 0; rr < 16; ++rr) {
+        const float s = score_at(rr, masked_tag);
+        const bool was = s >= th_old;
+        running += was ? 1 : 0;
+        if (was && running > lcap && s >= th) {  // at most 16 after a compaction to <= 16
+          cs[lf] = s;
+          ci[lf] = (uint16_t)(cb + 8 * (rr >> 2) + (rr & 3));
+          ++lf;
+        }
+      }
+    };
+    const bool masked = (ct + 1) * SEL_CT > Pmin;  // chunks >= Pmin are not past chunks of every row
+    if (masked)
+      append_all(std::true_type{});
+    else
+      append_all(std::false_type{});
+    const uint64_t ovf = __ballot(lf > lcap);
     if (ovf) {  // rare: compact the rows with a full half list, then re-append what was lost
-      const bool lost = fill > SEL_HALF;
       uint32_t rows_big = (uint32_t)ovf | (uint32_t)(ovf >> 32);
+      const int kh = (K + 1) >> 1;
       while (rows_big) {
         const int ra = __builtin_ctz(rows_big);
         rows_big &= rows_big - 1;
@@ -642,35 +652,26 @@ __global__ void __launch_bounds__(256, 2) score_topk_kernel(const IO* __restrict
           rb2 = __builtin_ctz(rows_big);
           rows_big &= rows_big - 1;
         }
-        float ls;
-        int li, nv;
-        settle2(ra, rb2, true, ls, li, nv);
+        uint64_t lk;
+        int nv;
+        settle2(ra, rb2, true, lk, nv);
         // new fills and thresholds of the two rows (half 0 of the wave did row ra, half 1 row rb2)
-        const int kh = (K + 1) >> 1;
         const int nva = __shfl(nv, 0), nvb = __shfl(nv, 32);
-        const float ka = readlane_f(ls, K - 1), kb = readlane_f(ls, 32 + K - 1);
+        const uint64_t kka = __shfl(lk, K - 1), kkb = __shfl(lk, 32 + K - 1);
+        const float ka = kka ? key_score(kka) : -INFINITY, kb = kkb ? key_score(kkb) : -INFINITY;
         if (n == ra) {
-          fill = hf ? max(0, nva - kh) : min(nva, kh);
+          lf = lbase + (hf ? max(0, nva - kh) : min(nva, kh));
           th = fmaxf(th, ka);
         }
         if (two && n == rb2) {
-          fill = hf ? max(0, nvb - kh) : min(nvb, kh);
+          lf = lbase + (hf ? max(0, nvb - kh) : min(nvb, kh));
           th = fmaxf(th, kb);
         }
       }
-      int running = f_start;
-#pragma unroll
-      for (int rr = 0; rr < 16; ++rr) {
-        const int c = cb + 8 * (rr >> 2) + (rr & 3);
-        const float s = score_at(rr);
-        const bool was = s >= th_old;
-        running += was ? 1 : 0;
-        if (lost && was && running > SEL_HALF && s >= th) {  // at most 16 after a compaction to <= 16
-          cs[lbase + fill] = s;
-          ci[lbase + fill] = (uint16_t)c;
-          ++fill;
-        }
-      }
+      if (masked)
+        reappend_lost(std::true_type{});
+      else
+        reappend_lost(std::false_type{});
     }
     __syncthreads();  // every wave is done with this tile
     if (more) {
@@ -682,15 +683,15 @@ __global__ void __launch_bounds__(256, 2) score_topk_kernel(const IO* __restrict
   // ---- final selection and output, two rows per step: lane j of each half writes slot j
 #pragma unroll 1
   for (int p = 0; p < 16; ++p) {
-    float ls;
-    int li, nv;
-    settle2(p, p + 16, false, ls, li, nv);
+    uint64_t lk;
+    int nv;
+    settle2(p, p + 16, false, lk, nv);
     const int rw = r0 + 32 * w + (hf ? p + 16 : p);
     if (rw < N && n < K) {
       const int64_t o = ((int64_t)bh * N + rw) * K + n;
-      const bool ok = li != 0x7fffffff;
-      sel_idx[o] = ok ? li : -1;
-      sel_score[o] = ok ? ls : -INFINITY;
+      const bool ok = lk != 0;
+      sel_idx[o] = ok ? key_chunk(lk) : -1;
+      sel_score[o] = ok ? key_score(lk) : -INFINITY;
     }
   }
 }
