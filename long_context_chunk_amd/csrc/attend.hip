@@ -192,23 +192,19 @@ HILS_DEV void stage_kv(KVTile<IO, D, NT>& tile, const IO* __restrict__ k, const 
 #pragma unroll
       for (int u = 0; u < 8; ++u) kx[u] = vx[u] = 0.f;
     }
-    uint16_t ks[8][NT], vs[8][NT];
-#pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      split_bf16<NT>(kx[u], ks[u]);
-      split_bf16<NT>(vx[u], vs[u]);
-    }
+    u32x4_t ks[NT], vs[NT];
+    split8<NT>(kx, ks);
+    split8<NT>(vx, vs);
 #pragma unroll
     for (int j = 0; j < NT; ++j) {
+      *reinterpret_cast<u32x2_t*>(&tile.k[j][key * LDK + e]) = u32x2_t{ks[j].x, ks[j].y};
+      *reinterpret_cast<u32x2_t*>(&tile.k[j][key * LDK + e + 4]) = u32x2_t{ks[j].z, ks[j].w};
+      const uint32_t vw[4] = {vs[j].x, vs[j].y, vs[j].z, vs[j].w};
 #pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        u32x2_t pk;
-        pk.x = (uint32_t)ks[4 * h][j] | ((uint32_t)ks[4 * h + 1][j] << 16);
-        pk.y = (uint32_t)ks[4 * h + 2][j] | ((uint32_t)ks[4 * h + 3][j] << 16);
-        *reinterpret_cast<u32x2_t*>(&tile.k[j][key * LDK + e + 4 * h]) = pk;
+      for (int u = 0; u < 4; ++u) {
+        tile.vt[j][(e + 2 * u) * LDV + key] = (uint16_t)(vw[u] & 0xffffu);
+        tile.vt[j][(e + 2 * u + 1) * LDV + key] = (uint16_t)(vw[u] >> 16);
       }
-#pragma unroll
-      for (int u = 0; u < 8; ++u) tile.vt[j][(e + u) * LDV + key] = vs[u][j];
     }
   }
 }
@@ -269,16 +265,13 @@ HILS_DEV void wave_chunk_attention(const KVTile<IO, D, NT>& tile, const bf16x8_t
   bf16x8_t pb[NT][4];
 #pragma unroll
   for (int ks2 = 0; ks2 < 4; ++ks2) {
-    uint16_t t[NT][8];
+    float pv[8];
 #pragma unroll
-    for (int mm = 0; mm < 8; ++mm) {
-      uint16_t sp[NT];
-      split_bf16<NT>(s[ks2 >> 1][8 * (ks2 & 1) + mm], sp);
+    for (int mm = 0; mm < 8; ++mm) pv[mm] = s[ks2 >> 1][8 * (ks2 & 1) + mm];
+    u32x4_t t[NT];
+    split8<NT>(pv, t);
 #pragma unroll
-      for (int j = 0; j < NT; ++j) t[j][mm] = sp[j];
-    }
-#pragma unroll
-    for (int j = 0; j < NT; ++j) pb[j][ks2] = pack8(t[j]);
+    for (int j = 0; j < NT; ++j) pb[j][ks2] = __builtin_bit_cast(bf16x8_t, t[j]);
   }
 #pragma unroll
   for (int dt = 0; dt < D / 32; ++dt) {
@@ -312,16 +305,10 @@ HILS_DEV void load_q_operand(const IO* __restrict__ q, int64_t qrow_off, bool ok
 #pragma unroll
       for (int m = 0; m < 8; ++m) x[m] = 0.f;
     }
-    uint16_t t[NT][8];
+    u32x4_t t[NT];
+    split8<NT>(x, t);
 #pragma unroll
-    for (int m = 0; m < 8; ++m) {
-      uint16_t s[NT];
-      split_bf16<NT>(x[m], s);
-#pragma unroll
-      for (int j = 0; j < NT; ++j) t[j][m] = s[j];
-    }
-#pragma unroll
-    for (int j = 0; j < NT; ++j) qb[j][ks] = pack8(t[j]);
+    for (int j = 0; j < NT; ++j) qb[j][ks] = __builtin_bit_cast(bf16x8_t, t[j]);
   }
 }
 
@@ -600,10 +587,10 @@ __global__ void __launch_bounds__(256) fuse(const float* __restrict__ sel_score,
       if (lane < LPS) {
         if constexpr (sizeof(IO) == 2) {
           u32x4_t pk;
-          pk.x = (uint32_t)f32_to_bf16(acc[0] * inv) | ((uint32_t)f32_to_bf16(acc[1] * inv) << 16);
-          pk.y = (uint32_t)f32_to_bf16(acc[2] * inv) | ((uint32_t)f32_to_bf16(acc[3] * inv) << 16);
-          pk.z = (uint32_t)f32_to_bf16(acc[4] * inv) | ((uint32_t)f32_to_bf16(acc[5] * inv) << 16);
-          pk.w = (uint32_t)f32_to_bf16(acc[6] * inv) | ((uint32_t)f32_to_bf16(acc[7] * inv) << 16);
+          pk.x = pack_bf16x2(acc[0] * inv, acc[1] * inv);
+          pk.y = pack_bf16x2(acc[2] * inv, acc[3] * inv);
+          pk.z = pack_bf16x2(acc[4] * inv, acc[5] * inv);
+          pk.w = pack_bf16x2(acc[6] * inv, acc[7] * inv);
           *reinterpret_cast<u32x4_t*>(o + row * D + dpos) = pk;
         } else {
           *reinterpret_cast<float4*>(reinterpret_cast<float*>(o) + row * D + dpos) =

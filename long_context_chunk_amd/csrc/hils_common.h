@@ -22,12 +22,15 @@ struct bf16_t {
 
 HILS_DEV float bf16_to_f32(uint16_t b) { return __uint_as_float(((uint32_t)b) << 16); }
 
-// float -> bf16, round to nearest even (NaN stays NaN)
-HILS_DEV uint16_t f32_to_bf16(float f) {
-  uint32_t x = __float_as_uint(f);
-  if ((x & 0x7f800000u) == 0x7f800000u) return (uint16_t)((x >> 16) | ((x & 0xffffu) ? 0x40u : 0u));
-  x += 0x7fffu + ((x >> 16) & 1u);
-  return (uint16_t)(x >> 16);
+typedef __attribute__((ext_vector_type(2))) float f32x2_t;
+typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2_t;
+
+// float -> bf16, round to nearest even (gfx950 v_cvt_pk_bf16_f32; NaN stays NaN)
+HILS_DEV uint16_t f32_to_bf16(float f) { return __builtin_bit_cast(uint16_t, (__bf16)f); }
+// two floats -> packed bf16 pair (lo in bits 0..15), one instruction
+HILS_DEV uint32_t pack_bf16x2(float lo, float hi) {
+  const f32x2_t v = {lo, hi};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_t));
 }
 
 HILS_DEV uint16_t f32_to_f16(float f) {
@@ -74,6 +77,29 @@ HILS_DEV void split_bf16(float x, uint16_t (&t)[NT]) {
   for (int i = 0; i < NT; ++i) {
     t[i] = f32_to_bf16(x);
     x -= bf16_to_f32(t[i]);
+  }
+}
+
+// The same for 8 values at once into NT packed MFMA operands (term j of element m in
+// lane slot m of out[j]), with packed conversions.  x is consumed.
+template <int NT>
+HILS_DEV void split8(float (&x)[8], u32x4_t (&out)[NT]) {
+#pragma unroll
+  for (int j = 0; j < NT; ++j) {
+    u32x4_t u;
+    u.x = pack_bf16x2(x[0], x[1]);
+    u.y = pack_bf16x2(x[2], x[3]);
+    u.z = pack_bf16x2(x[4], x[5]);
+    u.w = pack_bf16x2(x[6], x[7]);
+    out[j] = u;
+    if (j + 1 < NT) {
+      const uint32_t w4[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+      for (int m = 0; m < 4; ++m) {
+        x[2 * m] -= __uint_as_float(w4[m] << 16);
+        x[2 * m + 1] -= __uint_as_float(w4[m] & 0xffff0000u);
+      }
+    }
   }
 }
 

@@ -183,23 +183,17 @@ HILS_DEV void qhat_rows(const IO* __restrict__ q, const IO* __restrict__ Dw, con
     for (int ks = 0; ks < NKS; ++ks) {
       float v[8];
       load8(ks, v);
-      uint16_t t[NIO][8];
+      u32x4_t t[NIO];
+      split8<NIO>(v, t);
 #pragma unroll
-      for (int m = 0; m < 8; ++m) {
-        uint16_t sp[NIO];
-        split_bf16<NIO>(v[m], sp);
-#pragma unroll
-        for (int j = 0; j < NIO; ++j) t[j][m] = sp[j];
-      }
-#pragma unroll
-      for (int j = 0; j < NIO; ++j) qr[j][ks] = pack8(t[j]);
+      for (int j = 0; j < NIO; ++j) qr[j][ks] = __builtin_bit_cast(bf16x8_t, t[j]);
     }
     // T^T[a][row] = sum_e D[a][e] q[row][e]   (a < r; rows a >= r are zero)
     f32x16_t T = zero16();
     const int a_row = lane & 31;
 #pragma unroll
     for (int ks = 0; ks < NKS; ++ks) {
-      uint16_t dt[NIO][8];
+      u32x4_t dt[NIO];
       float dv[8];
       {
         float a4[4], b4[4];
@@ -212,34 +206,25 @@ HILS_DEV void qhat_rows(const IO* __restrict__ q, const IO* __restrict__ Dw, con
           dv[4 + m] = a_row < r ? b4[m] : 0.f;
         }
       }
-#pragma unroll
-      for (int m = 0; m < 8; ++m) {
-        uint16_t sp[NIO];
-        split_bf16<NIO>(dv[m], sp);
-#pragma unroll
-        for (int j = 0; j < NIO; ++j) dt[j][m] = sp[j];
-      }
+      split8<NIO>(dv, dt);
 #pragma unroll
       for (int i = 0; i < NIO; ++i)
 #pragma unroll
         for (int j = 0; j < NIO; ++j)
-          if (i + j < NIO) T = mfma32(pack8(dt[i]), qr[j][ks], T);
+          if (i + j < NIO) T = mfma32(__builtin_bit_cast(bf16x8_t, dt[i]), qr[j][ks], T);
     }
     // T as the B operand of U T: accumulator register 8*ks2 + m -> k-step ks2, element m
     constexpr int NT = NIO == 1 ? 2 : 3;
     bf16x8_t tb[NT][2];
 #pragma unroll
     for (int ks2 = 0; ks2 < 2; ++ks2) {
-      uint16_t t[NT][8];
+      float tv[8];
 #pragma unroll
-      for (int m = 0; m < 8; ++m) {
-        uint16_t sp[NT];
-        split_bf16<NT>(T[8 * ks2 + m], sp);
+      for (int m = 0; m < 8; ++m) tv[m] = T[8 * ks2 + m];
+      u32x4_t t[NT];
+      split8<NT>(tv, t);
 #pragma unroll
-        for (int j = 0; j < NT; ++j) t[j][m] = sp[j];
-      }
-#pragma unroll
-      for (int j = 0; j < NT; ++j) tb[j][ks2] = pack8(t[j]);
+      for (int j = 0; j < NT; ++j) tb[j][ks2] = __builtin_bit_cast(bf16x8_t, t[j]);
     }
     constexpr int NP = NIO > NT ? NIO : NT;
 #pragma unroll
@@ -248,7 +233,6 @@ HILS_DEV void qhat_rows(const IO* __restrict__ q, const IO* __restrict__ Dw, con
       const int e = 32 * dt2 + (lane & 31);
 #pragma unroll
       for (int ks2 = 0; ks2 < 2; ++ks2) {
-        uint16_t ut[NIO][8];
         float uv[8];
         const int64_t urow = ((int64_t)hh * D + e) * r;
         if ((r & 3) == 0) {  // 4-aligned rows: two vector loads
@@ -268,19 +252,13 @@ HILS_DEV void qhat_rows(const IO* __restrict__ q, const IO* __restrict__ Dw, con
             uv[m] = a < r ? x : 0.f;
           }
         }
-#pragma unroll
-        for (int m = 0; m < 8; ++m) {
-          const float x = uv[m];
-          uint16_t sp[NIO];
-          split_bf16<NIO>(x, sp);
-#pragma unroll
-          for (int j = 0; j < NIO; ++j) ut[j][m] = sp[j];
-        }
+        u32x4_t ut[NIO];
+        split8<NIO>(uv, ut);
 #pragma unroll
         for (int i = 0; i < NIO; ++i)
 #pragma unroll
           for (int j = 0; j < NT; ++j)
-            if (i + j < NP) Q = mfma32(pack8(ut[i]), tb[j][ks2], Q);
+            if (i + j < NP) Q = mfma32(__builtin_bit_cast(bf16x8_t, ut[i]), tb[j][ks2], Q);
       }
       // register rr of this tile is head dim 32*dt2 + acc_row(rr, hf) = k-step 2*dt2 + rr/8, element rr%8
 #pragma unroll
@@ -343,14 +321,15 @@ __global__ void __launch_bounds__(256, 2) score_threshold(const IO* __restrict__
   bf16x8_t qa[NKS + 1];
   float ss = 0.f;
   qhat_rows<IO, D, QCAL>(q, Dw, Uw, hh, r, qrow, row_ok, lane, [&](int ks, const float(&v)[8]) {
-    uint16_t t[8];
+    float x[8];
 #pragma unroll
     for (int m = 0; m < 8; ++m) {
-      const float x = v[m] * tau;
-      ss = fmaf(x, x, ss);
-      t[m] = f32_to_bf16(x);
+      x[m] = v[m] * tau;
+      ss = fmaf(x[m], x[m], ss);
     }
-    qa[ks] = pack8(t);
+    u32x4_t t[1];
+    split8<1>(x, t);
+    qa[ks] = __builtin_bit_cast(bf16x8_t, t[0]);
   });
   ss += __shfl_xor(ss, 32);
   {
@@ -501,16 +480,13 @@ __global__ void __launch_bounds__(256, 2) score_topk_kernel(const IO* __restrict
   // ---- the query's B operands: q^ split into NQ bf16 terms, plus the constant extension
   bf16x8_t qb[NQ][NKS];
   qhat_rows<IO, D, QCAL>(q, Dw, Uw, hh, r, qrow, row_ok, lane, [&](int ks, const float(&v)[8]) {
-    uint16_t t[NQ][8];
+    float x[8];
 #pragma unroll
-    for (int m = 0; m < 8; ++m) {
-      uint16_t sp[NQ];
-      split_bf16<NQ>(v[m], sp);
+    for (int m = 0; m < 8; ++m) x[m] = v[m];
+    u32x4_t t[NQ];
+    split8<NQ>(x, t);
 #pragma unroll
-      for (int j = 0; j < NQ; ++j) t[j][m] = sp[j];
-    }
-#pragma unroll
-    for (int j = 0; j < NQ; ++j) qb[j][ks] = pack8(t[j]);
+    for (int j = 0; j < NQ; ++j) qb[j][ks] = __builtin_bit_cast(bf16x8_t, t[j]);
   });
   bf16x8_t qext;
   {
@@ -730,22 +706,21 @@ __global__ void __launch_bounds__(256) prep_kprime(const float* __restrict__ kc,
     for (int m = 0; m < 8; ++m) s2 = fmaf(x[m], x[m], s2);
 #pragma unroll
     for (int o = 1; o < SPR; o <<= 1) s2 += __shfl_xor(s2, o);
-    uint16_t tm[NK][8], hi[8];
+    float xs[8], xh[8];
 #pragma unroll
     for (int m = 0; m < 8; ++m) {
-      uint16_t sp[NK];
-      split_bf16<NK>(tau * x[m], sp);
-#pragma unroll
-      for (int j = 0; j < NK; ++j) tm[j][m] = sp[j];
-      hi[m] = f32_to_bf16(x[m]);
+      xs[m] = tau * x[m];
+      xh[m] = x[m];
     }
+    u32x4_t tm[NK], hi[1];
+    split8<NK>(xs, tm);
+    split8<1>(xh, hi);
     if (ok) {
       uint16_t* o2 = p2 + rw * DE2;
 #pragma unroll
-      for (int j = 0; j < NK; ++j)
-        *reinterpret_cast<bf16x8_t*>(o2 + j * D + (j ? P2_EXT : 0) + 8 * sg) = pack8(tm[j]);
+      for (int j = 0; j < NK; ++j) *reinterpret_cast<u32x4_t*>(o2 + j * D + (j ? P2_EXT : 0) + 8 * sg) = tm[j];
       uint16_t* o1 = t1 + rw * DE;
-      *reinterpret_cast<bf16x8_t*>(o1 + 8 * sg) = pack8(hi);
+      *reinterpret_cast<u32x4_t*>(o1 + 8 * sg) = hi[0];
       if (sg < 2) {
         uint16_t e[8] = {0, 0, 0, 0, 0, 0, 0, 0}, f[8] = {0, 0, 0, 0, 0, 0, 0, 0};
         if (sg == 0) {
