@@ -31,7 +31,7 @@
 namespace hils {
 
 constexpr int AT_ROWS = 128;        // gathered rows per chunk_attend tile (4 waves x 32)
-constexpr int AT_TILES = 4;         // tiles per chunk_attend work item (one K/V staging)
+constexpr int AT_TILES = 8;         // tiles per chunk_attend work item (one K/V staging)
 constexpr int ITEM_ROWS = AT_ROWS * AT_TILES;
 constexpr int HIST_SLICE = 1 << 18; // selection entries per bucket_count / bucket_scatter workgroup
 constexpr int MAX_C = 16384;        // largest chunk count the LDS histograms hold
@@ -163,56 +163,84 @@ __global__ void __launch_bounds__(256) bucket_scatter(const int32_t* __restrict_
 }
 
 // ------------------------------------------------------ K/V chunk tile in LDS
-// K planes [key][d] (row stride D + 4) feed the A operand of S^T = K Q^T;
-// V^T planes [d][key] (row stride 68) feed the A operand of O^T = V^T P^T.
-// Keys at or beyond `nvalid` are stored as zeros.  NT bf16 terms per value.
+// K planes [key][d] in natural order (row stride D + 8) feed the A operand of
+// S^T = K Q^T, whose k-steps take 8 consecutive head dimensions per lane half;
+// V^T planes [d][key] (row stride 72) feed the A operand of O^T = V^T P^T, with each
+// row's keys stored in MFMA operand order (position 16 ks + 8 h + m holds key
+// kperm(ks, h, m)), so every operand is one 16-byte LDS read.  Keys at or beyond
+// `nvalid` are stored as zeros.  NT bf16 terms per value.
 template <typename IO, int D, int NT>
-struct KVTile {
-  static constexpr int LDK = D + 4;
-  static constexpr int LDV = 64 + 4;
+struct alignas(16) KVTile {
+  static constexpr int LDK = D + 8;
+  static constexpr int LDV = 64 + 8;
   uint16_t k[NT][64 * LDK];
   uint16_t vt[NT][D * LDV];
 };
 
-// Coalesced staging: each thread moves 8 consecutive elements of a key row and a value row.
+// position of key k (0..63) in a V^T row
+HILS_DEV constexpr int vt_pos(int k) {
+  return 16 * (k >> 4) + 8 * ((k >> 2) & 1) + 4 * ((k >> 3) & 1) + (k & 3);
+}
+
+// K: each thread moves 8 consecutive elements of a key row (16-byte loads and stores).
+// V^T: each unit is 2 keys x 4 dims written as 32-bit key pairs; the two halves of a
+// wave take dim groups 8 apart, so a wave's writes fall on distinct banks.
 template <typename IO, int D, int NT>
 HILS_DEV void stage_kv(KVTile<IO, D, NT>& tile, const IO* __restrict__ k, const IO* __restrict__ v, int64_t row0,
                        int nvalid, int tid, int nthreads) {
   constexpr int LDK = KVTile<IO, D, NT>::LDK, LDV = KVTile<IO, D, NT>::LDV;
   for (int i = tid * 8; i < 64 * D; i += nthreads * 8) {
     const int key = i / D, e = i % D;
-    float kx[8], vx[8];
+    float kx[8];
     if (key < nvalid) {
       const int64_t off = (row0 + key) * D + e;
       io_traits<IO>::load4(k, off, *reinterpret_cast<float(*)[4]>(kx));
       io_traits<IO>::load4(k, off + 4, *reinterpret_cast<float(*)[4]>(kx + 4));
-      io_traits<IO>::load4(v, off, *reinterpret_cast<float(*)[4]>(vx));
-      io_traits<IO>::load4(v, off + 4, *reinterpret_cast<float(*)[4]>(vx + 4));
     } else {
 #pragma unroll
-      for (int u = 0; u < 8; ++u) kx[u] = vx[u] = 0.f;
+      for (int u = 0; u < 8; ++u) kx[u] = 0.f;
     }
-    u32x4_t ks[NT], vs[NT];
+    u32x4_t ks[NT];
     split8<NT>(kx, ks);
-    split8<NT>(vx, vs);
 #pragma unroll
-    for (int j = 0; j < NT; ++j) {
-      *reinterpret_cast<u32x2_t*>(&tile.k[j][key * LDK + e]) = u32x2_t{ks[j].x, ks[j].y};
-      *reinterpret_cast<u32x2_t*>(&tile.k[j][key * LDK + e + 4]) = u32x2_t{ks[j].z, ks[j].w};
-      const uint32_t vw[4] = {vs[j].x, vs[j].y, vs[j].z, vs[j].w};
+    for (int j = 0; j < NT; ++j) *reinterpret_cast<u32x4_t*>(&tile.k[j][key * LDK + e]) = ks[j];
+  }
+  const int lane = tid & 63, wv = tid >> 6, nw = nthreads >> 6;
+  const int kp = lane & 31;
+  const int p0 = vt_pos(2 * kp);  // keys 2kp, 2kp+1 sit at p0, p0 + 1
+  for (int U = wv; U < D / 8; U += nw) {
+    const int g = 4 * (U >> 1) + (U & 1) + 2 * (lane >> 5);  // dim group (4 dims)
+    const int d0 = 4 * g;
+    float a0[4], a1[4];
+    if (2 * kp < nvalid) {
+      io_traits<IO>::load4(v, (row0 + 2 * kp) * D + d0, a0);
+    } else {
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        tile.vt[j][(e + 2 * u) * LDV + key] = (uint16_t)(vw[u] & 0xffffu);
-        tile.vt[j][(e + 2 * u + 1) * LDV + key] = (uint16_t)(vw[u] >> 16);
+      for (int u = 0; u < 4; ++u) a0[u] = 0.f;
+    }
+    if (2 * kp + 1 < nvalid) {
+      io_traits<IO>::load4(v, (row0 + 2 * kp + 1) * D + d0, a1);
+    } else {
+#pragma unroll
+      for (int u = 0; u < 4; ++u) a1[u] = 0.f;
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      float x0 = a0[u], x1 = a1[u];
+#pragma unroll
+      for (int j = 0; j < NT; ++j) {
+        const uint32_t w = pack_bf16x2(x0, x1);
+        *reinterpret_cast<uint32_t*>(&tile.vt[j][(d0 + u) * LDV + p0]) = w;
+        if (j + 1 < NT) {
+          x0 -= __uint_as_float(w << 16);
+          x1 -= __uint_as_float(w & 0xffff0000u);
+        }
       }
     }
   }
 }
 
-HILS_DEV bf16x8_t lds_kop(const uint16_t* rowp, int ks, int hf) {
-  const uint16_t* p = rowp + 16 * ks + 4 * hf;
-  return pack8(*reinterpret_cast<const u32x2_t*>(p), *reinterpret_cast<const u32x2_t*>(p + 8));
-}
+HILS_DEV bf16x8_t lds_op16(const uint16_t* p) { return *reinterpret_cast<const bf16x8_t*>(p); }
 
 // One wave: 32 query rows (B operands qb, NT terms) against the staged chunk.
 // Returns, per lane (row n = lane & 31, half hf), the O^T accumulators (unnormalised)
@@ -234,7 +262,7 @@ HILS_DEV void wave_chunk_attention(const KVTile<IO, D, NT>& tile, const bf16x8_t
     for (int ks = 0; ks < NKS; ++ks)
 #pragma unroll
       for (int j = 0; j < NT; ++j) {
-        const bf16x8_t a = lds_kop(&tile.k[j][key * LDK], ks, hf);
+        const bf16x8_t a = lds_op16(&tile.k[j][key * LDK + 16 * ks + 8 * hf]);
 #pragma unroll
         for (int i = 0; i < NT; ++i)
           if (i + j < NT) s[tt] = mfma32(a, qb[i][ks], s[tt]);
@@ -248,9 +276,12 @@ HILS_DEV void wave_chunk_attention(const KVTile<IO, D, NT>& tile, const bf16x8_t
       const int key = 32 * tt + acc_row(rr, hf);
       const float z = key < key_lim ? s[tt][rr] * tau : -INFINITY;
       s[tt][rr] = z;
-      m = fmaxf(m, z);
+      m = z > m ? z : m;
     }
-  m = fmaxf(m, __shfl_xor(m, 32));
+  {
+    const float mo = __shfl_xor(m, 32);
+    m = mo > m ? mo : m;
+  }
   float l = 0.f;
 #pragma unroll
   for (int tt = 0; tt < 2; ++tt)
@@ -281,7 +312,7 @@ HILS_DEV void wave_chunk_attention(const KVTile<IO, D, NT>& tile, const bf16x8_t
     for (int ks2 = 0; ks2 < 4; ++ks2)
 #pragma unroll
       for (int j = 0; j < NT; ++j) {
-        const bf16x8_t a = lds_kop(&tile.vt[j][e * LDV], ks2, hf);
+        const bf16x8_t a = lds_op16(&tile.vt[j][e * LDV + 16 * ks2 + 8 * hf]);
 #pragma unroll
         for (int i = 0; i < NT; ++i)
           if (i + j < NT) o[dt] = mfma32(a, pb[i][ks2], o[dt]);
@@ -299,8 +330,8 @@ HILS_DEV void load_q_operand(const IO* __restrict__ q, int64_t qrow_off, bool ok
   for (int ks = 0; ks < D / 16; ++ks) {
     float x[8];
     if (ok) {
-      io_traits<IO>::load4(q, qrow_off + kperm(ks, hf, 0), *reinterpret_cast<float(*)[4]>(x));
-      io_traits<IO>::load4(q, qrow_off + kperm(ks, hf, 4), *reinterpret_cast<float(*)[4]>(x + 4));
+      io_traits<IO>::load4(q, qrow_off + 16 * ks + 8 * hf, *reinterpret_cast<float(*)[4]>(x));
+      io_traits<IO>::load4(q, qrow_off + 16 * ks + 8 * hf + 4, *reinterpret_cast<float(*)[4]>(x + 4));
     } else {
 #pragma unroll
       for (int m = 0; m < 8; ++m) x[m] = 0.f;
@@ -317,7 +348,7 @@ template <int D>
 HILS_DEV void lds_q_operand(const uint16_t* rowp, bf16x8_t (&qb)[1][D / 16]) {
   const int hf = (threadIdx.x & 63) >> 5;
 #pragma unroll
-  for (int ks = 0; ks < D / 16; ++ks) qb[0][ks] = lds_kop(rowp, ks, hf);
+  for (int ks = 0; ks < D / 16; ++ks) qb[0][ks] = lds_op16(rowp + 16 * ks + 8 * hf);
 }
 
 template <typename IO>
@@ -372,33 +403,44 @@ __global__ void __launch_bounds__(256, 2) chunk_attend(const IO* __restrict__ q,
   const int kvh = h / (Hq / Hkv);
   const int64_t row0 = ((int64_t)b * Hkv + kvh) * N + (int64_t)c * 64;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, hf = lane >> 5;
-  for (int r = tid; r < ITEM_ROWS; r += 256) {
+  // each wave records the pair ids and query rows of its own 32 rows of every tile, so
+  // its gathers need no barrier and the first one overlaps the K/V staging below
+#pragma unroll
+  for (int j = 0; j < AT_TILES; j += 2) {
+    const int r = (j + (lane >> 5)) * AT_ROWS + 32 * w + (lane & 31);
     const uint32_t e = (uint32_t)r < nrows ? pp[r] : 0xffffffffu;
     ipid[r] = e;
     irow[r] = e != 0xffffffffu ? e / (uint32_t)K : 0u;
   }
-  stage_kv<IO, D, NT>(tile, k, v, row0, 64, tid, 256);
-  __syncthreads();
+  __builtin_amdgcn_wave_barrier();
   const int ntile = (int)((nrows + AT_ROWS - 1) / AT_ROWS);
   const int rl = 32 * w + (lane & 31);
   if constexpr (STAGE) {
     uint16_t* myq = &qs[32 * w * LDQ];   // this wave's 32 staged rows
     const int lr = lane / SEGS, sg = lane % SEGS;
-    u32x4_t qn[NLD];
-    // rows beyond the item load query row 0 (in bounds) and store nothing
-    auto gather = [&](int j) {
+    // query rows of tiles j and j+1 in flight (two register buffers); rows beyond the
+    // item load query row 0 (in bounds) and store nothing
+    u32x4_t qn[2][NLD];
+    auto gather = [&](int j, int buf) {
 #pragma unroll
       for (int u = 0; u < NLD; ++u) {
         const int r = j * AT_ROWS + 32 * w + RPL * u + lr;
-        qn[u] = *reinterpret_cast<const u32x4_t*>(q + (int64_t)irow[r] * D + 8 * sg);
+        qn[buf][u] = *reinterpret_cast<const u32x4_t*>(q + (int64_t)irow[r] * D + 8 * sg);
       }
     };
-    gather(0);
-    for (int j = 0; j < ntile; ++j) {
+    gather(0, 0);
+    if (ntile > 1) gather(1, 1);
+    stage_kv<IO, D, NT>(tile, k, v, row0, 64, tid, 256);
+    __syncthreads();
+    // unrolled over the (at most AT_TILES) tiles, so the buffers are registers
 #pragma unroll
-      for (int u = 0; u < NLD; ++u) *reinterpret_cast<u32x4_t*>(&myq[(RPL * u + lr) * LDQ + 8 * sg]) = qn[u];
+    for (int j = 0; j < AT_TILES; ++j) {
+      if (j >= ntile) break;
+#pragma unroll
+      for (int u = 0; u < NLD; ++u)
+        *reinterpret_cast<u32x4_t*>(&myq[(RPL * u + lr) * LDQ + 8 * sg]) = qn[j & 1][u];
       __builtin_amdgcn_wave_barrier();
-      if (j + 1 < ntile) gather(j + 1);
+      if (j + 2 < ntile) gather(j + 2, j & 1);
       bf16x8_t qb[1][D / 16];
       lds_q_operand<D>(&myq[(lane & 31) * LDQ], qb);
       f32x16_t o[D / 32];
@@ -430,6 +472,8 @@ __global__ void __launch_bounds__(256, 2) chunk_attend(const IO* __restrict__ q,
       __builtin_amdgcn_wave_barrier();
     }
   } else {
+    stage_kv<IO, D, NT>(tile, k, v, row0, 64, tid, 256);
+    __syncthreads();
     for (int j = 0; j < ntile; ++j) {
       const int r = j * AT_ROWS + rl;
       const uint32_t e_pair = ipid[r];
