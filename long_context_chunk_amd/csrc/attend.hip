@@ -163,81 +163,67 @@ __global__ void __launch_bounds__(256) bucket_scatter(const int32_t* __restrict_
 }
 
 // ------------------------------------------------------ K/V chunk tile in LDS
-// K planes [key][d] in natural order (row stride D + 8) feed the A operand of
-// S^T = K Q^T, whose k-steps take 8 consecutive head dimensions per lane half;
-// V^T planes [d][key] (row stride 72) feed the A operand of O^T = V^T P^T, with each
-// row's keys stored in MFMA operand order (position 16 ks + 8 h + m holds key
-// kperm(ks, h, m)), so every operand is one 16-byte LDS read.  Keys at or beyond
-// `nvalid` are stored as zeros.  NT bf16 terms per value.
+// Both planes in natural [key][d] order, staged with 16-byte loads and stores.
+// K (row stride D + 8) feeds the A operand of S^T = K Q^T, whose k-steps take 8
+// consecutive head dimensions per lane half: one 16-byte LDS read per operand.
+// V (row stride D + 32) feeds the A operand of O^T = V^T P^T (dims as rows, keys as k)
+// through ds_read_b64_tr_b16 transposing reads: within a 16-lane group, lane j points at
+// the 4 dims 4(j&3).. of key (j>>2) and lane i receives 4 consecutive keys of dim i.
+// Keys at or beyond `nvalid` are stored as zeros.  NT bf16 terms per value.
 template <typename IO, int D, int NT>
 struct alignas(16) KVTile {
   static constexpr int LDK = D + 8;
-  static constexpr int LDV = 64 + 8;
+  static constexpr int LDV = D + 32;
   uint16_t k[NT][64 * LDK];
-  uint16_t vt[NT][D * LDV];
+  uint16_t v[NT][64 * LDV];
 };
 
-// position of key k (0..63) in a V^T row
-HILS_DEV constexpr int vt_pos(int k) {
-  return 16 * (k >> 4) + 8 * ((k >> 2) & 1) + 4 * ((k >> 3) & 1) + (k & 3);
-}
-
-// K: each thread moves 8 consecutive elements of a key row (16-byte loads and stores).
-// V^T: each unit is 2 keys x 4 dims written as 32-bit key pairs; the two halves of a
-// wave take dim groups 8 apart, so a wave's writes fall on distinct banks.
 template <typename IO, int D, int NT>
 HILS_DEV void stage_kv(KVTile<IO, D, NT>& tile, const IO* __restrict__ k, const IO* __restrict__ v, int64_t row0,
                        int nvalid, int tid, int nthreads) {
   constexpr int LDK = KVTile<IO, D, NT>::LDK, LDV = KVTile<IO, D, NT>::LDV;
   for (int i = tid * 8; i < 64 * D; i += nthreads * 8) {
     const int key = i / D, e = i % D;
-    float kx[8];
+    float kx[8], vx[8];
     if (key < nvalid) {
       const int64_t off = (row0 + key) * D + e;
       io_traits<IO>::load4(k, off, *reinterpret_cast<float(*)[4]>(kx));
       io_traits<IO>::load4(k, off + 4, *reinterpret_cast<float(*)[4]>(kx + 4));
+      io_traits<IO>::load4(v, off, *reinterpret_cast<float(*)[4]>(vx));
+      io_traits<IO>::load4(v, off + 4, *reinterpret_cast<float(*)[4]>(vx + 4));
     } else {
 #pragma unroll
-      for (int u = 0; u < 8; ++u) kx[u] = 0.f;
+      for (int u = 0; u < 8; ++u) kx[u] = vx[u] = 0.f;
     }
-    u32x4_t ks[NT];
+    u32x4_t ks[NT], vs[NT];
     split8<NT>(kx, ks);
+    split8<NT>(vx, vs);
 #pragma unroll
-    for (int j = 0; j < NT; ++j) *reinterpret_cast<u32x4_t*>(&tile.k[j][key * LDK + e]) = ks[j];
-  }
-  const int lane = tid & 63, wv = tid >> 6, nw = nthreads >> 6;
-  const int kp = lane & 31;
-  const int p0 = vt_pos(2 * kp);  // keys 2kp, 2kp+1 sit at p0, p0 + 1
-  for (int U = wv; U < D / 8; U += nw) {
-    const int g = 4 * (U >> 1) + (U & 1) + 2 * (lane >> 5);  // dim group (4 dims)
-    const int d0 = 4 * g;
-    float a0[4], a1[4];
-    if (2 * kp < nvalid) {
-      io_traits<IO>::load4(v, (row0 + 2 * kp) * D + d0, a0);
-    } else {
-#pragma unroll
-      for (int u = 0; u < 4; ++u) a0[u] = 0.f;
-    }
-    if (2 * kp + 1 < nvalid) {
-      io_traits<IO>::load4(v, (row0 + 2 * kp + 1) * D + d0, a1);
-    } else {
-#pragma unroll
-      for (int u = 0; u < 4; ++u) a1[u] = 0.f;
-    }
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      float x0 = a0[u], x1 = a1[u];
-#pragma unroll
-      for (int j = 0; j < NT; ++j) {
-        const uint32_t w = pack_bf16x2(x0, x1);
-        *reinterpret_cast<uint32_t*>(&tile.vt[j][(d0 + u) * LDV + p0]) = w;
-        if (j + 1 < NT) {
-          x0 -= __uint_as_float(w << 16);
-          x1 -= __uint_as_float(w & 0xffff0000u);
-        }
-      }
+    for (int j = 0; j < NT; ++j) {
+      *reinterpret_cast<u32x4_t*>(&tile.k[j][key * LDK + e]) = ks[j];
+      *reinterpret_cast<u32x4_t*>(&tile.v[j][key * LDV + e]) = vs[j];
     }
   }
+}
+
+typedef __attribute__((ext_vector_type(4))) short s16x4_t;
+typedef __attribute__((address_space(3))) s16x4_t lds_s16x4_t;
+
+// A operand of O^T = V^T P^T for dim tile dt, key k-step ks2: lane l (dim 32 dt + (l & 31),
+// half h = l >> 5) gets keys kperm(ks2, h, 0..7) of its dim, in two transposing reads
+template <int LDV>
+HILS_DEV bf16x8_t vt_operand(const uint16_t* vplane, int dt, int ks2, int lane) {
+  const int g = lane >> 4, j = lane & 15;
+  const int e = 32 * dt + 16 * (g & 1) + 4 * (j & 3);
+  const int key = 16 * ks2 + 4 * (g >> 1) + (j >> 2);
+  const s16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(vplane + key * LDV + e));
+  const s16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(vplane + (key + 8) * LDV + e));
+  u32x4_t u;
+  u.x = (uint32_t)(uint16_t)lo[0] | ((uint32_t)(uint16_t)lo[1] << 16);
+  u.y = (uint32_t)(uint16_t)lo[2] | ((uint32_t)(uint16_t)lo[3] << 16);
+  u.z = (uint32_t)(uint16_t)hi[0] | ((uint32_t)(uint16_t)hi[1] << 16);
+  u.w = (uint32_t)(uint16_t)hi[2] | ((uint32_t)(uint16_t)hi[3] << 16);
+  return __builtin_bit_cast(bf16x8_t, u);
 }
 
 HILS_DEV bf16x8_t lds_op16(const uint16_t* p) { return *reinterpret_cast<const bf16x8_t*>(p); }
@@ -307,12 +293,11 @@ HILS_DEV void wave_chunk_attention(const KVTile<IO, D, NT>& tile, const bf16x8_t
 #pragma unroll
   for (int dt = 0; dt < D / 32; ++dt) {
     o[dt] = zero16();
-    const int e = 32 * dt + (lane & 31);
 #pragma unroll
     for (int ks2 = 0; ks2 < 4; ++ks2)
 #pragma unroll
       for (int j = 0; j < NT; ++j) {
-        const bf16x8_t a = lds_op16(&tile.vt[j][e * LDV + 16 * ks2 + 8 * hf]);
+        const bf16x8_t a = vt_operand<LDV>(tile.v[j], dt, ks2, lane);
 #pragma unroll
         for (int i = 0; i < NT; ++i)
           if (i + j < NT) o[dt] = mfma32(a, pb[i][ks2], o[dt]);
@@ -510,9 +495,14 @@ __global__ void __launch_bounds__(128) own_attend(const IO* __restrict__ q, cons
   constexpr int NT = io_traits<IO>::terms;
   using PT = typename partial_t<IO>::type;
   __shared__ KVTile<IO, D, NT> tile;
-  const int qc = blockIdx.x % NQC, bh = blockIdx.x / NQC;
-  const int h = bh % Hq, b = bh / Hq;
-  const int kvh = h / (Hq / Hkv);
+  // consecutive workgroups: the G query heads of one (b, KV head, chunk), so the
+  // chunk's K/V is read from HBM once and reused from L2
+  const int G = Hq / Hkv;
+  const int gi = blockIdx.x % G, rest = blockIdx.x / G;
+  const int qc = rest % NQC, bkv = rest / NQC;
+  const int kvh = bkv % Hkv, b = bkv / Hkv;
+  const int h = kvh * G + gi;
+  const int bh = b * Hq + h;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, hf = lane >> 5;
   const int key0 = qc * 64;
   const int nkeys = min(64, N - key0);
