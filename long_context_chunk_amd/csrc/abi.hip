@@ -218,17 +218,18 @@ int run_decode(const hils_dims_t* dims, const void* q, const void* k_cache, cons
   if (!ws && need > 0) return fail(HILS_E_WORKSPACE, "workspace is NULL (%zu bytes needed)", need);
   if (ws_bytes < need) return fail(HILS_E_WORKSPACE, "workspace too small: %zu < %zu", ws_bytes, need);
   hipStream_t st = (hipStream_t)stream;
-  hipEvent_t ev[5] = {};
+  constexpr int NS = HILS_DECODE_STAGES;
+  hipEvent_t ev[NS + 1] = {};
   hipError_t e = hipSuccess;
   if (stage_ms)
-    for (int i = 0; i < 5 && e == hipSuccess; ++i) e = hipEventCreate(&ev[i]);
+    for (int i = 0; i <= NS && e == hipSuccess; ++i) e = hipEventCreate(&ev[i]);
   if (e == hipSuccess)
     e = hils::launch_decode(g, q, k_cache, v_cache, seq_lens, kc, bc, qcal_D, qcal_U, sel_idx_out, o, ws, ws_bytes,
                             st, stage_ms ? ev : nullptr);
   if (stage_ms) {
-    if (e == hipSuccess) e = hipEventSynchronize(ev[4]);
-    for (int i = 0; i < 4 && e == hipSuccess; ++i) e = hipEventElapsedTime(&stage_ms[i], ev[i], ev[i + 1]);
-    for (int i = 0; i < 5; ++i)
+    if (e == hipSuccess) e = hipEventSynchronize(ev[NS]);
+    for (int i = 0; i < NS && e == hipSuccess; ++i) e = hipEventElapsedTime(&stage_ms[i], ev[i], ev[i + 1]);
+    for (int i = 0; i <= NS; ++i)
       if (ev[i]) hipEventDestroy(ev[i]);
   }
   if (e != hipSuccess) return hip_fail(e, "hils_attn_decode");

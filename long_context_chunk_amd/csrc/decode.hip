@@ -2,34 +2,39 @@
 // L_b - 1 (L_b = seq_lens[b], the cache length including the current token).
 //
 //   1. decode_scan    s_c = q^ . k'_c / sqrt(d) + b'_c for every complete past
-//                     chunk c < floor((L_b - 1)/S)  (fp32 GEMV, streams k' from HBM:
-//                     the dominant traffic of a decode step)
-//   2. decode_topk    exact top-K per (b, h) by radix selection on the ordered
-//                     score bits; ties at the threshold go to the lower chunk id
-//   3. decode_attend  one workgroup per (b, h, selected chunk) plus one for the
-//                     own (causal) chunk: gathers the chunk's K/V rows (coalesced),
-//                     softmax inside the chunk, o_c and its score (own: exact LSE)
-//   4. decode_combine softmax over the chunk scores, fused output
+//                     chunk c < floor((L_b - 1)/S)  (fp32 GEMV streaming k' from HBM:
+//                     the dominant traffic of a decode step).  Each workgroup keeps
+//                     the best 32 of its 1024 chunks (64-bit selection keys, bitonic
+//                     lane networks); decode_merge merges the splits of a (b, h) into
+//                     the exact top-K (ties to the lower chunk id).
+//   2. decode_attend  one workgroup per (b, h, selected chunk) plus one for the own
+//                     (causal) chunk: gathers the chunk's K/V rows (coalesced),
+//                     softmax inside the chunk, o_c and its score (own: exact LSE);
+//                     decode_combine fuses them with the softmax over the scores.
 // (aitrends.kr article, "Methodology" and "Main results": sparse KV access gives
 // near-constant decode cost; hotpaper.ai abstract: chunk outputs fused by the
 // retrieval scores.)
+#include <algorithm>
+
 #include "hils_common.h"
 #include "kernels.h"
 
 namespace hils {
 
-constexpr int DS_CHUNKS = 256;  // chunks scored per decode_scan workgroup
+constexpr int DS_CHUNKS = 1024;  // chunks scored per decode_scan workgroup
+constexpr int DS_KEEP = 32;      // candidates kept per workgroup (>= K)
 
 struct DecodeWs {
-  size_t scores, sel_i, sel_s, nsel, part, sig, total;
+  size_t cand, sel_i, sel_s, nsel, part, sig, total;
 };
 static size_t al2(size_t x) { return (x + 255) / 256 * 256; }
+static int nsplit_of(const Geom& g) { return (g.C() + DS_CHUNKS - 1) / DS_CHUNKS; }
 static DecodeWs decode_ws(const Geom& g) {
   DecodeWs w;
   const size_t bh = (size_t)g.B * g.Hq;
   size_t off = 0;
-  w.scores = off;
-  off += al2(bh * g.C() * 4);
+  w.cand = off;
+  off += al2(bh * std::max(1, nsplit_of(g)) * DS_KEEP * 8);
   w.sel_i = off;
   off += al2(bh * g.K * 4);
   w.sel_s = off;
@@ -44,6 +49,54 @@ static DecodeWs decode_ws(const Geom& g) {
   return w;
 }
 size_t decode_workspace_bytes(const Geom& g) { return decode_ws(g).total; }
+
+// 64-bit selection keys (make_key: larger = better, ties to the lower chunk; 0 = none)
+// exchanged with lane j ^ X of the same 32-lane half
+template <int X>
+HILS_DEV uint64_t dxl(uint64_t v) {
+  const int j = threadIdx.x & 31;
+  uint32_t lo = (uint32_t)v, hi = (uint32_t)(v >> 32);
+  if constexpr (X == 16) {
+    lo = (uint32_t)__builtin_amdgcn_ds_swizzle((int)lo, 0x401F);
+    hi = (uint32_t)__builtin_amdgcn_ds_swizzle((int)hi, 0x401F);
+  } else if constexpr (X == 31) {
+    lo = (uint32_t)__builtin_amdgcn_ds_swizzle((int)lo, 0x7C1F);
+    hi = (uint32_t)__builtin_amdgcn_ds_swizzle((int)hi, 0x7C1F);
+  } else {
+    lo = (uint32_t)__shfl_xor((int)lo, X);
+    hi = (uint32_t)__shfl_xor((int)hi, X);
+  }
+  (void)j;
+  return ((uint64_t)hi << 32) | lo;
+}
+template <int X>
+HILS_DEV void dcx(uint64_t& k, bool keep_larger) {
+  const uint64_t p = dxl<X>(k);
+  k = ((p > k) == keep_larger) ? p : k;
+}
+// bitonic sort of one key per lane, best first, within each 32-lane half
+HILS_DEV void dsort32(uint64_t& k) {
+  const int j = threadIdx.x & 31;
+#define HILS_STAGE(K_, X_) dcx<X_>(k, ((j & X_) == 0) == (((j & K_) == 0) || K_ == 32));
+  HILS_STAGE(2, 1)
+  HILS_STAGE(4, 2) HILS_STAGE(4, 1)
+  HILS_STAGE(8, 4) HILS_STAGE(8, 2) HILS_STAGE(8, 1)
+  HILS_STAGE(16, 8) HILS_STAGE(16, 4) HILS_STAGE(16, 2) HILS_STAGE(16, 1)
+  HILS_STAGE(32, 16) HILS_STAGE(32, 8) HILS_STAGE(32, 4) HILS_STAGE(32, 2) HILS_STAGE(32, 1)
+#undef HILS_STAGE
+}
+// merge unsorted keys nk into the sorted (best-first) list lk of each half; keep 32
+HILS_DEV void dmerge(uint64_t& lk, uint64_t nk) {
+  const int j = threadIdx.x & 31;
+  dsort32(nk);
+  const uint64_t r = dxl<31>(nk);
+  lk = r > lk ? r : lk;
+  dcx<16>(lk, (j & 16) == 0);
+  dcx<8>(lk, (j & 8) == 0);
+  dcx<4>(lk, (j & 4) == 0);
+  dcx<2>(lk, (j & 2) == 0);
+  dcx<1>(lk, (j & 1) == 0);
+}
 
 // q^ = q + U (D q) for one head into LDS (fp32).  256 threads.
 template <typename IO, int D>
@@ -72,33 +125,40 @@ template <typename IO, int D>
 __global__ void __launch_bounds__(256) decode_scan(const IO* __restrict__ q, const IO* __restrict__ Dw,
                                                    const IO* __restrict__ Uw, const float* __restrict__ kc,
                                                    const float* __restrict__ bc, const int32_t* __restrict__ seq_lens,
-                                                   float* __restrict__ scores, int Hq, int C, int r, int nsplit) {
+                                                   uint64_t* __restrict__ cand, int Hq, int C, int r, int nsplit) {
   __shared__ float qs[D];
   __shared__ float ts[32];
+  __shared__ uint64_t keys[DS_CHUNKS];
+  __shared__ uint64_t wl[4][32];
   const int sp = blockIdx.x % nsplit, bh = blockIdx.x / nsplit;
   const int b = bh / Hq, h = bh % Hq;
   const int L = seq_lens[b];
   const int P = min(C, (L - 1) / 64);
   const int c_beg = sp * DS_CHUNKS, c_end = min(P, c_beg + DS_CHUNKS);
-  if (c_beg >= c_end) return;
+  const int t = threadIdx.x, lane = t & 63, w = t >> 6;
   qhat_to_lds<IO, D>(q + (int64_t)bh * D, Dw, Uw, h, r, qs, ts);
   constexpr int TPC = D / 4;        // threads per chunk (one float4 each)
   constexpr int CPP = 256 / TPC;    // chunks per pass
-  const int t = threadIdx.x, sub = t % TPC, grp = t / TPC;
+  constexpr int UNR = 8;            // passes in flight
+  constexpr int STEP = CPP * UNR;
+  const int sub = t % TPC, grp = t / TPC;
   const float4 qv = *reinterpret_cast<const float4*>(&qs[4 * sub]);
   const float tau = 1.0f / sqrtf((float)D);
   const float* kb = kc + (int64_t)bh * C * D;
   const float* bb = bc + (int64_t)bh * C;
-  float* sb = scores + (int64_t)bh * C;
-  constexpr int UNR = 4;
-  for (int c0 = c_beg; c0 < c_end; c0 += CPP * UNR) {
-    float4 kv[UNR];
+  // chunks beyond c_end load chunk c_end - 1 (in bounds) and are dropped; two register
+  // buffers alternate so that the next UNR passes are in flight during the current ones
+  float4 ka[UNR], kb2[UNR];
+  float ba[UNR], bb2[UNR];
+  auto load = [&](int c0, float4(&kv)[UNR], float(&bv)[UNR]) {
 #pragma unroll
     for (int u = 0; u < UNR; ++u) {
-      const int c = c0 + u * CPP + grp;
-      kv[u] = c < c_end ? *reinterpret_cast<const float4*>(kb + (int64_t)c * D + 4 * sub)
-                        : make_float4(0.f, 0.f, 0.f, 0.f);
+      const int c = min(c0 + u * CPP + grp, c_end - 1);
+      kv[u] = *reinterpret_cast<const float4*>(kb + (int64_t)c * D + 4 * sub);
+      bv[u] = bb[c];
     }
+  };
+  auto score = [&](int c0, const float4(&kv)[UNR], const float(&bv)[UNR]) {
 #pragma unroll
     for (int u = 0; u < UNR; ++u) {
       float s = qv.x * kv[u].x;
@@ -108,126 +168,60 @@ __global__ void __launch_bounds__(256) decode_scan(const IO* __restrict__ q, con
 #pragma unroll
       for (int o = TPC / 2; o >= 1; o >>= 1) s += __shfl_xor(s, o);
       const int c = c0 + u * CPP + grp;
-      if (sub == 0 && c < c_end) sb[c] = fmaf(s, tau, bb[c]);
+      if (sub == 0) keys[c - c_beg] = c < c_end ? make_key(fmaf(s, tau, bv[u]), c) : 0ull;
     }
+  };
+  static_assert(DS_CHUNKS % (2 * STEP) == 0, "");
+  if (c_beg < c_end) load(c_beg, ka, ba);
+  for (int c0 = c_beg; c0 < c_beg + DS_CHUNKS; c0 += 2 * STEP) {
+    if (c0 + STEP < c_end) load(c0 + STEP, kb2, bb2);
+    score(c0, ka, ba);
+    if (c0 + 2 * STEP < c_end) load(c0 + 2 * STEP, ka, ba);
+    score(c0 + STEP, kb2, bb2);
+  }
+  __syncthreads();
+  // best 32 of this workgroup's chunks: each half-wave sorts 4 x 32 keys, the halves
+  // and then the four waves are merged
+  {
+    const int base = w * 256 + (lane >> 5) * 128 + (lane & 31);
+    uint64_t lk = keys[base];
+    dsort32(lk);
+    dmerge(lk, keys[base + 32]);
+    dmerge(lk, keys[base + 64]);
+    dmerge(lk, keys[base + 96]);
+    const uint64_t other = __shfl(lk, (lane & 31) + 32);
+    dmerge(lk, other);
+    if (lane < 32) wl[w][lane] = lk;
+  }
+  __syncthreads();
+  if (w == 0) {
+    uint64_t lk = wl[0][lane & 31];
+    dmerge(lk, wl[1][lane & 31]);
+    dmerge(lk, wl[2][lane & 31]);
+    dmerge(lk, wl[3][lane & 31]);
+    if (lane < 32) cand[((int64_t)bh * nsplit + sp) * DS_KEEP + lane] = lk;
   }
 }
 
-// exact top-K of the P scores of one (b, h); output in rank order.  The scores
-// are staged in LDS once; four 8-bit radix passes on the ordered score bits find
-// the K-th best value, then ties at that value are taken by ascending chunk id.
-constexpr int TK_MAXC = 16384;  // largest chunk count decode_topk stages in LDS
-
-__global__ void __launch_bounds__(256) decode_topk(const float* __restrict__ scores, const int32_t* __restrict__ seq_lens,
-                                                   int32_t* __restrict__ sel_i, float* __restrict__ sel_s,
-                                                   int32_t* __restrict__ nsel_out, int32_t* __restrict__ sel_user,
-                                                   int Hq, int C, int K) {
-  __shared__ uint32_t ov[TK_MAXC];
-  __shared__ uint32_t hist[256];
-  __shared__ uint32_t sh_prefix, sh_need;
-  __shared__ uint32_t cnt_gt[256], cnt_eq[256];
-  __shared__ uint64_t picked[32];
-  const int bh = blockIdx.x, b = bh / Hq;
-  const int t = threadIdx.x, lane = t & 63, w = t >> 6;
-  const int L = seq_lens[b];
+// exact top-K of one (b, h) from the candidates of its splits (one wave); rank order
+__global__ void __launch_bounds__(64) decode_merge(const uint64_t* __restrict__ cand,
+                                                   const int32_t* __restrict__ seq_lens, int32_t* __restrict__ sel_i,
+                                                   float* __restrict__ sel_s, int32_t* __restrict__ nsel_out,
+                                                   int32_t* __restrict__ sel_user, int Hq, int C, int K, int nsplit) {
+  const int bh = blockIdx.x, lane = threadIdx.x;
+  const int L = seq_lens[bh / Hq];
   const int P = min(C, (L - 1) / 64);
+  uint64_t lk = 0;
+  for (int s2 = 0; s2 < nsplit; ++s2) dmerge(lk, cand[((int64_t)bh * nsplit + s2) * DS_KEEP + (lane & 31)]);
   const int n = min(K, P);
-  const float* sb = scores + (int64_t)bh * C;
-  for (int c = t; c < P; c += 256) ov[c] = order_f32(sb[c]);
-  const int per = (P + 255) / 256;
-  const int beg = min(P, t * per), end = min(P, beg + per);
-  uint32_t prefix = 0, mask = 0;
-  uint32_t need = (uint32_t)n;
-  __syncthreads();
-  if (n > 0) {
-    for (int pass = 0; pass < 4; ++pass) {
-      const int shift = 24 - 8 * pass;
-      hist[t] = 0;
-      __syncthreads();
-      for (int c = t; c < P; c += 256) {
-        const uint32_t o = ov[c];
-        if ((o & mask) == prefix) atomicAdd(&hist[(o >> shift) & 255u], 1u);
-      }
-      __syncthreads();
-      if (w == 0) {
-        // lane owns digits 4*lane .. 4*lane+3; suffix sums from the top digit down
-        const uint32_t h0 = hist[4 * lane], h1 = hist[4 * lane + 1], h2 = hist[4 * lane + 2], h3 = hist[4 * lane + 3];
-        const uint32_t mine = h0 + h1 + h2 + h3;
-        // inclusive suffix scan over lanes of `mine`; `above` = count of digits > 4*lane+3
-        uint32_t suf = mine;
-        for (int o = 1; o < 64; o <<= 1) {
-          const uint32_t x = __shfl_down(suf, o);
-          if (lane + o < 64) suf += x;
-        }
-        const uint32_t above = suf - mine;
-        // the digit d with (count > d) < need <= (count >= d)
-        const uint32_t c3 = above + h3, c2 = c3 + h2, c1 = c2 + h1, c0 = c1 + h0;
-        int dg = -1;
-        uint32_t cum = 0;
-        if (above < need && c3 >= need) { dg = 4 * lane + 3; cum = above; }
-        else if (c3 < need && c2 >= need) { dg = 4 * lane + 2; cum = c3; }
-        else if (c2 < need && c1 >= need) { dg = 4 * lane + 1; cum = c2; }
-        else if (c1 < need && c0 >= need) { dg = 4 * lane; cum = c1; }
-        if (dg >= 0) {
-          sh_prefix = prefix | ((uint32_t)dg << shift);
-          sh_need = need - cum;
-        }
-      }
-      __syncthreads();
-      prefix = sh_prefix;
-      need = sh_need;
-      mask |= 255u << shift;
-      __syncthreads();
-    }
+  if (lane < K) {
+    const bool ok = lane < n && lk != 0;
+    const int32_t ci = ok ? key_chunk(lk) : -1;
+    sel_i[(int64_t)bh * K + lane] = ci;
+    sel_s[(int64_t)bh * K + lane] = ok ? key_score(lk) : -INFINITY;
+    if (sel_user) sel_user[(int64_t)bh * K + lane] = ci;
   }
-  // prefix = ordered bits of the K-th best score; `need` of the elements equal to it are taken (lowest ids)
-  uint32_t gt = 0, eq = 0;
-  for (int c = beg; c < end; ++c) {
-    const uint32_t o = ov[c];
-    gt += o > prefix;
-    eq += o == prefix;
-  }
-  cnt_gt[t] = gt;
-  cnt_eq[t] = eq;
-  __syncthreads();
-  for (int o = 1; o < 256; o <<= 1) {
-    const uint32_t a = t >= o ? cnt_gt[t - o] : 0, e = t >= o ? cnt_eq[t - o] : 0;
-    __syncthreads();
-    cnt_gt[t] += a;
-    cnt_eq[t] += e;
-    __syncthreads();
-  }
-  if (n > 0 && (gt | eq)) {
-    uint32_t pos_gt = cnt_gt[t] - gt;   // exclusive prefix
-    uint32_t rank_eq = cnt_eq[t] - eq;
-    const uint32_t ngt = cnt_gt[255];
-    for (int c = beg; c < end; ++c) {
-      const uint32_t o = ov[c];
-      if (o > prefix) {
-        picked[pos_gt++] = make_key(unorder_f32(o), c);
-      } else if (o == prefix) {
-        if (rank_eq < need) picked[ngt + rank_eq] = make_key(unorder_f32(o), c);
-        ++rank_eq;
-      }
-    }
-  }
-  __syncthreads();
-  if (t < K) {
-    int32_t ci = -1;
-    float cs = -INFINITY;
-    int rk = t;
-    if (t < n) {
-      const uint64_t mine = picked[t];
-      rk = 0;
-      for (int j = 0; j < n; ++j) rk += picked[j] > mine;
-      ci = key_chunk(mine);
-      cs = key_score(mine);
-    }
-    sel_i[(int64_t)bh * K + rk] = ci;
-    sel_s[(int64_t)bh * K + rk] = cs;
-    if (sel_user) sel_user[(int64_t)bh * K + rk] = ci;
-  }
-  if (t == 0) nsel_out[bh] = n;
+  if (lane == 0) nsel_out[bh] = n;
 }
 
 // slot s < nsel: selected chunk sel_i[s]; slot K: the own chunk.  Writes the
@@ -316,22 +310,25 @@ __global__ void __launch_bounds__(256) decode_attend(const IO* __restrict__ q, c
   if (t == 0) sig[(int64_t)bh * (K + 1) + slot] = slot == K ? ml[0] + logf(ml[1]) : sel_s[(int64_t)bh * K + slot];
 }
 
+// o = sum over the n + 1 slots of softmax(sig)_s part_s (one workgroup per (b, h))
 template <typename IO, int D>
-__global__ void __launch_bounds__(128) decode_combine(const float* __restrict__ part, const float* __restrict__ sig,
-                                                      const int32_t* __restrict__ nsel, IO* __restrict__ o, int K) {
-  const int bh = blockIdx.x;
+__global__ void __launch_bounds__(D) decode_combine(const float* __restrict__ part, const float* __restrict__ sig,
+                                                    const int32_t* __restrict__ nsel, IO* __restrict__ out, int K) {
+  const int bh = blockIdx.x, t = threadIdx.x;
   const int n = nsel[bh];
   const float* sg = sig + (int64_t)bh * (K + 1);
-  float M = sg[K];
-  for (int s = 0; s < n; ++s) M = fmaxf(M, sg[s]);
-  float Z = expf(sg[K] - M);
-  for (int s = 0; s < n; ++s) Z += expf(sg[s] - M);
-  const float inv = 1.0f / Z;
-  for (int e = threadIdx.x; e < D; e += 128) {
-    float a = expf(sg[K] - M) * part[((int64_t)bh * (K + 1) + K) * D + e];
-    for (int s = 0; s < n; ++s) a = fmaf(expf(sg[s] - M), part[((int64_t)bh * (K + 1) + s) * D + e], a);
-    io_traits<IO>::store(o, (int64_t)bh * D + e, a * inv);
+  const float* pp = part + (int64_t)bh * (K + 1) * D;
+  const float so = sg[K];
+  float M = so;
+  for (int s2 = 0; s2 < n; ++s2) M = fmaxf(M, sg[s2]);
+  const float wo = expf(so - M);
+  float Z = wo, a = wo * pp[K * D + t];
+  for (int s2 = 0; s2 < n; ++s2) {
+    const float ws = expf(sg[s2] - M);
+    Z += ws;
+    a = fmaf(ws, pp[s2 * D + t], a);
   }
+  io_traits<IO>::store(out, (int64_t)bh * D + t, a / Z);
 }
 
 template <typename IO, int D>
@@ -340,27 +337,25 @@ static hipError_t launch_decode_t(const Geom& g, const void* q, const void* kcac
                                   const void* Uw, int32_t* sel_user, void* o, char* ws, hipStream_t st,
                                   hipEvent_t* ev) {
   const DecodeWs w = decode_ws(g);
-  float* scores = (float*)(ws + w.scores);
+  uint64_t* cand = (uint64_t*)(ws + w.cand);
   int32_t* sel_i = (int32_t*)(ws + w.sel_i);
   float* sel_s = (float*)(ws + w.sel_s);
   int32_t* nsel = (int32_t*)(ws + w.nsel);
   float* part = (float*)(ws + w.part);
   float* sig = (float*)(ws + w.sig);
   const int C = g.C(), BH = g.B * g.Hq;
-  const int nsplit = (C + DS_CHUNKS - 1) / DS_CHUNKS;
-  if (ev) hipEventRecord(ev[0], st);
-  if (nsplit > 0)
-    hipLaunchKernelGGL((decode_scan<IO, D>), dim3(BH * nsplit), dim3(256), 0, st, (const IO*)q, (const IO*)Dw,
-                       (const IO*)Uw, kc, bc, seq_lens, scores, g.Hq, C, g.r, nsplit);
-  if (ev) hipEventRecord(ev[1], st);
-  hipLaunchKernelGGL(decode_topk, dim3(BH), dim3(256), 0, st, scores, seq_lens, sel_i, sel_s, nsel, sel_user, g.Hq,
-                     C, g.K);
-  if (ev) hipEventRecord(ev[2], st);
+  const int nsplit = std::max(1, nsplit_of(g));  // one (empty) split still writes the selection
+  if (ev) (void)hipEventRecord(ev[0], st);
+  hipLaunchKernelGGL((decode_scan<IO, D>), dim3(BH * nsplit), dim3(256), 0, st, (const IO*)q, (const IO*)Dw,
+                     (const IO*)Uw, kc, bc, seq_lens, cand, g.Hq, C, g.r, nsplit);
+  hipLaunchKernelGGL(decode_merge, dim3(BH), dim3(64), 0, st, (const uint64_t*)cand, seq_lens, sel_i, sel_s, nsel,
+                     sel_user, g.Hq, C, g.K, nsplit);
+  if (ev) (void)hipEventRecord(ev[1], st);
   hipLaunchKernelGGL((decode_attend<IO, D>), dim3(BH * (g.K + 1)), dim3(256), 0, st, (const IO*)q, (const IO*)kcache,
                      (const IO*)vcache, seq_lens, sel_i, sel_s, nsel, part, sig, g.Hq, g.Hkv, g.N, g.K);
-  if (ev) hipEventRecord(ev[3], st);
-  hipLaunchKernelGGL((decode_combine<IO, D>), dim3(BH), dim3(128), 0, st, part, sig, nsel, (IO*)o, g.K);
-  if (ev) hipEventRecord(ev[4], st);
+  hipLaunchKernelGGL((decode_combine<IO, D>), dim3(BH), dim3(D), 0, st, (const float*)part, (const float*)sig,
+                     (const int32_t*)nsel, (IO*)o, g.K);
+  if (ev) (void)hipEventRecord(ev[2], st);
   return hipGetLastError();
 }
 

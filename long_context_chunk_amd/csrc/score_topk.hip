@@ -364,7 +364,11 @@ __global__ void __launch_bounds__(256, 2) score_threshold(const IO* __restrict__
     }
   };
 
-  // each lane: the two largest values of its column of chunks, for 2 rows per register
+  // each lane: the two largest values of its column of chunks, for 2 rows per register.
+  // +inf goes through an empty asm so that med3(m1, v, +inf) stays one v_med3_f32
+  // instead of becoming an IEEE max with operand canonicalisation.
+  float pinf = INFINITY;
+  asm volatile("" : "+v"(pinf));
   float m1[16], m2[16];
 #pragma unroll
   for (int rr = 0; rr < 16; ++rr) m1[rr] = m2[rr] = -INFINITY;
@@ -394,7 +398,7 @@ __global__ void __launch_bounds__(256, 2) score_threshold(const IO* __restrict__
 #pragma unroll
         for (int rr = 0; rr < 16; ++rr) {
           m2[rr] = __builtin_amdgcn_fmed3f(m1[rr], m2[rr], acc[rr]);
-          m1[rr] = __builtin_amdgcn_fmed3f(m1[rr], acc[rr], INFINITY);
+          m1[rr] = __builtin_amdgcn_fmed3f(m1[rr], acc[rr], pinf);
         }
       } else {
         const int c = t * ST_TILE + ch;
@@ -404,7 +408,7 @@ __global__ void __launch_bounds__(256, 2) score_threshold(const IO* __restrict__
           const int prow = rw < N ? min(C, rw / 64) : 0;
           const float v = c >= prow ? -INFINITY : acc[rr];
           m2[rr] = __builtin_amdgcn_fmed3f(m1[rr], m2[rr], v);
-          m1[rr] = __builtin_amdgcn_fmed3f(m1[rr], v, INFINITY);
+          m1[rr] = __builtin_amdgcn_fmed3f(m1[rr], v, pinf);
         }
       }
     }

@@ -22,7 +22,7 @@ OK, E_INVAL, E_UNSUPPORTED, E_WORKSPACE, E_HIP = 0, -1, -2, -3, -4
 SYMBOLS = ("hils_workspace_bytes", "hils_landmark_compress", "hils_chunk_score_topk", "hils_attn_prefill",
            "hils_attn_prefill_timed", "hils_attn_decode", "hils_attn_decode_timed", "hils_last_error")
 STAGES = ("compress", "score_threshold", "score_select", "bucket", "chunk_attend", "own_attend", "fuse")
-DECODE_STAGES = ("scan", "topk", "attend", "combine")
+DECODE_STAGES = ("scan_topk", "attend_fuse")
 
 
 class Dims(ctypes.Structure):
@@ -199,7 +199,7 @@ def attn_decode(dm: Dims, q, k_cache, v_cache, seq_lens, kc, bc, o, ws, qcal_D=N
     args = (ctypes.byref(dm), _p(q), _p(k_cache), _p(v_cache), _p(seq_lens), _p(kc), _p(bc), _p(qcal_D), _p(qcal_U),
             _p(sel_idx), _p(o), _p(ws), ws.numel(), _stream())
     if timed:
-        ms = (ctypes.c_float * 4)()
+        ms = (ctypes.c_float * len(DECODE_STAGES))()
         _check(load().hils_attn_decode_timed(*args, ms))
         return dict(zip(DECODE_STAGES, [float(x) for x in ms]))
     _check(load().hils_attn_decode(*args))
