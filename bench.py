@@ -123,7 +123,7 @@ def stage_roofline(w, cnt, stage_ms):
 KERNEL_SOURCES = {
     "compress": "compress.hip", "score_threshold": "score_topk.hip", "score_select": "score_topk.hip",
     "bucket": "attend.hip", "chunk_attend": "attend.hip", "own_attend": "attend.hip", "fuse": "attend.hip",
-    "decode_scan": "decode.hip", "decode_topk": "decode.hip", "decode_attend": "decode.hip", "decode_combine": "decode.hip",
+    "decode_scan": "decode.hip", "decode_merge": "decode.hip", "decode_attend": "decode.hip", "decode_combine": "decode.hip",
 }
 
 
@@ -322,13 +322,17 @@ def run_decode(wd, steps, warmup, seed):
     o = torch.empty_like(q)
     sel = torch.empty((wd.B, wd.Hq, wd.K), dtype=torch.int32, device="cuda")
     ws = hils.workspace(dm, hils.OP_DECODE)
-    flush = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
+    # evicting by a READ of 512 MB of unrelated data leaves the 256 MB Infinity Cache and the
+    # L2s holding clean lines: a write-flush would leave dirty lines whose write-back the
+    # next step's first cache-allocating kernel pays for
+    flush = torch.ones(128 << 20, dtype=torch.float32, device="cuda")
+    flush_out = torch.empty((), dtype=torch.float32, device="cuda")
     for _ in range(warmup):
         hils.attn_decode(dm, q, kcache, vcache, lens, kc, bc, o, ws, sel_idx=sel)
     torch.cuda.synchronize()
     tot, stages = 0.0, {s: 0.0 for s in hils.DECODE_STAGES}
     for _ in range(steps):
-        flush.fill_(1)   # evict k' and the KV chunks from the 256 MB Infinity Cache (untimed)
+        torch.sum(flush, dim=0, out=flush_out)   # evict k' and the KV chunks (untimed)
         r = hils.attn_decode(dm, q, kcache, vcache, lens, kc, bc, o, ws, sel_idx=sel, timed=True)
         for s_ in stages:
             stages[s_] += r[s_] / steps

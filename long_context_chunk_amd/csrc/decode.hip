@@ -21,7 +21,10 @@
 
 namespace hils {
 
+typedef __attribute__((ext_vector_type(4))) float f32x4_t;
+
 constexpr int DS_CHUNKS = 1024;  // chunks scored per decode_scan workgroup
+constexpr int DS_MAX_SPLIT = 16;  // scan workgroups per (b, h): N/S <= 16384
 constexpr int DS_KEEP = 32;      // candidates kept per workgroup (>= K)
 
 struct DecodeWs {
@@ -85,10 +88,9 @@ HILS_DEV void dsort32(uint64_t& k) {
   HILS_STAGE(32, 16) HILS_STAGE(32, 8) HILS_STAGE(32, 4) HILS_STAGE(32, 2) HILS_STAGE(32, 1)
 #undef HILS_STAGE
 }
-// merge unsorted keys nk into the sorted (best-first) list lk of each half; keep 32
-HILS_DEV void dmerge(uint64_t& lk, uint64_t nk) {
+// merge the sorted (best-first) list nk into the sorted list lk of each half; keep 32
+HILS_DEV void dmerge_sorted(uint64_t& lk, uint64_t nk) {
   const int j = threadIdx.x & 31;
-  dsort32(nk);
   const uint64_t r = dxl<31>(nk);
   lk = r > lk ? r : lk;
   dcx<16>(lk, (j & 16) == 0);
@@ -96,6 +98,11 @@ HILS_DEV void dmerge(uint64_t& lk, uint64_t nk) {
   dcx<4>(lk, (j & 4) == 0);
   dcx<2>(lk, (j & 2) == 0);
   dcx<1>(lk, (j & 1) == 0);
+}
+// merge unsorted keys nk into the sorted list lk of each half; keep 32
+HILS_DEV void dmerge(uint64_t& lk, uint64_t nk) {
+  dsort32(nk);
+  dmerge_sorted(lk, nk);
 }
 
 // q^ = q + U (D q) for one head into LDS (fp32).  256 threads.
@@ -126,7 +133,7 @@ __global__ void __launch_bounds__(256) decode_scan(const IO* __restrict__ q, con
                                                    const IO* __restrict__ Uw, const float* __restrict__ kc,
                                                    const float* __restrict__ bc, const int32_t* __restrict__ seq_lens,
                                                    uint64_t* __restrict__ cand, int Hq, int C, int r, int nsplit) {
-  __shared__ float qs[D];
+  __shared__ __align__(16) float qs[D];
   __shared__ float ts[32];
   __shared__ uint64_t keys[DS_CHUNKS];
   __shared__ uint64_t wl[4][32];
@@ -137,34 +144,45 @@ __global__ void __launch_bounds__(256) decode_scan(const IO* __restrict__ q, con
   const int c_beg = sp * DS_CHUNKS, c_end = min(P, c_beg + DS_CHUNKS);
   const int t = threadIdx.x, lane = t & 63, w = t >> 6;
   qhat_to_lds<IO, D>(q + (int64_t)bh * D, Dw, Uw, h, r, qs, ts);
-  constexpr int TPC = D / 4;        // threads per chunk (one float4 each)
+  // TPC threads per chunk, each holding 16 of the D head dims as 4 float4 spread so
+  // that the TPC lanes of a chunk read 128 contiguous bytes per load
+  constexpr int TPC = D / 16;
   constexpr int CPP = 256 / TPC;    // chunks per pass
-  constexpr int UNR = 8;            // passes in flight
+  constexpr int UNR = 2;            // passes per register buffer
   constexpr int STEP = CPP * UNR;
   const int sub = t % TPC, grp = t / TPC;
-  const float4 qv = *reinterpret_cast<const float4*>(&qs[4 * sub]);
+  f32x4_t qv[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) qv[j] = *reinterpret_cast<const f32x4_t*>(&qs[4 * (sub + TPC * j)]);
   const float tau = 1.0f / sqrtf((float)D);
   const float* kb = kc + (int64_t)bh * C * D;
   const float* bb = bc + (int64_t)bh * C;
-  // chunks beyond c_end load chunk c_end - 1 (in bounds) and are dropped; two register
-  // buffers alternate so that the next UNR passes are in flight during the current ones
-  float4 ka[UNR], kb2[UNR];
+  // the landmark keys are streamed once (non-temporal loads); chunks beyond c_end load
+  // chunk c_end - 1 (in bounds) and are dropped; two register buffers alternate so that
+  // the next STEP chunks are in flight while the current ones are scored
+  f32x4_t ka[UNR][4], kb2[UNR][4];
   float ba[UNR], bb2[UNR];
-  auto load = [&](int c0, float4(&kv)[UNR], float(&bv)[UNR]) {
+  auto load = [&](int c0, f32x4_t(&kv)[UNR][4], float(&bv)[UNR]) {
 #pragma unroll
     for (int u = 0; u < UNR; ++u) {
       const int c = min(c0 + u * CPP + grp, c_end - 1);
-      kv[u] = *reinterpret_cast<const float4*>(kb + (int64_t)c * D + 4 * sub);
+      const f32x4_t* row = reinterpret_cast<const f32x4_t*>(kb + (int64_t)c * D);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) kv[u][j] = __builtin_nontemporal_load(row + sub + TPC * j);
       bv[u] = bb[c];
     }
   };
-  auto score = [&](int c0, const float4(&kv)[UNR], const float(&bv)[UNR]) {
+  auto score = [&](int c0, const f32x4_t(&kv)[UNR][4], const float(&bv)[UNR]) {
 #pragma unroll
     for (int u = 0; u < UNR; ++u) {
-      float s = qv.x * kv[u].x;
-      s = fmaf(qv.y, kv[u].y, s);
-      s = fmaf(qv.z, kv[u].z, s);
-      s = fmaf(qv.w, kv[u].w, s);
+      float s = 0.f;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        s = fmaf(qv[j].x, kv[u][j].x, s);
+        s = fmaf(qv[j].y, kv[u][j].y, s);
+        s = fmaf(qv[j].z, kv[u][j].z, s);
+        s = fmaf(qv[j].w, kv[u][j].w, s);
+      }
 #pragma unroll
       for (int o = TPC / 2; o >= 1; o >>= 1) s += __shfl_xor(s, o);
       const int c = c0 + u * CPP + grp;
@@ -190,30 +208,43 @@ __global__ void __launch_bounds__(256) decode_scan(const IO* __restrict__ q, con
     dmerge(lk, keys[base + 64]);
     dmerge(lk, keys[base + 96]);
     const uint64_t other = __shfl(lk, (lane & 31) + 32);
-    dmerge(lk, other);
+    dmerge_sorted(lk, other);
     if (lane < 32) wl[w][lane] = lk;
   }
   __syncthreads();
-  if (w == 0) {
-    uint64_t lk = wl[0][lane & 31];
-    dmerge(lk, wl[1][lane & 31]);
-    dmerge(lk, wl[2][lane & 31]);
-    dmerge(lk, wl[3][lane & 31]);
+  if (w == 0) {  // halves merge waves 0+1 and 2+3, then each other
+    uint64_t lk = wl[(lane >> 5) * 2][lane & 31];
+    dmerge_sorted(lk, wl[(lane >> 5) * 2 + 1][lane & 31]);
+    const uint64_t other = __shfl(lk, (lane & 31) + 32);
+    dmerge_sorted(lk, other);
     if (lane < 32) cand[((int64_t)bh * nsplit + sp) * DS_KEEP + lane] = lk;
   }
 }
 
-// exact top-K of one (b, h) from the candidates of its splits (one wave); rank order
-__global__ void __launch_bounds__(64) decode_merge(const uint64_t* __restrict__ cand,
-                                                   const int32_t* __restrict__ seq_lens, int32_t* __restrict__ sel_i,
-                                                   float* __restrict__ sel_s, int32_t* __restrict__ nsel_out,
-                                                   int32_t* __restrict__ sel_user, int Hq, int C, int K, int nsplit) {
-  const int bh = blockIdx.x, lane = threadIdx.x;
+// exact top-K of one (b, h) from the sorted candidate lists of its splits, rank order.
+// Half-wave x of wave w takes lists 2w + x and 2w + x + 8, the halves of each wave
+// merge, then wave 0 merges the four wave lists.
+__global__ void __launch_bounds__(256) decode_merge(const uint64_t* __restrict__ cand,
+                                                    const int32_t* __restrict__ seq_lens, int32_t* __restrict__ sel_i,
+                                                    float* __restrict__ sel_s, int32_t* __restrict__ nsel_out,
+                                                    int32_t* __restrict__ sel_user, int Hq, int C, int K, int nsplit) {
+  static_assert(DS_MAX_SPLIT == 16, "two lists per half-wave");
+  __shared__ uint64_t wl[4][32];
+  const int bh = blockIdx.x, t = threadIdx.x, lane = t & 63, w = t >> 6;
+  const int li = 2 * w + (lane >> 5);
+  const uint64_t* cb = cand + (int64_t)bh * nsplit * DS_KEEP + (lane & 31);
+  uint64_t lk = li < nsplit ? cb[li * DS_KEEP] : 0ull;        // empty lists are all-zero keys
+  const uint64_t l2 = li + 8 < nsplit ? cb[(li + 8) * DS_KEEP] : 0ull;
+  dmerge_sorted(lk, l2);
+  dmerge_sorted(lk, __shfl(lk, (lane & 31) + 32));
+  if (lane < 32) wl[w][lane] = lk;
+  __syncthreads();
+  if (w != 0) return;
+  lk = wl[(lane >> 5) * 2][lane & 31];
+  dmerge_sorted(lk, wl[(lane >> 5) * 2 + 1][lane & 31]);
+  dmerge_sorted(lk, __shfl(lk, (lane & 31) + 32));
   const int L = seq_lens[bh / Hq];
-  const int P = min(C, (L - 1) / 64);
-  uint64_t lk = 0;
-  for (int s2 = 0; s2 < nsplit; ++s2) dmerge(lk, cand[((int64_t)bh * nsplit + s2) * DS_KEEP + (lane & 31)]);
-  const int n = min(K, P);
+  const int n = min(K, min(C, (L - 1) / 64));
   if (lane < K) {
     const bool ok = lane < n && lk != 0;
     const int32_t ci = ok ? key_chunk(lk) : -1;
@@ -224,17 +255,40 @@ __global__ void __launch_bounds__(64) decode_merge(const uint64_t* __restrict__ 
   if (lane == 0) nsel_out[bh] = n;
 }
 
+// eight consecutive elements of a row, kept raw until used
+template <typename IO>
+struct raw8;
+template <>
+struct raw8<bf16_t> {
+  u32x4_t u;
+  __device__ __forceinline__ void load(const bf16_t* p) { u = *reinterpret_cast<const u32x4_t*>(p); }
+  __device__ __forceinline__ float operator[](int m) const {
+    return __uint_as_float((m & 1) ? (u[m >> 1] & 0xffff0000u) : (u[m >> 1] << 16));
+  }
+};
+template <>
+struct raw8<float> {
+  f32x4_t a, b;
+  __device__ __forceinline__ void load(const float* p) {
+    a = *reinterpret_cast<const f32x4_t*>(p);
+    b = *reinterpret_cast<const f32x4_t*>(p + 4);
+  }
+  __device__ __forceinline__ float operator[](int m) const { return m < 4 ? a[m] : b[m - 4]; }
+};
+
 // slot s < nsel: selected chunk sel_i[s]; slot K: the own chunk.  Writes the
-// normalised chunk output (fp32) and the chunk's fusion score.
+// normalised chunk output (fp32) and the chunk's fusion score.  The V rows a thread
+// needs are loaded together with the K rows, before the logits.
 template <typename IO, int D>
 __global__ void __launch_bounds__(256) decode_attend(const IO* __restrict__ q, const IO* __restrict__ kcache,
                                                      const IO* __restrict__ vcache, const int32_t* __restrict__ seq_lens,
                                                      const int32_t* __restrict__ sel_i, const float* __restrict__ sel_s,
                                                      const int32_t* __restrict__ nsel, float* __restrict__ part,
                                                      float* __restrict__ sig, int Hq, int Hkv, int N, int K) {
-  constexpr int NG = 256 / (D / 4);  // key groups for the value pass (4 head dims per thread)
-  constexpr int KPG = 64 / NG;
-  __shared__ float qs[D];
+  constexpr int KJ = D / 32;        // logits: 4 threads per key, KJ runs of 8 dims each
+  constexpr int TPR = D / 8;        // values: threads per row (8 dims each)
+  constexpr int NG = 256 / TPR;     // key groups
+  constexpr int KPG = 64 / NG;      // keys per group
   __shared__ float z[64];
   __shared__ float ml[2];
   __shared__ float red[NG][D];
@@ -251,23 +305,29 @@ __global__ void __launch_bounds__(256) decode_attend(const IO* __restrict__ q, c
     c = sel_i[(int64_t)bh * K + slot];
     nk = 64;
   }
-  if (t < D) qs[t] = io_traits<IO>::load(q, (int64_t)bh * D + t);
-  __syncthreads();
   const int64_t row0 = ((int64_t)b * Hkv + kvh) * N + (int64_t)c * 64;
-  const float tau = 1.0f / sqrtf((float)D);
-  {  // logits: 4 threads per key, each a quarter of the head dim (vector loads)
-    const int key = t >> 2, qd = t & 3;
-    float s = 0.f;
-    if (key < nk) {
-      const int64_t base = (row0 + key) * D + qd * (D / 4);
+  // keys past nk (own chunk only) read row nk - 1, in bounds, and get weight 0
+  const int key = t >> 2, qd = t & 3;
+  const int e8 = (t % TPR) * 8, kg = t / TPR;
+  raw8<IO> kr[KJ], qr[KJ], vr[KPG];
+  {
+    const IO* krow = kcache + (row0 + min(key, nk - 1)) * D;
+    const IO* qrow = q + (int64_t)bh * D;
 #pragma unroll
-      for (int e = 0; e < D / 4; e += 4) {
-        float x[4];
-        io_traits<IO>::load4(kcache, base + e, x);
-#pragma unroll
-        for (int u = 0; u < 4; ++u) s = fmaf(qs[qd * (D / 4) + e + u], x[u], s);
-      }
+    for (int j = 0; j < KJ; ++j) {
+      kr[j].load(krow + 8 * (qd + 4 * j));
+      qr[j].load(qrow + 8 * (qd + 4 * j));
     }
+#pragma unroll
+    for (int u = 0; u < KPG; ++u) vr[u].load(vcache + (row0 + min(kg * KPG + u, nk - 1)) * D + e8);
+  }
+  const float tau = 1.0f / sqrtf((float)D);
+  {
+    float s = 0.f;
+#pragma unroll
+    for (int j = 0; j < KJ; ++j)
+#pragma unroll
+      for (int m = 0; m < 8; ++m) s = fmaf(qr[j][m], kr[j][m], s);
     s += __shfl_xor(s, 1);
     s += __shfl_xor(s, 2);
     if (qd == 0) z[key] = key < nk ? s * tau : -INFINITY;
@@ -285,20 +345,16 @@ __global__ void __launch_bounds__(256) decode_attend(const IO* __restrict__ q, c
     }
   }
   __syncthreads();
-  {  // values: thread (4 head dims, key group)
-    const int e4 = (t % (D / 4)) * 4, kg = t / (D / 4);
-    float a[4] = {0.f, 0.f, 0.f, 0.f};
-    for (int j = kg * KPG; j < (kg + 1) * KPG; ++j) {
-      if (j < nk) {
-        float x[4];
-        io_traits<IO>::load4(vcache, (row0 + j) * D + e4, x);
-        const float pj = z[j];
+  {
+    float a[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int u = 0; u < 4; ++u) a[u] = fmaf(pj, x[u], a[u]);
-      }
+    for (int u = 0; u < KPG; ++u) {
+      const float pj = z[kg * KPG + u];
+#pragma unroll
+      for (int m = 0; m < 8; ++m) a[m] = fmaf(pj, vr[u][m], a[m]);
     }
 #pragma unroll
-    for (int u = 0; u < 4; ++u) red[kg][e4 + u] = a[u];
+    for (int m = 0; m < 8; ++m) red[kg][e8 + m] = a[m];
   }
   __syncthreads();
   if (t < D) {
@@ -310,25 +366,41 @@ __global__ void __launch_bounds__(256) decode_attend(const IO* __restrict__ q, c
   if (t == 0) sig[(int64_t)bh * (K + 1) + slot] = slot == K ? ml[0] + logf(ml[1]) : sel_s[(int64_t)bh * K + slot];
 }
 
-// o = sum over the n + 1 slots of softmax(sig)_s part_s (one workgroup per (b, h))
+// o = sum over the n + 1 live slots of softmax(sig)_s part_s, one workgroup per (b, h).
+// Lane s of every wave holds slot s's weight; the slot rows are all loaded at once.
 template <typename IO, int D>
-__global__ void __launch_bounds__(D) decode_combine(const float* __restrict__ part, const float* __restrict__ sig,
-                                                    const int32_t* __restrict__ nsel, IO* __restrict__ out, int K) {
-  const int bh = blockIdx.x, t = threadIdx.x;
+__global__ void __launch_bounds__(256) decode_combine(const float* __restrict__ part, const float* __restrict__ sig,
+                                                      const int32_t* __restrict__ nsel, IO* __restrict__ out, int K) {
+  constexpr int G = 256 / D;                    // slot groups
+  constexpr int MAXJ = (DS_KEEP + 1 + G - 1) / G;  // K + 1 <= 33 slots
+  __shared__ float red[G][D];
+  const int bh = blockIdx.x, t = threadIdx.x, lane = t & 63;
   const int n = nsel[bh];
   const float* sg = sig + (int64_t)bh * (K + 1);
   const float* pp = part + (int64_t)bh * (K + 1) * D;
-  const float so = sg[K];
-  float M = so;
-  for (int s2 = 0; s2 < n; ++s2) M = fmaxf(M, sg[s2]);
-  const float wo = expf(so - M);
-  float Z = wo, a = wo * pp[K * D + t];
-  for (int s2 = 0; s2 < n; ++s2) {
-    const float ws = expf(sg[s2] - M);
-    Z += ws;
-    a = fmaf(ws, pp[s2 * D + t], a);
+  const int e = t % D, g = t / D;
+  float pv[MAXJ];
+#pragma unroll
+  for (int j = 0; j < MAXJ; ++j) {
+    const int s2 = g + j * G;
+    pv[j] = (s2 < n || s2 == K) ? pp[(int64_t)s2 * D + e] : 0.f;
   }
-  io_traits<IO>::store(out, (int64_t)bh * D + t, a / Z);
+  const bool live = lane < n || lane == K;
+  const float v = live ? sg[lane] : -INFINITY;
+  const float M = wave_max(v);
+  const float wt = live ? expf(v - M) : 0.f;
+  const float Z = wave_sum(wt);
+  float a = 0.f;
+#pragma unroll
+  for (int j = 0; j < MAXJ; ++j) a = fmaf(__shfl(wt, min(g + j * G, 63)), pv[j], a);
+  red[g][e] = a;
+  __syncthreads();
+  if (t < D) {
+    float o = 0.f;
+#pragma unroll
+    for (int g2 = 0; g2 < G; ++g2) o += red[g2][t];
+    io_traits<IO>::store(out, (int64_t)bh * D + t, o / Z);
+  }
 }
 
 template <typename IO, int D>
@@ -345,15 +417,16 @@ static hipError_t launch_decode_t(const Geom& g, const void* q, const void* kcac
   float* sig = (float*)(ws + w.sig);
   const int C = g.C(), BH = g.B * g.Hq;
   const int nsplit = std::max(1, nsplit_of(g));  // one (empty) split still writes the selection
+  if (nsplit > DS_MAX_SPLIT) return hipErrorInvalidValue;  // N/S > 16384, rejected by the ABI first
   if (ev) (void)hipEventRecord(ev[0], st);
   hipLaunchKernelGGL((decode_scan<IO, D>), dim3(BH * nsplit), dim3(256), 0, st, (const IO*)q, (const IO*)Dw,
                      (const IO*)Uw, kc, bc, seq_lens, cand, g.Hq, C, g.r, nsplit);
-  hipLaunchKernelGGL(decode_merge, dim3(BH), dim3(64), 0, st, (const uint64_t*)cand, seq_lens, sel_i, sel_s, nsel,
+  hipLaunchKernelGGL(decode_merge, dim3(BH), dim3(256), 0, st, (const uint64_t*)cand, seq_lens, sel_i, sel_s, nsel,
                      sel_user, g.Hq, C, g.K, nsplit);
   if (ev) (void)hipEventRecord(ev[1], st);
   hipLaunchKernelGGL((decode_attend<IO, D>), dim3(BH * (g.K + 1)), dim3(256), 0, st, (const IO*)q, (const IO*)kcache,
                      (const IO*)vcache, seq_lens, sel_i, sel_s, nsel, part, sig, g.Hq, g.Hkv, g.N, g.K);
-  hipLaunchKernelGGL((decode_combine<IO, D>), dim3(BH), dim3(D), 0, st, (const float*)part, (const float*)sig,
+  hipLaunchKernelGGL((decode_combine<IO, D>), dim3(BH), dim3(256), 0, st, (const float*)part, (const float*)sig,
                      (const int32_t*)nsel, (IO*)o, g.K);
   if (ev) (void)hipEventRecord(ev[2], st);
   return hipGetLastError();
