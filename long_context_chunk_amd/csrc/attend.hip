@@ -19,7 +19,9 @@
 //
 //   bucket_count  : LDS-privatised histogram of the selections per bucket
 //   bucket_scan   : exclusive scans -> bucket offsets and tile offsets
-//   bucket_scatter: pair ids (= linear index into sel_idx) grouped by bucket
+//   bucket_part1/2: two-digit counting sort of the pair ids (= linear index into
+//                   sel_idx) by bucket: first into ranges of 64 chunks, then into
+//                   chunks, each pass sorting tiles in LDS and writing whole runs
 //   chunk_attend  : gathered-row MFMA attention per (bucket, 128-row tile)
 //   own_attend    : causal own-chunk MFMA attention -> slot K and LSE_own
 //   fuse          : softmax over {s_ic} U {LSE_own}, weighted sum of the slots -> o
@@ -33,7 +35,11 @@ namespace hils {
 constexpr int AT_ROWS = 128;        // gathered rows per chunk_attend tile (4 waves x 32)
 constexpr int AT_TILES = 8;         // tiles per chunk_attend work item (one K/V staging)
 constexpr int ITEM_ROWS = AT_ROWS * AT_TILES;
-constexpr int HIST_SLICE = 1 << 18; // selection entries per bucket_count / bucket_scatter workgroup
+constexpr int HIST_SLICE = 1 << 18; // selection entries per bucket_count / bucket_part1 workgroup
+constexpr int BK_TILE = 8192;       // entries sorted in LDS at a time by bucket_part1/2
+constexpr int BK_PER = BK_TILE / 256;
+constexpr int FINE_BITS = 6;        // chunks per first-pass range: 64
+constexpr int LOCAL_BITS = 26;      // in-group pair index bits of the first-pass keys
 constexpr int MAX_C = 16384;        // largest chunk count the LDS histograms hold
 
 struct AttendWs {
@@ -84,9 +90,16 @@ __global__ void __launch_bounds__(256) bucket_count(const int32_t* __restrict__ 
   __syncthreads();
   const int64_t beg = (int64_t)sl * HIST_SLICE, end = min(group_len, beg + HIST_SLICE);
   const int32_t* s = sel + (int64_t)grp * group_len;
-  for (int64_t i = beg + threadIdx.x; i < end; i += 256) {
-    const int c = s[i];
-    if (c >= 0) atomicAdd(&hist[c], 1u);
+  for (int64_t t0 = beg; t0 < end; t0 += BK_TILE) {
+    int32_t c[BK_PER];  // every load of the tile in flight at once
+#pragma unroll
+    for (int u = 0; u < BK_PER; ++u) {
+      const int64_t i = t0 + threadIdx.x + 256 * u;
+      c[u] = i < end ? s[i] : -1;
+    }
+#pragma unroll
+    for (int u = 0; u < BK_PER; ++u)
+      if (c[u] >= 0) atomicAdd(&hist[c[u]], 1u);
   }
   __syncthreads();
   for (int i = threadIdx.x; i < C; i += 256)
@@ -129,36 +142,139 @@ __global__ void __launch_bounds__(1024) bucket_scan(const uint32_t* __restrict__
   }
 }
 
-__global__ void __launch_bounds__(256) bucket_scatter(const int32_t* __restrict__ sel, const uint32_t* __restrict__ boff,
-                                                      uint32_t* __restrict__ cursor, uint32_t* __restrict__ pairs,
-                                                      int64_t group_len, int slices_per_group, int C) {
-  __shared__ uint32_t hist[MAX_C];
-  __shared__ uint32_t base[MAX_C];
-  const int grp = blockIdx.x / slices_per_group, sl = blockIdx.x % slices_per_group;
-  for (int i = threadIdx.x; i < C; i += 256) hist[i] = 0;
+// exclusive scan of v over the 256 threads of the workgroup; returns the total
+HILS_DEV uint32_t block_exscan256(uint32_t v, uint32_t& excl, uint32_t* wsum) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  uint32_t x = v;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const uint32_t y = __shfl_up(x, o);
+    if (lane >= o) x += y;
+  }
+  if (lane == 63) wsum[w] = x;
   __syncthreads();
+  uint32_t before = 0, total = 0;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    before += j < w ? wsum[j] : 0u;
+    total += wsum[j];
+  }
+  excl = before + x - v;
+  return total;
+}
+
+// First pass: the entries of one slice of a (b, h) group, LDS tile by LDS tile, are
+// sorted by 64-chunk range and each range's run is appended (one atomic reservation per
+// tile and range) to that range's region of the bucket-ordered array, which is the
+// concatenation of its chunks' buckets (offsets from boff).  Keys: (chunk & 63) << 26 |
+// in-group entry index.
+__global__ void __launch_bounds__(256) bucket_part1(const int32_t* __restrict__ sel, const uint32_t* __restrict__ boff,
+                                                    uint32_t* __restrict__ rcur, uint32_t* __restrict__ tmp,
+                                                    int64_t group_len, int slices_per_group, int C, int nrg) {
+  __shared__ uint32_t skey[BK_TILE];
+  __shared__ uint8_t srg[BK_TILE];
+  __shared__ uint32_t hist[256], loff[256], gpos[256], wsum[4];
+  const int grp = blockIdx.x / slices_per_group, sl = blockIdx.x % slices_per_group;
+  const int t = threadIdx.x;
   const int64_t beg = (int64_t)sl * HIST_SLICE, end = min(group_len, beg + HIST_SLICE);
   const int32_t* s = sel + (int64_t)grp * group_len;
-  for (int64_t i = beg + threadIdx.x; i < end; i += 256) {
-    const int c = s[i];
-    if (c >= 0) atomicAdd(&hist[c], 1u);
-  }
-  __syncthreads();
-  // reserve this slice's range inside every bucket it touches
-  for (int i = threadIdx.x; i < C; i += 256) {
-    const uint32_t h = hist[i];
-    const int64_t bk = (int64_t)grp * C + i;
-    base[i] = h ? boff[bk] + atomicAdd(&cursor[bk], h) : 0;
-    hist[i] = 0;
-  }
-  __syncthreads();
-  const int64_t e0 = (int64_t)grp * group_len;
-  for (int64_t i = beg + threadIdx.x; i < end; i += 256) {
-    const int c = s[i];
-    if (c >= 0) {
-      const uint32_t rank = atomicAdd(&hist[c], 1u);
-      pairs[base[c] + rank] = (uint32_t)(e0 + i);
+  for (int64_t t0 = beg; t0 < end; t0 += BK_TILE) {
+    hist[t] = 0;
+    __syncthreads();
+    int32_t c[BK_PER];
+    uint32_t rk[BK_PER];
+#pragma unroll
+    for (int u = 0; u < BK_PER; ++u) {
+      const int64_t i = t0 + t + 256 * u;
+      c[u] = i < end ? s[i] : -1;
     }
+#pragma unroll
+    for (int u = 0; u < BK_PER; ++u)
+      if (c[u] >= 0) rk[u] = atomicAdd(&hist[c[u] >> FINE_BITS], 1u);
+    __syncthreads();
+    const uint32_t h = hist[t];  // t < nrg <= 256; hist[t] = 0 beyond
+    uint32_t ex;
+    block_exscan256(h, ex, wsum);
+    loff[t] = ex;
+    if (t < nrg && h) {
+      const int64_t bk0 = (int64_t)grp * C + ((int64_t)t << FINE_BITS);
+      gpos[t] = boff[bk0] + atomicAdd(&rcur[(int64_t)grp * nrg + t], h);
+    }
+    __syncthreads();
+#pragma unroll
+    for (int u = 0; u < BK_PER; ++u)
+      if (c[u] >= 0) {
+        const int r = c[u] >> FINE_BITS;
+        const uint32_t pos = loff[r] + rk[u];
+        skey[pos] = ((uint32_t)(c[u] & ((1 << FINE_BITS) - 1)) << LOCAL_BITS) | (uint32_t)(t0 + t + 256 * u);
+        srg[pos] = (uint8_t)r;
+      }
+    __syncthreads();
+    const uint32_t n = loff[255] + hist[255];
+    for (uint32_t i = t; i < n; i += 256) {
+      const int r = srg[i];
+      tmp[gpos[r] + (i - loff[r])] = skey[i];
+    }
+    __syncthreads();
+  }
+}
+
+// Second pass: one workgroup per (group, 64-chunk range) sorts the range's region by
+// chunk, LDS tile by LDS tile, appending each chunk's run at that bucket's cursor.
+__global__ void __launch_bounds__(256) bucket_part2(const uint32_t* __restrict__ tmp, const uint32_t* __restrict__ boff,
+                                                    uint32_t* __restrict__ pairs, int64_t group_len, int C, int nrg) {
+  constexpr int NF = 1 << FINE_BITS;
+  __shared__ uint32_t skey[BK_TILE];
+  __shared__ uint8_t sfb[BK_TILE];
+  __shared__ uint32_t hist[NF], loff[NF], cur[NF];
+  const int grp = blockIdx.x / nrg, rg = blockIdx.x % nrg;
+  const int t = threadIdx.x, lane = t & 63;
+  const int c0 = rg << FINE_BITS;
+  const int nf = min(NF, C - c0);
+  const int64_t bk0 = (int64_t)grp * C + c0;
+  const uint32_t R0 = boff[bk0], R1 = boff[bk0 + nf];
+  if (t < NF) cur[t] = t < nf ? boff[bk0 + t] : 0u;
+  const uint32_t ebase = (uint32_t)(grp * group_len);
+  for (uint32_t t0 = R0; t0 < R1; t0 += BK_TILE) {
+    if (t < NF) hist[t] = 0;
+    __syncthreads();
+    uint32_t key[BK_PER], rk[BK_PER];
+#pragma unroll
+    for (int u = 0; u < BK_PER; ++u) {
+      const uint32_t i = t0 + t + 256 * u;
+      key[u] = i < R1 ? tmp[i] : 0xffffffffu;
+    }
+#pragma unroll
+    for (int u = 0; u < BK_PER; ++u)
+      if (key[u] != 0xffffffffu) rk[u] = atomicAdd(&hist[key[u] >> LOCAL_BITS], 1u);
+    __syncthreads();
+    if (t < 64) {  // one wave scans the NF = 64 chunk counts
+      const uint32_t h = hist[lane];
+      uint32_t x = h;
+#pragma unroll
+      for (int o = 1; o < 64; o <<= 1) {
+        const uint32_t y = __shfl_up(x, o);
+        if (lane >= o) x += y;
+      }
+      loff[lane] = x - h;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int u = 0; u < BK_PER; ++u)
+      if (key[u] != 0xffffffffu) {
+        const int f = key[u] >> LOCAL_BITS;
+        const uint32_t pos = loff[f] + rk[u];
+        skey[pos] = key[u] & ((1u << LOCAL_BITS) - 1);
+        sfb[pos] = (uint8_t)f;
+      }
+    __syncthreads();
+    const uint32_t n = min((uint32_t)BK_TILE, R1 - t0);
+    for (uint32_t i = t; i < n; i += 256) {
+      const int f = sfb[i];
+      pairs[cur[f] + (i - loff[f])] = ebase + skey[i];
+    }
+    __syncthreads();
+    if (t < NF) cur[t] += hist[t];
   }
 }
 
@@ -659,7 +775,13 @@ static hipError_t launch_attend_t(const Geom& g, const void* q, const void* k, c
     const int ngrp = g.B * g.Hq;
     hipLaunchKernelGGL(bucket_count, dim3(ngrp * spg), dim3(256), 0, st, sel, counts, group_len, spg, C);
     hipLaunchKernelGGL(bucket_scan, dim3(1), dim3(1024), 0, st, counts, boff, toff, nbk);
-    hipLaunchKernelGGL(bucket_scatter, dim3(ngrp * spg), dim3(256), 0, st, sel, boff, cursor, pairs, group_len, spg, C);
+    // the first pass's output lives in the (not yet written) partial-output region
+    const int nrg = (C + (1 << FINE_BITS) - 1) >> FINE_BITS;
+    uint32_t* tmp = (uint32_t*)partial;
+    hipLaunchKernelGGL(bucket_part1, dim3(ngrp * spg), dim3(256), 0, st, sel, boff, cursor, tmp, group_len, spg, C,
+                       nrg);
+    hipLaunchKernelGGL(bucket_part2, dim3(ngrp * nrg), dim3(256), 0, st, (const uint32_t*)tmp, boff, pairs, group_len,
+                       C, nrg);
     if (ev) hipEventRecord(ev[0], st);
     // work items <= total pairs / ITEM_ROWS + number of buckets (host bound; the exact count is read on the device)
     // rows of query chunk p (64 of them, fewer in the tail) select min(K, p, C) chunks each
@@ -693,6 +815,9 @@ hipError_t launch_prefill_attend(const Geom& g, const void* q, const void* k, co
                                  hipEvent_t* ev) {
   if (ws_bytes < attend_workspace_bytes(g)) return hipErrorInvalidValue;
   if (g.C() > MAX_C) return hipErrorNotSupported;
+  // first-pass keys hold an in-group entry index (N*K < 2^26 whenever N/S <= 16384, K <= 32)
+  if ((int64_t)g.N * g.K >= (int64_t)1 << LOCAL_BITS) return hipErrorNotSupported;
+  static_assert(MAX_C <= 256 << FINE_BITS, "first-pass ranges fit one 256-thread scan");
   char* w = (char*)ws;
   if (g.io == 0)
     return g.d == 64 ? launch_attend_t<float, 64>(g, q, k, v, sel_idx, sel_score, o, w, st, ev)
