@@ -43,7 +43,7 @@ constexpr int LOCAL_BITS = 26;      // in-group pair index bits of the first-pas
 constexpr int MAX_C = 16384;        // largest chunk count the LDS histograms hold
 
 struct AttendWs {
-  size_t counts, cursor, boff, toff, pairs, partial, lse, total;
+  size_t counts, cursor, boff, toff, pairs, partial, lse, sink, total;
 };
 
 static size_t al(size_t x) { return (x + 255) / 256 * 256; }
@@ -69,6 +69,8 @@ static AttendWs attend_ws(const Geom& g) {
   off += al(rows * (g.K + 1) * g.d * (g.io == 0 ? 4 : 2));
   w.lse = off;
   off += al(rows * 4);
+  w.sink = off;  // target of the stores of padding rows (never read)
+  off += al(4096);
   w.total = off;
   return w;
 }
@@ -345,16 +347,19 @@ HILS_DEV bf16x8_t vt_operand(const uint16_t* vplane, int dt, int ks2, int lane) 
 HILS_DEV bf16x8_t lds_op16(const uint16_t* p) { return *reinterpret_cast<const bf16x8_t*>(p); }
 
 // One wave: 32 query rows (B operands qb, NT terms) against the staged chunk.
-// Returns, per lane (row n = lane & 31, half hf), the O^T accumulators (unnormalised)
-// and the row's softmax max m and sum l over the keys allowed by `key_lim`
-// (key j is used iff j < key_lim; per row).
-template <typename IO, int D, int NT>
+// Returns, per lane (row n = lane & 31, half hf), the O^T accumulators (unnormalised:
+// P keeps its largest weight exactly 1 in bf16) and the row's softmax max m (of the
+// scaled logits) and sum l.  MASK: key j is used iff j < key_lim
+// (per row); otherwise all 64 keys are.  p = 2^((s - max s) tau log2 e) is one fma and
+// one exp per logit; masked logits are -inf and give p = 0.
+template <typename IO, int D, int NT, bool MASK>
 HILS_DEV void wave_chunk_attention(const KVTile<IO, D, NT>& tile, const bf16x8_t (&qb)[NT][D / 16], int key_lim,
                                    f32x16_t (&o)[D / 32], float& m_out, float& l_out) {
   constexpr int NKS = D / 16;
   constexpr int LDK = KVTile<IO, D, NT>::LDK, LDV = KVTile<IO, D, NT>::LDV;
   const int lane = threadIdx.x & 63, hf = lane >> 5;
   const float tau = 1.0f / sqrtf((float)D);
+  const float c = tau * 1.44269504088896340736f;  // tau log2(e)
   f32x16_t s[2];
 #pragma unroll
   for (int tt = 0; tt < 2; ++tt) {
@@ -370,26 +375,24 @@ HILS_DEV void wave_chunk_attention(const KVTile<IO, D, NT>& tile, const bf16x8_t
           if (i + j < NT) s[tt] = mfma32(a, qb[i][ks], s[tt]);
       }
   }
-  float m = -INFINITY;
+  if constexpr (MASK) {
 #pragma unroll
-  for (int tt = 0; tt < 2; ++tt)
+    for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
-    for (int rr = 0; rr < 16; ++rr) {
-      const int key = 32 * tt + acc_row(rr, hf);
-      const float z = key < key_lim ? s[tt][rr] * tau : -INFINITY;
-      s[tt][rr] = z;
-      m = z > m ? z : m;
-    }
-  {
-    const float mo = __shfl_xor(m, 32);
-    m = mo > m ? mo : m;
+      for (int rr = 0; rr < 16; ++rr)
+        if (32 * tt + acc_row(rr, hf) >= key_lim) s[tt][rr] = -INFINITY;
   }
+  float m = fmaxf(s[0][0], s[0][1]);
+#pragma unroll
+  for (int rr = 2; rr < 32; ++rr) m = fmaxf(m, s[rr >> 4][rr & 15]);
+  m = fmaxf(m, __shfl_xor(m, 32));
+  const float mc = m * c;
   float l = 0.f;
 #pragma unroll
   for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
     for (int rr = 0; rr < 16; ++rr) {
-      const float p = (m == -INFINITY) ? 0.f : __expf(s[tt][rr] - m);
+      const float p = __builtin_amdgcn_exp2f(fmaf(s[tt][rr], c, -mc));
       s[tt][rr] = p;
       l += p;
     }
@@ -419,7 +422,7 @@ HILS_DEV void wave_chunk_attention(const KVTile<IO, D, NT>& tile, const bf16x8_t
           if (i + j < NT) o[dt] = mfma32(a, pb[i][ks2], o[dt]);
       }
   }
-  m_out = m;
+  m_out = m * tau;
   l_out = l;
 }
 
@@ -474,18 +477,18 @@ __global__ void __launch_bounds__(256, 2) chunk_attend(const IO* __restrict__ q,
                                                        const IO* __restrict__ v, const uint32_t* __restrict__ pairs,
                                                        const uint32_t* __restrict__ boff,
                                                        const uint32_t* __restrict__ toff, void* __restrict__ partial_v,
-                                                       int Hq, int Hkv, int N, int C, int K, int nbk) {
+                                                       char* __restrict__ sink, int Hq, int Hkv, int N, int C, int K,
+                                                       int nbk) {
   constexpr int NT = io_traits<IO>::terms;
   constexpr bool STAGE = NT == 1;
   constexpr int LDQ = D + 8;   // bf16 row stride of the staged rows (16-byte aligned rows)
   constexpr int SEGS = D / 8;  // 16-byte segments per bf16 row
   constexpr int RPL = 64 / SEGS;  // rows covered by one wave-wide 16-byte load
   constexpr int NLD = 32 / RPL;   // loads per lane for the wave's 32 rows
-  using PT = typename partial_t<IO>::type;
   __shared__ KVTile<IO, D, NT> tile;
   __shared__ __align__(16) uint16_t qs[STAGE ? AT_ROWS * LDQ : 8];
-  __shared__ uint32_t ipid[ITEM_ROWS];  // the item's pair ids (linear selection index) ...
-  __shared__ uint32_t irow[ITEM_ROWS];  // ... and their query rows (pair id / K)
+  __shared__ uint32_t ipid[ITEM_ROWS];  // the item's output slots (in-head, K + 1 per row) ...
+  __shared__ uint32_t irow[ITEM_ROWS];  // ... and their in-head query rows
   const int item = blockIdx.x;
   if ((uint32_t)item >= toff[nbk]) return;
   // bucket = last index with toff[bk] <= item
@@ -504,14 +507,22 @@ __global__ void __launch_bounds__(256, 2) chunk_attend(const IO* __restrict__ q,
   const int kvh = h / (Hq / Hkv);
   const int64_t row0 = ((int64_t)b * Hkv + kvh) * N + (int64_t)c * 64;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, hf = lane >> 5;
+  // every row of a bucket belongs to head bh: 32-bit offsets from the head's bases
+  const int64_t bh = bk / C;
+  const IO* __restrict__ q_head = q + bh * N * D;
+  using PT = typename partial_t<IO>::type;
+  PT* __restrict__ part_head = reinterpret_cast<PT*>(partial_v) + bh * N * (K + 1) * D;
+  const uint32_t e_head = (uint32_t)(bh * N * K);
   // each wave records the pair ids and query rows of its own 32 rows of every tile, so
   // its gathers need no barrier and the first one overlaps the K/V staging below
 #pragma unroll
   for (int j = 0; j < AT_TILES; j += 2) {
     const int r = (j + (lane >> 5)) * AT_ROWS + 32 * w + (lane & 31);
-    const uint32_t e = (uint32_t)r < nrows ? pp[r] : 0xffffffffu;
-    ipid[r] = e;
-    irow[r] = e != 0xffffffffu ? e / (uint32_t)K : 0u;
+    const bool ok = (uint32_t)r < nrows;
+    const uint32_t el = ok ? pp[r] - e_head : 0u;  // in-head pair index i*K + slot
+    const uint32_t i = el / (uint32_t)K;
+    ipid[r] = ok ? el + i : 0xffffffffu;  // slot of row i, K + 1 slots per row
+    irow[r] = i;
   }
   __builtin_amdgcn_wave_barrier();
   const int ntile = (int)((nrows + AT_ROWS - 1) / AT_ROWS);
@@ -519,81 +530,95 @@ __global__ void __launch_bounds__(256, 2) chunk_attend(const IO* __restrict__ q,
   if constexpr (STAGE) {
     uint16_t* myq = &qs[32 * w * LDQ];   // this wave's 32 staged rows
     const int lr = lane / SEGS, sg = lane % SEGS;
-    // query rows of tiles j and j+1 in flight (two register buffers); rows beyond the
-    // item load query row 0 (in bounds) and store nothing
-    u32x4_t qn[2][NLD];
-    auto gather = [&](int j, int buf) {
+    char* pbase = reinterpret_cast<char*>(part_head) + 16 * sg;
+    char* sinkp = sink + 16 * sg;
+    // query rows of tiles j and j+1 in flight in two named register buffers, one per
+    // tile parity.  Tiles past the item load query row 0 and padding rows store to the
+    // sink: every load and store is issued unconditionally, so the wait counts stay exact
+    // and the loads land straight in the buffer they are consumed from.
+    u32x4_t qa[NLD], qb2[NLD];
+    auto gather = [&](int j, u32x4_t(&buf)[NLD]) {
+      const uint32_t keep = j < ntile ? 0xffffffffu : 0u;  // uniform
+      const int jr = min(j, AT_TILES - 1);
 #pragma unroll
       for (int u = 0; u < NLD; ++u) {
-        const int r = j * AT_ROWS + 32 * w + RPL * u + lr;
-        qn[buf][u] = *reinterpret_cast<const u32x4_t*>(q + (int64_t)irow[r] * D + 8 * sg);
+        const uint32_t ir = irow[jr * AT_ROWS + 32 * w + RPL * u + lr] & keep;
+        buf[u] = *reinterpret_cast<const u32x4_t*>(reinterpret_cast<const char*>(q_head) +
+                                                   (ir * (uint32_t)(D * sizeof(IO)) + 16u * sg));
       }
     };
-    gather(0, 0);
-    if (ntile > 1) gather(1, 1);
-    stage_kv<IO, D, NT>(tile, k, v, row0, 64, tid, 256);
-    __syncthreads();
-    // unrolled over the (at most AT_TILES) tiles, so the buffers are registers
+    // tile j: its rows (in buf) to the wave's LDS rows, the prefetch of tile j + 2 into
+    // buf, then the MFMA attention and whole-row fp16 stores through the same LDS rows
+    auto step = [&](int j, u32x4_t(&buf)[NLD]) {
 #pragma unroll
-    for (int j = 0; j < AT_TILES; ++j) {
-      if (j >= ntile) break;
-#pragma unroll
-      for (int u = 0; u < NLD; ++u)
-        *reinterpret_cast<u32x4_t*>(&myq[(RPL * u + lr) * LDQ + 8 * sg]) = qn[j & 1][u];
+      for (int u = 0; u < NLD; ++u) *reinterpret_cast<u32x4_t*>(&myq[(RPL * u + lr) * LDQ + 8 * sg]) = buf[u];
       __builtin_amdgcn_wave_barrier();
-      if (j + 2 < ntile) gather(j + 2, j & 1);
-      bf16x8_t qb[1][D / 16];
-      lds_q_operand<D>(&myq[(lane & 31) * LDQ], qb);
-      f32x16_t o[D / 32];
-      float m, l;
-      wave_chunk_attention<IO, D, NT>(tile, *reinterpret_cast<bf16x8_t(*)[NT][D / 16]>(&qb), 64, o, m, l);
-      const float inv = 1.0f / l;
-      __builtin_amdgcn_wave_barrier();
-      // normalised output (fp16) over this wave's staged rows, then whole-row stores
+      gather(j + 2, buf);
+      if (j < ntile) {
+        bf16x8_t qb[1][D / 16];
+        lds_q_operand<D>(&myq[(lane & 31) * LDQ], qb);
+        f32x16_t o[D / 32];
+        float m, l;
+        wave_chunk_attention<IO, D, NT, false>(tile, *reinterpret_cast<bf16x8_t(*)[NT][D / 16]>(&qb), 64, o, m, l);
+        const float inv = __builtin_amdgcn_rcpf(l);  // l >= 1 (the max logit's term)
+        __builtin_amdgcn_wave_barrier();
 #pragma unroll
-      for (int dt = 0; dt < D / 32; ++dt)
+        for (int dt = 0; dt < D / 32; ++dt)
 #pragma unroll
-        for (int g4 = 0; g4 < 4; ++g4) {
-          const int e = 32 * dt + 8 * g4 + 4 * hf;
-          u32x2_t pk;
-          pk.x = (uint32_t)f32_to_f16(o[dt][4 * g4 + 0] * inv) | ((uint32_t)f32_to_f16(o[dt][4 * g4 + 1] * inv) << 16);
-          pk.y = (uint32_t)f32_to_f16(o[dt][4 * g4 + 2] * inv) | ((uint32_t)f32_to_f16(o[dt][4 * g4 + 3] * inv) << 16);
-          *reinterpret_cast<u32x2_t*>(&myq[(lane & 31) * LDQ + e]) = pk;
+          for (int g4 = 0; g4 < 4; ++g4) {
+            const int e = 32 * dt + 8 * g4 + 4 * hf;
+            u32x2_t pk;
+            pk.x = pack_f16x2(o[dt][4 * g4 + 0] * inv, o[dt][4 * g4 + 1] * inv);
+            pk.y = pack_f16x2(o[dt][4 * g4 + 2] * inv, o[dt][4 * g4 + 3] * inv);
+            *reinterpret_cast<u32x2_t*>(&myq[(lane & 31) * LDQ + e]) = pk;
+          }
+        __builtin_amdgcn_wave_barrier();
+        uint32_t slot[NLD];
+        u32x4_t val[NLD];
+#pragma unroll
+        for (int u = 0; u < NLD; ++u) {
+          slot[u] = ipid[j * AT_ROWS + 32 * w + RPL * u + lr];
+          val[u] = *reinterpret_cast<const u32x4_t*>(&myq[(RPL * u + lr) * LDQ + 8 * sg]);
         }
-      __builtin_amdgcn_wave_barrier();
-      uint16_t* dst = reinterpret_cast<uint16_t*>(partial_v);
 #pragma unroll
-      for (int u = 0; u < NLD; ++u) {
-        const int r = j * AT_ROWS + 32 * w + RPL * u + lr;
-        const uint32_t e = ipid[r];
-        const u32x4_t val = *reinterpret_cast<const u32x4_t*>(&myq[(RPL * u + lr) * LDQ + 8 * sg]);
-        if (e != 0xffffffffu)  // slot (e mod K) of row e / K, K + 1 slots per row
-          __builtin_nontemporal_store(val, reinterpret_cast<u32x4_t*>(dst + ((int64_t)e + irow[r]) * D + 8 * sg));
+        for (int u = 0; u < NLD; ++u) {
+          char* dst = slot[u] != 0xffffffffu ? pbase + (uint64_t)slot[u] * (D * sizeof(PT)) : sinkp;
+          __builtin_nontemporal_store(val[u], reinterpret_cast<u32x4_t*>(dst));
+        }
       }
       __builtin_amdgcn_wave_barrier();
+    };
+    gather(0, qa);
+    gather(1, qb2);
+    stage_kv<IO, D, NT>(tile, k, v, row0, 64, tid, 256);
+    __syncthreads();
+    for (int j = 0; j < ntile; j += 2) {
+      step(j, qa);
+      step(j + 1, qb2);
     }
   } else {
     stage_kv<IO, D, NT>(tile, k, v, row0, 64, tid, 256);
     __syncthreads();
     for (int j = 0; j < ntile; ++j) {
       const int r = j * AT_ROWS + rl;
-      const uint32_t e_pair = ipid[r];
-      const bool ok = e_pair != 0xffffffffu;
+      const uint32_t slot = ipid[r];
+      const bool ok = slot != 0xffffffffu;
       bf16x8_t qb[NT][D / 16];
-      load_q_operand<IO, D, NT>(q, (int64_t)irow[r] * D, ok, qb);
+      load_q_operand<IO, D, NT>(q_head, (int64_t)irow[r] * D, ok, qb);
       f32x16_t o[D / 32];
       float m, l;
-      wave_chunk_attention<IO, D, NT>(tile, qb, 64, o, m, l);
+      wave_chunk_attention<IO, D, NT, false>(tile, qb, 64, o, m, l);
       const float inv = 1.0f / l;
       if (ok) {
-        PT* dst = reinterpret_cast<PT*>(partial_v) + ((int64_t)e_pair + irow[r]) * D;
+        PT* dst = part_head + (int64_t)slot * D;
 #pragma unroll
         for (int dt = 0; dt < D / 32; ++dt)
 #pragma unroll
           for (int g4 = 0; g4 < 4; ++g4) {
             const int e = 32 * dt + 8 * g4 + 4 * hf;
-            *reinterpret_cast<float4*>(dst + e) = make_float4(o[dt][4 * g4] * inv, o[dt][4 * g4 + 1] * inv,
-                                                              o[dt][4 * g4 + 2] * inv, o[dt][4 * g4 + 3] * inv);
+            *reinterpret_cast<float4*>(dst + e) =
+                make_float4(o[dt][4 * g4] * inv, o[dt][4 * g4 + 1] * inv, o[dt][4 * g4 + 2] * inv,
+                            o[dt][4 * g4 + 3] * inv);
           }
       }
     }
@@ -631,7 +656,7 @@ __global__ void __launch_bounds__(128) own_attend(const IO* __restrict__ q, cons
   __syncthreads();
   f32x16_t oa[D / 32];
   float m, l;
-  wave_chunk_attention<IO, D, NT>(tile, qb, rl + 1, oa, m, l);  // causal: keys 0..rl
+  wave_chunk_attention<IO, D, NT, true>(tile, qb, rl + 1, oa, m, l);  // causal: keys 0..rl
   if (!ok) return;
   const int64_t row = (int64_t)bh * N + i;
   const float inv = 1.0f / l;
@@ -643,8 +668,8 @@ __global__ void __launch_bounds__(128) own_attend(const IO* __restrict__ q, cons
       const int e = 32 * dt + 8 * g4 + 4 * hf;
       if constexpr (sizeof(PT) == 2) {
         u32x2_t pk;
-        pk.x = (uint32_t)f32_to_f16(oa[dt][4 * g4 + 0] * inv) | ((uint32_t)f32_to_f16(oa[dt][4 * g4 + 1] * inv) << 16);
-        pk.y = (uint32_t)f32_to_f16(oa[dt][4 * g4 + 2] * inv) | ((uint32_t)f32_to_f16(oa[dt][4 * g4 + 3] * inv) << 16);
+        pk.x = pack_f16x2(oa[dt][4 * g4 + 0] * inv, oa[dt][4 * g4 + 1] * inv);
+        pk.y = pack_f16x2(oa[dt][4 * g4 + 2] * inv, oa[dt][4 * g4 + 3] * inv);
         *reinterpret_cast<u32x2_t*>(dst + e) = pk;
       } else {
         *reinterpret_cast<float4*>(dst + e) = make_float4(oa[dt][4 * g4] * inv, oa[dt][4 * g4 + 1] * inv,
@@ -791,7 +816,7 @@ static hipError_t launch_attend_t(const Geom& g, const void* q, const void* k, c
     const int64_t items = std::min<int64_t>((pairs_total + ITEM_ROWS - 1) / ITEM_ROWS + nbk, 0x7fffffff);
     if (pairs_total > 0)
       hipLaunchKernelGGL((chunk_attend<IO, D>), dim3((unsigned)items), dim3(256), 0, st, (const IO*)q, (const IO*)k,
-                         (const IO*)v, pairs, boff, toff, partial, g.Hq, g.Hkv, g.N, C, g.K, nbk);
+                         (const IO*)v, pairs, boff, toff, partial, ws + w.sink, g.Hq, g.Hkv, g.N, C, g.K, nbk);
     if (ev) hipEventRecord(ev[1], st);
   } else if (ev) {
     hipEventRecord(ev[0], st);

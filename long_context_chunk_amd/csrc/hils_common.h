@@ -33,6 +33,13 @@ HILS_DEV uint32_t pack_bf16x2(float lo, float hi) {
   return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_t));
 }
 
+// two floats -> packed fp16 pair (lo in bits 0..15), round to nearest even, one instruction
+typedef __attribute__((ext_vector_type(2))) _Float16 f16x2_t;
+HILS_DEV uint32_t pack_f16x2(float lo, float hi) {
+  const f32x2_t v = {lo, hi};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, f16x2_t));
+}
+
 HILS_DEV uint16_t f32_to_f16(float f) {
   _Float16 h = (_Float16)f;
   return __builtin_bit_cast(uint16_t, h);
