@@ -352,7 +352,7 @@ def run_decode(wd, steps, warmup, seed):
     scan_bytes = sum(P * wd.Hlmk * (wd.d + 1) * 4 for P in Ps)
     total_bytes = scan_bytes + kv_bytes + 2 * 2 * wd.B * wd.Hq * wd.d
     step_gbs = total_bytes / (us * 1e-6) / 1e9
-    scan_gbs = scan_bytes / (stages["scan_topk"] * 1e-3) / 1e9
+    scan_gbs = scan_bytes / (stages["scan"] * 1e-3) / 1e9
     log("decode: %.1f us/step (stages ms %s)" % (us, stages))
     dense_kv = sum(int(L) for L in x["seq_lens"]) * wd.Hkv * wd.d * 2 * 2
     return {

@@ -155,10 +155,11 @@ int hils_attn_decode(const hils_dims_t* dims, const void* q, const void* k_cache
 /*
  * hils_attn_decode for measurement: the same work, plus the GPU time of each
  * stage in milliseconds (HIP events on `stream`) in stage_ms[HILS_DECODE_STAGES]
- * (a HOST array): [0] chunk scoring scan and top-K, [1] chunk gather-attention
- * and fusion.  Synchronises with the stream before returning.
+ * (a HOST array): [0] chunk scoring scan (with each split's best chunks), [1]
+ * the merge into the top-K, [2] chunk gather-attention and fusion.  Synchronises
+ * with the stream before returning.
  */
-#define HILS_DECODE_STAGES 2
+#define HILS_DECODE_STAGES 3
 int hils_attn_decode_timed(const hils_dims_t* dims, const void* q, const void* k_cache, const void* v_cache,
                            const int32_t* seq_lens, const float* kc, const float* bc, const void* qcal_D,
                            const void* qcal_U, int32_t* sel_idx_out, void* o, void* ws, size_t ws_bytes,

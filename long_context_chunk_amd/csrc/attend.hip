@@ -101,7 +101,7 @@ __global__ void __launch_bounds__(256) bucket_count(const int32_t* __restrict__ 
     }
 #pragma unroll
     for (int u = 0; u < BK_PER; ++u)
-      if (c[u] >= 0) atomicAdd(&hist[c[u]], 1u);
+      if ((unsigned)c[u] < (unsigned)C) atomicAdd(&hist[c[u]], 1u);  // -1 (padding) and bad ids skipped
   }
   __syncthreads();
   for (int i = threadIdx.x; i < C; i += 256)
@@ -188,7 +188,8 @@ __global__ void __launch_bounds__(256) bucket_part1(const int32_t* __restrict__ 
 #pragma unroll
     for (int u = 0; u < BK_PER; ++u) {
       const int64_t i = t0 + t + 256 * u;
-      c[u] = i < end ? s[i] : -1;
+      const int32_t x = i < end ? s[i] : -1;
+      c[u] = (unsigned)x < (unsigned)C ? x : -1;  // the same entries bucket_count counted
     }
 #pragma unroll
     for (int u = 0; u < BK_PER; ++u)

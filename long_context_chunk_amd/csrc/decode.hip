@@ -421,14 +421,15 @@ static hipError_t launch_decode_t(const Geom& g, const void* q, const void* kcac
   if (ev) (void)hipEventRecord(ev[0], st);
   hipLaunchKernelGGL((decode_scan<IO, D>), dim3(BH * nsplit), dim3(256), 0, st, (const IO*)q, (const IO*)Dw,
                      (const IO*)Uw, kc, bc, seq_lens, cand, g.Hq, C, g.r, nsplit);
+  if (ev) (void)hipEventRecord(ev[1], st);
   hipLaunchKernelGGL(decode_merge, dim3(BH), dim3(256), 0, st, (const uint64_t*)cand, seq_lens, sel_i, sel_s, nsel,
                      sel_user, g.Hq, C, g.K, nsplit);
-  if (ev) (void)hipEventRecord(ev[1], st);
+  if (ev) (void)hipEventRecord(ev[2], st);
   hipLaunchKernelGGL((decode_attend<IO, D>), dim3(BH * (g.K + 1)), dim3(256), 0, st, (const IO*)q, (const IO*)kcache,
                      (const IO*)vcache, seq_lens, sel_i, sel_s, nsel, part, sig, g.Hq, g.Hkv, g.N, g.K);
   hipLaunchKernelGGL((decode_combine<IO, D>), dim3(BH), dim3(256), 0, st, (const float*)part, (const float*)sig,
                      (const int32_t*)nsel, (IO*)o, g.K);
-  if (ev) (void)hipEventRecord(ev[2], st);
+  if (ev) (void)hipEventRecord(ev[3], st);
   return hipGetLastError();
 }
 

@@ -32,8 +32,8 @@ hipError_t launch_prefill_attend(const Geom& g, const void* q, const void* k, co
 
 // One decode step.
 size_t decode_workspace_bytes(const Geom& g);
-// ev (nullable): three events recorded before the scan, after scoring and top-K, and after
-// chunk attention and fusion.
+// ev (nullable): four events recorded before the scan, after it, after the top-K merge, and
+// after chunk attention and fusion.
 hipError_t launch_decode(const Geom& g, const void* q, const void* kcache, const void* vcache, const int32_t* seq_lens,
                          const float* kc, const float* bc, const void* D, const void* U, int32_t* sel_idx_out,
                          void* o, void* ws, size_t ws_bytes, hipStream_t st, hipEvent_t* ev = nullptr);

@@ -555,17 +555,10 @@ __global__ void __launch_bounds__(256, 2) score_topk_kernel(const IO* __restrict
     }
   };
 
-  const int nct = (Pmax + SEL_CT - 1) / SEL_CT;
-  if (nct > 0) {
-    load_tile(0);
-    store_tile();
-  }
-  __syncthreads();
-  for (int ct = 0; ct < nct; ++ct) {
-    const bool more = ct + 1 < nct;
-    if (more) load_tile(ct + 1);
-    f32x16_t acc = zero16();
-    const uint16_t* krow = &kt[n * LDR];   // A operand row: chunk n of the tile
+  // the scores of the tile in LDS (chunk n of the tile is the A operand row)
+  auto tile_scores = [&]() {
+    f32x16_t a_ = zero16();
+    const uint16_t* krow = &kt[n * LDR];
 #pragma unroll
     for (int ks = 0; ks < NKS; ++ks)
 #pragma unroll
@@ -573,9 +566,28 @@ __global__ void __launch_bounds__(256, 2) score_topk_kernel(const IO* __restrict
         const bf16x8_t a = *reinterpret_cast<const bf16x8_t*>(krow + j * D + (j ? P2_EXT : 0) + 16 * ks + 8 * hf);
 #pragma unroll
         for (int i = 0; i < NQ; ++i)
-          if (i + j < (NQ > NK ? NQ : NK)) acc = mfma32(a, qb[i][ks], acc);
+          if (i + j < (NQ > NK ? NQ : NK)) a_ = mfma32(a, qb[i][ks], a_);
       }
-    acc = mfma32(*reinterpret_cast<const bf16x8_t*>(krow + D + 8 * hf), qext, acc);  // + b'
+    return mfma32(*reinterpret_cast<const bf16x8_t*>(krow + D + 8 * hf), qext, a_);  // + b'
+  };
+
+  // Software pipeline: while tile ct's scores are tested and appended, the MFMAs of
+  // tile ct + 1 (already staged in LDS) run; tile ct + 2 is in flight from memory.
+  const int nct = (Pmax + SEL_CT - 1) / SEL_CT;
+  if (nct > 0) {
+    load_tile(0);
+    store_tile();
+  }
+  __syncthreads();
+  f32x16_t acc = tile_scores();
+  if (nct > 1) load_tile(1);
+  __syncthreads();  // every wave has read tile 0
+  if (nct > 1) store_tile();
+  __syncthreads();
+  for (int ct = 0; ct < nct; ++ct) {
+    const bool more2 = ct + 2 < nct;
+    if (more2) load_tile(ct + 2);
+    f32x16_t acc_next;
     // candidates: s >= th goes to this lane's half list.  A full list takes further
     // candidates in its spill slot (lost for now); the row is compacted after the tile
     // and the lost ones are appended again against the raised threshold.
@@ -614,11 +626,24 @@ __global__ void __launch_bounds__(256, 2) score_topk_kernel(const IO* __restrict
         }
       }
     };
+    // The MFMAs of tile ct + 1 (past the last tile they recompute the last one; never
+    // used) and the appends of tile ct in one block, interleaved one MFMA per score, so
+    // the matrix core works while the vector unit appends.
+    auto scores_and_append = [&](auto masked_tag) {
+      acc_next = tile_scores();
+      append_all(masked_tag);
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one MFMA
+        __builtin_amdgcn_sched_group_barrier(0x002, 10, 0);  // the VALU of one append
+        __builtin_amdgcn_sched_group_barrier(0x200, 2, 0);   // its two LDS writes
+      }
+    };
     const bool masked = (ct + 1) * SEL_CT > Pmin;  // chunks >= Pmin are not past chunks of every row
     if (masked)
-      append_all(std::true_type{});
+      scores_and_append(std::true_type{});
     else
-      append_all(std::false_type{});
+      scores_and_append(std::false_type{});
     const uint64_t ovf = __ballot(lf > lcap);
     if (ovf) {  // rare: compact the rows with a full half list, then re-append what was lost
       uint32_t rows_big = (uint32_t)ovf | (uint32_t)(ovf >> 32);
@@ -653,11 +678,10 @@ __global__ void __launch_bounds__(256, 2) score_topk_kernel(const IO* __restrict
       else
         reappend_lost(std::false_type{});
     }
-    __syncthreads();  // every wave is done with this tile
-    if (more) {
-      store_tile();
-      __syncthreads();
-    }
+    __syncthreads();  // every wave is done with tile ct + 1 in LDS
+    if (more2) store_tile();
+    __syncthreads();
+    acc = acc_next;
   }
 
   // ---- final selection and output, two rows per step: lane j of each half writes slot j

@@ -22,7 +22,7 @@ OK, E_INVAL, E_UNSUPPORTED, E_WORKSPACE, E_HIP = 0, -1, -2, -3, -4
 SYMBOLS = ("hils_workspace_bytes", "hils_landmark_compress", "hils_chunk_score_topk", "hils_attn_prefill",
            "hils_attn_prefill_timed", "hils_attn_decode", "hils_attn_decode_timed", "hils_last_error")
 STAGES = ("compress", "score_threshold", "score_select", "bucket", "chunk_attend", "own_attend", "fuse")
-DECODE_STAGES = ("scan_topk", "attend_fuse")
+DECODE_STAGES = ("scan", "merge", "attend_fuse")
 
 
 class Dims(ctypes.Structure):
