@@ -104,37 +104,56 @@ HILS_DEV void merge_intok(uint64_t& lk, uint64_t nk, int j, int K) {
 
 HILS_DEV float readlane_f(float v, int l) { return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), l)); }
 
-// float-only compare-exchange with lane j ^ X: keep the larger of the pair if keep_max
+// value of lane j ^ X within each 32-lane half: DPP quad permutations for X < 4, one
+// ds_swizzle (xor mode) otherwise
 template <int X>
-HILS_DEV float cxf(float s, int j, bool keep_max) {
-  const float p = __int_as_float(xlane<X>(__float_as_int(s), j));
-  return (p > s) == keep_max ? p : s;
+HILS_DEV float xl1(float v) {
+  if constexpr (X == 1 || X == 2) {
+    return __int_as_float(dpp<X == 1 ? 0xB1 : 0x4E>(__float_as_int(v)));
+  } else {
+    static_assert(X == 4 || X == 8 || X == 16 || X == 31, "");
+    constexpr int OFS = X == 31 ? 0x7C1F : (0x1F | (X << 10));  // X == 31: reverse the half
+    return __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(v), OFS));
+  }
 }
 
-// bitonic sort of one float per lane, descending, within each 32-lane half
-HILS_DEV float sort32f(float s, int j) {
-#define HILS_STAGE(K_, X_) s = cxf<X_>(s, j, ((j & X_) == 0) == (((j & K_) == 0) || K_ == 32));
+// One compare-exchange stage with lane j ^ X on R independent registers: med3(s, p, +inf)
+// keeps the larger, med3(s, p, -inf) the smaller; the bound is chosen per lane.
+template <int X, int R>
+HILS_DEV void cx_stage(float (&s)[R], float bnd) {
+  float p[R];
+#pragma unroll
+  for (int i = 0; i < R; ++i) p[i] = xl1<X>(s[i]);
+#pragma unroll
+  for (int i = 0; i < R; ++i) s[i] = __builtin_amdgcn_fmed3f(s[i], p[i], bnd);
+}
+
+// Descending bitonic sort within each 32-lane half, R registers at once.  pinf / ninf
+// are +-inf hidden from the compiler, so the med3s stay med3s.
+template <int R>
+HILS_DEV void sort32f_r(float (&s)[R], int j, float pinf, float ninf) {
+#define HILS_STAGE(K_, X_) cx_stage<X_, R>(s, (((j & X_) == 0) == (((j & K_) == 0) || K_ == 32)) ? pinf : ninf);
   HILS_STAGE(2, 1)
   HILS_STAGE(4, 2) HILS_STAGE(4, 1)
   HILS_STAGE(8, 4) HILS_STAGE(8, 2) HILS_STAGE(8, 1)
   HILS_STAGE(16, 8) HILS_STAGE(16, 4) HILS_STAGE(16, 2) HILS_STAGE(16, 1)
   HILS_STAGE(32, 16) HILS_STAGE(32, 8) HILS_STAGE(32, 4) HILS_STAGE(32, 2) HILS_STAGE(32, 1)
 #undef HILS_STAGE
-  return s;
 }
 
-// the K-th largest of the 64 values {a, b} of each 32-lane half, broadcast to its lanes
-HILS_DEV float kth_of_pairs(float a, float b, int j, int hf, int K) {
-  a = sort32f(a, j);
-  b = sort32f(b, j);
-  a = __builtin_amdgcn_fmed3f(a, __int_as_float(xlane<31>(__float_as_int(b), j)), INFINITY);  // the 32 largest, bitonic
-  a = cxf<16>(a, j, (j & 16) == 0);
-  a = cxf<8>(a, j, (j & 8) == 0);
-  a = cxf<4>(a, j, (j & 4) == 0);
-  a = cxf<2>(a, j, (j & 2) == 0);
-  a = cxf<1>(a, j, (j & 1) == 0);
-  const float t0 = readlane_f(a, K - 1), t1 = readlane_f(a, 32 + K - 1);
-  return hf ? t1 : t0;
+// For R registers at once: the K-th largest of the 64 values {a, b} of each 32-lane half,
+// left in lane K - 1 of the half (a is overwritten with the half's 32 largest, sorted).
+template <int R>
+HILS_DEV void kth_of_pairs_r(float (&a)[R], float (&b)[R], int j, float pinf, float ninf) {
+  sort32f_r<R>(a, j, pinf, ninf);
+  sort32f_r<R>(b, j, pinf, ninf);
+#pragma unroll
+  for (int i = 0; i < R; ++i) a[i] = __builtin_amdgcn_fmed3f(a[i], xl1<31>(b[i]), pinf);  // the 32 largest, bitonic
+  cx_stage<16, R>(a, (j & 16) == 0 ? pinf : ninf);
+  cx_stage<8, R>(a, (j & 8) == 0 ? pinf : ninf);
+  cx_stage<4, R>(a, (j & 4) == 0 ? pinf : ninf);
+  cx_stage<2, R>(a, (j & 2) == 0 ? pinf : ninf);
+  cx_stage<1, R>(a, (j & 1) == 0 ? pinf : ninf);
 }
 
 // bf16 bits of the smallest bf16 >= x (x >= 0), clamped to the largest finite bf16
@@ -296,8 +315,7 @@ __global__ void __launch_bounds__(256, 2) score_threshold(const IO* __restrict__
   constexpr int NSEG = ST_TILE * SEGS;
   constexpr int PL = (NSEG + 255) / 256;
   constexpr int TILE_BYTES = 2 * ST_TILE * LDT * 2;
-  constexpr int TOP2_BYTES = 4 * 16 * 2 * 64 * 4;  // per wave, register, top-2 slot, lane
-  __shared__ __align__(16) unsigned char smem[TILE_BYTES > TOP2_BYTES ? TILE_BYTES : TOP2_BYTES];
+  __shared__ __align__(16) unsigned char smem[TILE_BYTES];
   uint16_t(*kt)[ST_TILE * LDT] = reinterpret_cast<uint16_t(*)[ST_TILE * LDT]>(smem);
 
   const int item = remap_xcd(blockIdx.x, items);
@@ -415,19 +433,15 @@ __global__ void __launch_bounds__(256, 2) score_threshold(const IO* __restrict__
     if (more) store_tile(buf ^ 1);
     __syncthreads();
   }
-  // theta per row: park the top-two values in LDS (the tiles are no longer read) and
-  // reduce one register row-pair at a time
-  float* mm = reinterpret_cast<float*>(smem) + w * (16 * 2 * 64);
+  // theta per row: all 16 register rows (two rows each, one per half) at once
+  float ninf = -INFINITY;
+  asm volatile("" : "+v"(ninf));
+  kth_of_pairs_r<16>(m1, m2, n, pinf, ninf);
 #pragma unroll
   for (int rr = 0; rr < 16; ++rr) {
-    mm[(2 * rr) * 64 + lane] = m1[rr];
-    mm[(2 * rr + 1) * 64 + lane] = m2[rr];
-  }
-  __builtin_amdgcn_wave_barrier();
-#pragma unroll 1
-  for (int rr = 0; rr < 16; ++rr) {
-    const float th = kth_of_pairs(mm[(2 * rr) * 64 + lane], mm[(2 * rr + 1) * 64 + lane], n, hf, K);
     const int rw = r0 + 32 * w + acc_row(rr, hf);
+    const float t0 = readlane_f(m1[rr], K - 1), t1 = readlane_f(m1[rr], 32 + K - 1);
+    const float th = hf ? t1 : t0;
     if (n == 0 && rw < N) theta[(int64_t)bh * N + rw] = th;
   }
 }
