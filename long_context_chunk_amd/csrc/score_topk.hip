@@ -156,6 +156,34 @@ HILS_DEV void kth_of_pairs_r(float (&a)[R], float (&b)[R], int j, float pinf, fl
   cx_stage<1, R>(a, (j & 1) == 0 ? pinf : ninf);
 }
 
+// 64-bit key of lane j ^ X within each 32-lane half (X as in xl1)
+template <int X>
+HILS_DEV uint64_t xl64(uint64_t v) {
+  const uint32_t lo = __float_as_uint(xl1<X>(__uint_as_float((uint32_t)v)));
+  const uint32_t hi = __float_as_uint(xl1<X>(__uint_as_float((uint32_t)(v >> 32))));
+  return ((uint64_t)hi << 32) | lo;
+}
+// compare-exchange of R independent 64-bit keys with lane j ^ X: keep the larger if kb
+template <int X, int R>
+HILS_DEV void cxk_r(uint64_t (&k)[R], bool kb) {
+  uint64_t p[R];
+#pragma unroll
+  for (int i = 0; i < R; ++i) p[i] = xl64<X>(k[i]);
+#pragma unroll
+  for (int i = 0; i < R; ++i) k[i] = ((p[i] > k[i]) == kb) ? p[i] : k[i];
+}
+// best-first bitonic sort within each 32-lane half, R registers at once
+template <int R>
+HILS_DEV void sort32k_r(uint64_t (&k)[R], int j) {
+#define HILS_STAGE(K_, X_) cxk_r<X_, R>(k, ((j & X_) == 0) == (((j & K_) == 0) || K_ == 32));
+  HILS_STAGE(2, 1)
+  HILS_STAGE(4, 2) HILS_STAGE(4, 1)
+  HILS_STAGE(8, 4) HILS_STAGE(8, 2) HILS_STAGE(8, 1)
+  HILS_STAGE(16, 8) HILS_STAGE(16, 4) HILS_STAGE(16, 2) HILS_STAGE(16, 1)
+  HILS_STAGE(32, 16) HILS_STAGE(32, 8) HILS_STAGE(32, 4) HILS_STAGE(32, 2) HILS_STAGE(32, 1)
+#undef HILS_STAGE
+}
+
 // bf16 bits of the smallest bf16 >= x (x >= 0), clamped to the largest finite bf16
 HILS_DEV uint16_t bf16_up(float x) {
   if (!(x < 3.38e38f)) return 0x7f7f;
@@ -460,7 +488,7 @@ constexpr int SEL_HALF = 32;   // candidate slots per half-row list (plus one sp
 constexpr int P2_EXT = 16;     // extension elements after plane 0: [b'_hi, b'_mid, b'_lo, 0 ...]
 
 template <typename IO, int D, int NQ, int NK, bool QCAL>
-__global__ void __launch_bounds__(256, 2) score_topk_kernel(const IO* __restrict__ q, const IO* __restrict__ Dw,
+__global__ void __launch_bounds__(256, NQ * NK > 4 ? 1 : 2) score_topk_kernel(const IO* __restrict__ q, const IO* __restrict__ Dw,
                                                              const IO* __restrict__ Uw,
                                                              const uint16_t* __restrict__ p2,
                                                              const float* __restrict__ theta,
@@ -646,6 +674,7 @@ __global__ void __launch_bounds__(256, 2) score_topk_kernel(const IO* __restrict
     auto scores_and_append = [&](auto masked_tag) {
       acc_next = tile_scores();
       append_all(masked_tag);
+      if constexpr (NQ * NK <= 4)  // the fp32 path has too few registers left to interleave
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one MFMA
@@ -698,18 +727,42 @@ __global__ void __launch_bounds__(256, 2) score_topk_kernel(const IO* __restrict
     acc = acc_next;
   }
 
-  // ---- final selection and output, two rows per step: lane j of each half writes slot j
+  // ---- final selection and output: eight row pairs (p, p + 16) at a time, the two half
+  // lists of a row sorted as keys and merged to the best K; lane j of each half writes slot j
+  constexpr int FR = NQ * NK > 4 ? 4 : 8;  // fewer at once where the score operands take more registers
+  const int myfill = lf - lbase;
 #pragma unroll 1
-  for (int p = 0; p < 16; ++p) {
-    uint64_t lk;
-    int nv;
-    settle2(p, p + 16, false, lk, nv);
-    const int rw = r0 + 32 * w + (hf ? p + 16 : p);
-    if (rw < N && n < K) {
-      const int64_t o = ((int64_t)bh * N + rw) * K + n;
-      const bool ok = lk != 0;
-      sel_idx[o] = ok ? key_chunk(lk) : -1;
-      sel_score[o] = ok ? key_score(lk) : -INFINITY;
+  for (int p0 = 0; p0 < 16; p0 += FR) {
+    uint64_t x[FR], y[FR];
+#pragma unroll
+    for (int i = 0; i < FR; ++i) {
+      const int rw = hf ? p0 + i + 16 : p0 + i;
+      const int f0 = min(__shfl(myfill, rw), SEL_HALF), f1 = min(__shfl(myfill, 32 + rw), SEL_HALF);
+      const int base = (32 * w + rw) * LIST;
+      x[i] = n < f0 ? make_key(cs[base + n], ci[base + n]) : 0ull;
+      y[i] = n < f1 ? make_key(cs[base + HSTR + n], ci[base + HSTR + n]) : 0ull;
+    }
+    sort32k_r<FR>(x, n);
+    sort32k_r<FR>(y, n);
+#pragma unroll
+    for (int i = 0; i < FR; ++i) {  // the 32 best of both lists, a bitonic sequence
+      const uint64_t r = xl64<31>(y[i]);
+      x[i] = r > x[i] ? r : x[i];
+    }
+    cxk_r<16, FR>(x, (n & 16) == 0);
+    cxk_r<8, FR>(x, (n & 8) == 0);
+    cxk_r<4, FR>(x, (n & 4) == 0);
+    cxk_r<2, FR>(x, (n & 2) == 0);
+    cxk_r<1, FR>(x, (n & 1) == 0);
+#pragma unroll
+    for (int i = 0; i < FR; ++i) {
+      const int rw = r0 + 32 * w + (hf ? p0 + i + 16 : p0 + i);
+      if (rw < N && n < K) {
+        const int64_t o = ((int64_t)bh * N + rw) * K + n;
+        const bool ok = x[i] != 0;
+        sel_idx[o] = ok ? key_chunk(x[i]) : -1;
+        sel_score[o] = ok ? key_score(x[i]) : -INFINITY;
+      }
     }
   }
 }
