@@ -47,7 +47,8 @@ def _load():
         lib.hr_row_scores.restype = ctypes.c_int
         lib.hr_attend.argtypes = [sp, i32, i64, vp, vp, vp, vp, i32, vp, vp, i32, vp, vp, vp, vp, i32,
                                   vp, vp, vp, vp, vp, vp, vp]
-        for f in (lib.hr_compress, lib.hr_qcal, lib.hr_attend):
+        lib.hr_dense.argtypes = [sp, i64, vp, vp, vp, vp, i32, vp, vp, i32, vp]
+        for f in (lib.hr_compress, lib.hr_qcal, lib.hr_attend, lib.hr_dense):
             f.restype = None
         _lib = lib
     return _lib
@@ -140,3 +141,18 @@ def prefill_rows(s: Shape, q, k, v, kc, bc, rows, D=None, U=None, mode=LANDMARK)
     rows = np.asarray(rows, np.int64).reshape(-1, 3)
     qrows = q[rows[:, 0], rows[:, 1], rows[:, 2], :]
     return attend(s, rows[:, 0], rows[:, 1], rows[:, 2], qrows, k, v, kc, bc, D, U, mode)
+
+
+def dense(s: Shape, rows_b, rows_h, rows_pos, qrows, k, v):
+    """Dense causal attention for a list of queries (the baseline); returns o [n, d]."""
+    rb = np.ascontiguousarray(rows_b, np.int32)
+    rh = np.ascontiguousarray(rows_h, np.int32)
+    rp = np.ascontiguousarray(rows_pos, np.int32)
+    n = rb.size
+    qrows = np.ascontiguousarray(qrows).reshape(n, s.d)
+    k, v = np.ascontiguousarray(k), np.ascontiguousarray(v)
+    assert k.dtype == v.dtype
+    o = np.empty((n, s.d), np.float64)
+    _load().hr_dense(ctypes.byref(s), n, rb.ctypes.data, rh.ctypes.data, rp.ctypes.data, qrows.ctypes.data,
+                     _dt(qrows), k.ctypes.data, v.ctypes.data, _dt(k), o.ctypes.data)
+    return o

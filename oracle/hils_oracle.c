@@ -277,3 +277,24 @@ void hr_attend(const hr_shape* s, int mode, int64_t nrows, const int32_t* row_b,
     free(sig);
   }
 }
+
+/*
+ * Dense causal attention, the baseline the pages measure the sparse method
+ * against (hotpaper.ai abstract; ai-papers.net "Results"): query n of head
+ * row_h[n] at position row_pos[n] attends every key 0..pos of its KV head with
+ * one softmax over all of them.
+ */
+void hr_dense(const hr_shape* s, int64_t nrows, const int32_t* row_b, const int32_t* row_h,
+              const int32_t* row_pos, const void* qrows, int qdt, const void* k, const void* v, int kvdt,
+              double* o) {
+  const int d = s->d;
+#pragma omp parallel for schedule(dynamic, 4)
+  for (int64_t n = 0; n < nrows; ++n) {
+    double* q = (double*)malloc(sizeof(double) * d);
+    for (int e = 0; e < d; ++e) q[e] = ld(qrows, qdt, n * d + e);
+    const int kvh = row_h[n] / (s->Hq / s->Hkv);
+    const int64_t base = ((int64_t)row_b[n] * s->Hkv + kvh) * s->N;
+    attend_range(s, q, k, v, kvdt, base, 0, row_pos[n] + 1, o + n * d);
+    free(q);
+  }
+}

@@ -65,6 +65,12 @@ void hr_attend(const hr_shape* s, int mode, int64_t nrows, const int32_t* row_b,
                const void* D, const void* U, int wdt, const int32_t* sel_in, double* o,
                int32_t* sel_idx, double* sel_score, double* gap, double* lse_own, int32_t* nsel);
 
+/* Dense causal attention of nrows queries (as in hr_attend) over keys
+ * 0..row_pos[n] of their KV head: o [nrows,d]. */
+void hr_dense(const hr_shape* s, int64_t nrows, const int32_t* row_b, const int32_t* row_h,
+              const int32_t* row_pos, const void* qrows, int qdt, const void* k, const void* v, int kvdt,
+              double* o);
+
 #ifdef __cplusplus
 }
 #endif

@@ -13,6 +13,8 @@ operand, a wrong tie rule) fails at least one of them:
   * reductions of the whole pipeline to dense causal attention, checked against
     torch's scaled_dot_product_attention in float64 on the CPU;
   * Q-Cal special cases (D = 0, U D = I);
+  * the dense causal baseline against torch SDPA (grouped heads), its identical-key
+    closed form, and its equality with the HiLS pass under exact chunk scores;
   * a second, vectorised formulation of the full forward pass on tiny inputs.
 """
 import json
@@ -494,3 +496,48 @@ def test_workload_structure():
     assert len(nd) == 41 and np.all(np.diff(nd) > 0)
     pp = synth.planted_positions(4096, 0.25, 1234, 0)
     assert len(pp) == 1024 and len(np.unique(pp)) == 1024
+
+
+def _dense_case(seed, B, Hq, Hkv, d, N):
+    rng = _rng(seed)
+    q = rng.standard_normal((B, Hq, N, d))
+    k = rng.standard_normal((B, Hkv, N, d)) * 1.2
+    v = rng.standard_normal((B, Hkv, N, d))
+    rows = [(b, h, i) for b in range(B) for h in range(Hq) for i in range(0, N, 7)]
+    return q, k, v, np.asarray(rows)
+
+
+def test_dense_baseline_matches_sdpa_grouped_heads():
+    """oracle.dense = causal softmax attention, each query head reading KV head h // (Hq/Hkv)."""
+    B, Hq, Hkv, d, N = 2, 4, 2, 32, 90
+    q, k, v, rows = _dense_case(21, B, Hq, Hkv, d, N)
+    s = oracle.shape(B, Hq, Hkv, d, N=N)
+    o = oracle.dense(s, rows[:, 0], rows[:, 1], rows[:, 2], q[rows[:, 0], rows[:, 1], rows[:, 2]], k, v)
+    for t, (b, h, i) in enumerate(rows):
+        kvh = h // (Hq // Hkv)
+        ref = _dense_causal(q[b, h, i][None], k[b, kvh], v[b, kvh], [i], 1 / math.sqrt(d))[0]
+        np.testing.assert_allclose(o[t], ref, rtol=0, atol=1e-12)
+
+
+def test_dense_baseline_identical_keys_is_prefix_mean():
+    """Identical keys give uniform weights: the output is the mean of v[0..i]."""
+    rng = _rng(22)
+    d, N = 16, 50
+    s = oracle.shape(1, 1, 1, d, N=N)
+    k = np.repeat(rng.standard_normal((1, d)), N, axis=0).reshape(1, 1, N, d)
+    v = rng.standard_normal((1, 1, N, d))
+    q = rng.standard_normal((1, 1, N, d))
+    pos = np.arange(N)
+    o = oracle.dense(s, np.zeros(N), np.zeros(N), pos, q[0, 0], k, v)
+    ref = np.cumsum(v[0, 0], axis=0) / (pos[:, None] + 1)
+    np.testing.assert_allclose(o, ref, rtol=0, atol=1e-12)
+
+
+def test_dense_baseline_equals_hils_with_exact_scores():
+    """With exact chunk LSEs and every past chunk selected, the hierarchical softmax is the dense one."""
+    B, Hq, Hkv, d, N = 1, 4, 2, 32, 5 * 64 + 9
+    q, k, v, rows = _dense_case(23, B, Hq, Hkv, d, N)
+    s = oracle.shape(B, Hq, Hkv, d, N=N, S=64, K=5)
+    o = oracle.dense(s, rows[:, 0], rows[:, 1], rows[:, 2], q[rows[:, 0], rows[:, 1], rows[:, 2]], k, v)
+    r = oracle.prefill_rows(s, q, k, v, None, None, rows, mode=oracle.EXACT)
+    np.testing.assert_allclose(o, r["o"], rtol=0, atol=1e-12)
