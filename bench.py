@@ -12,11 +12,11 @@ Also reported on the same line:
     (32/8 heads, d=128, K=32), microseconds per step, with its roofline;
   * roofline of the dominant prefill kernel from HIP-event stage times;
   * cpu_baseline: the fp64 oracle on a bounded sample of the same workload;
-  * dense: torch SDPA causal attention on the same q/k/v (the pages compare
-    against full attention).
+  * dense: this library's dense causal attention kernel (same MFMA tiles) and
+    torch SDPA on the same q/k/v (the pages compare against full attention).
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-decode] [--no-cpu] [--no-dense]
-                       [--no-prefill] [--copy-calibration]
+                       [--no-prefill] [--copy-calibration] [--sweep] [--peaks]
 """
 from __future__ import annotations
 
@@ -129,9 +129,10 @@ KERNEL_SOURCES = {
 
 def source_hash(stage):
     import hashlib
-    src = os.path.join(ROOT, "long_context_chunk_amd", "csrc", KERNEL_SOURCES[stage])
+    import glob
+    csrc = os.path.join(ROOT, "long_context_chunk_amd", "csrc")
     h = hashlib.sha256()
-    for f in (src, os.path.join(ROOT, "long_context_chunk_amd", "csrc", "hils_common.h")):
+    for f in [os.path.join(csrc, KERNEL_SOURCES[stage])] + sorted(glob.glob(os.path.join(csrc, "*.h"))):
         h.update(open(f, "rb").read())
     return h.hexdigest()[:16]
 
@@ -275,28 +276,91 @@ def cpu_baseline(w, res, target_s=15.0):
                       "uniformly (%.1fs), scaled to the full layer" % (w.C, w.Hlmk, t_comp, done, total_rows, t_rows)}
 
 
-def dense_baseline(res, w, reps=2):
-    """torch SDPA causal attention (flash / memory-efficient kernels only) on the same q/k/v."""
+def _time_ms(fn, reps):
+    import torch
+    fn()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        fn()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / reps
+
+
+def dense_flops(w):
+    """Useful flops of dense causal attention: 4 d per (query, key <= query) pair."""
+    return 4.0 * w.d * w.B * w.Hq * (w.N * (w.N + 1) / 2)
+
+
+def dense_baseline(res, w, reps=2, sdpa=True):
+    """Dense causal attention on the same q/k/v: this library's MFMA kernel
+    (hils_dense_attention) and torch SDPA (flash / memory-efficient kernels only)."""
     import torch
     from torch.nn.attention import SDPBackend, sdpa_kernel
+    from long_context_chunk_amd import hils
     q, k, v = res["tensors"][:3]
-    G = w.Hq // w.Hkv
-    k2 = k.repeat_interleave(G, dim=1).contiguous()
-    v2 = v.repeat_interleave(G, dim=1).contiguous()
-    f = torch.nn.functional.scaled_dot_product_attention
-    with torch.no_grad(), sdpa_kernel([SDPBackend.FLASH_ATTENTION, SDPBackend.EFFICIENT_ATTENTION]):
-        f(q, k2, v2, is_causal=True)
-        torch.cuda.synchronize()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record()
-        for _ in range(reps):
-            f(q, k2, v2, is_causal=True)
-        e1.record()
-        torch.cuda.synchronize()
-    ms = e0.elapsed_time(e1) / reps
-    del k2, v2
-    return {"impl": "torch SDPA causal, flash/mem-efficient backend, KV heads repeated to Hq", "ms": ms,
-            "tokens_per_s": w.B * w.N / (ms * 1e-3)}
+    out = {}
+    o = torch.empty_like(q)
+    dm = hils.dims(w.B, w.Hq, w.Hkv, w.d, w.N, w.K, qcal_rank=0, io=w.io)
+    ms = _time_ms(lambda: hils.dense_attention(dm, q, k, v, o), reps)
+    fl = dense_flops(w)
+    out["own"] = {"impl": "hils_dense_attention (same MFMA tiles as the sparse pass)", "ms": ms,
+                  "tokens_per_s": w.B * w.N / (ms * 1e-3), "tflops": fl / (ms * 1e-3) / 1e12,
+                  "mfma_frac": fl / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS}
+    del o
+    if sdpa:
+        G = w.Hq // w.Hkv
+        k2 = k.repeat_interleave(G, dim=1).contiguous()
+        v2 = v.repeat_interleave(G, dim=1).contiguous()
+        f = torch.nn.functional.scaled_dot_product_attention
+        with torch.no_grad(), sdpa_kernel([SDPBackend.FLASH_ATTENTION, SDPBackend.EFFICIENT_ATTENTION]):
+            ms2 = _time_ms(lambda: f(q, k2, v2, is_causal=True), reps)
+        del k2, v2
+        out["torch_sdpa"] = {"impl": "torch SDPA causal, flash/mem-efficient backend, KV heads repeated to Hq",
+                             "ms": ms2, "tokens_per_s": w.B * w.N / (ms2 * 1e-3),
+                             "tflops": fl / (ms2 * 1e-3) / 1e12}
+    return out
+
+
+def run_sweep(args):
+    """HiLS prefill against the dense baseline over N, head layout 16/4, d = 64, K = 16:
+    where the sparse pass overtakes dense attention (one JSON line per N)."""
+    import torch
+    import synth
+    base = synth.Workload("sweep", B=1, Hq=16, Hkv=4, d=64, N=8192, K=16)
+    for n in (8192, 16384, 32768, 65536, 131072, 262144, 524288):
+        w = synth.scaled(base, N=n)
+        w.name = "sweep_%dk" % (n // 1024)
+        res = run_prefill(w, max(2, args.steps // 2), 1, synth.BASE_SEED + 5)
+        dn = dense_baseline(res, w, reps=2, sdpa=n <= 131072)
+        row = {"sweep": w.name, "N": n, "Hq": w.Hq, "Hkv": w.Hkv, "d": w.d, "K": w.K,
+               "hils_ms": res["ms"], "dense_own_ms": dn["own"]["ms"], "speedup_vs_own_dense": dn["own"]["ms"] / res["ms"],
+               "dense_own_tflops": dn["own"]["tflops"], "hils_stages_ms": res["stages"]}
+        if "torch_sdpa" in dn:
+            row["torch_sdpa_ms"] = dn["torch_sdpa"]["ms"]
+        print(json.dumps(row), flush=True)
+        res.clear()
+        torch.cuda.empty_cache()
+
+
+def run_peaks():
+    """Measured ceilings on this GPU: a plain device copy and a large bf16 GEMM (hipBLASLt)."""
+    import torch
+    nbytes = 2 << 30
+    src = torch.ones(nbytes // 4, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    ms = _time_ms(lambda: dst.copy_(src), 5)
+    copy_gbs = 2 * nbytes / (ms * 1e-3) / 1e9
+    del src, dst
+    n = 8192
+    a = torch.randn(n, n, device="cuda", dtype=torch.bfloat16)
+    b = torch.randn(n, n, device="cuda", dtype=torch.bfloat16)
+    ms2 = _time_ms(lambda: torch.matmul(a, b), 20)
+    print(json.dumps({"peaks": {"copy_GBs_read_plus_write": copy_gbs, "copy_bytes": nbytes,
+                                "bf16_gemm_tflops": 2.0 * n ** 3 / (ms2 * 1e-3) / 1e12, "gemm": "%d^3 torch.matmul" % n,
+                                "spec_hbm_GBs": PEAK_HBM_GBS, "spec_bf16_tflops": PEAK_BF16_TFLOPS}}), flush=True)
 
 
 def run_decode(wd, steps, warmup, seed):
@@ -380,6 +444,9 @@ def main():
     ap.add_argument("--no-dense", action="store_true")
     ap.add_argument("--no-parity", action="store_true")
     ap.add_argument("--no-prefill", action="store_true", help="decode step only (for profiling it alone)")
+    ap.add_argument("--sweep", action="store_true",
+                    help="HiLS prefill against the dense baseline over N = 8K..512K (16/4 heads, d = 64, K = 16)")
+    ap.add_argument("--peaks", action="store_true", help="only measure a device copy and a large bf16 GEMM")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 2 GiB device copy (counter calibration for the traffic figures)")
     args = ap.parse_args()
@@ -392,6 +459,13 @@ def main():
     from long_context_chunk_amd import hils
     if args.copy_calibration:
         copy_calibration()
+        return
+    if args.peaks:
+        run_peaks()
+        return
+    hils.load()
+    if args.sweep:
+        run_sweep(args)
         return
     hils.load()
     assert torch.cuda.is_available()
@@ -428,9 +502,11 @@ def main():
     if not args.no_dense:
         try:
             dn = dense_baseline(res, w)
-            dn["hils_speedup"] = dn["ms"] / res["ms"]
+            dn["hils_speedup_vs_own_dense"] = dn["own"]["ms"] / res["ms"]
+            if "torch_sdpa" in dn:
+                dn["hils_speedup_vs_torch_sdpa"] = dn["torch_sdpa"]["ms"] / res["ms"]
             line["dense"] = dn
-            log("dense SDPA: %.1f ms" % dn["ms"])
+            log("dense: own %.1f ms, SDPA %.1f ms" % (dn["own"]["ms"], dn.get("torch_sdpa", {}).get("ms", -1)))
         except Exception as ex:  # report, never hide
             line["dense"] = {"error": repr(ex)}
     if not args.no_cpu:

@@ -165,6 +165,18 @@ int hils_attn_decode_timed(const hils_dims_t* dims, const void* q, const void* k
                            const void* qcal_U, int32_t* sel_idx_out, void* o, void* ws, size_t ws_bytes,
                            void* stream, float* stage_ms);
 
+/*
+ * Dense causal attention, the baseline the pages measure the sparse method
+ * against (hotpaper.ai abstract; ai-papers.net "Results"): for every (b, h) and
+ * row i, o[b,h,i] = sum_{j <= i} softmax_j(q[b,h,i].k[b,kvh,j] / sqrt(d)) v[b,kvh,j]
+ * with kvh = h / (Hq/Hkv).  It uses the same MFMA tiles as the sparse pass.
+ * q, o [B,Hq,N,d]; k, v [B,Hkv,N,d] (device, io dtype, contiguous).  dims is
+ * validated as for the other calls (S, K, Hlmk and qcal_rank are not used).
+ * No workspace; asynchronous on `stream`.
+ */
+int hils_dense_attention(const hils_dims_t* dims, const void* q, const void* k, const void* v, void* o,
+                         void* stream);
+
 /* Message of the last non-OK return on this thread ("" if none). */
 const char* hils_last_error(void);
 

@@ -274,4 +274,18 @@ int hils_attn_decode_timed(const hils_dims_t* dims, const void* q, const void* k
                     stage_ms);
 }
 
+int hils_dense_attention(const hils_dims_t* dims, const void* q, const void* k, const void* v, void* o,
+                         void* stream) {
+  hils::Geom g;
+  int rc = check_dims(dims, g);
+  if (rc) return rc;
+  if (!q || !k || !v || !o) return fail(HILS_E_INVAL, "q, k, v and o must be non-NULL");
+  if ((int64_t)g.B * g.Hq * ((g.N + 127) / 128) > 0x7fffffff)
+    return fail(HILS_E_UNSUPPORTED, "B*Hq*ceil(N/128) must fit a 31-bit grid");
+  const hipError_t e = hils::launch_dense(g, q, k, v, o, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "hils_dense_attention");
+  g_err[0] = 0;
+  return HILS_OK;
+}
+
 }  // extern "C"

@@ -1,0 +1,183 @@
+// K/V chunk tiles in LDS and the per-wave MFMA attention of 32 query rows against one
+// 64-key tile, shared by the chunk attention kernels and the dense baseline.
+#pragma once
+#include "hils_common.h"
+
+namespace hils {
+
+// ------------------------------------------------------ K/V chunk tile in LDS
+// Both planes in natural [key][d] order, staged with 16-byte loads and stores.
+// K (row stride D + 8) feeds the A operand of S^T = K Q^T, whose k-steps take 8
+// consecutive head dimensions per lane half: one 16-byte LDS read per operand.
+// V (row stride D + 32) feeds the A operand of O^T = V^T P^T (dims as rows, keys as k)
+// through ds_read_b64_tr_b16 transposing reads: within a 16-lane group, lane j points at
+// the 4 dims 4(j&3).. of key (j>>2) and lane i receives 4 consecutive keys of dim i.
+// Keys at or beyond `nvalid` are stored as zeros.  NT bf16 terms per value.
+template <typename IO, int D, int NT>
+struct alignas(16) KVTile {
+  static constexpr int LDK = D + 8;
+  static constexpr int LDV = D + 32;
+  uint16_t k[NT][64 * LDK];
+  uint16_t v[NT][64 * LDV];
+};
+
+template <typename IO, int D, int NT>
+HILS_DEV void stage_kv(KVTile<IO, D, NT>& tile, const IO* __restrict__ k, const IO* __restrict__ v, int64_t row0,
+                       int nvalid, int tid, int nthreads) {
+  constexpr int LDK = KVTile<IO, D, NT>::LDK, LDV = KVTile<IO, D, NT>::LDV;
+  for (int i = tid * 8; i < 64 * D; i += nthreads * 8) {
+    const int key = i / D, e = i % D;
+    float kx[8], vx[8];
+    if (key < nvalid) {
+      const int64_t off = (row0 + key) * D + e;
+      io_traits<IO>::load4(k, off, *reinterpret_cast<float(*)[4]>(kx));
+      io_traits<IO>::load4(k, off + 4, *reinterpret_cast<float(*)[4]>(kx + 4));
+      io_traits<IO>::load4(v, off, *reinterpret_cast<float(*)[4]>(vx));
+      io_traits<IO>::load4(v, off + 4, *reinterpret_cast<float(*)[4]>(vx + 4));
+    } else {
+#pragma unroll
+      for (int u = 0; u < 8; ++u) kx[u] = vx[u] = 0.f;
+    }
+    u32x4_t ks[NT], vs[NT];
+    split8<NT>(kx, ks);
+    split8<NT>(vx, vs);
+#pragma unroll
+    for (int j = 0; j < NT; ++j) {
+      *reinterpret_cast<u32x4_t*>(&tile.k[j][key * LDK + e]) = ks[j];
+      *reinterpret_cast<u32x4_t*>(&tile.v[j][key * LDV + e]) = vs[j];
+    }
+  }
+}
+
+typedef __attribute__((ext_vector_type(4))) short s16x4_t;
+typedef __attribute__((address_space(3))) s16x4_t lds_s16x4_t;
+
+// A operand of O^T = V^T P^T for dim tile dt, key k-step ks2: lane l (dim 32 dt + (l & 31),
+// half h = l >> 5) gets keys kperm(ks2, h, 0..7) of its dim, in two transposing reads
+template <int LDV>
+HILS_DEV bf16x8_t vt_operand(const uint16_t* vplane, int dt, int ks2, int lane) {
+  const int g = lane >> 4, j = lane & 15;
+  const int e = 32 * dt + 16 * (g & 1) + 4 * (j & 3);
+  const int key = 16 * ks2 + 4 * (g >> 1) + (j >> 2);
+  const s16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(vplane + key * LDV + e));
+  const s16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(vplane + (key + 8) * LDV + e));
+  u32x4_t u;
+  u.x = (uint32_t)(uint16_t)lo[0] | ((uint32_t)(uint16_t)lo[1] << 16);
+  u.y = (uint32_t)(uint16_t)lo[2] | ((uint32_t)(uint16_t)lo[3] << 16);
+  u.z = (uint32_t)(uint16_t)hi[0] | ((uint32_t)(uint16_t)hi[1] << 16);
+  u.w = (uint32_t)(uint16_t)hi[2] | ((uint32_t)(uint16_t)hi[3] << 16);
+  return __builtin_bit_cast(bf16x8_t, u);
+}
+
+HILS_DEV bf16x8_t lds_op16(const uint16_t* p) { return *reinterpret_cast<const bf16x8_t*>(p); }
+
+// One wave: 32 query rows (B operands qb, NT terms) against the staged chunk.
+// Returns, per lane (row n = lane & 31, half hf), the O^T accumulators (unnormalised:
+// P keeps its largest weight exactly 1 in bf16) and the row's softmax max m (of the
+// scaled logits) and sum l.  MASK: key j is used iff j < key_lim
+// (per row); otherwise all 64 keys are.  p = 2^((s - max s) tau log2 e) is one fma and
+// one exp per logit; masked logits are -inf and give p = 0.
+template <typename IO, int D, int NT, bool MASK>
+HILS_DEV void wave_chunk_attention(const KVTile<IO, D, NT>& tile, const bf16x8_t (&qb)[NT][D / 16], int key_lim,
+                                   f32x16_t (&o)[D / 32], float& m_out, float& l_out) {
+  constexpr int NKS = D / 16;
+  constexpr int LDK = KVTile<IO, D, NT>::LDK, LDV = KVTile<IO, D, NT>::LDV;
+  const int lane = threadIdx.x & 63, hf = lane >> 5;
+  const float tau = 1.0f / sqrtf((float)D);
+  const float c = tau * 1.44269504088896340736f;  // tau log2(e)
+  f32x16_t s[2];
+#pragma unroll
+  for (int tt = 0; tt < 2; ++tt) {
+    s[tt] = zero16();
+    const int key = 32 * tt + (lane & 31);
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks)
+#pragma unroll
+      for (int j = 0; j < NT; ++j) {
+        const bf16x8_t a = lds_op16(&tile.k[j][key * LDK + 16 * ks + 8 * hf]);
+#pragma unroll
+        for (int i = 0; i < NT; ++i)
+          if (i + j < NT) s[tt] = mfma32(a, qb[i][ks], s[tt]);
+      }
+  }
+  if constexpr (MASK) {
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+      for (int rr = 0; rr < 16; ++rr)
+        if (32 * tt + acc_row(rr, hf) >= key_lim) s[tt][rr] = -INFINITY;
+  }
+  float m = fmaxf(s[0][0], s[0][1]);
+#pragma unroll
+  for (int rr = 2; rr < 32; ++rr) m = fmaxf(m, s[rr >> 4][rr & 15]);
+  m = fmaxf(m, __shfl_xor(m, 32));
+  const float mc = m * c;
+  float l = 0.f;
+#pragma unroll
+  for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+    for (int rr = 0; rr < 16; ++rr) {
+      const float p = __builtin_amdgcn_exp2f(fmaf(s[tt][rr], c, -mc));
+      s[tt][rr] = p;
+      l += p;
+    }
+  l += __shfl_xor(l, 32);
+  // P^T as B operand: k-step ks2 (keys 16*ks2 ..), element mm = register 8*(ks2&1)+mm of tile ks2>>1
+  bf16x8_t pb[NT][4];
+#pragma unroll
+  for (int ks2 = 0; ks2 < 4; ++ks2) {
+    float pv[8];
+#pragma unroll
+    for (int mm = 0; mm < 8; ++mm) pv[mm] = s[ks2 >> 1][8 * (ks2 & 1) + mm];
+    u32x4_t t[NT];
+    split8<NT>(pv, t);
+#pragma unroll
+    for (int j = 0; j < NT; ++j) pb[j][ks2] = __builtin_bit_cast(bf16x8_t, t[j]);
+  }
+#pragma unroll
+  for (int dt = 0; dt < D / 32; ++dt) {
+    o[dt] = zero16();
+#pragma unroll
+    for (int ks2 = 0; ks2 < 4; ++ks2)
+#pragma unroll
+      for (int j = 0; j < NT; ++j) {
+        const bf16x8_t a = vt_operand<LDV>(tile.v[j], dt, ks2, lane);
+#pragma unroll
+        for (int i = 0; i < NT; ++i)
+          if (i + j < NT) o[dt] = mfma32(a, pb[i][ks2], o[dt]);
+      }
+  }
+  m_out = m * tau;
+  l_out = l;
+}
+
+// Loads query row `qrow_off` (element offset of the row) from global memory as NT-term B operands.
+template <typename IO, int D, int NT>
+HILS_DEV void load_q_operand(const IO* __restrict__ q, int64_t qrow_off, bool ok, bf16x8_t (&qb)[NT][D / 16]) {
+  const int hf = (threadIdx.x & 63) >> 5;
+#pragma unroll
+  for (int ks = 0; ks < D / 16; ++ks) {
+    float x[8];
+    if (ok) {
+      io_traits<IO>::load4(q, qrow_off + 16 * ks + 8 * hf, *reinterpret_cast<float(*)[4]>(x));
+      io_traits<IO>::load4(q, qrow_off + 16 * ks + 8 * hf + 4, *reinterpret_cast<float(*)[4]>(x + 4));
+    } else {
+#pragma unroll
+      for (int m = 0; m < 8; ++m) x[m] = 0.f;
+    }
+    u32x4_t t[NT];
+    split8<NT>(x, t);
+#pragma unroll
+    for (int j = 0; j < NT; ++j) qb[j][ks] = __builtin_bit_cast(bf16x8_t, t[j]);
+  }
+}
+
+// bf16 query row already staged in LDS (row stride LDQ elements) as the B operand.
+template <int D>
+HILS_DEV void lds_q_operand(const uint16_t* rowp, bf16x8_t (&qb)[1][D / 16]) {
+  const int hf = (threadIdx.x & 63) >> 5;
+#pragma unroll
+  for (int ks = 0; ks < D / 16; ++ks) qb[0][ks] = lds_op16(rowp + 16 * ks + 8 * hf);
+}
+
+}  // namespace hils

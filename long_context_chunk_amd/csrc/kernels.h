@@ -38,4 +38,7 @@ hipError_t launch_decode(const Geom& g, const void* q, const void* kcache, const
                          const float* kc, const float* bc, const void* D, const void* U, int32_t* sel_idx_out,
                          void* o, void* ws, size_t ws_bytes, hipStream_t st, hipEvent_t* ev = nullptr);
 
+// Dense causal attention (the baseline).
+hipError_t launch_dense(const Geom& g, const void* q, const void* k, const void* v, void* o, hipStream_t st);
+
 }  // namespace hils

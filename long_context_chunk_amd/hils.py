@@ -20,7 +20,8 @@ OP_COMPRESS, OP_SCORE_TOPK, OP_PREFILL, OP_DECODE = 0, 1, 2, 3
 OK, E_INVAL, E_UNSUPPORTED, E_WORKSPACE, E_HIP = 0, -1, -2, -3, -4
 
 SYMBOLS = ("hils_workspace_bytes", "hils_landmark_compress", "hils_chunk_score_topk", "hils_attn_prefill",
-           "hils_attn_prefill_timed", "hils_attn_decode", "hils_attn_decode_timed", "hils_last_error")
+           "hils_attn_prefill_timed", "hils_attn_decode", "hils_attn_decode_timed", "hils_dense_attention",
+           "hils_last_error")
 STAGES = ("compress", "score_threshold", "score_select", "bucket", "chunk_attend", "own_attend", "fuse")
 DECODE_STAGES = ("scan", "merge", "attend_fuse")
 
@@ -60,8 +61,9 @@ def load():
         lib.hils_attn_decode.argtypes = [dp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
         lib.hils_attn_decode_timed.argtypes = [dp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp,
                                                ctypes.POINTER(ctypes.c_float)]
+        lib.hils_dense_attention.argtypes = [dp, vp, vp, vp, vp, vp]
         for f in ("hils_landmark_compress", "hils_chunk_score_topk", "hils_attn_prefill", "hils_attn_prefill_timed",
-                  "hils_attn_decode", "hils_attn_decode_timed"):
+                  "hils_attn_decode", "hils_attn_decode_timed", "hils_dense_attention"):
             getattr(lib, f).restype = ctypes.c_int
         lib.hils_last_error.argtypes = []
         lib.hils_last_error.restype = ctypes.c_char_p
@@ -203,3 +205,13 @@ def attn_decode(dm: Dims, q, k_cache, v_cache, seq_lens, kc, bc, o, ws, qcal_D=N
         _check(load().hils_attn_decode_timed(*args, ms))
         return dict(zip(DECODE_STAGES, [float(x) for x in ms]))
     _check(load().hils_attn_decode(*args))
+
+
+def dense_attention(dm: Dims, q, k, v, o):
+    """hils_dense_attention: the dense causal baseline on the same tensors."""
+    dt = torch.float32 if dm.io == F32 else torch.bfloat16
+    _req(q, "q", (dm.B, dm.Hq, dm.N, dm.d), dt)
+    _req(k, "k", (dm.B, dm.Hkv, dm.N, dm.d), dt)
+    _req(v, "v", (dm.B, dm.Hkv, dm.N, dm.d), dt)
+    _req(o, "o", (dm.B, dm.Hq, dm.N, dm.d), dt)
+    _check(load().hils_dense_attention(ctypes.byref(dm), _p(q), _p(k), _p(v), _p(o), _stream()))

@@ -116,3 +116,15 @@ def test_product_path_does_not_import_oracle():
             if f.endswith((".py", ".hip", ".h", ".cpp")):
                 txt = open(os.path.join(dirpath, f)).read()
                 assert "import oracle" not in txt and "hils_oracle" not in txt and "from oracle" not in txt, f
+
+
+def test_dense_attention_validation():
+    lib = hils.load()
+    d = hils.dims(1, 4, 2, 64, 100, 4)
+    fake = ctypes.c_void_p(0x1000)
+    assert lib.hils_dense_attention(None, fake, fake, fake, fake, None) == hils.E_INVAL
+    assert lib.hils_dense_attention(ctypes.byref(d), fake, None, fake, fake, None) == hils.E_INVAL
+    bad = hils.dims(1, 4, 3, 64, 100, 4)   # Hq not a multiple of Hkv
+    assert lib.hils_dense_attention(ctypes.byref(bad), fake, fake, fake, fake, None) == hils.E_INVAL
+    bad = hils.dims(1, 4, 2, 96, 100, 4)   # unsupported head dim
+    assert lib.hils_dense_attention(ctypes.byref(bad), fake, fake, fake, fake, None) == hils.E_UNSUPPORTED

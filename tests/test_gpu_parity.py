@@ -233,3 +233,30 @@ def test_decode_matches_prefill_row():
     for h in range(4):
         assert set(dec["sel_idx"][0, h]) == set(pre["sel_idx"][0, h, L - 1])
     np.testing.assert_allclose(dec["o"][0], pre["o"][0, :, L - 1], rtol=0, atol=1e-2)
+
+
+# ---------------------------------------------------------------- dense baseline
+DENSE = [
+    ("bf16_d128_gqa_ragged", synth.Workload("dense_a", B=1, Hq=4, Hkv=2, d=128, N=700, K=4)),
+    ("bf16_d64_B2_mqa", synth.Workload("dense_b", B=2, Hq=2, Hkv=1, d=64, N=333, K=4)),
+    ("f32_d64", synth.Workload("dense_c", B=1, Hq=2, Hkv=2, d=64, N=200, K=4, io=synth.F32)),
+    ("f32_d128_one_row", synth.Workload("dense_d", B=1, Hq=1, Hkv=1, d=128, N=1, K=4, io=synth.F32)),
+]
+
+
+@pytest.mark.parametrize("name,w", DENSE, ids=[n for n, _ in DENSE])
+def test_dense_baseline(name, w):
+    """hils_dense_attention against the oracle's dense causal attention, every row."""
+    _say("dense", name)
+    x = synth.make_inputs(w, SEED + 7)
+    q, k, v = (upload(x[n], w.io) for n in ("q", "k", "v"))
+    o = torch.full_like(q, float("nan"))
+    hils.dense_attention(dims_of(w), q, k, v, o)
+    torch.cuda.synchronize()
+    rows = np.asarray([(b, h, i) for b in range(w.B) for h in range(w.Hq) for i in range(w.N)])
+    ref = oracle.dense(shape_of(w), rows[:, 0], rows[:, 1], rows[:, 2], x["q"][rows[:, 0], rows[:, 1], rows[:, 2]],
+                       x["k"], x["v"])
+    got = o.float().cpu().numpy()[rows[:, 0], rows[:, 1], rows[:, 2]]
+    err = np.abs(got - ref)
+    mx, mean = TOL[w.io]
+    assert err.max() <= mx and err.mean() <= mean, (err.max(), err.mean())
