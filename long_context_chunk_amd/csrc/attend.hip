@@ -526,38 +526,48 @@ __global__ void __launch_bounds__(256) fuse(const float* __restrict__ sel_score,
   const int slot = lane / LPS, dpos = (lane % LPS) * EPL;
   const int64_t row0 = ((int64_t)blockIdx.x * 4 + w) * FZ_ROWS;
   const PT* part = reinterpret_cast<const PT*>(partial_v);
-  for (int u = 0; u < FZ_ROWS; u += 2) {
+  // bf16 outputs of the wave's rows, written at the end as one contiguous burst: small
+  // writes scattered through the read stream cost far more than their bytes
+  __shared__ __align__(16) IO ostage[4][sizeof(IO) == 2 ? FZ_ROWS * D : 8];
+  // two rows per buffer, two buffers: the loads of the next two rows are in flight while
+  // the current two are reduced
+  struct Rows {
     u32x4_t raw[2][NSEG];
     float sc[2];
     int nsel[2];
     bool live[2];
+  };
+  auto issue = [&](int u, Rows& R) {
 #pragma unroll
-    for (int v2 = 0; v2 < 2; ++v2) {  // issue every load of both rows first
+    for (int v2 = 0; v2 < 2; ++v2) {
       const int64_t row = row0 + u + v2;
-      live[v2] = row < rows;
-      const int i = live[v2] ? (int)(row % N) : 0;
+      R.live[v2] = u < FZ_ROWS && row < rows;
+      const int i = R.live[v2] ? (int)(row % N) : 0;
       const int ns = min(K, min(C, i / 64));
-      nsel[v2] = ns;
-      sc[v2] = -INFINITY;
-      if (live[v2]) {
-        if (lane < ns) sc[v2] = sel_score[row * K + lane];
-        else if (lane == ns) sc[v2] = lse[row];
+      R.nsel[v2] = ns;
+      R.sc[v2] = -INFINITY;
+      if (R.live[v2]) {
+        if (lane < ns) R.sc[v2] = sel_score[row * K + lane];
+        else if (lane == ns) R.sc[v2] = lse[row];
       }
 #pragma unroll
       for (int sg = 0; sg < NSEG; ++sg) {
         const int t = sg * SPL + slot;           // logical slot: 0..ns-1 selected, ns = own
         const int phys = t < ns ? t : K;
-        raw[v2][sg] = (live[v2] && t <= ns)
-                          ? __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(part + (row * (K + 1) + phys) * D + dpos))
-                          : u32x4_t{0u, 0u, 0u, 0u};
+        R.raw[v2][sg] = (R.live[v2] && t <= ns)
+                            ? __builtin_nontemporal_load(
+                                  reinterpret_cast<const u32x4_t*>(part + (row * (K + 1) + phys) * D + dpos))
+                            : u32x4_t{0u, 0u, 0u, 0u};
       }
     }
+  };
+  auto finish = [&](int u, const Rows& R) {
 #pragma unroll
     for (int v2 = 0; v2 < 2; ++v2) {
-      if (!live[v2]) continue;
+      if (!R.live[v2]) continue;
       const int64_t row = row0 + u + v2;
-      const float M = wave_max(sc[v2]);
-      const float wt = sc[v2] == -INFINITY ? 0.f : __expf(sc[v2] - M);
+      const float M = wave_max(R.sc[v2]);
+      const float wt = R.sc[v2] == -INFINITY ? 0.f : __expf(R.sc[v2] - M);
       const float inv = 1.0f / wave_sum(wt);
       float acc[EPL];
 #pragma unroll
@@ -565,8 +575,8 @@ __global__ void __launch_bounds__(256) fuse(const float* __restrict__ sel_score,
 #pragma unroll
       for (int sg = 0; sg < NSEG; ++sg) {
         const int t = sg * SPL + slot;
-        const float wtt = __shfl(wt, t < 64 ? t : 0) * (t <= nsel[v2] ? 1.f : 0.f);
-        const u32x4_t rw = raw[v2][sg];
+        const float wtt = __shfl(wt, t < 64 ? t : 0) * (t <= R.nsel[v2] ? 1.f : 0.f);
+        const u32x4_t rw = R.raw[v2][sg];
         if constexpr (sizeof(PT) == 2) {
           const uint32_t wd[4] = {rw.x, rw.y, rw.z, rw.w};
 #pragma unroll
@@ -593,12 +603,31 @@ __global__ void __launch_bounds__(256) fuse(const float* __restrict__ sel_score,
           pk.y = pack_bf16x2(acc[2] * inv, acc[3] * inv);
           pk.z = pack_bf16x2(acc[4] * inv, acc[5] * inv);
           pk.w = pack_bf16x2(acc[6] * inv, acc[7] * inv);
-          *reinterpret_cast<u32x4_t*>(o + row * D + dpos) = pk;
+          *reinterpret_cast<u32x4_t*>(&ostage[w][(u + v2) * D + dpos]) = pk;
         } else {
           *reinterpret_cast<float4*>(reinterpret_cast<float*>(o) + row * D + dpos) =
               make_float4(acc[0] * inv, acc[1] * inv, acc[2] * inv, acc[3] * inv);
         }
       }
+    }
+  };
+  static_assert(FZ_ROWS % 4 == 0, "");
+  Rows ra, rb;
+  issue(0, ra);
+  for (int u = 0; u < FZ_ROWS; u += 4) {
+    issue(u + 2, rb);
+    finish(u, ra);
+    issue(u + 4, ra);  // past the wave's rows: nothing is loaded
+    finish(u + 2, rb);
+  }
+  if constexpr (sizeof(IO) == 2) {
+    __builtin_amdgcn_wave_barrier();
+    const int nr = (int)min((int64_t)FZ_ROWS, rows - row0);  // rows of this wave that exist
+    constexpr int SEG16 = FZ_ROWS * D * (int)sizeof(IO) / 16;
+    for (int x = lane; x < SEG16; x += 64) {
+      if (x * 16 < nr * D * (int)sizeof(IO))
+        __builtin_nontemporal_store(reinterpret_cast<const u32x4_t*>(&ostage[w][0])[x],
+                                    reinterpret_cast<u32x4_t*>(o + row0 * D) + x);
     }
   }
 }
