@@ -166,6 +166,31 @@ int hils_attn_decode_timed(const hils_dims_t* dims, const void* q, const void* k
                            void* stream, float* stage_ms);
 
 /*
+ * Chunk-paged KV cache (the pages' chunks are the natural page: ai-papers.net
+ * "How HiLS Attention works"; aitrends.kr "Technical details" on decode cost).
+ * A page holds one S-token chunk of every KV head: k_pages / v_pages
+ * [num_pages, Hkv, S, d] (io dtype, device).  block_table [B, max_blocks] int32
+ * (device) gives the page of chunk c of sequence b; only chunks a call reads
+ * need valid entries.  dims.N must equal max_blocks * S (the capacity); page ids
+ * outside [0, num_pages) are clamped into the pool (wrong values, never an
+ * access outside it).  The landmark cache kc/bc stays contiguous
+ * [B, Hlmk, max_blocks, d] / [B, Hlmk, max_blocks].
+ *
+ * hils_landmark_compress_paged: hils_landmark_compress for chunks
+ * [c_begin, c_end) of every sequence, reading keys from the pages; call it for
+ * the chunk that a decode step completes (incremental compression).
+ * hils_attn_decode_paged: hils_attn_decode on the paged cache (same workspace,
+ * HILS_OP_DECODE).  Both are asynchronous on `stream`.
+ */
+int hils_landmark_compress_paged(const hils_dims_t* dims, const void* k_pages, const int32_t* block_table,
+                                 int32_t max_blocks, int32_t num_pages, const void* lmk_q, int32_t c_begin,
+                                 int32_t c_end, float* kc, float* bc, void* stream);
+int hils_attn_decode_paged(const hils_dims_t* dims, const void* q, const void* k_pages, const void* v_pages,
+                           const int32_t* block_table, int32_t max_blocks, int32_t num_pages, const int32_t* seq_lens,
+                           const float* kc, const float* bc, const void* qcal_D, const void* qcal_U,
+                           int32_t* sel_idx_out, void* o, void* ws, size_t ws_bytes, void* stream);
+
+/*
  * Dense causal attention, the baseline the pages measure the sparse method
  * against (hotpaper.ai abstract; ai-papers.net "Results"): for every (b, h) and
  * row i, o[b,h,i] = sum_{j <= i} softmax_j(q[b,h,i].k[b,kvh,j] / sqrt(d)) v[b,kvh,j]

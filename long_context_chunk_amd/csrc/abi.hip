@@ -50,6 +50,20 @@ int check_dims(const hils_dims_t* dims, hils::Geom& g) {
   return HILS_OK;
 }
 
+// Paged K/V: the capacity N must be max_blocks chunks; the table and pool sizes >= 1.
+int check_pages(const hils::Geom& g, const int32_t* table, int32_t max_blocks, int32_t num_pages,
+                hils::KvPages& pg) {
+  if (!table) return fail(HILS_E_INVAL, "block_table must be non-NULL");
+  if (max_blocks < 1 || num_pages < 1)
+    return fail(HILS_E_INVAL, "max_blocks and num_pages must be >= 1 (%d, %d)", max_blocks, num_pages);
+  if ((int64_t)max_blocks * g.S != g.N)
+    return fail(HILS_E_INVAL, "dims.N (%d) must equal max_blocks * S (%d * %d)", g.N, max_blocks, g.S);
+  pg.table = table;
+  pg.max_blocks = max_blocks;
+  pg.num_pages = num_pages;
+  return HILS_OK;
+}
+
 // Prefill-only limits: (row, slot) pair ids are 32-bit and the bucket histograms
 // hold at most 16384 chunks.
 int check_prefill(const hils::Geom& g) {
@@ -205,7 +219,8 @@ int run_prefill(const hils_dims_t* dims, const void* q, const void* k, const voi
 
 int run_decode(const hils_dims_t* dims, const void* q, const void* k_cache, const void* v_cache,
                const int32_t* seq_lens, const float* kc, const float* bc, const void* qcal_D, const void* qcal_U,
-               int32_t* sel_idx_out, void* o, void* ws, size_t ws_bytes, void* stream, float* stage_ms) {
+               int32_t* sel_idx_out, void* o, void* ws, size_t ws_bytes, void* stream, float* stage_ms,
+               hils::KvPages pg = hils::KvPages()) {
   hils::Geom g;
   int rc = check_dims(dims, g);
   if (rc) return rc;
@@ -225,7 +240,7 @@ int run_decode(const hils_dims_t* dims, const void* q, const void* k_cache, cons
     for (int i = 0; i <= NS && e == hipSuccess; ++i) e = hipEventCreate(&ev[i]);
   if (e == hipSuccess)
     e = hils::launch_decode(g, q, k_cache, v_cache, seq_lens, kc, bc, qcal_D, qcal_U, sel_idx_out, o, ws, ws_bytes,
-                            st, stage_ms ? ev : nullptr);
+                            st, stage_ms ? ev : nullptr, pg);
   if (stage_ms) {
     if (e == hipSuccess) e = hipEventSynchronize(ev[NS]);
     for (int i = 0; i < NS && e == hipSuccess; ++i) e = hipEventElapsedTime(&stage_ms[i], ev[i], ev[i + 1]);
@@ -272,6 +287,41 @@ int hils_attn_decode_timed(const hils_dims_t* dims, const void* q, const void* k
   if (!stage_ms) return fail(HILS_E_INVAL, "stage_ms must be non-NULL");
   return run_decode(dims, q, k_cache, v_cache, seq_lens, kc, bc, qcal_D, qcal_U, sel_idx_out, o, ws, ws_bytes, stream,
                     stage_ms);
+}
+
+int hils_landmark_compress_paged(const hils_dims_t* dims, const void* k_pages, const int32_t* block_table,
+                                 int32_t max_blocks, int32_t num_pages, const void* lmk_q, int32_t c_begin,
+                                 int32_t c_end, float* kc, float* bc, void* stream) {
+  hils::Geom g;
+  int rc = check_dims(dims, g);
+  if (rc) return rc;
+  hils::KvPages pg;
+  if ((rc = check_pages(g, block_table, max_blocks, num_pages, pg))) return rc;
+  if (c_begin < 0 || c_end < c_begin || c_end > g.C())
+    return fail(HILS_E_INVAL, "need 0 <= c_begin <= c_end <= N/S (c_begin=%d c_end=%d N/S=%d)", c_begin, c_end, g.C());
+  if (c_end == c_begin) {
+    g_err[0] = 0;
+    return HILS_OK;
+  }
+  if (!k_pages || !lmk_q || !kc || !bc) return fail(HILS_E_INVAL, "k_pages, lmk_q, kc and bc must be non-NULL");
+  hipError_t e = hils::launch_compress(g.io, k_pages, lmk_q, kc, bc, g.B, g.Hkv, g.Hl, g.N, g.d, c_begin, c_end,
+                                       (hipStream_t)stream, pg);
+  if (e != hipSuccess) return hip_fail(e, "hils_landmark_compress_paged");
+  g_err[0] = 0;
+  return HILS_OK;
+}
+
+int hils_attn_decode_paged(const hils_dims_t* dims, const void* q, const void* k_pages, const void* v_pages,
+                           const int32_t* block_table, int32_t max_blocks, int32_t num_pages, const int32_t* seq_lens,
+                           const float* kc, const float* bc, const void* qcal_D, const void* qcal_U,
+                           int32_t* sel_idx_out, void* o, void* ws, size_t ws_bytes, void* stream) {
+  hils::Geom g;
+  int rc = check_dims(dims, g);
+  if (rc) return rc;
+  hils::KvPages pg;
+  if ((rc = check_pages(g, block_table, max_blocks, num_pages, pg))) return rc;
+  return run_decode(dims, q, k_pages, v_pages, seq_lens, kc, bc, qcal_D, qcal_U, sel_idx_out, o, ws, ws_bytes, stream,
+                    nullptr, pg);
 }
 
 int hils_dense_attention(const hils_dims_t* dims, const void* q, const void* k, const void* v, void* o,

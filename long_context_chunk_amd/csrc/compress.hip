@@ -16,7 +16,7 @@ namespace hils {
 template <typename IO, int D>
 __global__ void __launch_bounds__(256) compress_kernel(const IO* __restrict__ k, const IO* __restrict__ lmk,
                                                         float* __restrict__ kc, float* __restrict__ bc, int Hkv,
-                                                        int Hl, int N, int C, int c_begin, int nchunks) {
+                                                        int Hl, int N, int C, int c_begin, int nchunks, KvPages pg) {
   constexpr int S = 64;
   constexpr int LD = D + 1;  // padded fp32 row stride: lane j reading row j is conflict-free
   __shared__ float ks[S * LD];
@@ -32,7 +32,7 @@ __global__ void __launch_bounds__(256) compress_kernel(const IO* __restrict__ k,
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
 
   // stage the key tile
-  const IO* kt = k + ((int64_t)bk * N + (int64_t)c * S) * D;
+  const IO* kt = k + pg.chunk_row(b, kvh, Hkv, N, c) * D;
   for (int i = tid; i < S * D; i += 256) ks[(i / D) * LD + (i % D)] = io_traits<IO>::load(kt, i);
   __syncthreads();
 
@@ -80,23 +80,23 @@ __global__ void __launch_bounds__(256) compress_kernel(const IO* __restrict__ k,
 
 template <typename IO>
 hipError_t launch_compress_t(const void* k, const void* lmk, float* kc, float* bc, int B, int Hkv, int Hl, int N,
-                             int d, int c_begin, int c_end, hipStream_t st) {
+                             int d, int c_begin, int c_end, hipStream_t st, KvPages pg) {
   const int C = N / 64, n = c_end - c_begin;
   if (n <= 0) return hipSuccess;
   dim3 grid((unsigned)((int64_t)B * Hkv * n)), block(256);
   if (d == 64)
     hipLaunchKernelGGL((compress_kernel<IO, 64>), grid, block, 0, st, (const IO*)k, (const IO*)lmk, kc, bc, Hkv,
-                       Hl, N, C, c_begin, n);
+                       Hl, N, C, c_begin, n, pg);
   else
     hipLaunchKernelGGL((compress_kernel<IO, 128>), grid, block, 0, st, (const IO*)k, (const IO*)lmk, kc, bc, Hkv,
-                       Hl, N, C, c_begin, n);
+                       Hl, N, C, c_begin, n, pg);
   return hipGetLastError();
 }
 
 hipError_t launch_compress(int io, const void* k, const void* lmk, float* kc, float* bc, int B, int Hkv, int Hl,
-                           int N, int d, int c_begin, int c_end, hipStream_t st) {
-  return io == 0 ? launch_compress_t<float>(k, lmk, kc, bc, B, Hkv, Hl, N, d, c_begin, c_end, st)
-                 : launch_compress_t<bf16_t>(k, lmk, kc, bc, B, Hkv, Hl, N, d, c_begin, c_end, st);
+                           int N, int d, int c_begin, int c_end, hipStream_t st, KvPages pg) {
+  return io == 0 ? launch_compress_t<float>(k, lmk, kc, bc, B, Hkv, Hl, N, d, c_begin, c_end, st, pg)
+                 : launch_compress_t<bf16_t>(k, lmk, kc, bc, B, Hkv, Hl, N, d, c_begin, c_end, st, pg);
 }
 
 }  // namespace hils

@@ -284,7 +284,7 @@ __global__ void __launch_bounds__(256) decode_attend(const IO* __restrict__ q, c
                                                      const IO* __restrict__ vcache, const int32_t* __restrict__ seq_lens,
                                                      const int32_t* __restrict__ sel_i, const float* __restrict__ sel_s,
                                                      const int32_t* __restrict__ nsel, float* __restrict__ part,
-                                                     float* __restrict__ sig, int Hq, int Hkv, int N, int K) {
+                                                     float* __restrict__ sig, int Hq, int Hkv, int N, int K, KvPages pg) {
   constexpr int KJ = D / 32;        // logits: 4 threads per key, KJ runs of 8 dims each
   constexpr int TPR = D / 8;        // values: threads per row (8 dims each)
   constexpr int NG = 256 / TPR;     // key groups
@@ -305,7 +305,7 @@ __global__ void __launch_bounds__(256) decode_attend(const IO* __restrict__ q, c
     c = sel_i[(int64_t)bh * K + slot];
     nk = 64;
   }
-  const int64_t row0 = ((int64_t)b * Hkv + kvh) * N + (int64_t)c * 64;
+  const int64_t row0 = pg.chunk_row(b, kvh, Hkv, N, c);
   // keys past nk (own chunk only) read row nk - 1, in bounds, and get weight 0
   const int key = t >> 2, qd = t & 3;
   const int e8 = (t % TPR) * 8, kg = t / TPR;
@@ -407,7 +407,7 @@ template <typename IO, int D>
 static hipError_t launch_decode_t(const Geom& g, const void* q, const void* kcache, const void* vcache,
                                   const int32_t* seq_lens, const float* kc, const float* bc, const void* Dw,
                                   const void* Uw, int32_t* sel_user, void* o, char* ws, hipStream_t st,
-                                  hipEvent_t* ev) {
+                                  hipEvent_t* ev, KvPages pg) {
   const DecodeWs w = decode_ws(g);
   uint64_t* cand = (uint64_t*)(ws + w.cand);
   int32_t* sel_i = (int32_t*)(ws + w.sel_i);
@@ -426,7 +426,7 @@ static hipError_t launch_decode_t(const Geom& g, const void* q, const void* kcac
                      sel_user, g.Hq, C, g.K, nsplit);
   if (ev) (void)hipEventRecord(ev[2], st);
   hipLaunchKernelGGL((decode_attend<IO, D>), dim3(BH * (g.K + 1)), dim3(256), 0, st, (const IO*)q, (const IO*)kcache,
-                     (const IO*)vcache, seq_lens, sel_i, sel_s, nsel, part, sig, g.Hq, g.Hkv, g.N, g.K);
+                     (const IO*)vcache, seq_lens, sel_i, sel_s, nsel, part, sig, g.Hq, g.Hkv, g.N, g.K, pg);
   hipLaunchKernelGGL((decode_combine<IO, D>), dim3(BH), dim3(256), 0, st, (const float*)part, (const float*)sig,
                      (const int32_t*)nsel, (IO*)o, g.K);
   if (ev) (void)hipEventRecord(ev[3], st);
@@ -435,14 +435,16 @@ static hipError_t launch_decode_t(const Geom& g, const void* q, const void* kcac
 
 hipError_t launch_decode(const Geom& g, const void* q, const void* kcache, const void* vcache, const int32_t* seq_lens,
                          const float* kc, const float* bc, const void* Dw, const void* Uw, int32_t* sel_idx_out,
-                         void* o, void* ws, size_t ws_bytes, hipStream_t st, hipEvent_t* ev) {
+                         void* o, void* ws, size_t ws_bytes, hipStream_t st, hipEvent_t* ev, KvPages pg) {
   if (ws_bytes < decode_workspace_bytes(g)) return hipErrorInvalidValue;
   char* w = (char*)ws;
   if (g.io == 0)
-    return g.d == 64 ? launch_decode_t<float, 64>(g, q, kcache, vcache, seq_lens, kc, bc, Dw, Uw, sel_idx_out, o, w, st, ev)
-                     : launch_decode_t<float, 128>(g, q, kcache, vcache, seq_lens, kc, bc, Dw, Uw, sel_idx_out, o, w, st, ev);
-  return g.d == 64 ? launch_decode_t<bf16_t, 64>(g, q, kcache, vcache, seq_lens, kc, bc, Dw, Uw, sel_idx_out, o, w, st, ev)
-                   : launch_decode_t<bf16_t, 128>(g, q, kcache, vcache, seq_lens, kc, bc, Dw, Uw, sel_idx_out, o, w, st, ev);
+    return g.d == 64
+               ? launch_decode_t<float, 64>(g, q, kcache, vcache, seq_lens, kc, bc, Dw, Uw, sel_idx_out, o, w, st, ev, pg)
+               : launch_decode_t<float, 128>(g, q, kcache, vcache, seq_lens, kc, bc, Dw, Uw, sel_idx_out, o, w, st, ev, pg);
+  return g.d == 64
+             ? launch_decode_t<bf16_t, 64>(g, q, kcache, vcache, seq_lens, kc, bc, Dw, Uw, sel_idx_out, o, w, st, ev, pg)
+             : launch_decode_t<bf16_t, 128>(g, q, kcache, vcache, seq_lens, kc, bc, Dw, Uw, sel_idx_out, o, w, st, ev, pg);
 }
 
 }  // namespace hils

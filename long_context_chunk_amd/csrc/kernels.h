@@ -13,8 +13,24 @@ struct Geom {
   int G() const { return Hq / Hkv; }
 };
 
+// Where the keys/values of chunk c of (sequence b, KV head kvh) live.  Contiguous caches
+// ([B,Hkv,N,d]) have table == nullptr.  Paged caches hold one chunk of every KV head per
+// page ([pages,Hkv,64,d]); chunk c of sequence b is page table[b * max_blocks + c].
+// Either way the chunk's 64 rows are consecutive d-vectors.
+struct KvPages {
+  const int32_t* table = nullptr;
+  int max_blocks = 0, num_pages = 0;
+  // first row of the chunk, in d-vectors from the base pointer; page ids outside the pool
+  // are clamped into it (a bad table gives wrong values, never an access outside the pool)
+  __device__ __forceinline__ int64_t chunk_row(int b, int kvh, int Hkv, int N, int c) const {
+    if (table == nullptr) return ((int64_t)b * Hkv + kvh) * N + (int64_t)c * 64;
+    const int p = min(max(table[(int64_t)b * max_blocks + c], 0), num_pages - 1);
+    return ((int64_t)p * Hkv + kvh) * 64;
+  }
+};
+
 hipError_t launch_compress(int io, const void* k, const void* lmk, float* kc, float* bc, int B, int Hkv, int Hl,
-                           int N, int d, int c_begin, int c_end, hipStream_t st);
+                           int N, int d, int c_begin, int c_end, hipStream_t st, KvPages pg = KvPages());
 
 // Chunk scores and per-row top-K for all N queries of every (b, h).
 size_t score_workspace_bytes(const Geom& g);
@@ -36,7 +52,8 @@ size_t decode_workspace_bytes(const Geom& g);
 // after chunk attention and fusion.
 hipError_t launch_decode(const Geom& g, const void* q, const void* kcache, const void* vcache, const int32_t* seq_lens,
                          const float* kc, const float* bc, const void* D, const void* U, int32_t* sel_idx_out,
-                         void* o, void* ws, size_t ws_bytes, hipStream_t st, hipEvent_t* ev = nullptr);
+                         void* o, void* ws, size_t ws_bytes, hipStream_t st, hipEvent_t* ev = nullptr,
+                         KvPages pg = KvPages());
 
 // Dense causal attention (the baseline).
 hipError_t launch_dense(const Geom& g, const void* q, const void* k, const void* v, void* o, hipStream_t st);

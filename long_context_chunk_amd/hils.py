@@ -20,8 +20,8 @@ OP_COMPRESS, OP_SCORE_TOPK, OP_PREFILL, OP_DECODE = 0, 1, 2, 3
 OK, E_INVAL, E_UNSUPPORTED, E_WORKSPACE, E_HIP = 0, -1, -2, -3, -4
 
 SYMBOLS = ("hils_workspace_bytes", "hils_landmark_compress", "hils_chunk_score_topk", "hils_attn_prefill",
-           "hils_attn_prefill_timed", "hils_attn_decode", "hils_attn_decode_timed", "hils_dense_attention",
-           "hils_last_error")
+           "hils_attn_prefill_timed", "hils_attn_decode", "hils_attn_decode_timed", "hils_landmark_compress_paged",
+           "hils_attn_decode_paged", "hils_dense_attention", "hils_last_error")
 STAGES = ("compress", "score_threshold", "score_select", "bucket", "chunk_attend", "own_attend", "fuse")
 DECODE_STAGES = ("scan", "merge", "attend_fuse")
 
@@ -62,8 +62,11 @@ def load():
         lib.hils_attn_decode_timed.argtypes = [dp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp,
                                                ctypes.POINTER(ctypes.c_float)]
         lib.hils_dense_attention.argtypes = [dp, vp, vp, vp, vp, vp]
+        lib.hils_landmark_compress_paged.argtypes = [dp, vp, vp, i32, i32, vp, i32, i32, vp, vp, vp]
+        lib.hils_attn_decode_paged.argtypes = [dp, vp, vp, vp, vp, i32, i32, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
         for f in ("hils_landmark_compress", "hils_chunk_score_topk", "hils_attn_prefill", "hils_attn_prefill_timed",
-                  "hils_attn_decode", "hils_attn_decode_timed", "hils_dense_attention"):
+                  "hils_attn_decode", "hils_attn_decode_timed", "hils_dense_attention", "hils_landmark_compress_paged",
+                  "hils_attn_decode_paged"):
             getattr(lib, f).restype = ctypes.c_int
         lib.hils_last_error.argtypes = []
         lib.hils_last_error.restype = ctypes.c_char_p
@@ -215,3 +218,43 @@ def dense_attention(dm: Dims, q, k, v, o):
     _req(v, "v", (dm.B, dm.Hkv, dm.N, dm.d), dt)
     _req(o, "o", (dm.B, dm.Hq, dm.N, dm.d), dt)
     _check(load().hils_dense_attention(ctypes.byref(dm), _p(q), _p(k), _p(v), _p(o), _stream()))
+
+
+def landmark_compress_paged(dm: Dims, k_pages, block_table, lmk_q, kc, bc, c_begin=0, c_end=None):
+    """hils_landmark_compress_paged: k_pages [pages,Hkv,S,d], block_table [B,max_blocks] int32."""
+    C = dm.N // dm.S
+    c_end = C if c_end is None else c_end
+    dt = torch.float32 if dm.io == F32 else torch.bfloat16
+    _req(k_pages, "k_pages", None, dt)
+    _req(block_table, "block_table", (dm.B, C), torch.int32)
+    _req(lmk_q, "lmk_q", (dm.B, dm.Hlmk, C, dm.d), dt)
+    _req(kc, "kc", (dm.B, dm.Hlmk, C, dm.d), torch.float32)
+    _req(bc, "bc", (dm.B, dm.Hlmk, C), torch.float32)
+    _check(load().hils_landmark_compress_paged(ctypes.byref(dm), _p(k_pages), _p(block_table), C, k_pages.shape[0],
+                                               _p(lmk_q), c_begin, c_end, _p(kc), _p(bc), _stream()))
+
+
+def attn_decode_paged(dm: Dims, q, k_pages, v_pages, block_table, seq_lens, kc, bc, o, ws, qcal_D=None, qcal_U=None,
+                      sel_idx=None):
+    """hils_attn_decode_paged: hils_attn_decode on a chunk-paged KV cache."""
+    C = dm.N // dm.S
+    dt = torch.float32 if dm.io == F32 else torch.bfloat16
+    _req(q, "q", (dm.B, dm.Hq, dm.d), dt)
+    _req(k_pages, "k_pages", None, dt)
+    _req(v_pages, "v_pages", tuple(k_pages.shape), dt)
+    if tuple(k_pages.shape[1:]) != (dm.Hkv, dm.S, dm.d):
+        raise ValueError("k_pages must be [pages, Hkv, S, d], got %s" % (tuple(k_pages.shape),))
+    _req(block_table, "block_table", (dm.B, C), torch.int32)
+    _req(seq_lens, "seq_lens", (dm.B,), torch.int32)
+    _req(kc, "kc", (dm.B, dm.Hlmk, C, dm.d), torch.float32)
+    _req(bc, "bc", (dm.B, dm.Hlmk, C), torch.float32)
+    _req(o, "o", (dm.B, dm.Hq, dm.d), dt)
+    _req(ws, "ws", dtype=torch.uint8)
+    if dm.qcal_rank > 0:
+        _req(qcal_D, "qcal_D", (dm.Hq, dm.qcal_rank, dm.d), dt)
+        _req(qcal_U, "qcal_U", (dm.Hq, dm.d, dm.qcal_rank), dt)
+    if sel_idx is not None:
+        _req(sel_idx, "sel_idx", (dm.B, dm.Hq, dm.K), torch.int32)
+    _check(load().hils_attn_decode_paged(ctypes.byref(dm), _p(q), _p(k_pages), _p(v_pages), _p(block_table), C,
+                                         k_pages.shape[0], _p(seq_lens), _p(kc), _p(bc), _p(qcal_D), _p(qcal_U),
+                                         _p(sel_idx), _p(o), _p(ws), ws.numel(), _stream()))

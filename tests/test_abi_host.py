@@ -128,3 +128,23 @@ def test_dense_attention_validation():
     assert lib.hils_dense_attention(ctypes.byref(bad), fake, fake, fake, fake, None) == hils.E_INVAL
     bad = hils.dims(1, 4, 2, 96, 100, 4)   # unsupported head dim
     assert lib.hils_dense_attention(ctypes.byref(bad), fake, fake, fake, fake, None) == hils.E_UNSUPPORTED
+
+
+def test_paged_entry_points_validation():
+    lib = hils.load()
+    d = hils.dims(2, 4, 2, 64, 1024, 8)   # N = 16 chunks
+    fake = ctypes.c_void_p(0x1000)
+    # capacity N must be max_blocks * S
+    assert lib.hils_landmark_compress_paged(ctypes.byref(d), fake, fake, 15, 40, fake, 0, 1, fake, fake,
+                                            None) == hils.E_INVAL
+    assert lib.hils_landmark_compress_paged(ctypes.byref(d), fake, None, 16, 40, fake, 0, 1, fake, fake,
+                                            None) == hils.E_INVAL
+    assert lib.hils_landmark_compress_paged(ctypes.byref(d), fake, fake, 16, 0, fake, 0, 1, fake, fake,
+                                            None) == hils.E_INVAL
+    assert lib.hils_landmark_compress_paged(ctypes.byref(d), fake, fake, 16, 40, fake, 3, 2, fake, fake,
+                                            None) == hils.E_INVAL
+    need = hils.workspace_bytes(d, hils.OP_DECODE)
+    assert lib.hils_attn_decode_paged(ctypes.byref(d), fake, fake, fake, fake, 8, 40, fake, fake, fake, None, None,
+                                      None, fake, fake, need, None) == hils.E_INVAL
+    assert lib.hils_attn_decode_paged(ctypes.byref(d), fake, fake, fake, fake, 16, 40, fake, fake, fake, None, None,
+                                      None, fake, fake, need - 1, None) == hils.E_WORKSPACE

@@ -260,3 +260,85 @@ def test_dense_baseline(name, w):
     err = np.abs(got - ref)
     mx, mean = TOL[w.io]
     assert err.max() <= mx and err.mean() <= mean, (err.max(), err.mean())
+
+
+# ------------------------------------------ ablation variants of the chunk summary
+# The pages' ablations replace the learned landmark: mean pooling of the chunk's keys
+# (a_j = 1/S, what a zero landmark query gives) and one shared query for every chunk.
+# Both are inputs to the same kernels.
+@pytest.mark.parametrize("variant", ["mean_pooled", "shared_query"])
+def test_summary_ablation_variants(variant):
+    w = synth.Workload("ablation_" + variant, B=1, Hq=4, Hkv=2, d=64, N=1500, K=8)
+    _say("ablation", variant)
+    x = synth.make_inputs(w, SEED + 11)
+    if variant == "mean_pooled":
+        x["lmk"] = np.zeros_like(x["lmk"])
+    else:
+        x["lmk"] = np.ascontiguousarray(np.broadcast_to(x["lmk"][:, :, :1, :], x["lmk"].shape))
+    g = gpu_prefill(w, x, fused=True)
+    kc_o, bc_o = oracle_compress(w, x)
+    if variant == "mean_pooled":  # closed form: the chunk mean and the entropy of uniform weights
+        kf = synth_bf16_to_f64(x["k"][:, :, :w.C * w.S]).reshape(w.B, w.Hkv, w.C, w.S, w.d).mean(axis=3)
+        kf = np.repeat(kf, w.Hq // w.Hkv, axis=1)
+        np.testing.assert_allclose(g["kc"], kf, rtol=0, atol=1e-5)
+        np.testing.assert_allclose(g["bc"], math.log(w.S), rtol=0, atol=1e-5)
+    rows = [(0, h, i) for h in range(w.Hq) for i in range(0, w.N, 2)]
+    ref = oracle_rows(w, x, kc_o, bc_o, rows)
+    rr = np.asarray(rows)
+    summ = check_selection_and_output(w, x, kc_o, bc_o, rows, ref, g["sel_idx"][rr[:, 0], rr[:, 1], rr[:, 2]],
+                                      g["sel_score"][rr[:, 0], rr[:, 1], rr[:, 2]],
+                                      g["o"][rr[:, 0], rr[:, 1], rr[:, 2]], label=variant)
+    _say(variant, summ)
+
+
+def synth_bf16_to_f64(a):
+    return (a.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+
+
+# ------------------------------------------------------- chunk-paged KV cache (decode)
+def _paginate(w, x, seed):
+    """The contiguous caches scattered into shuffled pages of one chunk each (plus spare pages)."""
+    C = w.C
+    rng = np.random.default_rng(seed)
+    npages = w.B * C + 3
+    perm = rng.permutation(npages)[: w.B * C].astype(np.int32)
+    table = perm.reshape(w.B, C)
+    kp = np.zeros((npages, w.Hkv, w.S, w.d), x["k"].dtype)
+    vp = np.zeros_like(kp)
+    for b in range(w.B):
+        for c in range(C):
+            kp[table[b, c]] = x["k"][b, :, c * w.S:(c + 1) * w.S]
+            vp[table[b, c]] = x["v"][b, :, c * w.S:(c + 1) * w.S]
+    return kp, vp, table
+
+
+@pytest.mark.parametrize("qcal", [0, 8])
+def test_paged_decode_matches_contiguous(qcal):
+    """Same kernels, different K/V addressing: outputs and selections are identical."""
+    w = synth.Workload("paged", B=3, Hq=4, Hkv=2, d=128, N=2048, K=8, decode=True, seq_lens=[2048, 1000, 70],
+                       qcal_rank=qcal)
+    _say("paged decode, qcal", qcal)
+    x = synth.make_inputs(w, SEED + 13)
+    ref = gpu_decode(w, x)
+    kp, vp, table = _paginate(w, x, 5)
+    dm = dims_of(w)
+    kpt, vpt = upload(kp, w.io), upload(vp, w.io)
+    tab = torch.from_numpy(table).cuda()
+    kc = torch.empty((w.B, w.Hlmk, w.C, w.d), dtype=torch.float32, device="cuda")
+    bc = torch.empty((w.B, w.Hlmk, w.C), dtype=torch.float32, device="cuda")
+    lmk = upload(x["lmk"], w.io)
+    for c in range(w.C):  # incremental: one chunk at a time, as chunks complete during decoding
+        hils.landmark_compress_paged(dm, kpt, tab, lmk, kc, bc, c, c + 1)
+    torch.cuda.synchronize()
+    assert torch.equal(kc, ref["kc"]) and torch.equal(bc, ref["bc"])
+    q = upload(x["q"], w.io)
+    o = torch.empty_like(q)
+    sel = torch.empty((w.B, w.Hq, w.K), dtype=torch.int32, device="cuda")
+    ws = hils.workspace(dm, hils.OP_DECODE)
+    D = upload(x["D"], w.io) if w.qcal_rank else None
+    U = upload(x["U"], w.io) if w.qcal_rank else None
+    hils.attn_decode_paged(dm, q, kpt, vpt, tab, torch.from_numpy(x["seq_lens"]).cuda(), kc, bc, o, ws, qcal_D=D,
+                           qcal_U=U, sel_idx=sel)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(sel.cpu().numpy(), ref["sel_idx"])
+    np.testing.assert_array_equal(o.float().cpu().numpy(), ref["o"])
