@@ -36,7 +36,8 @@ namespace hils {
 constexpr int AT_ROWS = 128;        // gathered rows per chunk_attend tile (4 waves x 32)
 constexpr int AT_TILES = 8;         // tiles per chunk_attend work item (one K/V staging)
 constexpr int ITEM_ROWS = AT_ROWS * AT_TILES;
-constexpr int HIST_SLICE = 1 << 18; // selection entries per bucket_count / bucket_part1 workgroup
+constexpr int HIST_SLICE = 1 << 17; // selection entries per bucket_count / bucket_part1 workgroup
+constexpr int P2_SPLIT = 4;         // workgroups sharing one 64-chunk range in bucket_part2
 constexpr int BK_TILE = 8192;       // entries sorted in LDS at a time by bucket_part1/2
 constexpr int BK_PER = BK_TILE / 256;
 constexpr int FINE_BITS = 6;        // chunks per first-pass range: 64
@@ -110,8 +111,9 @@ __global__ void __launch_bounds__(256) bucket_count(const int32_t* __restrict__ 
 }
 
 // Single workgroup: boff = exclusive scan of counts, toff = exclusive scan of
-// ceil(count / ITEM_ROWS) (work items).  Both get a final total entry.
-__global__ void __launch_bounds__(1024) bucket_scan(const uint32_t* __restrict__ counts, uint32_t* __restrict__ boff,
+// ceil(count / ITEM_ROWS) (work items).  Both get a final total entry; counts is
+// left zeroed for reuse as per-bucket cursors.
+__global__ void __launch_bounds__(1024) bucket_scan(uint32_t* __restrict__ counts, uint32_t* __restrict__ boff,
                                                     uint32_t* __restrict__ toff, int nbk) {
   __shared__ uint32_t sa[1024], sb[1024];
   const int t = threadIdx.x;
@@ -134,10 +136,12 @@ __global__ void __launch_bounds__(1024) bucket_scan(const uint32_t* __restrict__
   }
   uint32_t ra = sa[t] - a, rb = sb[t] - b;  // exclusive prefix of this thread's range
   for (int i = beg; i < end; ++i) {
+    const uint32_t ci = counts[i];
     boff[i] = ra;
     toff[i] = rb;
-    ra += counts[i];
-    rb += (counts[i] + ITEM_ROWS - 1) / ITEM_ROWS;
+    ra += ci;
+    rb += (ci + ITEM_ROWS - 1) / ITEM_ROWS;
+    counts[i] = 0;  // from here on: the second sorting pass's cursor of bucket i
   }
   if (t == 1023) {
     boff[nbk] = sa[t];
@@ -223,23 +227,25 @@ __global__ void __launch_bounds__(256) bucket_part1(const int32_t* __restrict__ 
   }
 }
 
-// Second pass: one workgroup per (group, 64-chunk range) sorts the range's region by
-// chunk, LDS tile by LDS tile, appending each chunk's run at that bucket's cursor.
+// Second pass: P2_SPLIT workgroups per (group, 64-chunk range) sort the range's region by
+// chunk, LDS tile by LDS tile (tiles dealt round-robin), reserving each chunk's run with
+// one atomic per (tile, chunk) on that bucket's cursor.
 __global__ void __launch_bounds__(256) bucket_part2(const uint32_t* __restrict__ tmp, const uint32_t* __restrict__ boff,
-                                                    uint32_t* __restrict__ pairs, int64_t group_len, int C, int nrg) {
+                                                    uint32_t* __restrict__ fcur, uint32_t* __restrict__ pairs,
+                                                    int64_t group_len, int C, int nrg) {
   constexpr int NF = 1 << FINE_BITS;
   __shared__ uint32_t skey[BK_TILE];
   __shared__ uint8_t sfb[BK_TILE];
-  __shared__ uint32_t hist[NF], loff[NF], cur[NF];
-  const int grp = blockIdx.x / nrg, rg = blockIdx.x % nrg;
+  __shared__ uint32_t hist[NF], loff[NF], gpos[NF];
+  const int sp = blockIdx.x % P2_SPLIT, gr = blockIdx.x / P2_SPLIT;
+  const int grp = gr / nrg, rg = gr % nrg;
   const int t = threadIdx.x, lane = t & 63;
   const int c0 = rg << FINE_BITS;
   const int nf = min(NF, C - c0);
   const int64_t bk0 = (int64_t)grp * C + c0;
   const uint32_t R0 = boff[bk0], R1 = boff[bk0 + nf];
-  if (t < NF) cur[t] = t < nf ? boff[bk0 + t] : 0u;
   const uint32_t ebase = (uint32_t)(grp * group_len);
-  for (uint32_t t0 = R0; t0 < R1; t0 += BK_TILE) {
+  for (uint32_t t0 = R0 + (uint32_t)sp * BK_TILE; t0 < R1; t0 += (uint32_t)P2_SPLIT * BK_TILE) {
     if (t < NF) hist[t] = 0;
     __syncthreads();
     uint32_t key[BK_PER], rk[BK_PER];
@@ -252,7 +258,7 @@ __global__ void __launch_bounds__(256) bucket_part2(const uint32_t* __restrict__
     for (int u = 0; u < BK_PER; ++u)
       if (key[u] != 0xffffffffu) rk[u] = atomicAdd(&hist[key[u] >> LOCAL_BITS], 1u);
     __syncthreads();
-    if (t < 64) {  // one wave scans the NF = 64 chunk counts
+    if (t < 64) {  // one wave scans the NF = 64 chunk counts and reserves their runs
       const uint32_t h = hist[lane];
       uint32_t x = h;
 #pragma unroll
@@ -261,6 +267,7 @@ __global__ void __launch_bounds__(256) bucket_part2(const uint32_t* __restrict__
         if (lane >= o) x += y;
       }
       loff[lane] = x - h;
+      if (lane < nf && h) gpos[lane] = boff[bk0 + lane] + atomicAdd(&fcur[bk0 + lane], h);
     }
     __syncthreads();
 #pragma unroll
@@ -275,12 +282,12 @@ __global__ void __launch_bounds__(256) bucket_part2(const uint32_t* __restrict__
     const uint32_t n = min((uint32_t)BK_TILE, R1 - t0);
     for (uint32_t i = t; i < n; i += 256) {
       const int f = sfb[i];
-      pairs[cur[f] + (i - loff[f])] = ebase + skey[i];
+      pairs[gpos[f] + (i - loff[f])] = ebase + skey[i];
     }
     __syncthreads();
-    if (t < NF) cur[t] += hist[t];
   }
 }
+
 
 template <typename IO>
 struct partial_t {
@@ -661,8 +668,8 @@ static hipError_t launch_attend_t(const Geom& g, const void* q, const void* k, c
     uint32_t* tmp = (uint32_t*)partial;
     hipLaunchKernelGGL(bucket_part1, dim3(ngrp * spg), dim3(256), 0, st, sel, boff, cursor, tmp, group_len, spg, C,
                        nrg);
-    hipLaunchKernelGGL(bucket_part2, dim3(ngrp * nrg), dim3(256), 0, st, (const uint32_t*)tmp, boff, pairs, group_len,
-                       C, nrg);
+    hipLaunchKernelGGL(bucket_part2, dim3(ngrp * nrg * P2_SPLIT), dim3(256), 0, st, (const uint32_t*)tmp, boff,
+                       counts, pairs, group_len, C, nrg);
     if (ev) hipEventRecord(ev[0], st);
     // work items <= total pairs / ITEM_ROWS + number of buckets (host bound; the exact count is read on the device)
     // rows of query chunk p (64 of them, fewer in the tail) select min(K, p, C) chunks each
