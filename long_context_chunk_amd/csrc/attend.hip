@@ -460,31 +460,36 @@ __global__ void __launch_bounds__(256, 2) chunk_attend(const IO* __restrict__ q,
 }
 
 // ---------------------------------------------------------------- own_attend
-// One workgroup (2 waves) per (b, h, query chunk qc): rows qc*64 .. qc*64+63 attend
-// their own chunk causally on the MFMA; the normalised output goes to output slot K
-// of the row and its log-sum-exp to lse[row].
+// One workgroup per (b, KV head, query chunk qc) and group of up to OWN_HEADS of its
+// query heads, two waves per head: rows qc*64 .. qc*64+63 of each head attend their own
+// chunk causally on the MFMA, against one staging of the chunk's K/V; the normalised
+// output goes to output slot K of the row and its log-sum-exp to lse[row].
+constexpr int OWN_HEADS = 4;
+
 template <typename IO, int D>
-__global__ void __launch_bounds__(128) own_attend(const IO* __restrict__ q, const IO* __restrict__ k,
-                                                  const IO* __restrict__ v, void* __restrict__ partial_v,
-                                                  float* __restrict__ lse, int Hq, int Hkv, int N, int K, int NQC) {
+__global__ void __launch_bounds__(128 * OWN_HEADS) own_attend(const IO* __restrict__ q, const IO* __restrict__ k,
+                                                              const IO* __restrict__ v, void* __restrict__ partial_v,
+                                                              float* __restrict__ lse, int Hq, int Hkv, int N, int K,
+                                                              int NQC, int hpw) {
   constexpr int NT = io_traits<IO>::terms;
   using PT = typename partial_t<IO>::type;
   __shared__ KVTile<IO, D, NT> tile;
-  // consecutive workgroups: the G query heads of one (b, KV head, chunk), so the
-  // chunk's K/V is read from HBM once and reused from L2
   const int G = Hq / Hkv;
-  const int gi = blockIdx.x % G, rest = blockIdx.x / G;
+  const int ngb = (G + hpw - 1) / hpw;
+  const int gb = blockIdx.x % ngb, rest = blockIdx.x / ngb;
   const int qc = rest % NQC, bkv = rest / NQC;
   const int kvh = bkv % Hkv, b = bkv / Hkv;
-  const int h = kvh * G + gi;
-  const int bh = b * Hq + h;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, hf = lane >> 5;
+  const int gi = gb * hpw + (w >> 1);  // this wave pair's query head in the group
+  const bool head_ok = gi < G;
+  const int h = kvh * G + min(gi, G - 1);
+  const int bh = b * Hq + h;
   const int key0 = qc * 64;
   const int nkeys = min(64, N - key0);
-  stage_kv<IO, D, NT>(tile, k, v, ((int64_t)b * Hkv + kvh) * N + key0, nkeys, tid, 128);
-  const int rl = 32 * w + (lane & 31);
+  stage_kv<IO, D, NT>(tile, k, v, ((int64_t)b * Hkv + kvh) * N + key0, nkeys, tid, blockDim.x);
+  const int rl = 32 * (w & 1) + (lane & 31);
   const int i = key0 + rl;
-  const bool ok = i < N;
+  const bool ok = i < N && head_ok;
   bf16x8_t qb[NT][D / 16];
   load_q_operand<IO, D, NT>(q, ((int64_t)bh * N + (ok ? i : 0)) * D, ok, qb);
   __syncthreads();
@@ -687,8 +692,10 @@ static hipError_t launch_attend_t(const Geom& g, const void* q, const void* k, c
   }
   const int NQC = (g.N + 63) / 64;
   float* lse = (float*)(ws + w.lse);
-  hipLaunchKernelGGL((own_attend<IO, D>), dim3(g.B * g.Hq * NQC), dim3(128), 0, st, (const IO*)q, (const IO*)k,
-                     (const IO*)v, partial, lse, g.Hq, g.Hkv, g.N, g.K, NQC);
+  const int hpw = std::min(g.G(), OWN_HEADS);
+  const int ngb = (g.G() + hpw - 1) / hpw;
+  hipLaunchKernelGGL((own_attend<IO, D>), dim3(g.B * g.Hkv * NQC * ngb), dim3(128 * hpw), 0, st, (const IO*)q,
+                     (const IO*)k, (const IO*)v, partial, lse, g.Hq, g.Hkv, g.N, g.K, NQC, hpw);
   if (ev) hipEventRecord(ev[2], st);
   const int64_t rows = (int64_t)g.B * g.Hq * g.N;
   const int64_t nwg = (rows + 4 * FZ_ROWS - 1) / (4 * FZ_ROWS);
