@@ -625,6 +625,10 @@ __global__ void __launch_bounds__(256, NQ * NK > 4 ? 1 : 2) score_topk_kernel(co
   if (nct > 1) load_tile(1);
   __syncthreads();  // every wave has read tile 0
   if (nct > 1) store_tile();
+  // No load may reach the loop still in flight on any path (the threshold's load does
+  // where nct < 2): the compiler would then wait for all loads at the first use of th in
+  // every iteration, the k' tile two ahead included, and expose its full latency.
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
   __syncthreads();
   for (int ct = 0; ct < nct; ++ct) {
     const bool more2 = ct + 2 < nct;
