@@ -22,7 +22,7 @@ LANDMARK, EXACT, GIVEN = 0, 1, 2
 
 
 class Shape(ctypes.Structure):
-    _fields_ = [(n, ctypes.c_int32) for n in ("B", "Hq", "Hkv", "Hl", "d", "S", "K", "N", "r")]
+    _fields_ = [(n, ctypes.c_int32) for n in ("B", "Hq", "Hkv", "Hl", "d", "S", "K", "N", "r", "W")]
 
 
 def build(force: bool = False) -> str:
@@ -68,8 +68,9 @@ def _ptr(a):
     return None if a is None else a.ctypes.data
 
 
-def shape(B, Hq, Hkv, d, N, S=64, K=16, Hl=None, r=0) -> Shape:
-    return Shape(B, Hq, Hkv, Hq if Hl is None else Hl, d, S, K, N, r)
+def shape(B, Hq, Hkv, d, N, S=64, K=16, Hl=None, r=0, W=0) -> Shape:
+    """W: local window in tokens (a multiple of S; 0 = S, the own chunk only)."""
+    return Shape(B, Hq, Hkv, Hq if Hl is None else Hl, d, S, K, N, r, W)
 
 
 def compress(s: Shape, k: np.ndarray, lmk: np.ndarray):
@@ -92,7 +93,7 @@ def qcal(s: Shape, h: int, q: np.ndarray, D=None, U=None) -> np.ndarray:
 
 
 def row_scores(s: Shape, b, h, pos, qrow, k=None, kc=None, bc=None, D=None, U=None, mode=LANDMARK):
-    """Every past-chunk score of one query (length pos // S)."""
+    """The score of every candidate chunk of one query (the complete chunks before the window)."""
     qrow = np.ascontiguousarray(qrow)
     out = np.empty(max(1, min(pos // s.S, s.N // s.S)), np.float64)
     kdt = _dt(k) if k is not None else F64

@@ -14,6 +14,13 @@
  *   - query i scores the complete past chunks c < floor(i/S); its own chunk
  *     floor(i/S) is always attended with a causal mask and takes its exact
  *     log-sum-exp as its score; the own chunk is not part of the top-K budget;
+ *   - the local sliding window (aitrends.kr "Technical details": window 512
+ *     with S = 64 and top-K = 32; the pages do not say how it joins the
+ *     fusion) is taken at chunk granularity: it holds the W/S most recent
+ *     chunks, the own one included, keys j <= i only.  It is one fusion entry
+ *     whose score is its exact log-sum-exp, and the top-K candidates are the
+ *     complete chunks before it, so every key j <= i is in exactly one entry.
+ *     W = S is the method without a window;
  *   - with fewer than K past chunks, all of them are selected;
  *   - ties in the chunk score go to the lower chunk index;
  *   - Q-Cal: q^ = q + U_h (D_h q) scores chunks; the raw q attends.
@@ -100,6 +107,17 @@ void hr_qcal(const hr_shape* s, int h, const double* q, const void* D, const voi
   free(t);
 }
 
+/* chunks in the local window (the own chunk counts) */
+static int window_chunks(const hr_shape* s) { return s->W > s->S ? s->W / s->S : 1; }
+
+/* candidate chunks of the query at position pos: complete chunks before the window */
+static int candidates(const hr_shape* s, int pos) {
+  const int C = s->N / s->S;
+  int P = pos / s->S - (window_chunks(s) - 1);
+  if (P > C) P = C;
+  return P > 0 ? P : 0;
+}
+
 /* softmax attention of q over keys [j0, j1) of one KV head: o (normalised) and the LSE */
 static double attend_range(const hr_shape* s, const double* q, const void* k, const void* v, int kvdt,
                            int64_t kvbase_row, int j0, int j1, double* o) {
@@ -138,8 +156,7 @@ int hr_row_scores(const hr_shape* s, int mode, int b, int h, int pos, const void
                   const void* U, int wdt, double* out) {
   const int d = s->d, S = s->S, C = s->N / s->S;
   const double tau = 1.0 / sqrt((double)d);
-  int P = pos / S;
-  if (P > C) P = C;
+  const int P = candidates(s, pos);
   double* q = (double*)malloc(sizeof(double) * d);
   double* qh = (double*)malloc(sizeof(double) * d);
   for (int e = 0; e < d; ++e) q[e] = ld(qrow, qdt, e);
@@ -188,9 +205,10 @@ static int by_idx_asc(const void* x, const void* y) {
  * One query through the hierarchical factorisation (hotpaper.ai abstract;
  * aitrends.kr "Methodology" calculation flow and "Key contributions"
  * second item; ai-papers.net "How HiLS Attention works", Fig. 1):
- *   1. score every complete past chunk with the surrogate, keep the top K;
+ *   1. score every candidate chunk with the surrogate, keep the top K;
  *   2. attend independently inside each selected chunk (intra-chunk softmax);
- *   3. the own, partial chunk is attended causally; its score is its exact LSE;
+ *   3. the local window (the own, partial chunk and the W/S - 1 chunks before
+ *      it) is attended causally with one softmax; its score is its exact LSE;
  *   4. fuse the per-chunk outputs with a softmax over the chunk scores.
  */
 void hr_attend(const hr_shape* s, int mode, int64_t nrows, const int32_t* row_b,
@@ -198,14 +216,13 @@ void hr_attend(const hr_shape* s, int mode, int64_t nrows, const int32_t* row_b,
                const void* k, const void* v, int kvdt, const double* kc, const double* bc,
                const void* D, const void* U, int wdt, const int32_t* sel_in, double* o,
                int32_t* sel_idx, double* sel_score, double* gap, double* lse_own, int32_t* nsel) {
-  const int d = s->d, S = s->S, K = s->K, C = s->N / s->S;
+  const int d = s->d, S = s->S, K = s->K;
 #pragma omp parallel for schedule(dynamic, 1)
   for (int64_t n = 0; n < nrows; ++n) {
     const int b = row_b[n], h = row_h[n], pos = row_pos[n];
     const int kvh = h / (s->Hq / s->Hkv);
     const int64_t row0 = ((int64_t)b * s->Hkv + kvh) * s->N;
-    int P = pos / S;
-    if (P > C) P = C;
+    const int P = candidates(s, pos);
     const void* qn = (const char*)qrows + (size_t)n * d * (qdt == HR_F64 ? 8 : qdt == HR_F32 ? 4 : 2);
 
     /* step 1: scores of all past chunks and the top-K */
@@ -248,8 +265,9 @@ void hr_attend(const hr_shape* s, int mode, int64_t nrows, const int32_t* row_b,
       attend_range(s, q, k, v, kvdt, row0, c * S, c * S + S, oc + (int64_t)t * d);
       sig[t] = cs[t].score;
     }
-    const int own = pos / S;
-    const double lse = attend_range(s, q, k, v, kvdt, row0, own * S, pos + 1, oc + (int64_t)ns * d);
+    int w0 = (pos / S - (window_chunks(s) - 1)) * S; /* first key of the window */
+    if (w0 < 0) w0 = 0;
+    const double lse = attend_range(s, q, k, v, kvdt, row0, w0, pos + 1, oc + (int64_t)ns * d);
     sig[ns] = lse;
     double M = -INFINITY;
     for (int t = 0; t <= ns; ++t)

@@ -34,6 +34,7 @@ typedef struct {
   int32_t d, S, K;        /* head dim, chunk size, top-K                           */
   int32_t N;              /* token rows of k/v (prefill length or cache capacity) */
   int32_t r;              /* Q-Cal rank (0: no Q-Cal)                             */
+  int32_t W;              /* local window in tokens, a multiple of S (0: S)        */
 } hr_shape;
 
 /* Landmark compression of every complete chunk c < N/S:
@@ -45,9 +46,10 @@ void hr_compress(const hr_shape* s, const void* k, int kdt, const void* lmk, int
 void hr_qcal(const hr_shape* s, int h, const double* q, const void* D, const void* U, int wdt,
              double* qhat);
 
-/* All past-chunk scores of one query (head h, batch b, position pos):
- * out[c] for c < pos/S, in the given mode (HR_LANDMARK or HR_EXACT).
- * Returns the number of scores written. */
+/* The scores of every candidate chunk of one query (head h, batch b, position
+ * pos): out[c] for c < pos/S - (W/S - 1) (the complete chunks before the local
+ * window), in the given mode (HR_LANDMARK or HR_EXACT).  Returns the number of
+ * scores written. */
 int hr_row_scores(const hr_shape* s, int mode, int b, int h, int pos, const void* qrow, int qdt,
                   const void* k, int kvdt, const double* kc, const double* bc, const void* D,
                   const void* U, int wdt, double* out);
@@ -58,7 +60,8 @@ int hr_row_scores(const hr_shape* s, int mode, int b, int h, int pos, const void
  * Outputs: o [nrows,d]; sel_idx [nrows,K] ascending chunk ids, -1 padded;
  * sel_score [nrows,K] the chunk scores in the same order (-inf padded);
  * gap [nrows] = K-th minus (K+1)-th best score (+inf if no (K+1)-th);
- * lse_own [nrows]; nsel [nrows].  Any output pointer may be NULL except o. */
+ * lse_own [nrows] (the LSE of the local window, the own chunk when W = S);
+ * nsel [nrows].  Any output pointer may be NULL except o. */
 void hr_attend(const hr_shape* s, int mode, int64_t nrows, const int32_t* row_b,
                const int32_t* row_h, const int32_t* row_pos, const void* qrows, int qdt,
                const void* k, const void* v, int kvdt, const double* kc, const double* bc,

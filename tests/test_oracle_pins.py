@@ -284,6 +284,73 @@ def test_dense_reduction_exact_lse_mode():
     np.testing.assert_allclose(r["o"], ref, rtol=0, atol=1e-12)
 
 
+@pytest.mark.parametrize("nw", [2, 3, 5, 40])
+def test_window_exact_lse_mode_is_dense(nw):
+    """Local window of nw chunks, exact-LSE scores and K >= every candidate: the window entry
+    and the selected chunks partition the keys j <= i, so the fusion is dense causal attention
+    (a gap or an overlap between window and candidates breaks it)."""
+    rng = _rng(30 + nw)
+    d, S, C = 16, 8, 9
+    N = C * S + 3
+    s = oracle.shape(1, 1, 1, d, N=N, S=S, K=C, W=nw * S)
+    k = rng.standard_normal((1, 1, N, d)) * 1.3
+    v = rng.standard_normal((1, 1, N, d))
+    q = rng.standard_normal((1, 1, N, d))
+    pos = list(range(N))
+    r = oracle.prefill_rows(s, q, k, v, None, None, [(0, 0, i) for i in pos], mode=oracle.EXACT)
+    ref = _dense_causal(q[0, 0], k[0, 0], v[0, 0], pos, 1 / math.sqrt(d))
+    np.testing.assert_allclose(r["o"], ref, rtol=0, atol=1e-12)
+    np.testing.assert_array_equal(r["nsel"], [min(C, max(0, i // S - nw + 1)) for i in pos])
+
+
+def test_window_covering_the_sequence_is_dense():
+    """A window longer than the sequence leaves no candidate: every row is dense causal attention."""
+    rng = _rng(36)
+    d, S, C = 32, 16, 6
+    N = C * S
+    s = oracle.shape(1, 1, 1, d, N=N, S=S, K=2, W=(C + 1) * S)
+    k = rng.standard_normal((1, 1, N, d))
+    v = rng.standard_normal((1, 1, N, d))
+    lmk = rng.standard_normal((1, 1, C, d))
+    q = rng.standard_normal((1, 1, N, d))
+    kc, bc = oracle.compress(s, k, lmk)
+    pos = list(range(N))
+    r = oracle.prefill_rows(s, q, k, v, kc, bc, [(0, 0, i) for i in pos])
+    assert np.all(r["nsel"] == 0)
+    ref = _dense_causal(q[0, 0], k[0, 0], v[0, 0], pos, 1 / math.sqrt(d))
+    np.testing.assert_allclose(r["o"], ref, rtol=0, atol=1e-12)
+
+
+def test_window_candidates_are_the_chunks_before_it():
+    """With a window of 3 chunks, a row selects among chunks c < i//S - 2 only, by the same
+    surrogate scores as without a window; the window's entry is the exact softmax over keys
+    (i//S - 2)*S .. i (checked against brute force)."""
+    rng = _rng(37)
+    d, S, C, K, nw = 16, 8, 12, 3, 3
+    N = C * S
+    s1 = oracle.shape(1, 1, 1, d, N=N, S=S, K=K)
+    sw = oracle.shape(1, 1, 1, d, N=N, S=S, K=K, W=nw * S)
+    k = rng.standard_normal((1, 1, N, d))
+    v = rng.standard_normal((1, 1, N, d))
+    lmk = rng.standard_normal((1, 1, C, d))
+    q = rng.standard_normal((1, 1, N, d))
+    kc, bc = oracle.compress(s1, k, lmk)
+    pos = list(range(N))
+    r = oracle.prefill_rows(sw, q, k, v, kc, bc, [(0, 0, i) for i in pos])
+    tau = 1 / math.sqrt(d)
+    for n, i in enumerate(pos):
+        P = max(0, i // S - nw + 1)
+        full = oracle.row_scores(s1, 0, 0, i, q[0, 0, i], kc=kc, bc=bc)
+        cand = oracle.row_scores(sw, 0, 0, i, q[0, 0, i], kc=kc, bc=bc)
+        assert cand.size == P
+        np.testing.assert_array_equal(cand, full[:P])
+        best = sorted(range(P), key=lambda c: (-cand[c], c))[:K]
+        assert sorted(r["sel_idx"][n, : r["nsel"][n]].tolist()) == sorted(best)
+        j0 = max(0, (i // S - nw + 1) * S)
+        z = tau * (k[0, 0, j0 : i + 1] @ q[0, 0, i])
+        assert abs(r["lse_own"][n] - (z.max() + math.log(np.exp(z - z.max()).sum()))) < 1e-12
+
+
 def test_rows_of_first_chunk_are_dense():
     rng = _rng(11)
     d, S = 64, 64
