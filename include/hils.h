@@ -16,6 +16,15 @@
  *   (4) the per-chunk outputs are fused with a softmax over the chunk scores
  *       (abstract; aitrends.kr "Key contributions", hierarchical softmax).
  *
+ * Local window (aitrends.kr "Technical details": a local sliding window of 512
+ * tokens beside S = 64 and top-K = 32; the pages do not say how it joins the
+ * fusion).  dims.window = W > S widens the own chunk of (3) to the W/S most
+ * recent chunks, the own one included (keys floor(i/S)*S - (W - S) .. i, at
+ * least 0): one causal softmax over them, scored by its exact log-sum-exp.
+ * The candidates of (2) are then the complete chunks c < floor(i/S) - (W/S - 1)
+ * before the window, so every key j <= i lies in exactly one fused entry.
+ * W = S (or 0) is the method without a window.
+ *
  * Conventions shared by every call:
  *   - Every pointer argument is a DEVICE pointer allocated by the caller, except
  *     `dims`, which is a host pointer.  The library allocates no memory and keeps
@@ -77,6 +86,8 @@ typedef struct {
   int32_t N;         /* prefill: tokens; decode: KV-cache capacity (row stride of k/v) */
   int32_t qcal_rank; /* Q-Cal rank r, 0 <= r <= 32 (0: no Q-Cal, q^ = q)                */
   int32_t io;        /* hils_dtype_t of q, k, v, o, lmk_q, qcal_D, qcal_U              */
+  int32_t window;    /* local window W in tokens, a multiple of S, W <= 32*S; 0 or S:   */
+                     /* the own chunk only (see "Local window" above)                   */
 } hils_dims_t;
 
 /* Bytes of device workspace the call `op` needs for these dims (0 if none).

@@ -2,6 +2,7 @@
 // dispatch to the kernel launchers.  Nothing is enqueued unless every argument
 // is valid.
 #include <stdarg.h>
+#include <algorithm>
 #include <stdio.h>
 #include <string.h>
 
@@ -46,7 +47,10 @@ int check_dims(const hils_dims_t* dims, hils::Geom& g) {
   if (s.S != 64) return fail(HILS_E_UNSUPPORTED, "chunk size %d not supported (64)", s.S);
   if (s.K > 32) return fail(HILS_E_UNSUPPORTED, "K=%d not supported (K <= 32)", s.K);
   if (s.qcal_rank > 32) return fail(HILS_E_UNSUPPORTED, "qcal_rank=%d not supported (<= 32)", s.qcal_rank);
-  g = hils::Geom{s.B, s.Hq, s.Hkv, s.Hlmk, s.d, s.S, s.K, s.N, s.qcal_rank, s.io};
+  if (s.window < 0 || s.window % s.S != 0)
+    return fail(HILS_E_INVAL, "window must be a non-negative multiple of S (window=%d S=%d)", s.window, s.S);
+  if (s.window > 32 * s.S) return fail(HILS_E_UNSUPPORTED, "window=%d not supported (<= 32*S)", s.window);
+  g = hils::Geom{s.B, s.Hq, s.Hkv, s.Hlmk, s.d, s.S, s.K, s.N, s.qcal_rank, s.io, std::max(1, s.window / s.S)};
   return HILS_OK;
 }
 

@@ -1,7 +1,9 @@
 // Intra-chunk attention and fusion for prefill, given each query's selection.
 //
 //   o_ic   = sum_{j in c} softmax_j(q_i . k_j / sqrt(d)) v_j       for each selected chunk c
-//   o_own  = the same over the own chunk, keys cS .. i (causal); LSE_own its log-sum-exp
+//   o_own  = the same over the own chunk, keys cS .. i (causal); LSE_own its log-sum-exp.
+//            With a local window of nw chunks: one softmax over chunks c - nw + 1 .. c
+//            (keys up to i), and the selections come from the chunks before them.
 //   o_i    = sum_c w_c o_ic + w_own o_own,  w = softmax over {s_ic} U {LSE_own}
 // (hotpaper.ai abstract: each query attends each retrieved chunk independently
 // and the outputs are fused by the chunk retrieval scores; aitrends.kr
@@ -23,7 +25,7 @@
 //                   sel_idx) by bucket: first into ranges of 64 chunks, then into
 //                   chunks, each pass sorting tiles in LDS and writing whole runs
 //   chunk_attend  : gathered-row MFMA attention per (bucket, 128-row tile)
-//   own_attend    : causal own-chunk MFMA attention -> slot K and LSE_own
+//   own_attend    : causal own-chunk (local window) MFMA attention -> slot K and LSE_own
 //   fuse          : softmax over {s_ic} U {LSE_own}, weighted sum of the slots -> o
 #include <algorithm>
 
@@ -461,16 +463,20 @@ __global__ void __launch_bounds__(256, 2) chunk_attend(const IO* __restrict__ q,
 
 // ---------------------------------------------------------------- own_attend
 // One workgroup per (b, KV head, query chunk qc) and group of up to OWN_HEADS of its
-// query heads, two waves per head: rows qc*64 .. qc*64+63 of each head attend their own
-// chunk causally on the MFMA, against one staging of the chunk's K/V; the normalised
-// output goes to output slot K of the row and its log-sum-exp to lse[row].
+// query heads, two waves per head: rows qc*64 .. qc*64+63 of each head attend their
+// local window -- chunks max(0, qc - nw + 1) .. qc, the own chunk qc causally -- on the
+// MFMA, each chunk's K/V staged once for every head of the group.  Each chunk gives the
+// wave unnormalised outputs against its own maximum; the chunks are merged by rescaling
+// to the running maximum (an online softmax over the window).  The normalised output
+// goes to output slot K of the row and the window's log-sum-exp to lse[row].  With
+// nw = 1 the window is the own chunk alone.
 constexpr int OWN_HEADS = 4;
 
 template <typename IO, int D>
 __global__ void __launch_bounds__(128 * OWN_HEADS) own_attend(const IO* __restrict__ q, const IO* __restrict__ k,
                                                               const IO* __restrict__ v, void* __restrict__ partial_v,
                                                               float* __restrict__ lse, int Hq, int Hkv, int N, int K,
-                                                              int NQC, int hpw) {
+                                                              int NQC, int hpw, int nw) {
   constexpr int NT = io_traits<IO>::terms;
   using PT = typename partial_t<IO>::type;
   __shared__ KVTile<IO, D, NT> tile;
@@ -484,18 +490,41 @@ __global__ void __launch_bounds__(128 * OWN_HEADS) own_attend(const IO* __restri
   const bool head_ok = gi < G;
   const int h = kvh * G + min(gi, G - 1);
   const int bh = b * Hq + h;
-  const int key0 = qc * 64;
-  const int nkeys = min(64, N - key0);
-  stage_kv<IO, D, NT>(tile, k, v, ((int64_t)b * Hkv + kvh) * N + key0, nkeys, tid, blockDim.x);
+  const int64_t kv0 = ((int64_t)b * Hkv + kvh) * N;
   const int rl = 32 * (w & 1) + (lane & 31);
-  const int i = key0 + rl;
+  const int i = qc * 64 + rl;
   const bool ok = i < N && head_ok;
   bf16x8_t qb[NT][D / 16];
   load_q_operand<IO, D, NT>(q, ((int64_t)bh * N + (ok ? i : 0)) * D, ok, qb);
-  __syncthreads();
+  const int c0 = max(0, qc - nw + 1);
   f32x16_t oa[D / 32];
   float m, l;
-  wave_chunk_attention<IO, D, NT, true>(tile, qb, rl + 1, oa, m, l);  // causal: keys 0..rl
+  for (int c = c0; c <= qc; ++c) {
+    if (c > c0) __syncthreads();  // every wave is done with the previous chunk
+    stage_kv<IO, D, NT>(tile, k, v, kv0 + (int64_t)c * 64, min(64, N - c * 64), tid, blockDim.x);
+    __syncthreads();
+    f32x16_t oc[D / 32];
+    float mc, lc;
+    if (c == qc)
+      wave_chunk_attention<IO, D, NT, true>(tile, qb, rl + 1, oc, mc, lc);  // causal: keys 0..rl
+    else
+      wave_chunk_attention<IO, D, NT, false>(tile, qb, 64, oc, mc, lc);    // a full earlier chunk
+    if (c == c0) {
+#pragma unroll
+      for (int dt = 0; dt < D / 32; ++dt) oa[dt] = oc[dt];
+      m = mc;
+      l = lc;
+    } else {
+      const float mn = fmaxf(m, mc);
+      const float a = __expf(m - mn), bb = __expf(mc - mn);
+#pragma unroll
+      for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+        for (int rr = 0; rr < 16; ++rr) oa[dt][rr] = fmaf(oa[dt][rr], a, oc[dt][rr] * bb);
+      l = fmaf(l, a, lc * bb);
+      m = mn;
+    }
+  }
   if (!ok) return;
   const int64_t row = (int64_t)bh * N + i;
   const float inv = 1.0f / l;
@@ -519,16 +548,17 @@ __global__ void __launch_bounds__(128 * OWN_HEADS) own_attend(const IO* __restri
 }
 
 // ---------------------------------------------------------------------- fuse
-// o_i = sum over the row's chunk outputs (selected chunks, then its own chunk) weighted
-// by the softmax of their scores (the selected chunks' s_ic, the own chunk's LSE).  The
-// number of selected chunks is min(K, past chunks), so every load of a row is issued at
+// o_i = sum over the row's chunk outputs (selected chunks, then its own chunk or local
+// window) weighted by the softmax of their scores (the selected chunks' s_ic, the own
+// entry's LSE).  The number of selected chunks is min(K, candidate chunks), known
+// without reading the selection, so every load of a row is issued at
 // once; each wave works on two rows at a time.  16-byte loads of whole output rows.
 constexpr int FZ_ROWS = 16;  // rows per wave
 
 template <typename IO, int D>
 __global__ void __launch_bounds__(256) fuse(const float* __restrict__ sel_score, const float* __restrict__ lse,
                                             const void* __restrict__ partial_v, IO* __restrict__ o, int N, int C,
-                                            int K, int64_t rows) {
+                                            int K, int64_t rows, int nw) {
   using PT = typename partial_t<IO>::type;
   constexpr int EPL = 16 / sizeof(PT);   // partial elements per 16-byte load
   constexpr int LPS = D / EPL;           // lanes per output row
@@ -555,7 +585,7 @@ __global__ void __launch_bounds__(256) fuse(const float* __restrict__ sel_score,
       const int64_t row = row0 + u + v2;
       R.live[v2] = u < FZ_ROWS && row < rows;
       const int i = R.live[v2] ? (int)(row % N) : 0;
-      const int ns = min(K, min(C, i / 64));
+      const int ns = min(K, candidate_chunks(i, C, nw));
       R.nsel[v2] = ns;
       R.sc[v2] = -INFINITY;
       if (R.live[v2]) {
@@ -677,9 +707,10 @@ static hipError_t launch_attend_t(const Geom& g, const void* q, const void* k, c
                        counts, pairs, group_len, C, nrg);
     if (ev) hipEventRecord(ev[0], st);
     // work items <= total pairs / ITEM_ROWS + number of buckets (host bound; the exact count is read on the device)
-    // rows of query chunk p (64 of them, fewer in the tail) select min(K, p, C) chunks each
+    // rows of query chunk p (64 of them, fewer in the tail) select min(K, p - nw + 1, C) chunks each
     int64_t pairs_total = 0;
-    for (int p = 0; p * 64 < g.N; ++p) pairs_total += (int64_t)std::min(64, g.N - p * 64) * std::min(g.K, std::min(C, p));
+    for (int p = 0; p * 64 < g.N; ++p)
+      pairs_total += (int64_t)std::min(64, g.N - p * 64) * std::min(g.K, std::min(C, std::max(0, p - g.nw + 1)));
     pairs_total *= (int64_t)g.B * g.Hq;
     const int64_t items = std::min<int64_t>((pairs_total + ITEM_ROWS - 1) / ITEM_ROWS + nbk, 0x7fffffff);
     if (pairs_total > 0)
@@ -695,12 +726,12 @@ static hipError_t launch_attend_t(const Geom& g, const void* q, const void* k, c
   const int hpw = std::min(g.G(), OWN_HEADS);
   const int ngb = (g.G() + hpw - 1) / hpw;
   hipLaunchKernelGGL((own_attend<IO, D>), dim3(g.B * g.Hkv * NQC * ngb), dim3(128 * hpw), 0, st, (const IO*)q,
-                     (const IO*)k, (const IO*)v, partial, lse, g.Hq, g.Hkv, g.N, g.K, NQC, hpw);
+                     (const IO*)k, (const IO*)v, partial, lse, g.Hq, g.Hkv, g.N, g.K, NQC, hpw, g.nw);
   if (ev) hipEventRecord(ev[2], st);
   const int64_t rows = (int64_t)g.B * g.Hq * g.N;
   const int64_t nwg = (rows + 4 * FZ_ROWS - 1) / (4 * FZ_ROWS);
   hipLaunchKernelGGL((fuse<IO, D>), dim3((unsigned)nwg), dim3(256), 0, st, scr, (const float*)lse,
-                     (const void*)partial, (IO*)o, g.N, C, g.K, rows);
+                     (const void*)partial, (IO*)o, g.N, C, g.K, rows, g.nw);
   if (ev) hipEventRecord(ev[3], st);
   return hipGetLastError();
 }

@@ -1,16 +1,19 @@
 // One decode step: every sequence b has one new query per head at position
 // L_b - 1 (L_b = seq_lens[b], the cache length including the current token).
 //
-//   1. decode_scan    s_c = q^ . k'_c / sqrt(d) + b'_c for every complete past
-//                     chunk c < floor((L_b - 1)/S)  (fp32 GEMV streaming k' from HBM:
+//   1. decode_scan    s_c = q^ . k'_c / sqrt(d) + b'_c for every candidate chunk
+//                     c < floor((L_b - 1)/S) - (nw - 1), the complete chunks before the
+//                     local window of nw chunks  (fp32 GEMV streaming k' from HBM:
 //                     the dominant traffic of a decode step).  Each workgroup keeps
 //                     the best 32 of its 1024 chunks (64-bit selection keys, bitonic
 //                     lane networks); decode_merge merges the splits of a (b, h) into
 //                     the exact top-K (ties to the lower chunk id).
-//   2. decode_attend  one workgroup per (b, h, selected chunk) plus one for the own
-//                     (causal) chunk: gathers the chunk's K/V rows (coalesced),
-//                     softmax inside the chunk, o_c and its score (own: exact LSE);
-//                     decode_combine fuses them with the softmax over the scores.
+//   2. decode_attend  one workgroup per (b, h, selected chunk) plus one per chunk of
+//                     the local window (the own chunk causal): gathers the chunk's
+//                     K/V rows (coalesced), softmax inside the chunk, o_c and its
+//                     score (window chunks: their exact LSE, so that together they
+//                     weigh as one softmax over the window); decode_combine fuses
+//                     them with the softmax over the scores.
 // (aitrends.kr article, "Methodology" and "Main results": sparse KV access gives
 // near-constant decode cost; hotpaper.ai abstract: chunk outputs fused by the
 // retrieval scores.)
@@ -45,9 +48,9 @@ static DecodeWs decode_ws(const Geom& g) {
   w.nsel = off;
   off += al2(bh * 4);
   w.part = off;
-  off += al2(bh * (g.K + 1) * g.d * 4);
+  off += al2(bh * (g.K + g.nw) * g.d * 4);
   w.sig = off;
-  off += al2(bh * (g.K + 1) * 4);
+  off += al2(bh * (g.K + g.nw) * 4);
   w.total = off;
   return w;
 }
@@ -132,7 +135,8 @@ template <typename IO, int D>
 __global__ void __launch_bounds__(256) decode_scan(const IO* __restrict__ q, const IO* __restrict__ Dw,
                                                    const IO* __restrict__ Uw, const float* __restrict__ kc,
                                                    const float* __restrict__ bc, const int32_t* __restrict__ seq_lens,
-                                                   uint64_t* __restrict__ cand, int Hq, int C, int r, int nsplit) {
+                                                   uint64_t* __restrict__ cand, int Hq, int C, int r, int nsplit,
+                                                   int nw) {
   __shared__ __align__(16) float qs[D];
   __shared__ float ts[32];
   __shared__ uint64_t keys[DS_CHUNKS];
@@ -140,7 +144,7 @@ __global__ void __launch_bounds__(256) decode_scan(const IO* __restrict__ q, con
   const int sp = blockIdx.x % nsplit, bh = blockIdx.x / nsplit;
   const int b = bh / Hq, h = bh % Hq;
   const int L = seq_lens[b];
-  const int P = min(C, (L - 1) / 64);
+  const int P = candidate_chunks(L - 1, C, nw);
   const int c_beg = sp * DS_CHUNKS, c_end = min(P, c_beg + DS_CHUNKS);
   const int t = threadIdx.x, lane = t & 63, w = t >> 6;
   qhat_to_lds<IO, D>(q + (int64_t)bh * D, Dw, Uw, h, r, qs, ts);
@@ -227,7 +231,8 @@ __global__ void __launch_bounds__(256) decode_scan(const IO* __restrict__ q, con
 __global__ void __launch_bounds__(256) decode_merge(const uint64_t* __restrict__ cand,
                                                     const int32_t* __restrict__ seq_lens, int32_t* __restrict__ sel_i,
                                                     float* __restrict__ sel_s, int32_t* __restrict__ nsel_out,
-                                                    int32_t* __restrict__ sel_user, int Hq, int C, int K, int nsplit) {
+                                                    int32_t* __restrict__ sel_user, int Hq, int C, int K, int nsplit,
+                                                    int nw) {
   static_assert(DS_MAX_SPLIT == 16, "two lists per half-wave");
   __shared__ uint64_t wl[4][32];
   const int bh = blockIdx.x, t = threadIdx.x, lane = t & 63, w = t >> 6;
@@ -244,7 +249,7 @@ __global__ void __launch_bounds__(256) decode_merge(const uint64_t* __restrict__
   dmerge_sorted(lk, wl[(lane >> 5) * 2 + 1][lane & 31]);
   dmerge_sorted(lk, __shfl(lk, (lane & 31) + 32));
   const int L = seq_lens[bh / Hq];
-  const int n = min(K, min(C, (L - 1) / 64));
+  const int n = min(K, candidate_chunks(L - 1, C, nw));
   if (lane < K) {
     const bool ok = lane < n && lk != 0;
     const int32_t ci = ok ? key_chunk(lk) : -1;
@@ -276,7 +281,8 @@ struct raw8<float> {
   __device__ __forceinline__ float operator[](int m) const { return m < 4 ? a[m] : b[m - 4]; }
 };
 
-// slot s < nsel: selected chunk sel_i[s]; slot K: the own chunk.  Writes the
+// slot s < nsel: selected chunk sel_i[s]; slot K + t: chunk own - t of the window
+// (t < nw; slots before chunk 0 do nothing).  Writes the
 // normalised chunk output (fp32) and the chunk's fusion score.  The V rows a thread
 // needs are loaded together with the K rows, before the logits.
 template <typename IO, int D>
@@ -284,7 +290,8 @@ __global__ void __launch_bounds__(256) decode_attend(const IO* __restrict__ q, c
                                                      const IO* __restrict__ vcache, const int32_t* __restrict__ seq_lens,
                                                      const int32_t* __restrict__ sel_i, const float* __restrict__ sel_s,
                                                      const int32_t* __restrict__ nsel, float* __restrict__ part,
-                                                     float* __restrict__ sig, int Hq, int Hkv, int N, int K, KvPages pg) {
+                                                     float* __restrict__ sig, int Hq, int Hkv, int N, int K, int nw,
+                                                     KvPages pg) {
   constexpr int KJ = D / 32;        // logits: 4 threads per key, KJ runs of 8 dims each
   constexpr int TPR = D / 8;        // values: threads per row (8 dims each)
   constexpr int NG = 256 / TPR;     // key groups
@@ -292,14 +299,16 @@ __global__ void __launch_bounds__(256) decode_attend(const IO* __restrict__ q, c
   __shared__ float z[64];
   __shared__ float ml[2];
   __shared__ float red[NG][D];
-  const int slot = blockIdx.x % (K + 1), bh = blockIdx.x / (K + 1);
+  const int NSL = K + nw;  // slots: K selected chunks, then the window's chunks, own chunk first
+  const int slot = blockIdx.x % NSL, bh = blockIdx.x / NSL;
   const int b = bh / Hq, h = bh % Hq, kvh = h / (Hq / Hkv);
   const int t = threadIdx.x, lane = t & 63, w = t >> 6;
   const int L = seq_lens[b];
   int c, nk;
-  if (slot == K) {
-    c = (L - 1) / 64;
-    nk = L - c * 64;
+  if (slot >= K) {
+    c = (L - 1) / 64 - (slot - K);
+    if (c < 0) return;  // the window reaches back past chunk 0
+    nk = slot == K ? L - c * 64 : 64;
   } else {
     if (slot >= nsel[bh]) return;
     c = sel_i[(int64_t)bh * K + slot];
@@ -361,31 +370,37 @@ __global__ void __launch_bounds__(256) decode_attend(const IO* __restrict__ q, c
     float o = 0.f;
 #pragma unroll
     for (int g2 = 0; g2 < NG; ++g2) o += red[g2][t];
-    part[((int64_t)bh * (K + 1) + slot) * D + t] = o / ml[1];
+    part[((int64_t)bh * NSL + slot) * D + t] = o / ml[1];
   }
-  if (t == 0) sig[(int64_t)bh * (K + 1) + slot] = slot == K ? ml[0] + logf(ml[1]) : sel_s[(int64_t)bh * K + slot];
+  if (t == 0) sig[(int64_t)bh * NSL + slot] = slot >= K ? ml[0] + logf(ml[1]) : sel_s[(int64_t)bh * K + slot];
 }
 
-// o = sum over the n + 1 live slots of softmax(sig)_s part_s, one workgroup per (b, h).
-// Lane s of every wave holds slot s's weight; the slot rows are all loaded at once.
+// o = sum over the live slots of softmax(sig)_s part_s, one workgroup per (b, h): the n
+// selected chunks and the window's chunks from the own one back to chunk 0 (at most nw).
+// Lane s of every wave holds slot s's weight; the live slot rows are all loaded at once.
 template <typename IO, int D>
 __global__ void __launch_bounds__(256) decode_combine(const float* __restrict__ part, const float* __restrict__ sig,
-                                                      const int32_t* __restrict__ nsel, IO* __restrict__ out, int K) {
-  constexpr int G = 256 / D;                    // slot groups
-  constexpr int MAXJ = (DS_KEEP + 1 + G - 1) / G;  // K + 1 <= 33 slots
+                                                      const int32_t* __restrict__ nsel,
+                                                      const int32_t* __restrict__ seq_lens, IO* __restrict__ out,
+                                                      int Hq, int K, int nw) {
+  constexpr int G = 256 / D;               // slot groups
+  constexpr int MAXJ = (64 + G - 1) / G;   // K + nw <= 64 slots
   __shared__ float red[G][D];
   const int bh = blockIdx.x, t = threadIdx.x, lane = t & 63;
   const int n = nsel[bh];
-  const float* sg = sig + (int64_t)bh * (K + 1);
-  const float* pp = part + (int64_t)bh * (K + 1) * D;
+  const int NSL = K + nw;
+  const int nwl = min(nw, (seq_lens[bh / Hq] - 1) / 64 + 1);  // window chunks that exist
+  const float* sg = sig + (int64_t)bh * NSL;
+  const float* pp = part + (int64_t)bh * NSL * D;
   const int e = t % D, g = t / D;
+  auto live_slot = [&](int s2) { return s2 < n || (s2 >= K && s2 < K + nwl); };
   float pv[MAXJ];
 #pragma unroll
   for (int j = 0; j < MAXJ; ++j) {
     const int s2 = g + j * G;
-    pv[j] = (s2 < n || s2 == K) ? pp[(int64_t)s2 * D + e] : 0.f;
+    pv[j] = live_slot(s2) ? pp[(int64_t)s2 * D + e] : 0.f;
   }
-  const bool live = lane < n || lane == K;
+  const bool live = live_slot(lane);
   const float v = live ? sg[lane] : -INFINITY;
   const float M = wave_max(v);
   const float wt = live ? expf(v - M) : 0.f;
@@ -420,15 +435,16 @@ static hipError_t launch_decode_t(const Geom& g, const void* q, const void* kcac
   if (nsplit > DS_MAX_SPLIT) return hipErrorInvalidValue;  // N/S > 16384, rejected by the ABI first
   if (ev) (void)hipEventRecord(ev[0], st);
   hipLaunchKernelGGL((decode_scan<IO, D>), dim3(BH * nsplit), dim3(256), 0, st, (const IO*)q, (const IO*)Dw,
-                     (const IO*)Uw, kc, bc, seq_lens, cand, g.Hq, C, g.r, nsplit);
+                     (const IO*)Uw, kc, bc, seq_lens, cand, g.Hq, C, g.r, nsplit, g.nw);
   if (ev) (void)hipEventRecord(ev[1], st);
   hipLaunchKernelGGL(decode_merge, dim3(BH), dim3(256), 0, st, (const uint64_t*)cand, seq_lens, sel_i, sel_s, nsel,
-                     sel_user, g.Hq, C, g.K, nsplit);
+                     sel_user, g.Hq, C, g.K, nsplit, g.nw);
   if (ev) (void)hipEventRecord(ev[2], st);
-  hipLaunchKernelGGL((decode_attend<IO, D>), dim3(BH * (g.K + 1)), dim3(256), 0, st, (const IO*)q, (const IO*)kcache,
-                     (const IO*)vcache, seq_lens, sel_i, sel_s, nsel, part, sig, g.Hq, g.Hkv, g.N, g.K, pg);
+  hipLaunchKernelGGL((decode_attend<IO, D>), dim3(BH * (g.K + g.nw)), dim3(256), 0, st, (const IO*)q,
+                     (const IO*)kcache, (const IO*)vcache, seq_lens, sel_i, sel_s, nsel, part, sig, g.Hq, g.Hkv, g.N,
+                     g.K, g.nw, pg);
   hipLaunchKernelGGL((decode_combine<IO, D>), dim3(BH), dim3(256), 0, st, (const float*)part, (const float*)sig,
-                     (const int32_t*)nsel, (IO*)o, g.K);
+                     (const int32_t*)nsel, seq_lens, (IO*)o, g.Hq, g.K, g.nw);
   if (ev) (void)hipEventRecord(ev[3], st);
   return hipGetLastError();
 }

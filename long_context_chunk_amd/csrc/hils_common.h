@@ -195,4 +195,9 @@ HILS_DEV int remap_xcd(int bid, int nblocks) {
   return xcd * per + j;  // may be >= nblocks: the caller skips it
 }
 
+// Candidate chunks of the query at position i (chunks of 64 keys): the complete chunks
+// before its local window of nw chunks (the own chunk and the nw - 1 before it), at
+// most C.  nw = 1 leaves every complete past chunk a candidate.
+HILS_DEV int candidate_chunks(int i, int C, int nw) { return min(C, max(0, (i >> 6) - nw + 1)); }
+
 }  // namespace hils

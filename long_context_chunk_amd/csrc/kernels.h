@@ -9,6 +9,7 @@ namespace hils {
 // Geometry of one call, validated by the ABI layer.
 struct Geom {
   int B, Hq, Hkv, Hl, d, S, K, N, r, io;
+  int nw = 1;  // chunks in the local window (the own chunk and the nw - 1 before it)
   int C() const { return N / S; }
   int G() const { return Hq / Hkv; }
 };

@@ -1,6 +1,7 @@
 // Chunk scoring and top-K for prefill queries.
 //
-//   s_ic = q^_i . k'_c / sqrt(d) + b'_c   for every complete past chunk c < floor(i/S)
+//   s_ic = q^_i . k'_c / sqrt(d) + b'_c   for every candidate chunk c < floor(i/S) - (nw - 1)
+//                                        (the complete chunks before the local window of nw chunks)
 //   q^_i = q_i + U_h (D_h q_i)             (Q-Cal; q^ = q without it)
 // keep the K best (ties -> lower chunk id).  (aitrends.kr article,
 // "Methodology": the score formula, the calculation flow and the Q-Cal module.)
@@ -335,7 +336,7 @@ template <typename IO, int D, bool QCAL>
 __global__ void __launch_bounds__(256, 2) score_threshold(const IO* __restrict__ q, const IO* __restrict__ Dw,
                                                           const IO* __restrict__ Uw, const uint16_t* __restrict__ t1,
                                                           float* __restrict__ theta, int H, int N, int C, int K, int r,
-                                                          int NB, int items) {
+                                                          int NB, int items, int nw) {
   constexpr int NKS = D / 16;
   constexpr int DE = D + TH_EXT;      // bf16 elements of a chunk row
   constexpr int LDT = DE + 8;         // LDS row stride (16-byte pad: conflict-free 16-byte reads)
@@ -357,8 +358,8 @@ __global__ void __launch_bounds__(256, 2) score_threshold(const IO* __restrict__
   const int row = r0 + 32 * w + n;
   const bool row_ok = row < N;
   const int last = min(r0 + ST_ROWS, N) - 1;
-  const int Pmax = min(C, last / 64);
-  const int Pmin = min(C, r0 / 64);
+  const int Pmax = candidate_chunks(last, C, nw);
+  const int Pmin = candidate_chunks(r0, C, nw);
   const float tau = 1.0f / sqrtf((float)D);
   const int64_t qrow = ((int64_t)bh * N + (row_ok ? row : 0)) * D;
 
@@ -451,7 +452,7 @@ __global__ void __launch_bounds__(256, 2) score_threshold(const IO* __restrict__
 #pragma unroll
         for (int rr = 0; rr < 16; ++rr) {
           const int rw = r0 + 32 * w + acc_row(rr, hf);
-          const int prow = rw < N ? min(C, rw / 64) : 0;
+          const int prow = rw < N ? candidate_chunks(rw, C, nw) : 0;
           const float v = c >= prow ? -INFINITY : acc[rr];
           m2[rr] = __builtin_amdgcn_fmed3f(m1[rr], m2[rr], v);
           m1[rr] = __builtin_amdgcn_fmed3f(m1[rr], v, pinf);
@@ -494,7 +495,7 @@ __global__ void __launch_bounds__(256, NQ * NK > 4 ? 1 : 2) score_topk_kernel(co
                                                              const float* __restrict__ theta,
                                                              int32_t* __restrict__ sel_idx,
                                                              float* __restrict__ sel_score, int H, int N, int C, int K,
-                                                             int r, int NB, int items) {
+                                                             int r, int NB, int items, int nw) {
   constexpr int NKS = D / 16;
   constexpr int DE2 = NK * D + P2_EXT;  // elements of a chunk row: plane 0, extension, planes 1..
   constexpr int LDR = DE2 + 8;          // LDS row stride (16-byte pad)
@@ -518,9 +519,9 @@ __global__ void __launch_bounds__(256, NQ * NK > 4 ? 1 : 2) score_topk_kernel(co
   const int row = r0 + 32 * w + n;       // this lane's query row
   const bool row_ok = row < N;
   const int last = min(r0 + ST_ROWS, N) - 1;
-  const int Pmax = min(C, last / 64);
-  const int Pmin = min(C, r0 / 64);
-  const int prow = row_ok ? min(C, row / 64) : 0;   // past chunks of this lane's row
+  const int Pmax = candidate_chunks(last, C, nw);
+  const int Pmin = candidate_chunks(r0, C, nw);
+  const int prow = row_ok ? candidate_chunks(row, C, nw) : 0;   // candidate chunks of this lane's row
   const int64_t qrow = ((int64_t)bh * N + (row_ok ? row : 0)) * D;
 
   // ---- the query's B operands: q^ split into NQ bf16 terms, plus the constant extension
@@ -872,11 +873,11 @@ static void launch_st(const Geom& g, const void* q, const void* Dw, const void* 
   const int items = g.B * g.Hq * NB;
   const int grid = ((items + 7) / 8) * 8;
   hipLaunchKernelGGL((score_threshold<IO, D, QCAL>), dim3(grid), dim3(256), 0, st, (const IO*)q, (const IO*)Dw,
-                     (const IO*)Uw, t1, theta, g.Hq, g.N, g.C(), g.K, g.r, NB, items);
+                     (const IO*)Uw, t1, theta, g.Hq, g.N, g.C(), g.K, g.r, NB, items, g.nw);
   if (ev) hipEventRecord(ev[0], st);
   hipLaunchKernelGGL((score_topk_kernel<IO, D, NQ, NK, QCAL>), dim3(grid), dim3(256), 0, st, (const IO*)q,
                      (const IO*)Dw, (const IO*)Uw, planes, (const float*)theta, si, ss, g.Hq, g.N, g.C(), g.K, g.r,
-                     NB, items);
+                     NB, items, g.nw);
 }
 
 template <typename IO, int D>

@@ -27,7 +27,8 @@ DECODE_STAGES = ("scan", "merge", "attend_fuse")
 
 
 class Dims(ctypes.Structure):
-    _fields_ = [(n, ctypes.c_int32) for n in ("B", "Hq", "Hkv", "Hlmk", "d", "S", "K", "N", "qcal_rank", "io")]
+    _fields_ = [(n, ctypes.c_int32) for n in ("B", "Hq", "Hkv", "Hlmk", "d", "S", "K", "N", "qcal_rank", "io",
+                                             "window")]
 
     def __repr__(self):
         return "Dims(%s)" % ", ".join("%s=%d" % (n, getattr(self, n)) for n, _ in self._fields_)
@@ -74,8 +75,9 @@ def load():
     return _lib
 
 
-def dims(B, Hq, Hkv, d, N, K, S=64, qcal_rank=0, io=BF16, Hlmk=None) -> Dims:
-    return Dims(B, Hq, Hkv, Hq if Hlmk is None else Hlmk, d, S, K, N, qcal_rank, io)
+def dims(B, Hq, Hkv, d, N, K, S=64, qcal_rank=0, io=BF16, Hlmk=None, window=0) -> Dims:
+    """window: local window in tokens (a multiple of S; 0 = the own chunk only)."""
+    return Dims(B, Hq, Hkv, Hq if Hlmk is None else Hlmk, d, S, K, N, qcal_rank, io, window)
 
 
 def _check(rc):

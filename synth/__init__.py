@@ -142,6 +142,7 @@ class Workload:
     decode: bool = False
     seq_lens: list = field(default_factory=list)   # decode: cache length per sequence
     planted_seqs: int = 2                          # decode: sequences whose query gets + 2u
+    window: int = 0        # local window in tokens (a multiple of S; 0 = the own chunk only)
 
     def __post_init__(self):
         if self.Hlmk == 0:

@@ -34,11 +34,12 @@ def download_f32(t: torch.Tensor) -> np.ndarray:
 
 
 def dims_of(w: synth.Workload) -> hils.Dims:
-    return hils.dims(w.B, w.Hq, w.Hkv, w.d, w.N, w.K, S=w.S, qcal_rank=w.qcal_rank, io=w.io, Hlmk=w.Hlmk)
+    return hils.dims(w.B, w.Hq, w.Hkv, w.d, w.N, w.K, S=w.S, qcal_rank=w.qcal_rank, io=w.io, Hlmk=w.Hlmk,
+                     window=w.window)
 
 
 def shape_of(w: synth.Workload) -> oracle.Shape:
-    return oracle.shape(w.B, w.Hq, w.Hkv, w.d, w.N, S=w.S, K=w.K, Hl=w.Hlmk, r=w.qcal_rank)
+    return oracle.shape(w.B, w.Hq, w.Hkv, w.d, w.N, S=w.S, K=w.K, Hl=w.Hlmk, r=w.qcal_rank, W=w.window)
 
 
 def gpu_compress(w, x):

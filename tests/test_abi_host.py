@@ -58,6 +58,7 @@ def test_workspace_bytes():
     ("d", 96, hils.E_UNSUPPORTED), ("S", 32, hils.E_UNSUPPORTED), ("K", 0, hils.E_INVAL), ("K", 33, hils.E_UNSUPPORTED),
     ("Hkv", 3, hils.E_INVAL), ("Hlmk", 8, hils.E_UNSUPPORTED), ("B", 0, hils.E_INVAL), ("N", 0, hils.E_INVAL),
     ("io", 5, hils.E_UNSUPPORTED), ("qcal_rank", -1, hils.E_INVAL), ("qcal_rank", 64, hils.E_UNSUPPORTED),
+    ("window", -64, hils.E_INVAL), ("window", 100, hils.E_INVAL), ("window", 33 * 64, hils.E_UNSUPPORTED),
 ])
 def test_invalid_dims_rejected(field, value, code):
     lib = hils.load()
@@ -70,6 +71,18 @@ def test_invalid_dims_rejected(field, value, code):
     rc = lib.hils_attn_prefill(ctypes.byref(d), fake, fake, fake, None, fake, fake, None, None, None, None, fake,
                                fake, 1 << 40, None)
     assert rc == code
+
+
+def test_window_workspace():
+    """The local window adds decode slots (one per window chunk) and no prefill workspace."""
+    d0 = hils.dims(2, 8, 2, 128, 4096, 16)
+    d1 = hils.dims(2, 8, 2, 128, 4096, 16, window=512)
+    d2 = hils.dims(2, 8, 2, 128, 4096, 16, window=64)
+    assert hils.workspace_bytes(d1, hils.OP_PREFILL) == hils.workspace_bytes(d0, hils.OP_PREFILL)
+    assert hils.workspace_bytes(d2, hils.OP_DECODE) == hils.workspace_bytes(d0, hils.OP_DECODE)
+    # 7 more slots per (b, h): an fp32 output row and a score each
+    assert hils.workspace_bytes(d1, hils.OP_DECODE) >= hils.workspace_bytes(d0, hils.OP_DECODE) + 2 * 8 * 7 * 128 * 4
+    assert hils.workspace_bytes(hils.dims(1, 4, 1, 64, 4096, 32, window=32 * 64), hils.OP_DECODE) > 0
 
 
 def test_null_pointers_and_ranges_rejected():

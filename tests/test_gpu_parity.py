@@ -342,3 +342,99 @@ def test_paged_decode_matches_contiguous(qcal):
     torch.cuda.synchronize()
     np.testing.assert_array_equal(sel.cpu().numpy(), ref["sel_idx"])
     np.testing.assert_array_equal(o.float().cpu().numpy(), ref["o"])
+
+
+# ---------------------------------------------------------------- local window
+WINDOW = [
+    ("bf16_d64_w512_ragged", synth.scaled(synth.WORKLOADS["prefill_8k"], N=2000, window=512)),
+    ("bf16_d128_qcal_w256", synth.scaled(synth.WORKLOADS["prefill_256k_qcal"], N=1500, Hq=8, Hkv=2, K=8,
+                                         window=256)),
+    ("f32_d128_qcal_w128", synth.Workload("f32_w128", B=2, Hq=4, Hkv=2, d=128, N=777, K=5, io=synth.F32,
+                                          qcal_rank=16, window=128)),
+    ("bf16_d64_B2_K32_w2048", synth.Workload("w2048", B=2, Hq=4, Hkv=1, d=64, N=3000, K=32, window=2048)),
+    ("bf16_window_covers_all", synth.Workload("wall", B=1, Hq=2, Hkv=1, d=128, N=300, K=3, window=512)),
+]
+
+
+@pytest.mark.parametrize("name,w", WINDOW, ids=[n for n, _ in WINDOW])
+def test_prefill_window(name, w):
+    """Local window of W/S chunks: every row against the oracle (selection from the chunks
+    before the window, one exact-LSE entry for the window)."""
+    _say("prefill window", name)
+    x = synth.make_inputs(w, SEED + 21)
+    g = gpu_prefill(w, x, fused=True)
+    kc_o, bc_o = oracle_compress(w, x)
+    rows = [(b, h, i) for b in range(w.B) for h in range(w.Hq) for i in range(w.N)]
+    ref = oracle_rows(w, x, kc_o, bc_o, rows)
+    nw = w.window // w.S
+    assert np.array_equal(ref["nsel"], [min(w.K, w.C, max(0, i // w.S - nw + 1)) for _, _, i in rows])
+    rr = np.asarray(rows)
+    summ = check_selection_and_output(w, x, kc_o, bc_o, rows, ref, g["sel_idx"][rr[:, 0], rr[:, 1], rr[:, 2]],
+                                      g["sel_score"][rr[:, 0], rr[:, 1], rr[:, 2]],
+                                      g["o"][rr[:, 0], rr[:, 1], rr[:, 2]], label=name)
+    _say(name, summ)
+
+
+def test_window_of_one_chunk_is_no_window():
+    """window = S and window = 0 are the same method: bit-identical prefill and decode."""
+    w0 = SMALL[2][1]
+    w1 = synth.scaled(w0, window=w0.S)
+    x = synth.make_inputs(w0, SEED + 22)
+    a, b = gpu_prefill(w0, x), gpu_prefill(w1, x)
+    np.testing.assert_array_equal(a["sel_idx"], b["sel_idx"])
+    np.testing.assert_array_equal(a["o"], b["o"])
+    d0 = DECODE_SMALL[0][1]
+    xd = synth.make_inputs(d0, SEED + 23)
+    p, r = gpu_decode(d0, xd), gpu_decode(synth.scaled(d0, window=d0.S), xd)
+    np.testing.assert_array_equal(p["sel_idx"], r["sel_idx"])
+    np.testing.assert_array_equal(p["o"], r["o"])
+
+
+DECODE_WINDOW = [
+    ("bf16_d128_w512", synth.Workload("dw512", B=5, Hq=8, Hkv=2, d=128, N=4096, K=8, decode=True,
+                                      seq_lens=[1, 64, 300, 1000, 4096], needle_frac=0.05, window=512)),
+    ("f32_d64_K32_w2048", synth.Workload("dw2048", B=3, Hq=2, Hkv=1, d=64, N=4096, K=32, io=synth.F32, decode=True,
+                                         seq_lens=[4096, 2100, 2047], planted=False, window=2048)),
+    ("bf16_d64_qcal_w192", synth.Workload("dw192", B=2, Hq=4, Hkv=4, d=64, N=3000, K=16, decode=True,
+                                          seq_lens=[2999, 640], qcal_rank=8, planted_seqs=1, window=192)),
+]
+
+
+@pytest.mark.parametrize("name,w", DECODE_WINDOW, ids=[n for n, _ in DECODE_WINDOW])
+def test_decode_window(name, w):
+    """Decode with a local window (K + W/S slots, up to 64) against the oracle."""
+    test_decode(name, w)
+
+
+def test_decode_window_matches_prefill_row():
+    L = 1000
+    w = synth.Workload("prew", B=1, Hq=4, Hkv=2, d=128, N=L, K=8, window=384)
+    x = synth.make_inputs(w, SEED + 24)
+    pre = gpu_prefill(w, x)
+    wd = synth.Workload("decw", B=1, Hq=4, Hkv=2, d=128, N=L, K=8, decode=True, seq_lens=[L], window=384)
+    xd = {"k": x["k"], "v": x["v"], "lmk": x["lmk"], "q": np.ascontiguousarray(x["q"][:, :, L - 1]),
+          "seq_lens": np.asarray([L], np.int32)}
+    dec = gpu_decode(wd, xd, kc=torch.from_numpy(pre["kc"]).cuda(), bc=torch.from_numpy(pre["bc"]).cuda())
+    for h in range(4):
+        assert set(dec["sel_idx"][0, h]) == set(pre["sel_idx"][0, h, L - 1])
+    np.testing.assert_allclose(dec["o"][0], pre["o"][0, :, L - 1], rtol=0, atol=1e-2)
+
+
+def test_paged_decode_window_matches_contiguous():
+    w = synth.Workload("pagedw", B=3, Hq=4, Hkv=2, d=128, N=2048, K=8, decode=True, seq_lens=[2048, 1000, 70],
+                       window=512)
+    x = synth.make_inputs(w, SEED + 25)
+    ref = gpu_decode(w, x)
+    kp, vp, table = _paginate(w, x, 6)
+    dm = dims_of(w)
+    kpt, vpt = upload(kp, w.io), upload(vp, w.io)
+    tab = torch.from_numpy(table).cuda()
+    q = upload(x["q"], w.io)
+    o = torch.empty_like(q)
+    sel = torch.empty((w.B, w.Hq, w.K), dtype=torch.int32, device="cuda")
+    ws = hils.workspace(dm, hils.OP_DECODE)
+    hils.attn_decode_paged(dm, q, kpt, vpt, tab, torch.from_numpy(x["seq_lens"]).cuda(), ref["kc"], ref["bc"], o, ws,
+                           sel_idx=sel)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(sel.cpu().numpy(), ref["sel_idx"])
+    np.testing.assert_array_equal(o.float().cpu().numpy(), ref["o"])
