@@ -52,18 +52,22 @@ def upload(a, io):
 def prefill_counts(w):
     """Algorithmic work of one prefill pass (2 flops per MAC, exp/log not counted)."""
     S, d, K, C, N = w.S, w.d, w.K, w.C, w.N
+    nw = max(1, w.window // S)                   # chunks of the local window (own included)
     rows_per_head = 0
     score_macs = 0
     intra_macs = 0
+    window_macs = 0
     pairs = 0
     for p in range((N + S - 1) // S):            # query chunk p holds rows p*S .. p*S+S-1
         nrow = min(S, N - p * S)
-        P = min(p, C)
+        P = min(C, max(0, p - nw + 1))           # candidates: the chunks before the window
         n = min(K, P)
         score_macs += nrow * P * d
         pairs += nrow * n
         own = sum(i + 1 for i in range(nrow))    # causal own-chunk keys
-        intra_macs += 2 * d * (nrow * n * S + own)
+        win = own + nrow * S * min(nw - 1, p)    # plus the full window chunks before it
+        intra_macs += 2 * d * (nrow * n * S + win)
+        window_macs += 2 * d * win
         rows_per_head += nrow
     H = w.B * w.Hq
     return {
@@ -71,6 +75,7 @@ def prefill_counts(w):
         "qcal_flops": 4.0 * w.qcal_rank * d * H * rows_per_head,
         "score_flops": 2.0 * score_macs * H,
         "intra_flops": 2.0 * intra_macs * H,
+        "window_flops": 2.0 * window_macs * H,
         "pairs": pairs * H,
     }
 
@@ -92,8 +97,10 @@ def kernel_work(w, cnt, io_bytes=2):
         # per (query, chunk) pair: the gathered query row and the fp16 chunk output; each
         # (batch, KV head, chunk) K/V tile once
         "chunk_attend": ("hbm", cnt["pairs"] * (d * io_bytes + d * 2) + w.B * w.Hkv * w.C * 2 * S * d * io_bytes),
-        # per row: q, the own chunk's K/V (once per head and chunk), the fp16 output slot and the LSE
-        "own_attend": ("hbm", rows * d * io_bytes + w.B * w.Hq * w.N * d * io_bytes * 2 + rows * (d * 2 + 4)),
+        # per row: q, the own chunk's K/V (once per head and chunk), the fp16 output slot and the
+        # LSE; with a local window of several chunks the kernel is bound by its MFMA work
+        "own_attend": (("hbm", rows * d * io_bytes + w.B * w.Hq * w.N * d * io_bytes * 2 + rows * (d * 2 + 4))
+                       if w.window <= S else ("mfma", cnt["window_flops"])),
         # per row: its selected chunk outputs + own output (fp16), their scores, the output row
         "fuse": ("hbm", (cnt["pairs"] + rows) * d * 2 + cnt["pairs"] * 4 + rows * 4 + rows * d * io_bytes),
     }
@@ -179,7 +186,7 @@ def run_prefill(w, steps, warmup, seed):
     t0 = time.time()
     x = synth.make_inputs(w, seed)
     log("prefill inputs generated in %.1fs" % (time.time() - t0))
-    dm = hils.dims(w.B, w.Hq, w.Hkv, w.d, w.N, w.K, S=w.S, qcal_rank=w.qcal_rank, io=w.io)
+    dm = hils.dims(w.B, w.Hq, w.Hkv, w.d, w.N, w.K, S=w.S, qcal_rank=w.qcal_rank, io=w.io, window=w.window)
     q, k, v, lmk = (upload(x[n], w.io) for n in ("q", "k", "v", "lmk"))
     D = upload(x["D"], w.io) if w.qcal_rank else None
     U = upload(x["U"], w.io) if w.qcal_rank else None
@@ -226,7 +233,7 @@ def sampled_parity(w, res, nrows=64, seed=7):
     q, k, v, o, sel, kc, bc = res["tensors"]
     rng = np.random.default_rng(seed)
     rows = [(0, int(rng.integers(w.Hq)), int(rng.integers(w.N))) for _ in range(nrows)]
-    s = oracle.shape(w.B, w.Hq, w.Hkv, w.d, w.N, S=w.S, K=w.K, r=w.qcal_rank)
+    s = oracle.shape(w.B, w.Hq, w.Hkv, w.d, w.N, S=w.S, K=w.K, r=w.qcal_rank, W=w.window)
     # landmarks of the needed heads only
     heads = sorted({h for _, h, _ in rows})
     kc_o = np.zeros((w.B, w.Hq, w.C, w.d))
@@ -254,7 +261,7 @@ def cpu_baseline(w, res, target_s=15.0):
     """The fp64 oracle on the host cores: all-chunk compression + a uniform sample of query rows."""
     import oracle
     x = res["host"]
-    s = oracle.shape(w.B, w.Hq, w.Hkv, w.d, w.N, S=w.S, K=w.K, r=w.qcal_rank)
+    s = oracle.shape(w.B, w.Hq, w.Hkv, w.d, w.N, S=w.S, K=w.K, r=w.qcal_rank, W=w.window)
     cores = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
     t0 = time.time()
     kc_o, bc_o = oracle.compress(s, x["k"], x["lmk"])
@@ -370,7 +377,8 @@ def run_decode(wd, steps, warmup, seed):
     t0 = time.time()
     x = synth.make_inputs(wd, seed)
     log("decode inputs generated in %.1fs" % (time.time() - t0))
-    dm = hils.dims(wd.B, wd.Hq, wd.Hkv, wd.d, wd.N, wd.K, S=wd.S, qcal_rank=wd.qcal_rank, io=wd.io)
+    dm = hils.dims(wd.B, wd.Hq, wd.Hkv, wd.d, wd.N, wd.K, S=wd.S, qcal_rank=wd.qcal_rank, io=wd.io,
+                   window=wd.window)
     kcache, vcache, lmk = (upload(x[n], wd.io) for n in ("k", "v", "lmk"))
     del x["k"], x["v"]
     q = upload(x["q"], wd.io)
@@ -401,18 +409,19 @@ def run_decode(wd, steps, warmup, seed):
         for s_ in stages:
             stages[s_] += r[s_] / steps
     us = sum(stages.values()) * 1e3
-    # algorithmic bytes per step: q, o; k' and b' of every past chunk; the K/V rows of the
-    # union of selected chunks per (sequence, KV head) plus the own chunk
+    # algorithmic bytes per step: q, o; k' and b' of every candidate chunk; the K/V rows of
+    # the union of selected chunks per (sequence, KV head) plus the local window (own chunk)
     seln = sel.cpu().numpy()
     G = wd.Hq // wd.Hkv
+    nw = max(1, wd.window // wd.S)
     kv_bytes = 0
     for b in range(wd.B):
         L = int(x["seq_lens"][b])
-        P = min(wd.C, (L - 1) // wd.S)
+        own = (L - 1) // wd.S
         for g in range(wd.Hkv):
             u = set(seln[b, g * G:(g + 1) * G].ravel().tolist()) - {-1}
-            kv_bytes += (len(u) * wd.S + (L - (L - 1) // wd.S * wd.S)) * wd.d * 2 * 2
-    Ps = [min(wd.C, (int(L) - 1) // wd.S) for L in x["seq_lens"]]
+            kv_bytes += (len(u) * wd.S + (L - own * wd.S) + min(nw - 1, own) * wd.S) * wd.d * 2 * 2
+    Ps = [min(wd.C, max(0, (int(L) - 1) // wd.S - nw + 1)) for L in x["seq_lens"]]
     scan_bytes = sum(P * wd.Hlmk * (wd.d + 1) * 4 for P in Ps)
     total_bytes = scan_bytes + kv_bytes + 2 * 2 * wd.B * wd.Hq * wd.d
     step_gbs = total_bytes / (us * 1e-6) / 1e9
@@ -421,7 +430,7 @@ def run_decode(wd, steps, warmup, seed):
     dense_kv = sum(int(L) for L in x["seq_lens"]) * wd.Hkv * wd.d * 2 * 2
     return {
         "workload": wd.name, "B": wd.B, "Hq": wd.Hq, "Hkv": wd.Hkv, "d": wd.d, "ctx": int(max(x["seq_lens"])),
-        "K": wd.K, "us_per_step": us, "stages_us": {k_: v_ * 1e3 for k_, v_ in stages.items()},
+        "K": wd.K, "window": wd.window, "us_per_step": us, "stages_us": {k_: v_ * 1e3 for k_, v_ in stages.items()},
         "one_off_compress_ms": comp_ms,
         "roofline": {"bound": "hbm", "achieved": scan_gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s",
                      "frac": scan_gbs / PEAK_HBM_GBS, "kernel": "decode_scan",
@@ -432,6 +441,14 @@ def run_decode(wd, steps, warmup, seed):
     }
 
 
+def with_window(w, window):
+    """The workload with a local window of `window` tokens (named apart from the plain one)."""
+    import synth
+    if window <= w.S:
+        return w
+    return synth.scaled(w, window=window, name="%s_w%d" % (w.name, window))
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -440,6 +457,8 @@ def main():
     ap.add_argument("--workload", default="prefill_256k_qcal")
     ap.add_argument("--decode-workload", default="decode_512k")
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--window", type=int, default=0,
+                    help="local window in tokens (a multiple of 64; 0 = the own chunk only) for prefill and decode")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-dense", action="store_true")
     ap.add_argument("--no-parity", action="store_true")
@@ -469,10 +488,10 @@ def main():
         return
     hils.load()
     assert torch.cuda.is_available()
-    w = synth.WORKLOADS[args.workload]
+    w = with_window(synth.WORKLOADS[args.workload], args.window)
     seed = synth.BASE_SEED + 5
     if args.no_prefill:
-        wd = synth.WORKLOADS[args.decode_workload]
+        wd = with_window(synth.WORKLOADS[args.decode_workload], args.window)
         print(json.dumps({"decode": run_decode(wd, max(args.steps, 20), args.warmup, seed + 1)}), flush=True)
         return
     res = run_prefill(w, args.steps, args.warmup, seed)
@@ -488,7 +507,7 @@ def main():
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
         "data": "synthetic (seeded counter-based generator; planted-direction needle chunks and queries)",
         "config": {"workload": w.name, "B": w.B, "Hq": w.Hq, "Hkv": w.Hkv, "d": w.d, "seq_len": w.N, "S": w.S,
-                   "K": w.K, "qcal_rank": w.qcal_rank, "compression": "in the same call"},
+                   "K": w.K, "qcal_rank": w.qcal_rank, "window": w.window, "compression": "in the same call"},
         "roofline": dict(roof[dom], kernel=dom, traffic=measured_traffic(dom, w.name)),
         "stages_ms": res["stages"],
         "stage_rooflines": roof,
@@ -518,7 +537,7 @@ def main():
     res.clear()
     torch.cuda.empty_cache()
     if not args.no_decode:
-        wd = synth.WORKLOADS[args.decode_workload]
+        wd = with_window(synth.WORKLOADS[args.decode_workload], args.window)
         line["decode"] = run_decode(wd, max(args.steps, 20), args.warmup, seed + 1)
     print(json.dumps(line), flush=True)
 

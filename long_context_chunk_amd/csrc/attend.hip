@@ -25,7 +25,8 @@
 //                   sel_idx) by bucket: first into ranges of 64 chunks, then into
 //                   chunks, each pass sorting tiles in LDS and writing whole runs
 //   chunk_attend  : gathered-row MFMA attention per (bucket, 128-row tile)
-//   own_attend    : causal own-chunk (local window) MFMA attention -> slot K and LSE_own
+//   own_attend    : causal own-chunk MFMA attention -> slot K and LSE_own
+//   window_attend : the same over a local window of several chunks (online softmax)
 //   fuse          : softmax over {s_ic} U {LSE_own}, weighted sum of the slots -> o
 #include <algorithm>
 
@@ -463,20 +464,16 @@ __global__ void __launch_bounds__(256, 2) chunk_attend(const IO* __restrict__ q,
 
 // ---------------------------------------------------------------- own_attend
 // One workgroup per (b, KV head, query chunk qc) and group of up to OWN_HEADS of its
-// query heads, two waves per head: rows qc*64 .. qc*64+63 of each head attend their
-// local window -- chunks max(0, qc - nw + 1) .. qc, the own chunk qc causally -- on the
-// MFMA, each chunk's K/V staged once for every head of the group.  Each chunk gives the
-// wave unnormalised outputs against its own maximum; the chunks are merged by rescaling
-// to the running maximum (an online softmax over the window).  The normalised output
-// goes to output slot K of the row and the window's log-sum-exp to lse[row].  With
-// nw = 1 the window is the own chunk alone.
+// query heads, two waves per head: rows qc*64 .. qc*64+63 of each head attend their own
+// chunk causally on the MFMA, against one staging of the chunk's K/V; the normalised
+// output goes to output slot K of the row and its log-sum-exp to lse[row].
 constexpr int OWN_HEADS = 4;
 
 template <typename IO, int D>
 __global__ void __launch_bounds__(128 * OWN_HEADS) own_attend(const IO* __restrict__ q, const IO* __restrict__ k,
                                                               const IO* __restrict__ v, void* __restrict__ partial_v,
                                                               float* __restrict__ lse, int Hq, int Hkv, int N, int K,
-                                                              int NQC, int hpw, int nw) {
+                                                              int NQC, int hpw) {
   constexpr int NT = io_traits<IO>::terms;
   using PT = typename partial_t<IO>::type;
   __shared__ KVTile<IO, D, NT> tile;
@@ -490,41 +487,18 @@ __global__ void __launch_bounds__(128 * OWN_HEADS) own_attend(const IO* __restri
   const bool head_ok = gi < G;
   const int h = kvh * G + min(gi, G - 1);
   const int bh = b * Hq + h;
-  const int64_t kv0 = ((int64_t)b * Hkv + kvh) * N;
+  const int key0 = qc * 64;
+  const int nkeys = min(64, N - key0);
+  stage_kv<IO, D, NT>(tile, k, v, ((int64_t)b * Hkv + kvh) * N + key0, nkeys, tid, blockDim.x);
   const int rl = 32 * (w & 1) + (lane & 31);
-  const int i = qc * 64 + rl;
+  const int i = key0 + rl;
   const bool ok = i < N && head_ok;
   bf16x8_t qb[NT][D / 16];
   load_q_operand<IO, D, NT>(q, ((int64_t)bh * N + (ok ? i : 0)) * D, ok, qb);
-  const int c0 = max(0, qc - nw + 1);
+  __syncthreads();
   f32x16_t oa[D / 32];
   float m, l;
-  for (int c = c0; c <= qc; ++c) {
-    if (c > c0) __syncthreads();  // every wave is done with the previous chunk
-    stage_kv<IO, D, NT>(tile, k, v, kv0 + (int64_t)c * 64, min(64, N - c * 64), tid, blockDim.x);
-    __syncthreads();
-    f32x16_t oc[D / 32];
-    float mc, lc;
-    if (c == qc)
-      wave_chunk_attention<IO, D, NT, true>(tile, qb, rl + 1, oc, mc, lc);  // causal: keys 0..rl
-    else
-      wave_chunk_attention<IO, D, NT, false>(tile, qb, 64, oc, mc, lc);    // a full earlier chunk
-    if (c == c0) {
-#pragma unroll
-      for (int dt = 0; dt < D / 32; ++dt) oa[dt] = oc[dt];
-      m = mc;
-      l = lc;
-    } else {
-      const float mn = fmaxf(m, mc);
-      const float a = __expf(m - mn), bb = __expf(mc - mn);
-#pragma unroll
-      for (int dt = 0; dt < D / 32; ++dt)
-#pragma unroll
-        for (int rr = 0; rr < 16; ++rr) oa[dt][rr] = fmaf(oa[dt][rr], a, oc[dt][rr] * bb);
-      l = fmaf(l, a, lc * bb);
-      m = mn;
-    }
-  }
+  wave_chunk_attention<IO, D, NT, true>(tile, qb, rl + 1, oa, m, l);  // causal: keys 0..rl
   if (!ok) return;
   const int64_t row = (int64_t)bh * N + i;
   const float inv = 1.0f / l;
@@ -545,6 +519,78 @@ __global__ void __launch_bounds__(128 * OWN_HEADS) own_attend(const IO* __restri
       }
     }
   if (hf == 0) lse[row] = m + logf(l);
+}
+
+// ------------------------------------------------------------- window_attend
+// The own chunk widened to a local window of nw > 1 chunks.  One workgroup of 512
+// threads per (b, KV head, query chunk qc) and group of four of its query heads, two
+// waves per head (the waves of heads past the group's last only help staging): rows
+// qc*64 .. qc*64+63 of each head attend chunks max(0, qc - nw + 1) .. qc, the own chunk
+// qc causally, with one online softmax on the MFMA.  Each chunk's K/V is staged once for
+// the four heads, and the next chunk's global loads are issued before the current one
+// is computed.  Output slot K and lse[row] as in own_attend.
+constexpr int WIN_HEADS = 4;
+constexpr int WIN_THREADS = 128 * WIN_HEADS;
+
+template <typename IO, int D>
+__global__ void __launch_bounds__(WIN_THREADS) window_attend(const IO* __restrict__ q, const IO* __restrict__ k,
+                                                             const IO* __restrict__ v, void* __restrict__ partial_v,
+                                                             float* __restrict__ lse, int Hq, int Hkv, int N, int K,
+                                                             int NQC, int nw) {
+  constexpr int NT = io_traits<IO>::terms;
+  using PT = typename partial_t<IO>::type;
+  __shared__ KVTile<IO, D, NT> tile;
+  const int G = Hq / Hkv;
+  const int ngb = (G + WIN_HEADS - 1) / WIN_HEADS;
+  const int gb = blockIdx.x % ngb, rest = blockIdx.x / ngb;
+  const int qc = rest % NQC, bkv = rest / NQC;
+  const int kvh = bkv % Hkv, b = bkv / Hkv;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, hf = lane >> 5;
+  const int gi = gb * WIN_HEADS + (w >> 1);  // this wave pair's query head in the group
+  const bool head_ok = gi < G;
+  const int h = kvh * G + min(gi, G - 1);
+  const int bh = b * Hq + h;
+  const int64_t kv0 = ((int64_t)b * Hkv + kvh) * N;
+  const int rl = 32 * (w & 1) + (lane & 31);
+  const int i = qc * 64 + rl;
+  const bool ok = i < N && head_ok;
+  bf16x8_t qb[NT][D / 16];
+  load_q_operand<IO, D, NT>(q, ((int64_t)bh * N + (ok ? i : 0)) * D, ok, qb);
+  const int c0 = max(0, qc - nw + 1);
+  KVPrefetch<IO, D, NT, WIN_THREADS> pf;
+  pf.load(k, v, kv0 + (int64_t)c0 * 64, min(64, N - c0 * 64), tid);
+  f32x16_t oa[D / 32];
+#pragma unroll
+  for (int dt = 0; dt < D / 32; ++dt) oa[dt] = zero16();
+  float m = -INFINITY, l = 0.f;
+  for (int c = c0; c <= qc; ++c) {
+    if (c > c0) __syncthreads();  // every wave is done with the previous chunk
+    pf.store(tile, min(64, N - c * 64), tid);
+    __syncthreads();
+    if (c < qc) pf.load(k, v, kv0 + (int64_t)(c + 1) * 64, min(64, N - (c + 1) * 64), tid);
+    if (head_ok)  // the own chunk causally (keys 0..rl), earlier chunks whole
+      wave_chunk_online<IO, D, NT, true>(tile, qb, c == qc ? rl + 1 : 64, oa, m, l);
+  }
+  if (!ok) return;
+  const int64_t row = (int64_t)bh * N + i;
+  const float inv = 1.0f / l;
+  PT* dst = reinterpret_cast<PT*>(partial_v) + (row * (K + 1) + K) * D;
+#pragma unroll
+  for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+    for (int g4 = 0; g4 < 4; ++g4) {
+      const int e = 32 * dt + 8 * g4 + 4 * hf;
+      if constexpr (sizeof(PT) == 2) {
+        u32x2_t pk;
+        pk.x = pack_f16x2(oa[dt][4 * g4 + 0] * inv, oa[dt][4 * g4 + 1] * inv);
+        pk.y = pack_f16x2(oa[dt][4 * g4 + 2] * inv, oa[dt][4 * g4 + 3] * inv);
+        *reinterpret_cast<u32x2_t*>(dst + e) = pk;
+      } else {
+        *reinterpret_cast<float4*>(dst + e) = make_float4(oa[dt][4 * g4] * inv, oa[dt][4 * g4 + 1] * inv,
+                                                          oa[dt][4 * g4 + 2] * inv, oa[dt][4 * g4 + 3] * inv);
+      }
+    }
+  if (hf == 0) lse[row] = m * (1.0f / sqrtf((float)D)) + logf(l);
 }
 
 // ---------------------------------------------------------------------- fuse
@@ -723,10 +769,16 @@ static hipError_t launch_attend_t(const Geom& g, const void* q, const void* k, c
   }
   const int NQC = (g.N + 63) / 64;
   float* lse = (float*)(ws + w.lse);
-  const int hpw = std::min(g.G(), OWN_HEADS);
-  const int ngb = (g.G() + hpw - 1) / hpw;
-  hipLaunchKernelGGL((own_attend<IO, D>), dim3(g.B * g.Hkv * NQC * ngb), dim3(128 * hpw), 0, st, (const IO*)q,
-                     (const IO*)k, (const IO*)v, partial, lse, g.Hq, g.Hkv, g.N, g.K, NQC, hpw, g.nw);
+  if (g.nw > 1) {
+    const int ngb = (g.G() + WIN_HEADS - 1) / WIN_HEADS;
+    hipLaunchKernelGGL((window_attend<IO, D>), dim3(g.B * g.Hkv * NQC * ngb), dim3(WIN_THREADS), 0, st,
+                       (const IO*)q, (const IO*)k, (const IO*)v, partial, lse, g.Hq, g.Hkv, g.N, g.K, NQC, g.nw);
+  } else {
+    const int hpw = std::min(g.G(), OWN_HEADS);
+    const int ngb = (g.G() + hpw - 1) / hpw;
+    hipLaunchKernelGGL((own_attend<IO, D>), dim3(g.B * g.Hkv * NQC * ngb), dim3(128 * hpw), 0, st, (const IO*)q,
+                       (const IO*)k, (const IO*)v, partial, lse, g.Hq, g.Hkv, g.N, g.K, NQC, hpw);
+  }
   if (ev) hipEventRecord(ev[2], st);
   const int64_t rows = (int64_t)g.B * g.Hq * g.N;
   const int64_t nwg = (rows + 4 * FZ_ROWS - 1) / (4 * FZ_ROWS);
