@@ -522,18 +522,19 @@ __global__ void __launch_bounds__(128 * OWN_HEADS) own_attend(const IO* __restri
 }
 
 // ------------------------------------------------------------- window_attend
-// The own chunk widened to a local window of nw > 1 chunks.  One workgroup of 512
-// threads per (b, KV head, query chunk qc) and group of four of its query heads, two
-// waves per head (the waves of heads past the group's last only help staging): rows
-// qc*64 .. qc*64+63 of each head attend chunks max(0, qc - nw + 1) .. qc, the own chunk
-// qc causally, with one online softmax on the MFMA.  Each chunk's K/V is staged once for
-// the four heads, and the next chunk's global loads are issued before the current one
-// is computed.  Output slot K and lse[row] as in own_attend.
-constexpr int WIN_HEADS = 4;
+// The own chunk widened to a local window of nw > 1 chunks.  One workgroup of 256
+// threads per (b, KV head, query chunk qc) and pair of its query heads, two waves per
+// head (the waves of a head past the group's last only help staging): rows qc*64 ..
+// qc*64+63 of each head attend chunks max(0, qc - nw + 1) .. qc, the own chunk qc
+// causally, with one online softmax on the MFMA.  Each chunk's K/V is staged once for
+// both heads, and the next chunk's global loads are issued before the current one is
+// computed; two workgroups per CU overlap one's staging with the other's MFMA work.
+// Output slot K and lse[row] as in own_attend.
+constexpr int WIN_HEADS = 2;
 constexpr int WIN_THREADS = 128 * WIN_HEADS;
 
 template <typename IO, int D>
-__global__ void __launch_bounds__(WIN_THREADS) window_attend(const IO* __restrict__ q, const IO* __restrict__ k,
+__global__ void __launch_bounds__(WIN_THREADS, 2) window_attend(const IO* __restrict__ q, const IO* __restrict__ k,
                                                              const IO* __restrict__ v, void* __restrict__ partial_v,
                                                              float* __restrict__ lse, int Hq, int Hkv, int N, int K,
                                                              int NQC, int nw) {
