@@ -425,43 +425,48 @@ __global__ void __launch_bounds__(256, 2) score_threshold(const IO* __restrict__
     store_tile(0);
   }
   __syncthreads();
-  for (int t = 0; t < ntiles; ++t) {
+  // One tile: the two 32-chunk halves' MFMA chains interleaved (independent
+  // accumulators), so each hides the other's latency and the updates of the first half
+  // overlap the second.  MASKED tiles reach chunks >= Pmin, which are not candidates of
+  // every row (the half of a last tile past Pmax holds copies of chunk Pmax - 1 and is
+  // masked out with them).  Masked and unmasked tiles run in separate loops: one loop
+  // with both kinds makes the compiler copy the running top-two at every iteration.
+  auto tile_step = [&](int t, auto masked_tag) {
+    constexpr bool MASKED = decltype(masked_tag)::value;
     const int buf = t & 1;
     const bool more = t + 1 < ntiles;
     if (more) load_tile(t + 1);
-    const bool masked = (t + 1) * ST_TILE > Pmin;  // chunks >= Pmin are not past chunks of every row
+    f32x16_t acc[2] = {zero16(), zero16()};
+#pragma unroll
+    for (int ks = 0; ks <= NKS; ++ks)
+#pragma unroll
+      for (int tt = 0; tt < 2; ++tt) {
+        const bf16x8_t bk = *reinterpret_cast<const bf16x8_t*>(&kt[buf][(32 * tt + n) * LDT + 16 * ks + 8 * hf]);
+        acc[tt] = mfma32(qa[ks], bk, acc[tt]);
+      }
+    // top two per lane (m1 >= m2): m2 = median(m1, m2, v), m1 = median(m1, v, +inf)
 #pragma unroll
     for (int tt = 0; tt < 2; ++tt) {
-      if (t * ST_TILE + 32 * tt >= Pmax) break;
-      const int ch = 32 * tt + n;
-      f32x16_t acc = zero16();
+      const int c = t * ST_TILE + 32 * tt + n;
 #pragma unroll
-      for (int ks = 0; ks <= NKS; ++ks) {
-        const bf16x8_t bk = *reinterpret_cast<const bf16x8_t*>(&kt[buf][ch * LDT + 16 * ks + 8 * hf]);
-        acc = mfma32(qa[ks], bk, acc);
-      }
-      // top two per lane (m1 >= m2): m2 = median(m1, m2, v), m1 = median(m1, v, +inf)
-      if (!masked) {
-#pragma unroll
-        for (int rr = 0; rr < 16; ++rr) {
-          m2[rr] = __builtin_amdgcn_fmed3f(m1[rr], m2[rr], acc[rr]);
-          m1[rr] = __builtin_amdgcn_fmed3f(m1[rr], acc[rr], pinf);
-        }
-      } else {
-        const int c = t * ST_TILE + ch;
-#pragma unroll
-        for (int rr = 0; rr < 16; ++rr) {
+      for (int rr = 0; rr < 16; ++rr) {
+        float v = acc[tt][rr];
+        if constexpr (MASKED) {
           const int rw = r0 + 32 * w + acc_row(rr, hf);
           const int prow = rw < N ? candidate_chunks(rw, C, nw) : 0;
-          const float v = c >= prow ? -INFINITY : acc[rr];
-          m2[rr] = __builtin_amdgcn_fmed3f(m1[rr], m2[rr], v);
-          m1[rr] = __builtin_amdgcn_fmed3f(m1[rr], v, pinf);
+          v = c >= prow ? -INFINITY : v;
         }
+        m2[rr] = __builtin_amdgcn_fmed3f(m1[rr], m2[rr], v);
+        m1[rr] = __builtin_amdgcn_fmed3f(m1[rr], v, pinf);
       }
     }
     if (more) store_tile(buf ^ 1);
     __syncthreads();
-  }
+  };
+  const int t_open = min(ntiles, Pmin / ST_TILE);  // tiles whose chunks are all below Pmin
+  int t = 0;
+  for (; t < t_open; ++t) tile_step(t, std::false_type{});
+  for (; t < ntiles; ++t) tile_step(t, std::true_type{});
   // theta per row: all 16 register rows (two rows each, one per half) at once
   float ninf = -INFINITY;
   asm volatile("" : "+v"(ninf));
