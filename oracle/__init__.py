@@ -48,7 +48,9 @@ def _load():
         lib.hr_attend.argtypes = [sp, i32, i64, vp, vp, vp, vp, i32, vp, vp, i32, vp, vp, vp, vp, i32,
                                   vp, vp, vp, vp, vp, vp, vp]
         lib.hr_dense.argtypes = [sp, i64, vp, vp, vp, vp, i32, vp, vp, i32, vp]
-        for f in (lib.hr_compress, lib.hr_qcal, lib.hr_attend, lib.hr_dense):
+        lib.hr_attend_backward.argtypes = [sp, i64, vp, vp, vp, vp, i32, vp, vp, i32, vp, vp, vp, i32, vp, vp, i32,
+                                           vp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
+        for f in (lib.hr_compress, lib.hr_qcal, lib.hr_attend, lib.hr_dense, lib.hr_attend_backward):
             f.restype = None
         _lib = lib
     return _lib
@@ -157,3 +159,31 @@ def dense(s: Shape, rows_b, rows_h, rows_pos, qrows, k, v):
     _load().hr_dense(ctypes.byref(s), n, rb.ctypes.data, rh.ctypes.data, rp.ctypes.data, qrows.ctypes.data,
                      _dt(qrows), k.ctypes.data, v.ctypes.data, _dt(k), o.ctypes.data)
     return o
+
+
+def attend_backward(s: Shape, rows_b, rows_h, rows_pos, qrows, k, v, kc, bc, lmk, sel_idx, dO, D=None, U=None):
+    """Gradients of attend()'s output o for the given rows, with their selections sel_idx
+    [n, K] held fixed and output gradients dO [n, d].  Returns a dict of dq [n, d], dk, dv
+    [B,Hkv,N,d], dkc [B,Hl,C,d], dbc [B,Hl,C], dlmk [B,Hl,C,d], dD [Hq,r,d], dU [Hq,d,r]."""
+    rb = np.ascontiguousarray(rows_b, np.int32)
+    rh = np.ascontiguousarray(rows_h, np.int32)
+    rp = np.ascontiguousarray(rows_pos, np.int32)
+    n = rb.size
+    qrows = np.ascontiguousarray(qrows).reshape(n, s.d)
+    k, v, lmk = np.ascontiguousarray(k), np.ascontiguousarray(v), np.ascontiguousarray(lmk)
+    kc = np.ascontiguousarray(kc, np.float64)
+    bc = np.ascontiguousarray(bc, np.float64)
+    sel = np.ascontiguousarray(sel_idx, np.int32).reshape(n, s.K)
+    dO = np.ascontiguousarray(dO, np.float64).reshape(n, s.d)
+    C = s.N // s.S
+    out = {"dq": np.empty((n, s.d)), "dk": np.empty((s.B, s.Hkv, s.N, s.d)), "dv": np.empty((s.B, s.Hkv, s.N, s.d)),
+           "dkc": np.empty((s.B, s.Hl, C, s.d)), "dbc": np.empty((s.B, s.Hl, C)), "dlmk": np.empty((s.B, s.Hl, C, s.d)),
+           "dD": np.zeros((s.Hq, max(s.r, 0), s.d)), "dU": np.zeros((s.Hq, s.d, max(s.r, 0)))}
+    wdt = _dt(D) if D is not None else F64
+    _load().hr_attend_backward(ctypes.byref(s), n, rb.ctypes.data, rh.ctypes.data, rp.ctypes.data, qrows.ctypes.data,
+                               _dt(qrows), k.ctypes.data, v.ctypes.data, _dt(k), kc.ctypes.data, bc.ctypes.data,
+                               lmk.ctypes.data, _dt(lmk), _ptr(D), _ptr(U), wdt, sel.ctypes.data, dO.ctypes.data,
+                               out["dq"].ctypes.data, out["dk"].ctypes.data, out["dv"].ctypes.data,
+                               out["dkc"].ctypes.data, out["dbc"].ctypes.data, out["dlmk"].ctypes.data,
+                               out["dD"].ctypes.data if s.r > 0 else None, out["dU"].ctypes.data if s.r > 0 else None)
+    return out

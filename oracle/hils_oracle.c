@@ -316,3 +316,208 @@ void hr_dense(const hr_shape* s, int64_t nrows, const int32_t* row_b, const int3
     free(q);
   }
 }
+
+/*
+ * Backward pass: the gradients of the forward pass above with respect to every
+ * input, for end-to-end retrieval learning (hotpaper.ai abstract and "Key
+ * contributions": the training signal reaches the landmark queries and the
+ * query calibration through the chunk scores; aitrends.kr "Key contributions").
+ * The selection is held fixed (top-K is piecewise constant in its inputs), so
+ * this is the exact gradient wherever the selection does not change.
+ *
+ * For query rows n (row_b/row_h/row_pos, query vectors qrows) with their
+ * selections sel_idx [n, K] (-1 padded; the forward's) and output gradients
+ * dO [n, d], the chain rule runs through the forward's steps in reverse:
+ *   4. fusion:  w = softmax(sigma), o = sum_e w_e o_e  ->
+ *      dsigma_e = w_e (dO.o_e - dO.o), do_e = w_e dO;
+ *   3. each entry's softmax attention (a selected chunk, or the window with its
+ *      exact LSE as the score): logits t_j = tau q.k_j, p = softmax(t) ->
+ *      dt_j = p_j (do_e.v_j - do_e.o_e) (+ dsigma_e p_j for the window, whose
+ *      score is log sum_j exp t_j), dq += tau sum_j dt_j k_j,
+ *      dk_j += tau dt_j q, dv_j += p_j do_e;
+ *   2. chunk score s_c = tau q^.k'_c + b'_c -> dq^ += tau dsigma_c k'_c,
+ *      dk'_c += tau dsigma_c q^, db'_c += dsigma_c;
+ *      Q-Cal q^ = q + U (D q) -> dq += dq^ + D^T (U^T dq^),
+ *      dU += dq^ (D q)^T, dD += (U^T dq^) q^T;
+ *   1. compression (every chunk with a nonzero dk'_c or db'_c):
+ *      a = softmax(z), z_j = tau L_c.k_j, k' = sum a_j k_j, b' = -sum a_j log a_j
+ *      -> da_j = dk'.k_j - db' (log a_j + 1), dz_j = a_j (da_j - sum_m a_m da_m),
+ *      dL_c = tau sum_j dz_j k_j, dk_j += a_j dk'_c + tau dz_j L_c.
+ * Outputs (all overwritten): dq [n, d]; dk, dv [B,Hkv,N,d]; dkc [B,Hl,C,d],
+ * dbc [B,Hl,C]; dlmk [B,Hl,C,d]; dD [Hq,r,d], dU [Hq,d,r] (may be NULL when
+ * r == 0).  Plain serial loops, fp64.
+ */
+void hr_attend_backward(const hr_shape* s, int64_t nrows, const int32_t* row_b, const int32_t* row_h,
+                        const int32_t* row_pos, const void* qrows, int qdt, const void* k, const void* v,
+                        int kvdt, const double* kc, const double* bc, const void* lmk, int ldt, const void* D,
+                        const void* U, int wdt, const int32_t* sel_idx, const double* dO, double* dq,
+                        double* dk, double* dv, double* dkc, double* dbc, double* dlmk, double* dD, double* dU) {
+  const int d = s->d, S = s->S, K = s->K, r = s->r, C = s->N / s->S;
+  const double tau = 1.0 / sqrt((double)d);
+  const int64_t kv_elems = (int64_t)s->B * s->Hkv * s->N * d;
+  const int64_t lm_elems = (int64_t)s->B * s->Hl * C * d;
+  memset(dq, 0, sizeof(double) * nrows * d);
+  memset(dk, 0, sizeof(double) * kv_elems);
+  memset(dv, 0, sizeof(double) * kv_elems);
+  memset(dkc, 0, sizeof(double) * lm_elems);
+  memset(dbc, 0, sizeof(double) * s->B * s->Hl * C);
+  memset(dlmk, 0, sizeof(double) * lm_elems);
+  if (r > 0 && dD) memset(dD, 0, sizeof(double) * s->Hq * r * d);
+  if (r > 0 && dU) memset(dU, 0, sizeof(double) * s->Hq * d * r);
+  double* q = (double*)malloc(sizeof(double) * d);
+  double* qh = (double*)malloc(sizeof(double) * d);
+  double* dqh = (double*)malloc(sizeof(double) * d);
+  double* oe = (double*)malloc(sizeof(double) * d * (K + 1));
+  double* o = (double*)malloc(sizeof(double) * d);
+  double* sig = (double*)malloc(sizeof(double) * (K + 1));
+  int* ent_c = (int*)malloc(sizeof(int) * (K + 1));
+  double* t = (double*)malloc(sizeof(double) * (s->N > 0 ? s->N : 1));
+  double* tr = (double*)malloc(sizeof(double) * (r > 0 ? r : 1));
+  double* ur = (double*)malloc(sizeof(double) * (r > 0 ? r : 1));
+  for (int64_t n = 0; n < nrows; ++n) {
+    const int b = row_b[n], h = row_h[n], pos = row_pos[n];
+    const int kvh = h / (s->Hq / s->Hkv), lm = h / (s->Hq / s->Hl);
+    const int64_t row0 = ((int64_t)b * s->Hkv + kvh) * s->N;
+    const int P = candidates(s, pos);
+    const size_t qsz = qdt == HR_F64 ? 8 : qdt == HR_F32 ? 4 : 2;
+    for (int e = 0; e < d; ++e) q[e] = ld((const char*)qrows + (size_t)n * d * qsz, qdt, e);
+    hr_qcal(s, h, q, D, U, wdt, qh);
+    /* forward, entry by entry: the selected chunks, then the window */
+    int ns = 0;
+    for (int x = 0; x < K; ++x) {
+      const int c = sel_idx[n * K + x];
+      if (c < 0 || c >= P) continue;
+      const double* kp = kc + (((int64_t)b * s->Hl + lm) * C + c) * d;
+      double acc = 0.0;
+      for (int e = 0; e < d; ++e) acc += qh[e] * kp[e];
+      sig[ns] = tau * acc + bc[((int64_t)b * s->Hl + lm) * C + c];
+      attend_range(s, q, k, v, kvdt, row0, c * S, c * S + S, oe + (int64_t)ns * d);
+      ent_c[ns++] = c;
+    }
+    int w0 = (pos / S - (window_chunks(s) - 1)) * S;
+    if (w0 < 0) w0 = 0;
+    sig[ns] = attend_range(s, q, k, v, kvdt, row0, w0, pos + 1, oe + (int64_t)ns * d);
+    double M = -INFINITY, Z = 0.0;
+    for (int x = 0; x <= ns; ++x)
+      if (sig[x] > M) M = sig[x];
+    for (int x = 0; x <= ns; ++x) Z += exp(sig[x] - M);
+    for (int e = 0; e < d; ++e) o[e] = 0.0;
+    for (int x = 0; x <= ns; ++x)
+      for (int e = 0; e < d; ++e) o[e] += exp(sig[x] - M) / Z * oe[(int64_t)x * d + e];
+    /* 4. fusion */
+    const double* g = dO + n * d;
+    double go = 0.0;
+    for (int e = 0; e < d; ++e) go += g[e] * o[e];
+    for (int e = 0; e < d; ++e) dqh[e] = 0.0;
+    double* dqn = dq + n * d;
+    for (int x = 0; x <= ns; ++x) {
+      const double w = exp(sig[x] - M) / Z;
+      const double* ox = oe + (int64_t)x * d;
+      double gx = 0.0;
+      for (int e = 0; e < d; ++e) gx += g[e] * ox[e];
+      const double dsig = w * (gx - go);
+      /* 3. the entry's softmax attention; do_e = w g, do_e.o_e = w gx */
+      const int window = x == ns;
+      const int j0 = window ? w0 : ent_c[x] * S, j1 = window ? pos + 1 : ent_c[x] * S + S;
+      double m = -INFINITY;
+      for (int j = j0; j < j1; ++j) {
+        double acc = 0.0;
+        for (int e = 0; e < d; ++e) acc += q[e] * ld(k, kvdt, (row0 + j) * d + e);
+        t[j - j0] = tau * acc;
+        if (t[j - j0] > m) m = t[j - j0];
+      }
+      double l = 0.0;
+      for (int j = j0; j < j1; ++j) l += exp(t[j - j0] - m);
+      for (int j = j0; j < j1; ++j) {
+        const double p = exp(t[j - j0] - m) / l;
+        double gv = 0.0;
+        for (int e = 0; e < d; ++e) gv += g[e] * ld(v, kvdt, (row0 + j) * d + e);
+        double dt = p * (w * gv - w * gx);
+        if (window) dt += dsig * p;
+        for (int e = 0; e < d; ++e) {
+          dqn[e] += tau * dt * ld(k, kvdt, (row0 + j) * d + e);
+          dk[(row0 + j) * d + e] += tau * dt * q[e];
+          dv[(row0 + j) * d + e] += p * w * g[e];
+        }
+      }
+      /* 2. the chunk score */
+      if (!window) {
+        const int64_t ci = ((int64_t)b * s->Hl + lm) * C + ent_c[x];
+        for (int e = 0; e < d; ++e) {
+          dqh[e] += tau * dsig * kc[ci * d + e];
+          dkc[ci * d + e] += tau * dsig * qh[e];
+        }
+        dbc[ci] += dsig;
+      }
+    }
+    /* Q-Cal */
+    for (int e = 0; e < d; ++e) dqn[e] += dqh[e];
+    if (r > 0 && D && U) {
+      for (int a = 0; a < r; ++a) {
+        double acc = 0.0, acc2 = 0.0;
+        for (int e = 0; e < d; ++e) {
+          acc += ld(D, wdt, ((int64_t)h * r + a) * d + e) * q[e];
+          acc2 += ld(U, wdt, ((int64_t)h * d + e) * r + a) * dqh[e];
+        }
+        tr[a] = acc;   /* D q */
+        ur[a] = acc2;  /* U^T dq^ */
+      }
+      for (int e = 0; e < d; ++e)
+        for (int a = 0; a < r; ++a) {
+          dqn[e] += ld(D, wdt, ((int64_t)h * r + a) * d + e) * ur[a];
+          if (dU) dU[((int64_t)h * d + e) * r + a] += dqh[e] * tr[a];
+          if (dD) dD[((int64_t)h * r + a) * d + e] += ur[a] * q[e];
+        }
+    }
+  }
+  /* 1. compression */
+  double* z = (double*)malloc(sizeof(double) * S);
+  double* a = (double*)malloc(sizeof(double) * S);
+  double* da = (double*)malloc(sizeof(double) * S);
+  for (int b = 0; b < s->B; ++b)
+    for (int l = 0; l < s->Hl; ++l)
+      for (int c = 0; c < C; ++c) {
+        const int64_t ci = ((int64_t)b * s->Hl + l) * C + c;
+        int nz = dbc[ci] != 0.0;
+        for (int e = 0; e < d && !nz; ++e) nz = dkc[ci * d + e] != 0.0;
+        if (!nz) continue;
+        const int kvh = l / (s->Hl / s->Hkv);
+        const int64_t kb = ((int64_t)b * s->Hkv + kvh) * s->N + (int64_t)c * S;
+        double m = -INFINITY, Zc = 0.0;
+        for (int j = 0; j < S; ++j) {
+          double acc = 0.0;
+          for (int e = 0; e < d; ++e) acc += ld(lmk, ldt, ci * d + e) * ld(k, kvdt, (kb + j) * d + e);
+          z[j] = tau * acc;
+          if (z[j] > m) m = z[j];
+        }
+        for (int j = 0; j < S; ++j) Zc += exp(z[j] - m);
+        double sda = 0.0;
+        for (int j = 0; j < S; ++j) {
+          a[j] = exp(z[j] - m) / Zc;
+          double acc = 0.0;
+          for (int e = 0; e < d; ++e) acc += dkc[ci * d + e] * ld(k, kvdt, (kb + j) * d + e);
+          da[j] = acc - (a[j] > 0.0 ? dbc[ci] * (log(a[j]) + 1.0) : 0.0);
+          sda += a[j] * da[j];
+        }
+        for (int j = 0; j < S; ++j) {
+          const double dz = a[j] * (da[j] - sda);
+          for (int e = 0; e < d; ++e) {
+            dlmk[ci * d + e] += tau * dz * ld(k, kvdt, (kb + j) * d + e);
+            dk[(kb + j) * d + e] += a[j] * dkc[ci * d + e] + tau * dz * ld(lmk, ldt, ci * d + e);
+          }
+        }
+      }
+  free(z);
+  free(a);
+  free(da);
+  free(q);
+  free(qh);
+  free(dqh);
+  free(oe);
+  free(o);
+  free(sig);
+  free(ent_c);
+  free(t);
+  free(tr);
+  free(ur);
+}

@@ -68,6 +68,18 @@ void hr_attend(const hr_shape* s, int mode, int64_t nrows, const int32_t* row_b,
                const void* D, const void* U, int wdt, const int32_t* sel_in, double* o,
                int32_t* sel_idx, double* sel_score, double* gap, double* lse_own, int32_t* nsel);
 
+/* Backward pass (gradients of hr_attend's output o with the selection held
+ * fixed): given the rows of hr_attend, their selections sel_idx [n, K] and the
+ * output gradients dO [n, d] (fp64), writes dq [n, d]; dk, dv [B,Hkv,N,d];
+ * dkc [B,Hl,C,d], dbc [B,Hl,C] (gradients of k', b'); dlmk [B,Hl,C,d];
+ * dD [Hq,r,d], dU [Hq,d,r] (NULL allowed when r == 0).  Surrogate scores only;
+ * kc/bc are the forward's compression of k and lmk. */
+void hr_attend_backward(const hr_shape* s, int64_t nrows, const int32_t* row_b, const int32_t* row_h,
+                        const int32_t* row_pos, const void* qrows, int qdt, const void* k, const void* v,
+                        int kvdt, const double* kc, const double* bc, const void* lmk, int ldt, const void* D,
+                        const void* U, int wdt, const int32_t* sel_idx, const double* dO, double* dq,
+                        double* dk, double* dv, double* dkc, double* dbc, double* dlmk, double* dD, double* dU);
+
 /* Dense causal attention of nrows queries (as in hr_attend) over keys
  * 0..row_pos[n] of their KV head: o [nrows,d]. */
 void hr_dense(const hr_shape* s, int64_t nrows, const int32_t* row_b, const int32_t* row_h,
