@@ -73,7 +73,7 @@ enum {
 };
 
 /* op codes of hils_workspace_bytes */
-enum { HILS_OP_COMPRESS = 0, HILS_OP_SCORE_TOPK = 1, HILS_OP_PREFILL = 2, HILS_OP_DECODE = 3 };
+enum { HILS_OP_COMPRESS = 0, HILS_OP_SCORE_TOPK = 1, HILS_OP_PREFILL = 2, HILS_OP_DECODE = 3, HILS_OP_BACKWARD = 4 };
 
 typedef struct {
   int32_t B;         /* batch (sequences)                                              */
@@ -200,6 +200,27 @@ int hils_attn_decode_paged(const hils_dims_t* dims, const void* q, const void* k
                            const int32_t* block_table, int32_t max_blocks, int32_t num_pages, const int32_t* seq_lens,
                            const float* kc, const float* bc, const void* qcal_D, const void* qcal_U,
                            int32_t* sel_idx_out, void* o, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * Backward pass of hils_attn_prefill (end-to-end retrieval learning: the training
+ * signal reaches the landmark queries and the query calibration through the chunk
+ * scores; hotpaper.ai abstract and "Key contributions", aitrends.kr "Key
+ * contributions").  Given the forward's inputs, its compressed keys kc, its
+ * selection (sel_idx, sel_score: the forward's sel_idx_out / sel_score_out), its
+ * output o and the output gradient dO [B,Hq,N,d], writes the gradients of
+ * sum(o * dO) with the selection held fixed (top-K is piecewise constant):
+ *   dq [B,Hq,N,d], dk, dv [B,Hkv,N,d], dlmk [B,Hlmk,C,d] (landmark queries, through
+ *   k' and b'), dD [Hq,r,d], dU [Hq,d,r] (Q-Cal; may be NULL when qcal_rank == 0).
+ * bf16 I/O only (HILS_E_UNSUPPORTED otherwise); gradients are accumulated in fp32
+ * in the workspace (hils_workspace_bytes(dims, HILS_OP_BACKWARD)) and rounded to
+ * bf16 once; float atomics make the low bits of dq, dk and dv depend on timing.
+ * lmk_q, kc and dlmk may be NULL when N < S.  Same limits as hils_attn_prefill.
+ * Asynchronous on `stream`.
+ */
+int hils_attn_prefill_backward(const hils_dims_t* dims, const void* q, const void* k, const void* v, const void* lmk_q,
+                               const float* kc, const void* qcal_D, const void* qcal_U, const int32_t* sel_idx,
+                               const float* sel_score, const void* o, const void* dO, void* dq, void* dk, void* dv,
+                               void* dlmk, void* dD, void* dU, void* ws, size_t ws_bytes, void* stream);
 
 /*
  * Dense causal attention, the baseline the pages measure the sparse method

@@ -118,6 +118,9 @@ size_t hils_workspace_bytes(const hils_dims_t* dims, int op) {
     case HILS_OP_PREFILL:
       if (check_prefill(g) != HILS_OK) return (size_t)-1;
       return prefill_ws(g).total;
+    case HILS_OP_BACKWARD:
+      if (check_prefill(g) != HILS_OK) return (size_t)-1;
+      return hils::backward_workspace_bytes(g);
     case HILS_OP_DECODE:
       if (g.C() > 16384) {
         fail(HILS_E_UNSUPPORTED, "decode needs N/S <= 16384 (N=%d)", g.N);
@@ -338,6 +341,31 @@ int hils_dense_attention(const hils_dims_t* dims, const void* q, const void* k, 
     return fail(HILS_E_UNSUPPORTED, "B*Hq*ceil(N/128) must fit a 31-bit grid");
   const hipError_t e = hils::launch_dense(g, q, k, v, o, (hipStream_t)stream);
   if (e != hipSuccess) return hip_fail(e, "hils_dense_attention");
+  g_err[0] = 0;
+  return HILS_OK;
+}
+
+int hils_attn_prefill_backward(const hils_dims_t* dims, const void* q, const void* k, const void* v, const void* lmk_q,
+                               const float* kc, const void* qcal_D, const void* qcal_U, const int32_t* sel_idx,
+                               const float* sel_score, const void* o, const void* dO, void* dq, void* dk, void* dv,
+                               void* dlmk, void* dD, void* dU, void* ws, size_t ws_bytes, void* stream) {
+  hils::Geom g;
+  int rc = check_dims(dims, g);
+  if (rc) return rc;
+  if ((rc = check_prefill(g))) return rc;
+  if (g.io != HILS_BF16) return fail(HILS_E_UNSUPPORTED, "the backward pass needs bf16 I/O");
+  if (!q || !k || !v || !o || !dO || !dq || !dk || !dv || !sel_idx || !sel_score)
+    return fail(HILS_E_INVAL, "q, k, v, o, dO, dq, dk, dv, sel_idx and sel_score must be non-NULL");
+  if (g.C() > 0 && (!lmk_q || !kc || !dlmk))
+    return fail(HILS_E_INVAL, "lmk_q, kc and dlmk must be non-NULL when N >= S");
+  if (g.r > 0 && (!qcal_D || !qcal_U || !dD || !dU))
+    return fail(HILS_E_INVAL, "qcal_D, qcal_U, dD and dU must be non-NULL when qcal_rank > 0");
+  const size_t need = hils::backward_workspace_bytes(g);
+  if (ws_bytes < need || (need > 0 && !ws))
+    return fail(HILS_E_WORKSPACE, "workspace of %zu bytes needed, %zu given", need, ws_bytes);
+  const hils::BwdArgs a{q, k, v, lmk_q, qcal_D, qcal_U, o, dO, kc, sel_score, sel_idx, dq, dk, dv, dlmk, dD, dU};
+  const hipError_t e = hils::launch_backward(g, a, ws, ws_bytes, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "hils_attn_prefill_backward");
   g_err[0] = 0;
   return HILS_OK;
 }

@@ -39,6 +39,7 @@ namespace hils {
 constexpr int AT_ROWS = 128;        // gathered rows per chunk_attend tile (4 waves x 32)
 constexpr int AT_TILES = 8;         // tiles per chunk_attend work item (one K/V staging)
 constexpr int ITEM_ROWS = AT_ROWS * AT_TILES;
+static_assert(ITEM_ROWS == BUCKET_ITEM_ROWS, "one work-item size for every user of the bucketing");
 constexpr int HIST_SLICE = 1 << 17; // selection entries per bucket_count / bucket_part1 workgroup
 constexpr int P2_SPLIT = 4;         // workgroups sharing one 64-chunk range in bucket_part2
 constexpr int BK_TILE = 8192;       // entries sorted in LDS at a time by bucket_part1/2
@@ -721,6 +722,40 @@ __global__ void __launch_bounds__(256) fuse(const float* __restrict__ sel_score,
   }
 }
 
+// ------------------------------------------------------- shared bucketing launch
+void launch_bucket_pairs(const Geom& g, const int32_t* sel, BucketBufs bb, hipStream_t st) {
+  const int C = g.C();
+  const int nbk = g.B * g.Hq * C;
+  // zero counts and cursors (contiguous) with a kernel: no memset nodes in captured streams
+  const int64_t nz = (int64_t)(bb.boff - bb.counts);
+  if (nz > 0)
+    hipLaunchKernelGGL(zero_u32, dim3((unsigned)std::min<int64_t>((nz + 255) / 256, 4096)), dim3(256), 0, st,
+                       bb.counts, nz);
+  if (nbk == 0) return;
+  const int64_t group_len = (int64_t)g.N * g.K;
+  const int spg = (int)((group_len + HIST_SLICE - 1) / HIST_SLICE);
+  const int ngrp = g.B * g.Hq;
+  hipLaunchKernelGGL(bucket_count, dim3(ngrp * spg), dim3(256), 0, st, sel, bb.counts, group_len, spg, C);
+  hipLaunchKernelGGL(bucket_scan, dim3(1), dim3(1024), 0, st, bb.counts, bb.boff, bb.toff, nbk);
+  const int nrg = (C + (1 << FINE_BITS) - 1) >> FINE_BITS;
+  hipLaunchKernelGGL(bucket_part1, dim3(ngrp * spg), dim3(256), 0, st, sel, bb.boff, bb.cursor, bb.tmp, group_len,
+                     spg, C, nrg);
+  hipLaunchKernelGGL(bucket_part2, dim3(ngrp * nrg * P2_SPLIT), dim3(256), 0, st, (const uint32_t*)bb.tmp, bb.boff,
+                     bb.counts, bb.pairs, group_len, C, nrg);
+}
+
+int64_t bucket_items_bound(const Geom& g) {
+  // rows of query chunk p (64 of them, fewer in the tail) select min(K, p - nw + 1, C) chunks each
+  const int C = g.C();
+  int64_t pairs_total = 0;
+  for (int p = 0; p * 64 < g.N; ++p)
+    pairs_total += (int64_t)std::min(64, g.N - p * 64) * std::min(g.K, std::min(C, std::max(0, p - g.nw + 1)));
+  pairs_total *= (int64_t)g.B * g.Hq;
+  if (pairs_total == 0) return 0;
+  // work items <= total pairs / ITEM_ROWS + number of buckets (the exact count is read on the device)
+  return std::min<int64_t>((pairs_total + ITEM_ROWS - 1) / ITEM_ROWS + (int64_t)g.B * g.Hq * C, 0x7fffffff);
+}
+
 // ------------------------------------------------------------------ launcher
 template <typename IO, int D>
 static hipError_t launch_attend_t(const Geom& g, const void* q, const void* k, const void* v, const int32_t* sel,
@@ -734,33 +769,12 @@ static hipError_t launch_attend_t(const Geom& g, const void* q, const void* k, c
   void* partial = ws + w.partial;
   const int C = g.C();
   const int nbk = g.B * g.Hq * C;
-  // zero counts and cursors (contiguous) with a kernel: no memset nodes in captured streams
-  const int64_t nz = (int64_t)(w.boff - w.counts) / 4;
-  if (nz > 0)
-    hipLaunchKernelGGL(zero_u32, dim3((unsigned)std::min<int64_t>((nz + 255) / 256, 4096)), dim3(256), 0, st, counts,
-                       nz);
   if (nbk > 0) {
-    const int64_t group_len = (int64_t)g.N * g.K;
-    const int spg = (int)((group_len + HIST_SLICE - 1) / HIST_SLICE);
-    const int ngrp = g.B * g.Hq;
-    hipLaunchKernelGGL(bucket_count, dim3(ngrp * spg), dim3(256), 0, st, sel, counts, group_len, spg, C);
-    hipLaunchKernelGGL(bucket_scan, dim3(1), dim3(1024), 0, st, counts, boff, toff, nbk);
     // the first pass's output lives in the (not yet written) partial-output region
-    const int nrg = (C + (1 << FINE_BITS) - 1) >> FINE_BITS;
-    uint32_t* tmp = (uint32_t*)partial;
-    hipLaunchKernelGGL(bucket_part1, dim3(ngrp * spg), dim3(256), 0, st, sel, boff, cursor, tmp, group_len, spg, C,
-                       nrg);
-    hipLaunchKernelGGL(bucket_part2, dim3(ngrp * nrg * P2_SPLIT), dim3(256), 0, st, (const uint32_t*)tmp, boff,
-                       counts, pairs, group_len, C, nrg);
+    launch_bucket_pairs(g, sel, BucketBufs{counts, cursor, boff, toff, pairs, (uint32_t*)partial}, st);
     if (ev) hipEventRecord(ev[0], st);
-    // work items <= total pairs / ITEM_ROWS + number of buckets (host bound; the exact count is read on the device)
-    // rows of query chunk p (64 of them, fewer in the tail) select min(K, p - nw + 1, C) chunks each
-    int64_t pairs_total = 0;
-    for (int p = 0; p * 64 < g.N; ++p)
-      pairs_total += (int64_t)std::min(64, g.N - p * 64) * std::min(g.K, std::min(C, std::max(0, p - g.nw + 1)));
-    pairs_total *= (int64_t)g.B * g.Hq;
-    const int64_t items = std::min<int64_t>((pairs_total + ITEM_ROWS - 1) / ITEM_ROWS + nbk, 0x7fffffff);
-    if (pairs_total > 0)
+    const int64_t items = bucket_items_bound(g);
+    if (items > 0)
       hipLaunchKernelGGL((chunk_attend<IO, D>), dim3((unsigned)items), dim3(256), 0, st, (const IO*)q, (const IO*)k,
                          (const IO*)v, pairs, boff, toff, partial, ws + w.sink, g.Hq, g.Hkv, g.N, C, g.K, nbk);
     if (ev) hipEventRecord(ev[1], st);

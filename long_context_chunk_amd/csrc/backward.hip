@@ -1,0 +1,774 @@
+// Backward pass of the prefill forward: gradients of the output with respect to q, k, v,
+// the landmark queries and the Q-Cal projections, with the selection held fixed (top-K is
+// piecewise constant).  End-to-end retrieval learning: the training signal reaches the
+// landmark queries and the query calibration through the chunk scores (hotpaper.ai
+// abstract and "Key contributions"; aitrends.kr "Key contributions").
+//
+// Per query row i with output gradient g = dO_i, forward output o_i and fusion
+// weights w_e = exp(sigma_e - Lambda_i), Lambda_i = log sum_e exp(sigma_e):
+//   selected chunk c (score s_ic = tau q^.k'_c + b'_c, chunk softmax P over its keys):
+//     dP'_j = g.v_j,  e_c = sum_j P_j dP'_j (= g.o_ic),  dsigma_c = w_c (e_c - g.o_i),
+//     dS_j = P_j w_c (dP'_j - e_c)     (gradient of the logit tau q.k_j)
+//   window (score = its exact LSE, softmax P over the window's keys):
+//     dS_j = P_j w_w (dP'_j - g.o_i)   (the LSE's own gradient folded in)
+//   dq += tau sum_j dS_j k_j,  dk_j += tau dS_j q,  dv_j += P_j w g;
+//   scores: dq^ += tau dsigma_c k'_c,  dk'_c += tau dsigma_c q^,  db'_c += dsigma_c;
+//   Q-Cal: dq += dq^ + D^T (U^T dq^),  dU += dq^ (D q)^T,  dD += (U^T dq^) q^T;
+//   compression: da_j = dk'.k_j - db' (log a_j + 1), dz_j = a_j (da_j - sum a da),
+//     dL_c = tau sum_j dz_j k_j,  dk_j += a_j dk'_c + tau dz_j L_c.
+//
+// Kernels, in launch order (bf16 I/O, fp32 accumulation in the workspace):
+//   bwd_prep      q^ rows (fp32) and zeroed accumulators
+//   bwd_window    per (b, KV head, query chunk, pair of heads): the window's LSE, the
+//                 row's fusion normaliser Lambda_i and g.o_i, then the window's
+//                 gradients on the MFMA (dq stored, dk/dv added atomically)
+//   bucketing     the forward's (b, head, chunk) bucketing of the selection pairs
+//   bwd_pairs     per bucket work item: the chunk's K/V staged once, 32 gathered rows
+//                 per wave: S, dP' on the MFMA, dsigma per pair, dq (atomic), then dk/dv
+//                 over the tile's 128 rows on the MFMA from transposed LDS tiles; dk'/db'
+//   bwd_rows      per row: dq^ from the pairs' dsigma and k', Q-Cal backward
+//   bwd_compress  per (b, KV head, chunk): the landmark compression's backward
+//   bwd_convert   fp32 accumulators to the output dtype
+#include <algorithm>
+
+#include "attn_tile.h"
+#include "hils_common.h"
+#include "kernels.h"
+
+namespace hils {
+
+namespace {
+
+constexpr int BW_ROWS = 128;  // rows per tile: 4 waves x 32
+constexpr int LDP = 64 + 8;   // bf16 row stride of the [row][key] P and dS tiles
+
+struct BwdWs {
+  size_t qh, dq, dk, dv, dkc, dbc, lam, dd, dsig, dD, dU, counts, cursor, boff, toff, pairs, tmp, total;
+};
+size_t alb(size_t x) { return (x + 255) / 256 * 256; }
+BwdWs bwd_ws(const Geom& g) {
+  BwdWs w;
+  const size_t rows = (size_t)g.B * g.Hq * g.N, kvrows = (size_t)g.B * g.Hkv * g.N;
+  const size_t lrows = (size_t)g.B * g.Hl * g.C(), nbk = (size_t)g.B * g.Hq * g.C();
+  const size_t ent = rows * g.K, r = (size_t)g.r;
+  size_t off = 0;
+  auto take = [&](size_t& f, size_t bytes) {
+    f = off;
+    off += alb(bytes);
+  };
+  take(w.qh, rows * g.d * 4);
+  take(w.dq, rows * g.d * 4);
+  take(w.dk, kvrows * g.d * 4);  // dk .. dU are zeroed together: keep them contiguous
+  take(w.dv, kvrows * g.d * 4);
+  take(w.dkc, lrows * g.d * 4);
+  take(w.dbc, lrows * 4);
+  take(w.dD, (size_t)g.Hq * r * g.d * 4);
+  take(w.dU, (size_t)g.Hq * g.d * r * 4);
+  take(w.lam, rows * 4);
+  take(w.dd, rows * 4);
+  take(w.dsig, ent * 4);
+  take(w.counts, nbk * 4);  // counts and cursor contiguous (zeroed together)
+  take(w.cursor, nbk * 4);
+  take(w.boff, (nbk + 1) * 4);
+  take(w.toff, (nbk + 1) * 4);
+  take(w.pairs, ent * 4);
+  take(w.tmp, ent * 4);
+  w.total = off;
+  return w;
+}
+
+HILS_DEV float wave_sum_f(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
+  return v;
+}
+
+__global__ void __launch_bounds__(256) bwd_zero(float* p, int64_t n) {
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256) p[i] = 0.f;
+}
+
+// q^ = q + U_h (D_h q) of every row (fp32), one wave per row, lanes over the head dims;
+// the rank-r intermediate t = D_h q goes through LDS.
+template <int D>
+__global__ void __launch_bounds__(256) bwd_prep(const bf16_t* __restrict__ q, const bf16_t* __restrict__ Dw,
+                                                const bf16_t* __restrict__ Uw, float* __restrict__ qh, int Hq, int N,
+                                                int r, int64_t rows) {
+  constexpr int EPL = D / 64;  // dims per lane
+  __shared__ float tq[4][32];
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  for (int64_t row = (int64_t)blockIdx.x * 4 + w; row < rows; row += (int64_t)gridDim.x * 4) {
+    const int h = (int)((row / N) % Hq);
+    float x[EPL];
+#pragma unroll
+    for (int u = 0; u < EPL; ++u) x[u] = bf16_to_f32(q[row * D + lane + 64 * u].bits);
+    float out[EPL];
+#pragma unroll
+    for (int u = 0; u < EPL; ++u) out[u] = x[u];
+    if (r > 0) {
+      for (int a = 0; a < r; ++a) {
+        float p = 0.f;
+#pragma unroll
+        for (int u = 0; u < EPL; ++u) p = fmaf(bf16_to_f32(Dw[((int64_t)h * r + a) * D + lane + 64 * u].bits), x[u], p);
+        p = wave_sum_f(p);
+        if (lane == 0) tq[w][a] = p;
+      }
+      __builtin_amdgcn_wave_barrier();
+#pragma unroll
+      for (int u = 0; u < EPL; ++u) {
+        const int e = lane + 64 * u;
+        float acc = 0.f;
+        for (int a = 0; a < r; ++a) acc = fmaf(bf16_to_f32(Uw[((int64_t)h * D + e) * r + a].bits), tq[w][a], acc);
+        out[u] += acc;
+      }
+      __builtin_amdgcn_wave_barrier();
+    }
+#pragma unroll
+    for (int u = 0; u < EPL; ++u) qh[row * D + lane + 64 * u] = out[u];
+  }
+}
+
+// --------------------------------------------------------- shared tile gradients
+// LDS of one gradient tile: the chunk's K/V, and for the tile's 128 rows their q and
+// g (bf16, [row][dim]) and P*w and dS (bf16, [row][key]) for the dk/dv products.
+template <int D>
+struct GradLds {
+  static constexpr int LDR = D + 8;
+  KVTile<bf16_t, D, 1> kv;
+  uint16_t qt[BW_ROWS * LDR];
+  uint16_t gt[BW_ROWS * LDR];
+  uint16_t pt[BW_ROWS * LDP];
+  uint16_t st[BW_ROWS * LDP];
+};
+
+// S^T = K Q^T style product of the staged chunk (plane = K or V, row stride LD) with a
+// wave's 32 rows given as B operands: x[tt][rr] = row n . key (32 tt + acc_row(rr, hf)).
+template <int D, int LD>
+HILS_DEV void keys_dot_rows(const uint16_t* plane, const bf16x8_t (&rb)[D / 16], f32x16_t (&x)[2]) {
+  const int lane = threadIdx.x & 63, hf = lane >> 5;
+#pragma unroll
+  for (int tt = 0; tt < 2; ++tt) {
+    x[tt] = zero16();
+    const int key = 32 * tt + (lane & 31);
+#pragma unroll
+    for (int ks = 0; ks < D / 16; ++ks) x[tt] = mfma32(lds_op16(&plane[key * LD + 16 * ks + 8 * hf]), rb[ks], x[tt]);
+  }
+}
+
+// The key-indexed registers x (layout of keys_dot_rows) as B operands over the keys.
+HILS_DEV void keys_to_b(const f32x16_t (&x)[2], bf16x8_t (&b)[4]) {
+#pragma unroll
+  for (int ks2 = 0; ks2 < 4; ++ks2) {
+    float pv[8];
+#pragma unroll
+    for (int mm = 0; mm < 8; ++mm) pv[mm] = x[ks2 >> 1][8 * (ks2 & 1) + mm];
+    u32x4_t t[1];
+    split8<1>(pv, t);
+    b[ks2] = __builtin_bit_cast(bf16x8_t, t[0]);
+  }
+}
+
+// Writes a wave's key-indexed registers (bf16) to its 32 rows of a [row][key] tile.
+HILS_DEV void keys_to_lds(const f32x16_t (&x)[2], uint16_t* tile, int row) {
+  const int hf = (threadIdx.x & 63) >> 5;
+#pragma unroll
+  for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+    for (int g4 = 0; g4 < 4; ++g4) {
+      u32x2_t pk;
+      pk.x = pack_bf16x2(x[tt][4 * g4], x[tt][4 * g4 + 1]);
+      pk.y = pack_bf16x2(x[tt][4 * g4 + 2], x[tt][4 * g4 + 3]);
+      *reinterpret_cast<u32x2_t*>(&tile[row * LDP + 32 * tt + 8 * g4 + 4 * hf]) = pk;
+    }
+}
+
+// A wave's 32 rows of B operands (D/16 x 8 dims per lane) to its rows of a [row][dim] tile.
+template <int D>
+HILS_DEV void rows_to_lds(const bf16x8_t (&rb)[D / 16], uint16_t* tile, int row) {
+  const int hf = (threadIdx.x & 63) >> 5;
+#pragma unroll
+  for (int ks = 0; ks < D / 16; ++ks)
+    *reinterpret_cast<bf16x8_t*>(&tile[row * GradLds<D>::LDR + 16 * ks + 8 * hf]) = rb[ks];
+}
+
+// dq^T += K^T dS^T for the wave's rows: dq[dt][rr] = dim (32 dt + acc_row(rr, hf)) of row n.
+template <int D>
+HILS_DEV void dq_from_ds(const KVTile<bf16_t, D, 1>& kv, const f32x16_t (&ds)[2], f32x16_t (&dq)[D / 32]) {
+  constexpr int LDK = KVTile<bf16_t, D, 1>::LDK;
+  const int lane = threadIdx.x & 63;
+  bf16x8_t db[4];
+  keys_to_b(ds, db);
+#pragma unroll
+  for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+    for (int ks2 = 0; ks2 < 4; ++ks2) dq[dt] = mfma32(vt_operand<LDK>(kv.k[0], dt, ks2, lane), db[ks2], dq[dt]);
+}
+
+// dv = sum_rows (P w)^T g and dk = tau sum_rows dS^T q over the tile's 128 rows (all four
+// waves' rows, from the LDS tiles), added to the fp32 accumulators of the chunk's keys
+// (row kvrow0 + key).  Each wave takes a quarter of the (kind, key tile, dim tile) blocks.
+template <int D>
+HILS_DEV void dkdv_from_tiles(const GradLds<D>& L, float* __restrict__ dk, float* __restrict__ dv, int64_t kvrow0,
+                              int nkeys, float tau) {
+  constexpr int NDT = D / 32, NBLK = 2 * 2 * NDT;
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, hf = lane >> 5;
+  for (int blk = w; blk < NBLK; blk += 4) {
+    const bool isk = blk >= 2 * NDT;
+    const int kt = (blk % (2 * NDT)) / NDT, dt = blk % NDT;
+    const uint16_t* a_tile = isk ? L.st : L.pt;
+    const uint16_t* b_tile = isk ? L.qt : L.gt;
+    f32x16_t acc = zero16();
+#pragma unroll
+    for (int ks2 = 0; ks2 < BW_ROWS / 16; ++ks2)
+      acc = mfma32(vt_operand<LDP>(a_tile, kt, ks2, lane), vt_operand<GradLds<D>::LDR>(b_tile, dt, ks2, lane), acc);
+    float* dst = isk ? dk : dv;
+    const float sc = isk ? tau : 1.0f;
+    const int e = 32 * dt + (lane & 31);
+#pragma unroll
+    for (int rr = 0; rr < 16; ++rr) {
+      const int key = 32 * kt + acc_row(rr, hf);
+      if (key < nkeys) atomicAdd(&dst[(kvrow0 + key) * D + e], acc[rr] * sc);
+    }
+  }
+}
+
+// ------------------------------------------------------------------ bwd_window
+// One workgroup per (b, KV head, query chunk qc, pair of its query heads), two waves per
+// head (rows qc*64 .. qc*64+63).  Pass 1: the window's LSE by an online max/sum over
+// its chunks.  Row statistics: Lambda_i over the selected scores and the window's LSE,
+// g.o_i from the forward output.  Pass 2, per window chunk: P = exp(tau s - LSE),
+// dS = P w (dP' - g.o), dq on the MFMA (kept in registers, stored at the end: this
+// kernel writes every row's dq first), dk/dv over the 128 rows, added atomically.
+template <int D>
+__global__ void __launch_bounds__(256) bwd_window(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
+                                                  const bf16_t* __restrict__ v, const bf16_t* __restrict__ o,
+                                                  const bf16_t* __restrict__ dO, const float* __restrict__ sel_score,
+                                                  float* __restrict__ dq, float* __restrict__ dk, float* __restrict__ dv,
+                                                  float* __restrict__ lam, float* __restrict__ dd, int Hq, int Hkv,
+                                                  int N, int C, int K, int NQC, int nw) {
+  __shared__ GradLds<D> L;
+  const int G = Hq / Hkv;
+  const int ngb = (G + 1) / 2;
+  const int gb = blockIdx.x % ngb, rest = blockIdx.x / ngb;
+  const int qc = rest % NQC, bkv = rest / NQC;
+  const int kvh = bkv % Hkv, b = bkv / Hkv;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, hf = lane >> 5;
+  const int gi = gb * 2 + (w >> 1);
+  const bool head_ok = gi < G;
+  const int h = kvh * G + min(gi, G - 1);
+  const int64_t bh = (int64_t)b * Hq + h;
+  const int64_t kv0 = ((int64_t)b * Hkv + kvh) * N;
+  const int rl = 32 * (w & 1) + (lane & 31);
+  const int i = qc * 64 + rl;
+  const bool ok = i < N && head_ok;
+  const int64_t row = bh * N + (ok ? i : 0);
+  const float tau = 1.0f / sqrtf((float)D);
+  const float cl = tau * 1.44269504088896340736f;
+  bf16x8_t qb[1][D / 16], gb8[D / 16], ob[D / 16];
+  load_q_operand<bf16_t, D, 1>(q, row * D, ok, qb);
+  {
+    bf16x8_t tmp[1][D / 16];
+    load_q_operand<bf16_t, D, 1>(dO, row * D, ok, tmp);
+#pragma unroll
+    for (int ks = 0; ks < D / 16; ++ks) gb8[ks] = tmp[0][ks];
+    load_q_operand<bf16_t, D, 1>(o, row * D, ok, tmp);
+#pragma unroll
+    for (int ks = 0; ks < D / 16; ++ks) ob[ks] = tmp[0][ks];
+  }
+  // g.o_i (each lane half holds 8 of every 16 dims)
+  float go = 0.f;
+#pragma unroll
+  for (int ks = 0; ks < D / 16; ++ks) {
+    const u32x4_t gw = __builtin_bit_cast(u32x4_t, gb8[ks]), ow = __builtin_bit_cast(u32x4_t, ob[ks]);
+    const uint32_t g4[4] = {gw.x, gw.y, gw.z, gw.w}, o4[4] = {ow.x, ow.y, ow.z, ow.w};
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+      go = fmaf(__uint_as_float(g4[m] << 16), __uint_as_float(o4[m] << 16), go);
+      go = fmaf(__uint_as_float(g4[m] & 0xffff0000u), __uint_as_float(o4[m] & 0xffff0000u), go);
+    }
+  }
+  go += __shfl_xor(go, 32);
+  const int c0 = max(0, qc - nw + 1);
+  // pass 1: the window's max logit and sum
+  float m = -INFINITY, l = 0.f;
+  for (int c = c0; c <= qc; ++c) {
+    if (c > c0) __syncthreads();
+    stage_kv<bf16_t, D, 1>(L.kv, k, v, kv0 + (int64_t)c * 64, min(64, N - c * 64), tid, 256);
+    __syncthreads();
+    f32x16_t s[2];
+    keys_dot_rows<D, KVTile<bf16_t, D, 1>::LDK>(L.kv.k[0], qb[0], s);
+    const int lim = c == qc ? rl + 1 : 64;
+    float mt = -INFINITY;
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+      for (int rr = 0; rr < 16; ++rr) {
+        if (32 * tt + acc_row(rr, hf) >= lim) s[tt][rr] = -INFINITY;
+        mt = fmaxf(mt, s[tt][rr]);
+      }
+    mt = fmaxf(mt, __shfl_xor(mt, 32));
+    const float mn = fmaxf(m, mt);
+    float lt = 0.f;
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+      for (int rr = 0; rr < 16; ++rr) lt += __builtin_amdgcn_exp2f(fmaf(s[tt][rr], cl, -mn * cl));
+    lt += __shfl_xor(lt, 32);
+    l = fmaf(l, __builtin_amdgcn_exp2f((m - mn) * cl), lt);
+    m = mn;
+  }
+  const float lse = m * tau + logf(l);
+  // the fusion normaliser over the selected scores and the window's LSE
+  const int ns = min(K, candidate_chunks(i, C, nw));
+  float smax = lse;
+  for (int x = 0; x < ns; ++x) smax = fmaxf(smax, ok ? sel_score[row * K + x] : -INFINITY);
+  float z = __expf(lse - smax);
+  for (int x = 0; x < ns; ++x) z += ok ? __expf(sel_score[row * K + x] - smax) : 0.f;
+  const float Lam = smax + logf(z);
+  const float ww = ok ? __expf(lse - Lam) : 0.f;
+  if (ok && hf == 0) {
+    lam[row] = Lam;
+    dd[row] = go;
+  }
+  // the rows' q and g as [row][dim] tiles for the dk / dv products (constant over the window)
+  const int trow = 32 * w + (lane & 31);
+  rows_to_lds<D>(qb[0], L.qt, trow);
+  {
+    bf16x8_t gs[D / 16];
+#pragma unroll
+    for (int ks = 0; ks < D / 16; ++ks) gs[ks] = ww == 0.f ? bf16x8_t{} : gb8[ks];
+    rows_to_lds<D>(gs, L.gt, trow);  // rows with no weight contribute nothing
+  }
+  f32x16_t dqa[D / 32];
+#pragma unroll
+  for (int dt = 0; dt < D / 32; ++dt) dqa[dt] = zero16();
+  const float lse2 = lse * 1.44269504088896340736f;
+  for (int c = c0; c <= qc; ++c) {
+    __syncthreads();  // every wave is done with the previous chunk's tiles
+    const int nkeys = min(64, N - c * 64);
+    stage_kv<bf16_t, D, 1>(L.kv, k, v, kv0 + (int64_t)c * 64, nkeys, tid, 256);
+    __syncthreads();
+    f32x16_t s[2], dp[2];
+    keys_dot_rows<D, KVTile<bf16_t, D, 1>::LDK>(L.kv.k[0], qb[0], s);
+    keys_dot_rows<D, KVTile<bf16_t, D, 1>::LDV>(L.kv.v[0], gb8, dp);
+    const int lim = c == qc ? rl + 1 : 64;
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+      for (int rr = 0; rr < 16; ++rr) {
+        const float p = 32 * tt + acc_row(rr, hf) < lim ? __builtin_amdgcn_exp2f(fmaf(s[tt][rr], cl, -lse2)) * ww : 0.f;
+        s[tt][rr] = p;                         // P w
+        dp[tt][rr] = p * (dp[tt][rr] - go);    // dS
+      }
+    keys_to_lds(s, L.pt, trow);
+    keys_to_lds(dp, L.st, trow);
+    dq_from_ds<D>(L.kv, dp, dqa);
+    __syncthreads();
+    dkdv_from_tiles<D>(L, dk, dv, kv0 + (int64_t)c * 64, nkeys, tau);
+  }
+  if (!ok) return;
+#pragma unroll
+  for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+    for (int g4 = 0; g4 < 4; ++g4) {
+      const int e = 32 * dt + 8 * g4 + 4 * hf;
+      *reinterpret_cast<float4*>(&dq[row * D + e]) =
+          make_float4(dqa[dt][4 * g4] * tau, dqa[dt][4 * g4 + 1] * tau, dqa[dt][4 * g4 + 2] * tau,
+                      dqa[dt][4 * g4 + 3] * tau);
+    }
+}
+
+// ------------------------------------------------------------------- bwd_pairs
+// One work item = up to BUCKET_ITEM_ROWS gathered rows of one bucket (b, h, c), in
+// tiles of 128 (32 per wave).  Per row: S and dP' on the MFMA, the chunk softmax P,
+// e = sum_j P_j dP'_j, w = exp(s_ic - Lambda_i), dsigma = w (e - g.o_i) (stored per pair),
+// dS = P w (dP' - e), dq (added atomically); dk/dv over the tile's rows; and the item's
+// dk'_c = tau sum dsigma q^, db'_c = sum dsigma, added atomically at the end.
+template <int D>
+__global__ void __launch_bounds__(256) bwd_pairs(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
+                                                 const bf16_t* __restrict__ v, const bf16_t* __restrict__ dO,
+                                                 const float* __restrict__ qh, const float* __restrict__ sel_score,
+                                                 const float* __restrict__ lam, const float* __restrict__ dd,
+                                                 const uint32_t* __restrict__ pairs, const uint32_t* __restrict__ boff,
+                                                 const uint32_t* __restrict__ toff, float* __restrict__ dsig,
+                                                 float* __restrict__ dq, float* __restrict__ dk, float* __restrict__ dv,
+                                                 float* __restrict__ dkc, float* __restrict__ dbc, int Hq, int Hkv,
+                                                 int N, int C, int K, int nbk) {
+  __shared__ GradLds<D> L;
+  __shared__ float sig_s[BW_ROWS];
+  __shared__ uint32_t srow[BW_ROWS];
+  __shared__ float red[2][D + 1];
+  const int item = blockIdx.x;
+  if ((uint32_t)item >= toff[nbk]) return;
+  int lo = 0, hi = nbk - 1;  // bucket = last index with toff[bk] <= item
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (toff[mid] <= (uint32_t)item) lo = mid;
+    else hi = mid - 1;
+  }
+  const int bk = lo;
+  const uint32_t count = boff[bk + 1] - boff[bk];
+  const uint32_t first = ((uint32_t)item - toff[bk]) * BUCKET_ITEM_ROWS;
+  const uint32_t nrows = min((uint32_t)BUCKET_ITEM_ROWS, count - first);
+  const uint32_t* pp = pairs + boff[bk] + first;
+  const int c = bk % C;
+  const int64_t bhq = bk / C;  // b * Hq + h
+  const int h = (int)(bhq % Hq), b = (int)(bhq / Hq);
+  const int kvh = h / (Hq / Hkv);
+  const int64_t kvrow0 = ((int64_t)b * Hkv + kvh) * N + (int64_t)c * 64;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, hf = lane >> 5;
+  const float tau = 1.0f / sqrtf((float)D);
+  const float cl = tau * 1.44269504088896340736f;
+  const int trow = 32 * w + (lane & 31);
+  stage_kv<bf16_t, D, 1>(L.kv, k, v, kvrow0, 64, tid, 256);
+  // dk'_c / db'_c partial sums: thread t sums dims t % D over its share of the rows
+  constexpr int RSPLIT = 256 / D;
+  float kacc = 0.f, bacc = 0.f;
+  const int ntile = (int)((nrows + BW_ROWS - 1) / BW_ROWS);
+  for (int j = 0; j < ntile; ++j) {
+    const uint32_t r = (uint32_t)j * BW_ROWS + trow;
+    const bool ok = r < nrows;
+    const uint32_t pid = ok ? pp[r] : 0u;  // linear index into sel_idx: row * K + slot
+    const int64_t row = ok ? (int64_t)(pid / (uint32_t)K) : bhq * N;
+    bf16x8_t qb[1][D / 16], gb8[1][D / 16];
+    load_q_operand<bf16_t, D, 1>(q, row * D, ok, qb);
+    load_q_operand<bf16_t, D, 1>(dO, row * D, ok, gb8);
+    const float sc = ok ? sel_score[pid] : 0.f;
+    const float Lam = ok ? lam[row] : 0.f;
+    const float go = ok ? dd[row] : 0.f;
+    __syncthreads();  // the K/V staging is done; the previous tile's LDS tiles are consumed
+    f32x16_t s[2], dp[2];
+    keys_dot_rows<D, KVTile<bf16_t, D, 1>::LDK>(L.kv.k[0], qb[0], s);
+    keys_dot_rows<D, KVTile<bf16_t, D, 1>::LDV>(L.kv.v[0], gb8[0], dp);
+    float mt = fmaxf(s[0][0], s[0][1]);
+#pragma unroll
+    for (int rr = 2; rr < 32; ++rr) mt = fmaxf(mt, s[rr >> 4][rr & 15]);
+    mt = fmaxf(mt, __shfl_xor(mt, 32));
+    float lt = 0.f;
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+      for (int rr = 0; rr < 16; ++rr) {
+        s[tt][rr] = __builtin_amdgcn_exp2f((s[tt][rr] - mt) * cl);
+        lt += s[tt][rr];
+      }
+    lt += __shfl_xor(lt, 32);
+    const float inv = 1.0f / lt;
+    float e = 0.f;
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+      for (int rr = 0; rr < 16; ++rr) {
+        s[tt][rr] *= inv;  // P
+        e = fmaf(s[tt][rr], dp[tt][rr], e);
+      }
+    e += __shfl_xor(e, 32);
+    const float wc = ok ? __expf(sc - Lam) : 0.f;
+    const float dsg = wc * (e - go);
+    if (ok && hf == 0) dsig[pid] = dsg;
+    if (hf == 0) {
+      sig_s[trow] = ok ? dsg : 0.f;
+      srow[trow] = (uint32_t)row;
+    }
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+      for (int rr = 0; rr < 16; ++rr) {
+        const float p = s[tt][rr] * wc;
+        s[tt][rr] = p;                      // P w
+        dp[tt][rr] = p * (dp[tt][rr] - e);  // dS
+      }
+    keys_to_lds(s, L.pt, trow);
+    keys_to_lds(dp, L.st, trow);
+    rows_to_lds<D>(qb[0], L.qt, trow);
+    rows_to_lds<D>(gb8[0], L.gt, trow);
+    f32x16_t dqa[D / 32];
+#pragma unroll
+    for (int dt = 0; dt < D / 32; ++dt) dqa[dt] = zero16();
+    dq_from_ds<D>(L.kv, dp, dqa);
+    if (ok) {
+#pragma unroll
+      for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+        for (int rr = 0; rr < 16; ++rr)
+          atomicAdd(&dq[row * D + 32 * dt + acc_row(rr, hf)], dqa[dt][rr] * tau);
+    }
+    __syncthreads();
+    dkdv_from_tiles<D>(L, dk, dv, kvrow0, 64, tau);
+    // dk'_c and db'_c over this tile's rows
+    {
+      const int e2 = tid % D, part = tid / D;
+#pragma unroll 4
+      for (int x = part; x < BW_ROWS; x += RSPLIT) {
+        const float sg = sig_s[x];
+        if (sg != 0.f) kacc = fmaf(sg, qh[(int64_t)srow[x] * D + e2], kacc);
+      }
+      if (tid < BW_ROWS) bacc += sig_s[tid];
+    }
+  }
+  // item totals of dk'_c and db'_c
+  const int e2 = tid % D, part = tid / D;
+  __syncthreads();
+  if (part < 2) red[part][e2] = kacc;
+  if (RSPLIT == 4) {
+    __syncthreads();
+    if (part >= 2) red[part - 2][e2] += kacc;
+  }
+  __syncthreads();
+  const int64_t ci = bhq * C + c;  // landmark head = query head
+  if (tid < D) atomicAdd(&dkc[ci * D + tid], tau * (red[0][tid] + red[1][tid]));
+  float bs = tid < BW_ROWS ? bacc : 0.f;
+  bs = wave_sum_f(bs);
+  if (lane == 0 && w < 2) atomicAdd(&dbc[ci], bs);
+}
+
+// -------------------------------------------------------------------- bwd_rows
+// Per row (one wave, lanes over the dims): dq^ = tau sum_x dsigma_x k'_(sel x), then the
+// Q-Cal backward: dq += dq^ + D^T (U^T dq^); dU += dq^ (D q)^T and dD += (U^T dq^) q^T are
+// summed over the wave's rows (all of one head) and added atomically at the end.
+template <int D>
+__global__ void __launch_bounds__(256) bwd_rows(const bf16_t* __restrict__ q, const bf16_t* __restrict__ Dw,
+                                                const bf16_t* __restrict__ Uw, const float* __restrict__ kc,
+                                                const int32_t* __restrict__ sel, const float* __restrict__ dsig,
+                                                float* __restrict__ dq, float* __restrict__ dD, float* __restrict__ dU,
+                                                int Hq, int N, int C, int K, int r, int rows_per_wave, int64_t nwaves) {
+  constexpr int EPL = D / 64;
+  constexpr int RMAX = 32;
+  __shared__ float tq[4][RMAX], uq[4][RMAX];
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int64_t gw = (int64_t)blockIdx.x * 4 + w;  // wave index: rows_per_wave rows of one (b, h)
+  if (gw >= nwaves) return;  // no barrier below: a whole wave leaves
+  const int64_t waves_per_head = (N + rows_per_wave - 1) / rows_per_wave;
+  const int64_t bh = gw / waves_per_head;
+  const int i0 = (int)(gw % waves_per_head) * rows_per_wave;
+  const int h = (int)(bh % Hq);
+  const float tau = 1.0f / sqrtf((float)D);
+  float aU[EPL][RMAX], aD[EPL][RMAX];
+#pragma unroll
+  for (int u = 0; u < EPL; ++u)
+#pragma unroll
+    for (int a = 0; a < RMAX; ++a) aU[u][a] = aD[u][a] = 0.f;
+  const float* kch = kc + bh * C * D;
+  for (int i = i0; i < min(N, i0 + rows_per_wave); ++i) {
+    const int64_t row = bh * N + i;
+    float dqh[EPL];
+#pragma unroll
+    for (int u = 0; u < EPL; ++u) dqh[u] = 0.f;
+    for (int x = 0; x < K; ++x) {
+      const int cc = sel[row * K + x];
+      if (cc < 0) break;
+      const float sg = dsig[row * K + x] * tau;
+#pragma unroll
+      for (int u = 0; u < EPL; ++u) dqh[u] = fmaf(sg, kch[(int64_t)cc * D + lane + 64 * u], dqh[u]);
+    }
+    float add[EPL];
+#pragma unroll
+    for (int u = 0; u < EPL; ++u) add[u] = dqh[u];
+    if (r > 0) {
+      float x[EPL];
+#pragma unroll
+      for (int u = 0; u < EPL; ++u) x[u] = bf16_to_f32(q[row * D + lane + 64 * u].bits);
+      for (int a = 0; a < r; ++a) {
+        float p = 0.f, p2 = 0.f;
+#pragma unroll
+        for (int u = 0; u < EPL; ++u) {
+          const int e = lane + 64 * u;
+          p = fmaf(bf16_to_f32(Dw[((int64_t)h * r + a) * D + e].bits), x[u], p);
+          p2 = fmaf(bf16_to_f32(Uw[((int64_t)h * D + e) * r + a].bits), dqh[u], p2);
+        }
+        p = wave_sum_f(p);
+        p2 = wave_sum_f(p2);
+        if (lane == 0) {
+          tq[w][a] = p;   // (D q)_a
+          uq[w][a] = p2;  // (U^T dq^)_a
+        }
+      }
+      __builtin_amdgcn_wave_barrier();
+#pragma unroll
+      for (int u = 0; u < EPL; ++u) {
+        const int e = lane + 64 * u;
+#pragma unroll
+        for (int a = 0; a < RMAX; ++a) {
+          if (a < r) {
+            add[u] = fmaf(bf16_to_f32(Dw[((int64_t)h * r + a) * D + e].bits), uq[w][a], add[u]);
+            aU[u][a] = fmaf(dqh[u], tq[w][a], aU[u][a]);
+            aD[u][a] = fmaf(uq[w][a], x[u], aD[u][a]);
+          }
+        }
+      }
+      __builtin_amdgcn_wave_barrier();
+    }
+#pragma unroll
+    for (int u = 0; u < EPL; ++u) dq[row * D + lane + 64 * u] += add[u];
+  }
+  if (r > 0 && i0 < N) {
+#pragma unroll
+    for (int u = 0; u < EPL; ++u) {
+      const int e = lane + 64 * u;
+#pragma unroll
+      for (int a = 0; a < RMAX; ++a)
+        if (a < r) {
+          atomicAdd(&dU[((int64_t)h * D + e) * r + a], aU[u][a]);
+          atomicAdd(&dD[((int64_t)h * r + a) * D + e], aD[u][a]);
+        }
+    }
+  }
+}
+
+// ---------------------------------------------------------------- bwd_compress
+// One workgroup per (b, KV head, chunk), looping over the landmark heads of the KV head:
+// recompute the compression weights a, then dz, the landmark query's gradient (written
+// out) and the keys' gradient, summed in LDS and added to the keys' accumulator (each
+// chunk's keys belong to this workgroup alone).
+template <int D>
+__global__ void __launch_bounds__(256) bwd_compress(const bf16_t* __restrict__ k, const bf16_t* __restrict__ lmk,
+                                                    const float* __restrict__ dkc, const float* __restrict__ dbc,
+                                                    float* __restrict__ dk, bf16_t* __restrict__ dlmk, int Hl, int Hkv,
+                                                    int N, int C) {
+  __shared__ float ks[64][D + 1];
+  __shared__ float acc[64][D + 1];
+  __shared__ float Ls[D], gk[D];
+  __shared__ float zs[64], as[64], das[64];
+  const int c = blockIdx.x % C, bkv = blockIdx.x / C;
+  const int kvh = bkv % Hkv, b = bkv / Hkv;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int64_t kb = ((int64_t)b * Hkv + kvh) * N + (int64_t)c * 64;
+  const float tau = 1.0f / sqrtf((float)D);
+  for (int x = tid; x < 64 * D; x += 256) {
+    ks[x / D][x % D] = bf16_to_f32(k[kb * D + x].bits);
+    acc[x / D][x % D] = 0.f;
+  }
+  const int lpk = Hl / Hkv;
+  for (int li = 0; li < lpk; ++li) {
+    const int l = kvh * lpk + li;
+    const int64_t ci = ((int64_t)b * Hl + l) * C + c;
+    __syncthreads();
+    for (int e = tid; e < D; e += 256) {
+      Ls[e] = bf16_to_f32(lmk[ci * D + e].bits);
+      gk[e] = dkc[ci * D + e];
+    }
+    const float gb = dbc[ci];
+    __syncthreads();
+    // z_j and dk'.k_j, four threads per key
+    {
+      const int j = tid >> 2, part = tid & 3;
+      float zz = 0.f, gg = 0.f;
+      for (int e = part; e < D; e += 4) {
+        zz = fmaf(Ls[e], ks[j][e], zz);
+        gg = fmaf(gk[e], ks[j][e], gg);
+      }
+      zz += __shfl_xor(zz, 1);
+      zz += __shfl_xor(zz, 2);
+      gg += __shfl_xor(gg, 1);
+      gg += __shfl_xor(gg, 2);
+      if (part == 0) {
+        zs[j] = zz * tau;
+        das[j] = gg;
+      }
+    }
+    __syncthreads();
+    if (w == 0) {
+      const float zz = zs[lane];
+      float mx = zz;
+#pragma unroll
+      for (int o = 32; o > 0; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o));
+      const float ex = __expf(zz - mx);
+      const float a = ex / wave_sum_f(ex);
+      const float da = das[lane] - (a > 0.f ? gb * (logf(a) + 1.0f) : 0.f);
+      const float sda = wave_sum_f(a * da);
+      as[lane] = a;
+      das[lane] = a * (da - sda);  // dz_j
+    }
+    __syncthreads();
+    for (int e = tid; e < D; e += 256) {
+      float s = 0.f;
+      for (int j = 0; j < 64; ++j) s = fmaf(das[j], ks[j][e], s);
+      dlmk[ci * D + e].bits = f32_to_bf16(s * tau);
+    }
+    for (int x = tid; x < 64 * D; x += 256) {
+      const int j = x / D, e = x % D;
+      acc[j][e] += as[j] * gk[e] + tau * das[j] * Ls[e];
+    }
+  }
+  __syncthreads();
+  for (int x = tid; x < 64 * D; x += 256) dk[kb * D + x] += acc[x / D][x % D];
+}
+
+__global__ void __launch_bounds__(256) bwd_convert(const float* __restrict__ src, bf16_t* __restrict__ dst, int64_t n) {
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256)
+    dst[i].bits = f32_to_bf16(src[i]);
+}
+
+unsigned grid_for(int64_t n) { return (unsigned)std::max<int64_t>(1, std::min<int64_t>((n + 255) / 256, 65536)); }
+
+template <int D>
+hipError_t launch_bwd_d(const Geom& g, const BwdArgs& a, char* ws, hipStream_t st) {
+  const BwdWs w = bwd_ws(g);
+  float* qh = (float*)(ws + w.qh);
+  float* dq = (float*)(ws + w.dq);
+  float* dk = (float*)(ws + w.dk);
+  float* dv = (float*)(ws + w.dv);
+  float* dkc = (float*)(ws + w.dkc);
+  float* dbc = (float*)(ws + w.dbc);
+  float* dD = (float*)(ws + w.dD);
+  float* dU = (float*)(ws + w.dU);
+  float* lam = (float*)(ws + w.lam);
+  float* dd = (float*)(ws + w.dd);
+  float* dsig = (float*)(ws + w.dsig);
+  const int C = g.C();
+  const int64_t rows = (int64_t)g.B * g.Hq * g.N;
+  const bf16_t *q = (const bf16_t*)a.q, *k = (const bf16_t*)a.k, *v = (const bf16_t*)a.v;
+  const bf16_t *Dw = (const bf16_t*)a.D, *Uw = (const bf16_t*)a.U;
+  // the accumulators dk .. dU are contiguous
+  const int64_t nz = (int64_t)(w.lam - w.dk) / 4;
+  hipLaunchKernelGGL(bwd_zero, dim3(grid_for(nz)), dim3(256), 0, st, dk, nz);
+  hipLaunchKernelGGL((bwd_prep<D>), dim3((unsigned)std::min<int64_t>((rows + 3) / 4, 65536)), dim3(256), 0, st, q, Dw,
+                     Uw, qh, g.Hq, g.N, g.r, rows);
+  const int NQC = (g.N + 63) / 64;
+  const int ngb = (g.G() + 1) / 2;
+  hipLaunchKernelGGL((bwd_window<D>), dim3(g.B * g.Hkv * NQC * ngb), dim3(256), 0, st, q, k, v, (const bf16_t*)a.o,
+                     (const bf16_t*)a.dO, a.sel_score, dq, dk, dv, lam, dd, g.Hq, g.Hkv, g.N, C, g.K, NQC, g.nw);
+  const int nbk = g.B * g.Hq * C;
+  const int64_t items = bucket_items_bound(g);
+  if (nbk > 0 && items > 0) {
+    uint32_t* boff = (uint32_t*)(ws + w.boff);
+    uint32_t* toff = (uint32_t*)(ws + w.toff);
+    uint32_t* pairs = (uint32_t*)(ws + w.pairs);
+    launch_bucket_pairs(g, a.sel_idx,
+                        BucketBufs{(uint32_t*)(ws + w.counts), (uint32_t*)(ws + w.cursor), boff, toff, pairs,
+                                   (uint32_t*)(ws + w.tmp)},
+                        st);
+    hipLaunchKernelGGL((bwd_pairs<D>), dim3((unsigned)items), dim3(256), 0, st, q, k, v, (const bf16_t*)a.dO,
+                       (const float*)qh, a.sel_score, (const float*)lam, (const float*)dd, (const uint32_t*)pairs,
+                       (const uint32_t*)boff, (const uint32_t*)toff, dsig, dq, dk, dv, dkc, dbc, g.Hq, g.Hkv, g.N, C,
+                       g.K, nbk);
+  }
+  constexpr int RPW = 64;  // rows per wave in bwd_rows
+  const int64_t nwaves = (int64_t)g.B * g.Hq * ((g.N + RPW - 1) / RPW);
+  hipLaunchKernelGGL((bwd_rows<D>), dim3((unsigned)((nwaves + 3) / 4)), dim3(256), 0, st, q, Dw, Uw, a.kc, a.sel_idx,
+                     (const float*)dsig, dq, dD, dU, g.Hq, g.N, C, g.K, g.r, RPW, nwaves);
+  if (C > 0)
+    hipLaunchKernelGGL((bwd_compress<D>), dim3(g.B * g.Hkv * C), dim3(256), 0, st, k, (const bf16_t*)a.lmk,
+                       (const float*)dkc, (const float*)dbc, dk, (bf16_t*)a.dlmk, g.Hl, g.Hkv, g.N, C);
+  const int64_t kvn = (int64_t)g.B * g.Hkv * g.N * D;
+  hipLaunchKernelGGL(bwd_convert, dim3(grid_for(rows * D)), dim3(256), 0, st, (const float*)dq, (bf16_t*)a.dq, rows * D);
+  hipLaunchKernelGGL(bwd_convert, dim3(grid_for(kvn)), dim3(256), 0, st, (const float*)dk, (bf16_t*)a.dk, kvn);
+  hipLaunchKernelGGL(bwd_convert, dim3(grid_for(kvn)), dim3(256), 0, st, (const float*)dv, (bf16_t*)a.dv, kvn);
+  if (g.r > 0) {
+    const int64_t nr = (int64_t)g.Hq * g.r * D;
+    hipLaunchKernelGGL(bwd_convert, dim3(grid_for(nr)), dim3(256), 0, st, (const float*)dD, (bf16_t*)a.dD, nr);
+    hipLaunchKernelGGL(bwd_convert, dim3(grid_for(nr)), dim3(256), 0, st, (const float*)dU, (bf16_t*)a.dU, nr);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace
+
+size_t backward_workspace_bytes(const Geom& g) { return bwd_ws(g).total; }
+
+hipError_t launch_backward(const Geom& g, const BwdArgs& a, void* ws, size_t ws_bytes, hipStream_t st) {
+  if (ws_bytes < backward_workspace_bytes(g)) return hipErrorInvalidValue;
+  if (g.io != 1) return hipErrorNotSupported;
+  return g.d == 64 ? launch_bwd_d<64>(g, a, (char*)ws, st) : launch_bwd_d<128>(g, a, (char*)ws, st);
+}
+
+}  // namespace hils

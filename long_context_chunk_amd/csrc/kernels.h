@@ -33,6 +33,28 @@ struct KvPages {
 hipError_t launch_compress(int io, const void* k, const void* lmk, float* kc, float* bc, int B, int Hkv, int Hl,
                            int N, int d, int c_begin, int c_end, hipStream_t st, KvPages pg = KvPages());
 
+// Bucketing of the (query row, selected chunk) pairs of a prefill selection by bucket
+// (b, query head, chunk), numbered head-major: pairs[boff[bk] .. boff[bk+1]) are the pair
+// ids (linear indices into sel_idx) of bucket bk; toff[bk] is its first work item of
+// BUCKET_ITEM_ROWS pairs, toff[nbk] the total.  counts and cursor hold nbk words each and
+// are contiguous (counts first); tmp holds B*Hq*N*K words.
+constexpr int BUCKET_ITEM_ROWS = 1024;
+struct BucketBufs {
+  uint32_t *counts, *cursor, *boff, *toff, *pairs, *tmp;
+};
+void launch_bucket_pairs(const Geom& g, const int32_t* sel, BucketBufs bb, hipStream_t st);
+int64_t bucket_items_bound(const Geom& g);  // host bound on the work items (0 if no pairs)
+
+// Backward pass of the prefill forward (bf16 I/O), the selection held fixed.
+struct BwdArgs {
+  const void *q, *k, *v, *lmk, *D, *U, *o, *dO;
+  const float *kc, *sel_score;
+  const int32_t* sel_idx;
+  void *dq, *dk, *dv, *dlmk, *dD, *dU;
+};
+size_t backward_workspace_bytes(const Geom& g);
+hipError_t launch_backward(const Geom& g, const BwdArgs& a, void* ws, size_t ws_bytes, hipStream_t st);
+
 // Chunk scores and per-row top-K for all N queries of every (b, h).
 size_t score_workspace_bytes(const Geom& g);
 // ev (nullable): two events recorded after the threshold pass and after the selection pass.

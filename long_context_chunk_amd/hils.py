@@ -16,12 +16,12 @@ _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libhils.so")
 
 F32, BF16 = 0, 1
-OP_COMPRESS, OP_SCORE_TOPK, OP_PREFILL, OP_DECODE = 0, 1, 2, 3
+OP_COMPRESS, OP_SCORE_TOPK, OP_PREFILL, OP_DECODE, OP_BACKWARD = 0, 1, 2, 3, 4
 OK, E_INVAL, E_UNSUPPORTED, E_WORKSPACE, E_HIP = 0, -1, -2, -3, -4
 
 SYMBOLS = ("hils_workspace_bytes", "hils_landmark_compress", "hils_chunk_score_topk", "hils_attn_prefill",
            "hils_attn_prefill_timed", "hils_attn_decode", "hils_attn_decode_timed", "hils_landmark_compress_paged",
-           "hils_attn_decode_paged", "hils_dense_attention", "hils_last_error")
+           "hils_attn_decode_paged", "hils_dense_attention", "hils_attn_prefill_backward", "hils_last_error")
 STAGES = ("compress", "score_threshold", "score_select", "bucket", "chunk_attend", "own_attend", "fuse")
 DECODE_STAGES = ("scan", "merge", "attend_fuse")
 
@@ -65,9 +65,10 @@ def load():
         lib.hils_dense_attention.argtypes = [dp, vp, vp, vp, vp, vp]
         lib.hils_landmark_compress_paged.argtypes = [dp, vp, vp, i32, i32, vp, i32, i32, vp, vp, vp]
         lib.hils_attn_decode_paged.argtypes = [dp, vp, vp, vp, vp, i32, i32, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+        lib.hils_attn_prefill_backward.argtypes = [dp] + [vp] * 18 + [sz, vp]
         for f in ("hils_landmark_compress", "hils_chunk_score_topk", "hils_attn_prefill", "hils_attn_prefill_timed",
                   "hils_attn_decode", "hils_attn_decode_timed", "hils_dense_attention", "hils_landmark_compress_paged",
-                  "hils_attn_decode_paged"):
+                  "hils_attn_decode_paged", "hils_attn_prefill_backward"):
             getattr(lib, f).restype = ctypes.c_int
         lib.hils_last_error.argtypes = []
         lib.hils_last_error.restype = ctypes.c_char_p
@@ -183,6 +184,32 @@ def attn_prefill(dm: Dims, q, k, v, o, ws, lmk_q=None, kc=None, bc=None, qcal_D=
         _check(load().hils_attn_prefill_timed(*args, ms))
         return dict(zip(STAGES, [float(x) for x in ms]))
     _check(load().hils_attn_prefill(*args))
+
+
+def attn_prefill_backward(dm: Dims, q, k, v, lmk_q, kc, sel_idx, sel_score, o, dO, dq, dk, dv, dlmk, ws,
+                          qcal_D=None, qcal_U=None, dD=None, dU=None):
+    """hils_attn_prefill_backward: gradients of sum(o * dO) with the forward's selection held fixed."""
+    C = dm.N // dm.S
+    dt = torch.bfloat16
+    for t, n, shp in ((q, "q", (dm.B, dm.Hq, dm.N, dm.d)), (k, "k", (dm.B, dm.Hkv, dm.N, dm.d)),
+                      (v, "v", (dm.B, dm.Hkv, dm.N, dm.d)), (o, "o", (dm.B, dm.Hq, dm.N, dm.d)),
+                      (dO, "dO", (dm.B, dm.Hq, dm.N, dm.d)), (dq, "dq", (dm.B, dm.Hq, dm.N, dm.d)),
+                      (dk, "dk", (dm.B, dm.Hkv, dm.N, dm.d)), (dv, "dv", (dm.B, dm.Hkv, dm.N, dm.d))):
+        _req(t, n, shp, dt)
+    if C > 0:
+        _req(lmk_q, "lmk_q", (dm.B, dm.Hlmk, C, dm.d), dt)
+        _req(dlmk, "dlmk", (dm.B, dm.Hlmk, C, dm.d), dt)
+        _req(kc, "kc", (dm.B, dm.Hlmk, C, dm.d), torch.float32)
+    _req(sel_idx, "sel_idx", (dm.B, dm.Hq, dm.N, dm.K), torch.int32)
+    _req(sel_score, "sel_score", (dm.B, dm.Hq, dm.N, dm.K), torch.float32)
+    _req(ws, "ws", dtype=torch.uint8)
+    if dm.qcal_rank > 0:
+        for t, n, shp in ((qcal_D, "qcal_D", (dm.Hq, dm.qcal_rank, dm.d)), (qcal_U, "qcal_U", (dm.Hq, dm.d, dm.qcal_rank)),
+                          (dD, "dD", (dm.Hq, dm.qcal_rank, dm.d)), (dU, "dU", (dm.Hq, dm.d, dm.qcal_rank))):
+            _req(t, n, shp, dt)
+    _check(load().hils_attn_prefill_backward(ctypes.byref(dm), _p(q), _p(k), _p(v), _p(lmk_q), _p(kc), _p(qcal_D),
+                                              _p(qcal_U), _p(sel_idx), _p(sel_score), _p(o), _p(dO), _p(dq), _p(dk),
+                                              _p(dv), _p(dlmk), _p(dD), _p(dU), _p(ws), ws.numel(), _stream()))
 
 
 def attn_decode(dm: Dims, q, k_cache, v_cache, seq_lens, kc, bc, o, ws, qcal_D=None, qcal_U=None, sel_idx=None,
