@@ -441,6 +441,60 @@ def run_decode(wd, steps, warmup, seed):
     }
 
 
+def backward_flops(w, cnt):
+    """Algorithmic MFMA work of the backward: per (row, selected chunk) pair and per window key,
+    the five products S = q K^T, dP = g V^T, dq = dS K, dk = dS^T q, dv = P^T g (2 d flops each
+    per (row, key)); the score, Q-Cal and compression gradients are small beside them."""
+    pair_keys = cnt["pairs"] * w.S
+    window_keys = cnt["window_flops"] / (4.0 * w.d)  # the forward's 4 d flops per (row, window key)
+    return 10.0 * w.d * (pair_keys + window_keys)
+
+
+def run_backward(w, steps, warmup, seed):
+    """Times hils_attn_prefill_backward on the forward's own outputs (selection, k', o) with a
+    seeded standard-normal output gradient."""
+    import torch
+    import synth
+    from long_context_chunk_amd import hils
+    x = synth.make_inputs(w, seed)
+    dm = hils.dims(w.B, w.Hq, w.Hkv, w.d, w.N, w.K, S=w.S, qcal_rank=w.qcal_rank, io=w.io, window=w.window)
+    q, k, v, lmk = (upload(x[n], w.io) for n in ("q", "k", "v", "lmk"))
+    D = upload(x["D"], w.io) if w.qcal_rank else None
+    U = upload(x["U"], w.io) if w.qcal_rank else None
+    del x
+    o = torch.empty_like(q)
+    kc = torch.empty((w.B, w.Hlmk, w.C, w.d), dtype=torch.float32, device="cuda")
+    bc = torch.empty((w.B, w.Hlmk, w.C), dtype=torch.float32, device="cuda")
+    sel = torch.empty((w.B, w.Hq, w.N, w.K), dtype=torch.int32, device="cuda")
+    scr = torch.empty((w.B, w.Hq, w.N, w.K), dtype=torch.float32, device="cuda")
+    ws = hils.workspace(dm, hils.OP_PREFILL)
+    hils.attn_prefill(dm, q, k, v, o, ws, lmk_q=lmk, kc=kc, bc=bc, qcal_D=D, qcal_U=U, sel_idx=sel, sel_score=scr)
+    torch.cuda.synchronize()
+    del ws
+    torch.cuda.empty_cache()
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(seed + 77)
+    dO = torch.randn(q.shape, generator=gen, device="cuda", dtype=torch.float32).to(torch.bfloat16)
+    dq, dk, dv, dlmk = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v), torch.empty_like(lmk)
+    dD = torch.empty_like(D) if D is not None else None
+    dU = torch.empty_like(U) if U is not None else None
+    wsb = hils.workspace(dm, hils.OP_BACKWARD)
+    log("backward workspace %.1f GiB" % (wsb.numel() / 2**30))
+
+    def step():
+        hils.attn_prefill_backward(dm, q, k, v, lmk, kc, sel, scr, o, dO, dq, dk, dv, dlmk, wsb, qcal_D=D, qcal_U=U,
+                                   dD=dD, dU=dU)
+
+    ms = _time_ms(step, steps)  # one untimed call first
+    cnt = prefill_counts(w)
+    fl = backward_flops(w, cnt)
+    ach = fl / (ms * 1e-3) / 1e12
+    log("backward: %.2f ms/step" % ms)
+    return {"workload": w.name, "ms_per_step": ms, "tokens_per_s": w.B * w.N / (ms * 1e-3),
+            "roofline": {"bound": "mfma", "achieved": ach, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                         "frac": ach / PEAK_BF16_TFLOPS, "algorithmic_flops": fl, "kernel": "whole backward"}}
+
+
 def with_window(w, window):
     """The workload with a local window of `window` tokens (named apart from the plain one)."""
     import synth
@@ -463,6 +517,8 @@ def main():
     ap.add_argument("--no-dense", action="store_true")
     ap.add_argument("--no-parity", action="store_true")
     ap.add_argument("--no-prefill", action="store_true", help="decode step only (for profiling it alone)")
+    ap.add_argument("--backward", action="store_true",
+                    help="only the backward pass (gradients of the prefill output) at --workload")
     ap.add_argument("--sweep", action="store_true",
                     help="HiLS prefill against the dense baseline over N = 8K..512K (16/4 heads, d = 64, K = 16)")
     ap.add_argument("--peaks", action="store_true", help="only measure a device copy and a large bf16 GEMM")
@@ -490,6 +546,9 @@ def main():
     assert torch.cuda.is_available()
     w = with_window(synth.WORKLOADS[args.workload], args.window)
     seed = synth.BASE_SEED + 5
+    if args.backward:
+        print(json.dumps({"backward": run_backward(w, args.steps, args.warmup, seed)}), flush=True)
+        return
     if args.no_prefill:
         wd = with_window(synth.WORKLOADS[args.decode_workload], args.window)
         print(json.dumps({"decode": run_decode(wd, max(args.steps, 20), args.warmup, seed + 1)}), flush=True)

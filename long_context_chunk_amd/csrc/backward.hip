@@ -231,6 +231,43 @@ HILS_DEV void dkdv_from_tiles(const GradLds<D>& L, float* __restrict__ dk, float
   }
 }
 
+// The same products accumulated over several tiles in per-wave registers (wave w owns
+// blocks w, w + 4, ...), and their flush to the fp32 accumulators.
+template <int D>
+HILS_DEV void dkdv_accumulate(const GradLds<D>& L, f32x16_t (&acc)[D / 32]) {
+  constexpr int NDT = D / 32;
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+#pragma unroll
+  for (int ib = 0; ib < NDT; ++ib) {
+    const int blk = w + 4 * ib;
+    const bool isk = blk >= 2 * NDT;
+    const int kt = (blk % (2 * NDT)) / NDT, dt = blk % NDT;
+    const uint16_t* a_tile = isk ? L.st : L.pt;
+    const uint16_t* b_tile = isk ? L.qt : L.gt;
+#pragma unroll
+    for (int ks2 = 0; ks2 < BW_ROWS / 16; ++ks2)
+      acc[ib] = mfma32(vt_operand<LDP>(a_tile, kt, ks2, lane), vt_operand<GradLds<D>::LDR>(b_tile, dt, ks2, lane),
+                       acc[ib]);
+  }
+}
+template <int D>
+HILS_DEV void dkdv_flush(const f32x16_t (&acc)[D / 32], float* __restrict__ dk, float* __restrict__ dv,
+                         int64_t kvrow0, float tau) {
+  constexpr int NDT = D / 32;
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, hf = lane >> 5;
+#pragma unroll
+  for (int ib = 0; ib < NDT; ++ib) {
+    const int blk = w + 4 * ib;
+    const bool isk = blk >= 2 * NDT;
+    const int kt = (blk % (2 * NDT)) / NDT, dt = blk % NDT;
+    float* dst = isk ? dk : dv;
+    const float sc = isk ? tau : 1.0f;
+    const int e = 32 * dt + (lane & 31);
+#pragma unroll
+    for (int rr = 0; rr < 16; ++rr) atomicAdd(&dst[(kvrow0 + 32 * kt + acc_row(rr, hf)) * D + e], acc[ib][rr] * sc);
+  }
+}
+
 // ------------------------------------------------------------------ bwd_window
 // One workgroup per (b, KV head, query chunk qc, pair of its query heads), two waves per
 // head (rows qc*64 .. qc*64+63).  Pass 1: the window's LSE by an online max/sum over
@@ -423,6 +460,10 @@ __global__ void __launch_bounds__(256) bwd_pairs(const bf16_t* __restrict__ q, c
   // dk'_c / db'_c partial sums: thread t sums dims t % D over its share of the rows
   constexpr int RSPLIT = 256 / D;
   float kacc = 0.f, bacc = 0.f;
+  f32x16_t dkv[D / 32];  // this wave's dk / dv blocks, summed over the item's tiles
+#pragma unroll
+  for (int ib = 0; ib < D / 32; ++ib) dkv[ib] = zero16();
+  static_assert(BW_ROWS * (D + 4) * 4 <= 2 * (int)sizeof(GradLds<D>::qt), "dq staging fits the q and g tiles");
   const int ntile = (int)((nrows + BW_ROWS - 1) / BW_ROWS);
   for (int j = 0; j < ntile; ++j) {
     const uint32_t r = (uint32_t)j * BW_ROWS + trow;
@@ -467,7 +508,7 @@ __global__ void __launch_bounds__(256) bwd_pairs(const bf16_t* __restrict__ q, c
     if (ok && hf == 0) dsig[pid] = dsg;
     if (hf == 0) {
       sig_s[trow] = ok ? dsg : 0.f;
-      srow[trow] = (uint32_t)row;
+      srow[trow] = ok ? (uint32_t)row : 0xffffffffu;
     }
 #pragma unroll
     for (int tt = 0; tt < 2; ++tt)
@@ -485,15 +526,8 @@ __global__ void __launch_bounds__(256) bwd_pairs(const bf16_t* __restrict__ q, c
 #pragma unroll
     for (int dt = 0; dt < D / 32; ++dt) dqa[dt] = zero16();
     dq_from_ds<D>(L.kv, dp, dqa);
-    if (ok) {
-#pragma unroll
-      for (int dt = 0; dt < D / 32; ++dt)
-#pragma unroll
-        for (int rr = 0; rr < 16; ++rr)
-          atomicAdd(&dq[row * D + 32 * dt + acc_row(rr, hf)], dqa[dt][rr] * tau);
-    }
     __syncthreads();
-    dkdv_from_tiles<D>(L, dk, dv, kvrow0, 64, tau);
+    dkdv_accumulate<D>(L, dkv);
     // dk'_c and db'_c over this tile's rows
     {
       const int e2 = tid % D, part = tid / D;
@@ -504,7 +538,24 @@ __global__ void __launch_bounds__(256) bwd_pairs(const bf16_t* __restrict__ q, c
       }
       if (tid < BW_ROWS) bacc += sig_s[tid];
     }
+    // dq: the tile's rows through LDS (over the q and g tiles, consumed above), then one
+    // atomic add per element with consecutive lanes on consecutive dims of a row
+    __syncthreads();
+    float* dqs = reinterpret_cast<float*>(L.qt);
+    constexpr int LDF = D + 4;
+#pragma unroll
+    for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+      for (int g4 = 0; g4 < 4; ++g4)
+        *reinterpret_cast<float4*>(&dqs[trow * LDF + 32 * dt + 8 * g4 + 4 * hf]) =
+            make_float4(dqa[dt][4 * g4], dqa[dt][4 * g4 + 1], dqa[dt][4 * g4 + 2], dqa[dt][4 * g4 + 3]);
+    __syncthreads();
+    for (int x = tid; x < BW_ROWS * D; x += 256) {
+      const uint32_t rw = srow[x / D];
+      if (rw != 0xffffffffu) atomicAdd(&dq[(int64_t)rw * D + x % D], dqs[(x / D) * LDF + x % D] * tau);
+    }
   }
+  dkdv_flush<D>(dkv, dk, dv, kvrow0, tau);
   // item totals of dk'_c and db'_c
   const int e2 = tid % D, part = tid / D;
   __syncthreads();
