@@ -18,15 +18,14 @@
 //     dL_c = tau sum_j dz_j k_j,  dk_j += a_j dk'_c + tau dz_j L_c.
 //
 // Kernels, in launch order (bf16 I/O, fp32 accumulation in the workspace):
-//   bwd_prep      q^ rows (fp32) and zeroed accumulators
 //   bwd_window    per (b, KV head, query chunk, pair of heads): the window's LSE, the
 //                 row's fusion normaliser Lambda_i and g.o_i, then the window's
 //                 gradients on the MFMA (dq stored, dk/dv added atomically)
 //   bucketing     the forward's (b, head, chunk) bucketing of the selection pairs
 //   bwd_pairs     per bucket work item: the chunk's K/V staged once, 32 gathered rows
-//                 per wave: S, dP' on the MFMA, dsigma per pair, dq (atomic), then dk/dv
+//                 per wave: S, dP' on the MFMA, dsigma and dq per pair, then dk/dv
 //                 over the tile's 128 rows on the MFMA from transposed LDS tiles; dk'/db'
-//   bwd_rows      per row: dq^ from the pairs' dsigma and k', Q-Cal backward
+//   bwd_rows      per row: the pairs' dq partials, dq^ from their dsigma and k', Q-Cal backward
 //   bwd_compress  per (b, KV head, chunk): the landmark compression's backward
 //   bwd_convert   fp32 accumulators to the output dtype
 #include <algorithm>
@@ -43,7 +42,7 @@ constexpr int BW_ROWS = 128;  // rows per tile: 4 waves x 32
 constexpr int LDP = 64 + 8;   // bf16 row stride of the [row][key] P and dS tiles
 
 struct BwdWs {
-  size_t qh, dq, dk, dv, dkc, dbc, lam, dd, dsig, dD, dU, counts, cursor, boff, toff, pairs, tmp, total;
+  size_t dq, dk, dv, dkc, dbc, lam, dd, dsig, dqp, dD, dU, counts, cursor, boff, toff, pairs, tmp, total;
 };
 size_t alb(size_t x) { return (x + 255) / 256 * 256; }
 BwdWs bwd_ws(const Geom& g) {
@@ -56,7 +55,6 @@ BwdWs bwd_ws(const Geom& g) {
     f = off;
     off += alb(bytes);
   };
-  take(w.qh, rows * g.d * 4);
   take(w.dq, rows * g.d * 4);
   take(w.dk, kvrows * g.d * 4);  // dk .. dU are zeroed together: keep them contiguous
   take(w.dv, kvrows * g.d * 4);
@@ -67,6 +65,7 @@ BwdWs bwd_ws(const Geom& g) {
   take(w.lam, rows * 4);
   take(w.dd, rows * 4);
   take(w.dsig, ent * 4);
+  take(w.dqp, ent * g.d * 4);  // per (row, slot) dq of the selected chunk's attention
   take(w.counts, nbk * 4);  // counts and cursor contiguous (zeroed together)
   take(w.cursor, nbk * 4);
   take(w.boff, (nbk + 1) * 4);
@@ -85,46 +84,6 @@ HILS_DEV float wave_sum_f(float v) {
 
 __global__ void __launch_bounds__(256) bwd_zero(float* p, int64_t n) {
   for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256) p[i] = 0.f;
-}
-
-// q^ = q + U_h (D_h q) of every row (fp32), one wave per row, lanes over the head dims;
-// the rank-r intermediate t = D_h q goes through LDS.
-template <int D>
-__global__ void __launch_bounds__(256) bwd_prep(const bf16_t* __restrict__ q, const bf16_t* __restrict__ Dw,
-                                                const bf16_t* __restrict__ Uw, float* __restrict__ qh, int Hq, int N,
-                                                int r, int64_t rows) {
-  constexpr int EPL = D / 64;  // dims per lane
-  __shared__ float tq[4][32];
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-  for (int64_t row = (int64_t)blockIdx.x * 4 + w; row < rows; row += (int64_t)gridDim.x * 4) {
-    const int h = (int)((row / N) % Hq);
-    float x[EPL];
-#pragma unroll
-    for (int u = 0; u < EPL; ++u) x[u] = bf16_to_f32(q[row * D + lane + 64 * u].bits);
-    float out[EPL];
-#pragma unroll
-    for (int u = 0; u < EPL; ++u) out[u] = x[u];
-    if (r > 0) {
-      for (int a = 0; a < r; ++a) {
-        float p = 0.f;
-#pragma unroll
-        for (int u = 0; u < EPL; ++u) p = fmaf(bf16_to_f32(Dw[((int64_t)h * r + a) * D + lane + 64 * u].bits), x[u], p);
-        p = wave_sum_f(p);
-        if (lane == 0) tq[w][a] = p;
-      }
-      __builtin_amdgcn_wave_barrier();
-#pragma unroll
-      for (int u = 0; u < EPL; ++u) {
-        const int e = lane + 64 * u;
-        float acc = 0.f;
-        for (int a = 0; a < r; ++a) acc = fmaf(bf16_to_f32(Uw[((int64_t)h * D + e) * r + a].bits), tq[w][a], acc);
-        out[u] += acc;
-      }
-      __builtin_amdgcn_wave_barrier();
-    }
-#pragma unroll
-    for (int u = 0; u < EPL; ++u) qh[row * D + lane + 64 * u] = out[u];
-  }
 }
 
 // --------------------------------------------------------- shared tile gradients
@@ -418,21 +377,22 @@ __global__ void __launch_bounds__(256) bwd_window(const bf16_t* __restrict__ q, 
 // One work item = up to BUCKET_ITEM_ROWS gathered rows of one bucket (b, h, c), in
 // tiles of 128 (32 per wave).  Per row: S and dP' on the MFMA, the chunk softmax P,
 // e = sum_j P_j dP'_j, w = exp(s_ic - Lambda_i), dsigma = w (e - g.o_i) (stored per pair),
-// dS = P w (dP' - e), dq (added atomically); dk/dv over the tile's rows; and the item's
-// dk'_c = tau sum dsigma q^, db'_c = sum dsigma, added atomically at the end.
+// dS = P w (dP' - e), the pair's dq (stored as a partial); dk/dv over the tile's rows; and the item's
+// sum dsigma q (q^ = (I + U D) q is linear in q) and db'_c = sum dsigma, added atomically.
 template <int D>
 __global__ void __launch_bounds__(256) bwd_pairs(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
                                                  const bf16_t* __restrict__ v, const bf16_t* __restrict__ dO,
-                                                 const float* __restrict__ qh, const float* __restrict__ sel_score,
+                                                 const float* __restrict__ sel_score,
                                                  const float* __restrict__ lam, const float* __restrict__ dd,
                                                  const uint32_t* __restrict__ pairs, const uint32_t* __restrict__ boff,
                                                  const uint32_t* __restrict__ toff, float* __restrict__ dsig,
-                                                 float* __restrict__ dq, float* __restrict__ dk, float* __restrict__ dv,
+                                                 float* __restrict__ dqp, float* __restrict__ dk, float* __restrict__ dv,
                                                  float* __restrict__ dkc, float* __restrict__ dbc, int Hq, int Hkv,
                                                  int N, int C, int K, int nbk) {
   __shared__ GradLds<D> L;
   __shared__ float sig_s[BW_ROWS];
   __shared__ uint32_t srow[BW_ROWS];
+  __shared__ uint32_t spid[BW_ROWS];
   __shared__ float red[2][D + 1];
   const int item = blockIdx.x;
   if ((uint32_t)item >= toff[nbk]) return;
@@ -509,6 +469,7 @@ __global__ void __launch_bounds__(256) bwd_pairs(const bf16_t* __restrict__ q, c
     if (hf == 0) {
       sig_s[trow] = ok ? dsg : 0.f;
       srow[trow] = ok ? (uint32_t)row : 0xffffffffu;
+      spid[trow] = ok ? pid : 0xffffffffu;
     }
 #pragma unroll
     for (int tt = 0; tt < 2; ++tt)
@@ -528,18 +489,17 @@ __global__ void __launch_bounds__(256) bwd_pairs(const bf16_t* __restrict__ q, c
     dq_from_ds<D>(L.kv, dp, dqa);
     __syncthreads();
     dkdv_accumulate<D>(L, dkv);
-    // dk'_c and db'_c over this tile's rows
+    // sum dsigma q and db'_c over this tile's rows (from the staged q rows); dk'_c is
+    // tau (I + U_h D_h) applied to the first sum, in bwd_compress
     {
       const int e2 = tid % D, part = tid / D;
 #pragma unroll 4
-      for (int x = part; x < BW_ROWS; x += RSPLIT) {
-        const float sg = sig_s[x];
-        if (sg != 0.f) kacc = fmaf(sg, qh[(int64_t)srow[x] * D + e2], kacc);
-      }
+      for (int x = part; x < BW_ROWS; x += RSPLIT)
+        kacc = fmaf(sig_s[x], __uint_as_float((uint32_t)L.qt[x * GradLds<D>::LDR + e2] << 16), kacc);
       if (tid < BW_ROWS) bacc += sig_s[tid];
     }
-    // dq: the tile's rows through LDS (over the q and g tiles, consumed above), then one
-    // atomic add per element with consecutive lanes on consecutive dims of a row
+    // dq: the tile's rows through LDS (over the q and g tiles, consumed above), then stored
+    // as the pair's partial (bwd_rows sums a row's partials), whole rows per wave
     __syncthreads();
     float* dqs = reinterpret_cast<float*>(L.qt);
     constexpr int LDF = D + 4;
@@ -551,8 +511,8 @@ __global__ void __launch_bounds__(256) bwd_pairs(const bf16_t* __restrict__ q, c
             make_float4(dqa[dt][4 * g4], dqa[dt][4 * g4 + 1], dqa[dt][4 * g4 + 2], dqa[dt][4 * g4 + 3]);
     __syncthreads();
     for (int x = tid; x < BW_ROWS * D; x += 256) {
-      const uint32_t rw = srow[x / D];
-      if (rw != 0xffffffffu) atomicAdd(&dq[(int64_t)rw * D + x % D], dqs[(x / D) * LDF + x % D] * tau);
+      const uint32_t pq = spid[x / D];
+      if (pq != 0xffffffffu) dqp[(int64_t)pq * D + x % D] = dqs[(x / D) * LDF + x % D] * tau;
     }
   }
   dkdv_flush<D>(dkv, dk, dv, kvrow0, tau);
@@ -566,101 +526,141 @@ __global__ void __launch_bounds__(256) bwd_pairs(const bf16_t* __restrict__ q, c
   }
   __syncthreads();
   const int64_t ci = bhq * C + c;  // landmark head = query head
-  if (tid < D) atomicAdd(&dkc[ci * D + tid], tau * (red[0][tid] + red[1][tid]));
+  if (tid < D) atomicAdd(&dkc[ci * D + tid], red[0][tid] + red[1][tid]);
   float bs = tid < BW_ROWS ? bacc : 0.f;
   bs = wave_sum_f(bs);
   if (lane == 0 && w < 2) atomicAdd(&dbc[ci], bs);
 }
 
 // -------------------------------------------------------------------- bwd_rows
-// Per row (one wave, lanes over the dims): dq^ = tau sum_x dsigma_x k'_(sel x), then the
-// Q-Cal backward: dq += dq^ + D^T (U^T dq^); dU += dq^ (D q)^T and dD += (U^T dq^) q^T are
-// summed over the wave's rows (all of one head) and added atomically at the end.
+// Per row: the selected chunks' dq partials summed into dq; dq^ = tau sum_x dsigma_x
+// k'_(sel x) and the Q-Cal backward dq += dq^ + D^T (U^T dq^); dU += dq^ (D q)^T and
+// dD += (U^T dq^) q^T summed over the workgroup's rows and added atomically at the end.
+// One workgroup per RB_BLOCK consecutive rows of one (b, h), RB rows at a time, with the
+// head's D and U in LDS (fp32): the rank-r products run one (row, a) pair per thread.
+constexpr int RB = 32;         // rows per step
+constexpr int RB_BLOCK = 512;  // rows per workgroup
+constexpr int RMAX = 32;
+
+template <int D>
+struct RowLds {
+  float Dh[RMAX][D];       // D_h [a][e]
+  float Uh[D][RMAX + 1];   // U_h [e][a]
+  float xs[RB][D + 1];     // q rows
+  float gs[RB][D + 1];     // dq^ rows
+  float ts[RB][RMAX + 1];  // D q
+  float us[RB][RMAX + 1];  // U^T dq^
+  int sl[RB][32];          // the rows' selections (K <= 32)
+  float sg[RB][32];        // and tau dsigma
+};
+
+template <int D>
+HILS_DEV void stage_qcal(RowLds<D>& L, const bf16_t* __restrict__ Dw, const bf16_t* __restrict__ Uw, int h, int r) {
+  for (int x = threadIdx.x; x < r * D; x += 256) {
+    L.Dh[x / D][x % D] = bf16_to_f32(Dw[(int64_t)h * r * D + x].bits);
+    L.Uh[x / r][x % r] = bf16_to_f32(Uw[(int64_t)h * D * r + x].bits);
+  }
+}
+
+// t[row][a] = sum_e D[a][e] x[row][e] (or with U^T) for the RB rows: thread -> (row, a).
+template <int D, bool UT>
+HILS_DEV void rank_r(RowLds<D>& L, const float (&x)[RB][D + 1], float (&t)[RB][RMAX + 1], int r) {
+  for (int p = threadIdx.x; p < RB * r; p += 256) {
+    const int row = p % RB, a = p / RB;
+    float acc = 0.f;
+#pragma unroll 8
+    for (int e = 0; e < D; ++e) acc = fmaf(UT ? L.Uh[e][a] : L.Dh[a][e], x[row][e], acc);
+    t[row][a] = acc;
+  }
+}
+
 template <int D>
 __global__ void __launch_bounds__(256) bwd_rows(const bf16_t* __restrict__ q, const bf16_t* __restrict__ Dw,
                                                 const bf16_t* __restrict__ Uw, const float* __restrict__ kc,
                                                 const int32_t* __restrict__ sel, const float* __restrict__ dsig,
-                                                float* __restrict__ dq, float* __restrict__ dD, float* __restrict__ dU,
-                                                int Hq, int N, int C, int K, int r, int rows_per_wave, int64_t nwaves) {
-  constexpr int EPL = D / 64;
-  constexpr int RMAX = 32;
-  __shared__ float tq[4][RMAX], uq[4][RMAX];
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-  const int64_t gw = (int64_t)blockIdx.x * 4 + w;  // wave index: rows_per_wave rows of one (b, h)
-  if (gw >= nwaves) return;  // no barrier below: a whole wave leaves
-  const int64_t waves_per_head = (N + rows_per_wave - 1) / rows_per_wave;
-  const int64_t bh = gw / waves_per_head;
-  const int i0 = (int)(gw % waves_per_head) * rows_per_wave;
+                                                const float* __restrict__ dqp, float* __restrict__ dq,
+                                                float* __restrict__ dD, float* __restrict__ dU, int Hq, int N, int C,
+                                                int K, int r) {
+  __shared__ RowLds<D> L;
+  const int nblk = (N + RB_BLOCK - 1) / RB_BLOCK;
+  const int64_t bh = blockIdx.x / nblk;
+  const int i0 = (int)(blockIdx.x % nblk) * RB_BLOCK, i1 = min(N, i0 + RB_BLOCK);
   const int h = (int)(bh % Hq);
+  const int tid = threadIdx.x;
   const float tau = 1.0f / sqrtf((float)D);
-  float aU[EPL][RMAX], aD[EPL][RMAX];
+  if (r > 0) stage_qcal<D>(L, Dw, Uw, h, r);
+  // this thread's share of dU [e][a] and dD [a][e]: e = tid % D, a in [a0, a0 + NA)
+  constexpr int NA = RMAX * D / 256;
+  const int e_own = tid % D, a0 = (tid / D) * NA;
+  float aU[NA], aD[NA];
 #pragma unroll
-  for (int u = 0; u < EPL; ++u)
-#pragma unroll
-    for (int a = 0; a < RMAX; ++a) aU[u][a] = aD[u][a] = 0.f;
+  for (int u = 0; u < NA; ++u) aU[u] = aD[u] = 0.f;
   const float* kch = kc + bh * C * D;
-  for (int i = i0; i < min(N, i0 + rows_per_wave); ++i) {
-    const int64_t row = bh * N + i;
-    float dqh[EPL];
-#pragma unroll
-    for (int u = 0; u < EPL; ++u) dqh[u] = 0.f;
-    for (int x = 0; x < K; ++x) {
-      const int cc = sel[row * K + x];
-      if (cc < 0) break;
-      const float sg = dsig[row * K + x] * tau;
-#pragma unroll
-      for (int u = 0; u < EPL; ++u) dqh[u] = fmaf(sg, kch[(int64_t)cc * D + lane + 64 * u], dqh[u]);
+  for (int rb = i0; rb < i1; rb += RB) {
+    const int nr = min(RB, i1 - rb);
+    __syncthreads();  // the previous step's rows are consumed (and D, U staged)
+    // the rows' selections and tau dsigma, then their dq partials and dq^ (thread: dim e of
+    // rows rw, rw + 256 / D, ...; independent loads, no trip count read from memory)
+    for (int p = tid; p < RB * K; p += 256) {
+      const int rw = p / K, x = p % K;
+      const bool ok = rw < nr;
+      L.sl[rw][x] = ok ? sel[(bh * N + rb + rw) * K + x] : -1;
+      L.sg[rw][x] = ok ? dsig[(bh * N + rb + rw) * K + x] * tau : 0.f;
     }
-    float add[EPL];
-#pragma unroll
-    for (int u = 0; u < EPL; ++u) add[u] = dqh[u];
-    if (r > 0) {
-      float x[EPL];
-#pragma unroll
-      for (int u = 0; u < EPL; ++u) x[u] = bf16_to_f32(q[row * D + lane + 64 * u].bits);
-      for (int a = 0; a < r; ++a) {
-        float p = 0.f, p2 = 0.f;
-#pragma unroll
-        for (int u = 0; u < EPL; ++u) {
-          const int e = lane + 64 * u;
-          p = fmaf(bf16_to_f32(Dw[((int64_t)h * r + a) * D + e].bits), x[u], p);
-          p2 = fmaf(bf16_to_f32(Uw[((int64_t)h * D + e) * r + a].bits), dqh[u], p2);
-        }
-        p = wave_sum_f(p);
-        p2 = wave_sum_f(p2);
-        if (lane == 0) {
-          tq[w][a] = p;   // (D q)_a
-          uq[w][a] = p2;  // (U^T dq^)_a
-        }
-      }
-      __builtin_amdgcn_wave_barrier();
-#pragma unroll
-      for (int u = 0; u < EPL; ++u) {
-        const int e = lane + 64 * u;
-#pragma unroll
-        for (int a = 0; a < RMAX; ++a) {
-          if (a < r) {
-            add[u] = fmaf(bf16_to_f32(Dw[((int64_t)h * r + a) * D + e].bits), uq[w][a], add[u]);
-            aU[u][a] = fmaf(dqh[u], tq[w][a], aU[u][a]);
-            aD[u][a] = fmaf(uq[w][a], x[u], aD[u][a]);
+    __syncthreads();
+    for (int p = tid; p < RB * D; p += 256) {
+      const int rw = p / D, e = p % D;
+      float gh = 0.f, part = 0.f, xq = 0.f;
+      if (rw < nr) {
+        const int64_t row = bh * N + rb + rw;
+        const float* dqr = dqp + row * K * D + e;
+#pragma unroll 8
+        for (int x = 0; x < K; ++x) {
+          const int cc = L.sl[rw][x];
+          if (cc >= 0) {
+            gh = fmaf(L.sg[rw][x], kch[(int64_t)cc * D + e], gh);
+            part += dqr[(int64_t)x * D];
           }
         }
+        xq = bf16_to_f32(q[row * D + e].bits);
+        dq[row * D + e] += part + gh;  // D^T (U^T dq^) is added below
       }
-      __builtin_amdgcn_wave_barrier();
+      L.gs[rw][e] = gh;
+      L.xs[rw][e] = xq;
+    }
+    if (r == 0) continue;
+    __syncthreads();
+    rank_r<D, false>(L, L.xs, L.ts, r);  // D q
+    rank_r<D, true>(L, L.gs, L.us, r);   // U^T dq^
+    __syncthreads();
+    for (int p = tid; p < nr * D; p += 256) {
+      const int rw = p / D, e = p % D;
+      float acc = 0.f;
+      for (int a = 0; a < r; ++a) acc = fmaf(L.Dh[a][e], L.us[rw][a], acc);
+      dq[(bh * N + rb + rw) * D + e] += acc;
     }
 #pragma unroll
-    for (int u = 0; u < EPL; ++u) dq[row * D + lane + 64 * u] += add[u];
-  }
-  if (r > 0 && i0 < N) {
-#pragma unroll
-    for (int u = 0; u < EPL; ++u) {
-      const int e = lane + 64 * u;
-#pragma unroll
-      for (int a = 0; a < RMAX; ++a)
-        if (a < r) {
-          atomicAdd(&dU[((int64_t)h * D + e) * r + a], aU[u][a]);
-          atomicAdd(&dD[((int64_t)h * r + a) * D + e], aD[u][a]);
+    for (int u = 0; u < NA; ++u) {
+      const int a = a0 + u;
+      if (a < r) {
+        float su = 0.f, sd = 0.f;
+        for (int rw = 0; rw < nr; ++rw) {
+          su = fmaf(L.gs[rw][e_own], L.ts[rw][a], su);
+          sd = fmaf(L.us[rw][a], L.xs[rw][e_own], sd);
         }
+        aU[u] += su;
+        aD[u] += sd;
+      }
+    }
+  }
+  if (r > 0) {
+#pragma unroll
+    for (int u = 0; u < NA; ++u) {
+      const int a = a0 + u;
+      if (a < r) {
+        atomicAdd(&dU[((int64_t)h * D + e_own) * r + a], aU[u]);
+        atomicAdd(&dD[((int64_t)h * r + a) * D + e_own], aD[u]);
+      }
     }
   }
 }
@@ -673,11 +673,12 @@ __global__ void __launch_bounds__(256) bwd_rows(const bf16_t* __restrict__ q, co
 template <int D>
 __global__ void __launch_bounds__(256) bwd_compress(const bf16_t* __restrict__ k, const bf16_t* __restrict__ lmk,
                                                     const float* __restrict__ dkc, const float* __restrict__ dbc,
+                                                    const bf16_t* __restrict__ Dw, const bf16_t* __restrict__ Uw,
                                                     float* __restrict__ dk, bf16_t* __restrict__ dlmk, int Hl, int Hkv,
-                                                    int N, int C) {
+                                                    int N, int C, int r) {
   __shared__ float ks[64][D + 1];
   __shared__ float acc[64][D + 1];
-  __shared__ float Ls[D], gk[D];
+  __shared__ float Ls[D], gk[D], tr[32];
   __shared__ float zs[64], as[64], das[64];
   const int c = blockIdx.x % C, bkv = blockIdx.x / C;
   const int kvh = bkv % Hkv, b = bkv / Hkv;
@@ -695,9 +696,26 @@ __global__ void __launch_bounds__(256) bwd_compress(const bf16_t* __restrict__ k
     __syncthreads();
     for (int e = tid; e < D; e += 256) {
       Ls[e] = bf16_to_f32(lmk[ci * D + e].bits);
-      gk[e] = dkc[ci * D + e];
+      gk[e] = dkc[ci * D + e];  // sum over the chunk's pairs of dsigma q
     }
     const float gb = dbc[ci];
+    __syncthreads();
+    // dk' = tau (I + U_l D_l) (sum dsigma q): the scores use q^ = q + U (D q)
+    if (r > 0) {
+      if (tid < r) {
+        float t = 0.f;
+        for (int e = 0; e < D; ++e) t = fmaf(bf16_to_f32(Dw[((int64_t)l * r + tid) * D + e].bits), gk[e], t);
+        tr[tid] = t;
+      }
+      __syncthreads();
+      for (int e = tid; e < D; e += 256) {
+        float acc2 = gk[e];
+        for (int a2 = 0; a2 < r; ++a2) acc2 = fmaf(bf16_to_f32(Uw[((int64_t)l * D + e) * r + a2].bits), tr[a2], acc2);
+        gk[e] = acc2 * tau;
+      }
+    } else {
+      for (int e = tid; e < D; e += 256) gk[e] *= tau;
+    }
     __syncthreads();
     // z_j and dk'.k_j, four threads per key
     {
@@ -754,7 +772,6 @@ unsigned grid_for(int64_t n) { return (unsigned)std::max<int64_t>(1, std::min<in
 template <int D>
 hipError_t launch_bwd_d(const Geom& g, const BwdArgs& a, char* ws, hipStream_t st) {
   const BwdWs w = bwd_ws(g);
-  float* qh = (float*)(ws + w.qh);
   float* dq = (float*)(ws + w.dq);
   float* dk = (float*)(ws + w.dk);
   float* dv = (float*)(ws + w.dv);
@@ -772,8 +789,7 @@ hipError_t launch_bwd_d(const Geom& g, const BwdArgs& a, char* ws, hipStream_t s
   // the accumulators dk .. dU are contiguous
   const int64_t nz = (int64_t)(w.lam - w.dk) / 4;
   hipLaunchKernelGGL(bwd_zero, dim3(grid_for(nz)), dim3(256), 0, st, dk, nz);
-  hipLaunchKernelGGL((bwd_prep<D>), dim3((unsigned)std::min<int64_t>((rows + 3) / 4, 65536)), dim3(256), 0, st, q, Dw,
-                     Uw, qh, g.Hq, g.N, g.r, rows);
+  const int nrb = (g.N + RB_BLOCK - 1) / RB_BLOCK;
   const int NQC = (g.N + 63) / 64;
   const int ngb = (g.G() + 1) / 2;
   hipLaunchKernelGGL((bwd_window<D>), dim3(g.B * g.Hkv * NQC * ngb), dim3(256), 0, st, q, k, v, (const bf16_t*)a.o,
@@ -789,17 +805,16 @@ hipError_t launch_bwd_d(const Geom& g, const BwdArgs& a, char* ws, hipStream_t s
                                    (uint32_t*)(ws + w.tmp)},
                         st);
     hipLaunchKernelGGL((bwd_pairs<D>), dim3((unsigned)items), dim3(256), 0, st, q, k, v, (const bf16_t*)a.dO,
-                       (const float*)qh, a.sel_score, (const float*)lam, (const float*)dd, (const uint32_t*)pairs,
-                       (const uint32_t*)boff, (const uint32_t*)toff, dsig, dq, dk, dv, dkc, dbc, g.Hq, g.Hkv, g.N, C,
+                       a.sel_score, (const float*)lam, (const float*)dd, (const uint32_t*)pairs,
+                       (const uint32_t*)boff, (const uint32_t*)toff, dsig, (float*)(ws + w.dqp), dk, dv, dkc, dbc,
+                       g.Hq, g.Hkv, g.N, C,
                        g.K, nbk);
   }
-  constexpr int RPW = 64;  // rows per wave in bwd_rows
-  const int64_t nwaves = (int64_t)g.B * g.Hq * ((g.N + RPW - 1) / RPW);
-  hipLaunchKernelGGL((bwd_rows<D>), dim3((unsigned)((nwaves + 3) / 4)), dim3(256), 0, st, q, Dw, Uw, a.kc, a.sel_idx,
-                     (const float*)dsig, dq, dD, dU, g.Hq, g.N, C, g.K, g.r, RPW, nwaves);
+  hipLaunchKernelGGL((bwd_rows<D>), dim3(g.B * g.Hq * nrb), dim3(256), 0, st, q, Dw, Uw, a.kc, a.sel_idx,
+                     (const float*)dsig, (const float*)(ws + w.dqp), dq, dD, dU, g.Hq, g.N, C, g.K, g.r);
   if (C > 0)
     hipLaunchKernelGGL((bwd_compress<D>), dim3(g.B * g.Hkv * C), dim3(256), 0, st, k, (const bf16_t*)a.lmk,
-                       (const float*)dkc, (const float*)dbc, dk, (bf16_t*)a.dlmk, g.Hl, g.Hkv, g.N, C);
+                       (const float*)dkc, (const float*)dbc, Dw, Uw, dk, (bf16_t*)a.dlmk, g.Hl, g.Hkv, g.N, C, g.r);
   const int64_t kvn = (int64_t)g.B * g.Hkv * g.N * D;
   hipLaunchKernelGGL(bwd_convert, dim3(grid_for(rows * D)), dim3(256), 0, st, (const float*)dq, (bf16_t*)a.dq, rows * D);
   hipLaunchKernelGGL(bwd_convert, dim3(grid_for(kvn)), dim3(256), 0, st, (const float*)dk, (bf16_t*)a.dk, kvn);
