@@ -25,7 +25,9 @@
 //   bwd_pairs     per bucket work item: the chunk's K/V staged once, 32 gathered rows
 //                 per wave: S, dP' on the MFMA, dsigma and dq per pair, then dk/dv
 //                 over the tile's 128 rows on the MFMA from transposed LDS tiles; dk'/db'
-//   bwd_rows      per row: the pairs' dq partials, dq^ from their dsigma and k', Q-Cal backward
+//   bwd_dq_sum    per row: the pairs' dq partials and dq^ from their dsigma and k'
+//   bwd_qcal      Q-Cal backward on the MFMA: dq += D^T U^T dq^, G = sum dq^ q^T per head,
+//                 then dU = G D^T, dD = U^T G (bwd_qcal_weights)
 //   bwd_compress  per (b, KV head, chunk): the landmark compression's backward
 //   bwd_convert   fp32 accumulators to the output dtype
 #include <algorithm>
@@ -42,7 +44,7 @@ constexpr int BW_ROWS = 128;  // rows per tile: 4 waves x 32
 constexpr int LDP = 64 + 8;   // bf16 row stride of the [row][key] P and dS tiles
 
 struct BwdWs {
-  size_t dq, dk, dv, dkc, dbc, lam, dd, dsig, dqp, dD, dU, counts, cursor, boff, toff, pairs, tmp, total;
+  size_t dq, dk, dv, dkc, dbc, G, lam, dd, dsig, dqp, dqh, counts, cursor, boff, toff, pairs, tmp, total;
 };
 size_t alb(size_t x) { return (x + 255) / 256 * 256; }
 BwdWs bwd_ws(const Geom& g) {
@@ -60,12 +62,12 @@ BwdWs bwd_ws(const Geom& g) {
   take(w.dv, kvrows * g.d * 4);
   take(w.dkc, lrows * g.d * 4);
   take(w.dbc, lrows * 4);
-  take(w.dD, (size_t)g.Hq * r * g.d * 4);
-  take(w.dU, (size_t)g.Hq * g.d * r * 4);
+  take(w.G, r > 0 ? (size_t)g.Hq * g.d * g.d * 4 : 0);  // sum over rows of dq^ q^T, per head
   take(w.lam, rows * 4);
   take(w.dd, rows * 4);
   take(w.dsig, ent * 4);
   take(w.dqp, ent * g.d * 4);  // per (row, slot) dq of the selected chunk's attention
+  take(w.dqh, r > 0 ? rows * g.d * 2 : 0);  // dq^ (bf16) for the Q-Cal backward
   take(w.counts, nbk * 4);  // counts and cursor contiguous (zeroed together)
   take(w.cursor, nbk * 4);
   take(w.boff, (nbk + 1) * 4);
@@ -532,136 +534,166 @@ __global__ void __launch_bounds__(256) bwd_pairs(const bf16_t* __restrict__ q, c
   if (lane == 0 && w < 2) atomicAdd(&dbc[ci], bs);
 }
 
-// -------------------------------------------------------------------- bwd_rows
-// Per row: the selected chunks' dq partials summed into dq; dq^ = tau sum_x dsigma_x
-// k'_(sel x) and the Q-Cal backward dq += dq^ + D^T (U^T dq^); dU += dq^ (D q)^T and
-// dD += (U^T dq^) q^T summed over the workgroup's rows and added atomically at the end.
-// One workgroup per RB_BLOCK consecutive rows of one (b, h), RB rows at a time, with the
-// head's D and U in LDS (fp32): the rank-r products run one (row, a) pair per thread.
-constexpr int RB = 32;         // rows per step
-constexpr int RB_BLOCK = 512;  // rows per workgroup
-constexpr int RMAX = 32;
+// ------------------------------------------------------------------ bwd_dq_sum
+// Per row (one wave, lanes over the dims): dq += the selected chunks' dq partials +
+// dq^, dq^ = tau sum_x dsigma_x k'_(sel x); dq^ is also kept (bf16) for the Q-Cal
+// backward.  The row's selections are read once and broadcast from lanes.
+template <int D>
+__global__ void __launch_bounds__(256) bwd_dq_sum(const float* __restrict__ kc, const int32_t* __restrict__ sel,
+                                                  const float* __restrict__ dsig, const float* __restrict__ dqp,
+                                                  float* __restrict__ dq, bf16_t* __restrict__ dqh, int N, int C, int K,
+                                                  int64_t rows) {
+  constexpr int EPL = D / 64;
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const float tau = 1.0f / sqrtf((float)D);
+  for (int64_t row = (int64_t)blockIdx.x * 4 + w; row < rows; row += (int64_t)gridDim.x * 4) {
+    const int32_t sl = lane < K ? sel[row * K + lane] : -1;
+    const float sg = lane < K ? dsig[row * K + lane] * tau : 0.f;
+    const int n = __popcll(__ballot(sl >= 0));  // valid selections come first
+    const float* kch = kc + (row / N) * (int64_t)C * D + lane * EPL;
+    const float* pr = dqp + row * K * D + lane * EPL;
+    float acc[EPL], gh[EPL];
+#pragma unroll
+    for (int u = 0; u < EPL; ++u) acc[u] = gh[u] = 0.f;
+#pragma unroll 4
+    for (int x = 0; x < n; ++x) {
+      const int cc = __builtin_amdgcn_readlane(sl, x);
+      const float sgx = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(sg), x));
+#pragma unroll
+      for (int u = 0; u < EPL; ++u) {
+        gh[u] = fmaf(sgx, kch[(int64_t)cc * D + u], gh[u]);
+        acc[u] += pr[(int64_t)x * D + u];
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < EPL; ++u) {
+      dq[row * D + lane * EPL + u] += acc[u] + gh[u];
+      if (dqh) dqh[row * D + lane * EPL + u].bits = f32_to_bf16(gh[u]);
+    }
+  }
+}
+
+// -------------------------------------------------------------------- bwd_qcal
+// Q-Cal backward on the MFMA for the rows of one (b, h), 128 rows (32 per wave) at a time:
+//   u = dQ^ U (rows x r),  dq += u D (rows x d),  G += dQ^^T Q (d x d, summed over rows),
+// with D^T, U^T and the rows' q, dq^ and u as bf16 tiles in LDS; each wave keeps a
+// quarter of G's 32x32 tiles in registers and adds them to the head's G at the end.
+// dU = G D^T and dD = U^T G follow per head (bwd_qcal_weights).
+constexpr int QC_BLOCK = 1024;  // rows per workgroup
+constexpr int RPAD = 32 + 8;    // row stride of the rank-r tiles (r <= 32, zero padded)
 
 template <int D>
-struct RowLds {
-  float Dh[RMAX][D];       // D_h [a][e]
-  float Uh[D][RMAX + 1];   // U_h [e][a]
-  float xs[RB][D + 1];     // q rows
-  float gs[RB][D + 1];     // dq^ rows
-  float ts[RB][RMAX + 1];  // D q
-  float us[RB][RMAX + 1];  // U^T dq^
-  int sl[RB][32];          // the rows' selections (K <= 32)
-  float sg[RB][32];        // and tau dsigma
+struct QcalLds {
+  static constexpr int LDG = D + 8;
+  uint16_t dt[D * RPAD];        // D^T [e][a]
+  uint16_t ut[32 * LDG];        // U^T [a][e]
+  uint16_t qt[BW_ROWS * LDG];   // q rows
+  uint16_t gt[BW_ROWS * LDG];   // dq^ rows
+  uint16_t vt[BW_ROWS * RPAD];  // u rows
 };
 
 template <int D>
-HILS_DEV void stage_qcal(RowLds<D>& L, const bf16_t* __restrict__ Dw, const bf16_t* __restrict__ Uw, int h, int r) {
-  for (int x = threadIdx.x; x < r * D; x += 256) {
-    L.Dh[x / D][x % D] = bf16_to_f32(Dw[(int64_t)h * r * D + x].bits);
-    L.Uh[x / r][x % r] = bf16_to_f32(Uw[(int64_t)h * D * r + x].bits);
-  }
-}
-
-// t[row][a] = sum_e D[a][e] x[row][e] (or with U^T) for the RB rows: thread -> (row, a).
-template <int D, bool UT>
-HILS_DEV void rank_r(RowLds<D>& L, const float (&x)[RB][D + 1], float (&t)[RB][RMAX + 1], int r) {
-  for (int p = threadIdx.x; p < RB * r; p += 256) {
-    const int row = p % RB, a = p / RB;
-    float acc = 0.f;
-#pragma unroll 8
-    for (int e = 0; e < D; ++e) acc = fmaf(UT ? L.Uh[e][a] : L.Dh[a][e], x[row][e], acc);
-    t[row][a] = acc;
-  }
-}
-
-template <int D>
-__global__ void __launch_bounds__(256) bwd_rows(const bf16_t* __restrict__ q, const bf16_t* __restrict__ Dw,
-                                                const bf16_t* __restrict__ Uw, const float* __restrict__ kc,
-                                                const int32_t* __restrict__ sel, const float* __restrict__ dsig,
-                                                const float* __restrict__ dqp, float* __restrict__ dq,
-                                                float* __restrict__ dD, float* __restrict__ dU, int Hq, int N, int C,
-                                                int K, int r) {
-  __shared__ RowLds<D> L;
-  const int nblk = (N + RB_BLOCK - 1) / RB_BLOCK;
+__global__ void __launch_bounds__(256) bwd_qcal(const bf16_t* __restrict__ q, const bf16_t* __restrict__ Dw,
+                                                const bf16_t* __restrict__ Uw, const bf16_t* __restrict__ dqh,
+                                                float* __restrict__ dq, float* __restrict__ G, int Hq, int N, int r) {
+  constexpr int LDG = QcalLds<D>::LDG, NDT = D / 32;
+  constexpr int NGT = NDT * NDT, GPW = (NGT + 3) / 4;  // G tiles, per wave
+  __shared__ QcalLds<D> L;
+  const int nblk = (N + QC_BLOCK - 1) / QC_BLOCK;
   const int64_t bh = blockIdx.x / nblk;
-  const int i0 = (int)(blockIdx.x % nblk) * RB_BLOCK, i1 = min(N, i0 + RB_BLOCK);
+  const int i0 = (int)(blockIdx.x % nblk) * QC_BLOCK, i1 = min(N, i0 + QC_BLOCK);
   const int h = (int)(bh % Hq);
-  const int tid = threadIdx.x;
-  const float tau = 1.0f / sqrtf((float)D);
-  if (r > 0) stage_qcal<D>(L, Dw, Uw, h, r);
-  // this thread's share of dU [e][a] and dD [a][e]: e = tid % D, a in [a0, a0 + NA)
-  constexpr int NA = RMAX * D / 256;
-  const int e_own = tid % D, a0 = (tid / D) * NA;
-  float aU[NA], aD[NA];
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, hf = lane >> 5;
+  for (int x = tid; x < D * RPAD; x += 256) {  // D^T and U^T, zero beyond rank r
+    const int e = x / RPAD, a = x % RPAD;
+    L.dt[x] = a < r ? Dw[((int64_t)h * r + a) * D + e].bits : (uint16_t)0;
+  }
+  for (int x = tid; x < 32 * LDG; x += 256) {
+    const int a = x / LDG, e = x % LDG;
+    L.ut[x] = (a < r && e < D) ? Uw[((int64_t)h * D + e) * r + a].bits : (uint16_t)0;
+  }
+  f32x16_t gacc[GPW];
 #pragma unroll
-  for (int u = 0; u < NA; ++u) aU[u] = aD[u] = 0.f;
-  const float* kch = kc + bh * C * D;
-  for (int rb = i0; rb < i1; rb += RB) {
-    const int nr = min(RB, i1 - rb);
-    __syncthreads();  // the previous step's rows are consumed (and D, U staged)
-    // the rows' selections and tau dsigma, then their dq partials and dq^ (thread: dim e of
-    // rows rw, rw + 256 / D, ...; independent loads, no trip count read from memory)
-    for (int p = tid; p < RB * K; p += 256) {
-      const int rw = p / K, x = p % K;
-      const bool ok = rw < nr;
-      L.sl[rw][x] = ok ? sel[(bh * N + rb + rw) * K + x] : -1;
-      L.sg[rw][x] = ok ? dsig[(bh * N + rb + rw) * K + x] * tau : 0.f;
-    }
-    __syncthreads();
-    for (int p = tid; p < RB * D; p += 256) {
-      const int rw = p / D, e = p % D;
-      float gh = 0.f, part = 0.f, xq = 0.f;
-      if (rw < nr) {
-        const int64_t row = bh * N + rb + rw;
-        const float* dqr = dqp + row * K * D + e;
-#pragma unroll 8
-        for (int x = 0; x < K; ++x) {
-          const int cc = L.sl[rw][x];
-          if (cc >= 0) {
-            gh = fmaf(L.sg[rw][x], kch[(int64_t)cc * D + e], gh);
-            part += dqr[(int64_t)x * D];
-          }
-        }
-        xq = bf16_to_f32(q[row * D + e].bits);
-        dq[row * D + e] += part + gh;  // D^T (U^T dq^) is added below
+  for (int t = 0; t < GPW; ++t) gacc[t] = zero16();
+  const int rl = 32 * w + (lane & 31);
+  for (int rb = i0; rb < i1; rb += BW_ROWS) {
+    __syncthreads();  // previous rows consumed (and the weights staged)
+    for (int x = tid; x < BW_ROWS * (D / 8); x += 256) {  // q and dq^ rows, 16 bytes per thread
+      const int rw = x / (D / 8), sg = x % (D / 8);
+      u32x4_t qv = {0u, 0u, 0u, 0u}, gv = {0u, 0u, 0u, 0u};
+      if (rb + rw < i1) {
+        const int64_t off = (bh * N + rb + rw) * D + 8 * sg;
+        qv = *reinterpret_cast<const u32x4_t*>(q + off);
+        gv = *reinterpret_cast<const u32x4_t*>(dqh + off);
       }
-      L.gs[rw][e] = gh;
-      L.xs[rw][e] = xq;
+      *reinterpret_cast<u32x4_t*>(&L.qt[rw * LDG + 8 * sg]) = qv;
+      *reinterpret_cast<u32x4_t*>(&L.gt[rw * LDG + 8 * sg]) = gv;
     }
-    if (r == 0) continue;
     __syncthreads();
-    rank_r<D, false>(L, L.xs, L.ts, r);  // D q
-    rank_r<D, true>(L, L.gs, L.us, r);   // U^T dq^
-    __syncthreads();
-    for (int p = tid; p < nr * D; p += 256) {
-      const int rw = p / D, e = p % D;
-      float acc = 0.f;
-      for (int a = 0; a < r; ++a) acc = fmaf(L.Dh[a][e], L.us[rw][a], acc);
-      dq[(bh * N + rb + rw) * D + e] += acc;
-    }
+    // u = dQ^ U for the wave's 32 rows: A = dq^ rows (k = dims), B = U^T rows (lane = a)
+    f32x16_t u = zero16();
 #pragma unroll
-    for (int u = 0; u < NA; ++u) {
-      const int a = a0 + u;
-      if (a < r) {
-        float su = 0.f, sd = 0.f;
-        for (int rw = 0; rw < nr; ++rw) {
-          su = fmaf(L.gs[rw][e_own], L.ts[rw][a], su);
-          sd = fmaf(L.us[rw][a], L.xs[rw][e_own], sd);
-        }
-        aU[u] += su;
-        aD[u] += sd;
+    for (int ks = 0; ks < D / 16; ++ks)
+      u = mfma32(lds_op16(&L.gt[rl * LDG + 16 * ks + 8 * hf]), lds_op16(&L.ut[(lane & 31) * LDG + 16 * ks + 8 * hf]), u);
+    // u[row acc_row][a = lane] -> the u tile (bf16), then dq += u D
+#pragma unroll
+    for (int rr = 0; rr < 16; ++rr) L.vt[(32 * w + acc_row(rr, hf)) * RPAD + (lane & 31)] = f32_to_bf16(u[rr]);
+    __builtin_amdgcn_wave_barrier();
+#pragma unroll
+    for (int dtile = 0; dtile < NDT; ++dtile) {
+      f32x16_t y = zero16();
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks)
+        y = mfma32(lds_op16(&L.vt[rl * RPAD + 16 * ks + 8 * hf]),
+                   lds_op16(&L.dt[(32 * dtile + (lane & 31)) * RPAD + 16 * ks + 8 * hf]), y);
+#pragma unroll
+      for (int rr = 0; rr < 16; ++rr) {
+        const int rw = rb + 32 * w + acc_row(rr, hf);
+        if (rw < i1) dq[(bh * N + rw) * D + 32 * dtile + (lane & 31)] += y[rr];
+      }
+    }
+    // G += dQ^^T Q over the 128 rows: A = dq^^T, B = Q (both transposed reads, k = rows)
+#pragma unroll
+    for (int t = 0; t < GPW; ++t) {
+      const int gt_ = w + 4 * t;
+      if (gt_ < NGT) {
+        const int ta = gt_ / NDT, tb = gt_ % NDT;
+#pragma unroll
+        for (int ks2 = 0; ks2 < BW_ROWS / 16; ++ks2)
+          gacc[t] = mfma32(vt_operand<LDG>(L.gt, ta, ks2, lane), vt_operand<LDG>(L.qt, tb, ks2, lane), gacc[t]);
       }
     }
   }
-  if (r > 0) {
 #pragma unroll
-    for (int u = 0; u < NA; ++u) {
-      const int a = a0 + u;
-      if (a < r) {
-        atomicAdd(&dU[((int64_t)h * D + e_own) * r + a], aU[u]);
-        atomicAdd(&dD[((int64_t)h * r + a) * D + e_own], aD[u]);
-      }
+  for (int t = 0; t < GPW; ++t) {
+    const int gt_ = w + 4 * t;
+    if (gt_ < NGT) {
+      const int ta = gt_ / NDT, tb = gt_ % NDT;
+#pragma unroll
+      for (int rr = 0; rr < 16; ++rr)
+        atomicAdd(&G[((int64_t)h * D + 32 * ta + acc_row(rr, hf)) * D + 32 * tb + (lane & 31)], gacc[t][rr]);
     }
+  }
+}
+
+// dU_h = G_h D_h^T and dD_h = U_h^T G_h (bf16 out), one workgroup per head.
+template <int D>
+__global__ void __launch_bounds__(256) bwd_qcal_weights(const float* __restrict__ G, const bf16_t* __restrict__ Dw,
+                                                        const bf16_t* __restrict__ Uw, bf16_t* __restrict__ dD,
+                                                        bf16_t* __restrict__ dU, int r) {
+  const int h = blockIdx.x;
+  const float* Gh = G + (int64_t)h * D * D;
+  for (int x = threadIdx.x; x < D * r; x += 256) {
+    const int e = x / r, a = x % r;  // dU [e][a] = sum_f G[e][f] D[a][f]
+    float acc = 0.f;
+    for (int f = 0; f < D; ++f) acc = fmaf(Gh[e * D + f], bf16_to_f32(Dw[((int64_t)h * r + a) * D + f].bits), acc);
+    dU[((int64_t)h * D + e) * r + a].bits = f32_to_bf16(acc);
+  }
+  for (int x = threadIdx.x; x < r * D; x += 256) {
+    const int a = x / D, f = x % D;  // dD [a][f] = sum_e U[e][a] G[e][f]
+    float acc = 0.f;
+    for (int e = 0; e < D; ++e) acc = fmaf(bf16_to_f32(Uw[((int64_t)h * D + e) * r + a].bits), Gh[e * D + f], acc);
+    dD[((int64_t)h * r + a) * D + f].bits = f32_to_bf16(acc);
   }
 }
 
@@ -777,8 +809,7 @@ hipError_t launch_bwd_d(const Geom& g, const BwdArgs& a, char* ws, hipStream_t s
   float* dv = (float*)(ws + w.dv);
   float* dkc = (float*)(ws + w.dkc);
   float* dbc = (float*)(ws + w.dbc);
-  float* dD = (float*)(ws + w.dD);
-  float* dU = (float*)(ws + w.dU);
+  float* G = (float*)(ws + w.G);
   float* lam = (float*)(ws + w.lam);
   float* dd = (float*)(ws + w.dd);
   float* dsig = (float*)(ws + w.dsig);
@@ -789,7 +820,6 @@ hipError_t launch_bwd_d(const Geom& g, const BwdArgs& a, char* ws, hipStream_t s
   // the accumulators dk .. dU are contiguous
   const int64_t nz = (int64_t)(w.lam - w.dk) / 4;
   hipLaunchKernelGGL(bwd_zero, dim3(grid_for(nz)), dim3(256), 0, st, dk, nz);
-  const int nrb = (g.N + RB_BLOCK - 1) / RB_BLOCK;
   const int NQC = (g.N + 63) / 64;
   const int ngb = (g.G() + 1) / 2;
   hipLaunchKernelGGL((bwd_window<D>), dim3(g.B * g.Hkv * NQC * ngb), dim3(256), 0, st, q, k, v, (const bf16_t*)a.o,
@@ -810,8 +840,16 @@ hipError_t launch_bwd_d(const Geom& g, const BwdArgs& a, char* ws, hipStream_t s
                        g.Hq, g.Hkv, g.N, C,
                        g.K, nbk);
   }
-  hipLaunchKernelGGL((bwd_rows<D>), dim3(g.B * g.Hq * nrb), dim3(256), 0, st, q, Dw, Uw, a.kc, a.sel_idx,
-                     (const float*)dsig, (const float*)(ws + w.dqp), dq, dD, dU, g.Hq, g.N, C, g.K, g.r);
+  bf16_t* dqh = g.r > 0 ? (bf16_t*)(ws + w.dqh) : nullptr;
+  hipLaunchKernelGGL((bwd_dq_sum<D>), dim3((unsigned)std::min<int64_t>((rows + 3) / 4, 1 << 20)), dim3(256), 0, st,
+                     a.kc, a.sel_idx, (const float*)dsig, (const float*)(ws + w.dqp), dq, dqh, g.N, C, g.K, rows);
+  if (g.r > 0) {
+    const int nqb = (g.N + QC_BLOCK - 1) / QC_BLOCK;
+    hipLaunchKernelGGL((bwd_qcal<D>), dim3(g.B * g.Hq * nqb), dim3(256), 0, st, q, Dw, Uw, (const bf16_t*)dqh, dq, G,
+                       g.Hq, g.N, g.r);
+    hipLaunchKernelGGL((bwd_qcal_weights<D>), dim3(g.Hq), dim3(256), 0, st, (const float*)G, Dw, Uw, (bf16_t*)a.dD,
+                       (bf16_t*)a.dU, g.r);
+  }
   if (C > 0)
     hipLaunchKernelGGL((bwd_compress<D>), dim3(g.B * g.Hkv * C), dim3(256), 0, st, k, (const bf16_t*)a.lmk,
                        (const float*)dkc, (const float*)dbc, Dw, Uw, dk, (bf16_t*)a.dlmk, g.Hl, g.Hkv, g.N, C, g.r);
@@ -819,11 +857,6 @@ hipError_t launch_bwd_d(const Geom& g, const BwdArgs& a, char* ws, hipStream_t s
   hipLaunchKernelGGL(bwd_convert, dim3(grid_for(rows * D)), dim3(256), 0, st, (const float*)dq, (bf16_t*)a.dq, rows * D);
   hipLaunchKernelGGL(bwd_convert, dim3(grid_for(kvn)), dim3(256), 0, st, (const float*)dk, (bf16_t*)a.dk, kvn);
   hipLaunchKernelGGL(bwd_convert, dim3(grid_for(kvn)), dim3(256), 0, st, (const float*)dv, (bf16_t*)a.dv, kvn);
-  if (g.r > 0) {
-    const int64_t nr = (int64_t)g.Hq * g.r * D;
-    hipLaunchKernelGGL(bwd_convert, dim3(grid_for(nr)), dim3(256), 0, st, (const float*)dD, (bf16_t*)a.dD, nr);
-    hipLaunchKernelGGL(bwd_convert, dim3(grid_for(nr)), dim3(256), 0, st, (const float*)dU, (bf16_t*)a.dU, nr);
-  }
   return hipGetLastError();
 }
 
