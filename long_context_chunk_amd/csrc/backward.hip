@@ -395,6 +395,7 @@ __global__ void __launch_bounds__(256) bwd_pairs(const bf16_t* __restrict__ q, c
   __shared__ float sig_s[BW_ROWS];
   __shared__ uint32_t srow[BW_ROWS];
   __shared__ uint32_t spid[BW_ROWS];
+  __shared__ uint32_t ipid[BUCKET_ITEM_ROWS];  // the item's pair ids
   __shared__ float red[2][D + 1];
   const int item = blockIdx.x;
   if ((uint32_t)item >= toff[nbk]) return;
@@ -418,7 +419,9 @@ __global__ void __launch_bounds__(256) bwd_pairs(const bf16_t* __restrict__ q, c
   const float tau = 1.0f / sqrtf((float)D);
   const float cl = tau * 1.44269504088896340736f;
   const int trow = 32 * w + (lane & 31);
+  for (uint32_t x = tid; x < nrows; x += 256) ipid[x] = pp[x];
   stage_kv<bf16_t, D, 1>(L.kv, k, v, kvrow0, 64, tid, 256);
+  __syncthreads();
   // dk'_c / db'_c partial sums: thread t sums dims t % D over its share of the rows
   constexpr int RSPLIT = 256 / D;
   float kacc = 0.f, bacc = 0.f;
@@ -427,18 +430,36 @@ __global__ void __launch_bounds__(256) bwd_pairs(const bf16_t* __restrict__ q, c
   for (int ib = 0; ib < D / 32; ++ib) dkv[ib] = zero16();
   static_assert(BW_ROWS * (D + 4) * 4 <= 2 * (int)sizeof(GradLds<D>::qt), "dq staging fits the q and g tiles");
   const int ntile = (int)((nrows + BW_ROWS - 1) / BW_ROWS);
-  for (int j = 0; j < ntile; ++j) {
+  // a tile's inputs: the gathered rows' q and g operands and their scalars; the next
+  // tile's are loaded while the current one runs its dk / dv products and dq stores
+  struct TileIn {
+    bool ok;
+    uint32_t pid;
+    int64_t row;
+    bf16x8_t qb[1][D / 16], gb[1][D / 16];
+    float sc, Lam, go;
+  };
+  auto fetch = [&](int j, TileIn& t) {
     const uint32_t r = (uint32_t)j * BW_ROWS + trow;
-    const bool ok = r < nrows;
-    const uint32_t pid = ok ? pp[r] : 0u;  // linear index into sel_idx: row * K + slot
-    const int64_t row = ok ? (int64_t)(pid / (uint32_t)K) : bhq * N;
-    bf16x8_t qb[1][D / 16], gb8[1][D / 16];
-    load_q_operand<bf16_t, D, 1>(q, row * D, ok, qb);
-    load_q_operand<bf16_t, D, 1>(dO, row * D, ok, gb8);
-    const float sc = ok ? sel_score[pid] : 0.f;
-    const float Lam = ok ? lam[row] : 0.f;
-    const float go = ok ? dd[row] : 0.f;
-    __syncthreads();  // the K/V staging is done; the previous tile's LDS tiles are consumed
+    t.ok = r < nrows;
+    t.pid = t.ok ? ipid[r] : 0u;  // linear index into sel_idx: row * K + slot
+    t.row = t.ok ? (int64_t)(t.pid / (uint32_t)K) : bhq * N;
+    load_q_operand<bf16_t, D, 1>(q, t.row * D, t.ok, t.qb);
+    load_q_operand<bf16_t, D, 1>(dO, t.row * D, t.ok, t.gb);
+    t.sc = t.ok ? sel_score[t.pid] : 0.f;
+    t.Lam = t.ok ? lam[t.row] : 0.f;
+    t.go = t.ok ? dd[t.row] : 0.f;
+  };
+  TileIn cur;
+  if (ntile > 0) fetch(0, cur);
+  for (int j = 0; j < ntile; ++j) {
+    const bool ok = cur.ok;
+    const uint32_t pid = cur.pid;
+    const int64_t row = cur.row;
+    const float sc = cur.sc, Lam = cur.Lam, go = cur.go;
+    auto& qb = cur.qb;
+    auto& gb8 = cur.gb;
+    __syncthreads();  // the previous tile's LDS tiles are consumed
     f32x16_t s[2], dp[2];
     keys_dot_rows<D, KVTile<bf16_t, D, 1>::LDK>(L.kv.k[0], qb[0], s);
     keys_dot_rows<D, KVTile<bf16_t, D, 1>::LDV>(L.kv.v[0], gb8[0], dp);
@@ -485,6 +506,7 @@ __global__ void __launch_bounds__(256) bwd_pairs(const bf16_t* __restrict__ q, c
     keys_to_lds(dp, L.st, trow);
     rows_to_lds<D>(qb[0], L.qt, trow);
     rows_to_lds<D>(gb8[0], L.gt, trow);
+    if (j + 1 < ntile) fetch(j + 1, cur);  // every use of this tile's inputs is above
     f32x16_t dqa[D / 32];
 #pragma unroll
     for (int dt = 0; dt < D / 32; ++dt) dqa[dt] = zero16();
