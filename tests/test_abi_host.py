@@ -161,3 +161,29 @@ def test_paged_entry_points_validation():
                                       None, fake, fake, need, None) == hils.E_INVAL
     assert lib.hils_attn_decode_paged(ctypes.byref(d), fake, fake, fake, fake, 16, 40, fake, fake, fake, None, None,
                                       None, fake, fake, need - 1, None) == hils.E_WORKSPACE
+
+
+def test_backward_validation_and_workspace():
+    """The backward entry: bf16 only, the documented NULL checks and the workspace size, checked
+    before anything touches the device."""
+    lib = hils.load()
+    d = hils.dims(1, 8, 2, 64, 1024, 8)   # N = 16 chunks
+    fake = ctypes.c_void_p(0x1000)
+    need = hils.workspace_bytes(d, hils.OP_BACKWARD)
+    # the fp32 per-pair dq partials alone: B*Hq*N*K*d*4 bytes
+    assert need >= 1 * 8 * 1024 * 8 * 64 * 4
+    dr = hils.dims(1, 8, 2, 64, 1024, 8, qcal_rank=4)
+    assert hils.workspace_bytes(dr, hils.OP_BACKWARD) > need   # plus the per-head d x d sums
+
+    def call(dm, lmk=fake, kc=fake, D=None, U=None, dlmk=fake, dD=None, dU=None, dq=fake, ws_bytes=need):
+        return lib.hils_attn_prefill_backward(ctypes.byref(dm), fake, fake, fake, lmk, kc, D, U, fake, fake, fake,
+                                              fake, dq, fake, fake, dlmk, dD, dU, fake, ws_bytes, None)
+
+    assert call(d, dq=None) == hils.E_INVAL
+    assert call(d, lmk=None) == hils.E_INVAL
+    assert call(d, dlmk=None) == hils.E_INVAL
+    assert call(dr, ws_bytes=1 << 40) == hils.E_INVAL            # Q-Cal without D, U, dD, dU
+    assert call(d, ws_bytes=need - 1) == hils.E_WORKSPACE
+    f32 = hils.dims(1, 8, 2, 64, 1024, 8, io=hils.F32)
+    assert call(f32, ws_bytes=1 << 40) == hils.E_UNSUPPORTED
+    assert b"bf16" in lib.hils_last_error()
