@@ -25,6 +25,19 @@ template <typename IO, int D, int NT>
 HILS_DEV void stage_kv(KVTile<IO, D, NT>& tile, const IO* __restrict__ k, const IO* __restrict__ v, int64_t row0,
                        int nvalid, int tid, int nthreads) {
   constexpr int LDK = KVTile<IO, D, NT>::LDK, LDV = KVTile<IO, D, NT>::LDV;
+  if constexpr (sizeof(IO) == 2 && NT == 1) {  // bf16 values are their own single term
+    for (int i = tid * 8; i < 64 * D; i += nthreads * 8) {
+      const int key = i / D, e = i % D;
+      const int64_t off = (row0 + min(key, nvalid - 1)) * D + e;  // nvalid >= 1: in bounds; zeroed below
+      const uint32_t keep = key < nvalid ? 0xffffffffu : 0u;
+      u32x4_t kr = *reinterpret_cast<const u32x4_t*>(k + off), vr = *reinterpret_cast<const u32x4_t*>(v + off);
+      kr.x &= keep, kr.y &= keep, kr.z &= keep, kr.w &= keep;
+      vr.x &= keep, vr.y &= keep, vr.z &= keep, vr.w &= keep;
+      *reinterpret_cast<u32x4_t*>(&tile.k[0][key * LDK + e]) = kr;
+      *reinterpret_cast<u32x4_t*>(&tile.v[0][key * LDV + e]) = vr;
+    }
+    return;
+  }
   for (int i = tid * 8; i < 64 * D; i += nthreads * 8) {
     const int key = i / D, e = i % D;
     float kx[8], vx[8];

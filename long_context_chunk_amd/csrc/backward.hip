@@ -192,25 +192,8 @@ HILS_DEV void dkdv_from_tiles(const GradLds<D>& L, float* __restrict__ dk, float
   }
 }
 
-// The same products accumulated over several tiles in per-wave registers (wave w owns
-// blocks w, w + 4, ...), and their flush to the fp32 accumulators.
-template <int D>
-HILS_DEV void dkdv_accumulate(const GradLds<D>& L, f32x16_t (&acc)[D / 32]) {
-  constexpr int NDT = D / 32;
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-#pragma unroll
-  for (int ib = 0; ib < NDT; ++ib) {
-    const int blk = w + 4 * ib;
-    const bool isk = blk >= 2 * NDT;
-    const int kt = (blk % (2 * NDT)) / NDT, dt = blk % NDT;
-    const uint16_t* a_tile = isk ? L.st : L.pt;
-    const uint16_t* b_tile = isk ? L.qt : L.gt;
-#pragma unroll
-    for (int ks2 = 0; ks2 < BW_ROWS / 16; ++ks2)
-      acc[ib] = mfma32(vt_operand<LDP>(a_tile, kt, ks2, lane), vt_operand<GradLds<D>::LDR>(b_tile, dt, ks2, lane),
-                       acc[ib]);
-  }
-}
+// The flush of a wave's dk / dv blocks (wave w owns blocks w, w + 4, ..., summed over a
+// work item's tiles in registers) to the fp32 accumulators.
 template <int D>
 HILS_DEV void dkdv_flush(const f32x16_t (&acc)[D / 32], float* __restrict__ dk, float* __restrict__ dv,
                          int64_t kvrow0, float tau) {
@@ -379,8 +362,17 @@ __global__ void __launch_bounds__(256) bwd_window(const bf16_t* __restrict__ q, 
 // One work item = up to BUCKET_ITEM_ROWS gathered rows of one bucket (b, h, c), in
 // tiles of 128 (32 per wave).  Per row: S and dP' on the MFMA, the chunk softmax P,
 // e = sum_j P_j dP'_j, w = exp(s_ic - Lambda_i), dsigma = w (e - g.o_i) (stored per pair),
-// dS = P w (dP' - e), the pair's dq (stored as a partial); dk/dv over the tile's rows; and the item's
-// sum dsigma q (q^ = (I + U D) q is linear in q) and db'_c = sum dsigma, added atomically.
+// dS = P w (dP' - e), the pair's dq (stored as a partial); dk/dv over the tile's rows; and
+// the item's sum dsigma q (q^ = (I + U D) q is linear in q) and db'_c = sum dsigma, added
+// atomically.
+//
+// The q and g rows of a wave's 32 rows are gathered as whole rows (16 bytes per lane)
+// straight into registers one tile ahead and written to the wave's rows of the LDS
+// tiles, from which both the row operands of S and dP' and the transposed operands of
+// the dk/dv products are read.  sum dsigma q runs on the MFMA beside dk: dsigma (split
+// into two bf16 terms) sits in columns 64 and 65 of the P w tile's rows (its padding),
+// and a 32-column operand read there meets the q tile; only output columns 0 and 1 are
+// used (an MFMA output column depends on its own operand column only).
 template <int D>
 __global__ void __launch_bounds__(256) bwd_pairs(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
                                                  const bf16_t* __restrict__ v, const bf16_t* __restrict__ dO,
@@ -391,12 +383,16 @@ __global__ void __launch_bounds__(256) bwd_pairs(const bf16_t* __restrict__ q, c
                                                  float* __restrict__ dqp, float* __restrict__ dk, float* __restrict__ dv,
                                                  float* __restrict__ dkc, float* __restrict__ dbc, int Hq, int Hkv,
                                                  int N, int C, int K, int nbk) {
+  constexpr int LDR = GradLds<D>::LDR;
+  constexpr int LDK = KVTile<bf16_t, D, 1>::LDK, LDV = KVTile<bf16_t, D, 1>::LDV;
+  constexpr int SEGS = D / 8;      // 16-byte segments of a bf16 row
+  constexpr int RPL = 64 / SEGS;   // rows covered by one wave-wide 16-byte load
+  constexpr int NLD = 32 / RPL;    // loads per lane for the wave's 32 rows
+  constexpr int NDT = D / 32;
+  static_assert(LDP >= 66, "dsigma terms live in columns 64 and 65 of the P w rows");
   __shared__ GradLds<D> L;
-  __shared__ float sig_s[BW_ROWS];
-  __shared__ uint32_t srow[BW_ROWS];
-  __shared__ uint32_t spid[BW_ROWS];
-  __shared__ uint32_t ipid[BUCKET_ITEM_ROWS];  // the item's pair ids
-  __shared__ float red[2][D + 1];
+  __shared__ uint32_t ipid[BUCKET_ITEM_ROWS];  // pair ids (row * K + slot); ~0 past the item
+  __shared__ uint32_t irow[BUCKET_ITEM_ROWS];  // in-head query rows (0 past the item)
   const int item = blockIdx.x;
   if ((uint32_t)item >= toff[nbk]) return;
   int lo = 0, hi = nbk - 1;  // bucket = last index with toff[bk] <= item
@@ -415,54 +411,73 @@ __global__ void __launch_bounds__(256) bwd_pairs(const bf16_t* __restrict__ q, c
   const int h = (int)(bhq % Hq), b = (int)(bhq / Hq);
   const int kvh = h / (Hq / Hkv);
   const int64_t kvrow0 = ((int64_t)b * Hkv + kvh) * N + (int64_t)c * 64;
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, hf = lane >> 5;
+  const int tid = threadIdx.x, lane = tid & 63, hf = lane >> 5;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const float tau = 1.0f / sqrtf((float)D);
   const float cl = tau * 1.44269504088896340736f;
   const int trow = 32 * w + (lane & 31);
-  for (uint32_t x = tid; x < nrows; x += 256) ipid[x] = pp[x];
-  stage_kv<bf16_t, D, 1>(L.kv, k, v, kvrow0, 64, tid, 256);
-  __syncthreads();
-  // dk'_c / db'_c partial sums: thread t sums dims t % D over its share of the rows
-  constexpr int RSPLIT = 256 / D;
-  float kacc = 0.f, bacc = 0.f;
-  f32x16_t dkv[D / 32];  // this wave's dk / dv blocks, summed over the item's tiles
-#pragma unroll
-  for (int ib = 0; ib < D / 32; ++ib) dkv[ib] = zero16();
-  static_assert(BW_ROWS * (D + 4) * 4 <= 2 * (int)sizeof(GradLds<D>::qt), "dq staging fits the q and g tiles");
+  // every row of a bucket belongs to head bhq: 32-bit offsets from the head's bases
+  const char* q_head = reinterpret_cast<const char*>(q + bhq * N * D);
+  const char* g_head = reinterpret_cast<const char*>(dO + bhq * N * D);
+  const uint32_t e_head = (uint32_t)(bhq * N * K);
+  for (int x = tid; x < BUCKET_ITEM_ROWS; x += 256) {
+    const bool ok = (uint32_t)x < nrows;
+    const uint32_t pid = ok ? pp[x] : 0xffffffffu;
+    ipid[x] = pid;
+    irow[x] = ok ? (pid - e_head) / (uint32_t)K : 0u;
+  }
   const int ntile = (int)((nrows + BW_ROWS - 1) / BW_ROWS);
-  // a tile's inputs: the gathered rows' q and g operands and their scalars; the next
-  // tile's are loaded while the current one runs its dk / dv products and dq stores
-  struct TileIn {
-    bool ok;
-    uint32_t pid;
-    int64_t row;
-    bf16x8_t qb[1][D / 16], gb[1][D / 16];
-    float sc, Lam, go;
+  __syncthreads();  // ipid / irow
+
+  // a tile's inputs: the wave's 32 rows of q and g as raw 16-byte row segments, and
+  // this lane's row's pair id, score, Lambda and g.o
+  const int lr = lane / SEGS, sg = lane % SEGS;
+  u32x4_t gq[NLD], gg[NLD];
+  uint32_t n_pid;
+  float n_sc, n_lam, n_go;
+  auto fetch = [&](int j) {
+#pragma unroll
+    for (int u = 0; u < NLD; ++u) {
+      const uint32_t off = irow[j * BW_ROWS + 32 * w + RPL * u + lr] * (uint32_t)(D * 2) + 16u * sg;
+      gq[u] = *reinterpret_cast<const u32x4_t*>(q_head + off);
+      gg[u] = *reinterpret_cast<const u32x4_t*>(g_head + off);
+    }
+    n_pid = ipid[j * BW_ROWS + trow];
+    const bool ok = n_pid != 0xffffffffu;
+    const int64_t row = bhq * N + irow[j * BW_ROWS + trow];
+    n_sc = ok ? sel_score[n_pid] : 0.f;
+    n_lam = lam[row];
+    n_go = dd[row];
   };
-  auto fetch = [&](int j, TileIn& t) {
-    const uint32_t r = (uint32_t)j * BW_ROWS + trow;
-    t.ok = r < nrows;
-    t.pid = t.ok ? ipid[r] : 0u;  // linear index into sel_idx: row * K + slot
-    t.row = t.ok ? (int64_t)(t.pid / (uint32_t)K) : bhq * N;
-    load_q_operand<bf16_t, D, 1>(q, t.row * D, t.ok, t.qb);
-    load_q_operand<bf16_t, D, 1>(dO, t.row * D, t.ok, t.gb);
-    t.sc = t.ok ? sel_score[t.pid] : 0.f;
-    t.Lam = t.ok ? lam[t.row] : 0.f;
-    t.go = t.ok ? dd[t.row] : 0.f;
-  };
-  TileIn cur;
-  if (ntile > 0) fetch(0, cur);
+  if (ntile > 0) fetch(0);
+  stage_kv<bf16_t, D, 1>(L.kv, k, v, kvrow0, 64, tid, 256);
+  f32x16_t dkv[NDT];  // this wave's dk / dv blocks, summed over the item's tiles
+#pragma unroll
+  for (int ib = 0; ib < NDT; ++ib) dkv[ib] = zero16();
+  f32x16_t kq = zero16();  // sum dsigma q for dims 32 w + ... (waves w < NDT)
+  float bacc = 0.f;        // sum dsigma over this lane's rows
   for (int j = 0; j < ntile; ++j) {
-    const bool ok = cur.ok;
-    const uint32_t pid = cur.pid;
-    const int64_t row = cur.row;
-    const float sc = cur.sc, Lam = cur.Lam, go = cur.go;
-    auto& qb = cur.qb;
-    auto& gb8 = cur.gb;
-    __syncthreads();  // the previous tile's LDS tiles are consumed
+    __syncthreads();  // K/V staged (first tile); the previous tile's LDS tiles consumed
+#pragma unroll
+    for (int u = 0; u < NLD; ++u) {
+      const int r = 32 * w + RPL * u + lr;
+      *reinterpret_cast<u32x4_t*>(&L.qt[r * LDR + 8 * sg]) = gq[u];
+      *reinterpret_cast<u32x4_t*>(&L.gt[r * LDR + 8 * sg]) = gg[u];
+    }
+    const uint32_t pid = n_pid;
+    const bool ok = pid != 0xffffffffu;
+    const float sc = n_sc, Lam = n_lam, go = n_go;
+    __builtin_amdgcn_wave_barrier();  // the wave's rows are in LDS
     f32x16_t s[2], dp[2];
-    keys_dot_rows<D, KVTile<bf16_t, D, 1>::LDK>(L.kv.k[0], qb[0], s);
-    keys_dot_rows<D, KVTile<bf16_t, D, 1>::LDV>(L.kv.v[0], gb8[0], dp);
+    {
+      bf16x8_t rb[D / 16];
+#pragma unroll
+      for (int ks = 0; ks < D / 16; ++ks) rb[ks] = lds_op16(&L.qt[trow * LDR + 16 * ks + 8 * hf]);
+      keys_dot_rows<D, LDK>(L.kv.k[0], rb, s);
+#pragma unroll
+      for (int ks = 0; ks < D / 16; ++ks) rb[ks] = lds_op16(&L.gt[trow * LDR + 16 * ks + 8 * hf]);
+      keys_dot_rows<D, LDV>(L.kv.v[0], rb, dp);
+    }
     float mt = fmaxf(s[0][0], s[0][1]);
 #pragma unroll
     for (int rr = 2; rr < 32; ++rr) mt = fmaxf(mt, s[rr >> 4][rr & 15]);
@@ -476,84 +491,80 @@ __global__ void __launch_bounds__(256) bwd_pairs(const bf16_t* __restrict__ q, c
         lt += s[tt][rr];
       }
     lt += __shfl_xor(lt, 32);
-    const float inv = 1.0f / lt;
+    const float inv = __builtin_amdgcn_rcpf(lt);  // lt >= 1 (the largest logit's term)
     float e = 0.f;
 #pragma unroll
     for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
-      for (int rr = 0; rr < 16; ++rr) {
-        s[tt][rr] *= inv;  // P
-        e = fmaf(s[tt][rr], dp[tt][rr], e);
-      }
-    e += __shfl_xor(e, 32);
+      for (int rr = 0; rr < 16; ++rr) e = fmaf(s[tt][rr], dp[tt][rr], e);
+    e = (e + __shfl_xor(e, 32)) * inv;
     const float wc = ok ? __expf(sc - Lam) : 0.f;
     const float dsg = wc * (e - go);
-    if (ok && hf == 0) dsig[pid] = dsg;
-    if (hf == 0) {
-      sig_s[trow] = ok ? dsg : 0.f;
-      srow[trow] = ok ? (uint32_t)row : 0xffffffffu;
-      spid[trow] = ok ? pid : 0xffffffffu;
-    }
+    const float pw = inv * wc;
 #pragma unroll
     for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
       for (int rr = 0; rr < 16; ++rr) {
-        const float p = s[tt][rr] * wc;
+        const float p = s[tt][rr] * pw;
         s[tt][rr] = p;                      // P w
         dp[tt][rr] = p * (dp[tt][rr] - e);  // dS
       }
     keys_to_lds(s, L.pt, trow);
     keys_to_lds(dp, L.st, trow);
-    rows_to_lds<D>(qb[0], L.qt, trow);
-    rows_to_lds<D>(gb8[0], L.gt, trow);
-    if (j + 1 < ntile) fetch(j + 1, cur);  // every use of this tile's inputs is above
-    f32x16_t dqa[D / 32];
-#pragma unroll
-    for (int dt = 0; dt < D / 32; ++dt) dqa[dt] = zero16();
-    dq_from_ds<D>(L.kv, dp, dqa);
-    __syncthreads();
-    dkdv_accumulate<D>(L, dkv);
-    // sum dsigma q and db'_c over this tile's rows (from the staged q rows); dk'_c is
-    // tau (I + U_h D_h) applied to the first sum, in bwd_compress
-    {
-      const int e2 = tid % D, part = tid / D;
-#pragma unroll 4
-      for (int x = part; x < BW_ROWS; x += RSPLIT)
-        kacc = fmaf(sig_s[x], __uint_as_float((uint32_t)L.qt[x * GradLds<D>::LDR + e2] << 16), kacc);
-      if (tid < BW_ROWS) bacc += sig_s[tid];
+    if (hf == 0) {
+      const uint16_t s_hi = f32_to_bf16(dsg);
+      const uint16_t s_lo = f32_to_bf16(dsg - bf16_to_f32(s_hi));
+      *reinterpret_cast<uint32_t*>(&L.pt[trow * LDP + 64]) = (uint32_t)s_hi | ((uint32_t)s_lo << 16);
+      bacc += dsg;
+      if (ok) dsig[pid] = dsg;
     }
-    // dq: the tile's rows through LDS (over the q and g tiles, consumed above), then stored
-    // as the pair's partial (bwd_rows sums a row's partials), whole rows per wave
-    __syncthreads();
-    float* dqs = reinterpret_cast<float*>(L.qt);
-    constexpr int LDF = D + 4;
+    // the next tile's rows are loaded from here on, through the dq and dk/dv products
+    bf16x8_t db[4];
+    keys_to_b(dp, db);
+    if (j + 1 < ntile) fetch(j + 1);
+    // the pair's dq (dq^T += K^T dS^T, 32 dims at a time), stored as a partial straight
+    // from the accumulators (bwd_dq_sum adds a row's partials)
+    float* dst = dqp + (int64_t)(ok ? pid : 0u) * D + 4 * hf;
 #pragma unroll
-    for (int dt = 0; dt < D / 32; ++dt)
+    for (int dt = 0; dt < NDT; ++dt) {
+      f32x16_t dqa = zero16();
 #pragma unroll
-      for (int g4 = 0; g4 < 4; ++g4)
-        *reinterpret_cast<float4*>(&dqs[trow * LDF + 32 * dt + 8 * g4 + 4 * hf]) =
-            make_float4(dqa[dt][4 * g4], dqa[dt][4 * g4 + 1], dqa[dt][4 * g4 + 2], dqa[dt][4 * g4 + 3]);
-    __syncthreads();
-    for (int x = tid; x < BW_ROWS * D; x += 256) {
-      const uint32_t pq = spid[x / D];
-      if (pq != 0xffffffffu) dqp[(int64_t)pq * D + x % D] = dqs[(x / D) * LDF + x % D] * tau;
+      for (int ks2 = 0; ks2 < 4; ++ks2) dqa = mfma32(vt_operand<LDK>(L.kv.k[0], dt, ks2, lane), db[ks2], dqa);
+      if (ok)
+#pragma unroll
+        for (int g4 = 0; g4 < 4; ++g4)
+          *reinterpret_cast<float4*>(dst + 32 * dt + 8 * g4) =
+              make_float4(dqa[4 * g4] * tau, dqa[4 * g4 + 1] * tau, dqa[4 * g4 + 2] * tau, dqa[4 * g4 + 3] * tau);
+    }
+    __syncthreads();  // all four waves' rows of the P w, dS, q and g tiles are written
+    // dk / dv blocks over the tile's 128 rows (wave w owns blocks w, w + 4, ...), and sum
+    // dsigma q for dims 32 w .. 32 w + 31 (waves w < NDT)
+#pragma unroll 2
+    for (int ks2 = 0; ks2 < BW_ROWS / 16; ++ks2) {
+#pragma unroll
+      for (int ib = 0; ib < NDT; ++ib) {
+        const int blk = w + 4 * ib;
+        const bool isk = blk >= 2 * NDT;
+        const int kt = (blk % (2 * NDT)) / NDT, dt = blk % NDT;
+        dkv[ib] = mfma32(vt_operand<LDP>(isk ? L.st : L.pt, kt, ks2, lane),
+                         vt_operand<LDR>(isk ? L.qt : L.gt, dt, ks2, lane), dkv[ib]);
+      }
+      if (NDT == 4 || w < NDT)
+        kq = mfma32(vt_operand<LDR>(L.qt, w, ks2, lane), vt_operand<LDP>(L.pt, 2, ks2, lane), kq);
     }
   }
   dkdv_flush<D>(dkv, dk, dv, kvrow0, tau);
-  // item totals of dk'_c and db'_c
-  const int e2 = tid % D, part = tid / D;
-  __syncthreads();
-  if (part < 2) red[part][e2] = kacc;
-  if (RSPLIT == 4) {
-    __syncthreads();
-    if (part >= 2) red[part - 2][e2] += kacc;
-  }
-  __syncthreads();
   const int64_t ci = bhq * C + c;  // landmark head = query head
-  if (tid < D) atomicAdd(&dkc[ci * D + tid], red[0][tid] + red[1][tid]);
-  float bs = tid < BW_ROWS ? bacc : 0.f;
-  bs = wave_sum_f(bs);
-  if (lane == 0 && w < 2) atomicAdd(&dbc[ci], bs);
+  if (NDT == 4 || w < NDT) {
+    // column 0 (lanes 0, 32) holds the high terms' sums, column 1 (lanes 1, 33) the low
+#pragma unroll
+    for (int rr = 0; rr < 16; ++rr) {
+      const float lo2 = __shfl_down(kq[rr], 1);
+      if ((lane & 31) == 0) atomicAdd(&dkc[ci * D + 32 * w + acc_row(rr, hf)], kq[rr] + lo2);
+    }
+  }
+  bacc = wave_sum_f(hf == 0 ? bacc : 0.f);
+  if (lane == 0) atomicAdd(&dbc[ci], bacc);
 }
 
 // ------------------------------------------------------------------ bwd_dq_sum
