@@ -66,7 +66,7 @@ BwdWs bwd_ws(const Geom& g) {
   take(w.lam, rows * 4);
   take(w.dd, rows * 4);
   take(w.dsig, ent * 4);
-  take(w.dqp, ent * g.d * 4);  // per (row, slot) dq of the selected chunk's attention
+  take(w.dqp, ent * g.d * 2);  // per (row, slot) dq of the selected chunk's attention (bf16)
   take(w.dqh, r > 0 ? rows * g.d * 2 : 0);  // dq^ (bf16) for the Q-Cal backward
   take(w.counts, nbk * 4);  // counts and cursor contiguous (zeroed together)
   take(w.cursor, nbk * 4);
@@ -380,7 +380,7 @@ __global__ void __launch_bounds__(256) bwd_pairs(const bf16_t* __restrict__ q, c
                                                  const float* __restrict__ lam, const float* __restrict__ dd,
                                                  const uint32_t* __restrict__ pairs, const uint32_t* __restrict__ boff,
                                                  const uint32_t* __restrict__ toff, float* __restrict__ dsig,
-                                                 float* __restrict__ dqp, float* __restrict__ dk, float* __restrict__ dv,
+                                                 uint16_t* __restrict__ dqp, float* __restrict__ dk, float* __restrict__ dv,
                                                  float* __restrict__ dkc, float* __restrict__ dbc, int Hq, int Hkv,
                                                  int N, int C, int K, int nbk) {
   constexpr int LDR = GradLds<D>::LDR;
@@ -524,7 +524,7 @@ __global__ void __launch_bounds__(256) bwd_pairs(const bf16_t* __restrict__ q, c
     if (j + 1 < ntile) fetch(j + 1);
     // the pair's dq (dq^T += K^T dS^T, 32 dims at a time), stored as a partial straight
     // from the accumulators (bwd_dq_sum adds a row's partials)
-    float* dst = dqp + (int64_t)(ok ? pid : 0u) * D + 4 * hf;
+    uint16_t* dst = dqp + (int64_t)(ok ? pid : 0u) * D + 4 * hf;
 #pragma unroll
     for (int dt = 0; dt < NDT; ++dt) {
       f32x16_t dqa = zero16();
@@ -533,8 +533,9 @@ __global__ void __launch_bounds__(256) bwd_pairs(const bf16_t* __restrict__ q, c
       if (ok)
 #pragma unroll
         for (int g4 = 0; g4 < 4; ++g4)
-          *reinterpret_cast<float4*>(dst + 32 * dt + 8 * g4) =
-              make_float4(dqa[4 * g4] * tau, dqa[4 * g4 + 1] * tau, dqa[4 * g4 + 2] * tau, dqa[4 * g4 + 3] * tau);
+          *reinterpret_cast<u32x2_t*>(dst + 32 * dt + 8 * g4) =
+              u32x2_t{pack_bf16x2(dqa[4 * g4] * tau, dqa[4 * g4 + 1] * tau),
+                      pack_bf16x2(dqa[4 * g4 + 2] * tau, dqa[4 * g4 + 3] * tau)};
     }
     __syncthreads();  // all four waves' rows of the P w, dS, q and g tiles are written
     // dk / dv blocks over the tile's 128 rows (wave w owns blocks w, w + 4, ...), and sum
@@ -568,12 +569,12 @@ __global__ void __launch_bounds__(256) bwd_pairs(const bf16_t* __restrict__ q, c
 }
 
 // ------------------------------------------------------------------ bwd_dq_sum
-// Per row (one wave, lanes over the dims): dq += the selected chunks' dq partials +
+// Per row (one wave, lanes over the dims): dq += the selected chunks' dq partials (bf16) +
 // dq^, dq^ = tau sum_x dsigma_x k'_(sel x); dq^ is also kept (bf16) for the Q-Cal
 // backward.  The row's selections are read once and broadcast from lanes.
-template <int D>
+template <int D, int KMAX>
 __global__ void __launch_bounds__(256) bwd_dq_sum(const float* __restrict__ kc, const int32_t* __restrict__ sel,
-                                                  const float* __restrict__ dsig, const float* __restrict__ dqp,
+                                                  const float* __restrict__ dsig, const uint16_t* __restrict__ dqp,
                                                   float* __restrict__ dq, bf16_t* __restrict__ dqh, int N, int C, int K,
                                                   int64_t rows) {
   constexpr int EPL = D / 64;
@@ -584,19 +585,40 @@ __global__ void __launch_bounds__(256) bwd_dq_sum(const float* __restrict__ kc, 
     const float sg = lane < K ? dsig[row * K + lane] * tau : 0.f;
     const int n = __popcll(__ballot(sl >= 0));  // valid selections come first
     const float* kch = kc + (row / N) * (int64_t)C * D + lane * EPL;
-    const float* pr = dqp + row * K * D + lane * EPL;
+    const uint16_t* pr = dqp + row * K * D + lane * EPL;
+    // every slot's loads at once (slots past n read slot 0 and chunk 0, in bounds, and
+    // are dropped), so the row's reads are all in flight together.  A row without
+    // selections reads nothing: with no complete chunk there is no k' at all.
+    uint32_t pv[KMAX];
+    float kv[KMAX][EPL];
+#pragma unroll
+    for (int x = 0; x < KMAX; ++x) {
+      pv[x] = 0u;
+#pragma unroll
+      for (int u = 0; u < EPL; ++u) kv[x][u] = 0.f;
+    }
+    if (n > 0) {  // wave-uniform
+#pragma unroll
+      for (int x = 0; x < KMAX; ++x) {
+        const int xs = x < n ? x : 0;
+        const int cc = max(__builtin_amdgcn_readlane(sl, x < K ? x : 0), 0);
+        pv[x] = EPL == 2 ? *reinterpret_cast<const uint32_t*>(pr + (int64_t)xs * D) : pr[(int64_t)xs * D];
+#pragma unroll
+        for (int u = 0; u < EPL; ++u) kv[x][u] = kch[(int64_t)cc * D + u];
+      }
+    }
     float acc[EPL], gh[EPL];
 #pragma unroll
     for (int u = 0; u < EPL; ++u) acc[u] = gh[u] = 0.f;
-#pragma unroll 4
-    for (int x = 0; x < n; ++x) {
-      const int cc = __builtin_amdgcn_readlane(sl, x);
-      const float sgx = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(sg), x));
 #pragma unroll
-      for (int u = 0; u < EPL; ++u) {
-        gh[u] = fmaf(sgx, kch[(int64_t)cc * D + u], gh[u]);
-        acc[u] += pr[(int64_t)x * D + u];
-      }
+    for (int x = 0; x < KMAX; ++x) {
+      const bool live = x < n;
+      const float sgx = live ? __int_as_float(__builtin_amdgcn_readlane(__float_as_int(sg), x)) : 0.f;
+      const float p0 = __uint_as_float(pv[x] << 16), p1 = __uint_as_float(pv[x] & 0xffff0000u);
+      acc[0] += live ? p0 : 0.f;
+      if constexpr (EPL == 2) acc[1] += live ? p1 : 0.f;
+#pragma unroll
+      for (int u = 0; u < EPL; ++u) gh[u] = fmaf(sgx, kv[x][u], gh[u]);
     }
 #pragma unroll
     for (int u = 0; u < EPL; ++u) {
@@ -869,13 +891,24 @@ hipError_t launch_bwd_d(const Geom& g, const BwdArgs& a, char* ws, hipStream_t s
                         st);
     hipLaunchKernelGGL((bwd_pairs<D>), dim3((unsigned)items), dim3(256), 0, st, q, k, v, (const bf16_t*)a.dO,
                        a.sel_score, (const float*)lam, (const float*)dd, (const uint32_t*)pairs,
-                       (const uint32_t*)boff, (const uint32_t*)toff, dsig, (float*)(ws + w.dqp), dk, dv, dkc, dbc,
+                       (const uint32_t*)boff, (const uint32_t*)toff, dsig, (uint16_t*)(ws + w.dqp), dk, dv, dkc, dbc,
                        g.Hq, g.Hkv, g.N, C,
                        g.K, nbk);
   }
   bf16_t* dqh = g.r > 0 ? (bf16_t*)(ws + w.dqh) : nullptr;
-  hipLaunchKernelGGL((bwd_dq_sum<D>), dim3((unsigned)std::min<int64_t>((rows + 3) / 4, 1 << 20)), dim3(256), 0, st,
-                     a.kc, a.sel_idx, (const float*)dsig, (const float*)(ws + w.dqp), dq, dqh, g.N, C, g.K, rows);
+  {
+    const dim3 grid((unsigned)std::min<int64_t>((rows + 3) / 4, 1 << 20));
+    const uint16_t* dqp = (const uint16_t*)(ws + w.dqp);
+    if (g.K <= 8)
+      hipLaunchKernelGGL((bwd_dq_sum<D, 8>), grid, dim3(256), 0, st, a.kc, a.sel_idx, dsig, dqp, dq, dqh, g.N, C, g.K,
+                         rows);
+    else if (g.K <= 16)
+      hipLaunchKernelGGL((bwd_dq_sum<D, 16>), grid, dim3(256), 0, st, a.kc, a.sel_idx, dsig, dqp, dq, dqh, g.N, C, g.K,
+                         rows);
+    else
+      hipLaunchKernelGGL((bwd_dq_sum<D, 32>), grid, dim3(256), 0, st, a.kc, a.sel_idx, dsig, dqp, dq, dqh, g.N, C, g.K,
+                         rows);
+  }
   if (g.r > 0) {
     const int nqb = (g.N + QC_BLOCK - 1) / QC_BLOCK;
     hipLaunchKernelGGL((bwd_qcal<D>), dim3(g.B * g.Hq * nqb), dim3(256), 0, st, q, Dw, Uw, (const bf16_t*)dqh, dq, G,

@@ -170,8 +170,8 @@ def test_backward_validation_and_workspace():
     d = hils.dims(1, 8, 2, 64, 1024, 8)   # N = 16 chunks
     fake = ctypes.c_void_p(0x1000)
     need = hils.workspace_bytes(d, hils.OP_BACKWARD)
-    # the fp32 per-pair dq partials alone: B*Hq*N*K*d*4 bytes
-    assert need >= 1 * 8 * 1024 * 8 * 64 * 4
+    # the bf16 per-pair dq partials alone: B*Hq*N*K*d*2 bytes
+    assert need >= 1 * 8 * 1024 * 8 * 64 * 2
     dr = hils.dims(1, 8, 2, 64, 1024, 8, qcal_rank=4)
     assert hils.workspace_bytes(dr, hils.OP_BACKWARD) > need   # plus the per-head d x d sums
 
