@@ -13,18 +13,19 @@ namespace hils {
 // through ds_read_b64_tr_b16 transposing reads: within a 16-lane group, lane j points at
 // the 4 dims 4(j&3).. of key (j>>2) and lane i receives 4 consecutive keys of dim i.
 // Keys at or beyond `nvalid` are stored as zeros.  NT bf16 terms per value.
-template <typename IO, int D, int NT>
+// VPAD: V row padding; D + 32 suits the transposing reads, D + 8 whole-row reads.
+template <typename IO, int D, int NT, int VPAD = 32>
 struct alignas(16) KVTile {
   static constexpr int LDK = D + 8;
-  static constexpr int LDV = D + 32;
+  static constexpr int LDV = D + VPAD;
   uint16_t k[NT][64 * LDK];
   uint16_t v[NT][64 * LDV];
 };
 
-template <typename IO, int D, int NT>
-HILS_DEV void stage_kv(KVTile<IO, D, NT>& tile, const IO* __restrict__ k, const IO* __restrict__ v, int64_t row0,
+template <typename IO, int D, int NT, int VPAD>
+HILS_DEV void stage_kv(KVTile<IO, D, NT, VPAD>& tile, const IO* __restrict__ k, const IO* __restrict__ v, int64_t row0,
                        int nvalid, int tid, int nthreads) {
-  constexpr int LDK = KVTile<IO, D, NT>::LDK, LDV = KVTile<IO, D, NT>::LDV;
+  constexpr int LDK = KVTile<IO, D, NT, VPAD>::LDK, LDV = KVTile<IO, D, NT, VPAD>::LDV;
   if constexpr (sizeof(IO) == 2 && NT == 1) {  // bf16 values are their own single term
     for (int i = tid * 8; i < 64 * D; i += nthreads * 8) {
       const int key = i / D, e = i % D;

@@ -94,7 +94,7 @@ __global__ void __launch_bounds__(256) bwd_zero(float* p, int64_t n) {
 template <int D>
 struct GradLds {
   static constexpr int LDR = D + 8;
-  KVTile<bf16_t, D, 1> kv;
+  KVTile<bf16_t, D, 1, 8> kv;  // V is read by whole rows only (dP' = g V^T)
   uint16_t qt[BW_ROWS * LDR];
   uint16_t gt[BW_ROWS * LDR];
   uint16_t pt[BW_ROWS * LDP];
@@ -153,8 +153,8 @@ HILS_DEV void rows_to_lds(const bf16x8_t (&rb)[D / 16], uint16_t* tile, int row)
 
 // dq^T += K^T dS^T for the wave's rows: dq[dt][rr] = dim (32 dt + acc_row(rr, hf)) of row n.
 template <int D>
-HILS_DEV void dq_from_ds(const KVTile<bf16_t, D, 1>& kv, const f32x16_t (&ds)[2], f32x16_t (&dq)[D / 32]) {
-  constexpr int LDK = KVTile<bf16_t, D, 1>::LDK;
+HILS_DEV void dq_from_ds(const KVTile<bf16_t, D, 1, 8>& kv, const f32x16_t (&ds)[2], f32x16_t (&dq)[D / 32]) {
+  constexpr int LDK = KVTile<bf16_t, D, 1, 8>::LDK;
   const int lane = threadIdx.x & 63;
   bf16x8_t db[4];
   keys_to_b(ds, db);
@@ -276,7 +276,7 @@ __global__ void __launch_bounds__(256) bwd_window(const bf16_t* __restrict__ q, 
     stage_kv<bf16_t, D, 1>(L.kv, k, v, kv0 + (int64_t)c * 64, min(64, N - c * 64), tid, 256);
     __syncthreads();
     f32x16_t s[2];
-    keys_dot_rows<D, KVTile<bf16_t, D, 1>::LDK>(L.kv.k[0], qb[0], s);
+    keys_dot_rows<D, KVTile<bf16_t, D, 1, 8>::LDK>(L.kv.k[0], qb[0], s);
     const int lim = c == qc ? rl + 1 : 64;
     float mt = -INFINITY;
 #pragma unroll
@@ -329,8 +329,8 @@ __global__ void __launch_bounds__(256) bwd_window(const bf16_t* __restrict__ q, 
     stage_kv<bf16_t, D, 1>(L.kv, k, v, kv0 + (int64_t)c * 64, nkeys, tid, 256);
     __syncthreads();
     f32x16_t s[2], dp[2];
-    keys_dot_rows<D, KVTile<bf16_t, D, 1>::LDK>(L.kv.k[0], qb[0], s);
-    keys_dot_rows<D, KVTile<bf16_t, D, 1>::LDV>(L.kv.v[0], gb8, dp);
+    keys_dot_rows<D, KVTile<bf16_t, D, 1, 8>::LDK>(L.kv.k[0], qb[0], s);
+    keys_dot_rows<D, KVTile<bf16_t, D, 1, 8>::LDV>(L.kv.v[0], gb8, dp);
     const int lim = c == qc ? rl + 1 : 64;
 #pragma unroll
     for (int tt = 0; tt < 2; ++tt)
@@ -384,7 +384,7 @@ __global__ void __launch_bounds__(256) bwd_pairs(const bf16_t* __restrict__ q, c
                                                  float* __restrict__ dkc, float* __restrict__ dbc, int Hq, int Hkv,
                                                  int N, int C, int K, int nbk) {
   constexpr int LDR = GradLds<D>::LDR;
-  constexpr int LDK = KVTile<bf16_t, D, 1>::LDK, LDV = KVTile<bf16_t, D, 1>::LDV;
+  constexpr int LDK = KVTile<bf16_t, D, 1, 8>::LDK, LDV = KVTile<bf16_t, D, 1, 8>::LDV;
   constexpr int SEGS = D / 8;      // 16-byte segments of a bf16 row
   constexpr int RPL = 64 / SEGS;   // rows covered by one wave-wide 16-byte load
   constexpr int NLD = 32 / RPL;    // loads per lane for the wave's 32 rows
@@ -467,6 +467,7 @@ __global__ void __launch_bounds__(256) bwd_pairs(const bf16_t* __restrict__ q, c
     const uint32_t pid = n_pid;
     const bool ok = pid != 0xffffffffu;
     const float sc = n_sc, Lam = n_lam, go = n_go;
+    if (j + 1 < ntile) fetch(j + 1);  // the next tile's rows load during this whole tile
     __builtin_amdgcn_wave_barrier();  // the wave's rows are in LDS
     f32x16_t s[2], dp[2];
     {
@@ -518,10 +519,8 @@ __global__ void __launch_bounds__(256) bwd_pairs(const bf16_t* __restrict__ q, c
       bacc += dsg;
       if (ok) dsig[pid] = dsg;
     }
-    // the next tile's rows are loaded from here on, through the dq and dk/dv products
     bf16x8_t db[4];
     keys_to_b(dp, db);
-    if (j + 1 < ntile) fetch(j + 1);
     // the pair's dq (dq^T += K^T dS^T, 32 dims at a time), stored as a partial straight
     // from the accumulators (bwd_dq_sum adds a row's partials)
     uint16_t* dst = dqp + (int64_t)(ok ? pid : 0u) * D + 4 * hf;
