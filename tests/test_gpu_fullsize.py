@@ -109,3 +109,71 @@ def test_decode_full_size():
     summ = check_selection_and_output(w, xx, kc_o, bc_o, list(zip(rows_b, rows_h, pos)), ref,
                                       g["sel_idx"].reshape(-1, w.K), None, g["o"].reshape(-1, w.d), label=w.name)
     _say(w.name, summ)
+
+
+def test_backward_full_size_sampled_rows():
+    """The backward at the benchmark's size and launch configuration, with the output
+    gradient nonzero on sampled rows only.  Every gradient is then a sum over those rows'
+    pairs, so the oracle's backward over the sampled rows gives all of them exactly: dq on
+    every row (zero off the sample), and dk, dv, the landmark and Q-Cal gradients whole.
+    Bar as for the small backward cases: per tensor, max error <= 2e-2 and mean <= 2e-3 of
+    max |ref|."""
+    w = synth.WORKLOADS["prefill_256k_qcal"]
+    _say("full-size backward", w.name)
+    x = synth.make_inputs(w, SEED)
+    dm = dims_of(w)
+    q, k, v, lmk = (upload(x[n], w.io) for n in ("q", "k", "v", "lmk"))
+    D, U = upload(x["D"], w.io), upload(x["U"], w.io)
+    o = torch.empty_like(q)
+    kc = torch.empty((w.B, w.Hlmk, w.C, w.d), dtype=torch.float32, device="cuda")
+    bc = torch.empty((w.B, w.Hlmk, w.C), dtype=torch.float32, device="cuda")
+    sel = torch.empty((w.B, w.Hq, w.N, w.K), dtype=torch.int32, device="cuda")
+    scr = torch.empty((w.B, w.Hq, w.N, w.K), dtype=torch.float32, device="cuda")
+    ws = hils.workspace(dm, hils.OP_PREFILL)
+    hils.attn_prefill(dm, q, k, v, o, ws, lmk_q=lmk, kc=kc, bc=bc, qcal_D=D, qcal_U=U, sel_idx=sel, sel_score=scr)
+    torch.cuda.synchronize()
+    del ws
+    torch.cuda.empty_cache()
+
+    rng = np.random.default_rng(11)
+    rows = sorted({(0, int(rng.integers(w.Hq)), int(rng.integers(w.N))) for _ in range(192)})
+    rows += [(0, h, w.N - 1) for h in range(w.Hq)]
+    rows += [(0, h, i) for h in (0, w.Hq - 1) for i in (63, 64, 65, 130)]
+    rows = sorted(set(rows))
+    rr = np.asarray(rows)
+    g_rows = synth.normal((len(rows), w.d), SEED, 978, synth.BF16)
+    dO = np.zeros((w.B, w.Hq, w.N, w.d), np.uint16)
+    dO[rr[:, 0], rr[:, 1], rr[:, 2]] = g_rows
+    dOt = upload(dO, w.io)
+    dq, dk, dv, dlmk = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v), torch.empty_like(lmk)
+    dD, dU = torch.empty_like(D), torch.empty_like(U)
+    wsb = hils.workspace(dm, hils.OP_BACKWARD)
+    hils.attn_prefill_backward(dm, q, k, v, lmk, kc, sel, scr, o, dOt, dq, dk, dv, dlmk, wsb, qcal_D=D, qcal_U=U,
+                               dD=dD, dU=dU)
+    torch.cuda.synchronize()
+    del wsb
+    torch.cuda.empty_cache()
+    for t in (dq, dk, dv, dlmk, dD, dU):
+        assert torch.isfinite(t.float()).all()
+    mask = torch.ones((w.B, w.Hq, w.N), dtype=torch.bool, device="cuda")
+    mask[rr[:, 0], rr[:, 1], rr[:, 2]] = False
+    assert int((dq.float().abs().amax(-1) * mask).count_nonzero()) == 0, "dq nonzero on a row without gradient"
+
+    s = shape_of(w)
+    kc_o, bc_o = oracle.compress(s, x["k"], x["lmk"])
+    sel_rows = sel[0].cpu().numpy()[rr[:, 1], rr[:, 2]]
+    ref = oracle.attend_backward(s, rr[:, 0], rr[:, 1], rr[:, 2], x["q"][rr[:, 0], rr[:, 1], rr[:, 2]], x["k"],
+                                 x["v"], kc_o, bc_o, x["lmk"], sel_rows, synth.bf16_to_f32(g_rows), D=x["D"], U=x["U"])
+    got = {"dq": dq[0].float().cpu().numpy()[rr[:, 1], rr[:, 2]], "dk": dk.float().cpu().numpy(),
+           "dv": dv.float().cpu().numpy(), "dlmk": dlmk.float().cpu().numpy(), "dD": dD.float().cpu().numpy(),
+           "dU": dU.float().cpu().numpy()}
+    for name in ("dq", "dk", "dv", "dlmk", "dD", "dU"):
+        r, gt = ref[name], got[name]
+        scale = np.abs(r).max()
+        assert scale > 0, name
+        err = np.abs(gt - r)
+        nz = np.abs(r) > 0
+        _say("  %-5s max|ref| %.3g  max err %.3g (%.2e rel)  mean err on nonzero %.3g" %
+             (name, scale, err.max(), err.max() / scale, err[nz].mean()))
+        assert err.max() <= 2e-2 * scale, name
+        assert err[nz].mean() <= 2e-3 * scale, name
