@@ -49,7 +49,7 @@ constexpr int LOCAL_BITS = 26;      // in-group pair index bits of the first-pas
 constexpr int MAX_C = 16384;        // largest chunk count the LDS histograms hold
 
 struct AttendWs {
-  size_t counts, cursor, boff, toff, pairs, partial, lse, sink, total;
+  size_t counts, cursor, boff, toff, pairs, imap, partial, lse, sink, total;
 };
 
 static size_t al(size_t x) { return (x + 255) / 256 * 256; }
@@ -69,6 +69,8 @@ static AttendWs attend_ws(const Geom& g) {
   off += al((nbk + 1) * 4);
   w.pairs = off;
   off += al(ent * 4);
+  w.imap = off;
+  off += al((size_t)bucket_items_bound(g) * 4);
   // per row K + 1 output slots: the selected chunks' in selection order, then the own chunk
   const size_t rows = (size_t)g.B * g.Hq * g.N;
   w.partial = off;
@@ -151,6 +153,16 @@ __global__ void __launch_bounds__(1024) bucket_scan(uint32_t* __restrict__ count
     boff[nbk] = sa[t];
     toff[nbk] = sb[t];
   }
+}
+
+// Work item -> bucket: each bucket writes its own items' entries, so the work kernels
+// find their bucket with one load instead of a search over toff.
+__global__ void __launch_bounds__(256) bucket_item_map(const uint32_t* __restrict__ toff, uint32_t* __restrict__ imap,
+                                                       int nbk) {
+  const int bk = blockIdx.x * 256 + threadIdx.x;
+  if (bk >= nbk) return;
+  const uint32_t t0 = toff[bk], t1 = toff[bk + 1];
+  for (uint32_t t = t0; t < t1; ++t) imap[t] = (uint32_t)bk;
 }
 
 // exclusive scan of v over the 256 threads of the workgroup; returns the total
@@ -314,7 +326,8 @@ template <typename IO, int D>
 __global__ void __launch_bounds__(256, 2) chunk_attend(const IO* __restrict__ q, const IO* __restrict__ k,
                                                        const IO* __restrict__ v, const uint32_t* __restrict__ pairs,
                                                        const uint32_t* __restrict__ boff,
-                                                       const uint32_t* __restrict__ toff, void* __restrict__ partial_v,
+                                                       const uint32_t* __restrict__ toff,
+                                                       const uint32_t* __restrict__ imap, void* __restrict__ partial_v,
                                                        char* __restrict__ sink, int Hq, int Hkv, int N, int C, int K,
                                                        int nbk) {
   constexpr int NT = io_traits<IO>::terms;
@@ -329,14 +342,7 @@ __global__ void __launch_bounds__(256, 2) chunk_attend(const IO* __restrict__ q,
   __shared__ uint32_t irow[ITEM_ROWS];  // ... and their in-head query rows
   const int item = blockIdx.x;
   if ((uint32_t)item >= toff[nbk]) return;
-  // bucket = last index with toff[bk] <= item
-  int lo = 0, hi = nbk - 1;
-  while (lo < hi) {
-    const int mid = (lo + hi + 1) >> 1;
-    if (toff[mid] <= (uint32_t)item) lo = mid;
-    else hi = mid - 1;
-  }
-  const int bk = lo;
+  const int bk = (int)imap[item];
   const uint32_t count = boff[bk + 1] - boff[bk];
   const uint32_t first = ((uint32_t)item - toff[bk]) * ITEM_ROWS;
   const uint32_t nrows = min((uint32_t)ITEM_ROWS, count - first);
@@ -737,6 +743,8 @@ void launch_bucket_pairs(const Geom& g, const int32_t* sel, BucketBufs bb, hipSt
   const int ngrp = g.B * g.Hq;
   hipLaunchKernelGGL(bucket_count, dim3(ngrp * spg), dim3(256), 0, st, sel, bb.counts, group_len, spg, C);
   hipLaunchKernelGGL(bucket_scan, dim3(1), dim3(1024), 0, st, bb.counts, bb.boff, bb.toff, nbk);
+  hipLaunchKernelGGL(bucket_item_map, dim3((nbk + 255) / 256), dim3(256), 0, st, (const uint32_t*)bb.toff, bb.imap,
+                     nbk);
   const int nrg = (C + (1 << FINE_BITS) - 1) >> FINE_BITS;
   hipLaunchKernelGGL(bucket_part1, dim3(ngrp * spg), dim3(256), 0, st, sel, bb.boff, bb.cursor, bb.tmp, group_len,
                      spg, C, nrg);
@@ -766,17 +774,19 @@ static hipError_t launch_attend_t(const Geom& g, const void* q, const void* k, c
   uint32_t* boff = (uint32_t*)(ws + w.boff);
   uint32_t* toff = (uint32_t*)(ws + w.toff);
   uint32_t* pairs = (uint32_t*)(ws + w.pairs);
+  uint32_t* imap = (uint32_t*)(ws + w.imap);
   void* partial = ws + w.partial;
   const int C = g.C();
   const int nbk = g.B * g.Hq * C;
   if (nbk > 0) {
     // the first pass's output lives in the (not yet written) partial-output region
-    launch_bucket_pairs(g, sel, BucketBufs{counts, cursor, boff, toff, pairs, (uint32_t*)partial}, st);
+    launch_bucket_pairs(g, sel, BucketBufs{counts, cursor, boff, toff, pairs, (uint32_t*)partial, imap}, st);
     if (ev) hipEventRecord(ev[0], st);
     const int64_t items = bucket_items_bound(g);
     if (items > 0)
       hipLaunchKernelGGL((chunk_attend<IO, D>), dim3((unsigned)items), dim3(256), 0, st, (const IO*)q, (const IO*)k,
-                         (const IO*)v, pairs, boff, toff, partial, ws + w.sink, g.Hq, g.Hkv, g.N, C, g.K, nbk);
+                         (const IO*)v, pairs, boff, toff, imap, partial, ws + w.sink, g.Hq, g.Hkv, g.N, C, g.K,
+                         nbk);
     if (ev) hipEventRecord(ev[1], st);
   } else if (ev) {
     hipEventRecord(ev[0], st);

@@ -44,7 +44,7 @@ constexpr int BW_ROWS = 128;  // rows per tile: 4 waves x 32
 constexpr int LDP = 64 + 8;   // bf16 row stride of the [row][key] P and dS tiles
 
 struct BwdWs {
-  size_t dq, dk, dv, dkc, dbc, G, lam, dd, dsig, dqp, dqh, counts, cursor, boff, toff, pairs, tmp, total;
+  size_t dq, dk, dv, dkc, dbc, G, lam, dd, dsig, dqp, dqh, counts, cursor, boff, toff, pairs, tmp, imap, total;
 };
 size_t alb(size_t x) { return (x + 255) / 256 * 256; }
 BwdWs bwd_ws(const Geom& g) {
@@ -74,6 +74,7 @@ BwdWs bwd_ws(const Geom& g) {
   take(w.toff, (nbk + 1) * 4);
   take(w.pairs, ent * 4);
   take(w.tmp, ent * 4);
+  take(w.imap, (size_t)bucket_items_bound(g) * 4);
   w.total = off;
   return w;
 }
@@ -189,26 +190,6 @@ HILS_DEV void dkdv_from_tiles(const GradLds<D>& L, float* __restrict__ dk, float
       const int key = 32 * kt + acc_row(rr, hf);
       if (key < nkeys) atomicAdd(&dst[(kvrow0 + key) * D + e], acc[rr] * sc);
     }
-  }
-}
-
-// The flush of a wave's dk / dv blocks (wave w owns blocks w, w + 4, ..., summed over a
-// work item's tiles in registers) to the fp32 accumulators.
-template <int D>
-HILS_DEV void dkdv_flush(const f32x16_t (&acc)[D / 32], float* __restrict__ dk, float* __restrict__ dv,
-                         int64_t kvrow0, float tau) {
-  constexpr int NDT = D / 32;
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, hf = lane >> 5;
-#pragma unroll
-  for (int ib = 0; ib < NDT; ++ib) {
-    const int blk = w + 4 * ib;
-    const bool isk = blk >= 2 * NDT;
-    const int kt = (blk % (2 * NDT)) / NDT, dt = blk % NDT;
-    float* dst = isk ? dk : dv;
-    const float sc = isk ? tau : 1.0f;
-    const int e = 32 * dt + (lane & 31);
-#pragma unroll
-    for (int rr = 0; rr < 16; ++rr) atomicAdd(&dst[(kvrow0 + 32 * kt + acc_row(rr, hf)) * D + e], acc[ib][rr] * sc);
   }
 }
 
@@ -360,48 +341,73 @@ __global__ void __launch_bounds__(256) bwd_window(const bf16_t* __restrict__ q, 
 
 // ------------------------------------------------------------------- bwd_pairs
 // One work item = up to BUCKET_ITEM_ROWS gathered rows of one bucket (b, h, c), in
-// tiles of 128 (32 per wave).  Per row: S and dP' on the MFMA, the chunk softmax P,
-// e = sum_j P_j dP'_j, w = exp(s_ic - Lambda_i), dsigma = w (e - g.o_i) (stored per pair),
-// dS = P w (dP' - e), the pair's dq (stored as a partial); dk/dv over the tile's rows; and
-// the item's sum dsigma q (q^ = (I + U D) q is linear in q) and db'_c = sum dsigma, added
-// atomically.
+// tiles of 128 rows, eight waves: two waves share each SIMD, so one hides the other's
+// latencies.  Per row (16 per wave, on 16x16x32 MFMAs): S and dP' against the staged
+// chunk, the chunk softmax P, e = sum_j P_j dP'_j, w = exp(s_ic - Lambda_i),
+// dsigma = w (e - g.o_i) (stored per pair), dS = P w (dP' - e) and the pair's dq (stored
+// as a bf16 partial).  Then, over the tile's 128 rows (32x32x16 MFMAs from transposed
+// LDS tiles), dk/dv summed in registers over the item's tiles before one atomic flush,
+// and the item's sum dsigma q (q^ = (I + U D) q is linear in q) and db'_c = sum dsigma,
+// added atomically.
 //
-// The q and g rows of a wave's 32 rows are gathered as whole rows (16 bytes per lane)
-// straight into registers one tile ahead and written to the wave's rows of the LDS
-// tiles, from which both the row operands of S and dP' and the transposed operands of
-// the dk/dv products are read.  sum dsigma q runs on the MFMA beside dk: dsigma (split
-// into two bf16 terms) sits in columns 64 and 65 of the P w tile's rows (its padding),
-// and a 32-column operand read there meets the q tile; only output columns 0 and 1 are
-// used (an MFMA output column depends on its own operand column only).
+// The q and g rows of a wave's 16 rows are gathered as whole rows (16 bytes per lane)
+// into registers one tile ahead and written to the wave's rows of the LDS tiles, from
+// which both the row operands of S and dP' and the transposed operands of the dk/dv
+// products are read.  sum dsigma q runs on the MFMA beside dk: dsigma (split into two
+// bf16 terms) sits in columns 64 and 65 of the P w tile's rows (its padding), and a
+// 32-column operand read there meets the q tile; only output columns 0 and 1 are used
+// (an MFMA output column depends on its own operand column only).
+constexpr int BP_WAVES = 8;
+constexpr int BP_THREADS = 64 * BP_WAVES;
+constexpr int BP_RW = BW_ROWS / BP_WAVES;  // rows per wave in the row products
+static_assert(BP_RW == 16, "the row products are 16x16x32 MFMAs");
+
+// K^T as the A operand of dq^T = K^T dS^T (16x16x32): lane l gets head dim 16 dt + (l & 15)
+// and keys 32 kk + 4 (l >> 4) + 0..3, then 32 kk + 16 + 4 (l >> 4) + 0..3 -- the keys
+// that lane's dS registers hold -- by two transposing reads of the [key][dim] tile.
+template <int LDK>
+HILS_DEV bf16x8_t kt16_operand(const uint16_t* kplane, int dt, int kk, int lane) {
+  const int g = lane >> 4, j = lane & 15;
+  const int e = 16 * dt + 4 * (j & 3);
+  const int k0 = 32 * kk + 4 * g + (j >> 2);
+  const s16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(kplane + k0 * LDK + e));
+  const s16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(kplane + (k0 + 16) * LDK + e));
+  u32x4_t u;
+  u.x = (uint32_t)(uint16_t)lo[0] | ((uint32_t)(uint16_t)lo[1] << 16);
+  u.y = (uint32_t)(uint16_t)lo[2] | ((uint32_t)(uint16_t)lo[3] << 16);
+  u.z = (uint32_t)(uint16_t)hi[0] | ((uint32_t)(uint16_t)hi[1] << 16);
+  u.w = (uint32_t)(uint16_t)hi[2] | ((uint32_t)(uint16_t)hi[3] << 16);
+  return __builtin_bit_cast(bf16x8_t, u);
+}
+
 template <int D>
-__global__ void __launch_bounds__(256) bwd_pairs(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
-                                                 const bf16_t* __restrict__ v, const bf16_t* __restrict__ dO,
-                                                 const float* __restrict__ sel_score,
-                                                 const float* __restrict__ lam, const float* __restrict__ dd,
-                                                 const uint32_t* __restrict__ pairs, const uint32_t* __restrict__ boff,
-                                                 const uint32_t* __restrict__ toff, float* __restrict__ dsig,
-                                                 uint16_t* __restrict__ dqp, float* __restrict__ dk, float* __restrict__ dv,
-                                                 float* __restrict__ dkc, float* __restrict__ dbc, int Hq, int Hkv,
-                                                 int N, int C, int K, int nbk) {
+__global__ void __launch_bounds__(BP_THREADS) bwd_pairs(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
+                                                        const bf16_t* __restrict__ v, const bf16_t* __restrict__ dO,
+                                                        const float* __restrict__ sel_score,
+                                                        const float* __restrict__ lam, const float* __restrict__ dd,
+                                                        const uint32_t* __restrict__ pairs,
+                                                        const uint32_t* __restrict__ boff,
+                                                        const uint32_t* __restrict__ toff,
+                                                        const uint32_t* __restrict__ imap, float* __restrict__ dsig,
+                                                        uint16_t* __restrict__ dqp, float* __restrict__ dk,
+                                                        float* __restrict__ dv, float* __restrict__ dkc,
+                                                        float* __restrict__ dbc, int Hq, int Hkv, int N, int C, int K,
+                                                        int nbk) {
   constexpr int LDR = GradLds<D>::LDR;
   constexpr int LDK = KVTile<bf16_t, D, 1, 8>::LDK, LDV = KVTile<bf16_t, D, 1, 8>::LDV;
-  constexpr int SEGS = D / 8;      // 16-byte segments of a bf16 row
-  constexpr int RPL = 64 / SEGS;   // rows covered by one wave-wide 16-byte load
-  constexpr int NLD = 32 / RPL;    // loads per lane for the wave's 32 rows
-  constexpr int NDT = D / 32;
+  constexpr int SEGS = D / 8;       // 16-byte segments of a bf16 row
+  constexpr int RPL = 64 / SEGS;    // rows covered by one wave-wide 16-byte load
+  constexpr int NLD = BP_RW / RPL;  // loads per lane for the wave's 16 rows
+  constexpr int NDT = D / 32;       // 32-dim tiles of the dk / dv blocks
+  constexpr int NB = 4 * NDT / BP_WAVES;  // dk / dv blocks per wave
+  static_assert(NB >= 1 && NB * BP_WAVES == 4 * NDT, "whole dk / dv blocks per wave");
   static_assert(LDP >= 66, "dsigma terms live in columns 64 and 65 of the P w rows");
   __shared__ GradLds<D> L;
   __shared__ uint32_t ipid[BUCKET_ITEM_ROWS];  // pair ids (row * K + slot); ~0 past the item
   __shared__ uint32_t irow[BUCKET_ITEM_ROWS];  // in-head query rows (0 past the item)
   const int item = blockIdx.x;
   if ((uint32_t)item >= toff[nbk]) return;
-  int lo = 0, hi = nbk - 1;  // bucket = last index with toff[bk] <= item
-  while (lo < hi) {
-    const int mid = (lo + hi + 1) >> 1;
-    if (toff[mid] <= (uint32_t)item) lo = mid;
-    else hi = mid - 1;
-  }
-  const int bk = lo;
+  const int bk = (int)imap[item];
   const uint32_t count = boff[bk + 1] - boff[bk];
   const uint32_t first = ((uint32_t)item - toff[bk]) * BUCKET_ITEM_ROWS;
   const uint32_t nrows = min((uint32_t)BUCKET_ITEM_ROWS, count - first);
@@ -413,14 +419,15 @@ __global__ void __launch_bounds__(256) bwd_pairs(const bf16_t* __restrict__ q, c
   const int64_t kvrow0 = ((int64_t)b * Hkv + kvh) * N + (int64_t)c * 64;
   const int tid = threadIdx.x, lane = tid & 63, hf = lane >> 5;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int j16 = lane & 15, g4 = lane >> 4;
   const float tau = 1.0f / sqrtf((float)D);
   const float cl = tau * 1.44269504088896340736f;
-  const int trow = 32 * w + (lane & 31);
+  const int trow = BP_RW * w + j16;  // this lane's row of the tile in the row products
   // every row of a bucket belongs to head bhq: 32-bit offsets from the head's bases
   const char* q_head = reinterpret_cast<const char*>(q + bhq * N * D);
   const char* g_head = reinterpret_cast<const char*>(dO + bhq * N * D);
   const uint32_t e_head = (uint32_t)(bhq * N * K);
-  for (int x = tid; x < BUCKET_ITEM_ROWS; x += 256) {
+  for (int x = tid; x < BUCKET_ITEM_ROWS; x += BP_THREADS) {
     const bool ok = (uint32_t)x < nrows;
     const uint32_t pid = ok ? pp[x] : 0xffffffffu;
     ipid[x] = pid;
@@ -429,7 +436,7 @@ __global__ void __launch_bounds__(256) bwd_pairs(const bf16_t* __restrict__ q, c
   const int ntile = (int)((nrows + BW_ROWS - 1) / BW_ROWS);
   __syncthreads();  // ipid / irow
 
-  // a tile's inputs: the wave's 32 rows of q and g as raw 16-byte row segments, and
+  // a tile's inputs: the wave's 16 rows of q and g as raw 16-byte row segments, and
   // this lane's row's pair id, score, Lambda and g.o
   const int lr = lane / SEGS, sg = lane % SEGS;
   u32x4_t gq[NLD], gg[NLD];
@@ -438,7 +445,7 @@ __global__ void __launch_bounds__(256) bwd_pairs(const bf16_t* __restrict__ q, c
   auto fetch = [&](int j) {
 #pragma unroll
     for (int u = 0; u < NLD; ++u) {
-      const uint32_t off = irow[j * BW_ROWS + 32 * w + RPL * u + lr] * (uint32_t)(D * 2) + 16u * sg;
+      const uint32_t off = irow[j * BW_ROWS + BP_RW * w + RPL * u + lr] * (uint32_t)(D * 2) + 16u * sg;
       gq[u] = *reinterpret_cast<const u32x4_t*>(q_head + off);
       gg[u] = *reinterpret_cast<const u32x4_t*>(g_head + off);
     }
@@ -450,17 +457,19 @@ __global__ void __launch_bounds__(256) bwd_pairs(const bf16_t* __restrict__ q, c
     n_go = dd[row];
   };
   if (ntile > 0) fetch(0);
-  stage_kv<bf16_t, D, 1>(L.kv, k, v, kvrow0, 64, tid, 256);
-  f32x16_t dkv[NDT];  // this wave's dk / dv blocks, summed over the item's tiles
+  stage_kv<bf16_t, D, 1>(L.kv, k, v, kvrow0, 64, tid, BP_THREADS);
+  f32x16_t dkv[NB];  // this wave's dk / dv blocks, summed over the item's tiles
 #pragma unroll
-  for (int ib = 0; ib < NDT; ++ib) dkv[ib] = zero16();
-  f32x16_t kq = zero16();  // sum dsigma q for dims 32 w + ... (waves w < NDT)
-  float bacc = 0.f;        // sum dsigma over this lane's rows
+  for (int ib = 0; ib < NB; ++ib) dkv[ib] = zero16();
+  f32x16_t kq = zero16();                // sum dsigma q, dim tile w - (BP_WAVES - NDT)
+  const bool kq_wave = w >= BP_WAVES - NDT;
+  const int kq_dt = w - (BP_WAVES - NDT);
+  float bacc = 0.f;  // sum dsigma over this lane's rows
   for (int j = 0; j < ntile; ++j) {
     __syncthreads();  // K/V staged (first tile); the previous tile's LDS tiles consumed
 #pragma unroll
     for (int u = 0; u < NLD; ++u) {
-      const int r = 32 * w + RPL * u + lr;
+      const int r = BP_RW * w + RPL * u + lr;
       *reinterpret_cast<u32x4_t*>(&L.qt[r * LDR + 8 * sg]) = gq[u];
       *reinterpret_cast<u32x4_t*>(&L.gt[r * LDR + 8 * sg]) = gg[u];
     }
@@ -469,101 +478,132 @@ __global__ void __launch_bounds__(256) bwd_pairs(const bf16_t* __restrict__ q, c
     const float sc = n_sc, Lam = n_lam, go = n_go;
     if (j + 1 < ntile) fetch(j + 1);  // the next tile's rows load during this whole tile
     __builtin_amdgcn_wave_barrier();  // the wave's rows are in LDS
-    f32x16_t s[2], dp[2];
-    {
-      bf16x8_t rb[D / 16];
+    // S^T and dP'^T in four 16-key tiles: register i of tile t holds key 16 t + 4 g4 + i
+    // of row trow
+    f32x4_t s[4], dp[4];
 #pragma unroll
-      for (int ks = 0; ks < D / 16; ++ks) rb[ks] = lds_op16(&L.qt[trow * LDR + 16 * ks + 8 * hf]);
-      keys_dot_rows<D, LDK>(L.kv.k[0], rb, s);
+    for (int t = 0; t < 4; ++t) s[t] = dp[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int ks = 0; ks < D / 16; ++ks) rb[ks] = lds_op16(&L.gt[trow * LDR + 16 * ks + 8 * hf]);
-      keys_dot_rows<D, LDV>(L.kv.v[0], rb, dp);
-    }
-    float mt = fmaxf(s[0][0], s[0][1]);
+    for (int ks = 0; ks < D / 32; ++ks) {
+      const bf16x8_t bq = lds_op16(&L.qt[trow * LDR + 32 * ks + 8 * g4]);
+      const bf16x8_t bg = lds_op16(&L.gt[trow * LDR + 32 * ks + 8 * g4]);
 #pragma unroll
-    for (int rr = 2; rr < 32; ++rr) mt = fmaxf(mt, s[rr >> 4][rr & 15]);
-    mt = fmaxf(mt, __shfl_xor(mt, 32));
-    float lt = 0.f;
-#pragma unroll
-    for (int tt = 0; tt < 2; ++tt)
-#pragma unroll
-      for (int rr = 0; rr < 16; ++rr) {
-        s[tt][rr] = __builtin_amdgcn_exp2f((s[tt][rr] - mt) * cl);
-        lt += s[tt][rr];
+      for (int t = 0; t < 4; ++t) {
+        s[t] = mfma16(lds_op16(&L.kv.k[0][(16 * t + j16) * LDK + 32 * ks + 8 * g4]), bq, s[t]);
+        dp[t] = mfma16(lds_op16(&L.kv.v[0][(16 * t + j16) * LDV + 32 * ks + 8 * g4]), bg, dp[t]);
       }
+    }
+    // the row's softmax over its 64 keys: 16 in each of the lanes j16 + 16 g4
+    float mt = s[0][0];
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) mt = fmaxf(mt, s[t][i]);
+    mt = fmaxf(mt, __shfl_xor(mt, 16));
+    mt = fmaxf(mt, __shfl_xor(mt, 32));
+    float lt = 0.f, e = 0.f;
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        s[t][i] = __builtin_amdgcn_exp2f((s[t][i] - mt) * cl);
+        lt += s[t][i];
+        e = fmaf(s[t][i], dp[t][i], e);
+      }
+    lt += __shfl_xor(lt, 16);
     lt += __shfl_xor(lt, 32);
+    e += __shfl_xor(e, 16);
+    e += __shfl_xor(e, 32);
     const float inv = __builtin_amdgcn_rcpf(lt);  // lt >= 1 (the largest logit's term)
-    float e = 0.f;
-#pragma unroll
-    for (int tt = 0; tt < 2; ++tt)
-#pragma unroll
-      for (int rr = 0; rr < 16; ++rr) e = fmaf(s[tt][rr], dp[tt][rr], e);
-    e = (e + __shfl_xor(e, 32)) * inv;
+    e *= inv;
     const float wc = ok ? __expf(sc - Lam) : 0.f;
     const float dsg = wc * (e - go);
     const float pw = inv * wc;
 #pragma unroll
-    for (int tt = 0; tt < 2; ++tt)
+    for (int t = 0; t < 4; ++t)
 #pragma unroll
-      for (int rr = 0; rr < 16; ++rr) {
-        const float p = s[tt][rr] * pw;
-        s[tt][rr] = p;                      // P w
-        dp[tt][rr] = p * (dp[tt][rr] - e);  // dS
+      for (int i = 0; i < 4; ++i) {
+        const float p = s[t][i] * pw;
+        s[t][i] = p;                      // P w
+        dp[t][i] = p * (dp[t][i] - e);    // dS
       }
-    keys_to_lds(s, L.pt, trow);
-    keys_to_lds(dp, L.st, trow);
-    if (hf == 0) {
+    // P w and dS rows (bf16) for the dk/dv products; dsigma's two terms in columns 64, 65
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      *reinterpret_cast<u32x2_t*>(&L.pt[trow * LDP + 16 * t + 4 * g4]) =
+          u32x2_t{pack_bf16x2(s[t][0], s[t][1]), pack_bf16x2(s[t][2], s[t][3])};
+      *reinterpret_cast<u32x2_t*>(&L.st[trow * LDP + 16 * t + 4 * g4]) =
+          u32x2_t{pack_bf16x2(dp[t][0], dp[t][1]), pack_bf16x2(dp[t][2], dp[t][3])};
+    }
+    if (g4 == 0) {
       const uint16_t s_hi = f32_to_bf16(dsg);
       const uint16_t s_lo = f32_to_bf16(dsg - bf16_to_f32(s_hi));
       *reinterpret_cast<uint32_t*>(&L.pt[trow * LDP + 64]) = (uint32_t)s_hi | ((uint32_t)s_lo << 16);
       bacc += dsg;
       if (ok) dsig[pid] = dsg;
     }
-    bf16x8_t db[4];
-    keys_to_b(dp, db);
-    // the pair's dq (dq^T += K^T dS^T, 32 dims at a time), stored as a partial straight
-    // from the accumulators (bwd_dq_sum adds a row's partials)
-    uint16_t* dst = dqp + (int64_t)(ok ? pid : 0u) * D + 4 * hf;
+    // the pair's dq: dq^T = K^T dS^T, 16 dims at a time (register i of tile dt holds dim
+    // 16 dt + 4 g4 + i of row trow), stored as a bf16 partial (bwd_dq_sum adds a row's)
+    bf16x8_t db[2];
 #pragma unroll
-    for (int dt = 0; dt < NDT; ++dt) {
-      f32x16_t dqa = zero16();
-#pragma unroll
-      for (int ks2 = 0; ks2 < 4; ++ks2) dqa = mfma32(vt_operand<LDK>(L.kv.k[0], dt, ks2, lane), db[ks2], dqa);
-      if (ok)
-#pragma unroll
-        for (int g4 = 0; g4 < 4; ++g4)
-          *reinterpret_cast<u32x2_t*>(dst + 32 * dt + 8 * g4) =
-              u32x2_t{pack_bf16x2(dqa[4 * g4] * tau, dqa[4 * g4 + 1] * tau),
-                      pack_bf16x2(dqa[4 * g4 + 2] * tau, dqa[4 * g4 + 3] * tau)};
+    for (int kk = 0; kk < 2; ++kk) {
+      u32x4_t u;
+      u.x = pack_bf16x2(dp[2 * kk][0], dp[2 * kk][1]);
+      u.y = pack_bf16x2(dp[2 * kk][2], dp[2 * kk][3]);
+      u.z = pack_bf16x2(dp[2 * kk + 1][0], dp[2 * kk + 1][1]);
+      u.w = pack_bf16x2(dp[2 * kk + 1][2], dp[2 * kk + 1][3]);
+      db[kk] = __builtin_bit_cast(bf16x8_t, u);
     }
-    __syncthreads();  // all four waves' rows of the P w, dS, q and g tiles are written
-    // dk / dv blocks over the tile's 128 rows (wave w owns blocks w, w + 4, ...), and sum
-    // dsigma q for dims 32 w .. 32 w + 31 (waves w < NDT)
+    uint16_t* dst = dqp + (int64_t)(ok ? pid : 0u) * D + 4 * g4;
+#pragma unroll
+    for (int dt = 0; dt < D / 16; ++dt) {
+      f32x4_t a = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk) a = mfma16(kt16_operand<LDK>(L.kv.k[0], dt, kk, lane), db[kk], a);
+      if (ok)
+        *reinterpret_cast<u32x2_t*>(dst + 16 * dt) =
+            u32x2_t{pack_bf16x2(a[0] * tau, a[1] * tau), pack_bf16x2(a[2] * tau, a[3] * tau)};
+    }
+    __syncthreads();  // all eight waves' rows of the P w, dS, q and g tiles are written
+    // dk / dv blocks over the tile's 128 rows (wave w owns blocks w, w + 8), and sum
+    // dsigma q for one 32-dim tile (the last NDT waves)
 #pragma unroll 2
     for (int ks2 = 0; ks2 < BW_ROWS / 16; ++ks2) {
 #pragma unroll
-      for (int ib = 0; ib < NDT; ++ib) {
-        const int blk = w + 4 * ib;
+      for (int ib = 0; ib < NB; ++ib) {
+        const int blk = w + BP_WAVES * ib;
         const bool isk = blk >= 2 * NDT;
         const int kt = (blk % (2 * NDT)) / NDT, dt = blk % NDT;
         dkv[ib] = mfma32(vt_operand<LDP>(isk ? L.st : L.pt, kt, ks2, lane),
                          vt_operand<LDR>(isk ? L.qt : L.gt, dt, ks2, lane), dkv[ib]);
       }
-      if (NDT == 4 || w < NDT)
-        kq = mfma32(vt_operand<LDR>(L.qt, w, ks2, lane), vt_operand<LDP>(L.pt, 2, ks2, lane), kq);
+      if (kq_wave)
+        kq = mfma32(vt_operand<LDR>(L.qt, kq_dt, ks2, lane), vt_operand<LDP>(L.pt, 2, ks2, lane), kq);
     }
   }
-  dkdv_flush<D>(dkv, dk, dv, kvrow0, tau);
+  // flush: register rr of block (kt, dt) holds key 32 kt + acc_row(rr, hf), dim 32 dt + (lane & 31)
+#pragma unroll
+  for (int ib = 0; ib < NB; ++ib) {
+    const int blk = w + BP_WAVES * ib;
+    const bool isk = blk >= 2 * NDT;
+    const int kt = (blk % (2 * NDT)) / NDT, dt = blk % NDT;
+    float* dst = isk ? dk : dv;
+    const float scl = isk ? tau : 1.0f;
+    const int e = 32 * dt + (lane & 31);
+#pragma unroll
+    for (int rr = 0; rr < 16; ++rr)
+      atomicAdd(&dst[(kvrow0 + 32 * kt + acc_row(rr, hf)) * D + e], dkv[ib][rr] * scl);
+  }
   const int64_t ci = bhq * C + c;  // landmark head = query head
-  if (NDT == 4 || w < NDT) {
+  if (kq_wave) {
     // column 0 (lanes 0, 32) holds the high terms' sums, column 1 (lanes 1, 33) the low
 #pragma unroll
     for (int rr = 0; rr < 16; ++rr) {
       const float lo2 = __shfl_down(kq[rr], 1);
-      if ((lane & 31) == 0) atomicAdd(&dkc[ci * D + 32 * w + acc_row(rr, hf)], kq[rr] + lo2);
+      if ((lane & 31) == 0) atomicAdd(&dkc[ci * D + 32 * kq_dt + acc_row(rr, hf)], kq[rr] + lo2);
     }
   }
-  bacc = wave_sum_f(hf == 0 ? bacc : 0.f);
+  bacc = wave_sum_f(bacc);  // lanes g4 != 0 hold 0
   if (lane == 0) atomicAdd(&dbc[ci], bacc);
 }
 
@@ -886,11 +926,12 @@ hipError_t launch_bwd_d(const Geom& g, const BwdArgs& a, char* ws, hipStream_t s
     uint32_t* pairs = (uint32_t*)(ws + w.pairs);
     launch_bucket_pairs(g, a.sel_idx,
                         BucketBufs{(uint32_t*)(ws + w.counts), (uint32_t*)(ws + w.cursor), boff, toff, pairs,
-                                   (uint32_t*)(ws + w.tmp)},
+                                   (uint32_t*)(ws + w.tmp), (uint32_t*)(ws + w.imap)},
                         st);
-    hipLaunchKernelGGL((bwd_pairs<D>), dim3((unsigned)items), dim3(256), 0, st, q, k, v, (const bf16_t*)a.dO,
+    hipLaunchKernelGGL((bwd_pairs<D>), dim3((unsigned)items), dim3(BP_THREADS), 0, st, q, k, v, (const bf16_t*)a.dO,
                        a.sel_score, (const float*)lam, (const float*)dd, (const uint32_t*)pairs,
-                       (const uint32_t*)boff, (const uint32_t*)toff, dsig, (uint16_t*)(ws + w.dqp), dk, dv, dkc, dbc,
+                       (const uint32_t*)boff, (const uint32_t*)toff, (const uint32_t*)(ws + w.imap), dsig,
+                       (uint16_t*)(ws + w.dqp), dk, dv, dkc, dbc,
                        g.Hq, g.Hkv, g.N, C,
                        g.K, nbk);
   }

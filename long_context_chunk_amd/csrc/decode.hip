@@ -24,8 +24,6 @@
 
 namespace hils {
 
-typedef __attribute__((ext_vector_type(4))) float f32x4_t;
-
 constexpr int DS_CHUNKS = 1024;  // chunks scored per decode_scan workgroup
 constexpr int DS_MAX_SPLIT = 16;  // scan workgroups per (b, h): N/S <= 16384
 constexpr int DS_KEEP = 32;      // candidates kept per workgroup (>= K)

@@ -121,6 +121,15 @@ HILS_DEV f32x16_t mfma32(const bf16x8_t& a, const bf16x8_t& b, const f32x16_t& c
 }
 HILS_DEV constexpr int acc_row(int r, int h) { return 8 * (r >> 2) + 4 * h + (r & 3); }
 
+// -------------------------------------------------------------------- MFMA 16x16x32
+// D[16x16] += A[16x32] * B[32x16]: A lane l supplies row (l & 15) and B lane l column
+// (l & 15), each with k-elements 8 (l >> 4) + m (m = 0..7); accumulator register i of
+// lane l holds D[row = 4 (l >> 4) + i][col = l & 15].
+typedef __attribute__((ext_vector_type(4))) float f32x4_t;
+HILS_DEV f32x4_t mfma16(const bf16x8_t& a, const bf16x8_t& b, const f32x4_t& c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
 // The k-permutation used for every MFMA k-operand: k-step ks (16 values), lane
 // half h, element m (0..7) -> index 16*ks + 8*(m>>2) + 4*h + (m&3).  With it, the
 // accumulator register r of an output tile t feeds k-step 2t + (r>>3), element

@@ -41,6 +41,7 @@ hipError_t launch_compress(int io, const void* k, const void* lmk, float* kc, fl
 constexpr int BUCKET_ITEM_ROWS = 1024;
 struct BucketBufs {
   uint32_t *counts, *cursor, *boff, *toff, *pairs, *tmp;
+  uint32_t* imap;  // work item -> bucket (bucket_items_bound entries)
 };
 void launch_bucket_pairs(const Geom& g, const int32_t* sel, BucketBufs bb, hipStream_t st);
 int64_t bucket_items_bound(const Geom& g);  // host bound on the work items (0 if no pairs)
