@@ -461,9 +461,11 @@ __global__ void __launch_bounds__(BP_THREADS) bwd_pairs(const bf16_t* __restrict
   f32x16_t dkv[NB];  // this wave's dk / dv blocks, summed over the item's tiles
 #pragma unroll
   for (int ib = 0; ib < NB; ++ib) dkv[ib] = zero16();
-  f32x16_t kq = zero16();                // sum dsigma q, dim tile w - (BP_WAVES - NDT)
-  const bool kq_wave = w >= BP_WAVES - NDT;
-  const int kq_dt = w - (BP_WAVES - NDT);
+  f32x16_t kq = zero16();  // sum dsigma q for dim tile kq_dt (waves with kq_wave)
+  // two blocks per wave: the dk waves 4..7, each on a dim tile of its own blocks;
+  // otherwise the last NDT waves
+  const bool kq_wave = NB == 2 ? w >= 4 : w >= BP_WAVES - NDT;
+  const int kq_dt = NB == 2 ? 2 * (w & 1) + ((w >> 1) & 1) : w - (BP_WAVES - NDT);
   float bacc = 0.f;  // sum dsigma over this lane's rows
   for (int j = 0; j < ntile; ++j) {
     __syncthreads();  // K/V staged (first tile); the previous tile's LDS tiles consumed
@@ -565,28 +567,47 @@ __global__ void __launch_bounds__(BP_THREADS) bwd_pairs(const bf16_t* __restrict
             u32x2_t{pack_bf16x2(a[0] * tau, a[1] * tau), pack_bf16x2(a[2] * tau, a[3] * tau)};
     }
     __syncthreads();  // all eight waves' rows of the P w, dS, q and g tiles are written
-    // dk / dv blocks over the tile's 128 rows (wave w owns blocks w, w + 8), and sum
-    // dsigma q for one 32-dim tile (the last NDT waves)
+    // dk / dv blocks over the tile's 128 rows, and sum dsigma q for one 32-dim tile.  With
+    // two blocks per wave (D = 128) a wave owns one kind and key tile and two dim tiles, so
+    // their P w / dS operand is read once, and the dk waves' sum dsigma q reuses one of
+    // their q operands.
+    if constexpr (NB == 2) {
+      const bool isk = w >= 4;
+      const int kt = (w >> 1) & 1, dt0 = 2 * (w & 1);
+      const uint16_t* at = isk ? L.st : L.pt;
+      const uint16_t* bt = isk ? L.qt : L.gt;
 #pragma unroll 2
-    for (int ks2 = 0; ks2 < BW_ROWS / 16; ++ks2) {
-#pragma unroll
-      for (int ib = 0; ib < NB; ++ib) {
-        const int blk = w + BP_WAVES * ib;
-        const bool isk = blk >= 2 * NDT;
-        const int kt = (blk % (2 * NDT)) / NDT, dt = blk % NDT;
-        dkv[ib] = mfma32(vt_operand<LDP>(isk ? L.st : L.pt, kt, ks2, lane),
-                         vt_operand<LDR>(isk ? L.qt : L.gt, dt, ks2, lane), dkv[ib]);
+      for (int ks2 = 0; ks2 < BW_ROWS / 16; ++ks2) {
+        const bf16x8_t a = vt_operand<LDP>(at, kt, ks2, lane);
+        const bf16x8_t b0 = vt_operand<LDR>(bt, dt0, ks2, lane);
+        const bf16x8_t b1 = vt_operand<LDR>(bt, dt0 + 1, ks2, lane);
+        dkv[0] = mfma32(a, b0, dkv[0]);
+        dkv[1] = mfma32(a, b1, dkv[1]);
+        if (isk) kq = mfma32(kt ? b1 : b0, vt_operand<LDP>(L.pt, 2, ks2, lane), kq);
       }
-      if (kq_wave)
-        kq = mfma32(vt_operand<LDR>(L.qt, kq_dt, ks2, lane), vt_operand<LDP>(L.pt, 2, ks2, lane), kq);
+    } else {
+#pragma unroll 2
+      for (int ks2 = 0; ks2 < BW_ROWS / 16; ++ks2) {
+#pragma unroll
+        for (int ib = 0; ib < NB; ++ib) {
+          const int blk = w + BP_WAVES * ib;
+          const bool isk = blk >= 2 * NDT;
+          const int kt = (blk % (2 * NDT)) / NDT, dt = blk % NDT;
+          dkv[ib] = mfma32(vt_operand<LDP>(isk ? L.st : L.pt, kt, ks2, lane),
+                           vt_operand<LDR>(isk ? L.qt : L.gt, dt, ks2, lane), dkv[ib]);
+        }
+        if (kq_wave)
+          kq = mfma32(vt_operand<LDR>(L.qt, kq_dt, ks2, lane), vt_operand<LDP>(L.pt, 2, ks2, lane), kq);
+      }
     }
   }
   // flush: register rr of block (kt, dt) holds key 32 kt + acc_row(rr, hf), dim 32 dt + (lane & 31)
 #pragma unroll
   for (int ib = 0; ib < NB; ++ib) {
     const int blk = w + BP_WAVES * ib;
-    const bool isk = blk >= 2 * NDT;
-    const int kt = (blk % (2 * NDT)) / NDT, dt = blk % NDT;
+    const bool isk = NB == 2 ? w >= 4 : blk >= 2 * NDT;
+    const int kt = NB == 2 ? (w >> 1) & 1 : (blk % (2 * NDT)) / NDT;
+    const int dt = NB == 2 ? 2 * (w & 1) + ib : blk % NDT;
     float* dst = isk ? dk : dv;
     const float scl = isk ? tau : 1.0f;
     const int e = 32 * dt + (lane & 31);
