@@ -357,6 +357,38 @@ __global__ void __launch_bounds__(256) bwd_window(const bf16_t* __restrict__ q, 
 // bf16 terms) sits in columns 64 and 65 of the P w tile's rows (its padding), and a
 // 32-column operand read there meets the q tile; only output columns 0 and 1 are used
 // (an MFMA output column depends on its own operand column only).
+// LDS of the pair kernel: as GradLds, but the q and g rows have a stride of D + 32 (so
+// the transposing reads of 4 consecutive rows hit disjoint banks) and their 16-byte
+// segments are swizzled by row (segment s of row r at s ^ pseg(r)), so that 16 lanes
+// reading one segment of 16 consecutive rows hit disjoint banks too.
+template <int D>
+struct PairLds {
+  static constexpr int LDR = D + 32;
+  KVTile<bf16_t, D, 1, 8> kv;
+  uint16_t qt[BW_ROWS * LDR];
+  uint16_t gt[BW_ROWS * LDR];
+  uint16_t pt[BW_ROWS * LDP];
+  uint16_t st[BW_ROWS * LDP];  // follows pt: the 32-column read at column 64 of pt's last rows stays inside
+};
+HILS_DEV constexpr int pseg(int r) { return (r >> 2) & 3; }
+
+// vt_operand on a swizzled q / g tile
+template <int LD>
+HILS_DEV bf16x8_t vt_operand_sw(const uint16_t* plane, int dt, int ks2, int lane) {
+  const int g = lane >> 4, j = lane & 15;
+  const int e = 32 * dt + 16 * (g & 1) + 4 * (j & 3);
+  const int key = 16 * ks2 + 4 * (g >> 1) + (j >> 2);
+  auto at = [&](int r) { return plane + r * LD + (((e >> 3) ^ pseg(r)) << 3) + (e & 7); };
+  const s16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)at(key));
+  const s16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)at(key + 8));
+  u32x4_t u;
+  u.x = (uint32_t)(uint16_t)lo[0] | ((uint32_t)(uint16_t)lo[1] << 16);
+  u.y = (uint32_t)(uint16_t)lo[2] | ((uint32_t)(uint16_t)lo[3] << 16);
+  u.z = (uint32_t)(uint16_t)hi[0] | ((uint32_t)(uint16_t)hi[1] << 16);
+  u.w = (uint32_t)(uint16_t)hi[2] | ((uint32_t)(uint16_t)hi[3] << 16);
+  return __builtin_bit_cast(bf16x8_t, u);
+}
+
 constexpr int BP_WAVES = 8;
 constexpr int BP_THREADS = 64 * BP_WAVES;
 constexpr int BP_RW = BW_ROWS / BP_WAVES;  // rows per wave in the row products
@@ -393,7 +425,7 @@ __global__ void __launch_bounds__(BP_THREADS) bwd_pairs(const bf16_t* __restrict
                                                         float* __restrict__ dv, float* __restrict__ dkc,
                                                         float* __restrict__ dbc, int Hq, int Hkv, int N, int C, int K,
                                                         int nbk) {
-  constexpr int LDR = GradLds<D>::LDR;
+  constexpr int LDR = PairLds<D>::LDR;
   constexpr int LDK = KVTile<bf16_t, D, 1, 8>::LDK, LDV = KVTile<bf16_t, D, 1, 8>::LDV;
   constexpr int SEGS = D / 8;       // 16-byte segments of a bf16 row
   constexpr int RPL = 64 / SEGS;    // rows covered by one wave-wide 16-byte load
@@ -402,9 +434,8 @@ __global__ void __launch_bounds__(BP_THREADS) bwd_pairs(const bf16_t* __restrict
   constexpr int NB = 4 * NDT / BP_WAVES;  // dk / dv blocks per wave
   static_assert(NB >= 1 && NB * BP_WAVES == 4 * NDT, "whole dk / dv blocks per wave");
   static_assert(LDP >= 66, "dsigma terms live in columns 64 and 65 of the P w rows");
-  __shared__ GradLds<D> L;
-  __shared__ uint32_t ipid[BUCKET_ITEM_ROWS];  // pair ids (row * K + slot); ~0 past the item
-  __shared__ uint32_t irow[BUCKET_ITEM_ROWS];  // in-head query rows (0 past the item)
+  __shared__ PairLds<D> L;
+  __shared__ uint32_t ipid[BUCKET_ITEM_ROWS];  // in-head pair index (row * K + slot); 0 past the item
   const int item = blockIdx.x;
   if ((uint32_t)item >= toff[nbk]) return;
   const int bk = (int)imap[item];
@@ -427,14 +458,13 @@ __global__ void __launch_bounds__(BP_THREADS) bwd_pairs(const bf16_t* __restrict
   const char* q_head = reinterpret_cast<const char*>(q + bhq * N * D);
   const char* g_head = reinterpret_cast<const char*>(dO + bhq * N * D);
   const uint32_t e_head = (uint32_t)(bhq * N * K);
-  for (int x = tid; x < BUCKET_ITEM_ROWS; x += BP_THREADS) {
-    const bool ok = (uint32_t)x < nrows;
-    const uint32_t pid = ok ? pp[x] : 0xffffffffu;
-    ipid[x] = pid;
-    irow[x] = ok ? (pid - e_head) / (uint32_t)K : 0u;
-  }
+  // in-head row = index / K as (index * (floor(2^32 / K) + 1)) >> 32: exact for
+  // index < 2^26 and K <= 32 (the multiplier's excess adds less than 2^-6 to index / K)
+  const uint64_t kmul = 0x100000000ull / (uint32_t)K + 1u;
+  auto row_of = [&](uint32_t x) { return (uint32_t)(((uint64_t)x * kmul) >> 32); };
+  for (int x = tid; x < BUCKET_ITEM_ROWS; x += BP_THREADS) ipid[x] = (uint32_t)x < nrows ? pp[x] - e_head : 0u;
   const int ntile = (int)((nrows + BW_ROWS - 1) / BW_ROWS);
-  __syncthreads();  // ipid / irow
+  __syncthreads();  // ipid
 
   // a tile's inputs: the wave's 16 rows of q and g as raw 16-byte row segments, and
   // this lane's row's pair id, score, Lambda and g.o
@@ -445,13 +475,14 @@ __global__ void __launch_bounds__(BP_THREADS) bwd_pairs(const bf16_t* __restrict
   auto fetch = [&](int j) {
 #pragma unroll
     for (int u = 0; u < NLD; ++u) {
-      const uint32_t off = irow[j * BW_ROWS + BP_RW * w + RPL * u + lr] * (uint32_t)(D * 2) + 16u * sg;
+      const uint32_t off = row_of(ipid[j * BW_ROWS + BP_RW * w + RPL * u + lr]) * (uint32_t)(D * 2) + 16u * sg;
       gq[u] = *reinterpret_cast<const u32x4_t*>(q_head + off);
       gg[u] = *reinterpret_cast<const u32x4_t*>(g_head + off);
     }
-    n_pid = ipid[j * BW_ROWS + trow];
-    const bool ok = n_pid != 0xffffffffu;
-    const int64_t row = bhq * N + irow[j * BW_ROWS + trow];
+    const uint32_t el = ipid[j * BW_ROWS + trow];
+    const bool ok = (uint32_t)(j * BW_ROWS + trow) < nrows;
+    n_pid = ok ? e_head + el : 0xffffffffu;
+    const int64_t row = bhq * N + row_of(el);
     n_sc = ok ? sel_score[n_pid] : 0.f;
     n_lam = lam[row];
     n_go = dd[row];
@@ -472,8 +503,8 @@ __global__ void __launch_bounds__(BP_THREADS) bwd_pairs(const bf16_t* __restrict
 #pragma unroll
     for (int u = 0; u < NLD; ++u) {
       const int r = BP_RW * w + RPL * u + lr;
-      *reinterpret_cast<u32x4_t*>(&L.qt[r * LDR + 8 * sg]) = gq[u];
-      *reinterpret_cast<u32x4_t*>(&L.gt[r * LDR + 8 * sg]) = gg[u];
+      *reinterpret_cast<u32x4_t*>(&L.qt[r * LDR + 8 * (sg ^ pseg(r))]) = gq[u];
+      *reinterpret_cast<u32x4_t*>(&L.gt[r * LDR + 8 * (sg ^ pseg(r))]) = gg[u];
     }
     const uint32_t pid = n_pid;
     const bool ok = pid != 0xffffffffu;
@@ -487,8 +518,9 @@ __global__ void __launch_bounds__(BP_THREADS) bwd_pairs(const bf16_t* __restrict
     for (int t = 0; t < 4; ++t) s[t] = dp[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int ks = 0; ks < D / 32; ++ks) {
-      const bf16x8_t bq = lds_op16(&L.qt[trow * LDR + 32 * ks + 8 * g4]);
-      const bf16x8_t bg = lds_op16(&L.gt[trow * LDR + 32 * ks + 8 * g4]);
+      const int so = 8 * ((4 * ks + g4) ^ pseg(trow));
+      const bf16x8_t bq = lds_op16(&L.qt[trow * LDR + so]);
+      const bf16x8_t bg = lds_op16(&L.gt[trow * LDR + so]);
 #pragma unroll
       for (int t = 0; t < 4; ++t) {
         s[t] = mfma16(lds_op16(&L.kv.k[0][(16 * t + j16) * LDK + 32 * ks + 8 * g4]), bq, s[t]);
@@ -579,8 +611,8 @@ __global__ void __launch_bounds__(BP_THREADS) bwd_pairs(const bf16_t* __restrict
 #pragma unroll 2
       for (int ks2 = 0; ks2 < BW_ROWS / 16; ++ks2) {
         const bf16x8_t a = vt_operand<LDP>(at, kt, ks2, lane);
-        const bf16x8_t b0 = vt_operand<LDR>(bt, dt0, ks2, lane);
-        const bf16x8_t b1 = vt_operand<LDR>(bt, dt0 + 1, ks2, lane);
+        const bf16x8_t b0 = vt_operand_sw<LDR>(bt, dt0, ks2, lane);
+        const bf16x8_t b1 = vt_operand_sw<LDR>(bt, dt0 + 1, ks2, lane);
         dkv[0] = mfma32(a, b0, dkv[0]);
         dkv[1] = mfma32(a, b1, dkv[1]);
         if (isk) kq = mfma32(kt ? b1 : b0, vt_operand<LDP>(L.pt, 2, ks2, lane), kq);
@@ -594,10 +626,10 @@ __global__ void __launch_bounds__(BP_THREADS) bwd_pairs(const bf16_t* __restrict
           const bool isk = blk >= 2 * NDT;
           const int kt = (blk % (2 * NDT)) / NDT, dt = blk % NDT;
           dkv[ib] = mfma32(vt_operand<LDP>(isk ? L.st : L.pt, kt, ks2, lane),
-                           vt_operand<LDR>(isk ? L.qt : L.gt, dt, ks2, lane), dkv[ib]);
+                           vt_operand_sw<LDR>(isk ? L.qt : L.gt, dt, ks2, lane), dkv[ib]);
         }
         if (kq_wave)
-          kq = mfma32(vt_operand<LDR>(L.qt, kq_dt, ks2, lane), vt_operand<LDP>(L.pt, 2, ks2, lane), kq);
+          kq = mfma32(vt_operand_sw<LDR>(L.qt, kq_dt, ks2, lane), vt_operand<LDP>(L.pt, 2, ks2, lane), kq);
       }
     }
   }
