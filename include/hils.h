@@ -79,7 +79,7 @@ typedef struct {
   int32_t B;         /* batch (sequences)                                              */
   int32_t Hq;        /* query heads                                                    */
   int32_t Hkv;       /* KV heads; Hq % Hkv == 0                                        */
-  int32_t Hlmk;      /* landmark heads; this build requires Hlmk == Hq                  */
+  int32_t Hlmk;      /* landmark heads; the library requires Hlmk == Hq                */
   int32_t d;         /* head dimension: 64 or 128                                      */
   int32_t S;         /* chunk size: 64                                                 */
   int32_t K;         /* top-K chunks per query: 1 <= K <= 32                            */
@@ -155,7 +155,7 @@ int hils_attn_prefill_timed(const hils_dims_t* dims, const void* q, const void* 
  * kc/bc [B,Hlmk,floor(N/S),d] must hold the compressed keys of every complete
  * chunk c < floor((seq_lens[b]-1)/S) (see hils_landmark_compress).
  * Writes o [B,Hq,d]; sel_idx_out (nullable) [B,Hq,K].
- * Limits of this build: N/S <= 16384 (decode and prefill); prefill also needs
+ * Limits of the library: N/S <= 16384 (decode and prefill); prefill also needs
  * B*Hq*N*K < 2^32.
  */
 int hils_attn_decode(const hils_dims_t* dims, const void* q, const void* k_cache, const void* v_cache,

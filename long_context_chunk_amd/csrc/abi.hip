@@ -42,7 +42,7 @@ int check_dims(const hils_dims_t* dims, hils::Geom& g) {
   if (s.qcal_rank < 0) return fail(HILS_E_INVAL, "qcal_rank must be >= 0 (%d)", s.qcal_rank);
   if (s.d < 1 || s.S < 1) return fail(HILS_E_INVAL, "d and S must be >= 1 (d=%d S=%d)", s.d, s.S);
   if (s.io != HILS_F32 && s.io != HILS_BF16) return fail(HILS_E_UNSUPPORTED, "io dtype %d not supported", s.io);
-  if (s.Hlmk != s.Hq) return fail(HILS_E_UNSUPPORTED, "this build needs Hlmk == Hq (got Hlmk=%d Hq=%d)", s.Hlmk, s.Hq);
+  if (s.Hlmk != s.Hq) return fail(HILS_E_UNSUPPORTED, "the library needs Hlmk == Hq (got Hlmk=%d Hq=%d)", s.Hlmk, s.Hq);
   if (s.d != 64 && s.d != 128) return fail(HILS_E_UNSUPPORTED, "head dim %d not supported (64 or 128)", s.d);
   if (s.S != 64) return fail(HILS_E_UNSUPPORTED, "chunk size %d not supported (64)", s.S);
   if (s.K > 32) return fail(HILS_E_UNSUPPORTED, "K=%d not supported (K <= 32)", s.K);

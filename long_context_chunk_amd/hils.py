@@ -44,11 +44,11 @@ _lib = None
 
 
 def load():
-    """Load libhils.so (built in-tree by __graft_entry__.build())."""
+    """Load libhils.so (built in-tree by long_context_chunk_amd.build.build())."""
     global _lib
     if _lib is None:
         if not os.path.exists(LIB_PATH):
-            raise RuntimeError("libhils.so is not built (%s); run __graft_entry__.build()" % LIB_PATH)
+            raise RuntimeError("libhils.so is not built (%s); run long_context_chunk_amd.build.build()" % LIB_PATH)
         lib = ctypes.CDLL(LIB_PATH)
         vp, i32, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t
         dp = ctypes.POINTER(Dims)
