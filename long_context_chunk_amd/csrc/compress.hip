@@ -31,9 +31,26 @@ __global__ void __launch_bounds__(256) compress_kernel(const IO* __restrict__ k,
   const int G = Hl / Hkv;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
 
-  // stage the key tile
+  // stage the key tile (fp32 in LDS), 16-byte loads: the chunk's rows are consecutive
   const IO* kt = k + pg.chunk_row(b, kvh, Hkv, N, c) * D;
-  for (int i = tid; i < S * D; i += 256) ks[(i / D) * LD + (i % D)] = io_traits<IO>::load(kt, i);
+  constexpr int EPV = 16 / (int)sizeof(IO);  // elements per 16-byte load
+  for (int i = tid * EPV; i < S * D; i += 256 * EPV) {
+    const u32x4_t raw = *reinterpret_cast<const u32x4_t*>(kt + i);
+    float* dst = ks + (i / D) * LD + (i % D);
+    if constexpr (sizeof(IO) == 2) {
+      const uint32_t wd[4] = {raw.x, raw.y, raw.z, raw.w};
+#pragma unroll
+      for (int m = 0; m < 4; ++m) {
+        dst[2 * m] = __uint_as_float(wd[m] << 16);
+        dst[2 * m + 1] = __uint_as_float(wd[m] & 0xffff0000u);
+      }
+    } else {
+      dst[0] = __uint_as_float(raw.x);
+      dst[1] = __uint_as_float(raw.y);
+      dst[2] = __uint_as_float(raw.z);
+      dst[3] = __uint_as_float(raw.w);
+    }
+  }
   __syncthreads();
 
   const float tau = 1.0f / sqrtf((float)D);
