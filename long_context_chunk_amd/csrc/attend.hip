@@ -155,6 +155,123 @@ __global__ void __launch_bounds__(1024) bucket_scan(uint32_t* __restrict__ count
   }
 }
 
+// The same scan for many buckets, in three steps over blocks of 1024 buckets: block
+// totals (parked in the first entry of the block's boff / toff range), their exclusive
+// scan by one workgroup (which also writes the grand totals), then each block's own scan
+// from its offset.  Each block reads only its own parked totals before overwriting them.
+constexpr int SCAN_BLOCK = 1024;
+
+__global__ void __launch_bounds__(256) bucket_block_sums(const uint32_t* __restrict__ counts,
+                                                         uint32_t* __restrict__ boff, uint32_t* __restrict__ toff,
+                                                         int nbk) {
+  __shared__ uint32_t wsum[8];
+  const int i0 = blockIdx.x * SCAN_BLOCK, t = threadIdx.x;
+  uint32_t a = 0, b = 0;
+  for (int i = i0 + t; i < min(nbk, i0 + SCAN_BLOCK); i += 256) {
+    const uint32_t ci = counts[i];
+    a += ci;
+    b += (ci + ITEM_ROWS - 1) / ITEM_ROWS;
+  }
+  for (int o = 32; o > 0; o >>= 1) {
+    a += __shfl_xor(a, o);
+    b += __shfl_xor(b, o);
+  }
+  if ((t & 63) == 0) {
+    wsum[t >> 6] = a;
+    wsum[4 + (t >> 6)] = b;
+  }
+  __syncthreads();
+  if (t == 0) {
+    boff[i0] = wsum[0] + wsum[1] + wsum[2] + wsum[3];
+    toff[i0] = wsum[4] + wsum[5] + wsum[6] + wsum[7];
+  }
+}
+
+__global__ void __launch_bounds__(1024) bucket_block_scan(uint32_t* __restrict__ boff, uint32_t* __restrict__ toff,
+                                                          int nbk, int nblk) {
+  __shared__ uint32_t sa[1024], sb[1024];
+  const int t = threadIdx.x;
+  const int per = (nblk + 1023) / 1024;
+  const int beg = min(nblk, t * per), end = min(nblk, beg + per);
+  uint32_t a = 0, b = 0;
+  for (int j = beg; j < end; ++j) {
+    a += boff[j * SCAN_BLOCK];
+    b += toff[j * SCAN_BLOCK];
+  }
+  sa[t] = a;
+  sb[t] = b;
+  __syncthreads();
+  for (int o = 1; o < 1024; o <<= 1) {  // Hillis-Steele inclusive scan
+    const uint32_t xa = t >= o ? sa[t - o] : 0, xb = t >= o ? sb[t - o] : 0;
+    __syncthreads();
+    sa[t] += xa;
+    sb[t] += xb;
+    __syncthreads();
+  }
+  uint32_t ra = sa[t] - a, rb = sb[t] - b;
+  for (int j = beg; j < end; ++j) {
+    const uint32_t xa = boff[j * SCAN_BLOCK], xb = toff[j * SCAN_BLOCK];
+    boff[j * SCAN_BLOCK] = ra;
+    toff[j * SCAN_BLOCK] = rb;
+    ra += xa;
+    rb += xb;
+  }
+  if (t == 1023) {
+    boff[nbk] = sa[t];
+    toff[nbk] = sb[t];
+  }
+}
+
+__global__ void __launch_bounds__(256) bucket_block_fill(uint32_t* __restrict__ counts, uint32_t* __restrict__ boff,
+                                                         uint32_t* __restrict__ toff, int nbk) {
+  __shared__ uint32_t wsum[8];
+  const int i0 = blockIdx.x * SCAN_BLOCK, t = threadIdx.x, lane = t & 63, w = t >> 6;
+  const uint32_t a0 = boff[i0], b0 = toff[i0];  // the block's offsets (parked by the scan)
+  // four consecutive buckets per thread
+  uint32_t c[4], it[4], a = 0, b = 0;
+#pragma unroll
+  for (int m = 0; m < 4; ++m) {
+    const int i = i0 + 4 * t + m;
+    c[m] = i < nbk ? counts[i] : 0u;
+    it[m] = (c[m] + ITEM_ROWS - 1) / ITEM_ROWS;
+    a += c[m];
+    b += it[m];
+  }
+  // exclusive scan of (a, b) over the 256 threads
+  uint32_t xa = a, xb = b;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const uint32_t ya = __shfl_up(xa, o), yb = __shfl_up(xb, o);
+    if (lane >= o) {
+      xa += ya;
+      xb += yb;
+    }
+  }
+  if (lane == 63) {
+    wsum[w] = xa;
+    wsum[4 + w] = xb;
+  }
+  __syncthreads();  // every thread has read boff[i0] / toff[i0] above
+  uint32_t ra = a0 + xa - a, rb = b0 + xb - b;
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+    if (j < w) {
+      ra += wsum[j];
+      rb += wsum[4 + j];
+    }
+#pragma unroll
+  for (int m = 0; m < 4; ++m) {
+    const int i = i0 + 4 * t + m;
+    if (i < nbk) {
+      boff[i] = ra;
+      toff[i] = rb;
+      counts[i] = 0;  // from here on: the second sorting pass's cursor of bucket i
+    }
+    ra += c[m];
+    rb += it[m];
+  }
+}
+
 // Work item -> bucket: each bucket writes its own items' entries, so the work kernels
 // find their bucket with one load instead of a search over toff.
 __global__ void __launch_bounds__(256) bucket_item_map(const uint32_t* __restrict__ toff, uint32_t* __restrict__ imap,
@@ -744,7 +861,15 @@ void launch_bucket_pairs(const Geom& g, const int32_t* sel, BucketBufs bb, hipSt
   const int spg = (int)((group_len + HIST_SLICE - 1) / HIST_SLICE);
   const int ngrp = g.B * g.Hq;
   hipLaunchKernelGGL(bucket_count, dim3(ngrp * spg), dim3(256), 0, st, sel, bb.counts, group_len, spg, C);
-  hipLaunchKernelGGL(bucket_scan, dim3(1), dim3(1024), 0, st, bb.counts, bb.boff, bb.toff, nbk);
+  if (nbk <= 16 * 1024) {  // one workgroup scans up to 16K buckets quickly
+    hipLaunchKernelGGL(bucket_scan, dim3(1), dim3(1024), 0, st, bb.counts, bb.boff, bb.toff, nbk);
+  } else {
+    const int nblk = (nbk + SCAN_BLOCK - 1) / SCAN_BLOCK;
+    hipLaunchKernelGGL(bucket_block_sums, dim3(nblk), dim3(256), 0, st, (const uint32_t*)bb.counts, bb.boff, bb.toff,
+                       nbk);
+    hipLaunchKernelGGL(bucket_block_scan, dim3(1), dim3(1024), 0, st, bb.boff, bb.toff, nbk, nblk);
+    hipLaunchKernelGGL(bucket_block_fill, dim3(nblk), dim3(256), 0, st, bb.counts, bb.boff, bb.toff, nbk);
+  }
   hipLaunchKernelGGL(bucket_item_map, dim3((nbk + 255) / 256), dim3(256), 0, st, (const uint32_t*)bb.toff, bb.imap,
                      nbk);
   const int nrg = (C + (1 << FINE_BITS) - 1) >> FINE_BITS;
