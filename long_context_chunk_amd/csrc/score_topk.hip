@@ -835,7 +835,7 @@ __global__ void __launch_bounds__(256) prep_kprime(const float* __restrict__ kc,
           split_bf16<2>(bv, sp2);
           e[0] = sp2[0];
           e[1] = sp2[1];
-          e[2] = 0x3980;  // TH_ABS = 2^-12
+          e[2] = f32_to_bf16(TH_ABS);  // 2^-12, exact in bf16 (0x3980)
           e[3] = bf16_up(sqrtf(s2));
           f[0] = sp3[0];
           f[1] = sp3[1];
