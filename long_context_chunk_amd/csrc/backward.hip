@@ -44,7 +44,7 @@ constexpr int BW_ROWS = 128;  // rows per tile: 4 waves x 32
 constexpr int LDP = 64 + 8;   // bf16 row stride of the [row][key] P and dS tiles
 
 struct BwdWs {
-  size_t dq, dk, dv, dkc, dbc, G, lam, dd, dsig, dqp, dqh, counts, cursor, boff, toff, pairs, tmp, imap, total;
+  size_t dq, dk, dv, dkc, dbc, G, lam, dd, dsig, dqp, kdq, counts, cursor, boff, toff, pairs, tmp, imap, total;
 };
 size_t alb(size_t x) { return (x + 255) / 256 * 256; }
 BwdWs bwd_ws(const Geom& g) {
@@ -67,7 +67,7 @@ BwdWs bwd_ws(const Geom& g) {
   take(w.dd, rows * 4);
   take(w.dsig, ent * 4);
   take(w.dqp, ent * g.d * 2);  // per (row, slot) dq of the selected chunk's attention (bf16)
-  take(w.dqh, r > 0 ? rows * g.d * 2 : 0);  // dq^ (bf16) for the Q-Cal backward
+  take(w.kdq, r > 0 ? lrows * g.d * 4 : 0);  // k'_c + D^T U^T k'_c per chunk (Q-Cal)
   take(w.counts, nbk * 4);  // counts and cursor contiguous (zeroed together)
   take(w.cursor, nbk * 4);
   take(w.boff, (nbk + 1) * 4);
@@ -420,7 +420,8 @@ __global__ void __launch_bounds__(BP_THREADS) bwd_pairs(const bf16_t* __restrict
                                                         const uint32_t* __restrict__ pairs,
                                                         const uint32_t* __restrict__ boff,
                                                         const uint32_t* __restrict__ toff,
-                                                        const uint32_t* __restrict__ imap, float* __restrict__ dsig,
+                                                        const uint32_t* __restrict__ imap,
+                                                        const float* __restrict__ kdq, float* __restrict__ dsig,
                                                         uint16_t* __restrict__ dqp, float* __restrict__ dk,
                                                         float* __restrict__ dv, float* __restrict__ dkc,
                                                         float* __restrict__ dbc, int Hq, int Hkv, int N, int C, int K,
@@ -436,6 +437,7 @@ __global__ void __launch_bounds__(BP_THREADS) bwd_pairs(const bf16_t* __restrict
   static_assert(LDP >= 66, "dsigma terms live in columns 64 and 65 of the P w rows");
   __shared__ PairLds<D> L;
   __shared__ uint32_t ipid[BUCKET_ITEM_ROWS];  // in-head pair index (row * K + slot); 0 past the item
+  __shared__ __align__(16) float kdq_s[D];     // the chunk's score direction (I + D^T U^T) k'_c
   const int item = blockIdx.x;
   if ((uint32_t)item >= toff[nbk]) return;
   const int bk = (int)imap[item];
@@ -463,6 +465,7 @@ __global__ void __launch_bounds__(BP_THREADS) bwd_pairs(const bf16_t* __restrict
   const uint64_t kmul = 0x100000000ull / (uint32_t)K + 1u;
   auto row_of = [&](uint32_t x) { return (uint32_t)(((uint64_t)x * kmul) >> 32); };
   for (int x = tid; x < BUCKET_ITEM_ROWS; x += BP_THREADS) ipid[x] = (uint32_t)x < nrows ? pp[x] - e_head : 0u;
+  if (tid < D) kdq_s[tid] = kdq[(bhq * C + c) * D + tid];  // landmark head = query head
   const int ntile = (int)((nrows + BW_ROWS - 1) / BW_ROWS);
   __syncthreads();  // ipid
 
@@ -577,7 +580,8 @@ __global__ void __launch_bounds__(BP_THREADS) bwd_pairs(const bf16_t* __restrict
       if (ok) dsig[pid] = dsg;
     }
     // the pair's dq: dq^T = K^T dS^T, 16 dims at a time (register i of tile dt holds dim
-    // 16 dt + 4 g4 + i of row trow), stored as a bf16 partial (bwd_dq_sum adds a row's)
+    // 16 dt + 4 g4 + i of row trow), plus the score term dsigma (I + D^T U^T) k'_c, times
+    // tau, stored as a bf16 partial (bwd_dq_sum adds a row's)
     bf16x8_t db[2];
 #pragma unroll
     for (int kk = 0; kk < 2; ++kk) {
@@ -594,9 +598,12 @@ __global__ void __launch_bounds__(BP_THREADS) bwd_pairs(const bf16_t* __restrict
       f32x4_t a = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int kk = 0; kk < 2; ++kk) a = mfma16(kt16_operand<LDK>(L.kv.k[0], dt, kk, lane), db[kk], a);
-      if (ok)
+      if (ok) {
+        const f32x4_t kd = *reinterpret_cast<const f32x4_t*>(&kdq_s[16 * dt + 4 * g4]);
         *reinterpret_cast<u32x2_t*>(dst + 16 * dt) =
-            u32x2_t{pack_bf16x2(a[0] * tau, a[1] * tau), pack_bf16x2(a[2] * tau, a[3] * tau)};
+            u32x2_t{pack_bf16x2(tau * fmaf(dsg, kd[0], a[0]), tau * fmaf(dsg, kd[1], a[1])),
+                    pack_bf16x2(tau * fmaf(dsg, kd[2], a[2]), tau * fmaf(dsg, kd[3], a[3]))};
+      }
     }
     __syncthreads();  // all eight waves' rows of the P w, dS, q and g tiles are written
     // dk / dv blocks over the tile's 128 rows, and sum dsigma q for one 32-dim tile.  With
@@ -661,166 +668,104 @@ __global__ void __launch_bounds__(BP_THREADS) bwd_pairs(const bf16_t* __restrict
 }
 
 // ------------------------------------------------------------------ bwd_dq_sum
-// Per row (one wave, lanes over the dims): dq += the selected chunks' dq partials (bf16) +
-// dq^, dq^ = tau sum_x dsigma_x k'_(sel x); dq^ is also kept (bf16) for the Q-Cal
-// backward.  The row's selections are read once and broadcast from lanes.
+// Per row (one wave, lanes over the dims): dq += the selected chunks' dq partials (bf16;
+// each already holds the pair's score term tau dsigma (I + D^T U^T) k'_c).  The row's
+// number of selections comes from one ballot.
 template <int D, int KMAX>
-__global__ void __launch_bounds__(256) bwd_dq_sum(const float* __restrict__ kc, const int32_t* __restrict__ sel,
-                                                  const float* __restrict__ dsig, const uint16_t* __restrict__ dqp,
-                                                  float* __restrict__ dq, bf16_t* __restrict__ dqh, int N, int C, int K,
-                                                  int64_t rows) {
+__global__ void __launch_bounds__(256) bwd_dq_sum(const int32_t* __restrict__ sel, const uint16_t* __restrict__ dqp,
+                                                  float* __restrict__ dq, int K, int64_t rows) {
   constexpr int EPL = D / 64;
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-  const float tau = 1.0f / sqrtf((float)D);
   for (int64_t row = (int64_t)blockIdx.x * 4 + w; row < rows; row += (int64_t)gridDim.x * 4) {
     const int32_t sl = lane < K ? sel[row * K + lane] : -1;
-    const float sg = lane < K ? dsig[row * K + lane] * tau : 0.f;
     const int n = __popcll(__ballot(sl >= 0));  // valid selections come first
-    const float* kch = kc + (row / N) * (int64_t)C * D + lane * EPL;
     const uint16_t* pr = dqp + row * K * D + lane * EPL;
-    // every slot's loads at once (slots past n read slot 0 and chunk 0, in bounds, and
-    // are dropped), so the row's reads are all in flight together.  A row without
-    // selections reads nothing: with no complete chunk there is no k' at all.
+    // every slot's load at once (slots past n read slot 0, in bounds, and are dropped)
     uint32_t pv[KMAX];
-    float kv[KMAX][EPL];
 #pragma unroll
     for (int x = 0; x < KMAX; ++x) {
-      pv[x] = 0u;
-#pragma unroll
-      for (int u = 0; u < EPL; ++u) kv[x][u] = 0.f;
+      const int xs = x < n ? x : 0;
+      pv[x] = EPL == 2 ? *reinterpret_cast<const uint32_t*>(pr + (int64_t)xs * D) : pr[(int64_t)xs * D];
     }
-    if (n > 0) {  // wave-uniform
+    float acc[EPL];
 #pragma unroll
-      for (int x = 0; x < KMAX; ++x) {
-        const int xs = x < n ? x : 0;
-        const int cc = max(__builtin_amdgcn_readlane(sl, x < K ? x : 0), 0);
-        pv[x] = EPL == 2 ? *reinterpret_cast<const uint32_t*>(pr + (int64_t)xs * D) : pr[(int64_t)xs * D];
-#pragma unroll
-        for (int u = 0; u < EPL; ++u) kv[x][u] = kch[(int64_t)cc * D + u];
-      }
-    }
-    float acc[EPL], gh[EPL];
-#pragma unroll
-    for (int u = 0; u < EPL; ++u) acc[u] = gh[u] = 0.f;
+    for (int u = 0; u < EPL; ++u) acc[u] = 0.f;
 #pragma unroll
     for (int x = 0; x < KMAX; ++x) {
       const bool live = x < n;
-      const float sgx = live ? __int_as_float(__builtin_amdgcn_readlane(__float_as_int(sg), x)) : 0.f;
-      const float p0 = __uint_as_float(pv[x] << 16), p1 = __uint_as_float(pv[x] & 0xffff0000u);
-      acc[0] += live ? p0 : 0.f;
-      if constexpr (EPL == 2) acc[1] += live ? p1 : 0.f;
-#pragma unroll
-      for (int u = 0; u < EPL; ++u) gh[u] = fmaf(sgx, kv[x][u], gh[u]);
+      acc[0] += live ? __uint_as_float(pv[x] << 16) : 0.f;
+      if constexpr (EPL == 2) acc[1] += live ? __uint_as_float(pv[x] & 0xffff0000u) : 0.f;
     }
 #pragma unroll
-    for (int u = 0; u < EPL; ++u) {
-      dq[row * D + lane * EPL + u] += acc[u] + gh[u];
-      if (dqh) dqh[row * D + lane * EPL + u].bits = f32_to_bf16(gh[u]);
+    for (int u = 0; u < EPL; ++u) dq[row * D + lane * EPL + u] += acc[u];
+  }
+}
+
+// -------------------------------------------------------------------- Q-Cal
+// The scores' query gradient dq^_i = tau sum_x dsigma_ix k'_(c_x) enters dq through
+// (I + D^T U^T), and the weight gradients through G_h = sum_i dq^_i q_i^T.  Both are
+// linear in the per-chunk quantities, so neither needs dq^ per row:
+//   dq_i gets tau dsigma_ic (k'_c + D^T U^T k'_c) with each selected pair (bwd_pairs adds
+//     it to the pair's partial; bwd_kdq forms k'_c + D^T (U^T k'_c) per chunk), and
+//   G_h = tau sum_(b,c) k'_(b,h,c) S_(b,h,c)^T with S_c = sum over the chunk's pairs of
+//     dsigma q, the sums bwd_pairs leaves for the compression backward (bwd_qcal_g).
+// dU = G D^T and dD = U^T G follow per head (bwd_qcal_weights).
+constexpr int KDQ_CHUNKS = 8;  // chunks per bwd_kdq workgroup
+
+template <int D>
+__global__ void __launch_bounds__(256) bwd_kdq(const float* __restrict__ kc, const bf16_t* __restrict__ Dw,
+                                               const bf16_t* __restrict__ Uw, float* __restrict__ kdq, int Hl,
+                                               int C, int r) {
+  __shared__ float kr[D], t[32];
+  const int nblk = (C + KDQ_CHUNKS - 1) / KDQ_CHUNKS;
+  const int64_t bh = blockIdx.x / nblk;  // b * Hl + h
+  const int h = (int)(bh % Hl);
+  const int c0 = (int)(blockIdx.x % nblk) * KDQ_CHUNKS;
+  const int tid = threadIdx.x;
+  for (int c = c0; c < min(C, c0 + KDQ_CHUNKS); ++c) {
+    const int64_t row = (bh * C + c) * D;
+    __syncthreads();  // the previous chunk's kr / t consumed
+    if (tid < D) kr[tid] = kc[row + tid];
+    __syncthreads();
+    if (tid < r) {  // t = U_h^T k'_c
+      float acc = 0.f;
+      for (int e = 0; e < D; ++e) acc = fmaf(bf16_to_f32(Uw[((int64_t)h * D + e) * r + tid].bits), kr[e], acc);
+      t[tid] = acc;
+    }
+    __syncthreads();
+    if (tid < D) {  // k'_c + D_h^T t
+      float acc = kr[tid];
+      for (int a = 0; a < r; ++a) acc = fmaf(bf16_to_f32(Dw[((int64_t)h * r + a) * D + tid].bits), t[a], acc);
+      kdq[row + tid] = acc;
     }
   }
 }
 
-// -------------------------------------------------------------------- bwd_qcal
-// Q-Cal backward on the MFMA for the rows of one (b, h), 128 rows (32 per wave) at a time:
-//   u = dQ^ U (rows x r),  dq += u D (rows x d),  G += dQ^^T Q (d x d, summed over rows),
-// with D^T, U^T and the rows' q, dq^ and u as bf16 tiles in LDS; each wave keeps a
-// quarter of G's 32x32 tiles in registers and adds them to the head's G at the end.
-// dU = G D^T and dD = U^T G follow per head (bwd_qcal_weights).
-constexpr int QC_BLOCK = 1024;  // rows per workgroup
-constexpr int RPAD = 32 + 8;    // row stride of the rank-r tiles (r <= 32, zero padded)
-
+// G_h[a][e] = tau sum over (b, c) of k'[b,h,c][a] S[b,h,c][e]; one workgroup per head and
+// 16 rows a, one thread per (e, group of rows).
 template <int D>
-struct QcalLds {
-  static constexpr int LDG = D + 8;
-  uint16_t dt[D * RPAD];        // D^T [e][a]
-  uint16_t ut[32 * LDG];        // U^T [a][e]
-  uint16_t qt[BW_ROWS * LDG];   // q rows
-  uint16_t gt[BW_ROWS * LDG];   // dq^ rows
-  uint16_t vt[BW_ROWS * RPAD];  // u rows
-};
-
-template <int D>
-__global__ void __launch_bounds__(256) bwd_qcal(const bf16_t* __restrict__ q, const bf16_t* __restrict__ Dw,
-                                                const bf16_t* __restrict__ Uw, const bf16_t* __restrict__ dqh,
-                                                float* __restrict__ dq, float* __restrict__ G, int Hq, int N, int r) {
-  constexpr int LDG = QcalLds<D>::LDG, NDT = D / 32;
-  constexpr int NGT = NDT * NDT, GPW = (NGT + 3) / 4;  // G tiles, per wave
-  __shared__ QcalLds<D> L;
-  const int nblk = (N + QC_BLOCK - 1) / QC_BLOCK;
-  const int64_t bh = blockIdx.x / nblk;
-  const int i0 = (int)(blockIdx.x % nblk) * QC_BLOCK, i1 = min(N, i0 + QC_BLOCK);
-  const int h = (int)(bh % Hq);
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, hf = lane >> 5;
-  for (int x = tid; x < D * RPAD; x += 256) {  // D^T and U^T, zero beyond rank r
-    const int e = x / RPAD, a = x % RPAD;
-    L.dt[x] = a < r ? Dw[((int64_t)h * r + a) * D + e].bits : (uint16_t)0;
-  }
-  for (int x = tid; x < 32 * LDG; x += 256) {
-    const int a = x / LDG, e = x % LDG;
-    L.ut[x] = (a < r && e < D) ? Uw[((int64_t)h * D + e) * r + a].bits : (uint16_t)0;
-  }
-  f32x16_t gacc[GPW];
+__global__ void __launch_bounds__(256) bwd_qcal_g(const float* __restrict__ kc, const float* __restrict__ S,
+                                                  float* __restrict__ G, int B, int Hq, int C) {
+  constexpr int ARB = 16;               // rows a per workgroup
+  constexpr int TPE = 256 / D;          // threads per column e
+  constexpr int APT = ARB / TPE;        // rows per thread
+  const int h = blockIdx.x / (D / ARB), a0 = (blockIdx.x % (D / ARB)) * ARB;
+  const int e = threadIdx.x % D, ag = threadIdx.x / D;
+  float acc[APT];
 #pragma unroll
-  for (int t = 0; t < GPW; ++t) gacc[t] = zero16();
-  const int rl = 32 * w + (lane & 31);
-  for (int rb = i0; rb < i1; rb += BW_ROWS) {
-    __syncthreads();  // previous rows consumed (and the weights staged)
-    for (int x = tid; x < BW_ROWS * (D / 8); x += 256) {  // q and dq^ rows, 16 bytes per thread
-      const int rw = x / (D / 8), sg = x % (D / 8);
-      u32x4_t qv = {0u, 0u, 0u, 0u}, gv = {0u, 0u, 0u, 0u};
-      if (rb + rw < i1) {
-        const int64_t off = (bh * N + rb + rw) * D + 8 * sg;
-        qv = *reinterpret_cast<const u32x4_t*>(q + off);
-        gv = *reinterpret_cast<const u32x4_t*>(dqh + off);
-      }
-      *reinterpret_cast<u32x4_t*>(&L.qt[rw * LDG + 8 * sg]) = qv;
-      *reinterpret_cast<u32x4_t*>(&L.gt[rw * LDG + 8 * sg]) = gv;
-    }
-    __syncthreads();
-    // u = dQ^ U for the wave's 32 rows: A = dq^ rows (k = dims), B = U^T rows (lane = a)
-    f32x16_t u = zero16();
+  for (int m = 0; m < APT; ++m) acc[m] = 0.f;
+  for (int b = 0; b < B; ++b) {
+    const int64_t base = ((int64_t)b * Hq + h) * C * D;
+    for (int c = 0; c < C; ++c) {
+      const float sv = S[base + (int64_t)c * D + e];
+      const float* kr = kc + base + (int64_t)c * D + a0 + ag * APT;
 #pragma unroll
-    for (int ks = 0; ks < D / 16; ++ks)
-      u = mfma32(lds_op16(&L.gt[rl * LDG + 16 * ks + 8 * hf]), lds_op16(&L.ut[(lane & 31) * LDG + 16 * ks + 8 * hf]), u);
-    // u[row acc_row][a = lane] -> the u tile (bf16), then dq += u D
-#pragma unroll
-    for (int rr = 0; rr < 16; ++rr) L.vt[(32 * w + acc_row(rr, hf)) * RPAD + (lane & 31)] = f32_to_bf16(u[rr]);
-    __builtin_amdgcn_wave_barrier();
-#pragma unroll
-    for (int dtile = 0; dtile < NDT; ++dtile) {
-      f32x16_t y = zero16();
-#pragma unroll
-      for (int ks = 0; ks < 2; ++ks)
-        y = mfma32(lds_op16(&L.vt[rl * RPAD + 16 * ks + 8 * hf]),
-                   lds_op16(&L.dt[(32 * dtile + (lane & 31)) * RPAD + 16 * ks + 8 * hf]), y);
-#pragma unroll
-      for (int rr = 0; rr < 16; ++rr) {
-        const int rw = rb + 32 * w + acc_row(rr, hf);
-        if (rw < i1) dq[(bh * N + rw) * D + 32 * dtile + (lane & 31)] += y[rr];
-      }
-    }
-    // G += dQ^^T Q over the 128 rows: A = dq^^T, B = Q (both transposed reads, k = rows)
-#pragma unroll
-    for (int t = 0; t < GPW; ++t) {
-      const int gt_ = w + 4 * t;
-      if (gt_ < NGT) {
-        const int ta = gt_ / NDT, tb = gt_ % NDT;
-#pragma unroll
-        for (int ks2 = 0; ks2 < BW_ROWS / 16; ++ks2)
-          gacc[t] = mfma32(vt_operand<LDG>(L.gt, ta, ks2, lane), vt_operand<LDG>(L.qt, tb, ks2, lane), gacc[t]);
-      }
+      for (int m = 0; m < APT; ++m) acc[m] = fmaf(kr[m], sv, acc[m]);
     }
   }
+  const float tau = 1.0f / sqrtf((float)D);
 #pragma unroll
-  for (int t = 0; t < GPW; ++t) {
-    const int gt_ = w + 4 * t;
-    if (gt_ < NGT) {
-      const int ta = gt_ / NDT, tb = gt_ % NDT;
-#pragma unroll
-      for (int rr = 0; rr < 16; ++rr)
-        atomicAdd(&G[((int64_t)h * D + 32 * ta + acc_row(rr, hf)) * D + 32 * tb + (lane & 31)], gacc[t][rr]);
-    }
-  }
+  for (int m = 0; m < APT; ++m) G[((int64_t)h * D + a0 + ag * APT + m) * D + e] = tau * acc[m];
 }
 
 // dU_h = G_h D_h^T and dD_h = U_h^T G_h (bf16 out), one workgroup per head.
@@ -967,6 +912,13 @@ hipError_t launch_bwd_d(const Geom& g, const BwdArgs& a, char* ws, hipStream_t s
   // the accumulators dk .. dU are contiguous
   const int64_t nz = (int64_t)(w.lam - w.dk) / 4;
   hipLaunchKernelGGL(bwd_zero, dim3(grid_for(nz)), dim3(256), 0, st, dk, nz);
+  // the chunks' score directions: k' itself, or k' + D^T U^T k' under Q-Cal
+  const float* kdq = a.kc;
+  if (g.r > 0 && C > 0) {
+    kdq = (const float*)(ws + w.kdq);
+    hipLaunchKernelGGL((bwd_kdq<D>), dim3(g.B * g.Hl * ((C + KDQ_CHUNKS - 1) / KDQ_CHUNKS)), dim3(256), 0, st, a.kc,
+                       Dw, Uw, (float*)(ws + w.kdq), g.Hl, C, g.r);
+  }
   const int NQC = (g.N + 63) / 64;
   const int ngb = (g.G() + 1) / 2;
   hipLaunchKernelGGL((bwd_window<D>), dim3(g.B * g.Hkv * NQC * ngb), dim3(256), 0, st, q, k, v, (const bf16_t*)a.o,
@@ -983,29 +935,24 @@ hipError_t launch_bwd_d(const Geom& g, const BwdArgs& a, char* ws, hipStream_t s
                         st);
     hipLaunchKernelGGL((bwd_pairs<D>), dim3((unsigned)items), dim3(BP_THREADS), 0, st, q, k, v, (const bf16_t*)a.dO,
                        a.sel_score, (const float*)lam, (const float*)dd, (const uint32_t*)pairs,
-                       (const uint32_t*)boff, (const uint32_t*)toff, (const uint32_t*)(ws + w.imap), dsig,
+                       (const uint32_t*)boff, (const uint32_t*)toff, (const uint32_t*)(ws + w.imap), kdq, dsig,
                        (uint16_t*)(ws + w.dqp), dk, dv, dkc, dbc,
                        g.Hq, g.Hkv, g.N, C,
                        g.K, nbk);
   }
-  bf16_t* dqh = g.r > 0 ? (bf16_t*)(ws + w.dqh) : nullptr;
   {
     const dim3 grid((unsigned)std::min<int64_t>((rows + 3) / 4, 1 << 20));
     const uint16_t* dqp = (const uint16_t*)(ws + w.dqp);
     if (g.K <= 8)
-      hipLaunchKernelGGL((bwd_dq_sum<D, 8>), grid, dim3(256), 0, st, a.kc, a.sel_idx, dsig, dqp, dq, dqh, g.N, C, g.K,
-                         rows);
+      hipLaunchKernelGGL((bwd_dq_sum<D, 8>), grid, dim3(256), 0, st, a.sel_idx, dqp, dq, g.K, rows);
     else if (g.K <= 16)
-      hipLaunchKernelGGL((bwd_dq_sum<D, 16>), grid, dim3(256), 0, st, a.kc, a.sel_idx, dsig, dqp, dq, dqh, g.N, C, g.K,
-                         rows);
+      hipLaunchKernelGGL((bwd_dq_sum<D, 16>), grid, dim3(256), 0, st, a.sel_idx, dqp, dq, g.K, rows);
     else
-      hipLaunchKernelGGL((bwd_dq_sum<D, 32>), grid, dim3(256), 0, st, a.kc, a.sel_idx, dsig, dqp, dq, dqh, g.N, C, g.K,
-                         rows);
+      hipLaunchKernelGGL((bwd_dq_sum<D, 32>), grid, dim3(256), 0, st, a.sel_idx, dqp, dq, g.K, rows);
   }
   if (g.r > 0) {
-    const int nqb = (g.N + QC_BLOCK - 1) / QC_BLOCK;
-    hipLaunchKernelGGL((bwd_qcal<D>), dim3(g.B * g.Hq * nqb), dim3(256), 0, st, q, Dw, Uw, (const bf16_t*)dqh, dq, G,
-                       g.Hq, g.N, g.r);
+    hipLaunchKernelGGL((bwd_qcal_g<D>), dim3(g.Hq * (D / 16)), dim3(256), 0, st, a.kc, (const float*)dkc, G, g.B,
+                       g.Hq, C);
     hipLaunchKernelGGL((bwd_qcal_weights<D>), dim3(g.Hq), dim3(256), 0, st, (const float*)G, Dw, Uw, (bf16_t*)a.dD,
                        (bf16_t*)a.dU, g.r);
   }
