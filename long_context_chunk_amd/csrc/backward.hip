@@ -225,16 +225,15 @@ __global__ void __launch_bounds__(256) bwd_window(const bf16_t* __restrict__ q, 
   const int64_t row = bh * N + (ok ? i : 0);
   const float tau = 1.0f / sqrtf((float)D);
   const float cl = tau * 1.44269504088896340736f;
+  // the row's q, g and o as MFMA operands (16 bytes per k-step), read unconditionally:
+  // a row past N or of a missing head reads row 0 of the head and gets zero weight below
   bf16x8_t qb[1][D / 16], gb8[D / 16], ob[D / 16];
-  load_q_operand<bf16_t, D, 1>(q, row * D, ok, qb);
-  {
-    bf16x8_t tmp[1][D / 16];
-    load_q_operand<bf16_t, D, 1>(dO, row * D, ok, tmp);
 #pragma unroll
-    for (int ks = 0; ks < D / 16; ++ks) gb8[ks] = tmp[0][ks];
-    load_q_operand<bf16_t, D, 1>(o, row * D, ok, tmp);
-#pragma unroll
-    for (int ks = 0; ks < D / 16; ++ks) ob[ks] = tmp[0][ks];
+  for (int ks = 0; ks < D / 16; ++ks) {
+    const int64_t off = row * D + 16 * ks + 8 * hf;
+    qb[0][ks] = *reinterpret_cast<const bf16x8_t*>(q + off);
+    gb8[ks] = *reinterpret_cast<const bf16x8_t*>(dO + off);
+    ob[ks] = *reinterpret_cast<const bf16x8_t*>(o + off);
   }
   // g.o_i (each lane half holds 8 of every 16 dims)
   float go = 0.f;
@@ -305,10 +304,12 @@ __global__ void __launch_bounds__(256) bwd_window(const bf16_t* __restrict__ q, 
   for (int dt = 0; dt < D / 32; ++dt) dqa[dt] = zero16();
   const float lse2 = lse * 1.44269504088896340736f;
   for (int c = c0; c <= qc; ++c) {
-    __syncthreads();  // every wave is done with the previous chunk's tiles
     const int nkeys = min(64, N - c * 64);
-    stage_kv<bf16_t, D, 1>(L.kv, k, v, kv0 + (int64_t)c * 64, nkeys, tid, 256);
-    __syncthreads();
+    if (c0 != qc) {  // a one-chunk window reuses the tile pass 1 left staged
+      __syncthreads();  // every wave is done with the previous chunk's tiles
+      stage_kv<bf16_t, D, 1>(L.kv, k, v, kv0 + (int64_t)c * 64, nkeys, tid, 256);
+      __syncthreads();
+    }
     f32x16_t s[2], dp[2];
     keys_dot_rows<D, KVTile<bf16_t, D, 1, 8>::LDK>(L.kv.k[0], qb[0], s);
     keys_dot_rows<D, KVTile<bf16_t, D, 1, 8>::LDV>(L.kv.v[0], gb8, dp);
