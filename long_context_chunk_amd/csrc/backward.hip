@@ -810,9 +810,16 @@ __global__ void __launch_bounds__(256) bwd_compress(const bf16_t* __restrict__ k
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int64_t kb = ((int64_t)b * Hkv + kvh) * N + (int64_t)c * 64;
   const float tau = 1.0f / sqrtf((float)D);
-  for (int x = tid; x < 64 * D; x += 256) {
-    ks[x / D][x % D] = bf16_to_f32(k[kb * D + x].bits);
-    acc[x / D][x % D] = 0.f;
+  for (int x = tid * 8; x < 64 * D; x += 256 * 8) {  // 16-byte loads: the chunk's rows are consecutive
+    const u32x4_t raw = *reinterpret_cast<const u32x4_t*>(k + kb * D + x);
+    const uint32_t wd[4] = {raw.x, raw.y, raw.z, raw.w};
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+      ks[x / D][x % D + 2 * m] = __uint_as_float(wd[m] << 16);
+      ks[x / D][x % D + 2 * m + 1] = __uint_as_float(wd[m] & 0xffff0000u);
+    }
+#pragma unroll
+    for (int m = 0; m < 8; ++m) acc[x / D][x % D + m] = 0.f;
   }
   const int lpk = Hl / Hkv;
   for (int li = 0; li < lpk; ++li) {
@@ -827,16 +834,25 @@ __global__ void __launch_bounds__(256) bwd_compress(const bf16_t* __restrict__ k
     __syncthreads();
     // dk' = tau (I + U_l D_l) (sum dsigma q): the scores use q^ = q + U (D q)
     if (r > 0) {
-      if (tid < r) {
+      {  // t = D_l gk: eight threads per rank index a, each over D / 8 dims
+        const int a = tid >> 3, part = tid & 7;
         float t = 0.f;
-        for (int e = 0; e < D; ++e) t = fmaf(bf16_to_f32(Dw[((int64_t)l * r + tid) * D + e].bits), gk[e], t);
-        tr[tid] = t;
+        if (a < r)
+          for (int e = part; e < D; e += 8) t = fmaf(bf16_to_f32(Dw[((int64_t)l * r + a) * D + e].bits), gk[e], t);
+        t += __shfl_xor(t, 1);
+        t += __shfl_xor(t, 2);
+        t += __shfl_xor(t, 4);
+        if (a < r && part == 0) tr[a] = t;
       }
       __syncthreads();
-      for (int e = tid; e < D; e += 256) {
-        float acc2 = gk[e];
-        for (int a2 = 0; a2 < r; ++a2) acc2 = fmaf(bf16_to_f32(Uw[((int64_t)l * D + e) * r + a2].bits), tr[a2], acc2);
-        gk[e] = acc2 * tau;
+      {  // gk += U_l t: 256 / D threads per dim, each over a share of the rank
+        constexpr int TPE = 256 / D;
+        const int e = tid / TPE, part = tid % TPE;
+        float acc2 = 0.f;
+        for (int a2 = part; a2 < r; a2 += TPE) acc2 = fmaf(bf16_to_f32(Uw[((int64_t)l * D + e) * r + a2].bits), tr[a2], acc2);
+        for (int o = 1; o < TPE; o <<= 1) acc2 += __shfl_xor(acc2, o);
+        __syncthreads();  // every thread has read gk (in t) before it is rewritten
+        if (part == 0) gk[e] = (gk[e] + acc2) * tau;
       }
     } else {
       for (int e = tid; e < D; e += 256) gk[e] *= tau;
@@ -884,7 +900,14 @@ __global__ void __launch_bounds__(256) bwd_compress(const bf16_t* __restrict__ k
     }
   }
   __syncthreads();
-  for (int x = tid; x < 64 * D; x += 256) dk[kb * D + x] += acc[x / D][x % D];
+  for (int x = tid * 4; x < 64 * D; x += 256 * 4) {
+    float4 d4 = *reinterpret_cast<const float4*>(dk + kb * D + x);
+    d4.x += acc[x / D][x % D];
+    d4.y += acc[x / D][x % D + 1];
+    d4.z += acc[x / D][x % D + 2];
+    d4.w += acc[x / D][x % D + 3];
+    *reinterpret_cast<float4*>(dk + kb * D + x) = d4;
+  }
 }
 
 __global__ void __launch_bounds__(256) bwd_convert(const float* __restrict__ src, bf16_t* __restrict__ dst, int64_t n) {
