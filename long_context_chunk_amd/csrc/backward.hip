@@ -669,12 +669,14 @@ __global__ void __launch_bounds__(BP_THREADS) bwd_pairs(const bf16_t* __restrict
 }
 
 // ------------------------------------------------------------------ bwd_dq_sum
-// Per row (one wave, lanes over the dims): dq += the selected chunks' dq partials (bf16;
-// each already holds the pair's score term tau dsigma (I + D^T U^T) k'_c).  The row's
-// number of selections comes from one ballot.
+// Per row (one wave, lanes over the dims): the output dq (bf16) = the window's dq (fp32) +
+// the selected chunks' dq partials (bf16; each already holds the pair's score term
+// tau dsigma (I + D^T U^T) k'_c).  The row's number of selections comes from one ballot.
+// This is the last step of dq, so the sum is rounded straight into the output.
 template <int D, int KMAX>
 __global__ void __launch_bounds__(256) bwd_dq_sum(const int32_t* __restrict__ sel, const uint16_t* __restrict__ dqp,
-                                                  float* __restrict__ dq, int K, int64_t rows) {
+                                                  const float* __restrict__ dq, bf16_t* __restrict__ out, int K,
+                                                  int64_t rows) {
   constexpr int EPL = D / 64;
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   for (int64_t row = (int64_t)blockIdx.x * 4 + w; row < rows; row += (int64_t)gridDim.x * 4) {
@@ -698,7 +700,7 @@ __global__ void __launch_bounds__(256) bwd_dq_sum(const int32_t* __restrict__ se
       if constexpr (EPL == 2) acc[1] += live ? __uint_as_float(pv[x] & 0xffff0000u) : 0.f;
     }
 #pragma unroll
-    for (int u = 0; u < EPL; ++u) dq[row * D + lane * EPL + u] += acc[u];
+    for (int u = 0; u < EPL; ++u) out[row * D + lane * EPL + u].bits = f32_to_bf16(dq[row * D + lane * EPL + u] + acc[u]);
   }
 }
 
@@ -968,11 +970,14 @@ hipError_t launch_bwd_d(const Geom& g, const BwdArgs& a, char* ws, hipStream_t s
     const dim3 grid((unsigned)std::min<int64_t>((rows + 3) / 4, 1 << 20));
     const uint16_t* dqp = (const uint16_t*)(ws + w.dqp);
     if (g.K <= 8)
-      hipLaunchKernelGGL((bwd_dq_sum<D, 8>), grid, dim3(256), 0, st, a.sel_idx, dqp, dq, g.K, rows);
+      hipLaunchKernelGGL((bwd_dq_sum<D, 8>), grid, dim3(256), 0, st, a.sel_idx, dqp, (const float*)dq,
+                         (bf16_t*)a.dq, g.K, rows);
     else if (g.K <= 16)
-      hipLaunchKernelGGL((bwd_dq_sum<D, 16>), grid, dim3(256), 0, st, a.sel_idx, dqp, dq, g.K, rows);
+      hipLaunchKernelGGL((bwd_dq_sum<D, 16>), grid, dim3(256), 0, st, a.sel_idx, dqp, (const float*)dq,
+                         (bf16_t*)a.dq, g.K, rows);
     else
-      hipLaunchKernelGGL((bwd_dq_sum<D, 32>), grid, dim3(256), 0, st, a.sel_idx, dqp, dq, g.K, rows);
+      hipLaunchKernelGGL((bwd_dq_sum<D, 32>), grid, dim3(256), 0, st, a.sel_idx, dqp, (const float*)dq,
+                         (bf16_t*)a.dq, g.K, rows);
   }
   if (g.r > 0) {
     hipLaunchKernelGGL((bwd_qcal_g<D>), dim3(g.Hq * (D / 16)), dim3(256), 0, st, a.kc, (const float*)dkc, G, g.B,
@@ -984,7 +989,6 @@ hipError_t launch_bwd_d(const Geom& g, const BwdArgs& a, char* ws, hipStream_t s
     hipLaunchKernelGGL((bwd_compress<D>), dim3(g.B * g.Hkv * C), dim3(256), 0, st, k, (const bf16_t*)a.lmk,
                        (const float*)dkc, (const float*)dbc, Dw, Uw, dk, (bf16_t*)a.dlmk, g.Hl, g.Hkv, g.N, C, g.r);
   const int64_t kvn = (int64_t)g.B * g.Hkv * g.N * D;
-  hipLaunchKernelGGL(bwd_convert, dim3(grid_for(rows * D)), dim3(256), 0, st, (const float*)dq, (bf16_t*)a.dq, rows * D);
   hipLaunchKernelGGL(bwd_convert, dim3(grid_for(kvn)), dim3(256), 0, st, (const float*)dk, (bf16_t*)a.dk, kvn);
   hipLaunchKernelGGL(bwd_convert, dim3(grid_for(kvn)), dim3(256), 0, st, (const float*)dv, (bf16_t*)a.dv, kvn);
   return hipGetLastError();
