@@ -18,18 +18,20 @@
 //     dL_c = tau sum_j dz_j k_j,  dk_j += a_j dk'_c + tau dz_j L_c.
 //
 // Kernels, in launch order (bf16 I/O, fp32 accumulation in the workspace):
+//   bwd_kdq       (Q-Cal) per chunk: the score direction k'_c + D^T (U^T k'_c)
 //   bwd_window    per (b, KV head, query chunk, pair of heads): the window's LSE, the
 //                 row's fusion normaliser Lambda_i and g.o_i, then the window's
 //                 gradients on the MFMA (dq stored, dk/dv added atomically)
 //   bucketing     the forward's (b, head, chunk) bucketing of the selection pairs
-//   bwd_pairs     per bucket work item: the chunk's K/V staged once, 32 gathered rows
-//                 per wave: S, dP' on the MFMA, dsigma and dq per pair, then dk/dv
-//                 over the tile's 128 rows on the MFMA from transposed LDS tiles; dk'/db'
-//   bwd_dq_sum    per row: the pairs' dq partials and dq^ from their dsigma and k'
-//   bwd_qcal      Q-Cal backward on the MFMA: dq += D^T U^T dq^, G = sum dq^ q^T per head,
-//                 then dU = G D^T, dD = U^T G (bwd_qcal_weights)
+//   bwd_pairs     per bucket work item, eight waves: the chunk's K/V staged once, 16
+//                 gathered rows per wave: S, dP' on the MFMA, dsigma and the pair's dq
+//                 (with its score term) as a bf16 partial, then dk/dv over the tile's 128
+//                 rows on the MFMA from transposed LDS tiles; the chunk's sum dsigma q, db'
+//   bwd_dq_sum    per row: the window's dq plus the pairs' partials, rounded to the output
+//   bwd_qcal_g    (Q-Cal) per head: G = tau sum_c k'_c (sum dsigma q)_c^T, then
+//                 dU = G D^T, dD = U^T G (bwd_qcal_weights)
 //   bwd_compress  per (b, KV head, chunk): the landmark compression's backward
-//   bwd_convert   fp32 accumulators to the output dtype
+//   bwd_convert   dk, dv accumulators to the output dtype
 #include <algorithm>
 
 #include "attn_tile.h"
