@@ -211,9 +211,12 @@ int hils_attn_decode_paged(const hils_dims_t* dims, const void* q, const void* k
  * sum(o * dO) with the selection held fixed (top-K is piecewise constant):
  *   dq [B,Hq,N,d], dk, dv [B,Hkv,N,d], dlmk [B,Hlmk,C,d] (landmark queries, through
  *   k' and b'), dD [Hq,r,d], dU [Hq,d,r] (Q-Cal; may be NULL when qcal_rank == 0).
- * bf16 I/O only (HILS_E_UNSUPPORTED otherwise); gradients are accumulated in fp32
- * in the workspace (hils_workspace_bytes(dims, HILS_OP_BACKWARD)) and rounded to
- * bf16 once; float atomics make the low bits of dq, dk and dv depend on timing.
+ * bf16 I/O only (HILS_E_UNSUPPORTED otherwise).  Workspace:
+ * hils_workspace_bytes(dims, HILS_OP_BACKWARD).  dq is the sum of one bf16 partial per
+ * (row, selected chunk) (its attention term and its score term) and the window's fp32
+ * term, added in a fixed order and rounded to bf16 once: deterministic.  dk, dv, the
+ * landmark and Q-Cal gradients are accumulated in fp32 with float atomics and rounded
+ * once, so their low bits depend on timing.
  * lmk_q, kc and dlmk may be NULL when N < S.  Same limits as hils_attn_prefill.
  * Asynchronous on `stream`.
  */

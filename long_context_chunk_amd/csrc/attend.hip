@@ -12,7 +12,7 @@
 // Chunk-major execution.  The pages' kernel packs M adjacent queries x G heads and
 // loads the union of their chunks; on near-independent selections that union is
 // dozens of times larger than K and most MFMA work is masked out.  Here every
-// (query row, selected chunk) pair is bucketed by (batch, KV head, chunk); each
+// (query row, selected chunk) pair is bucketed by (batch, query head, chunk); each
 // workgroup loads one chunk's K/V tile into LDS once and runs full 32-row MFMA
 // tiles of gathered query rows against it.  Per pair it writes the normalised
 // chunk output o_ic (fp16 for bf16 I/O, fp32 for fp32 I/O) to a slot of its row

@@ -64,7 +64,7 @@ BwdWs bwd_ws(const Geom& g) {
   take(w.dv, kvrows * g.d * 4);
   take(w.dkc, lrows * g.d * 4);
   take(w.dbc, lrows * 4);
-  take(w.G, r > 0 ? (size_t)g.Hq * g.d * g.d * 4 : 0);  // sum over rows of dq^ q^T, per head
+  take(w.G, r > 0 ? (size_t)g.Hq * g.d * g.d * 4 : 0);  // G = tau sum_c k'_c S_c^T per head (S_c = sum dsigma q)
   take(w.lam, rows * 4);
   take(w.dd, rows * 4);
   take(w.dsig, ent * 4);

@@ -438,3 +438,205 @@ def test_paged_decode_window_matches_contiguous():
     torch.cuda.synchronize()
     np.testing.assert_array_equal(sel.cpu().numpy(), ref["sel_idx"])
     np.testing.assert_array_equal(o.float().cpu().numpy(), ref["o"])
+
+
+# --------------------------------------- chunk-paged KV cache against the oracle
+PAGED = [
+    ("bf16_d128", 0, 0),
+    ("bf16_d128_qcal", 8, 0),
+    ("bf16_d128_w512", 0, 512),
+    ("bf16_d128_qcal_w256", 8, 256),
+]
+
+
+@pytest.mark.parametrize("name,qcal,window", PAGED, ids=[p[0] for p in PAGED])
+def test_paged_decode_against_oracle(name, qcal, window):
+    """The paged path on its own: landmark compression one chunk at a time from shuffled
+    pages against the oracle's compression, then the paged decode step against the oracle's
+    forward pass on the contiguous cache (selection and output, the usual bar)."""
+    w = synth.Workload("paged_" + name, B=3, Hq=4, Hkv=2, d=128, N=2048, K=8, decode=True,
+                       seq_lens=[2048, 1000, 70], qcal_rank=qcal, window=window, needle_frac=0.05)
+    _say("paged decode vs oracle", name)
+    x = synth.make_inputs(w, SEED + 31)
+    kp, vp, table = _paginate(w, x, 17)
+    dm = dims_of(w)
+    kpt, vpt = upload(kp, w.io), upload(vp, w.io)
+    tab = torch.from_numpy(table).cuda()
+    kc = torch.full((w.B, w.Hlmk, w.C, w.d), float("nan"), dtype=torch.float32, device="cuda")
+    bc = torch.full((w.B, w.Hlmk, w.C), float("nan"), dtype=torch.float32, device="cuda")
+    lmk = upload(x["lmk"], w.io)
+    for c in range(w.C):  # incremental, as chunks complete during decoding
+        hils.landmark_compress_paged(dm, kpt, tab, lmk, kc, bc, c, c + 1)
+    torch.cuda.synchronize()
+    kc_o, bc_o = oracle_compress(w, x)
+    np.testing.assert_allclose(kc.cpu().numpy(), kc_o, rtol=0, atol=1e-5 * max(1.0, np.abs(kc_o).max()))
+    np.testing.assert_allclose(bc.cpu().numpy(), bc_o, rtol=0, atol=1e-5)
+    q = upload(x["q"], w.io)
+    o = torch.full_like(q, float("nan"))
+    sel = torch.empty((w.B, w.Hq, w.K), dtype=torch.int32, device="cuda")
+    ws = hils.workspace(dm, hils.OP_DECODE)
+    D = upload(x["D"], w.io) if w.qcal_rank else None
+    U = upload(x["U"], w.io) if w.qcal_rank else None
+    hils.attn_decode_paged(dm, q, kpt, vpt, tab, torch.from_numpy(x["seq_lens"]).cuda(), kc, bc, o, ws, qcal_D=D,
+                           qcal_U=U, sel_idx=sel)
+    torch.cuda.synchronize()
+    rows_b = [b for b in range(w.B) for h in range(w.Hq)]
+    rows_h = [h for b in range(w.B) for h in range(w.Hq)]
+    pos = [int(x["seq_lens"][b]) - 1 for b in rows_b]
+    ref = oracle.attend(shape_of(w), rows_b, rows_h, pos, x["q"].reshape(-1, w.d), x["k"], x["v"], kc_o, bc_o,
+                        D=x.get("D"), U=x.get("U"))
+    xx = dict(x)
+
+    class QView:
+        def __getitem__(self, key):
+            b, h, i = key
+            return x["q"][b, h]
+    xx["q"] = QView()
+    summ = check_selection_and_output(w, xx, kc_o, bc_o, list(zip(rows_b, rows_h, pos)), ref,
+                                      sel.cpu().numpy().reshape(-1, w.K), None, o.float().cpu().numpy().reshape(-1, w.d),
+                                      label="paged " + name)
+    _say(name, summ)
+
+
+# ------------------------------------------------------------------ exact ties
+# Bitwise-identical chunks (the same keys and the same landmark query) get bitwise-identical
+# k', b' and scores on both sides, so wherever the K-th and (K+1)-th best scores of a row
+# come from two such twins the tie rule alone decides the selection: the lower chunk id wins.
+# The twins carry a strong shared direction that the queries share too, so they outscore
+# every other chunk and the K boundary falls inside the twin group.
+def _to_bf16_bits(a):
+    return torch.from_numpy(np.ascontiguousarray(a, np.float32)).to(torch.bfloat16).view(torch.int16).numpy().view(
+        np.uint16)
+
+
+def _io_to_f32(a, io):
+    return synth.bf16_to_f32(a) if io == synth.BF16 else np.asarray(a, np.float32)
+
+
+def _io_from_f32(a, io):
+    return _to_bf16_bits(a) if io == synth.BF16 else np.ascontiguousarray(a, np.float32)
+
+
+def _twin_inputs(w, seed, twins, kboost=6.0, qboost=4.0):
+    """Inputs of w where every chunk in `twins` is a copy of chunk twins[0] (keys of every KV
+    head and landmark queries of every landmark head), boosted along a unit vector u that
+    every query also carries (decode: every sequence's query)."""
+    x = synth.make_inputs(w, seed)
+    u = synth.unit_vector(w.d, seed + 1)
+    S, t0 = w.S, twins[0]
+    k = _io_to_f32(x["k"], w.io).copy()
+    base = k[:, :, t0 * S:(t0 + 1) * S] + kboost * u
+    lmk = x["lmk"].copy()
+    for t in twins:
+        k[:, :, t * S:(t + 1) * S] = base
+        lmk[:, :, t] = x["lmk"][:, :, t0]
+    x["k"] = _io_from_f32(k, w.io)
+    x["lmk"] = lmk
+    x["q"] = _io_from_f32(_io_to_f32(x["q"], w.io) + qboost * u, w.io)
+    return x
+
+
+def _assert_tie_rows(label, ref, gpu_sel, min_rows):
+    """Rows whose oracle K-th and (K+1)-th scores are exactly equal: the GPU set must be the
+    oracle's, which takes the lower chunk ids (no tolerance, no near-tie allowance)."""
+    gap = np.asarray(ref["gap"])
+    ties = np.flatnonzero(gap == 0.0)
+    assert ties.size >= min_rows, "%s: only %d exact-tie rows (setup)" % (label, ties.size)
+    for t in ties:
+        ns = ref["nsel"][t]
+        o_sel = np.sort(ref["sel_idx"][t][:ns])
+        g = gpu_sel[t]
+        assert np.array_equal(np.sort(g[g >= 0]), o_sel), "%s row %d: tie broken wrongly\n gpu %s\n ora %s" % (
+            label, t, np.sort(g[g >= 0]), o_sel)
+    return int(ties.size)
+
+
+TIE_PREFILL = [
+    ("bf16_d64", synth.Workload("tie_a", B=1, Hq=4, Hkv=2, d=64, N=4096, K=8, planted=False),
+     [1, 2, 3, 5, 8, 9, 12, 15, 16, 20, 21, 37]),
+    ("bf16_d128_qcal", synth.Workload("tie_b", B=1, Hq=4, Hkv=1, d=128, N=3000, K=5, qcal_rank=8, planted=False),
+     [1, 2, 7, 11, 20, 21, 33, 40, 45]),
+    ("f32_d64_K32", synth.Workload("tie_c", B=2, Hq=2, Hkv=2, d=64, N=4500, K=32, io=synth.F32, planted=False),
+     list(range(1, 21)) + [22, 25, 27, 30, 31, 33, 36, 38, 40, 41, 43, 44, 46, 47]),
+]
+
+
+@pytest.mark.parametrize("name,w,twins", TIE_PREFILL, ids=[t[0] for t in TIE_PREFILL])
+def test_prefill_exact_ties_to_lower_chunk(name, w, twins):
+    _say("prefill exact ties", name)
+    x = _twin_inputs(w, SEED + 41, twins)
+    g = gpu_prefill(w, x, fused=True)
+    kc_o, bc_o = oracle_compress(w, x)
+    for t in twins[1:]:  # the twins are exact copies on both sides
+        assert np.array_equal(kc_o[:, :, t], kc_o[:, :, twins[0]]) and np.array_equal(bc_o[:, :, t], bc_o[:, :, twins[0]])
+        assert np.array_equal(g["kc"][:, :, t], g["kc"][:, :, twins[0]])
+    rows = [(b, h, i) for b in range(w.B) for h in range(w.Hq) for i in range(w.N)]
+    ref = oracle_rows(w, x, kc_o, bc_o, rows)
+    rr = np.asarray(rows)
+    gsel = g["sel_idx"][rr[:, 0], rr[:, 1], rr[:, 2]]
+    nt = _assert_tie_rows(name, ref, gsel, min_rows=len(rows) // 4)
+    summ = check_selection_and_output(w, x, kc_o, bc_o, rows, ref, gsel, g["sel_score"][rr[:, 0], rr[:, 1], rr[:, 2]],
+                                      g["o"][rr[:, 0], rr[:, 1], rr[:, 2]], label=name)
+    _say(name, "exact-tie rows", nt, summ)
+
+
+@pytest.mark.parametrize("K", [8, 32])
+def test_prefill_all_chunks_identical(K):
+    """Every chunk identical: every score of a row ties, so every row with more than K
+    candidates must select chunks 0..K-1.  Every candidate passes the selection kernel's
+    threshold, so its per-row candidate lists fill and are compacted again and again."""
+    w = synth.Workload("same_%d" % K, B=1, Hq=2, Hkv=1, d=64, N=16384, K=K, planted=False)
+    _say("all chunks identical, K", K)
+    x = _twin_inputs(w, SEED + 43, list(range(w.C)), kboost=0.0, qboost=0.0)
+    g = gpu_prefill(w, x, fused=True)
+    P = np.minimum(np.arange(w.N) // w.S, w.C)
+    sel = g["sel_idx"][0]
+    expect = np.where(np.arange(K)[None, :] < np.minimum(P, K)[:, None], np.arange(K)[None, :], -1)
+    for h in range(w.Hq):
+        got = np.sort(np.where(sel[h] >= 0, sel[h], 1 << 30), axis=1)
+        got = np.where(got == 1 << 30, -1, got)
+        assert np.array_equal(got, expect), "head %d: rows %s" % (h, np.flatnonzero(np.any(got != expect, axis=1))[:8])
+    kc_o, bc_o = oracle_compress(w, x)
+    rows = [(0, h, i) for h in range(w.Hq) for i in range(0, w.N, 7)]
+    ref = oracle_rows(w, x, kc_o, bc_o, rows)
+    rr = np.asarray(rows)
+    gsel = g["sel_idx"][rr[:, 0], rr[:, 1], rr[:, 2]]
+    _assert_tie_rows("same_%d" % K, ref, gsel, min_rows=len(rows) // 2)
+    summ = check_selection_and_output(w, x, kc_o, bc_o, rows, ref, gsel, g["sel_score"][rr[:, 0], rr[:, 1], rr[:, 2]],
+                                      g["o"][rr[:, 0], rr[:, 1], rr[:, 2]], label="same_%d" % K)
+    _say("same", K, summ)
+
+
+TIE_DECODE = [
+    ("bf16_d128", synth.Workload("tie_dec_a", B=4, Hq=8, Hkv=2, d=128, N=4096, K=8, decode=True,
+                                 seq_lens=[4096, 3001, 1500, 700], planted=False),
+     [1, 2, 4, 5, 7, 8, 9, 10, 12, 15, 18, 44]),
+    ("bf16_d64_qcal_K32", synth.Workload("tie_dec_b", B=2, Hq=4, Hkv=4, d=64, N=8192, K=32, decode=True,
+                                         seq_lens=[8192, 5000], qcal_rank=8, planted=False),
+     list(range(1, 100, 2))),
+]
+
+
+@pytest.mark.parametrize("name,w,twins", TIE_DECODE, ids=[t[0] for t in TIE_DECODE])
+def test_decode_exact_ties_to_lower_chunk(name, w, twins):
+    _say("decode exact ties", name)
+    x = _twin_inputs(w, SEED + 45, twins)
+    g = gpu_decode(w, x)
+    kc_o, bc_o = oracle_compress(w, x)
+    rows_b = [b for b in range(w.B) for h in range(w.Hq)]
+    rows_h = [h for b in range(w.B) for h in range(w.Hq)]
+    pos = [int(x["seq_lens"][b]) - 1 for b in rows_b]
+    ref = oracle.attend(shape_of(w), rows_b, rows_h, pos, x["q"].reshape(-1, w.d), x["k"], x["v"], kc_o, bc_o,
+                        D=x.get("D"), U=x.get("U"))
+    gsel = g["sel_idx"].reshape(-1, w.K)
+    nt = _assert_tie_rows(name, ref, gsel, min_rows=len(rows_b) // 2)
+    xx = dict(x)
+
+    class QView:
+        def __getitem__(self, key):
+            b, h, i = key
+            return x["q"][b, h]
+    xx["q"] = QView()
+    summ = check_selection_and_output(w, xx, kc_o, bc_o, list(zip(rows_b, rows_h, pos)), ref, gsel, None,
+                                      g["o"].reshape(-1, w.d), label=name)
+    _say(name, "exact-tie rows", nt, summ)
