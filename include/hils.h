@@ -177,6 +177,22 @@ int hils_attn_decode_timed(const hils_dims_t* dims, const void* q, const void* k
                            void* stream, float* stage_ms);
 
 /*
+ * hils_attn_decode for callers that cannot allocate memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the same decode step
+ * and results, with no workspace argument.  Its scratch memory is a device array inside
+ * the library, HILS_NOALLOC_SCRATCH_BYTES on each GPU it runs on, held until the process
+ * ends; its address is looked up once per device on the first call.  The call allocates
+ * nothing.  Dims whose decode workspace (hils_workspace_bytes(dims, HILS_OP_DECODE))
+ * exceeds HILS_NOALLOC_SCRATCH_BYTES return HILS_E_UNSUPPORTED.  Every call on one GPU
+ * uses that GPU's one array: calls that overlap on one GPU (other streams, other host
+ * threads) race and give wrong results; order them on one stream.
+ */
+#define HILS_NOALLOC_SCRATCH_BYTES (16u << 20)
+int hils_attn_decode_noalloc(const hils_dims_t* dims, const void* q, const void* k_cache, const void* v_cache,
+                             const int32_t* seq_lens, const float* kc, const float* bc, const void* qcal_D,
+                             const void* qcal_U, int32_t* sel_idx_out, void* o, void* stream);
+
+/*
  * Chunk-paged KV cache (the pages' chunks are the natural page: ai-papers.net
  * "How HiLS Attention works"; aitrends.kr "Technical details" on decode cost).
  * A page holds one S-token chunk of every KV head: k_pages / v_pages

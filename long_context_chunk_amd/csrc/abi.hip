@@ -3,6 +3,7 @@
 // is valid.
 #include <stdarg.h>
 #include <algorithm>
+#include <mutex>
 #include <stdio.h>
 #include <string.h>
 
@@ -259,6 +260,32 @@ int run_decode(const hils_dims_t* dims, const void* q, const void* k_cache, cons
   return HILS_OK;
 }
 
+// Scratch memory of hils_attn_decode_noalloc: a file-scope device array, one copy per GPU,
+// held until the process ends.  Host code never uses the array's name as an address: its
+// device address is looked up once per device (with that device current) and cached.
+static __device__ __align__(256) unsigned char scratch[HILS_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// The current device's address of `scratch` (looked up on the first call on that device).
+int scratch_address(void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hils_attn_decode_noalloc: hipGetDevice");
+  if (dev < 0 || dev >= kMaxDevices) return fail(HILS_E_UNSUPPORTED, "device %d beyond the %d supported", dev, kMaxDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return hip_fail(e, "hils_attn_decode_noalloc: hipGetSymbolAddress");
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return HILS_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -294,6 +321,25 @@ int hils_attn_decode_timed(const hils_dims_t* dims, const void* q, const void* k
   if (!stage_ms) return fail(HILS_E_INVAL, "stage_ms must be non-NULL");
   return run_decode(dims, q, k_cache, v_cache, seq_lens, kc, bc, qcal_D, qcal_U, sel_idx_out, o, ws, ws_bytes, stream,
                     stage_ms);
+}
+
+int hils_attn_decode_noalloc(const hils_dims_t* dims, const void* q, const void* k_cache, const void* v_cache,
+                             const int32_t* seq_lens, const float* kc, const float* bc, const void* qcal_D,
+                             const void* qcal_U, int32_t* sel_idx_out, void* o, void* stream) {
+  hils::Geom g;
+  int rc = check_dims(dims, g);
+  if (rc) return rc;
+  if (g.C() > 16384) return fail(HILS_E_UNSUPPORTED, "decode needs N/S <= 16384 (N=%d)", g.N);
+  const size_t need = hils::decode_workspace_bytes(g);
+  if (need > (size_t)HILS_NOALLOC_SCRATCH_BYTES)
+    return fail(HILS_E_UNSUPPORTED, "hils_attn_decode_noalloc: these dims need %zu bytes of scratch, above its %zu",
+                need, (size_t)HILS_NOALLOC_SCRATCH_BYTES);
+  if (!q || !k_cache || !v_cache || !seq_lens || !o)
+    return fail(HILS_E_INVAL, "q, k_cache, v_cache, seq_lens and o must be non-NULL");
+  void* ws = nullptr;
+  if ((rc = scratch_address(&ws))) return rc;
+  return run_decode(dims, q, k_cache, v_cache, seq_lens, kc, bc, qcal_D, qcal_U, sel_idx_out, o, ws,
+                    (size_t)HILS_NOALLOC_SCRATCH_BYTES, stream, nullptr);
 }
 
 int hils_landmark_compress_paged(const hils_dims_t* dims, const void* k_pages, const int32_t* block_table,

@@ -21,7 +21,9 @@ OK, E_INVAL, E_UNSUPPORTED, E_WORKSPACE, E_HIP = 0, -1, -2, -3, -4
 
 SYMBOLS = ("hils_workspace_bytes", "hils_landmark_compress", "hils_chunk_score_topk", "hils_attn_prefill",
            "hils_attn_prefill_timed", "hils_attn_decode", "hils_attn_decode_timed", "hils_landmark_compress_paged",
-           "hils_attn_decode_paged", "hils_dense_attention", "hils_attn_prefill_backward", "hils_last_error")
+           "hils_attn_decode_paged", "hils_dense_attention", "hils_attn_prefill_backward", "hils_attn_decode_noalloc",
+           "hils_last_error")
+NOALLOC_SCRATCH_BYTES = 16 << 20   # HILS_NOALLOC_SCRATCH_BYTES of include/hils.h
 STAGES = ("compress", "score_threshold", "score_select", "bucket", "chunk_attend", "own_attend", "fuse")
 DECODE_STAGES = ("scan", "merge", "attend_fuse")
 
@@ -63,12 +65,13 @@ def load():
         lib.hils_attn_decode_timed.argtypes = [dp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp,
                                                ctypes.POINTER(ctypes.c_float)]
         lib.hils_dense_attention.argtypes = [dp, vp, vp, vp, vp, vp]
+        lib.hils_attn_decode_noalloc.argtypes = [dp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
         lib.hils_landmark_compress_paged.argtypes = [dp, vp, vp, i32, i32, vp, i32, i32, vp, vp, vp]
         lib.hils_attn_decode_paged.argtypes = [dp, vp, vp, vp, vp, i32, i32, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
         lib.hils_attn_prefill_backward.argtypes = [dp] + [vp] * 18 + [sz, vp]
         for f in ("hils_landmark_compress", "hils_chunk_score_topk", "hils_attn_prefill", "hils_attn_prefill_timed",
                   "hils_attn_decode", "hils_attn_decode_timed", "hils_dense_attention", "hils_landmark_compress_paged",
-                  "hils_attn_decode_paged", "hils_attn_prefill_backward"):
+                  "hils_attn_decode_paged", "hils_attn_prefill_backward", "hils_attn_decode_noalloc"):
             getattr(lib, f).restype = ctypes.c_int
         lib.hils_last_error.argtypes = []
         lib.hils_last_error.restype = ctypes.c_char_p
@@ -237,6 +240,26 @@ def attn_decode(dm: Dims, q, k_cache, v_cache, seq_lens, kc, bc, o, ws, qcal_D=N
         _check(load().hils_attn_decode_timed(*args, ms))
         return dict(zip(DECODE_STAGES, [float(x) for x in ms]))
     _check(load().hils_attn_decode(*args))
+
+
+def attn_decode_noalloc(dm: Dims, q, k_cache, v_cache, seq_lens, kc, bc, o, qcal_D=None, qcal_U=None, sel_idx=None):
+    """hils_attn_decode_noalloc: hils_attn_decode with the library's own scratch (no workspace)."""
+    C = dm.N // dm.S
+    dt = torch.float32 if dm.io == F32 else torch.bfloat16
+    _req(q, "q", (dm.B, dm.Hq, dm.d), dt)
+    _req(k_cache, "k_cache", (dm.B, dm.Hkv, dm.N, dm.d), dt)
+    _req(v_cache, "v_cache", (dm.B, dm.Hkv, dm.N, dm.d), dt)
+    _req(seq_lens, "seq_lens", (dm.B,), torch.int32)
+    _req(kc, "kc", (dm.B, dm.Hlmk, C, dm.d), torch.float32)
+    _req(bc, "bc", (dm.B, dm.Hlmk, C), torch.float32)
+    _req(o, "o", (dm.B, dm.Hq, dm.d), dt)
+    if dm.qcal_rank > 0:
+        _req(qcal_D, "qcal_D", (dm.Hq, dm.qcal_rank, dm.d), dt)
+        _req(qcal_U, "qcal_U", (dm.Hq, dm.d, dm.qcal_rank), dt)
+    if sel_idx is not None:
+        _req(sel_idx, "sel_idx", (dm.B, dm.Hq, dm.K), torch.int32)
+    _check(load().hils_attn_decode_noalloc(ctypes.byref(dm), _p(q), _p(k_cache), _p(v_cache), _p(seq_lens), _p(kc),
+                                           _p(bc), _p(qcal_D), _p(qcal_U), _p(sel_idx), _p(o), _stream()))
 
 
 def dense_attention(dm: Dims, q, k, v, o):

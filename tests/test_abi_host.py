@@ -188,3 +188,22 @@ def test_backward_validation_and_workspace():
     f32 = hils.dims(1, 8, 2, 64, 1024, 8, io=hils.F32)
     assert call(f32, ws_bytes=1 << 40) == hils.E_UNSUPPORTED
     assert b"bf16" in lib.hils_last_error()
+
+
+def test_decode_noalloc_rejects_dims_beyond_its_scratch():
+    """hils_attn_decode_noalloc checks its fixed scratch size on the host, before any HIP call."""
+    lib = hils.load()
+    fake = ctypes.c_void_p(0x1000)  # never dereferenced: validation fails first
+    big = hils.dims(64, 64, 8, 128, 1 << 20, 32)
+    assert hils.workspace_bytes(big, hils.OP_DECODE) > hils.NOALLOC_SCRATCH_BYTES
+    rc = lib.hils_attn_decode_noalloc(ctypes.byref(big), fake, fake, fake, fake, fake, fake, None, None, None, fake,
+                                      None)
+    assert rc == hils.E_UNSUPPORTED, (rc, lib.hils_last_error())
+    assert b"scratch" in lib.hils_last_error()
+    ok = hils.dims(8, 32, 8, 128, 524288, 32)   # the 512K decode workload fits
+    assert hils.workspace_bytes(ok, hils.OP_DECODE) <= hils.NOALLOC_SCRATCH_BYTES
+    rc = lib.hils_attn_decode_noalloc(ctypes.byref(ok), None, fake, fake, fake, fake, fake, None, None, None, fake, None)
+    assert rc == hils.E_INVAL
+    bad = hils.dims(8, 32, 8, 96, 4096, 32)
+    rc = lib.hils_attn_decode_noalloc(ctypes.byref(bad), fake, fake, fake, fake, fake, fake, None, None, None, fake, None)
+    assert rc == hils.E_UNSUPPORTED
