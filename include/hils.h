@@ -48,7 +48,10 @@
  *     Query head h uses KV head h / (Hq / Hkv) and landmark head h / (Hq / Hlmk).
  *   - Selection lists are in rank order: best score first, equal scores by
  *     ascending chunk id.  Rows with fewer than K past chunks select all of them
- *     and pad with id -1 and score -inf.
+ *     and pad with id -1 and score -inf.  (The fusion does not depend on the order;
+ *     rank order is what the selection produces and keeps the ranking, so a caller
+ *     can take the best k <= K of a list without re-sorting.  Sorting a list's valid
+ *     ids gives the ascending form.)
  *   - q, k, v, o, lmk_q, qcal_D, qcal_U all have the element type `io`;
  *     kc, bc and sel_score are always fp32.
  */
@@ -79,7 +82,9 @@ typedef struct {
   int32_t B;         /* batch (sequences)                                              */
   int32_t Hq;        /* query heads                                                    */
   int32_t Hkv;       /* KV heads; Hq % Hkv == 0                                        */
-  int32_t Hlmk;      /* landmark heads; the library requires Hlmk == Hq                */
+  int32_t Hlmk;      /* landmark heads, Hq % Hlmk == 0 and Hlmk % Hkv == 0: Hq (one per */
+                     /* query head) or Hkv (one per KV group, shared by its query      */
+                     /* heads); the backward pass needs Hlmk == Hq                      */
   int32_t d;         /* head dimension: 64 or 128                                      */
   int32_t S;         /* chunk size: 64                                                 */
   int32_t K;         /* top-K chunks per query: 1 <= K <= 32                            */
@@ -107,15 +112,21 @@ int hils_landmark_compress(const hils_dims_t* dims, const void* k, const void* l
                            int32_t c_end, float* kc, float* bc, void* stream);
 
 /*
- * Chunk scoring and top-K, step (2), for all N prefill queries:
- * s_ic = q^_i . kc[c] / sqrt(d) + bc[c] for c < floor(i/S), q^ = q + U_h (D_h q)
- * when qcal_rank > 0 (qcal_D/qcal_U may be NULL only if qcal_rank == 0).
- * Writes sel_idx and sel_score [B,Hq,N,K] (rank order, padded).  Needs a
- * workspace of hils_workspace_bytes(dims, HILS_OP_SCORE_TOPK) bytes.
+ * Chunk scoring and top-K, step (2), for a block of Nq queries per (batch, query
+ * head): q [B,Hq,Nq,d]; query i of batch b sits at position p = q_pos0[b] + i
+ * (q_pos0: [B] int32 on the device, 0 <= q_pos0[b] < 2^30; NULL: every block starts
+ * at position 0, as in a prefill of the whole sequence).  It scores the complete
+ * chunks c < floor(p/S) - (W/S - 1) of the context held in kc/bc
+ * ([B,Hlmk,floor(N/S),d] / [B,Hlmk,floor(N/S)], N = dims.N) with
+ * s_ic = q^_i . kc[c] / sqrt(d) + bc[c], q^ = q + U_h (D_h q) when qcal_rank > 0
+ * (qcal_D/qcal_U may be NULL only if qcal_rank == 0), and keeps the K best.
+ * Writes sel_idx and sel_score [B,Hq,Nq,K] (rank order, padded).  0 <= Nq <= N;
+ * Nq == 0 does nothing (the arrays may then be NULL).  Needs a workspace of
+ * hils_workspace_bytes(dims, HILS_OP_SCORE_TOPK) bytes (sized for Nq = N).
  */
-int hils_chunk_score_topk(const hils_dims_t* dims, const void* q, const void* qcal_D, const void* qcal_U,
-                          const float* kc, const float* bc, int32_t* sel_idx, float* sel_score, void* ws,
-                          size_t ws_bytes, void* stream);
+int hils_chunk_score_topk(const hils_dims_t* dims, int32_t Nq, const void* q, const int32_t* q_pos0,
+                          const void* qcal_D, const void* qcal_U, const float* kc, const float* bc, int32_t* sel_idx,
+                          float* sel_score, void* ws, size_t ws_bytes, void* stream);
 
 /*
  * The whole prefill forward pass, steps (1)-(4), for all N queries of every

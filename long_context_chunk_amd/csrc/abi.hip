@@ -43,7 +43,6 @@ int check_dims(const hils_dims_t* dims, hils::Geom& g) {
   if (s.qcal_rank < 0) return fail(HILS_E_INVAL, "qcal_rank must be >= 0 (%d)", s.qcal_rank);
   if (s.d < 1 || s.S < 1) return fail(HILS_E_INVAL, "d and S must be >= 1 (d=%d S=%d)", s.d, s.S);
   if (s.io != HILS_F32 && s.io != HILS_BF16) return fail(HILS_E_UNSUPPORTED, "io dtype %d not supported", s.io);
-  if (s.Hlmk != s.Hq) return fail(HILS_E_UNSUPPORTED, "the library needs Hlmk == Hq (got Hlmk=%d Hq=%d)", s.Hlmk, s.Hq);
   if (s.d != 64 && s.d != 128) return fail(HILS_E_UNSUPPORTED, "head dim %d not supported (64 or 128)", s.d);
   if (s.S != 64) return fail(HILS_E_UNSUPPORTED, "chunk size %d not supported (64)", s.S);
   if (s.K > 32) return fail(HILS_E_UNSUPPORTED, "K=%d not supported (K <= 32)", s.K);
@@ -153,20 +152,25 @@ int hils_landmark_compress(const hils_dims_t* dims, const void* k, const void* l
   return HILS_OK;
 }
 
-int hils_chunk_score_topk(const hils_dims_t* dims, const void* q, const void* qcal_D, const void* qcal_U,
-                          const float* kc, const float* bc, int32_t* sel_idx, float* sel_score, void* ws,
-                          size_t ws_bytes, void* stream) {
+int hils_chunk_score_topk(const hils_dims_t* dims, int32_t Nq, const void* q, const int32_t* q_pos0,
+                          const void* qcal_D, const void* qcal_U, const float* kc, const float* bc, int32_t* sel_idx,
+                          float* sel_score, void* ws, size_t ws_bytes, void* stream) {
   hils::Geom g;
   int rc = check_dims(dims, g);
   if (rc) return rc;
   if (g.C() > 16384) return fail(HILS_E_UNSUPPORTED, "scoring needs N/S <= 16384 (N=%d)", g.N);
+  if (Nq < 0 || Nq > g.N) return fail(HILS_E_INVAL, "need 0 <= Nq <= N (Nq=%d N=%d)", Nq, g.N);
+  if (Nq == 0) {  // no query: nothing to do, the arrays may be empty (NULL)
+    g_err[0] = 0;
+    return HILS_OK;
+  }
   if (!q || !sel_idx || !sel_score) return fail(HILS_E_INVAL, "q, sel_idx and sel_score must be non-NULL");
   if (g.C() > 0 && (!kc || !bc)) return fail(HILS_E_INVAL, "kc and bc must be non-NULL");
   if (g.r > 0 && (!qcal_D || !qcal_U)) return fail(HILS_E_INVAL, "qcal_rank > 0 needs qcal_D and qcal_U");
   const size_t need = hils::score_workspace_bytes(g);
   if (!ws && need > 0) return fail(HILS_E_WORKSPACE, "workspace is NULL (%zu bytes needed)", need);
   if (ws_bytes < need) return fail(HILS_E_WORKSPACE, "workspace too small: %zu < %zu", ws_bytes, need);
-  hipError_t e = hils::launch_score_topk(g, q, qcal_D, qcal_U, kc, bc, sel_idx, sel_score, ws, ws_bytes,
+  hipError_t e = hils::launch_score_topk(g, Nq, q_pos0, q, qcal_D, qcal_U, kc, bc, sel_idx, sel_score, ws, ws_bytes,
                                          (hipStream_t)stream);
   if (e != hipSuccess) return hip_fail(e, "hils_chunk_score_topk");
   g_err[0] = 0;
@@ -209,7 +213,8 @@ int run_prefill(const hils_dims_t* dims, const void* q, const void* k, const voi
   }
   if (e == hipSuccess && stage_ms) e = hipEventRecord(ev[1], st);
   if (e == hipSuccess)
-    e = hils::launch_score_topk(g, q, qcal_D, qcal_U, kcp, bcp, sel, scr, base + w.score, w.attend - w.score, st,
+    e = hils::launch_score_topk(g, g.N, nullptr, q, qcal_D, qcal_U, kcp, bcp, sel, scr, base + w.score,
+                                w.attend - w.score, st,
                                 stage_ms ? ev + 2 : nullptr);
   if (e == hipSuccess)
     e = hils::launch_prefill_attend(g, q, k, v, sel, scr, o, base + w.attend, w.total - w.attend, st,
@@ -400,6 +405,9 @@ int hils_attn_prefill_backward(const hils_dims_t* dims, const void* q, const voi
   if (rc) return rc;
   if ((rc = check_prefill(g))) return rc;
   if (g.io != HILS_BF16) return fail(HILS_E_UNSUPPORTED, "the backward pass needs bf16 I/O");
+  if (g.Hl != g.Hq)
+    return fail(HILS_E_UNSUPPORTED, "the backward pass needs one landmark head per query head (Hlmk=%d Hq=%d)", g.Hl,
+                g.Hq);
   if (!q || !k || !v || !o || !dO || !dq || !dk || !dv || !sel_idx || !sel_score)
     return fail(HILS_E_INVAL, "q, k, v, o, dO, dq, dk, dv, sel_idx and sel_score must be non-NULL");
   if (g.C() > 0 && (!lmk_q || !kc || !dlmk))

@@ -133,8 +133,8 @@ template <typename IO, int D>
 __global__ void __launch_bounds__(256) decode_scan(const IO* __restrict__ q, const IO* __restrict__ Dw,
                                                    const IO* __restrict__ Uw, const float* __restrict__ kc,
                                                    const float* __restrict__ bc, const int32_t* __restrict__ seq_lens,
-                                                   uint64_t* __restrict__ cand, int Hq, int C, int r, int nsplit,
-                                                   int nw) {
+                                                   uint64_t* __restrict__ cand, int Hq, int Hl, int C, int r,
+                                                   int nsplit, int nw) {
   __shared__ __align__(16) float qs[D];
   __shared__ float ts[32];
   __shared__ uint64_t keys[DS_CHUNKS];
@@ -157,8 +157,9 @@ __global__ void __launch_bounds__(256) decode_scan(const IO* __restrict__ q, con
 #pragma unroll
   for (int j = 0; j < 4; ++j) qv[j] = *reinterpret_cast<const f32x4_t*>(&qs[4 * (sub + TPC * j)]);
   const float tau = 1.0f / sqrtf((float)D);
-  const float* kb = kc + (int64_t)bh * C * D;
-  const float* bb = bc + (int64_t)bh * C;
+  const int64_t lrow = (int64_t)b * Hl + h / (Hq / Hl);   // the query head's landmark head
+  const float* kb = kc + lrow * C * D;
+  const float* bb = bc + lrow * C;
   // the landmark keys are streamed once (non-temporal loads); chunks beyond c_end load
   // chunk c_end - 1 (in bounds) and are dropped; two register buffers alternate so that
   // the next STEP chunks are in flight while the current ones are scored
@@ -433,7 +434,7 @@ static hipError_t launch_decode_t(const Geom& g, const void* q, const void* kcac
   if (nsplit > DS_MAX_SPLIT) return hipErrorInvalidValue;  // N/S > 16384, rejected by the ABI first
   if (ev) (void)hipEventRecord(ev[0], st);
   hipLaunchKernelGGL((decode_scan<IO, D>), dim3(BH * nsplit), dim3(256), 0, st, (const IO*)q, (const IO*)Dw,
-                     (const IO*)Uw, kc, bc, seq_lens, cand, g.Hq, C, g.r, nsplit, g.nw);
+                     (const IO*)Uw, kc, bc, seq_lens, cand, g.Hq, g.Hl, C, g.r, nsplit, g.nw);
   if (ev) (void)hipEventRecord(ev[1], st);
   hipLaunchKernelGGL(decode_merge, dim3(BH), dim3(256), 0, st, (const uint64_t*)cand, seq_lens, sel_i, sel_s, nsel,
                      sel_user, g.Hq, C, g.K, nsplit, g.nw);

@@ -56,12 +56,13 @@ struct BwdArgs {
 size_t backward_workspace_bytes(const Geom& g);
 hipError_t launch_backward(const Geom& g, const BwdArgs& a, void* ws, size_t ws_bytes, hipStream_t st);
 
-// Chunk scores and per-row top-K for all N queries of every (b, h).
+// Chunk scores and per-row top-K for a block of Nq <= N queries of every (b, h), query i of
+// batch b at position pos0[b] + i (pos0 nullable: 0); q, sel_idx, sel_score hold Nq rows per (b, h).
 size_t score_workspace_bytes(const Geom& g);
 // ev (nullable): two events recorded after the threshold pass and after the selection pass.
-hipError_t launch_score_topk(const Geom& g, const void* q, const void* D, const void* U, const float* kc,
-                             const float* bc, int32_t* sel_idx, float* sel_score, void* ws, size_t ws_bytes,
-                             hipStream_t st, hipEvent_t* ev = nullptr);
+hipError_t launch_score_topk(const Geom& g, int Nq, const int32_t* pos0, const void* q, const void* D, const void* U,
+                             const float* kc, const float* bc, int32_t* sel_idx, float* sel_score, void* ws,
+                             size_t ws_bytes, hipStream_t st, hipEvent_t* ev = nullptr);
 
 // Intra-chunk attention and fusion for prefill, given the selection.
 size_t attend_workspace_bytes(const Geom& g);

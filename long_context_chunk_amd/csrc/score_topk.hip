@@ -1,7 +1,9 @@
-// Chunk scoring and top-K for prefill queries.
+// Chunk scoring and top-K for a block of queries.
 //
-//   s_ic = q^_i . k'_c / sqrt(d) + b'_c   for every candidate chunk c < floor(i/S) - (nw - 1)
+//   s_ic = q^_i . k'_c / sqrt(d) + b'_c   for every candidate chunk c < floor(p_i/S) - (nw - 1)
 //                                        (the complete chunks before the local window of nw chunks)
+// where query i of batch b sits at position p_i = pos0[b] + i (prefill: pos0 = 0, the
+// block is the whole sequence) and k' comes from its landmark head h / (Hq / Hl).
 //   q^_i = q_i + U_h (D_h q_i)             (Q-Cal; q^ = q without it)
 // keep the K best (ties -> lower chunk id).  (aitrends.kr article,
 // "Methodology": the score formula, the calculation flow and the Q-Cal module.)
@@ -335,8 +337,9 @@ constexpr int TH_EXT = 16;                  // elements of the extension k-step
 template <typename IO, int D, bool QCAL>
 __global__ void __launch_bounds__(256, 2) score_threshold(const IO* __restrict__ q, const IO* __restrict__ Dw,
                                                           const IO* __restrict__ Uw, const uint16_t* __restrict__ t1,
-                                                          float* __restrict__ theta, int H, int N, int C, int K, int r,
-                                                          int NB, int items, int nw) {
+                                                          float* __restrict__ theta, const int32_t* __restrict__ pos0,
+                                                          int H, int Hl, int N, int C, int K, int r, int NB, int items,
+                                                          int nw) {
   constexpr int NKS = D / 16;
   constexpr int DE = D + TH_EXT;      // bf16 elements of a chunk row
   constexpr int LDT = DE + 8;         // LDS row stride (16-byte pad: conflict-free 16-byte reads)
@@ -351,15 +354,16 @@ __global__ void __launch_bounds__(256, 2) score_threshold(const IO* __restrict__
   if (item >= items) return;
   const int bh = item / NB;
   const int rb = NB - 1 - (item % NB);  // heavier (later) row blocks first
-  const int hh = bh % H;
+  const int hh = bh % H, bb = bh / H;
+  const int p0 = pos0 ? pos0[bb] : 0;   // position of the block's query 0 (N = queries here)
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int n = lane & 31, hf = lane >> 5;
   const int r0 = rb * ST_ROWS;
   const int row = r0 + 32 * w + n;
   const bool row_ok = row < N;
   const int last = min(r0 + ST_ROWS, N) - 1;
-  const int Pmax = candidate_chunks(last, C, nw);
-  const int Pmin = candidate_chunks(r0, C, nw);
+  const int Pmax = candidate_chunks(p0 + last, C, nw);
+  const int Pmin = candidate_chunks(p0 + r0, C, nw);
   const float tau = 1.0f / sqrtf((float)D);
   const int64_t qrow = ((int64_t)bh * N + (row_ok ? row : 0)) * D;
 
@@ -389,7 +393,7 @@ __global__ void __launch_bounds__(256, 2) score_threshold(const IO* __restrict__
     qa[NKS] = pack8(t);
   }
 
-  const uint16_t* src = t1 + (int64_t)bh * C * DE;
+  const uint16_t* src = t1 + ((int64_t)bb * Hl + hh / (H / Hl)) * C * DE;   // the landmark head's rows
   u32x4_t pf[PL];
   // chunks beyond Pmax load chunk Pmax-1 (finite; masked out below); the last partial
   // group of segments repeats the final segment: no divergent loads
@@ -453,7 +457,7 @@ __global__ void __launch_bounds__(256, 2) score_threshold(const IO* __restrict__
         float v = acc[tt][rr];
         if constexpr (MASKED) {
           const int rw = r0 + 32 * w + acc_row(rr, hf);
-          const int prow = rw < N ? candidate_chunks(rw, C, nw) : 0;
+          const int prow = rw < N ? candidate_chunks(p0 + rw, C, nw) : 0;
           v = c >= prow ? -INFINITY : v;
         }
         m2[rr] = __builtin_amdgcn_fmed3f(m1[rr], m2[rr], v);
@@ -499,8 +503,9 @@ __global__ void __launch_bounds__(256, NQ * NK > 4 ? 1 : 2) score_topk_kernel(co
                                                              const uint16_t* __restrict__ p2,
                                                              const float* __restrict__ theta,
                                                              int32_t* __restrict__ sel_idx,
-                                                             float* __restrict__ sel_score, int H, int N, int C, int K,
-                                                             int r, int NB, int items, int nw) {
+                                                             float* __restrict__ sel_score,
+                                                             const int32_t* __restrict__ pos0, int H, int Hl, int N,
+                                                             int C, int K, int r, int NB, int items, int nw) {
   constexpr int NKS = D / 16;
   constexpr int DE2 = NK * D + P2_EXT;  // elements of a chunk row: plane 0, extension, planes 1..
   constexpr int LDR = DE2 + 8;          // LDS row stride (16-byte pad)
@@ -517,16 +522,17 @@ __global__ void __launch_bounds__(256, NQ * NK > 4 ? 1 : 2) score_topk_kernel(co
   if (item >= items) return;
   const int bh = item / NB;
   const int rb = NB - 1 - (item % NB);  // heavier (later) row blocks first
-  const int hh = bh % H;
+  const int hh = bh % H, bb = bh / H;
+  const int p0 = pos0 ? pos0[bb] : 0;   // position of the block's query 0 (N = queries here)
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int n = lane & 31, hf = lane >> 5;
   const int r0 = rb * ST_ROWS;
   const int row = r0 + 32 * w + n;       // this lane's query row
   const bool row_ok = row < N;
   const int last = min(r0 + ST_ROWS, N) - 1;
-  const int Pmax = candidate_chunks(last, C, nw);
-  const int Pmin = candidate_chunks(r0, C, nw);
-  const int prow = row_ok ? candidate_chunks(row, C, nw) : 0;   // candidate chunks of this lane's row
+  const int Pmax = candidate_chunks(p0 + last, C, nw);
+  const int Pmin = candidate_chunks(p0 + r0, C, nw);
+  const int prow = row_ok ? candidate_chunks(p0 + row, C, nw) : 0;   // candidate chunks of this lane's row
   const int64_t qrow = ((int64_t)bh * N + (row_ok ? row : 0)) * D;
 
   // ---- the query's B operands: q^ split into NQ bf16 terms, plus the constant extension
@@ -581,7 +587,7 @@ __global__ void __launch_bounds__(256, NQ * NK > 4 ? 1 : 2) score_topk_kernel(co
     lk = x;
   };
 
-  const uint16_t* src = p2 + (int64_t)bh * C * DE2;
+  const uint16_t* src = p2 + ((int64_t)bb * Hl + hh / (H / Hl)) * C * DE2;   // the landmark head's rows
   u32x4_t pf[PL];
   // chunks beyond Pmax load chunk Pmax-1 (finite; masked out below) and the last
   // partial group of segments repeats the final segment: no divergent loads
@@ -855,7 +861,7 @@ struct ScoreWs {
   size_t planes, t1, theta, total;
 };
 static ScoreWs score_ws(const Geom& g) {
-  const size_t rows = (size_t)g.B * g.Hq * g.C();
+  const size_t rows = (size_t)g.B * g.Hl * g.C();   // k' rows: one per (b, landmark head, chunk)
   ScoreWs w;
   size_t off = 0;
   w.planes = off;
@@ -863,7 +869,7 @@ static ScoreWs score_ws(const Geom& g) {
   w.t1 = off;
   off += al3(rows * (g.d + TH_EXT) * 2);
   w.theta = off;
-  off += al3((size_t)g.B * g.Hq * g.N * 4);
+  off += al3((size_t)g.B * g.Hq * g.N * 4);   // one per query, for up to N queries
   w.total = off;
   return w;
 }
@@ -871,35 +877,39 @@ static ScoreWs score_ws(const Geom& g) {
 size_t score_workspace_bytes(const Geom& g) { return score_ws(g).total; }
 
 template <typename IO, int D, int NQ, int NK, bool QCAL>
-static void launch_st(const Geom& g, const void* q, const void* Dw, const void* Uw, const uint16_t* planes,
-                      const uint16_t* t1, float* theta, const float* bc, int32_t* si, float* ss, hipStream_t st,
+static void launch_st(const Geom& g, int Nq, const int32_t* pos0, const void* q, const void* Dw, const void* Uw,
+                      const uint16_t* planes, const uint16_t* t1, float* theta, int32_t* si, float* ss, hipStream_t st,
                       hipEvent_t* ev) {
-  const int NB = (g.N + ST_ROWS - 1) / ST_ROWS;
+  const int NB = (Nq + ST_ROWS - 1) / ST_ROWS;
   const int items = g.B * g.Hq * NB;
   const int grid = ((items + 7) / 8) * 8;
-  hipLaunchKernelGGL((score_threshold<IO, D, QCAL>), dim3(grid), dim3(256), 0, st, (const IO*)q, (const IO*)Dw,
-                     (const IO*)Uw, t1, theta, g.Hq, g.N, g.C(), g.K, g.r, NB, items, g.nw);
+  if (items > 0) {
+    hipLaunchKernelGGL((score_threshold<IO, D, QCAL>), dim3(grid), dim3(256), 0, st, (const IO*)q, (const IO*)Dw,
+                       (const IO*)Uw, t1, theta, pos0, g.Hq, g.Hl, Nq, g.C(), g.K, g.r, NB, items, g.nw);
+  }
   if (ev) hipEventRecord(ev[0], st);
-  hipLaunchKernelGGL((score_topk_kernel<IO, D, NQ, NK, QCAL>), dim3(grid), dim3(256), 0, st, (const IO*)q,
-                     (const IO*)Dw, (const IO*)Uw, planes, (const float*)theta, si, ss, g.Hq, g.N, g.C(), g.K, g.r,
-                     NB, items, g.nw);
+  if (items > 0) {
+    hipLaunchKernelGGL((score_topk_kernel<IO, D, NQ, NK, QCAL>), dim3(grid), dim3(256), 0, st, (const IO*)q,
+                       (const IO*)Dw, (const IO*)Uw, planes, (const float*)theta, si, ss, pos0, g.Hq, g.Hl, Nq, g.C(),
+                       g.K, g.r, NB, items, g.nw);
+  }
 }
 
 template <typename IO, int D>
-static void launch_st_d(const Geom& g, const void* q, const void* Dw, const void* Uw, const uint16_t* planes,
-                        const uint16_t* t1, float* theta, const float* bc, int32_t* si, float* ss, hipStream_t st,
-                        hipEvent_t* ev) {
+static void launch_st_d(const Geom& g, int Nq, const int32_t* pos0, const void* q, const void* Dw, const void* Uw,
+                        const uint16_t* planes, const uint16_t* t1, float* theta, int32_t* si, float* ss,
+                        hipStream_t st, hipEvent_t* ev) {
   constexpr bool F32 = io_traits<IO>::terms == 3;
   if (g.r > 0)
-    launch_st<IO, D, F32 ? 3 : 2, F32 ? 3 : 2, true>(g, q, Dw, Uw, planes, t1, theta, bc, si, ss, st, ev);
+    launch_st<IO, D, F32 ? 3 : 2, F32 ? 3 : 2, true>(g, Nq, pos0, q, Dw, Uw, planes, t1, theta, si, ss, st, ev);
   else
-    launch_st<IO, D, F32 ? 3 : 1, F32 ? 3 : 2, false>(g, q, Dw, Uw, planes, t1, theta, bc, si, ss, st, ev);
+    launch_st<IO, D, F32 ? 3 : 1, F32 ? 3 : 2, false>(g, Nq, pos0, q, Dw, Uw, planes, t1, theta, si, ss, st, ev);
 }
 
 template <int D>
 static void launch_prep(const Geom& g, const float* kc, const float* bc, uint16_t* planes, uint16_t* t1,
                         hipStream_t st) {
-  const int64_t rows = (int64_t)g.B * g.Hq * g.C();
+  const int64_t rows = (int64_t)g.B * g.Hl * g.C();
   const int64_t rpb = 256 / (D / 8);
   const unsigned gs = (unsigned)std::min<int64_t>((rows + rpb - 1) / rpb, 16384);
   if (nk_of(g) == 3)
@@ -908,10 +918,10 @@ static void launch_prep(const Geom& g, const float* kc, const float* bc, uint16_
     hipLaunchKernelGGL((prep_kprime<D, 2>), dim3(gs), dim3(256), 0, st, kc, bc, planes, t1, rows);
 }
 
-hipError_t launch_score_topk(const Geom& g, const void* q, const void* Dw, const void* Uw, const float* kc,
-                             const float* bc, int32_t* sel_idx, float* sel_score, void* ws, size_t ws_bytes,
-                             hipStream_t st, hipEvent_t* ev) {
-  if (ws_bytes < score_workspace_bytes(g)) return hipErrorInvalidValue;
+hipError_t launch_score_topk(const Geom& g, int Nq, const int32_t* pos0, const void* q, const void* Dw, const void* Uw,
+                             const float* kc, const float* bc, int32_t* sel_idx, float* sel_score, void* ws,
+                             size_t ws_bytes, hipStream_t st, hipEvent_t* ev) {
+  if (ws_bytes < score_workspace_bytes(g) || Nq > g.N) return hipErrorInvalidValue;
   const ScoreWs w = score_ws(g);
   uint16_t* planes = (uint16_t*)((char*)ws + w.planes);
   uint16_t* t1 = (uint16_t*)((char*)ws + w.t1);
@@ -924,14 +934,14 @@ hipError_t launch_score_topk(const Geom& g, const void* q, const void* Dw, const
   }
   if (g.io == 0) {
     if (g.d == 64)
-      launch_st_d<float, 64>(g, q, Dw, Uw, planes, t1, theta, bc, sel_idx, sel_score, st, ev);
+      launch_st_d<float, 64>(g, Nq, pos0, q, Dw, Uw, planes, t1, theta, sel_idx, sel_score, st, ev);
     else
-      launch_st_d<float, 128>(g, q, Dw, Uw, planes, t1, theta, bc, sel_idx, sel_score, st, ev);
+      launch_st_d<float, 128>(g, Nq, pos0, q, Dw, Uw, planes, t1, theta, sel_idx, sel_score, st, ev);
   } else {
     if (g.d == 64)
-      launch_st_d<bf16_t, 64>(g, q, Dw, Uw, planes, t1, theta, bc, sel_idx, sel_score, st, ev);
+      launch_st_d<bf16_t, 64>(g, Nq, pos0, q, Dw, Uw, planes, t1, theta, sel_idx, sel_score, st, ev);
     else
-      launch_st_d<bf16_t, 128>(g, q, Dw, Uw, planes, t1, theta, bc, sel_idx, sel_score, st, ev);
+      launch_st_d<bf16_t, 128>(g, Nq, pos0, q, Dw, Uw, planes, t1, theta, sel_idx, sel_score, st, ev);
   }
   if (ev) hipEventRecord(ev[1], st);
   return hipGetLastError();

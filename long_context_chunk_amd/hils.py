@@ -57,7 +57,7 @@ def load():
         lib.hils_workspace_bytes.argtypes = [dp, ctypes.c_int]
         lib.hils_workspace_bytes.restype = sz
         lib.hils_landmark_compress.argtypes = [dp, vp, vp, i32, i32, vp, vp, vp]
-        lib.hils_chunk_score_topk.argtypes = [dp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+        lib.hils_chunk_score_topk.argtypes = [dp, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
         lib.hils_attn_prefill.argtypes = [dp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
         lib.hils_attn_prefill_timed.argtypes = [dp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp,
                                                 ctypes.POINTER(ctypes.c_float)]
@@ -140,22 +140,29 @@ def landmark_compress(dm: Dims, k, lmk_q, kc, bc, c_begin=0, c_end=None):
                                          _stream()))
 
 
-def chunk_score_topk(dm: Dims, q, kc, bc, sel_idx, sel_score, qcal_D=None, qcal_U=None, ws=None):
+def chunk_score_topk(dm: Dims, q, kc, bc, sel_idx, sel_score, qcal_D=None, qcal_U=None, ws=None, q_pos0=None):
+    """hils_chunk_score_topk for q [B, Hq, Nq, d]: query i of batch b at position q_pos0[b] + i
+    (q_pos0: int32 [B] on the device, or None for 0) against the context's kc/bc."""
     C = dm.N // dm.S
     dt = torch.float32 if dm.io == F32 else torch.bfloat16
-    _req(q, "q", (dm.B, dm.Hq, dm.N, dm.d), dt)
+    if q is None or q.dim() != 4:
+        raise ValueError("q must be [B, Hq, Nq, d]")
+    Nq = q.shape[2]
+    _req(q, "q", (dm.B, dm.Hq, Nq, dm.d), dt)
     _req(kc, "kc", (dm.B, dm.Hlmk, C, dm.d), torch.float32)
     _req(bc, "bc", (dm.B, dm.Hlmk, C), torch.float32)
-    _req(sel_idx, "sel_idx", (dm.B, dm.Hq, dm.N, dm.K), torch.int32)
-    _req(sel_score, "sel_score", (dm.B, dm.Hq, dm.N, dm.K), torch.float32)
+    _req(sel_idx, "sel_idx", (dm.B, dm.Hq, Nq, dm.K), torch.int32)
+    _req(sel_score, "sel_score", (dm.B, dm.Hq, Nq, dm.K), torch.float32)
+    if q_pos0 is not None:
+        _req(q_pos0, "q_pos0", (dm.B,), torch.int32)
     if dm.qcal_rank > 0:
         _req(qcal_D, "qcal_D", (dm.Hq, dm.qcal_rank, dm.d), dt)
         _req(qcal_U, "qcal_U", (dm.Hq, dm.d, dm.qcal_rank), dt)
     if ws is None:
         ws = workspace(dm, OP_SCORE_TOPK)
     nws = ws.numel()
-    _check(load().hils_chunk_score_topk(ctypes.byref(dm), _p(q), _p(qcal_D), _p(qcal_U), _p(kc), _p(bc), _p(sel_idx),
-                                        _p(sel_score), _p(ws), nws, _stream()))
+    _check(load().hils_chunk_score_topk(ctypes.byref(dm), Nq, _p(q), _p(q_pos0), _p(qcal_D), _p(qcal_U), _p(kc), _p(bc),
+                                        _p(sel_idx), _p(sel_score), _p(ws), nws, _stream()))
 
 
 def attn_prefill(dm: Dims, q, k, v, o, ws, lmk_q=None, kc=None, bc=None, qcal_D=None, qcal_U=None, sel_idx=None,

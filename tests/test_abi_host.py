@@ -56,7 +56,7 @@ def test_workspace_bytes():
 
 @pytest.mark.parametrize("field,value,code", [
     ("d", 96, hils.E_UNSUPPORTED), ("S", 32, hils.E_UNSUPPORTED), ("K", 0, hils.E_INVAL), ("K", 33, hils.E_UNSUPPORTED),
-    ("Hkv", 3, hils.E_INVAL), ("Hlmk", 8, hils.E_UNSUPPORTED), ("B", 0, hils.E_INVAL), ("N", 0, hils.E_INVAL),
+    ("Hkv", 3, hils.E_INVAL), ("Hlmk", 3, hils.E_INVAL), ("Hlmk", 2, hils.E_INVAL), ("B", 0, hils.E_INVAL), ("N", 0, hils.E_INVAL),
     ("io", 5, hils.E_UNSUPPORTED), ("qcal_rank", -1, hils.E_INVAL), ("qcal_rank", 64, hils.E_UNSUPPORTED),
     ("window", -64, hils.E_INVAL), ("window", 100, hils.E_INVAL), ("window", 33 * 64, hils.E_UNSUPPORTED),
 ])
@@ -94,7 +94,7 @@ def test_null_pointers_and_ranges_rejected():
     assert lib.hils_landmark_compress(ctypes.byref(d), None, fake, 0, 1, fake, fake, None) == hils.E_INVAL
     assert lib.hils_landmark_compress(ctypes.byref(d), fake, fake, 5, 4, fake, fake, None) == hils.E_INVAL
     assert lib.hils_landmark_compress(ctypes.byref(d), fake, fake, 0, 17, fake, fake, None) == hils.E_INVAL
-    assert lib.hils_chunk_score_topk(ctypes.byref(d), fake, None, None, fake, fake, None, fake, None, 0,
+    assert lib.hils_chunk_score_topk(ctypes.byref(d), 1024, fake, None, None, None, fake, fake, None, fake, None, 0,
                                      None) == hils.E_INVAL
     # prefill without landmark queries needs kc/bc
     assert lib.hils_attn_prefill(ctypes.byref(d), fake, fake, fake, None, None, None, None, None, None, None, fake,
@@ -207,3 +207,27 @@ def test_decode_noalloc_rejects_dims_beyond_its_scratch():
     bad = hils.dims(8, 32, 8, 96, 4096, 32)
     rc = lib.hils_attn_decode_noalloc(ctypes.byref(bad), fake, fake, fake, fake, fake, fake, None, None, None, fake, None)
     assert rc == hils.E_UNSUPPORTED
+
+
+def test_landmark_heads_per_kv_group_accepted_backward_rejects():
+    """Hlmk = Hkv (one landmark head per KV group) is valid for the forward calls; the
+    backward pass needs Hlmk == Hq and says so before touching the device."""
+    lib = hils.load()
+    d = hils.dims(1, 16, 4, 64, 1024, 16, Hlmk=4)
+    assert hils.workspace_bytes(d, hils.OP_PREFILL) > 0
+    assert hils.workspace_bytes(d, hils.OP_SCORE_TOPK) >= 4 * 16 * (2 * 64 + 16) * 2   # k' planes of 4 landmark heads
+    fake = ctypes.c_void_p(0x1000)
+    rc = lib.hils_attn_prefill_backward(ctypes.byref(d), *([fake] * 18), 1 << 40, None)
+    assert rc == hils.E_UNSUPPORTED and b"landmark" in lib.hils_last_error()
+
+
+def test_score_topk_block_arguments():
+    lib = hils.load()
+    d = hils.dims(2, 4, 2, 64, 4096, 8)
+    fake = ctypes.c_void_p(0x1000)
+    args = lambda nq: (ctypes.byref(d), nq, fake, None, None, None, fake, fake, fake, fake, fake, 1 << 40, None)
+    assert lib.hils_chunk_score_topk(*args(4097)) == hils.E_INVAL      # more queries than N
+    assert lib.hils_chunk_score_topk(*args(-1)) == hils.E_INVAL
+    # no query: nothing to do, NULL arrays allowed, nothing enqueued
+    assert lib.hils_chunk_score_topk(ctypes.byref(d), 0, None, None, None, None, None, None, None, None, None, 0,
+                                     None) == hils.OK

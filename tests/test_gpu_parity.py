@@ -640,3 +640,104 @@ def test_decode_exact_ties_to_lower_chunk(name, w, twins):
     summ = check_selection_and_output(w, xx, kc_o, bc_o, list(zip(rows_b, rows_h, pos)), ref, gsel, None,
                                       g["o"].reshape(-1, w.d), label=name)
     _say(name, "exact-tie rows", nt, summ)
+
+
+# ------------------------------------------- a block of queries at a position offset
+# hils_chunk_score_topk scores any block of Nq queries of a sequence whose context kc/bc
+# holds floor(N/S) complete chunks: query i of batch b sits at q_pos0[b] + i (chunked
+# prefill, several new tokens of a decode stream).
+from hils_testutil import check_selection  # noqa: E402
+
+OFFSET = [
+    ("bf16_d64", synth.Workload("off_a", B=2, Hq=4, Hkv=2, d=64, N=4096, K=8), 700, [1000, 3333]),
+    ("bf16_d128_qcal", synth.Workload("off_b", B=2, Hq=4, Hkv=1, d=128, N=5000, K=16, qcal_rank=8), 333, [64, 4600]),
+    ("f32_d64_w256", synth.Workload("off_c", B=1, Hq=2, Hkv=1, d=64, N=3000, K=5, io=synth.F32, window=256), 257,
+     [2100]),
+    ("bf16_d64_shared_lmk", synth.Workload("off_d", B=2, Hq=8, Hkv=2, d=64, N=4096, K=8, Hlmk=2), 500, [0, 3500]),
+    ("bf16_d64_past_end", synth.Workload("off_e", B=1, Hq=2, Hkv=2, d=64, N=2048, K=8), 130, [2000]),
+]
+
+
+@pytest.mark.parametrize("name,w,Nq,p0", OFFSET, ids=[o[0] for o in OFFSET])
+def test_score_topk_query_block_at_offset(name, w, Nq, p0):
+    _say("score_topk block at offset", name)
+    x = synth.make_inputs(w, SEED + 51)
+    kc_o, bc_o = oracle_compress(w, x)
+    pos0 = np.asarray(p0, np.int32)
+    # the block's queries: rows q_pos0[b] .. of the sequence where they exist, fresh draws past its end
+    qb = synth.normal((w.B, w.Hq, Nq, w.d), SEED + 52, 901, w.io)
+    for b in range(w.B):
+        n_in = max(0, min(Nq, w.N - int(pos0[b])))
+        qb[b, :, :n_in] = x["q"][b, :, pos0[b]:pos0[b] + n_in]
+    dm = dims_of(w)
+    sel = torch.full((w.B, w.Hq, Nq, w.K), -9, dtype=torch.int32, device="cuda")
+    scr = torch.empty((w.B, w.Hq, Nq, w.K), dtype=torch.float32, device="cuda")
+    D = upload(x["D"], w.io) if w.qcal_rank else None
+    U = upload(x["U"], w.io) if w.qcal_rank else None
+    hils.chunk_score_topk(dm, upload(qb, w.io), torch.from_numpy(kc_o.astype(np.float32)).cuda(),
+                          torch.from_numpy(bc_o.astype(np.float32)).cuda(), sel, scr, qcal_D=D, qcal_U=U,
+                          q_pos0=torch.from_numpy(pos0).cuda())
+    torch.cuda.synchronize()
+    kc32 = kc_o.astype(np.float32).astype(np.float64)
+    bc32 = bc_o.astype(np.float32).astype(np.float64)
+    rows = [(b, h, int(pos0[b]) + i) for b in range(w.B) for h in range(w.Hq) for i in range(Nq)]
+    qrows = np.stack([qb[b, h, i] for b in range(w.B) for h in range(w.Hq) for i in range(Nq)])
+    ref = oracle.attend(shape_of(w), [r[0] for r in rows], [r[1] for r in rows], [r[2] for r in rows], qrows,
+                        x["k"], x["v"], kc32, bc32, D=x.get("D"), U=x.get("U"))
+    xx = dict(x)
+
+    class QView:
+        def __getitem__(self, key):
+            b, h, i = key
+            return qb[b, h, i - int(pos0[b])]
+    xx["q"] = QView()
+    summ = check_selection(w, xx, kc32, bc32, rows, ref, sel.cpu().numpy().reshape(-1, w.K),
+                           scr.cpu().numpy().reshape(-1, w.K), label=name)
+    _say(name, summ)
+
+
+def test_score_topk_whole_sequence_block_matches_prefill():
+    """Nq = N with no offsets is the prefill's own scoring: identical selection."""
+    w = SMALL[2][1]
+    x = synth.make_inputs(w, SEED + 53)
+    g = gpu_prefill(w, x, fused=True)
+    dm = dims_of(w)
+    sel = torch.empty((w.B, w.Hq, w.N, w.K), dtype=torch.int32, device="cuda")
+    scr = torch.empty((w.B, w.Hq, w.N, w.K), dtype=torch.float32, device="cuda")
+    hils.chunk_score_topk(dm, upload(x["q"], w.io), torch.from_numpy(g["kc"]).cuda(), torch.from_numpy(g["bc"]).cuda(),
+                          sel, scr, qcal_D=upload(x["D"], w.io), qcal_U=upload(x["U"], w.io),
+                          q_pos0=torch.zeros(w.B, dtype=torch.int32, device="cuda"))
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(sel.cpu().numpy(), g["sel_idx"])
+    np.testing.assert_array_equal(scr.cpu().numpy(), g["sel_score"])
+
+
+# ------------------------------------ one landmark head per KV group (Hlmk = Hkv)
+SHARED_LMK = [
+    ("prefill_bf16_d128_qcal", synth.Workload("shl_a", B=1, Hq=8, Hkv=2, d=128, N=2500, K=8, qcal_rank=8, Hlmk=2)),
+    ("prefill_f32_d64_w192", synth.Workload("shl_b", B=2, Hq=4, Hkv=1, d=64, N=1300, K=4, io=synth.F32, Hlmk=1,
+                                            window=192)),
+]
+
+
+@pytest.mark.parametrize("name,w", SHARED_LMK, ids=[s_[0] for s_ in SHARED_LMK])
+def test_prefill_landmark_head_per_kv_group(name, w):
+    _say("shared landmark heads", name)
+    x = synth.make_inputs(w, SEED + 55)
+    g = gpu_prefill(w, x, fused=True)
+    kc_o, bc_o = oracle_compress(w, x)
+    assert g["kc"].shape == kc_o.shape == (w.B, w.Hkv, w.C, w.d)
+    np.testing.assert_allclose(g["kc"], kc_o, rtol=0, atol=1e-5 * max(1.0, np.abs(kc_o).max()))
+    rows = [(b, h, i) for b in range(w.B) for h in range(w.Hq) for i in range(w.N)]
+    ref = oracle_rows(w, x, kc_o, bc_o, rows)
+    rr = np.asarray(rows)
+    summ = check_selection_and_output(w, x, kc_o, bc_o, rows, ref, g["sel_idx"][rr[:, 0], rr[:, 1], rr[:, 2]],
+                                      g["sel_score"][rr[:, 0], rr[:, 1], rr[:, 2]],
+                                      g["o"][rr[:, 0], rr[:, 1], rr[:, 2]], label=name)
+    _say(name, summ)
+
+
+def test_decode_landmark_head_per_kv_group():
+    w = synth.Workload("shl_dec", B=3, Hq=8, Hkv=2, d=128, N=4096, K=16, decode=True, seq_lens=[4096, 2222, 65],
+                       qcal_rank=8, Hlmk=2, needle_frac=0.05)
+    test_decode("shared_lmk", w)
