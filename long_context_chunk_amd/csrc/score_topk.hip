@@ -335,7 +335,7 @@ constexpr float TH_ABS = 1.0f / 4096.0f;   // bf16 0x3980
 constexpr int TH_EXT = 16;                  // elements of the extension k-step
 
 template <typename IO, int D, bool QCAL>
-__global__ void __launch_bounds__(256, 2) score_threshold(const IO* __restrict__ q, const IO* __restrict__ Dw,
+__global__ void __launch_bounds__(256, 3) score_threshold(const IO* __restrict__ q, const IO* __restrict__ Dw,
                                                           const IO* __restrict__ Uw, const uint16_t* __restrict__ t1,
                                                           float* __restrict__ theta, const int32_t* __restrict__ pos0,
                                                           int H, int Hl, int N, int C, int K, int r, int NB, int items,
