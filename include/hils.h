@@ -136,6 +136,10 @@ int hils_chunk_score_topk(const hils_dims_t* dims, int32_t Nq, const void* q, co
  *   lmk_q == NULL: kc/bc are inputs (precomputed by hils_landmark_compress).
  * When N < S there is no complete chunk and lmk_q, kc and bc may all be NULL.
  * sel_idx_out/sel_score_out (nullable) receive the selection of step (2).
+ * Range: with bf16 I/O each (query, chunk) output travels between kernels as fp16;
+ * it is a convex combination of v rows, so it is finite whenever every |v| <= 65504
+ * (fp16's largest finite value).  Larger |v| overflow to infinity.  fp32 I/O keeps
+ * fp32 outputs and has no such limit.
  */
 int hils_attn_prefill(const hils_dims_t* dims, const void* q, const void* k, const void* v, const void* lmk_q,
                       float* kc, float* bc, const void* qcal_D, const void* qcal_U, int32_t* sel_idx_out,

@@ -741,3 +741,25 @@ def test_decode_landmark_head_per_kv_group():
     w = synth.Workload("shl_dec", B=3, Hq=8, Hkv=2, d=128, N=4096, K=16, decode=True, seq_lens=[4096, 2222, 65],
                        qcal_rank=8, Hlmk=2, needle_frac=0.05)
     test_decode("shared_lmk", w)
+
+
+def test_prefill_values_near_the_fp16_limit():
+    """bf16 I/O carries each (query, chunk) output as fp16 between kernels: values up to
+    about 5.4e4 (below fp16's 65504) must come through with the usual bar scaled by the
+    value range."""
+    w = synth.Workload("big_v", B=1, Hq=4, Hkv=2, d=128, N=1500, K=8, qcal_rank=8)
+    x = synth.make_inputs(w, SEED + 71)
+    scale = 12000.0
+    vf = synth.bf16_to_f32(x["v"]) * scale
+    x["v"] = _to_bf16_bits(vf)
+    assert np.abs(synth.bf16_to_f32(x["v"])).max() < 65504
+    g = gpu_prefill(w, x, fused=True)
+    assert np.isfinite(g["o"]).all()
+    kc_o, bc_o = oracle_compress(w, x)
+    rows = [(0, h, i) for h in range(w.Hq) for i in range(w.N)]
+    ref = oracle_rows(w, x, kc_o, bc_o, rows)
+    rr = np.asarray(rows)
+    exact = ref["gap"] > 1e-4
+    got = g["o"][rr[:, 0], rr[:, 1], rr[:, 2]][exact]
+    err = np.abs(got - ref["o"][exact])
+    assert err.max() <= 1e-2 * scale and err.mean() <= 1e-3 * scale, (err.max() / scale, err.mean() / scale)
