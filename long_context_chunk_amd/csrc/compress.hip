@@ -7,44 +7,46 @@
 // HBM-bound: each key tile is read once (coalesced 16-byte loads) and serves every
 // landmark head of its KV head.
 #include <algorithm>
+#include <atomic>
 
+#include "attn_tile.h"
 #include "hils_common.h"
 #include "kernels.h"
 
 namespace hils {
 
-// One wave per work item (b, KV head, chunk), all landmark heads of the KV head; the waves
-// of a workgroup are independent (no workgroup barrier) and stride over the items, the
-// next item's keys in flight in registers while the current one is computed.
-//   * the 64 x D key tile goes to the wave's LDS region in its io type, rows padded by 16
-//     bytes, so lane j reading row j with 16-byte reads is free of bank conflicts;
-//   * logits: lane j owns key j; its row is read once and dotted with each landmark
-//     query (bf16: v_dot2 of bf16 pairs with fp32 accumulation; fp32: fma), the query
-//     broadcast from LDS;
+// fp32 I/O on the VALU.  One wave per work item (b, KV head, chunk), all landmark heads of
+// the KV head; the waves of a workgroup are independent (no workgroup barrier) and stride
+// over the items, the next item's keys in flight in registers while the current one is
+// computed.
+//   * the 64 x D key tile goes to the wave's LDS region, rows padded by 16 bytes, so lane j
+//     reading row j with 16-byte reads is free of bank conflicts;
+//   * logits: lane j owns key j; its row is read once and dotted with each landmark query
+//     (fma), the query broadcast from LDS;
 //   * softmax, k'_c and b'_c per landmark head with wave reductions; for k'_c lane e owns
 //     dimensions (2e, 2e+1) (D = 128) or e (D = 64) and reads one word of each key row,
 //     shared by all landmark heads of the group (a_j taken from lane j with readlane).
 constexpr int CP_WAVES = 4;    // waves per workgroup
 
 // GP: landmark heads handled per pass over the key rows (4, 2 or 1, dividing the group)
-template <typename IO, int D, int GP>
+template <int D, int GP>
 struct CompressLds {
-  static constexpr int LDK = D + 16 / (int)sizeof(IO);   // elements per padded key row
-  IO kt[64 * LDK];
-  IO lq[GP][D];
+  static constexpr int LDK = D + 4;   // floats per padded key row
+  float kt[64 * LDK];
+  float lq[GP][D];
 };
 
-template <typename IO, int D, int GP>
-__global__ void __launch_bounds__(64 * CP_WAVES) compress_kernel(const IO* __restrict__ k, const IO* __restrict__ lmk,
-                                                                float* __restrict__ kc, float* __restrict__ bc,
-                                                                int Hkv, int Hl, int N, int C, int c_begin,
-                                                                int nchunks, int64_t items, KvPages pg) {
+template <int D, int GP>
+__global__ void __launch_bounds__(64 * CP_WAVES) compress_f32(const float* __restrict__ k, const float* __restrict__ lmk,
+                                                             float* __restrict__ kc, float* __restrict__ bc, int Hkv,
+                                                             int Hl, int N, int C, int c_begin, int nchunks,
+                                                             int64_t items, KvPages pg) {
   constexpr int S = 64;
-  using L = CompressLds<IO, D, GP>;
+  using L = CompressLds<D, GP>;
   constexpr int LDK = L::LDK;
-  constexpr int EPV = 16 / (int)sizeof(IO);    // elements per 16-byte piece
+  constexpr int EPV = 4;                       // floats per 16-byte piece
   constexpr int NL = S * D / EPV / 64;         // 16-byte pieces per lane for a whole tile
-  constexpr int RW = D * (int)sizeof(IO) / 16; // 16-byte pieces per key row
+  constexpr int RW = D / EPV;                  // 16-byte pieces per key row
   constexpr int DPL = D / 64;                  // k' dimensions per lane (1 or 2)
   __shared__ L lds[CP_WAVES];
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
@@ -63,7 +65,7 @@ __global__ void __launch_bounds__(64 * CP_WAVES) compress_kernel(const IO* __res
     const int cl = (int)(it % nchunks);
     const int64_t bk = it / nchunks;  // b * Hkv + kvh
     const int kvh = (int)(bk % Hkv), b = (int)(bk / Hkv);
-    const IO* kt = k + pg.chunk_row(b, kvh, Hkv, N, c_begin + cl) * D;
+    const float* kt = k + pg.chunk_row(b, kvh, Hkv, N, c_begin + cl) * D;
 #pragma unroll
     for (int u = 0; u < NL; ++u) raw[u] = *reinterpret_cast<const u32x4_t*>(kt + (u * 64 + lane) * EPV);
 #pragma unroll
@@ -118,25 +120,10 @@ __global__ void __launch_bounds__(64 * CP_WAVES) compress_kernel(const IO* __res
 #pragma unroll
           for (int pc = 0; pc < RW; ++pc) {
             const u32x4_t lv = *reinterpret_cast<const u32x4_t*>(&sm.lq[g][pc * EPV]);   // broadcast
-            if constexpr (sizeof(IO) == 2) {
-              // pairs taken with shufflevector from whole 8-element vectors (a bit cast of
-              // one 32-bit element of a vector register was miscompiled to element 0)
-              const bf16x8_t kv8 = __builtin_bit_cast(bf16x8_t, kr[pc]);
-              const bf16x8_t lv8 = __builtin_bit_cast(bf16x8_t, lv);
-              z = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(kv8, kv8, 0, 1),
-                                                  __builtin_shufflevector(lv8, lv8, 0, 1), z, false);
-              z = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(kv8, kv8, 2, 3),
-                                                  __builtin_shufflevector(lv8, lv8, 2, 3), z, false);
-              z = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(kv8, kv8, 4, 5),
-                                                  __builtin_shufflevector(lv8, lv8, 4, 5), z, false);
-              z = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(kv8, kv8, 6, 7),
-                                                  __builtin_shufflevector(lv8, lv8, 6, 7), z, false);
-            } else {
-              z = fmaf(__uint_as_float(kr[pc].x), __uint_as_float(lv.x), z);
-              z = fmaf(__uint_as_float(kr[pc].y), __uint_as_float(lv.y), z);
-              z = fmaf(__uint_as_float(kr[pc].z), __uint_as_float(lv.z), z);
-              z = fmaf(__uint_as_float(kr[pc].w), __uint_as_float(lv.w), z);
-            }
+            z = fmaf(__uint_as_float(kr[pc].x), __uint_as_float(lv.x), z);
+            z = fmaf(__uint_as_float(kr[pc].y), __uint_as_float(lv.y), z);
+            z = fmaf(__uint_as_float(kr[pc].z), __uint_as_float(lv.z), z);
+            z = fmaf(__uint_as_float(kr[pc].w), __uint_as_float(lv.w), z);
           }
           z *= tau;
           const float m = wave_max(z);
@@ -156,14 +143,8 @@ __global__ void __launch_bounds__(64 * CP_WAVES) compress_kernel(const IO* __res
 #pragma unroll 4
       for (int j = 0; j < S; ++j) {
         float kv[DPL];
-        if constexpr (sizeof(IO) == 2 && DPL == 2) {
-          const uint32_t wd = *reinterpret_cast<const uint32_t*>(&sm.kt[j * LDK + 2 * lane]);
-          kv[0] = __uint_as_float(wd << 16);
-          kv[1] = __uint_as_float(wd & 0xffff0000u);
-        } else {
 #pragma unroll
-          for (int x = 0; x < DPL; ++x) kv[x] = io_traits<IO>::load(sm.kt, j * LDK + DPL * lane + x);
-        }
+        for (int x = 0; x < DPL; ++x) kv[x] = sm.kt[j * LDK + DPL * lane + x];
 #pragma unroll
         for (int g = 0; g < GP; ++g) {
           const float aj = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(a[g]), j));
@@ -190,24 +171,243 @@ __global__ void __launch_bounds__(64 * CP_WAVES) compress_kernel(const IO* __res
   }
 }
 
-template <typename IO, int D, int GP>
+// bf16 I/O on the MFMA: per work item (one wave, one chunk of one KV head) the landmark
+// queries of the group's heads are the columns of one 32x32x16 product,
+//   S^T = K L^T            (keys x heads; K rows and the queries from LDS),
+// the softmax over the 64 keys runs on the accumulators (a lane holds 32 keys of its
+// column, the other lane half the rest), and the weighted sum
+//   k'^T = K^T P^T / l     (dims x heads; K^T through transposing LDS reads of the same
+//                           tile, P^T split into two bf16 terms, about 2^-17 relative)
+// takes the accumulators of S^T as its operand without moving data between lanes.
+// Lanes of columns beyond the group compute on zero queries and store nothing.  The keys
+// and the first GQ landmark queries of the next DEPTH items are in flight in registers
+// while the current one is computed; a group of more than 32 landmark heads takes further
+// passes whose queries are read directly.
+template <int D, int GQ, int DEPTH>
+__global__ void __launch_bounds__(64 * CP_WAVES, DEPTH == 1 ? 2 : 1) compress_mfma(const bf16_t* __restrict__ k,
+                                                              const bf16_t* __restrict__ lmk, float* __restrict__ kc,
+                                                              float* __restrict__ bc, int Hkv, int Hl, int N, int C,
+                                                              int c_begin, int nchunks, int64_t items, KvPages pg) {
+  constexpr int S = 64;
+  constexpr int LDK = D + 8;                // padded bf16 row stride (conflict-free 16-byte rows)
+  constexpr int NL = S * D / 8 / 64;        // 16-byte key pieces per lane
+  constexpr int NKS = D / 16;               // k-steps of S^T
+  constexpr int QP = D / 8;                 // 16-byte pieces per landmark query
+  constexpr int NQ = (GQ * QP + 63) / 64;   // query pieces per lane
+  struct Lds {
+    uint16_t kt[S * LDK];
+    uint16_t lq[GQ * LDK];
+  };
+  __shared__ __align__(16) Lds lds[CP_WAVES];
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, h = lane >> 5, col = lane & 31;
+  uint16_t* kt = lds[w].kt;
+  uint16_t* lq = lds[w].lq;
+  const int G = Hl / Hkv;
+  const int Gq = min(G, GQ);   // heads whose queries are staged with the keys
+  const float tau = 1.0f / sqrtf((float)D);
+  const float c2 = tau * 1.44269504088896340736f;  // tau log2(e)
+  const int64_t stride = (int64_t)gridDim.x * CP_WAVES;
+  int64_t item = (int64_t)blockIdx.x * CP_WAVES + w;
+  if (item >= items) return;   // the whole wave: no barrier below waits for it
+
+  // item -> (b, KV head, chunk); landmark row of head g of the group = l0 + g C
+  auto where = [&](int64_t it, int& b, int& kvh, int& c) {
+    const int64_t bk = it / nchunks;
+    c = c_begin + (int)(it - bk * nchunks);
+    kvh = (int)(bk % Hkv);
+    b = (int)(bk / Hkv);
+  };
+  auto issue = [&](u32x4_t(&r)[NL], u32x4_t(&qr)[NQ], int64_t it) {
+    int b, kvh, c;
+    where(it, b, kvh, c);
+    const bf16_t* src = k + pg.chunk_row(b, kvh, Hkv, N, c) * D;
+#pragma unroll
+    for (int u = 0; u < NL; ++u) r[u] = *reinterpret_cast<const u32x4_t*>(src + (u * 64 + lane) * 8);
+    const int64_t l0 = ((int64_t)b * Hl + (int64_t)kvh * G) * C + c;
+#pragma unroll
+    for (int u = 0; u < NQ; ++u) {
+      const int p = u * 64 + lane, g = p / QP;
+      if (g < Gq) qr[u] = *reinterpret_cast<const u32x4_t*>(lmk + (l0 + (int64_t)g * C) * D + (p % QP) * 8);
+    }
+  };
+  auto stage = [&](const u32x4_t(&r)[NL], const u32x4_t(&qr)[NQ]) {
+#pragma unroll
+    for (int u = 0; u < NL; ++u) {
+      const int e0 = (u * 64 + lane) * 8;
+      *reinterpret_cast<u32x4_t*>(&kt[(e0 / D) * LDK + e0 % D]) = r[u];
+    }
+#pragma unroll
+    for (int u = 0; u < NQ; ++u) {
+      const int p = u * 64 + lane, g = p / QP;
+      if (g < Gq) *reinterpret_cast<u32x4_t*>(&lq[g * LDK + (p % QP) * 8]) = qr[u];
+    }
+  };
+  auto compute = [&](int64_t it) {
+    int b, kvh, c;
+    where(it, b, kvh, c);
+    const int64_t l0 = ((int64_t)b * Hl + (int64_t)kvh * G) * C + c;
+    for (int g0 = 0; g0 < G; g0 += 32) {
+      const int g = g0 + col;
+      const bool ok = g < G;
+      bf16x8_t lv[NKS];   // this lane's head column of L (dims 16 ks + 8 h + 0..7)
+      const uint32_t keep = ok ? 0xffffffffu : 0u;
+#pragma unroll
+      for (int ks = 0; ks < NKS; ++ks) {
+        u32x4_t x = g0 == 0 ? *reinterpret_cast<const u32x4_t*>(&lq[min(col, Gq - 1) * LDK + 16 * ks + 8 * h])
+                            : *reinterpret_cast<const u32x4_t*>(lmk + (l0 + (int64_t)min(g, G - 1) * C) * D +
+                                                                16 * ks + 8 * h);
+        x.x &= keep, x.y &= keep, x.z &= keep, x.w &= keep;
+        lv[ks] = __builtin_bit_cast(bf16x8_t, x);
+      }
+      // S^T: sacc[tt] register r = key 32 tt + acc_row(r, h), column = head g
+      f32x16_t sacc[2];
+#pragma unroll
+      for (int tt = 0; tt < 2; ++tt) {
+        sacc[tt] = zero16();
+        const int key = 32 * tt + col;
+#pragma unroll
+        for (int ks = 0; ks < NKS; ++ks)
+          sacc[tt] = mfma32(lds_op16(&kt[key * LDK + 16 * ks + 8 * h]), lv[ks], sacc[tt]);
+      }
+      float m = fmaxf(sacc[0][0], sacc[0][1]);
+#pragma unroll
+      for (int rr = 2; rr < 32; ++rr) m = fmaxf(m, sacc[rr >> 4][rr & 15]);
+      m = fmaxf(m, __shfl_xor(m, 32));
+      float l = 0.f, t = 0.f;
+#pragma unroll
+      for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+        for (int rr = 0; rr < 16; ++rr) {
+          const float dz = sacc[tt][rr] - m;
+          const float pe = __builtin_amdgcn_exp2f(dz * c2);
+          sacc[tt][rr] = pe;
+          l += pe;
+          t = fmaf(pe, dz, t);
+        }
+      l += __shfl_xor(l, 32);
+      t += __shfl_xor(t, 32);
+      // -sum_j a_j log a_j with a_j = p_j / l, log a_j = tau (s_j - m) - log l
+      const float ent = logf(l) - tau * t / l;
+      // P^T as two-term B operands: k-step ks2 takes registers 8 (ks2 & 1) .. of tile ks2 >> 1
+      bf16x8_t pb[2][4];
+#pragma unroll
+      for (int ks2 = 0; ks2 < 4; ++ks2) {
+        float pv[8];
+#pragma unroll
+        for (int mm = 0; mm < 8; ++mm) pv[mm] = sacc[ks2 >> 1][8 * (ks2 & 1) + mm];
+        u32x4_t t2[2];
+        split8<2>(pv, t2);
+        pb[0][ks2] = __builtin_bit_cast(bf16x8_t, t2[0]);
+        pb[1][ks2] = __builtin_bit_cast(bf16x8_t, t2[1]);
+      }
+      const int64_t row = l0 + (int64_t)min(g, G - 1) * C;
+      const float inv = 1.0f / l;
+#pragma unroll
+      for (int dt = 0; dt < D / 32; ++dt) {
+        f32x16_t o = zero16();
+#pragma unroll
+        for (int ks2 = 0; ks2 < 4; ++ks2) {
+          const bf16x8_t a = vt_operand<LDK>(kt, dt, ks2, lane);
+          o = mfma32(a, pb[0][ks2], o);
+          o = mfma32(a, pb[1][ks2], o);
+        }
+        if (ok) {
+#pragma unroll
+          for (int r4 = 0; r4 < 4; ++r4)
+            *reinterpret_cast<float4*>(kc + row * D + 32 * dt + 8 * r4 + 4 * h) =
+                make_float4(o[4 * r4] * inv, o[4 * r4 + 1] * inv, o[4 * r4 + 2] * inv, o[4 * r4 + 3] * inv);
+        }
+      }
+      if (ok && h == 0) bc[row] = ent;
+    }
+  };
+  // one step: stage the item's registers into LDS, refill them with the item DEPTH strides
+  // ahead, compute; LDS operations of one wave execute in order, so only the compiler has
+  // to be kept from moving LDS accesses across the stage (wave barriers)
+  auto step = [&](u32x4_t(&r)[NL], u32x4_t(&qr)[NQ], int64_t it) {
+    stage(r, qr);
+    __builtin_amdgcn_wave_barrier();
+    if (it + DEPTH * stride < items) issue(r, qr, it + DEPTH * stride);
+    compute(it);
+    __builtin_amdgcn_wave_barrier();
+  };
+  u32x4_t rk[DEPTH][NL], rq[DEPTH][NQ];
+#pragma unroll
+  for (int s = 0; s < DEPTH; ++s)
+    if (item + s * stride < items) issue(rk[s], rq[s], item + s * stride);
+  for (;;) {
+#pragma unroll
+    for (int s = 0; s < DEPTH; ++s) {
+      if (item >= items) return;
+      step(rk[s], rq[s], item);
+      item += stride;
+    }
+  }
+}
+
+template <int D, int GQ, int DEPTH>
+static void launch_cm(hipStream_t st, const void* k, const void* lmk, float* kc, float* bc, int Hkv, int Hl, int N,
+                      int C, int c_begin, int n, int64_t items, KvPages pg) {
+  // persistent waves: as many workgroups as fit on the chip at once, each wave striding
+  // over the items with its prefetch running ahead
+  static std::atomic<int> resident[64];   // per device, 0 until first queried
+  int dev = 0;
+  (void)hipGetDevice(&dev);
+  int occ = resident[dev & 63].load(std::memory_order_relaxed);
+  if (occ == 0) {
+    int cus = 0, blocks = 0;
+    (void)hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+    (void)hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, compress_mfma<D, GQ, DEPTH>, 64 * CP_WAVES, 0);
+    occ = std::max(1, cus) * std::max(1, blocks);
+    resident[dev & 63].store(occ, std::memory_order_relaxed);
+  }
+  const dim3 grid((unsigned)std::min<int64_t>((items + CP_WAVES - 1) / CP_WAVES, occ));
+  hipLaunchKernelGGL((compress_mfma<D, GQ, DEPTH>), grid, dim3(64 * CP_WAVES), 0, st, (const bf16_t*)k,
+                     (const bf16_t*)lmk, kc, bc, Hkv, Hl, N, C, c_begin, n, items, pg);
+}
+
+template <int D, int DEPTH>
+static void launch_cm_g(int G, hipStream_t st, const void* k, const void* lmk, float* kc, float* bc, int Hkv, int Hl,
+                        int N, int C, int c_begin, int n, int64_t items, KvPages pg) {
+  if (G <= 4)
+    launch_cm<D, 4, DEPTH>(st, k, lmk, kc, bc, Hkv, Hl, N, C, c_begin, n, items, pg);
+  else if (G <= 8)
+    launch_cm<D, 8, DEPTH>(st, k, lmk, kc, bc, Hkv, Hl, N, C, c_begin, n, items, pg);
+  else if (G <= 16)
+    launch_cm<D, 16, DEPTH>(st, k, lmk, kc, bc, Hkv, Hl, N, C, c_begin, n, items, pg);
+  else
+    launch_cm<D, 32, DEPTH>(st, k, lmk, kc, bc, Hkv, Hl, N, C, c_begin, n, items, pg);
+}
+
+template <int D, int GP>
 static void launch_cp(dim3 grid, hipStream_t st, const void* k, const void* lmk, float* kc, float* bc, int Hkv, int Hl,
                       int N, int C, int c_begin, int n, int64_t items, KvPages pg) {
-  hipLaunchKernelGGL((compress_kernel<IO, D, GP>), grid, dim3(64 * CP_WAVES), 0, st, (const IO*)k, (const IO*)lmk, kc,
+  hipLaunchKernelGGL((compress_f32<D, GP>), grid, dim3(64 * CP_WAVES), 0, st, (const float*)k, (const float*)lmk, kc,
                      bc, Hkv, Hl, N, C, c_begin, n, items, pg);
 }
 
-template <typename IO>
-hipError_t launch_compress_t(const void* k, const void* lmk, float* kc, float* bc, int B, int Hkv, int Hl, int N,
-                             int d, int c_begin, int c_end, hipStream_t st, KvPages pg) {
-  const int C = N / 64, n = c_end - c_begin;
-  if (n <= 0) return hipSuccess;
+static hipError_t launch_compress_bf16(const void* k, const void* lmk, float* kc, float* bc, int B, int Hkv, int Hl,
+                                       int N, int d, int c_begin, int n, hipStream_t st, KvPages pg) {
+  const int C = N / 64;
+  const int64_t items = (int64_t)B * Hkv * n;
+  // d = 64: one item in flight per wave, two waves per SIMD; d = 128: two items in flight
+  // per wave, one wave per SIMD (the two measured alike within noise at either size)
+  if (d == 64)
+    launch_cm_g<64, 1>(Hl / Hkv, st, k, lmk, kc, bc, Hkv, Hl, N, C, c_begin, n, items, pg);
+  else
+    launch_cm_g<128, 2>(Hl / Hkv, st, k, lmk, kc, bc, Hkv, Hl, N, C, c_begin, n, items, pg);
+  return hipGetLastError();
+}
+
+static hipError_t launch_compress_f32(const void* k, const void* lmk, float* kc, float* bc, int B, int Hkv, int Hl,
+                                      int N, int d, int c_begin, int n, hipStream_t st, KvPages pg) {
+  const int C = N / 64;
   const int64_t items = (int64_t)B * Hkv * n;
   // enough waves to fill the chip several times over; each strides over the items
   const dim3 grid((unsigned)std::min<int64_t>((items + CP_WAVES - 1) / CP_WAVES, 256 * 16));
   const int G = Hl / Hkv;
   const int gp = G % 4 == 0 ? 4 : (G % 2 == 0 ? 2 : 1);
-#define HILS_CP(D_, GP_) launch_cp<IO, D_, GP_>(grid, st, k, lmk, kc, bc, Hkv, Hl, N, C, c_begin, n, items, pg)
+#define HILS_CP(D_, GP_) launch_cp<D_, GP_>(grid, st, k, lmk, kc, bc, Hkv, Hl, N, C, c_begin, n, items, pg)
   if (d == 64) {
     if (gp == 4) HILS_CP(64, 4);
     else if (gp == 2) HILS_CP(64, 2);
@@ -223,8 +423,10 @@ hipError_t launch_compress_t(const void* k, const void* lmk, float* kc, float* b
 
 hipError_t launch_compress(int io, const void* k, const void* lmk, float* kc, float* bc, int B, int Hkv, int Hl,
                            int N, int d, int c_begin, int c_end, hipStream_t st, KvPages pg) {
-  return io == 0 ? launch_compress_t<float>(k, lmk, kc, bc, B, Hkv, Hl, N, d, c_begin, c_end, st, pg)
-                 : launch_compress_t<bf16_t>(k, lmk, kc, bc, B, Hkv, Hl, N, d, c_begin, c_end, st, pg);
+  const int n = c_end - c_begin;
+  if (n <= 0) return hipSuccess;
+  return io == 0 ? launch_compress_f32(k, lmk, kc, bc, B, Hkv, Hl, N, d, c_begin, n, st, pg)
+                 : launch_compress_bf16(k, lmk, kc, bc, B, Hkv, Hl, N, d, c_begin, n, st, pg);
 }
 
 }  // namespace hils
