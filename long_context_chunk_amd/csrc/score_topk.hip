@@ -40,6 +40,9 @@ namespace hils {
 
 constexpr int ST_ROWS = 128;   // queries per workgroup
 constexpr int ST_TILE = 64;    // chunks per LDS tile
+constexpr int KP_PAD = 64;     // k' rows per head are padded to a multiple of this (zero rows)
+
+static __host__ __device__ inline int kp_rows(int C) { return (C + KP_PAD - 1) / KP_PAD * KP_PAD; }
 
 template <int CTRL>
 HILS_DEV int dpp(int v) {
@@ -393,26 +396,27 @@ __global__ void __launch_bounds__(256, 3) score_threshold(const IO* __restrict__
     qa[NKS] = pack8(t);
   }
 
-  const uint16_t* src = t1 + ((int64_t)bb * Hl + hh / (H / Hl)) * C * DE;   // the landmark head's rows
-  u32x4_t pf[PL];
-  // chunks beyond Pmax load chunk Pmax-1 (finite; masked out below); the last partial
-  // group of segments repeats the final segment: no divergent loads
-  auto load_tile = [&](int t) {
+  // the landmark head's rows, padded to a multiple of KP_PAD zero rows: a tile never reads
+  // past them.  A tile's rows are contiguous: thread t moves 16-byte segments t + 256 u
+  // (the final partial group repeats the last segment; its duplicate store writes the
+  // same bytes), at offsets that are the same for every tile.
+  const uint16_t* src = t1 + ((int64_t)bb * Hl + hh / (H / Hl)) * kp_rows(C) * DE;
+  int goff[PL], soff[PL];
 #pragma unroll
-    for (int u = 0; u < PL; ++u) {
-      const int it = min(tid + 256 * u, NSEG - 1);
-      const int e = it / SEGS, sg = it % SEGS;
-      const int c = min(t * ST_TILE + e, Pmax - 1);
-      pf[u] = *reinterpret_cast<const u32x4_t*>(src + (int64_t)c * DE + 8 * sg);
-    }
+  for (int u = 0; u < PL; ++u) {
+    const int it = min(tid + 256 * u, NSEG - 1);
+    goff[u] = 8 * it;
+    soff[u] = (it / SEGS) * LDT + 8 * (it % SEGS);
+  }
+  u32x4_t pf[PL];
+  auto load_tile = [&](int t) {
+    const uint16_t* tp = src + (int64_t)t * ST_TILE * DE;
+#pragma unroll
+    for (int u = 0; u < PL; ++u) pf[u] = *reinterpret_cast<const u32x4_t*>(tp + goff[u]);
   };
   auto store_tile = [&](int buf) {
 #pragma unroll
-    for (int u = 0; u < PL; ++u) {
-      const int it = min(tid + 256 * u, NSEG - 1);
-      const int e = it / SEGS, sg = it % SEGS;
-      *reinterpret_cast<u32x4_t*>(&kt[buf][e * LDT + 8 * sg]) = pf[u];
-    }
+    for (int u = 0; u < PL; ++u) *reinterpret_cast<u32x4_t*>(&kt[buf][soff[u]]) = pf[u];
   };
 
   // each lane: the two largest values of its column of chunks, for 2 rows per register.
@@ -432,8 +436,8 @@ __global__ void __launch_bounds__(256, 3) score_threshold(const IO* __restrict__
   // One tile: the two 32-chunk halves' MFMA chains interleaved (independent
   // accumulators), so each hides the other's latency and the updates of the first half
   // overlap the second.  MASKED tiles reach chunks >= Pmin, which are not candidates of
-  // every row (the half of a last tile past Pmax holds copies of chunk Pmax - 1 and is
-  // masked out with them).  Masked and unmasked tiles run in separate loops: one loop
+  // every row (the chunks of a last tile past Pmax, later chunks or zero padding rows,
+  // are masked out with them).  Masked and unmasked tiles run in separate loops: one loop
   // with both kinds makes the compiler copy the running top-two at every iteration.
   auto tile_step = [&](int t, auto masked_tag) {
     constexpr bool MASKED = decltype(masked_tag)::value;
@@ -489,8 +493,12 @@ __global__ void __launch_bounds__(256, 3) score_threshold(const IO* __restrict__
 // S^T = k' q^T on the MFMA: k' rows (chunks) are the A operand, the queries the B
 // operand, so accumulator register r of lane l holds the score of chunk
 // acc_row(r, l >> 5) of the 32-chunk tile for query row l & 31.  Each lane therefore
-// owns one row's scores and appends its passing candidates to its own half of the
-// row's list (LDS) with a per-lane fill: no cross-lane bookkeeping per score.
+// owns one row's scores (half of each tile's chunks) and appends its passing candidates
+// to its own half of the row's list in LDS.  Only lanes whose score passes the row's
+// threshold execute an append (about 2% of the scores pass), and the appends of tile ct
+// are interleaved one for one with the MFMAs of tile ct + 1.  A half list that overflows
+// takes further candidates in a spill slot (lost for now); the row is then compacted to
+// its best K, its threshold raised to the K-th of them, and the lost ones appended again.
 // tau is folded into the k' planes and b' (three exact bf16 terms) enters through an
 // extra k-step against a constant [1, 1, 1, 0 ...] query operand.
 constexpr int SEL_CT = 32;     // chunks per column tile (single LDS buffer)
@@ -498,14 +506,13 @@ constexpr int SEL_HALF = 32;   // candidate slots per half-row list (plus one sp
 constexpr int P2_EXT = 16;     // extension elements after plane 0: [b'_hi, b'_mid, b'_lo, 0 ...]
 
 template <typename IO, int D, int NQ, int NK, bool QCAL>
-__global__ void __launch_bounds__(256, NQ * NK > 4 ? 1 : 2) score_topk_kernel(const IO* __restrict__ q, const IO* __restrict__ Dw,
-                                                             const IO* __restrict__ Uw,
-                                                             const uint16_t* __restrict__ p2,
-                                                             const float* __restrict__ theta,
-                                                             int32_t* __restrict__ sel_idx,
-                                                             float* __restrict__ sel_score,
-                                                             const int32_t* __restrict__ pos0, int H, int Hl, int N,
-                                                             int C, int K, int r, int NB, int items, int nw) {
+__global__ void __launch_bounds__(256, 2) score_topk_kernel(const IO* __restrict__ q, const IO* __restrict__ Dw,
+                                                           const IO* __restrict__ Uw, const uint16_t* __restrict__ p2,
+                                                           const float* __restrict__ theta,
+                                                           int32_t* __restrict__ sel_idx,
+                                                           float* __restrict__ sel_score,
+                                                           const int32_t* __restrict__ pos0, int H, int Hl, int N,
+                                                           int C, int K, int r, int NB, int items, int nw) {
   constexpr int NKS = D / 16;
   constexpr int DE2 = NK * D + P2_EXT;  // elements of a chunk row: plane 0, extension, planes 1..
   constexpr int LDR = DE2 + 8;          // LDS row stride (16-byte pad)
@@ -514,9 +521,20 @@ __global__ void __launch_bounds__(256, NQ * NK > 4 ? 1 : 2) score_topk_kernel(co
   constexpr int PL = (NSEG + 255) / 256;
   constexpr int HSTR = SEL_HALF + 1;    // half-list stride: SEL_HALF slots + a spill slot
   constexpr int LIST = 2 * HSTR;        // slots per row
+  constexpr int NPROD = NQ > NK ? NQ : NK;
+  constexpr int NMF = [] {              // MFMAs per tile: the products i + j < NPROD, then b'
+    int c = 0;
+    for (int i = 0; i < NQ; ++i)
+      for (int j = 0; j < NK; ++j) c += i + j < NPROD ? 1 : 0;
+    return c * NKS + 1;
+  }();
+  // candidate lists: scores (fp32) then chunks (uint16) of slot s at byte 4 s and
+  // CI_OFS + 2 s: one address register serves both writes
+  constexpr int CI_OFS = ST_ROWS * LIST * 4;
   __shared__ __align__(16) uint16_t kt[SEL_CT * LDR];
-  __shared__ float cs[ST_ROWS * LIST + 256];      // candidate scores; the last 256 are per-lane sinks
-  __shared__ uint16_t ci[ST_ROWS * LIST + 256];   // candidate chunks
+  __shared__ __align__(16) unsigned char lists[ST_ROWS * LIST * 6];
+  float* cs = reinterpret_cast<float*>(lists);
+  uint16_t* ci = reinterpret_cast<uint16_t*>(lists + CI_OFS);
 
   const int item = remap_xcd(blockIdx.x, items);
   if (item >= items) return;
@@ -554,22 +572,20 @@ __global__ void __launch_bounds__(256, NQ * NK > 4 ? 1 : 2) score_topk_kernel(co
   }
 
   // ---- per-lane state: the row's threshold (theta, raised when its list is compacted)
-  // and this half's list position lf (absolute slot index, lbase + fill); rows beyond
-  // N take +inf and never collect anything
+  // and the fill of this half's list; rows beyond N take +inf and never collect anything
   float th = row_ok ? theta[(int64_t)bh * N + row] : INFINITY;
   const int lrow = 32 * w + n;           // row within the workgroup
   const int lbase = lrow * LIST + hf * HSTR;
-  const int lcap = lbase + SEL_HALF;     // the spill slot
-  const int sink = ST_ROWS * LIST + tid;
-  int lf = lbase;
+  const uint32_t cap4 = 4u * (lbase + SEL_HALF);   // byte offset of the spill slot's score
+  int fill = 0;
+  const int kh = (K + 1) >> 1;           // a compacted row keeps its best kh in half 0, the rest in half 1
 
-  // Sort the lists of rows ra (lanes 0..31) and rb_ (lanes 32..63) of this wave as
-  // selection keys (lane j holds slot j of each half list), keep the best K (lane j =
-  // j-th best) and optionally write them back split over the two half lists.
+  // Sort the lists of rows ra (lanes 0..31) and rb2 (lanes 32..63) of this wave as
+  // selection keys (lane j holds slot j of each half list) and keep the best K (lane j =
+  // j-th best); with write_back they go back split over the two half lists.
   auto settle2 = [&](int ra, int rb2, bool write_back, uint64_t& lk, int& nvalid) {
     const int rw = hf ? rb2 : ra;
-    const int myfill = lf - lbase;
-    const int f0 = min(__shfl(myfill, rw), SEL_HALF), f1 = min(__shfl(myfill, 32 + rw), SEL_HALF);
+    const int f0 = min(__shfl(fill, rw), SEL_HALF), f1 = min(__shfl(fill, 32 + rw), SEL_HALF);
     const int base = (32 * w + rw) * LIST;
     uint64_t x = 0, y = 0;
     if (n < f0) x = make_key(cs[base + n], ci[base + n]);
@@ -578,8 +594,7 @@ __global__ void __launch_bounds__(256, NQ * NK > 4 ? 1 : 2) score_topk_kernel(co
     merge_intok(x, y, n, K);
     const uint64_t vm = __ballot(x != 0);
     nvalid = __popc(hf ? (uint32_t)(vm >> 32) : (uint32_t)vm);
-    if (write_back && n < K) {  // best (K+1)/2 to half 0, the rest to half 1
-      const int kh = (K + 1) >> 1;
+    if (write_back && n < K) {
       const int slot = n < kh ? n : HSTR + n - kh;
       cs[base + slot] = key_score(x);
       ci[base + slot] = (uint16_t)key_chunk(x);
@@ -587,46 +602,73 @@ __global__ void __launch_bounds__(256, NQ * NK > 4 ? 1 : 2) score_topk_kernel(co
     lk = x;
   };
 
-  const uint16_t* src = p2 + ((int64_t)bb * Hl + hh / (H / Hl)) * C * DE2;   // the landmark head's rows
-  u32x4_t pf[PL];
-  // chunks beyond Pmax load chunk Pmax-1 (finite; masked out below) and the last
-  // partial group of segments repeats the final segment: no divergent loads
-  auto load_tile = [&](int ct) {
+  // the tile's rows are contiguous: thread t moves 16-byte segments t + 256 u; the global
+  // and LDS offsets are the same for every tile (the final partial group repeats the last
+  // segment, whose duplicate store writes the same bytes)
+  int goff[PL], soff[PL];
 #pragma unroll
-    for (int u = 0; u < PL; ++u) {
-      const int it = min(tid + 256 * u, NSEG - 1);
-      const int e = it / SEGS, sg = it % SEGS;
-      const int c = min(ct * SEL_CT + e, Pmax - 1);
-      pf[u] = *reinterpret_cast<const u32x4_t*>(src + (int64_t)c * DE2 + 8 * sg);
-    }
+  for (int u = 0; u < PL; ++u) {
+    const int it = min(tid + 256 * u, NSEG - 1);
+    goff[u] = 8 * it;
+    soff[u] = (it / SEGS) * LDR + 8 * (it % SEGS);
+  }
+  // k' rows of the landmark head, padded to a multiple of KP_PAD zero rows: a tile never
+  // reads past them
+  const uint16_t* src = p2 + ((int64_t)bb * Hl + hh / (H / Hl)) * kp_rows(C) * DE2;
+  u32x4_t pf[PL];
+  auto load_tile = [&](int ct) {
+    const uint16_t* t = src + (int64_t)ct * SEL_CT * DE2;
+#pragma unroll
+    for (int u = 0; u < PL; ++u) pf[u] = *reinterpret_cast<const u32x4_t*>(t + goff[u]);
   };
   auto store_tile = [&]() {
 #pragma unroll
-    for (int u = 0; u < PL; ++u) {
-      const int it = min(tid + 256 * u, NSEG - 1);
-      const int e = it / SEGS, sg = it % SEGS;
-      *reinterpret_cast<u32x4_t*>(&kt[e * LDR + 8 * sg]) = pf[u];
-    }
+    for (int u = 0; u < PL; ++u) *reinterpret_cast<u32x4_t*>(&kt[soff[u]]) = pf[u];
   };
 
-  // the scores of the tile in LDS (chunk n of the tile is the A operand row)
+  // The MFMAs of a tile's scores (chunk n of the tile is the A operand row): per k-step
+  // the products (i, j) with i + j < NPROD, then b'.  after(m) runs after MFMA number m;
+  // the A operands of the next k-step are read from LDS one k-step ahead.
+  constexpr int PF = 1;   // k-steps of A operands read ahead
+  auto tile_mfma = [&](f32x16_t& a_, auto&& after) {
+    const uint16_t* krow = &kt[n * LDR];
+    auto opA = [&](int ks, int j) {
+      return *reinterpret_cast<const bf16x8_t*>(krow + j * D + (j ? P2_EXT : 0) + 16 * ks + 8 * hf);
+    };
+    bf16x8_t A[PF + 1][NK];
+#pragma unroll
+    for (int k0 = 0; k0 < PF && k0 < NKS; ++k0)
+#pragma unroll
+      for (int j = 0; j < NK; ++j) A[k0][j] = opA(k0, j);
+    const bf16x8_t ae = *reinterpret_cast<const bf16x8_t*>(krow + D + 8 * hf);
+    int m = 0;
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) {
+      if (ks + PF < NKS)
+#pragma unroll
+        for (int j = 0; j < NK; ++j) A[(ks + PF) % (PF + 1)][j] = opA(ks + PF, j);
+#pragma unroll
+      for (int j = 0; j < NK; ++j)
+#pragma unroll
+        for (int i = 0; i < NQ; ++i) {
+          if (i + j >= NPROD) continue;
+          a_ = mfma32(A[ks % (PF + 1)][j], qb[i][ks], a_);
+          after(m++);
+        }
+    }
+    a_ = mfma32(ae, qext, a_);  // + b'
+    after(m);
+  };
   auto tile_scores = [&]() {
     f32x16_t a_ = zero16();
-    const uint16_t* krow = &kt[n * LDR];
-#pragma unroll
-    for (int ks = 0; ks < NKS; ++ks)
-#pragma unroll
-      for (int j = 0; j < NK; ++j) {
-        const bf16x8_t a = *reinterpret_cast<const bf16x8_t*>(krow + j * D + (j ? P2_EXT : 0) + 16 * ks + 8 * hf);
-#pragma unroll
-        for (int i = 0; i < NQ; ++i)
-          if (i + j < (NQ > NK ? NQ : NK)) a_ = mfma32(a, qb[i][ks], a_);
-      }
-    return mfma32(*reinterpret_cast<const bf16x8_t*>(krow + D + 8 * hf), qext, a_);  // + b'
+    tile_mfma(a_, [](int) {});
+    return a_;
   };
 
   // Software pipeline: while tile ct's scores are tested and appended, the MFMAs of
   // tile ct + 1 (already staged in LDS) run; tile ct + 2 is in flight from memory.
+  // (A second LDS buffer, saving one barrier per tile, measured no faster: it leaves
+  // room for fewer candidate slots.)
   const int nct = (Pmax + SEL_CT - 1) / SEL_CT;
   if (nct > 0) {
     load_tile(0);
@@ -645,115 +687,115 @@ __global__ void __launch_bounds__(256, NQ * NK > 4 ? 1 : 2) score_topk_kernel(co
   for (int ct = 0; ct < nct; ++ct) {
     const bool more2 = ct + 2 < nct;
     if (more2) load_tile(ct + 2);
-    f32x16_t acc_next;
-    // candidates: s >= th goes to this lane's half list.  A full list takes further
-    // candidates in its spill slot (lost for now); the row is compacted after the tile
-    // and the lost ones are appended again against the raised threshold.
+    // register rr holds chunk cb + 8 (rr >> 2) + (rr & 3)
     const int cb = ct * SEL_CT + 4 * hf;
-    const int lf_start = lf;
-    const float th_old = th;
-    auto score_at = [&](int rr, auto masked_tag) {
-      float s = acc[rr];
-      if constexpr (decltype(masked_tag)::value) {
-        if (cb + 8 * (rr >> 2) + (rr & 3) >= prow) s = __builtin_nanf("");
-      }
-      return s;
-    };
-    auto append_all = [&](auto masked_tag) {
-#pragma unroll
-      for (int rr = 0; rr < 16; ++rr) {
-        const float s = score_at(rr, masked_tag);
-        const bool pass = s >= th;   // NaN never passes
-        const int pos = pass ? min(lf, lcap) : sink;
-        cs[pos] = s;
-        ci[pos] = (uint16_t)(cb + 8 * (rr >> 2) + (rr & 3));
-        lf += pass ? 1 : 0;
-      }
-    };
-    auto reappend_lost = [&](auto masked_tag) {
-      int running = lf_start;
-#pragma unroll
-      for (int rr = 0; rr < 16; ++rr) {
-        const float s = score_at(rr, masked_tag);
-        const bool was = s >= th_old;
-        running += was ? 1 : 0;
-        if (was && running > lcap && s >= th) {  // at most 16 after a compaction to <= 16
-          cs[lf] = s;
-          ci[lf] = (uint16_t)(cb + 8 * (rr >> 2) + (rr & 3));
-          ++lf;
+    const int fill0 = fill;
+    const float th0 = th;
+    const int lim = prow - cb;   // this row's chunks in the tile: offsets < lim
+    // append of register rr: only the lanes whose score passes run it.  MASKED tiles
+    // reach chunks >= Pmin, which are not past chunks of every row, and test the row's
+    // limit; the two kinds run as separate code.
+    f32x16_t an = zero16();
+    auto run = [&](auto masked_tag) {
+      constexpr bool MASKED = decltype(masked_tag)::value;
+      auto append = [&](int rr) {
+        const bool inside = !MASKED || 8 * (rr >> 2) + (rr & 3) < lim;
+        if (acc[rr] >= th && inside) {   // NaN never passes
+          const uint32_t a4 = min(4u * (lbase + fill), cap4);
+          *reinterpret_cast<float*>(lists + a4) = acc[rr];
+          *reinterpret_cast<uint16_t*>(lists + CI_OFS + (a4 >> 1)) = (uint16_t)(cb + 8 * (rr >> 2) + (rr & 3));
+          ++fill;
         }
-      }
+      };
+      tile_mfma(an, [&](int m) {
+        if (m < 16) append(m);
+        if (m == NMF - 1)
+          for (int rr = NMF; rr < 16; ++rr) append(rr);   // fewer MFMAs than registers
+      });
     };
-    // The MFMAs of tile ct + 1 (past the last tile they recompute the last one; never
-    // used) and the appends of tile ct in one block, interleaved one MFMA per score, so
-    // the matrix core works while the vector unit appends.
-    auto scores_and_append = [&](auto masked_tag) {
-      acc_next = tile_scores();
-      append_all(masked_tag);
-      if constexpr (NQ * NK <= 4)  // the fp32 path has too few registers left to interleave
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one MFMA
-        __builtin_amdgcn_sched_group_barrier(0x002, 10, 0);  // the VALU of one append
-        __builtin_amdgcn_sched_group_barrier(0x200, 2, 0);   // its two LDS writes
-      }
-    };
-    const bool masked = (ct + 1) * SEL_CT > Pmin;  // chunks >= Pmin are not past chunks of every row
-    if (masked)
-      scores_and_append(std::true_type{});
+    if ((ct + 1) * SEL_CT > Pmin)
+      run(std::true_type{});
     else
-      scores_and_append(std::false_type{});
-    const uint64_t ovf = __ballot(lf > lcap);
-    if (ovf) {  // rare: compact the rows with a full half list, then re-append what was lost
-      uint32_t rows_big = (uint32_t)ovf | (uint32_t)(ovf >> 32);
-      const int kh = (K + 1) >> 1;
-      while (rows_big) {
-        const int ra = __builtin_ctz(rows_big);
-        rows_big &= rows_big - 1;
-        int rb2 = ra;
-        const bool two = rows_big != 0;
-        if (two) {
-          rb2 = __builtin_ctz(rows_big);
-          rows_big &= rows_big - 1;
-        }
-        uint64_t lk;
-        int nv;
-        settle2(ra, rb2, true, lk, nv);
-        // new fills and thresholds of the two rows (half 0 of the wave did row ra, half 1 row rb2)
-        const int nva = __shfl(nv, 0), nvb = __shfl(nv, 32);
-        const uint64_t kka = __shfl(lk, K - 1), kkb = __shfl(lk, 32 + K - 1);
-        const float ka = kka ? key_score(kka) : -INFINITY, kb = kkb ? key_score(kkb) : -INFINITY;
-        if (n == ra) {
-          lf = lbase + (hf ? max(0, nva - kh) : min(nva, kh));
-          th = fmaxf(th, ka);
-        }
-        if (two && n == rb2) {
-          lf = lbase + (hf ? max(0, nvb - kh) : min(nvb, kh));
-          th = fmaxf(th, kb);
+      run(std::false_type{});
+    if (__ballot(fill > SEL_HALF)) {
+      // Rare: some half lists overflowed; the passes of this tile at slot index >=
+      // SEL_HALF went to the spill slot and are lost for now.  Compact the rows of the
+      // overflowed lanes (each half then holds at most 16), drop the lost ones that no
+      // longer pass the raised thresholds, append the rest while there is room, and
+      // repeat for lanes that filled up again.
+      uint32_t lost = 0;
+      {
+        int running = fill0;
+#pragma unroll
+        for (int rr = 0; rr < 16; ++rr) {
+          if (acc[rr] >= th0 && 8 * (rr >> 2) + (rr & 3) < lim) {
+            if (running >= SEL_HALF) lost |= 1u << rr;
+            ++running;
+          }
         }
       }
-      if (masked)
-        reappend_lost(std::true_type{});
-      else
-        reappend_lost(std::false_type{});
+      uint64_t ovf = __ballot(fill > SEL_HALF);
+      while (ovf) {
+        uint32_t rows_big = (uint32_t)ovf | (uint32_t)(ovf >> 32);
+        while (rows_big) {
+          const int ra = __builtin_ctz(rows_big);
+          rows_big &= rows_big - 1;
+          int rb2 = ra;
+          const bool two = rows_big != 0;
+          if (two) {
+            rb2 = __builtin_ctz(rows_big);
+            rows_big &= rows_big - 1;
+          }
+          uint64_t lk;
+          int nv;
+          settle2(ra, rb2, true, lk, nv);
+          // new fills and thresholds of the two rows (half 0 of the wave did row ra, half 1 row rb2)
+          const int nva = __shfl(nv, 0), nvb = __shfl(nv, 32);
+          const uint64_t kka = __shfl(lk, K - 1), kkb = __shfl(lk, 32 + K - 1);
+          const float ka = kka ? key_score(kka) : -INFINITY, kb = kkb ? key_score(kkb) : -INFINITY;
+          if (n == ra) {
+            fill = hf ? max(0, nva - kh) : min(nva, kh);
+            th = fmaxf(th, ka);
+          }
+          if (two && n == rb2) {
+            fill = hf ? max(0, nvb - kh) : min(nvb, kh);
+            th = fmaxf(th, kb);
+          }
+        }
+#pragma unroll
+        for (int rr = 0; rr < 16; ++rr) {
+          if ((lost >> rr) & 1u) {
+            const float sv = acc[rr];
+            if (!(sv >= th)) {
+              lost &= ~(1u << rr);
+            } else if (fill < SEL_HALF) {
+              cs[lbase + fill] = sv;
+              ci[lbase + fill] = (uint16_t)(cb + 8 * (rr >> 2) + (rr & 3));
+              ++fill;
+              lost &= ~(1u << rr);
+            }
+          }
+        }
+        if (lost) fill = SEL_HALF + 1;   // still lost ones: the half is full, compact again
+        ovf = __ballot(lost != 0);
+      }
     }
     __syncthreads();  // every wave is done with tile ct + 1 in LDS
     if (more2) store_tile();
     __syncthreads();
-    acc = acc_next;
+    acc = an;
   }
 
   // ---- final selection and output: eight row pairs (p, p + 16) at a time, the two half
   // lists of a row sorted as keys and merged to the best K; lane j of each half writes slot j
   constexpr int FR = NQ * NK > 4 ? 4 : 8;  // fewer at once where the score operands take more registers
-  const int myfill = lf - lbase;
 #pragma unroll 1
-  for (int p0 = 0; p0 < 16; p0 += FR) {
+  for (int p0r = 0; p0r < 16; p0r += FR) {
     uint64_t x[FR], y[FR];
 #pragma unroll
     for (int i = 0; i < FR; ++i) {
-      const int rw = hf ? p0 + i + 16 : p0 + i;
-      const int f0 = min(__shfl(myfill, rw), SEL_HALF), f1 = min(__shfl(myfill, 32 + rw), SEL_HALF);
+      const int rw = hf ? p0r + i + 16 : p0r + i;
+      const int f0 = min(__shfl(fill, rw), SEL_HALF), f1 = min(__shfl(fill, 32 + rw), SEL_HALF);
       const int base = (32 * w + rw) * LIST;
       x[i] = n < f0 ? make_key(cs[base + n], ci[base + n]) : 0ull;
       y[i] = n < f1 ? make_key(cs[base + HSTR + n], ci[base + HSTR + n]) : 0ull;
@@ -762,8 +804,8 @@ __global__ void __launch_bounds__(256, NQ * NK > 4 ? 1 : 2) score_topk_kernel(co
     sort32k_r<FR>(y, n);
 #pragma unroll
     for (int i = 0; i < FR; ++i) {  // the 32 best of both lists, a bitonic sequence
-      const uint64_t r = xl64<31>(y[i]);
-      x[i] = r > x[i] ? r : x[i];
+      const uint64_t rk = xl64<31>(y[i]);
+      x[i] = rk > x[i] ? rk : x[i];
     }
     cxk_r<16, FR>(x, (n & 16) == 0);
     cxk_r<8, FR>(x, (n & 8) == 0);
@@ -772,7 +814,7 @@ __global__ void __launch_bounds__(256, NQ * NK > 4 ? 1 : 2) score_topk_kernel(co
     cxk_r<1, FR>(x, (n & 1) == 0);
 #pragma unroll
     for (int i = 0; i < FR; ++i) {
-      const int rw = r0 + 32 * w + (hf ? p0 + i + 16 : p0 + i);
+      const int rw = r0 + 32 * w + (hf ? p0r + i + 16 : p0r + i);
       if (rw < N && n < K) {
         const int64_t o = ((int64_t)bh * N + rw) * K + n;
         const bool ok = x[i] != 0;
@@ -788,11 +830,11 @@ __global__ void __launch_bounds__(256, NQ * NK > 4 ? 1 : 2) score_topk_kernel(co
 // the extension [b'_hi, b'_mid, b'_lo, 0 ...] after plane 0, and (b) the threshold pass's
 // rows: bf16(k') followed by [b'_hi, b'_lo, TH_ABS, |k'_c| rounded up, 0 ...].  Both hold
 // each 16-element k-block in MFMA operand order: position 16 ks + 8 h + m holds element
-// kperm(ks, h, m).
+// kperm(ks, h, m).  Each (batch, landmark head) gets kp_rows(C) rows, those past C zero.
 template <int D, int NK>
 __global__ void __launch_bounds__(256) prep_kprime(const float* __restrict__ kc, const float* __restrict__ bc,
                                                    uint16_t* __restrict__ p2, uint16_t* __restrict__ t1,
-                                                   int64_t rows) {
+                                                   int64_t rows, int C, int Cp) {
   constexpr int SPR = D / 8;        // 16-byte segments (threads) per chunk row
   constexpr int RPB = 256 / SPR;    // chunk rows per workgroup pass
   constexpr int DE = D + TH_EXT;
@@ -801,12 +843,15 @@ __global__ void __launch_bounds__(256) prep_kprime(const float* __restrict__ kc,
   const int tid = threadIdx.x;
   const int sg = tid % SPR, ks = sg >> 1, h = sg & 1;
   for (int64_t base = (int64_t)blockIdx.x * RPB; base < rows; base += (int64_t)gridDim.x * RPB) {
-    const int64_t rw = base + tid / SPR;
+    const int64_t rw = base + tid / SPR;   // output row: (b, landmark head) * Cp + chunk
     const bool ok = rw < rows;
+    const int c = (int)(rw % Cp);
+    const bool real = ok && c < C;         // rows c >= C are zero padding
+    const int64_t sr = rw / Cp * C + c;    // source row of kc / bc
     float x[8];
-    if (ok) {
-      const float4 a = *reinterpret_cast<const float4*>(kc + rw * D + kperm(ks, h, 0));
-      const float4 b = *reinterpret_cast<const float4*>(kc + rw * D + kperm(ks, h, 4));
+    if (real) {
+      const float4 a = *reinterpret_cast<const float4*>(kc + sr * D + kperm(ks, h, 0));
+      const float4 b = *reinterpret_cast<const float4*>(kc + sr * D + kperm(ks, h, 4));
       x[0] = a.x, x[1] = a.y, x[2] = a.z, x[3] = a.w, x[4] = b.x, x[5] = b.y, x[6] = b.z, x[7] = b.w;
     } else {
 #pragma unroll
@@ -835,7 +880,7 @@ __global__ void __launch_bounds__(256) prep_kprime(const float* __restrict__ kc,
       if (sg < 2) {
         uint16_t e[8] = {0, 0, 0, 0, 0, 0, 0, 0}, f[8] = {0, 0, 0, 0, 0, 0, 0, 0};
         if (sg == 0) {
-          const float bv = bc[rw];
+          const float bv = real ? bc[sr] : 0.f;
           uint16_t sp3[3], sp2[2];
           split_bf16<3>(bv, sp3);
           split_bf16<2>(bv, sp2);
@@ -861,7 +906,7 @@ struct ScoreWs {
   size_t planes, t1, theta, total;
 };
 static ScoreWs score_ws(const Geom& g) {
-  const size_t rows = (size_t)g.B * g.Hl * g.C();   // k' rows: one per (b, landmark head, chunk)
+  const size_t rows = (size_t)g.B * g.Hl * kp_rows(g.C());   // k' rows per (b, landmark head): padded
   ScoreWs w;
   size_t off = 0;
   w.planes = off;
@@ -909,13 +954,14 @@ static void launch_st_d(const Geom& g, int Nq, const int32_t* pos0, const void* 
 template <int D>
 static void launch_prep(const Geom& g, const float* kc, const float* bc, uint16_t* planes, uint16_t* t1,
                         hipStream_t st) {
-  const int64_t rows = (int64_t)g.B * g.Hl * g.C();
+  const int Cp = kp_rows(g.C());
+  const int64_t rows = (int64_t)g.B * g.Hl * Cp;
   const int64_t rpb = 256 / (D / 8);
   const unsigned gs = (unsigned)std::min<int64_t>((rows + rpb - 1) / rpb, 16384);
   if (nk_of(g) == 3)
-    hipLaunchKernelGGL((prep_kprime<D, 3>), dim3(gs), dim3(256), 0, st, kc, bc, planes, t1, rows);
+    hipLaunchKernelGGL((prep_kprime<D, 3>), dim3(gs), dim3(256), 0, st, kc, bc, planes, t1, rows, g.C(), Cp);
   else
-    hipLaunchKernelGGL((prep_kprime<D, 2>), dim3(gs), dim3(256), 0, st, kc, bc, planes, t1, rows);
+    hipLaunchKernelGGL((prep_kprime<D, 2>), dim3(gs), dim3(256), 0, st, kc, bc, planes, t1, rows, g.C(), Cp);
 }
 
 hipError_t launch_score_topk(const Geom& g, int Nq, const int32_t* pos0, const void* q, const void* Dw, const void* Uw,
