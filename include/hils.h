@@ -87,7 +87,7 @@ typedef struct {
                      /* heads); the backward pass needs Hlmk == Hq                      */
   int32_t d;         /* head dimension: 64 or 128                                      */
   int32_t S;         /* chunk size: 64                                                 */
-  int32_t K;         /* top-K chunks per query: 1 <= K <= 32                            */
+  int32_t K;         /* top-K chunks per query: 1 <= K <= 64 (the backward: K <= 32)    */
   int32_t N;         /* prefill: tokens; decode: KV-cache capacity (row stride of k/v) */
   int32_t qcal_rank; /* Q-Cal rank r, 0 <= r <= 32 (0: no Q-Cal, q^ = q)                */
   int32_t io;        /* hils_dtype_t of q, k, v, o, lmk_q, qcal_D, qcal_U              */
@@ -171,7 +171,7 @@ int hils_attn_prefill_timed(const hils_dims_t* dims, const void* q, const void* 
  * chunk c < floor((seq_lens[b]-1)/S) (see hils_landmark_compress).
  * Writes o [B,Hq,d]; sel_idx_out (nullable) [B,Hq,K].
  * Limits of the library: N/S <= 16384 (decode and prefill); prefill also needs
- * B*Hq*N*K < 2^32.
+ * B*Hq*N*K < 2^32 and N*K < 2^26 (the latter only binds for K > 32).
  */
 int hils_attn_decode(const hils_dims_t* dims, const void* q, const void* k_cache, const void* v_cache,
                      const int32_t* seq_lens, const float* kc, const float* bc, const void* qcal_D,

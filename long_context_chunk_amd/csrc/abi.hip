@@ -45,7 +45,7 @@ int check_dims(const hils_dims_t* dims, hils::Geom& g) {
   if (s.io != HILS_F32 && s.io != HILS_BF16) return fail(HILS_E_UNSUPPORTED, "io dtype %d not supported", s.io);
   if (s.d != 64 && s.d != 128) return fail(HILS_E_UNSUPPORTED, "head dim %d not supported (64 or 128)", s.d);
   if (s.S != 64) return fail(HILS_E_UNSUPPORTED, "chunk size %d not supported (64)", s.S);
-  if (s.K > 32) return fail(HILS_E_UNSUPPORTED, "K=%d not supported (K <= 32)", s.K);
+  if (s.K > 64) return fail(HILS_E_UNSUPPORTED, "K=%d not supported (K <= 64)", s.K);
   if (s.qcal_rank > 32) return fail(HILS_E_UNSUPPORTED, "qcal_rank=%d not supported (<= 32)", s.qcal_rank);
   if (s.window < 0 || s.window % s.S != 0)
     return fail(HILS_E_INVAL, "window must be a non-negative multiple of S (window=%d S=%d)", s.window, s.S);
@@ -68,11 +68,13 @@ int check_pages(const hils::Geom& g, const int32_t* table, int32_t max_blocks, i
   return HILS_OK;
 }
 
-// Prefill-only limits: (row, slot) pair ids are 32-bit and the bucket histograms
-// hold at most 16384 chunks.
+// Prefill-only limits: (row, slot) pair ids are 32-bit, the bucket histograms hold at
+// most 16384 chunks, and a bucketing key holds an entry index of one (b, h) below 2^26.
 int check_prefill(const hils::Geom& g) {
   if ((int64_t)g.B * g.Hq * (int64_t)g.N * g.K >= ((int64_t)1 << 32))
     return fail(HILS_E_UNSUPPORTED, "prefill needs B*Hq*N*K < 2^32");
+  if ((int64_t)g.N * g.K >= ((int64_t)1 << 26))
+    return fail(HILS_E_UNSUPPORTED, "prefill needs N*K < 2^26 (N=%d K=%d)", g.N, g.K);
   if (g.C() > 16384) return fail(HILS_E_UNSUPPORTED, "prefill needs N/S <= 16384 (N=%d)", g.N);
   return HILS_OK;
 }
@@ -405,6 +407,7 @@ int hils_attn_prefill_backward(const hils_dims_t* dims, const void* q, const voi
   if (rc) return rc;
   if ((rc = check_prefill(g))) return rc;
   if (g.io != HILS_BF16) return fail(HILS_E_UNSUPPORTED, "the backward pass needs bf16 I/O");
+  if (g.K > 32) return fail(HILS_E_UNSUPPORTED, "the backward pass needs K <= 32 (K=%d)", g.K);
   if (g.Hl != g.Hq)
     return fail(HILS_E_UNSUPPORTED, "the backward pass needs one landmark head per query head (Hlmk=%d Hq=%d)", g.Hl,
                 g.Hq);

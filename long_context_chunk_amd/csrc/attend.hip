@@ -728,7 +728,9 @@ __global__ void __launch_bounds__(WIN_THREADS, 2) window_attend(const IO* __rest
 // (16 rows per wave ran 12% slower at 256K: more pages in use at once)
 constexpr int FZ_ROWS = 4;
 
-template <typename IO, int D>
+// KMAX: the largest K served (32, or 64 for 32 < K <= 64: scores for slots 64.. in a
+// second register per lane)
+template <typename IO, int D, int KMAX>
 __global__ void __launch_bounds__(256) fuse(const float* __restrict__ sel_score, const float* __restrict__ lse,
                                             const void* __restrict__ partial_v, IO* __restrict__ o, int N, int C,
                                             int K, int64_t rows, int nw) {
@@ -736,7 +738,7 @@ __global__ void __launch_bounds__(256) fuse(const float* __restrict__ sel_score,
   constexpr int EPL = 16 / sizeof(PT);   // partial elements per 16-byte load
   constexpr int LPS = D / EPL;           // lanes per output row
   constexpr int SPL = 64 / LPS;          // output rows per wave-wide load
-  constexpr int NSEG = (32 + 1 + SPL - 1) / SPL;  // loads per lane for up to 32 + 1 slots
+  constexpr int NSEG = (KMAX + 1 + SPL - 1) / SPL;  // loads per lane for up to KMAX + 1 slots
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int slot = lane / LPS, dpos = (lane % LPS) * EPL;
   const int64_t row0 = ((int64_t)blockIdx.x * 4 + w) * FZ_ROWS;
@@ -748,7 +750,7 @@ __global__ void __launch_bounds__(256) fuse(const float* __restrict__ sel_score,
   // the current two are reduced
   struct Rows {
     u32x4_t raw[2][NSEG];
-    float sc[2];
+    float sc[2], sc2[2];   // the score of slot lane, and of slot 64 + lane (KMAX = 64)
     int nsel[2];
     bool live[2];
   };
@@ -760,10 +762,14 @@ __global__ void __launch_bounds__(256) fuse(const float* __restrict__ sel_score,
       const int i = R.live[v2] ? (int)(row % N) : 0;
       const int ns = min(K, candidate_chunks(i, C, nw));
       R.nsel[v2] = ns;
-      R.sc[v2] = -INFINITY;
+      R.sc[v2] = R.sc2[v2] = -INFINITY;
       if (R.live[v2]) {
         if (lane < ns) R.sc[v2] = sel_score[row * K + lane];
         else if (lane == ns) R.sc[v2] = lse[row];
+        if constexpr (KMAX > 32) {
+          if (64 + lane < ns) R.sc2[v2] = sel_score[row * K + 64 + lane];
+          else if (64 + lane == ns) R.sc2[v2] = lse[row];
+        }
       }
 #pragma unroll
       for (int sg = 0; sg < NSEG; ++sg) {
@@ -781,16 +787,18 @@ __global__ void __launch_bounds__(256) fuse(const float* __restrict__ sel_score,
     for (int v2 = 0; v2 < 2; ++v2) {
       if (!R.live[v2]) continue;
       const int64_t row = row0 + u + v2;
-      const float M = wave_max(R.sc[v2]);
+      const float M = wave_max(KMAX > 32 ? fmaxf(R.sc[v2], R.sc2[v2]) : R.sc[v2]);
       const float wt = R.sc[v2] == -INFINITY ? 0.f : __expf(R.sc[v2] - M);
-      const float inv = 1.0f / wave_sum(wt);
+      const float wt2 = KMAX > 32 && R.sc2[v2] != -INFINITY ? __expf(R.sc2[v2] - M) : 0.f;
+      const float inv = 1.0f / wave_sum(wt + wt2);
       float acc[EPL];
 #pragma unroll
       for (int x = 0; x < EPL; ++x) acc[x] = 0.f;
 #pragma unroll
       for (int sg = 0; sg < NSEG; ++sg) {
         const int t = sg * SPL + slot;
-        const float wtt = __shfl(wt, t < 64 ? t : 0) * (t <= R.nsel[v2] ? 1.f : 0.f);
+        const float wtt = (KMAX > 32 && t >= 64 ? __shfl(wt2, t - 64) : __shfl(wt, t < 64 ? t : 0)) *
+                          (t <= R.nsel[v2] ? 1.f : 0.f);
         const u32x4_t rw = R.raw[v2][sg];
         if constexpr (sizeof(PT) == 2) {
           const uint32_t wd[4] = {rw.x, rw.y, rw.z, rw.w};
@@ -934,8 +942,12 @@ static hipError_t launch_attend_t(const Geom& g, const void* q, const void* k, c
   if (ev) hipEventRecord(ev[2], st);
   const int64_t rows = (int64_t)g.B * g.Hq * g.N;
   const int64_t nwg = (rows + 4 * FZ_ROWS - 1) / (4 * FZ_ROWS);
-  hipLaunchKernelGGL((fuse<IO, D>), dim3((unsigned)nwg), dim3(256), 0, st, scr, (const float*)lse,
-                     (const void*)partial, (IO*)o, g.N, C, g.K, rows, g.nw);
+  if (g.K > 32)
+    hipLaunchKernelGGL((fuse<IO, D, 64>), dim3((unsigned)nwg), dim3(256), 0, st, scr, (const float*)lse,
+                       (const void*)partial, (IO*)o, g.N, C, g.K, rows, g.nw);
+  else
+    hipLaunchKernelGGL((fuse<IO, D, 32>), dim3((unsigned)nwg), dim3(256), 0, st, scr, (const float*)lse,
+                       (const void*)partial, (IO*)o, g.N, C, g.K, rows, g.nw);
   if (ev) hipEventRecord(ev[3], st);
   return hipGetLastError();
 }

@@ -20,13 +20,14 @@
 #include <algorithm>
 
 #include "hils_common.h"
+#include "keylists.h"
 #include "kernels.h"
 
 namespace hils {
 
 constexpr int DS_CHUNKS = 1024;  // chunks scored per decode_scan workgroup
 constexpr int DS_MAX_SPLIT = 16;  // scan workgroups per (b, h): N/S <= 16384
-constexpr int DS_KEEP = 32;      // candidates kept per workgroup (>= K)
+constexpr int DS_KEEP = 64;      // candidate slots per workgroup (K <= 32 fills 32 of them)
 
 struct DecodeWs {
   size_t cand, sel_i, sel_s, nsel, part, sig, total;
@@ -129,7 +130,8 @@ HILS_DEV void qhat_to_lds(const IO* __restrict__ qv, const IO* __restrict__ Dw, 
   }
 }
 
-template <typename IO, int D>
+// KB (32 < K <= 64): each workgroup keeps its best 64 as a sorted 64-list (keylists.h)
+template <typename IO, int D, bool KB>
 __global__ void __launch_bounds__(256) decode_scan(const IO* __restrict__ q, const IO* __restrict__ Dw,
                                                    const IO* __restrict__ Uw, const float* __restrict__ kc,
                                                    const float* __restrict__ bc, const int32_t* __restrict__ seq_lens,
@@ -138,7 +140,7 @@ __global__ void __launch_bounds__(256) decode_scan(const IO* __restrict__ q, con
   __shared__ __align__(16) float qs[D];
   __shared__ float ts[32];
   __shared__ uint64_t keys[DS_CHUNKS];
-  __shared__ uint64_t wl[4][32];
+  __shared__ uint64_t wl[4][64];
   const int sp = blockIdx.x % nsplit, bh = blockIdx.x / nsplit;
   const int b = bh / Hq, h = bh % Hq;
   const int L = seq_lens[b];
@@ -201,54 +203,113 @@ __global__ void __launch_bounds__(256) decode_scan(const IO* __restrict__ q, con
     score(c0 + STEP, kb2, bb2);
   }
   __syncthreads();
-  // best 32 of this workgroup's chunks: each half-wave sorts 4 x 32 keys, the halves
-  // and then the four waves are merged
-  {
-    const int base = w * 256 + (lane >> 5) * 128 + (lane & 31);
-    uint64_t lk = keys[base];
-    dsort32(lk);
-    dmerge(lk, keys[base + 32]);
-    dmerge(lk, keys[base + 64]);
-    dmerge(lk, keys[base + 96]);
-    const uint64_t other = __shfl(lk, (lane & 31) + 32);
-    dmerge_sorted(lk, other);
-    if (lane < 32) wl[w][lane] = lk;
-  }
-  __syncthreads();
-  if (w == 0) {  // halves merge waves 0+1 and 2+3, then each other
-    uint64_t lk = wl[(lane >> 5) * 2][lane & 31];
-    dmerge_sorted(lk, wl[(lane >> 5) * 2 + 1][lane & 31]);
-    const uint64_t other = __shfl(lk, (lane & 31) + 32);
-    dmerge_sorted(lk, other);
-    if (lane < 32) cand[((int64_t)bh * nsplit + sp) * DS_KEEP + lane] = lk;
+  // best 32 (KB: 64) of this workgroup's chunks: each half-wave sorts 4 x 32 keys, the
+  // halves and then the four waves are merged
+  uint64_t* out = cand + ((int64_t)bh * nsplit + sp) * DS_KEEP;
+  const int j = lane & 31;
+  if constexpr (!KB) {
+    {
+      const int base = w * 256 + (lane >> 5) * 128 + j;
+      uint64_t lk = keys[base];
+      dsort32(lk);
+      dmerge(lk, keys[base + 32]);
+      dmerge(lk, keys[base + 64]);
+      dmerge(lk, keys[base + 96]);
+      const uint64_t other = __shfl(lk, j + 32);
+      dmerge_sorted(lk, other);
+      if (lane < 32) wl[w][lane] = lk;
+    }
+    __syncthreads();
+    if (w == 0) {  // halves merge waves 0+1 and 2+3, then each other
+      uint64_t lk = wl[(lane >> 5) * 2][j];
+      dmerge_sorted(lk, wl[(lane >> 5) * 2 + 1][j]);
+      const uint64_t other = __shfl(lk, j + 32);
+      dmerge_sorted(lk, other);
+      if (lane < 32) out[lane] = lk;
+    }
+  } else {
+    {
+      const int base = w * 256 + (lane >> 5) * 128 + j;
+      uint64_t hi = keys[base], lo = keys[base + 32], nk = keys[base + 64];
+      kl::sort(hi, j);
+      kl::sort(lo, j);
+      kl::split(hi, lo, j);
+      kl::sort(nk, j);
+      kl::insert64(hi, lo, nk, j);
+      nk = keys[base + 96];
+      kl::sort(nk, j);
+      kl::insert64(hi, lo, nk, j);
+      kl::merge64(hi, lo, __shfl(hi, j + 32), __shfl(lo, j + 32), j);
+      if (lane < 32) {
+        wl[w][lane] = hi;
+        wl[w][32 + lane] = lo;
+      }
+    }
+    __syncthreads();
+    if (w == 0) {  // halves merge waves 0+1 and 2+3, then each other
+      const int a = (lane >> 5) * 2;
+      uint64_t hi = wl[a][j], lo = wl[a][32 + j];
+      kl::merge64(hi, lo, wl[a + 1][j], wl[a + 1][32 + j], j);
+      kl::merge64(hi, lo, __shfl(hi, j + 32), __shfl(lo, j + 32), j);
+      if (lane < 32) {
+        out[lane] = hi;
+        out[32 + lane] = lo;
+      }
+    }
   }
 }
 
 // exact top-K of one (b, h) from the sorted candidate lists of its splits, rank order.
 // Half-wave x of wave w takes lists 2w + x and 2w + x + 8, the halves of each wave
 // merge, then wave 0 merges the four wave lists.
+template <bool KB>
 __global__ void __launch_bounds__(256) decode_merge(const uint64_t* __restrict__ cand,
                                                     const int32_t* __restrict__ seq_lens, int32_t* __restrict__ sel_i,
                                                     float* __restrict__ sel_s, int32_t* __restrict__ nsel_out,
                                                     int32_t* __restrict__ sel_user, int Hq, int C, int K, int nsplit,
                                                     int nw) {
   static_assert(DS_MAX_SPLIT == 16, "two lists per half-wave");
-  __shared__ uint64_t wl[4][32];
+  __shared__ uint64_t wl[4][64];
   const int bh = blockIdx.x, t = threadIdx.x, lane = t & 63, w = t >> 6;
+  const int j = lane & 31;
   const int li = 2 * w + (lane >> 5);
-  const uint64_t* cb = cand + (int64_t)bh * nsplit * DS_KEEP + (lane & 31);
-  uint64_t lk = li < nsplit ? cb[li * DS_KEEP] : 0ull;        // empty lists are all-zero keys
-  const uint64_t l2 = li + 8 < nsplit ? cb[(li + 8) * DS_KEEP] : 0ull;
-  dmerge_sorted(lk, l2);
-  dmerge_sorted(lk, __shfl(lk, (lane & 31) + 32));
-  if (lane < 32) wl[w][lane] = lk;
-  __syncthreads();
-  if (w != 0) return;
-  lk = wl[(lane >> 5) * 2][lane & 31];
-  dmerge_sorted(lk, wl[(lane >> 5) * 2 + 1][lane & 31]);
-  dmerge_sorted(lk, __shfl(lk, (lane & 31) + 32));
+  const uint64_t* cb = cand + (int64_t)bh * nsplit * DS_KEEP + j;
+  // the best 32 (KB: 64) of all splits, sorted, in half 0 of wave 0 (half 1 ends up
+  // with a list merged with itself); key of rank `lane`: hi of lane j < 32, lo of lane
+  // j of half 0 for ranks 32 + j
+  uint64_t hi, lo = 0;
+  auto ld = [&](int l, int off) { return l < nsplit ? cb[l * DS_KEEP + off] : 0ull; };  // empty lists: zero keys
+  if constexpr (!KB) {
+    hi = ld(li, 0);
+    dmerge_sorted(hi, ld(li + 8, 0));
+    dmerge_sorted(hi, __shfl(hi, j + 32));
+    if (lane < 32) wl[w][lane] = hi;
+    __syncthreads();
+    if (w != 0) return;
+    hi = wl[(lane >> 5) * 2][j];
+    dmerge_sorted(hi, wl[(lane >> 5) * 2 + 1][j]);
+    dmerge_sorted(hi, __shfl(hi, j + 32));
+  } else {
+    hi = ld(li, 0);
+    lo = ld(li, 32);
+    kl::merge64(hi, lo, ld(li + 8, 0), ld(li + 8, 32), j);
+    kl::merge64(hi, lo, __shfl(hi, j + 32), __shfl(lo, j + 32), j);
+    if (lane < 32) {
+      wl[w][lane] = hi;
+      wl[w][32 + lane] = lo;
+    }
+    __syncthreads();
+    if (w != 0) return;
+    const int a = (lane >> 5) * 2;
+    hi = wl[a][j];
+    lo = wl[a][32 + j];
+    kl::merge64(hi, lo, wl[a + 1][j], wl[a + 1][32 + j], j);
+    kl::merge64(hi, lo, __shfl(hi, j + 32), __shfl(lo, j + 32), j);
+  }
   const int L = seq_lens[bh / Hq];
   const int n = min(K, candidate_chunks(L - 1, C, nw));
+  const uint64_t lo0 = __shfl(lo, j);   // half 0's ranks 32 + j
+  const uint64_t lk = lane < 32 ? hi : lo0;
   if (lane < K) {
     const bool ok = lane < n && lk != 0;
     const int32_t ci = ok ? key_chunk(lk) : -1;
@@ -311,6 +372,7 @@ __global__ void __launch_bounds__(256) decode_attend(const IO* __restrict__ q, c
   } else {
     if (slot >= nsel[bh]) return;
     c = sel_i[(int64_t)bh * K + slot];
+    if (c < 0) return;   // never for a selection the merge wrote; no access before the cache
     nk = 64;
   }
   const int64_t row0 = pg.chunk_row(b, kvh, Hkv, N, c);
@@ -376,14 +438,15 @@ __global__ void __launch_bounds__(256) decode_attend(const IO* __restrict__ q, c
 
 // o = sum over the live slots of softmax(sig)_s part_s, one workgroup per (b, h): the n
 // selected chunks and the window's chunks from the own one back to chunk 0 (at most nw).
-// Lane s of every wave holds slot s's weight; the live slot rows are all loaded at once.
-template <typename IO, int D>
+// Lane s of every wave holds slot s's weight (MAXS = 128: slot 64 + s's too); the live
+// slot rows are all loaded at once.
+template <typename IO, int D, int MAXS>
 __global__ void __launch_bounds__(256) decode_combine(const float* __restrict__ part, const float* __restrict__ sig,
                                                       const int32_t* __restrict__ nsel,
                                                       const int32_t* __restrict__ seq_lens, IO* __restrict__ out,
                                                       int Hq, int K, int nw) {
   constexpr int G = 256 / D;               // slot groups
-  constexpr int MAXJ = (64 + G - 1) / G;   // K + nw <= 64 slots
+  constexpr int MAXJ = (MAXS + G - 1) / G;   // K + nw <= MAXS slots
   __shared__ float red[G][D];
   const int bh = blockIdx.x, t = threadIdx.x, lane = t & 63;
   const int n = nsel[bh];
@@ -399,14 +462,17 @@ __global__ void __launch_bounds__(256) decode_combine(const float* __restrict__ 
     const int s2 = g + j * G;
     pv[j] = live_slot(s2) ? pp[(int64_t)s2 * D + e] : 0.f;
   }
-  const bool live = live_slot(lane);
-  const float v = live ? sg[lane] : -INFINITY;
-  const float M = wave_max(v);
-  const float wt = live ? expf(v - M) : 0.f;
-  const float Z = wave_sum(wt);
+  const bool live = live_slot(lane), live2 = MAXS > 64 && live_slot(64 + lane);
+  const float v = live ? sg[lane] : -INFINITY, v2 = live2 ? sg[64 + lane] : -INFINITY;
+  const float M = wave_max(fmaxf(v, v2));
+  const float wt = live ? expf(v - M) : 0.f, wt2 = live2 ? expf(v2 - M) : 0.f;
+  const float Z = wave_sum(wt + wt2);
   float a = 0.f;
 #pragma unroll
-  for (int j = 0; j < MAXJ; ++j) a = fmaf(__shfl(wt, min(g + j * G, 63)), pv[j], a);
+  for (int j = 0; j < MAXJ; ++j) {
+    const int s2 = g + j * G;
+    a = fmaf(s2 < 64 ? __shfl(wt, s2) : __shfl(wt2, min(s2 - 64, 63)), pv[j], a);
+  }
   red[g][e] = a;
   __syncthreads();
   if (t < D) {
@@ -433,17 +499,30 @@ static hipError_t launch_decode_t(const Geom& g, const void* q, const void* kcac
   const int nsplit = std::max(1, nsplit_of(g));  // one (empty) split still writes the selection
   if (nsplit > DS_MAX_SPLIT) return hipErrorInvalidValue;  // N/S > 16384, rejected by the ABI first
   if (ev) (void)hipEventRecord(ev[0], st);
-  hipLaunchKernelGGL((decode_scan<IO, D>), dim3(BH * nsplit), dim3(256), 0, st, (const IO*)q, (const IO*)Dw,
-                     (const IO*)Uw, kc, bc, seq_lens, cand, g.Hq, g.Hl, C, g.r, nsplit, g.nw);
+  const bool kb = g.K > 32;   // keep 64 candidates per split
+  if (kb)
+    hipLaunchKernelGGL((decode_scan<IO, D, true>), dim3(BH * nsplit), dim3(256), 0, st, (const IO*)q, (const IO*)Dw,
+                       (const IO*)Uw, kc, bc, seq_lens, cand, g.Hq, g.Hl, C, g.r, nsplit, g.nw);
+  else
+    hipLaunchKernelGGL((decode_scan<IO, D, false>), dim3(BH * nsplit), dim3(256), 0, st, (const IO*)q,
+                       (const IO*)Dw, (const IO*)Uw, kc, bc, seq_lens, cand, g.Hq, g.Hl, C, g.r, nsplit, g.nw);
   if (ev) (void)hipEventRecord(ev[1], st);
-  hipLaunchKernelGGL(decode_merge, dim3(BH), dim3(256), 0, st, (const uint64_t*)cand, seq_lens, sel_i, sel_s, nsel,
-                     sel_user, g.Hq, C, g.K, nsplit, g.nw);
+  if (kb)
+    hipLaunchKernelGGL(decode_merge<true>, dim3(BH), dim3(256), 0, st, (const uint64_t*)cand, seq_lens, sel_i, sel_s,
+                       nsel, sel_user, g.Hq, C, g.K, nsplit, g.nw);
+  else
+    hipLaunchKernelGGL(decode_merge<false>, dim3(BH), dim3(256), 0, st, (const uint64_t*)cand, seq_lens, sel_i,
+                       sel_s, nsel, sel_user, g.Hq, C, g.K, nsplit, g.nw);
   if (ev) (void)hipEventRecord(ev[2], st);
   hipLaunchKernelGGL((decode_attend<IO, D>), dim3(BH * (g.K + g.nw)), dim3(256), 0, st, (const IO*)q,
                      (const IO*)kcache, (const IO*)vcache, seq_lens, sel_i, sel_s, nsel, part, sig, g.Hq, g.Hkv, g.N,
                      g.K, g.nw, pg);
-  hipLaunchKernelGGL((decode_combine<IO, D>), dim3(BH), dim3(256), 0, st, (const float*)part, (const float*)sig,
-                     (const int32_t*)nsel, seq_lens, (IO*)o, g.Hq, g.K, g.nw);
+  if (g.K + g.nw > 64)
+    hipLaunchKernelGGL((decode_combine<IO, D, 128>), dim3(BH), dim3(256), 0, st, (const float*)part,
+                       (const float*)sig, (const int32_t*)nsel, seq_lens, (IO*)o, g.Hq, g.K, g.nw);
+  else
+    hipLaunchKernelGGL((decode_combine<IO, D, 64>), dim3(BH), dim3(256), 0, st, (const float*)part,
+                       (const float*)sig, (const int32_t*)nsel, seq_lens, (IO*)o, g.Hq, g.K, g.nw);
   if (ev) (void)hipEventRecord(ev[3], st);
   return hipGetLastError();
 }

@@ -34,6 +34,7 @@
 #include <type_traits>
 
 #include "hils_common.h"
+#include "keylists.h"
 #include "kernels.h"
 
 namespace hils {
@@ -147,14 +148,18 @@ HILS_DEV void sort32f_r(float (&s)[R], int j, float pinf, float ninf) {
 #undef HILS_STAGE
 }
 
-// For R registers at once: the K-th largest of the 64 values {a, b} of each 32-lane half,
-// left in lane K - 1 of the half (a is overwritten with the half's 32 largest, sorted).
+// For R registers at once: the K-th largest (K <= 64) of the 64 values {a, b} of each
+// 32-lane half, left in lane (K - 1) & 31 of the half.  a is overwritten with the half's
+// 32 largest (K <= 32) or 32 smallest (K > 32), sorted best first: with a and b sorted,
+// lane j's larger (smaller) of a_j and b_(31-j) forms the top (bottom) half of the 64 as
+// a bitonic sequence.
 template <int R>
-HILS_DEV void kth_of_pairs_r(float (&a)[R], float (&b)[R], int j, float pinf, float ninf) {
+HILS_DEV void kth_of_pairs_r(float (&a)[R], float (&b)[R], int j, int K, float pinf, float ninf) {
   sort32f_r<R>(a, j, pinf, ninf);
   sort32f_r<R>(b, j, pinf, ninf);
+  const float side = K > 32 ? ninf : pinf;
 #pragma unroll
-  for (int i = 0; i < R; ++i) a[i] = __builtin_amdgcn_fmed3f(a[i], xl1<31>(b[i]), pinf);  // the 32 largest, bitonic
+  for (int i = 0; i < R; ++i) a[i] = __builtin_amdgcn_fmed3f(a[i], xl1<31>(b[i]), side);
   cx_stage<16, R>(a, (j & 16) == 0 ? pinf : ninf);
   cx_stage<8, R>(a, (j & 8) == 0 ? pinf : ninf);
   cx_stage<4, R>(a, (j & 4) == 0 ? pinf : ninf);
@@ -478,11 +483,12 @@ __global__ void __launch_bounds__(256, 3) score_threshold(const IO* __restrict__
   // theta per row: all 16 register rows (two rows each, one per half) at once
   float ninf = -INFINITY;
   asm volatile("" : "+v"(ninf));
-  kth_of_pairs_r<16>(m1, m2, n, pinf, ninf);
+  kth_of_pairs_r<16>(m1, m2, n, K, pinf, ninf);
+  const int kl = (K - 1) & 31;   // lane of the K-th within the half
 #pragma unroll
   for (int rr = 0; rr < 16; ++rr) {
     const int rw = r0 + 32 * w + acc_row(rr, hf);
-    const float t0 = readlane_f(m1[rr], K - 1), t1 = readlane_f(m1[rr], 32 + K - 1);
+    const float t0 = readlane_f(m1[rr], kl), t1 = readlane_f(m1[rr], 32 + kl);
     const float th = hf ? t1 : t0;
     if (n == 0 && rw < N) theta[(int64_t)bh * N + rw] = th;
   }
@@ -505,8 +511,13 @@ constexpr int SEL_CT = 32;     // chunks per column tile (single LDS buffer)
 constexpr int SEL_HALF = 32;   // candidate slots per half-row list (plus one spill slot)
 constexpr int P2_EXT = 16;     // extension elements after plane 0: [b'_hi, b'_mid, b'_lo, 0 ...]
 
-template <typename IO, int D, int NQ, int NK, bool QCAL>
-__global__ void __launch_bounds__(256, 2) score_topk_kernel(const IO* __restrict__ q, const IO* __restrict__ Dw,
+// KB (K > 32): half lists of SEL_HALF_KB slots and 64-entry sorted lists (two keys per
+// lane of a half-wave, keylists.h) for compaction and output; the LDS this takes leaves
+// one workgroup per CU.
+constexpr int SEL_HALF_KB = 48;
+
+template <typename IO, int D, int NQ, int NK, bool QCAL, bool KB>
+__global__ void __launch_bounds__(256, KB ? 1 : 2) score_topk_kernel(const IO* __restrict__ q, const IO* __restrict__ Dw,
                                                            const IO* __restrict__ Uw, const uint16_t* __restrict__ p2,
                                                            const float* __restrict__ theta,
                                                            int32_t* __restrict__ sel_idx,
@@ -519,7 +530,8 @@ __global__ void __launch_bounds__(256, 2) score_topk_kernel(const IO* __restrict
   constexpr int SEGS = DE2 / 8;
   constexpr int NSEG = SEL_CT * SEGS;
   constexpr int PL = (NSEG + 255) / 256;
-  constexpr int HSTR = SEL_HALF + 1;    // half-list stride: SEL_HALF slots + a spill slot
+  constexpr int SH = KB ? SEL_HALF_KB : SEL_HALF;   // slots per half list
+  constexpr int HSTR = SH + 1;          // half-list stride: SH slots + a spill slot
   constexpr int LIST = 2 * HSTR;        // slots per row
   constexpr int NPROD = NQ > NK ? NQ : NK;
   constexpr int NMF = [] {              // MFMAs per tile: the products i + j < NPROD, then b'
@@ -576,30 +588,59 @@ __global__ void __launch_bounds__(256, 2) score_topk_kernel(const IO* __restrict
   float th = row_ok ? theta[(int64_t)bh * N + row] : INFINITY;
   const int lrow = 32 * w + n;           // row within the workgroup
   const int lbase = lrow * LIST + hf * HSTR;
-  const uint32_t cap4 = 4u * (lbase + SEL_HALF);   // byte offset of the spill slot's score
+  const uint32_t cap4 = 4u * (lbase + SH);   // byte offset of the spill slot's score
   int fill = 0;
   const int kh = (K + 1) >> 1;           // a compacted row keeps its best kh in half 0, the rest in half 1
 
-  // Sort the lists of rows ra (lanes 0..31) and rb2 (lanes 32..63) of this wave as
-  // selection keys (lane j holds slot j of each half list) and keep the best K (lane j =
-  // j-th best); with write_back they go back split over the two half lists.
-  auto settle2 = [&](int ra, int rb2, bool write_back, uint64_t& lk, int& nvalid) {
-    const int rw = hf ? rb2 : ra;
-    const int f0 = min(__shfl(fill, rw), SEL_HALF), f1 = min(__shfl(fill, 32 + rw), SEL_HALF);
+  // The candidates of row rw (of this wave) as a sorted list of selection keys, best
+  // first: K <= 32: x, lane j of the half = rank j (the best 32); KB: the 64-list (x, y),
+  // ranks 0..31 and 32..63.  Half list 0 holds slots 0.., half list 1 the rest.
+  auto row_list = [&](int rw, uint64_t& x, uint64_t& y) {
+    const int f0 = min(__shfl(fill, rw), SH), f1 = min(__shfl(fill, 32 + rw), SH);
     const int base = (32 * w + rw) * LIST;
-    uint64_t x = 0, y = 0;
-    if (n < f0) x = make_key(cs[base + n], ci[base + n]);
-    if (n < f1) y = make_key(cs[base + HSTR + n], ci[base + HSTR + n]);
-    sort32k(x, n);
-    merge_intok(x, y, n, K);
-    const uint64_t vm = __ballot(x != 0);
-    nvalid = __popc(hf ? (uint32_t)(vm >> 32) : (uint32_t)vm);
-    if (write_back && n < K) {
-      const int slot = n < kh ? n : HSTR + n - kh;
-      cs[base + slot] = key_score(x);
-      ci[base + slot] = (uint16_t)key_chunk(x);
+    auto key = [&](int s2) { return make_key(cs[base + s2], ci[base + s2]); };
+    if constexpr (!KB) {
+      x = n < f0 ? key(n) : 0ull;
+      y = n < f1 ? key(HSTR + n) : 0ull;
+      sort32k(x, n);
+      merge_intok(x, y, n, 32);
+      y = 0;
+    } else {
+      // 96 slots as three 32-key registers: list 0 [0, 32), list 0 [32, 48) + list 1
+      // [0, 16), list 1 [16, 48)
+      static_assert(SH == 48, "");
+      x = n < f0 ? key(n) : 0ull;
+      y = n < 16 ? (32 + n < f0 ? key(32 + n) : 0ull) : (n - 16 < f1 ? key(HSTR + n - 16) : 0ull);
+      uint64_t z = 16 + n < f1 ? key(HSTR + 16 + n) : 0ull;
+      kl::sort(x, n);
+      kl::sort(y, n);
+      kl::sort(z, n);
+      kl::split(x, y, n);
+      kl::insert64(x, y, z, n);
     }
-    lk = x;
+  };
+  // Compact rows ra (lanes 0..31) and rb2 (lanes 32..63) of this wave: keep the best K,
+  // the best kh back in half list 0 and the rest in half list 1.  nvalid: the number
+  // kept; kkey: the K-th best key (0 if fewer than K), both per half.
+  auto settle2 = [&](int ra, int rb2, int& nvalid, uint64_t& kkey) {
+    const int rw = hf ? rb2 : ra;
+    const int base = (32 * w + rw) * LIST;
+    uint64_t x, y;
+    row_list(rw, x, y);
+    if (n >= K) x = 0;
+    if (n + 32 >= K) y = 0;
+    const uint64_t vx = __ballot(x != 0), vy = __ballot(y != 0);
+    nvalid = __popc(hf ? (uint32_t)(vx >> 32) : (uint32_t)vx) + __popc(hf ? (uint32_t)(vy >> 32) : (uint32_t)vy);
+    auto put = [&](int rank, uint64_t kk) {
+      if (rank < K) {
+        const int slot = rank < kh ? rank : HSTR + rank - kh;
+        cs[base + slot] = key_score(kk);
+        ci[base + slot] = (uint16_t)key_chunk(kk);
+      }
+    };
+    put(n, x);
+    if constexpr (KB) put(32 + n, y);
+    kkey = kl::rank_key(x, y, K - 1, lane);
   };
 
   // the tile's rows are contiguous: thread t moves 16-byte segments t + 256 u; the global
@@ -717,9 +758,9 @@ __global__ void __launch_bounds__(256, 2) score_topk_kernel(const IO* __restrict
       run(std::true_type{});
     else
       run(std::false_type{});
-    if (__ballot(fill > SEL_HALF)) {
-      // Rare: some half lists overflowed; the passes of this tile at slot index >=
-      // SEL_HALF went to the spill slot and are lost for now.  Compact the rows of the
+    if (__ballot(fill > SH)) {
+      // Rare: some half lists overflowed; the passes of this tile at slot index >= SH
+      // went to the spill slot and are lost for now.  Compact the rows of the
       // overflowed lanes (each half then holds at most 16), drop the lost ones that no
       // longer pass the raised thresholds, append the rest while there is room, and
       // repeat for lanes that filled up again.
@@ -729,12 +770,12 @@ __global__ void __launch_bounds__(256, 2) score_topk_kernel(const IO* __restrict
 #pragma unroll
         for (int rr = 0; rr < 16; ++rr) {
           if (acc[rr] >= th0 && 8 * (rr >> 2) + (rr & 3) < lim) {
-            if (running >= SEL_HALF) lost |= 1u << rr;
+            if (running >= SH) lost |= 1u << rr;
             ++running;
           }
         }
       }
-      uint64_t ovf = __ballot(fill > SEL_HALF);
+      uint64_t ovf = __ballot(fill > SH);
       while (ovf) {
         uint32_t rows_big = (uint32_t)ovf | (uint32_t)(ovf >> 32);
         while (rows_big) {
@@ -746,12 +787,12 @@ __global__ void __launch_bounds__(256, 2) score_topk_kernel(const IO* __restrict
             rb2 = __builtin_ctz(rows_big);
             rows_big &= rows_big - 1;
           }
-          uint64_t lk;
+          uint64_t kk;
           int nv;
-          settle2(ra, rb2, true, lk, nv);
+          settle2(ra, rb2, nv, kk);
           // new fills and thresholds of the two rows (half 0 of the wave did row ra, half 1 row rb2)
           const int nva = __shfl(nv, 0), nvb = __shfl(nv, 32);
-          const uint64_t kka = __shfl(lk, K - 1), kkb = __shfl(lk, 32 + K - 1);
+          const uint64_t kka = __shfl(kk, 0), kkb = __shfl(kk, 32);
           const float ka = kka ? key_score(kka) : -INFINITY, kb = kkb ? key_score(kkb) : -INFINITY;
           if (n == ra) {
             fill = hf ? max(0, nva - kh) : min(nva, kh);
@@ -768,7 +809,7 @@ __global__ void __launch_bounds__(256, 2) score_topk_kernel(const IO* __restrict
             const float sv = acc[rr];
             if (!(sv >= th)) {
               lost &= ~(1u << rr);
-            } else if (fill < SEL_HALF) {
+            } else if (fill < SH) {
               cs[lbase + fill] = sv;
               ci[lbase + fill] = (uint16_t)(cb + 8 * (rr >> 2) + (rr & 3));
               ++fill;
@@ -776,7 +817,7 @@ __global__ void __launch_bounds__(256, 2) score_topk_kernel(const IO* __restrict
             }
           }
         }
-        if (lost) fill = SEL_HALF + 1;   // still lost ones: the half is full, compact again
+        if (lost) fill = SH + 1;   // still lost ones: the half is full, compact again
         ovf = __ballot(lost != 0);
       }
     }
@@ -786,41 +827,60 @@ __global__ void __launch_bounds__(256, 2) score_topk_kernel(const IO* __restrict
     acc = an;
   }
 
-  // ---- final selection and output: eight row pairs (p, p + 16) at a time, the two half
-  // lists of a row sorted as keys and merged to the best K; lane j of each half writes slot j
-  constexpr int FR = NQ * NK > 4 ? 4 : 8;  // fewer at once where the score operands take more registers
+  // ---- final selection and output, rank order.  K <= 32: eight row pairs (p, p + 16) at
+  // a time, the two half lists of a row sorted as keys and merged to the best 32; lane j of
+  // each half writes slot j.  KB: one row pair at a time as 64-lists.
+  if constexpr (!KB) {
+    constexpr int FR = NQ * NK > 4 ? 4 : 8;  // fewer at once where the score operands take more registers
 #pragma unroll 1
-  for (int p0r = 0; p0r < 16; p0r += FR) {
-    uint64_t x[FR], y[FR];
+    for (int p0r = 0; p0r < 16; p0r += FR) {
+      uint64_t x[FR], y[FR];
 #pragma unroll
-    for (int i = 0; i < FR; ++i) {
-      const int rw = hf ? p0r + i + 16 : p0r + i;
-      const int f0 = min(__shfl(fill, rw), SEL_HALF), f1 = min(__shfl(fill, 32 + rw), SEL_HALF);
-      const int base = (32 * w + rw) * LIST;
-      x[i] = n < f0 ? make_key(cs[base + n], ci[base + n]) : 0ull;
-      y[i] = n < f1 ? make_key(cs[base + HSTR + n], ci[base + HSTR + n]) : 0ull;
-    }
-    sort32k_r<FR>(x, n);
-    sort32k_r<FR>(y, n);
-#pragma unroll
-    for (int i = 0; i < FR; ++i) {  // the 32 best of both lists, a bitonic sequence
-      const uint64_t rk = xl64<31>(y[i]);
-      x[i] = rk > x[i] ? rk : x[i];
-    }
-    cxk_r<16, FR>(x, (n & 16) == 0);
-    cxk_r<8, FR>(x, (n & 8) == 0);
-    cxk_r<4, FR>(x, (n & 4) == 0);
-    cxk_r<2, FR>(x, (n & 2) == 0);
-    cxk_r<1, FR>(x, (n & 1) == 0);
-#pragma unroll
-    for (int i = 0; i < FR; ++i) {
-      const int rw = r0 + 32 * w + (hf ? p0r + i + 16 : p0r + i);
-      if (rw < N && n < K) {
-        const int64_t o = ((int64_t)bh * N + rw) * K + n;
-        const bool ok = x[i] != 0;
-        sel_idx[o] = ok ? key_chunk(x[i]) : -1;
-        sel_score[o] = ok ? key_score(x[i]) : -INFINITY;
+      for (int i = 0; i < FR; ++i) {
+        const int rw = hf ? p0r + i + 16 : p0r + i;
+        const int f0 = min(__shfl(fill, rw), SH), f1 = min(__shfl(fill, 32 + rw), SH);
+        const int base = (32 * w + rw) * LIST;
+        x[i] = n < f0 ? make_key(cs[base + n], ci[base + n]) : 0ull;
+        y[i] = n < f1 ? make_key(cs[base + HSTR + n], ci[base + HSTR + n]) : 0ull;
       }
+      sort32k_r<FR>(x, n);
+      sort32k_r<FR>(y, n);
+#pragma unroll
+      for (int i = 0; i < FR; ++i) {  // the 32 best of both lists, a bitonic sequence
+        const uint64_t rk = xl64<31>(y[i]);
+        x[i] = rk > x[i] ? rk : x[i];
+      }
+      cxk_r<16, FR>(x, (n & 16) == 0);
+      cxk_r<8, FR>(x, (n & 8) == 0);
+      cxk_r<4, FR>(x, (n & 4) == 0);
+      cxk_r<2, FR>(x, (n & 2) == 0);
+      cxk_r<1, FR>(x, (n & 1) == 0);
+#pragma unroll
+      for (int i = 0; i < FR; ++i) {
+        const int rw = r0 + 32 * w + (hf ? p0r + i + 16 : p0r + i);
+        if (rw < N && n < K) {
+          const int64_t o = ((int64_t)bh * N + rw) * K + n;
+          const bool ok = x[i] != 0;
+          sel_idx[o] = ok ? key_chunk(x[i]) : -1;
+          sel_score[o] = ok ? key_score(x[i]) : -INFINITY;
+        }
+      }
+    }
+  } else {
+#pragma unroll 1
+    for (int p = 0; p < 16; ++p) {
+      uint64_t x, y;
+      row_list(hf ? p + 16 : p, x, y);
+      const int rw = r0 + 32 * w + (hf ? p + 16 : p);
+      auto out = [&](int rank, uint64_t kk) {
+        if (rw < N && rank < K) {
+          const int64_t o = ((int64_t)bh * N + rw) * K + rank;
+          sel_idx[o] = kk ? key_chunk(kk) : -1;
+          sel_score[o] = kk ? key_score(kk) : -INFINITY;
+        }
+      };
+      out(n, x);
+      out(32 + n, y);
     }
   }
 }
@@ -934,9 +994,14 @@ static void launch_st(const Geom& g, int Nq, const int32_t* pos0, const void* q,
   }
   if (ev) hipEventRecord(ev[0], st);
   if (items > 0) {
-    hipLaunchKernelGGL((score_topk_kernel<IO, D, NQ, NK, QCAL>), dim3(grid), dim3(256), 0, st, (const IO*)q,
-                       (const IO*)Dw, (const IO*)Uw, planes, (const float*)theta, si, ss, pos0, g.Hq, g.Hl, Nq, g.C(),
-                       g.K, g.r, NB, items, g.nw);
+    if (g.K > 32)
+      hipLaunchKernelGGL((score_topk_kernel<IO, D, NQ, NK, QCAL, true>), dim3(grid), dim3(256), 0, st, (const IO*)q,
+                         (const IO*)Dw, (const IO*)Uw, planes, (const float*)theta, si, ss, pos0, g.Hq, g.Hl, Nq,
+                         g.C(), g.K, g.r, NB, items, g.nw);
+    else
+      hipLaunchKernelGGL((score_topk_kernel<IO, D, NQ, NK, QCAL, false>), dim3(grid), dim3(256), 0, st, (const IO*)q,
+                         (const IO*)Dw, (const IO*)Uw, planes, (const float*)theta, si, ss, pos0, g.Hq, g.Hl, Nq,
+                         g.C(), g.K, g.r, NB, items, g.nw);
   }
 }
 

@@ -55,7 +55,7 @@ def test_workspace_bytes():
 
 
 @pytest.mark.parametrize("field,value,code", [
-    ("d", 96, hils.E_UNSUPPORTED), ("S", 32, hils.E_UNSUPPORTED), ("K", 0, hils.E_INVAL), ("K", 33, hils.E_UNSUPPORTED),
+    ("d", 96, hils.E_UNSUPPORTED), ("S", 32, hils.E_UNSUPPORTED), ("K", 0, hils.E_INVAL), ("K", 65, hils.E_UNSUPPORTED),
     ("Hkv", 3, hils.E_INVAL), ("Hlmk", 3, hils.E_INVAL), ("Hlmk", 2, hils.E_INVAL), ("B", 0, hils.E_INVAL), ("N", 0, hils.E_INVAL),
     ("io", 5, hils.E_UNSUPPORTED), ("qcal_rank", -1, hils.E_INVAL), ("qcal_rank", 64, hils.E_UNSUPPORTED),
     ("window", -64, hils.E_INVAL), ("window", 100, hils.E_INVAL), ("window", 33 * 64, hils.E_UNSUPPORTED),
@@ -219,6 +219,23 @@ def test_landmark_heads_per_kv_group_accepted_backward_rejects():
     fake = ctypes.c_void_p(0x1000)
     rc = lib.hils_attn_prefill_backward(ctypes.byref(d), *([fake] * 18), 1 << 40, None)
     assert rc == hils.E_UNSUPPORTED and b"landmark" in lib.hils_last_error()
+
+
+def test_k_above_32_limits():
+    """K up to 64 is valid for the forward calls; prefill also needs N*K < 2^26 (its
+    bucketing keys), and the backward pass keeps K <= 32; both say so before touching
+    the device."""
+    lib = hils.load()
+    d = hils.dims(1, 16, 4, 64, 4096, 64)
+    assert hils.workspace_bytes(d, hils.OP_PREFILL) > 0
+    assert hils.workspace_bytes(d, hils.OP_DECODE) > 0
+    fake = ctypes.c_void_p(0x1000)
+    rc = lib.hils_attn_prefill_backward(ctypes.byref(d), *([fake] * 18), 1 << 40, None)
+    assert rc == hils.E_UNSUPPORTED and b"K <= 32" in lib.hils_last_error()
+    big = hils.dims(1, 1, 1, 64, 16384 * 64, 64)   # N*K = 2^26
+    with pytest.raises(hils.HilsError):
+        hils.workspace_bytes(big, hils.OP_PREFILL)
+    assert hils.workspace_bytes(big, hils.OP_DECODE) > 0
 
 
 def test_score_topk_block_arguments():

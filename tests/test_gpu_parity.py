@@ -34,6 +34,10 @@ SMALL = [
     ("f32_d128_qcal", synth.Workload("f32_d128_qcal", B=2, Hq=4, Hkv=2, d=128, N=777, K=5, io=synth.F32,
                                      qcal_rank=16)),
     ("bf16_d64_B2_K32", synth.Workload("bf16_d64_B2_K32", B=2, Hq=4, Hkv=1, d=64, N=3000, K=32)),
+    # K above 32: 64-entry candidate lists in the selection and decode kernels
+    ("bf16_d64_K48", synth.Workload("bf16_d64_K48", B=1, Hq=4, Hkv=2, d=64, N=4000, K=48)),
+    ("bf16_d128_qcal_K64", synth.Workload("bf16_d128_qcal_K64", B=1, Hq=4, Hkv=1, d=128, N=6000, K=64, qcal_rank=8)),
+    ("f32_d64_K40", synth.Workload("f32_d64_K40", B=2, Hq=2, Hkv=1, d=64, N=3500, K=40, io=synth.F32)),
 ]
 
 
@@ -191,6 +195,8 @@ DECODE_SMALL = [
                                      seq_lens=[2999, 3000, 640], qcal_rank=8, planted_seqs=1)),
     ("f32_d64", synth.Workload("dec_f32_d64", B=2, Hq=2, Hkv=1, d=64, N=2048, K=4, io=synth.F32, decode=True,
                                seq_lens=[2048, 1111], planted=False)),
+    ("bf16_d128_K64", synth.Workload("dec_bf16_d128_K64", B=3, Hq=4, Hkv=2, d=128, N=70000, K=64, decode=True,
+                                     seq_lens=[70000, 5000, 4100], needle_frac=0.02)),
 ]
 
 
@@ -397,6 +403,9 @@ DECODE_WINDOW = [
                                          seq_lens=[4096, 2100, 2047], planted=False, window=2048)),
     ("bf16_d64_qcal_w192", synth.Workload("dw192", B=2, Hq=4, Hkv=4, d=64, N=3000, K=16, decode=True,
                                           seq_lens=[2999, 640], qcal_rank=8, planted_seqs=1, window=192)),
+    # K + W/S = 72 slots: the combine's second weight register
+    ("f32_d64_K56_w1024", synth.Workload("dw1024", B=2, Hq=2, Hkv=1, d=64, N=8192, K=56, io=synth.F32, decode=True,
+                                         seq_lens=[8192, 5000], planted=False, window=1024)),
 ]
 
 
@@ -580,7 +589,7 @@ def test_prefill_exact_ties_to_lower_chunk(name, w, twins):
     _say(name, "exact-tie rows", nt, summ)
 
 
-@pytest.mark.parametrize("K", [8, 32])
+@pytest.mark.parametrize("K", [8, 32, 64])
 def test_prefill_all_chunks_identical(K):
     """Every chunk identical: every score of a row ties, so every row with more than K
     candidates must select chunks 0..K-1.  Every candidate passes the selection kernel's
