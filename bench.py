@@ -142,7 +142,7 @@ def stage_roofline(w, cnt, stage_ms):
 KERNEL_SOURCES = {
     "compress": "compress.hip", "score_threshold": "score_topk.hip", "score_select": "score_topk.hip",
     "bucket": "attend.hip", "chunk_attend": "attend.hip", "own_attend": "attend.hip", "fuse": "attend.hip",
-    "decode_scan": "decode.hip", "decode_merge": "decode.hip", "decode_attend": "decode.hip", "decode_combine": "decode.hip",
+    "decode_scan": "decode.hip", "decode_merge": "decode.hip", "decode_scan_m": "decode.hip", "decode_attend": "decode.hip", "decode_combine": "decode.hip",
 }
 
 
@@ -413,6 +413,13 @@ def run_decode(wd, steps, warmup, seed, dense=False):
     e1.record()
     torch.cuda.synchronize()
     comp_ms = e0.elapsed_time(e1)
+    # the bf16 landmark mirror (built once per chunk, like k' and b'): the scan reads it
+    kcm = torch.empty(hils.mirror_shape(dm), dtype=torch.int16, device="cuda")
+    e0.record()
+    hils.landmark_mirror(dm, kc, bc, kcm)
+    e1.record()
+    torch.cuda.synchronize()
+    mirror_ms = e0.elapsed_time(e1)
     o = torch.empty_like(q)
     sel = torch.empty((wd.B, wd.Hq, wd.K), dtype=torch.int32, device="cuda")
     ws = hils.workspace(dm, hils.OP_DECODE)
@@ -421,19 +428,30 @@ def run_decode(wd, steps, warmup, seed, dense=False):
     # next step's first cache-allocating kernel pays for
     flush = torch.ones(128 << 20, dtype=torch.float32, device="cuda")
     flush_out = torch.empty((), dtype=torch.float32, device="cuda")
-    for _ in range(warmup):
-        hils.attn_decode(dm, q, kcache, vcache, lens, kc, bc, o, ws, sel_idx=sel)
-    torch.cuda.synchronize()
-    tot, stages = 0.0, {s: 0.0 for s in hils.DECODE_STAGES}
-    per = []
-    for _ in range(steps):
-        torch.sum(flush, dim=0, out=flush_out)   # evict k' and the KV chunks (untimed)
-        r = hils.attn_decode(dm, q, kcache, vcache, lens, kc, bc, o, ws, sel_idx=sel, timed=True)
-        for s_ in stages:
-            stages[s_] += r[s_] / steps
-        per.append(sum(r.values()) * 1e3)
-    us = sum(stages.values()) * 1e3
-    dist = {"median": float(np.median(per)), "p10": float(np.percentile(per, 10)), "p90": float(np.percentile(per, 90))}
+
+    def timed_steps(mirror):
+        for _ in range(warmup):
+            hils.attn_decode(dm, q, kcache, vcache, lens, kc, bc, o, ws, sel_idx=sel, kc_mirror=mirror)
+        torch.cuda.synchronize()
+        stages, per = {s: 0.0 for s in hils.DECODE_STAGES}, []
+        for _ in range(steps):
+            torch.sum(flush, dim=0, out=flush_out)   # evict k' and the KV chunks (untimed)
+            r = hils.attn_decode(dm, q, kcache, vcache, lens, kc, bc, o, ws, sel_idx=sel, timed=True,
+                                 kc_mirror=mirror)
+            for s_ in stages:
+                stages[s_] += r[s_] / steps
+            per.append(sum(r.values()) * 1e3)
+        dist = {"median": float(np.median(per)), "p10": float(np.percentile(per, 10)),
+                "p90": float(np.percentile(per, 90))}
+        return sum(stages.values()) * 1e3, stages, dist
+
+    # the exact fp32 scan (hils_attn_decode), then the mirror scan (hils_attn_decode_mirror):
+    # the same step, bit for bit
+    us_f, stages_f, dist_f = timed_steps(None)
+    sel_f, o_f = sel.clone(), o.clone()
+    us, stages, dist = timed_steps(kcm)
+    same = bool(torch.equal(sel, sel_f) and torch.equal(o.view(torch.int16), o_f.view(torch.int16)))
+    log("decode, fp32 scan: %.1f us/step (stages ms %s)" % (us_f, stages_f))
     # algorithmic bytes per step: q, o; k' and b' of every candidate chunk; the K/V rows of
     # the union of selected chunks per (sequence, KV head) plus the local window (own chunk)
     seln = sel.cpu().numpy()
@@ -447,11 +465,13 @@ def run_decode(wd, steps, warmup, seed, dense=False):
             u = set(seln[b, g * G:(g + 1) * G].ravel().tolist()) - {-1}
             kv_bytes += (len(u) * wd.S + (L - own * wd.S) + min(nw - 1, own) * wd.S) * wd.d * 2 * 2
     Ps = [min(wd.C, max(0, (int(L) - 1) // wd.S - nw + 1)) for L in x["seq_lens"]]
-    scan_bytes = sum(P * wd.Hlmk * (wd.d + 1) * 4 for P in Ps)
+    scan_bytes_f = sum(P * wd.Hlmk * (wd.d + 1) * 4 for P in Ps)          # fp32 k' and b'
+    scan_bytes = sum(P * wd.Hlmk * (wd.d * 2 + 8) for P in Ps)   # mirror: bf16 k', fp32 b' and norm bound
     total_bytes = scan_bytes + kv_bytes + 2 * 2 * wd.B * wd.Hq * wd.d
     step_gbs = total_bytes / (us * 1e-6) / 1e9
     scan_gbs = scan_bytes / (stages["scan"] * 1e-3) / 1e9
-    log("decode: %.1f us/step (stages ms %s)" % (us, stages))
+    scan_gbs_f = scan_bytes_f / (stages_f["scan"] * 1e-3) / 1e9
+    log("decode: %.1f us/step (stages ms %s), same result as the fp32 scan: %s" % (us, stages, same))
     dense_kv = sum(int(L) for L in x["seq_lens"]) * wd.Hkv * wd.d * 2 * 2
     dense_meas = None
     if dense and len(set(int(L) for L in x["seq_lens"])) == 1:
@@ -462,12 +482,20 @@ def run_decode(wd, steps, warmup, seed, dense=False):
         "workload": wd.name, "B": wd.B, "Hq": wd.Hq, "Hkv": wd.Hkv, "d": wd.d, "ctx": int(max(x["seq_lens"])),
         "K": wd.K, "window": wd.window, "us_per_step": us, "us_per_step_dist": dist,
         "stages_us": {k_: v_ * 1e3 for k_, v_ in stages.items()},
-        "one_off_compress_ms": comp_ms,
+        "scan": "bf16 landmark mirror + exact fp32 rescoring (hils_attn_decode_mirror)",
+        "one_off_compress_ms": comp_ms, "one_off_mirror_ms": mirror_ms,
         "roofline": {"bound": "hbm", "achieved": scan_gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                     "frac": scan_gbs / PEAK_HBM_GBS, "kernel": "decode_scan",
-                     "traffic": measured_traffic("decode_scan", wd.name)},
+                     "frac": scan_gbs / PEAK_HBM_GBS, "kernel": "decode_scan_m",
+                     "traffic": measured_traffic("decode_scan_m", wd.name)},
         "step_hbm": {"algorithmic_bytes": total_bytes, "achieved_GBs": step_gbs, "frac": step_gbs / PEAK_HBM_GBS,
                      "kv_union_bytes": kv_bytes, "kprime_bytes": scan_bytes},
+        "fp32_scan": {"us_per_step": us_f, "us_per_step_dist": dist_f,
+                      "stages_us": {k_: v_ * 1e3 for k_, v_ in stages_f.items()},
+                      "roofline": {"bound": "hbm", "achieved": scan_gbs_f, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                                   "frac": scan_gbs_f / PEAK_HBM_GBS, "kernel": "decode_scan",
+                                   "traffic": measured_traffic("decode_scan", wd.name)},
+                      "kprime_bytes": scan_bytes_f},
+        "mirror_result_identical": same,
         "dense_kv_bytes": dense_kv, "dense_us_at_hbm_peak": dense_kv / (PEAK_HBM_GBS * 1e9) * 1e6,
         "dense_measured": dense_meas,
     }

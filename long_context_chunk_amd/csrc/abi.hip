@@ -235,7 +235,7 @@ int run_prefill(const hils_dims_t* dims, const void* q, const void* k, const voi
 int run_decode(const hils_dims_t* dims, const void* q, const void* k_cache, const void* v_cache,
                const int32_t* seq_lens, const float* kc, const float* bc, const void* qcal_D, const void* qcal_U,
                int32_t* sel_idx_out, void* o, void* ws, size_t ws_bytes, void* stream, float* stage_ms,
-               hils::KvPages pg = hils::KvPages()) {
+               hils::KvPages pg = hils::KvPages(), const uint16_t* kcm = nullptr) {
   hils::Geom g;
   int rc = check_dims(dims, g);
   if (rc) return rc;
@@ -254,8 +254,8 @@ int run_decode(const hils_dims_t* dims, const void* q, const void* k_cache, cons
   if (stage_ms)
     for (int i = 0; i <= NS && e == hipSuccess; ++i) e = hipEventCreate(&ev[i]);
   if (e == hipSuccess)
-    e = hils::launch_decode(g, q, k_cache, v_cache, seq_lens, kc, bc, qcal_D, qcal_U, sel_idx_out, o, ws, ws_bytes,
-                            st, stage_ms ? ev : nullptr, pg);
+    e = hils::launch_decode(g, q, k_cache, v_cache, seq_lens, kc, bc, kcm, qcal_D, qcal_U, sel_idx_out, o, ws,
+                            ws_bytes, st, stage_ms ? ev : nullptr, pg);
   if (stage_ms) {
     if (e == hipSuccess) e = hipEventSynchronize(ev[NS]);
     for (int i = 0; i < NS && e == hipSuccess; ++i) e = hipEventElapsedTime(&stage_ms[i], ev[i], ev[i + 1]);
@@ -264,6 +264,15 @@ int run_decode(const hils_dims_t* dims, const void* q, const void* k_cache, cons
   }
   if (e != hipSuccess) return hip_fail(e, "hils_attn_decode");
   g_err[0] = 0;
+  return HILS_OK;
+}
+
+// The mirror decode calls need the mirror whenever the cache has a complete chunk.
+int check_mirror(const hils_dims_t* dims, const uint16_t* kcm) {
+  hils::Geom g;
+  int rc = check_dims(dims, g);
+  if (rc) return rc;
+  if (g.C() > 0 && !kcm) return fail(HILS_E_INVAL, "kc_mirror must be non-NULL");
   return HILS_OK;
 }
 
@@ -328,6 +337,46 @@ int hils_attn_decode_timed(const hils_dims_t* dims, const void* q, const void* k
   if (!stage_ms) return fail(HILS_E_INVAL, "stage_ms must be non-NULL");
   return run_decode(dims, q, k_cache, v_cache, seq_lens, kc, bc, qcal_D, qcal_U, sel_idx_out, o, ws, ws_bytes, stream,
                     stage_ms);
+}
+
+int hils_landmark_mirror(const hils_dims_t* dims, const float* kc, const float* bc, int32_t c_begin, int32_t c_end,
+                         uint16_t* kc_mirror, void* stream) {
+  hils::Geom g;
+  int rc = check_dims(dims, g);
+  if (rc) return rc;
+  if (c_begin < 0 || c_end < c_begin || c_end > g.C())
+    return fail(HILS_E_INVAL, "need 0 <= c_begin <= c_end <= N/S (c_begin=%d c_end=%d N/S=%d)", c_begin, c_end, g.C());
+  if (c_end == c_begin) {
+    g_err[0] = 0;
+    return HILS_OK;
+  }
+  if (!kc || !bc || !kc_mirror) return fail(HILS_E_INVAL, "kc, bc and kc_mirror must be non-NULL");
+  hipError_t e = hils::launch_mirror(g, kc, bc, kc_mirror, c_begin, c_end, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "hils_landmark_mirror");
+  g_err[0] = 0;
+  return HILS_OK;
+}
+
+int hils_attn_decode_mirror(const hils_dims_t* dims, const void* q, const void* k_cache, const void* v_cache,
+                            const int32_t* seq_lens, const float* kc, const float* bc, const uint16_t* kc_mirror,
+                            const void* qcal_D, const void* qcal_U, int32_t* sel_idx_out, void* o, void* ws,
+                            size_t ws_bytes, void* stream) {
+  int rc;
+  if ((rc = check_mirror(dims, kc_mirror))) return rc;
+  return run_decode(dims, q, k_cache, v_cache, seq_lens, kc, bc, qcal_D, qcal_U, sel_idx_out, o, ws, ws_bytes, stream,
+                    nullptr, hils::KvPages(), kc_mirror);
+}
+
+int hils_attn_decode_mirror_timed(const hils_dims_t* dims, const void* q, const void* k_cache, const void* v_cache,
+                                  const int32_t* seq_lens, const float* kc, const float* bc,
+                                  const uint16_t* kc_mirror, const void* qcal_D, const void* qcal_U,
+                                  int32_t* sel_idx_out, void* o, void* ws, size_t ws_bytes, void* stream,
+                                  float* stage_ms) {
+  if (!stage_ms) return fail(HILS_E_INVAL, "stage_ms must be non-NULL");
+  int rc;
+  if ((rc = check_mirror(dims, kc_mirror))) return rc;
+  return run_decode(dims, q, k_cache, v_cache, seq_lens, kc, bc, qcal_D, qcal_U, sel_idx_out, o, ws, ws_bytes, stream,
+                    stage_ms, hils::KvPages(), kc_mirror);
 }
 
 int hils_attn_decode_noalloc(const hils_dims_t* dims, const void* q, const void* k_cache, const void* v_cache,

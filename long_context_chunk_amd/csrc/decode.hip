@@ -28,6 +28,9 @@ namespace hils {
 constexpr int DS_CHUNKS = 1024;  // chunks scored per decode_scan workgroup
 constexpr int DS_MAX_SPLIT = 16;  // scan workgroups per (b, h): N/S <= 16384
 constexpr int DS_KEEP = 64;      // candidate slots per workgroup (K <= 32 fills 32 of them)
+#ifndef DSM_UNR
+#define DSM_UNR 2                // chunk passes per register buffer of the mirror scan
+#endif
 
 struct DecodeWs {
   size_t cand, sel_i, sel_s, nsel, part, sig, total;
@@ -105,6 +108,62 @@ HILS_DEV void dmerge_sorted(uint64_t& lk, uint64_t nk) {
 HILS_DEV void dmerge(uint64_t& lk, uint64_t nk) {
   dsort32(nk);
   dmerge_sorted(lk, nk);
+}
+
+// The best 32 of the 1024 keys in LDS, sorted, in half 0 of wave 0 (256 threads; every
+// thread calls it): each half-wave sorts 4 x 32 keys, the halves of a wave and then the
+// four waves are merged.
+HILS_DEV uint64_t best32_of_1024(const uint64_t* keys, uint64_t (*wl)[64]) {
+  const int t = threadIdx.x, lane = t & 63, w = t >> 6, j = lane & 31;
+  {
+    const int base = w * 256 + (lane >> 5) * 128 + j;
+    uint64_t lk = keys[base];
+    dsort32(lk);
+    dmerge(lk, keys[base + 32]);
+    dmerge(lk, keys[base + 64]);
+    dmerge(lk, keys[base + 96]);
+    dmerge_sorted(lk, __shfl(lk, j + 32));
+    if (lane < 32) wl[w][lane] = lk;
+  }
+  __syncthreads();
+  uint64_t lk = wl[(lane >> 5) * 2][j];   // halves merge waves 0+1 and 2+3, then each other
+  dmerge_sorted(lk, wl[(lane >> 5) * 2 + 1][j]);
+  dmerge_sorted(lk, __shfl(lk, j + 32));
+  __syncthreads();   // wl may be reused
+  return lk;
+}
+
+// The best 64 of the 1024 keys in LDS, as a sorted 64-list (hi, lo) in half 0 of wave 0
+// (256 threads; every thread calls it): each half-wave sorts 4 x 32 keys into a 64-list,
+// the halves of a wave and then the four waves are merged.
+HILS_DEV void best64_of_1024(const uint64_t* keys, uint64_t (*wl)[64], uint64_t& hi, uint64_t& lo) {
+  const int t = threadIdx.x, lane = t & 63, w = t >> 6, j = lane & 31;
+  {
+    const int base = w * 256 + (lane >> 5) * 128 + j;
+    hi = keys[base];
+    lo = keys[base + 32];
+    uint64_t nk = keys[base + 64];
+    kl::sort(hi, j);
+    kl::sort(lo, j);
+    kl::split(hi, lo, j);
+    kl::sort(nk, j);
+    kl::insert64(hi, lo, nk, j);
+    nk = keys[base + 96];
+    kl::sort(nk, j);
+    kl::insert64(hi, lo, nk, j);
+    kl::merge64(hi, lo, __shfl(hi, j + 32), __shfl(lo, j + 32), j);
+    if (lane < 32) {
+      wl[w][lane] = hi;
+      wl[w][32 + lane] = lo;
+    }
+  }
+  __syncthreads();
+  const int a = (lane >> 5) * 2;   // wave 0: halves merge waves 0+1 and 2+3, then each other
+  hi = wl[a][j];
+  lo = wl[a][32 + j];
+  kl::merge64(hi, lo, wl[a + 1][j], wl[a + 1][32 + j], j);
+  kl::merge64(hi, lo, __shfl(hi, j + 32), __shfl(lo, j + 32), j);
+  __syncthreads();   // wl may be reused
 }
 
 // q^ = q + U (D q) for one head into LDS (fp32).  256 threads.
@@ -194,13 +253,25 @@ __global__ void __launch_bounds__(256) decode_scan(const IO* __restrict__ q, con
       if (sub == 0) keys[c - c_beg] = c < c_end ? make_key(fmaf(s, tau, bv[u]), c) : 0ull;
     }
   };
+  // every load is issued whether or not its chunks are live (they clamp in bounds): with a
+  // fixed number of loads in flight the compiler waits for exactly the buffer it uses next
   static_assert(DS_CHUNKS % (2 * STEP) == 0, "");
-  if (c_beg < c_end) load(c_beg, ka, ba);
-  for (int c0 = c_beg; c0 < c_beg + DS_CHUNKS; c0 += 2 * STEP) {
-    if (c0 + STEP < c_end) load(c0 + STEP, kb2, bb2);
+  constexpr int NIT = DS_CHUNKS / (2 * STEP);
+  if (c_beg < c_end) {   // uniform
+    load(c_beg, ka, ba);
+    for (int it = 0; it < NIT - 1; ++it) {
+      const int c0 = c_beg + it * 2 * STEP;
+      load(c0 + STEP, kb2, bb2);
+      score(c0, ka, ba);
+      load(c0 + 2 * STEP, ka, ba);
+      score(c0 + STEP, kb2, bb2);
+    }
+    const int c0 = c_beg + (NIT - 1) * 2 * STEP;
+    load(c0 + STEP, kb2, bb2);
     score(c0, ka, ba);
-    if (c0 + 2 * STEP < c_end) load(c0 + 2 * STEP, ka, ba);
     score(c0 + STEP, kb2, bb2);
+  } else {
+    for (int x = threadIdx.x; x < DS_CHUNKS; x += 256) keys[x] = 0ull;
   }
   __syncthreads();
   // best 32 (KB: 64) of this workgroup's chunks: each half-wave sorts 4 x 32 keys, the
@@ -208,53 +279,14 @@ __global__ void __launch_bounds__(256) decode_scan(const IO* __restrict__ q, con
   uint64_t* out = cand + ((int64_t)bh * nsplit + sp) * DS_KEEP;
   const int j = lane & 31;
   if constexpr (!KB) {
-    {
-      const int base = w * 256 + (lane >> 5) * 128 + j;
-      uint64_t lk = keys[base];
-      dsort32(lk);
-      dmerge(lk, keys[base + 32]);
-      dmerge(lk, keys[base + 64]);
-      dmerge(lk, keys[base + 96]);
-      const uint64_t other = __shfl(lk, j + 32);
-      dmerge_sorted(lk, other);
-      if (lane < 32) wl[w][lane] = lk;
-    }
-    __syncthreads();
-    if (w == 0) {  // halves merge waves 0+1 and 2+3, then each other
-      uint64_t lk = wl[(lane >> 5) * 2][j];
-      dmerge_sorted(lk, wl[(lane >> 5) * 2 + 1][j]);
-      const uint64_t other = __shfl(lk, j + 32);
-      dmerge_sorted(lk, other);
-      if (lane < 32) out[lane] = lk;
-    }
+    const uint64_t lk = best32_of_1024(keys, wl);
+    if (lane < 32 && w == 0) out[lane] = lk;
   } else {
-    {
-      const int base = w * 256 + (lane >> 5) * 128 + j;
-      uint64_t hi = keys[base], lo = keys[base + 32], nk = keys[base + 64];
-      kl::sort(hi, j);
-      kl::sort(lo, j);
-      kl::split(hi, lo, j);
-      kl::sort(nk, j);
-      kl::insert64(hi, lo, nk, j);
-      nk = keys[base + 96];
-      kl::sort(nk, j);
-      kl::insert64(hi, lo, nk, j);
-      kl::merge64(hi, lo, __shfl(hi, j + 32), __shfl(lo, j + 32), j);
-      if (lane < 32) {
-        wl[w][lane] = hi;
-        wl[w][32 + lane] = lo;
-      }
-    }
-    __syncthreads();
-    if (w == 0) {  // halves merge waves 0+1 and 2+3, then each other
-      const int a = (lane >> 5) * 2;
-      uint64_t hi = wl[a][j], lo = wl[a][32 + j];
-      kl::merge64(hi, lo, wl[a + 1][j], wl[a + 1][32 + j], j);
-      kl::merge64(hi, lo, __shfl(hi, j + 32), __shfl(lo, j + 32), j);
-      if (lane < 32) {
-        out[lane] = hi;
-        out[32 + lane] = lo;
-      }
+    uint64_t hi, lo;
+    best64_of_1024(keys, wl, hi, lo);
+    if (lane < 32 && w == 0) {
+      out[lane] = hi;
+      out[32 + lane] = lo;
     }
   }
 }
@@ -483,10 +515,295 @@ __global__ void __launch_bounds__(256) decode_combine(const float* __restrict__ 
   }
 }
 
+// ---------------------------------------------------------------- landmark mirror
+// A bf16 mirror of the landmark cache for the decode scan, in two planes: the rows
+// bf16(k'_c) [B*Hlmk*C, d] (each row 128 or 256 bytes, so the scan reads whole cache
+// lines), then per row the pair (b'_c, an upper bound of ||k'_c||_2) as fp32 [B*Hlmk*C, 2].
+template <int D>
+__global__ void __launch_bounds__(256) mirror_build(const float* __restrict__ kc, const float* __restrict__ bc,
+                                                    uint16_t* __restrict__ kcm, int C, int c_begin, int n,
+                                                    int64_t rows, int64_t all_rows) {
+  constexpr int TPR = D / 8;        // threads per row, 8 elements each
+  constexpr int RPB = 256 / TPR;    // rows per workgroup pass
+  const int t = threadIdx.x, sub = t % TPR;
+  for (int64_t base = (int64_t)blockIdx.x * RPB; base < rows; base += (int64_t)gridDim.x * RPB) {
+    const int64_t it = base + t / TPR;   // item: (b, l) * n + chunk offset
+    const bool ok = it < rows;
+    const int64_t r = ok ? (it / n) * C + c_begin + it % n : 0;   // row of kc / the mirror
+    float x[8];
+    if (ok) {
+      const float4 a = *reinterpret_cast<const float4*>(kc + r * D + 8 * sub);
+      const float4 b = *reinterpret_cast<const float4*>(kc + r * D + 8 * sub + 4);
+      x[0] = a.x, x[1] = a.y, x[2] = a.z, x[3] = a.w, x[4] = b.x, x[5] = b.y, x[6] = b.z, x[7] = b.w;
+    } else {
+#pragma unroll
+      for (int m = 0; m < 8; ++m) x[m] = 0.f;
+    }
+    float s2 = 0.f;
+#pragma unroll
+    for (int m = 0; m < 8; ++m) s2 = fmaf(x[m], x[m], s2);
+#pragma unroll
+    for (int o = TPR / 2; o >= 1; o >>= 1) s2 += __shfl_xor(s2, o);
+    if (ok) {
+      uint16_t* dst = kcm + r * D;
+      u32x4_t v;
+      v.x = pack_bf16x2(x[0], x[1]);
+      v.y = pack_bf16x2(x[2], x[3]);
+      v.z = pack_bf16x2(x[4], x[5]);
+      v.w = pack_bf16x2(x[6], x[7]);
+      *reinterpret_cast<u32x4_t*>(dst + 8 * sub) = v;
+      if (sub == 0) {
+        // the fp32 sum of squares errs by at most D 2^-24 relative; the margin covers it
+        const float nrm = sqrtf(s2) * (1.0f + 1.0f / 4096.0f) + 1e-30f;
+        reinterpret_cast<u32x2_t*>(kcm + all_rows * D)[r] = u32x2_t{__float_as_uint(bc[r]), __float_as_uint(nrm)};
+      }
+    }
+  }
+}
+
+// The decode scan over the mirror.  Per chunk, from the mirror row, a lower and an upper
+// bound of the exact score, L <= s <= U with s = fmaf(q^ . k', tau, b') as decode_scan
+// computes it in fp32.  Within the workgroup's chunks, theta = the n-th largest L (n =
+// min(K, chunks)) is at most the n-th best exact score there, so every chunk among the
+// workgroup's exact best n has U >= theta: those survivors are rescored exactly from the
+// fp32 k' and b' in decode_scan's arithmetic (same lanes, same order of sums, so the
+// same bits), and the best of their exact keys are written as decode_scan writes its
+// list.  The list's first n entries equal decode_scan's; further entries (exact keys of
+// other chunks, or empty) rank below them, so decode_merge takes the same top K.
+template <typename IO, int D, bool KB, int UNR>
+__global__ void __launch_bounds__(256) decode_scan_m(const IO* __restrict__ q, const IO* __restrict__ Dw,
+                                                     const IO* __restrict__ Uw, const uint16_t* __restrict__ kcm,
+                                                     const float* __restrict__ kc, const float* __restrict__ bc,
+                                                     const int32_t* __restrict__ seq_lens, uint64_t* __restrict__ cand,
+                                                     int Hq, int Hl, int C, int K, int r, int nsplit, int nw,
+                                                     int64_t mrows) {
+  constexpr int TPM = D / 16;       // mirror: threads per chunk, 16 dims (two 16-byte loads) each
+  constexpr int CPM = 256 / TPM;    // mirror: chunks per pass
+  constexpr int STEP = CPM * UNR;
+  constexpr int TPC = D / 16;       // exact rescoring: decode_scan's arrangement
+  constexpr int CPP = 256 / TPC;
+  __shared__ __align__(16) float qs[D];
+  __shared__ float ts[32];
+  __shared__ float qn_s, theta_s;
+  __shared__ uint64_t keys[DS_CHUNKS];   // lower-bound keys, then the survivors' exact keys
+  __shared__ float ubs[DS_CHUNKS];       // upper bounds
+  __shared__ int16_t surv[DS_CHUNKS];    // survivors (offsets in the workgroup's range)
+  __shared__ uint64_t wl[4][64];
+  __shared__ int wcnt[4];
+  const int sp = blockIdx.x % nsplit, bh = blockIdx.x / nsplit;
+  const int b = bh / Hq, h = bh % Hq;
+  const int L = seq_lens[b];
+  const int P = candidate_chunks(L - 1, C, nw);
+  const int c_beg = sp * DS_CHUNKS, c_end = min(P, c_beg + DS_CHUNKS);
+  const int nloc = max(0, c_end - c_beg), n = min(K, nloc);
+  const int t = threadIdx.x, lane = t & 63, w = t >> 6, j = lane & 31;
+  uint64_t* out = cand + ((int64_t)bh * nsplit + sp) * DS_KEEP;
+  if (n == 0) {   // no chunk here (uniform): an empty list
+    if (t < DS_KEEP) out[t] = 0ull;
+    return;
+  }
+  qhat_to_lds<IO, D>(q + (int64_t)bh * D, Dw, Uw, h, r, qs, ts);
+  if (w == 0) {
+    float a = 0.f;
+    for (int e = lane; e < D; e += 64) a = fmaf(qs[e], qs[e], a);
+    a = wave_sum(a);
+    if (lane == 0) qn_s = sqrtf(a) * (1.0f + 1.0f / 4096.0f);
+  }
+  __syncthreads();
+  const int msub = t % TPM, mgrp = t / TPM;
+  // q^ rounded to bf16 pairs: dims 8 (msub + TPM x) + 2 y + {0, 1}, x = 0, 1, y = 0..3
+  bf16x2_t qp[8];
+#pragma unroll
+  for (int x = 0; x < 2; ++x)
+#pragma unroll
+    for (int y = 0; y < 4; ++y) {
+      const int e = 8 * (msub + TPM * x) + 2 * y;
+      qp[4 * x + y] = __builtin_bit_cast(bf16x2_t, pack_bf16x2(qs[e], qs[e + 1]));
+    }
+  const float tau = 1.0f / sqrtf((float)D);
+  // The mirror score sums bf16(q^_e) bf16(k'_e) (products exact in fp32, bf16 rounding
+  // at most 2^-8 relative each): it differs from sum q^_e k'_e by at most
+  // (2 2^-8 + 2^-16) sum |q^_e| |k'_e| <= (2^-7 + 2^-16) ||q^|| ||k'||.  2^-9 more covers
+  // the roundings of both sums (at most about D 2^-24 relative) and of the norms many
+  // times over; a tiny absolute term covers values below the normal range.
+  const float dfac = tau * qn_s * (1.0f / 128.0f + 1.0f / 512.0f);
+  const float dabs = 0x1p-110f * (qn_s + 1.0f);
+  const int64_t lrow = (int64_t)b * Hl + h / (Hq / Hl);
+  const uint16_t* mb = kcm + lrow * C * D;   // this head's bf16 rows
+  const u32x2_t* mt = reinterpret_cast<const u32x2_t*>(kcm + mrows * D) + lrow * C;   // (b', bound)
+  u32x4_t ka[UNR][2], kb2[UNR][2];
+  u32x2_t ta[UNR], tb[UNR];
+  auto load = [&](int c0, u32x4_t(&kv)[UNR][2], u32x2_t(&tv)[UNR]) {
+#pragma unroll
+    for (int u = 0; u < UNR; ++u) {
+      const int c = min(c0 + u * CPM + mgrp, c_end - 1);
+      const uint16_t* row = mb + (int64_t)c * D;
+#pragma unroll
+      for (int x = 0; x < 2; ++x)   // the TPM lanes of a chunk read a whole 128-byte line per load
+        kv[u][x] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(row + 8 * (msub + TPM * x)));
+      // every lane loads the pair (the lanes of a chunk share it): a load under a lane mask
+      // would make the compiler wait for all loads in flight
+      tv[u] = __builtin_nontemporal_load(mt + c);
+    }
+  };
+  auto bound = [&](int c0, const u32x4_t(&kv)[UNR][2], const u32x2_t(&tv)[UNR]) {
+#pragma unroll
+    for (int u = 0; u < UNR; ++u) {
+      float s = 0.f;
+#pragma unroll
+      for (int x = 0; x < 2; ++x) {
+        // the words go through scalars: a bit cast of a vector element (v.y) is compiled
+        // as a cast of element 0 by this toolchain
+        const uint32_t wd[4] = {kv[u][x].x, kv[u][x].y, kv[u][x].z, kv[u][x].w};
+#pragma unroll
+        for (int y = 0; y < 4; ++y)
+          s = __builtin_amdgcn_fdot2_f32_bf16(qp[4 * x + y], __builtin_bit_cast(bf16x2_t, wd[y]), s, false);
+      }
+#pragma unroll
+      for (int o = TPM / 2; o >= 1; o >>= 1) s += __shfl_xor(s, o);
+      const int c = c0 + u * CPM + mgrp;
+      if (msub == 0) {
+        const float bv = __uint_as_float(tv[u].x), nrm = __uint_as_float(tv[u].y);
+        const float sh = fmaf(s, tau, bv);
+        const float dl = fmaf(dfac, nrm, fmaf(0x1p-20f, fabsf(sh) + fabsf(bv), dabs * (nrm + 1.0f)));
+        const bool live = c < c_end;
+        keys[c - c_beg] = live ? make_key(sh - dl, c) : 0ull;
+        ubs[c - c_beg] = live ? sh + dl : -INFINITY;
+      }
+    }
+  };
+  // Two register buffers alternate.  Every load is issued whether or not its chunks are
+  // live (they clamp to chunk c_end - 1, so they stay in bounds): with a fixed number of
+  // loads in flight the compiler waits for exactly the buffer it is about to use.
+  static_assert(DS_CHUNKS % (2 * STEP) == 0, "");
+  constexpr int NIT = DS_CHUNKS / (2 * STEP);
+  load(c_beg, ka, ta);
+  for (int it = 0; it < NIT - 1; ++it) {
+    const int c0 = c_beg + it * 2 * STEP;
+    load(c0 + STEP, kb2, tb);
+    bound(c0, ka, ta);
+    load(c0 + 2 * STEP, ka, ta);
+    bound(c0 + STEP, kb2, tb);
+  }
+  {
+    const int c0 = c_beg + (NIT - 1) * 2 * STEP;
+    load(c0 + STEP, kb2, tb);
+    bound(c0, ka, ta);
+    bound(c0 + STEP, kb2, tb);
+  }
+  __syncthreads();
+  // theta: rank n - 1 of the lower bounds
+  if constexpr (KB) {
+    uint64_t hi, lo;
+    best64_of_1024(keys, wl, hi, lo);
+    const uint64_t kk = kl::rank_key(hi, lo, n - 1, lane);
+    if (t == 0) theta_s = key_score(kk);
+  } else {
+    const uint64_t lk = best32_of_1024(keys, wl);
+    const uint64_t kk = __shfl(lk, n - 1);
+    if (t == 0) theta_s = key_score(kk);
+  }
+  __syncthreads();
+  const float theta = theta_s;
+  // survivors U >= theta, in chunk order
+  int ns = 0;
+#pragma unroll
+  for (int i = 0; i < DS_CHUNKS / 256; ++i) {
+    const int x = i * 256 + t;
+    const bool sv = ubs[x] >= theta;
+    const uint64_t bal = __ballot(sv);
+    if (lane == 0) wcnt[w] = __popcll(bal);
+    __syncthreads();
+    int before = ns, total = ns;
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      before += v < w ? wcnt[v] : 0;
+      total += wcnt[v];
+    }
+    if (sv) surv[before + __popcll(bal & ((1ull << lane) - 1ull))] = (int16_t)x;
+    ns = total;
+    __syncthreads();   // wcnt is rewritten next round
+  }
+  // exact keys of the survivors in decode_scan's arrangement: dims 4 (sub + TPC y) .. + 3
+  const bool small = ns <= 64;
+  if (!small)
+    for (int x = ns + t; x < DS_CHUNKS; x += 256) keys[x] = 0ull;
+  {
+    const int sub = t % TPC, grp = t / TPC;
+    f32x4_t qe[4];
+#pragma unroll
+    for (int y = 0; y < 4; ++y) qe[y] = *reinterpret_cast<const f32x4_t*>(&qs[4 * (sub + TPC * y)]);
+    const float* kb = kc + lrow * C * D;
+    const float* bb = bc + lrow * C;
+    for (int p0 = 0; p0 < ns; p0 += CPP) {
+      const int x = p0 + grp;
+      const int c = c_beg + surv[min(x, ns - 1)];
+      const f32x4_t* row = reinterpret_cast<const f32x4_t*>(kb + (int64_t)c * D);
+      f32x4_t kv[4];
+#pragma unroll
+      for (int y = 0; y < 4; ++y) kv[y] = row[sub + TPC * y];
+      const float bv = bb[c];
+      float s = 0.f;
+#pragma unroll
+      for (int y = 0; y < 4; ++y) {
+        s = fmaf(qe[y].x, kv[y].x, s);
+        s = fmaf(qe[y].y, kv[y].y, s);
+        s = fmaf(qe[y].z, kv[y].z, s);
+        s = fmaf(qe[y].w, kv[y].w, s);
+      }
+#pragma unroll
+      for (int o = TPC / 2; o >= 1; o >>= 1) s += __shfl_xor(s, o);
+      if (sub == 0 && x < ns) keys[x] = make_key(fmaf(s, tau, bv), c);
+    }
+  }
+  __syncthreads();
+  if (small) {   // at most 64 survivors: one sorted 64-list (both halves of wave 0 build it)
+    if (w == 0) {
+      uint64_t hi = j < ns ? keys[j] : 0ull, lo = 32 + j < ns ? keys[32 + j] : 0ull;
+      kl::sort(hi, j);
+      kl::sort(lo, j);
+      kl::split(hi, lo, j);
+      if (lane < 32) {
+        out[lane] = hi;
+        if constexpr (KB) out[32 + lane] = lo;
+      }
+    }
+  } else if constexpr (KB) {
+    uint64_t hi, lo;
+    best64_of_1024(keys, wl, hi, lo);
+    if (lane < 32 && w == 0) {
+      out[lane] = hi;
+      out[32 + lane] = lo;
+    }
+  } else {
+    const uint64_t lk = best32_of_1024(keys, wl);
+    if (lane < 32 && w == 0) out[lane] = lk;
+  }
+}
+
+template <int D>
+static hipError_t launch_mirror_d(const float* kc, const float* bc, uint16_t* kcm, int BL, int C, int c_begin, int n,
+                                  hipStream_t st) {
+  const int64_t rows = (int64_t)BL * n;
+  const int64_t rpb = 256 / (D / 8);
+  const unsigned gs = (unsigned)std::min<int64_t>((rows + rpb - 1) / rpb, 16384);
+  hipLaunchKernelGGL((mirror_build<D>), dim3(gs), dim3(256), 0, st, kc, bc, kcm, C, c_begin, n, rows,
+                     (int64_t)BL * C);
+  return hipGetLastError();
+}
+
+hipError_t launch_mirror(const Geom& g, const float* kc, const float* bc, uint16_t* kcm, int c_begin, int c_end,
+                         hipStream_t st) {
+  const int n = c_end - c_begin;
+  if (n <= 0) return hipSuccess;
+  return g.d == 64 ? launch_mirror_d<64>(kc, bc, kcm, g.B * g.Hl, g.C(), c_begin, n, st)
+                   : launch_mirror_d<128>(kc, bc, kcm, g.B * g.Hl, g.C(), c_begin, n, st);
+}
+
 template <typename IO, int D>
 static hipError_t launch_decode_t(const Geom& g, const void* q, const void* kcache, const void* vcache,
-                                  const int32_t* seq_lens, const float* kc, const float* bc, const void* Dw,
-                                  const void* Uw, int32_t* sel_user, void* o, char* ws, hipStream_t st,
+                                  const int32_t* seq_lens, const float* kc, const float* bc, const uint16_t* kcm,
+                                  const void* Dw, const void* Uw, int32_t* sel_user, void* o, char* ws, hipStream_t st,
                                   hipEvent_t* ev, KvPages pg) {
   const DecodeWs w = decode_ws(g);
   uint64_t* cand = (uint64_t*)(ws + w.cand);
@@ -500,19 +817,35 @@ static hipError_t launch_decode_t(const Geom& g, const void* q, const void* kcac
   if (nsplit > DS_MAX_SPLIT) return hipErrorInvalidValue;  // N/S > 16384, rejected by the ABI first
   if (ev) (void)hipEventRecord(ev[0], st);
   const bool kb = g.K > 32;   // keep 64 candidates per split
-  if (kb)
+  if (kcm) {   // the scan over the bf16 mirror, exact rescoring of each split's survivors
+    if (kb)
+      hipLaunchKernelGGL((decode_scan_m<IO, D, true, DSM_UNR>), dim3(BH * nsplit), dim3(256), 0, st, (const IO*)q,
+                         (const IO*)Dw, (const IO*)Uw, kcm, kc, bc, seq_lens, cand, g.Hq, g.Hl, C, g.K, g.r, nsplit,
+                         g.nw, (int64_t)g.B * g.Hl * C);
+    else
+      hipLaunchKernelGGL((decode_scan_m<IO, D, false, DSM_UNR>), dim3(BH * nsplit), dim3(256), 0, st, (const IO*)q,
+                         (const IO*)Dw, (const IO*)Uw, kcm, kc, bc, seq_lens, cand, g.Hq, g.Hl, C, g.K, g.r, nsplit,
+                         g.nw, (int64_t)g.B * g.Hl * C);
+    if (ev) (void)hipEventRecord(ev[1], st);
+    if (kb)
+      hipLaunchKernelGGL(decode_merge<true>, dim3(BH), dim3(256), 0, st, (const uint64_t*)cand, seq_lens, sel_i,
+                         sel_s, nsel, sel_user, g.Hq, C, g.K, nsplit, g.nw);
+    else
+      hipLaunchKernelGGL(decode_merge<false>, dim3(BH), dim3(256), 0, st, (const uint64_t*)cand, seq_lens, sel_i,
+                         sel_s, nsel, sel_user, g.Hq, C, g.K, nsplit, g.nw);
+  } else if (kb) {
     hipLaunchKernelGGL((decode_scan<IO, D, true>), dim3(BH * nsplit), dim3(256), 0, st, (const IO*)q, (const IO*)Dw,
                        (const IO*)Uw, kc, bc, seq_lens, cand, g.Hq, g.Hl, C, g.r, nsplit, g.nw);
-  else
-    hipLaunchKernelGGL((decode_scan<IO, D, false>), dim3(BH * nsplit), dim3(256), 0, st, (const IO*)q,
-                       (const IO*)Dw, (const IO*)Uw, kc, bc, seq_lens, cand, g.Hq, g.Hl, C, g.r, nsplit, g.nw);
-  if (ev) (void)hipEventRecord(ev[1], st);
-  if (kb)
+    if (ev) (void)hipEventRecord(ev[1], st);
     hipLaunchKernelGGL(decode_merge<true>, dim3(BH), dim3(256), 0, st, (const uint64_t*)cand, seq_lens, sel_i, sel_s,
                        nsel, sel_user, g.Hq, C, g.K, nsplit, g.nw);
-  else
+  } else {
+    hipLaunchKernelGGL((decode_scan<IO, D, false>), dim3(BH * nsplit), dim3(256), 0, st, (const IO*)q,
+                       (const IO*)Dw, (const IO*)Uw, kc, bc, seq_lens, cand, g.Hq, g.Hl, C, g.r, nsplit, g.nw);
+    if (ev) (void)hipEventRecord(ev[1], st);
     hipLaunchKernelGGL(decode_merge<false>, dim3(BH), dim3(256), 0, st, (const uint64_t*)cand, seq_lens, sel_i,
                        sel_s, nsel, sel_user, g.Hq, C, g.K, nsplit, g.nw);
+  }
   if (ev) (void)hipEventRecord(ev[2], st);
   hipLaunchKernelGGL((decode_attend<IO, D>), dim3(BH * (g.K + g.nw)), dim3(256), 0, st, (const IO*)q,
                      (const IO*)kcache, (const IO*)vcache, seq_lens, sel_i, sel_s, nsel, part, sig, g.Hq, g.Hkv, g.N,
@@ -528,17 +861,18 @@ static hipError_t launch_decode_t(const Geom& g, const void* q, const void* kcac
 }
 
 hipError_t launch_decode(const Geom& g, const void* q, const void* kcache, const void* vcache, const int32_t* seq_lens,
-                         const float* kc, const float* bc, const void* Dw, const void* Uw, int32_t* sel_idx_out,
-                         void* o, void* ws, size_t ws_bytes, hipStream_t st, hipEvent_t* ev, KvPages pg) {
+                         const float* kc, const float* bc, const uint16_t* kcm, const void* Dw, const void* Uw,
+                         int32_t* sel_idx_out, void* o, void* ws, size_t ws_bytes, hipStream_t st, hipEvent_t* ev,
+                         KvPages pg) {
   if (ws_bytes < decode_workspace_bytes(g)) return hipErrorInvalidValue;
   char* w = (char*)ws;
   if (g.io == 0)
     return g.d == 64
-               ? launch_decode_t<float, 64>(g, q, kcache, vcache, seq_lens, kc, bc, Dw, Uw, sel_idx_out, o, w, st, ev, pg)
-               : launch_decode_t<float, 128>(g, q, kcache, vcache, seq_lens, kc, bc, Dw, Uw, sel_idx_out, o, w, st, ev, pg);
+               ? launch_decode_t<float, 64>(g, q, kcache, vcache, seq_lens, kc, bc, kcm, Dw, Uw, sel_idx_out, o, w, st, ev, pg)
+               : launch_decode_t<float, 128>(g, q, kcache, vcache, seq_lens, kc, bc, kcm, Dw, Uw, sel_idx_out, o, w, st, ev, pg);
   return g.d == 64
-             ? launch_decode_t<bf16_t, 64>(g, q, kcache, vcache, seq_lens, kc, bc, Dw, Uw, sel_idx_out, o, w, st, ev, pg)
-             : launch_decode_t<bf16_t, 128>(g, q, kcache, vcache, seq_lens, kc, bc, Dw, Uw, sel_idx_out, o, w, st, ev, pg);
+             ? launch_decode_t<bf16_t, 64>(g, q, kcache, vcache, seq_lens, kc, bc, kcm, Dw, Uw, sel_idx_out, o, w, st, ev, pg)
+             : launch_decode_t<bf16_t, 128>(g, q, kcache, vcache, seq_lens, kc, bc, kcm, Dw, Uw, sel_idx_out, o, w, st, ev, pg);
 }
 
 }  // namespace hils

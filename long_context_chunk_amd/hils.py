@@ -22,7 +22,7 @@ OK, E_INVAL, E_UNSUPPORTED, E_WORKSPACE, E_HIP = 0, -1, -2, -3, -4
 SYMBOLS = ("hils_workspace_bytes", "hils_landmark_compress", "hils_chunk_score_topk", "hils_attn_prefill",
            "hils_attn_prefill_timed", "hils_attn_decode", "hils_attn_decode_timed", "hils_landmark_compress_paged",
            "hils_attn_decode_paged", "hils_dense_attention", "hils_attn_prefill_backward", "hils_attn_decode_noalloc",
-           "hils_last_error")
+           "hils_landmark_mirror", "hils_attn_decode_mirror", "hils_attn_decode_mirror_timed", "hils_last_error")
 NOALLOC_SCRATCH_BYTES = 16 << 20   # HILS_NOALLOC_SCRATCH_BYTES of include/hils.h
 STAGES = ("compress", "score_threshold", "score_select", "bucket", "chunk_attend", "own_attend", "fuse")
 DECODE_STAGES = ("scan", "merge", "attend_fuse")
@@ -69,9 +69,14 @@ def load():
         lib.hils_landmark_compress_paged.argtypes = [dp, vp, vp, i32, i32, vp, i32, i32, vp, vp, vp]
         lib.hils_attn_decode_paged.argtypes = [dp, vp, vp, vp, vp, i32, i32, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
         lib.hils_attn_prefill_backward.argtypes = [dp] + [vp] * 18 + [sz, vp]
+        lib.hils_landmark_mirror.argtypes = [dp, vp, vp, i32, i32, vp, vp]
+        lib.hils_attn_decode_mirror.argtypes = [dp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+        lib.hils_attn_decode_mirror_timed.argtypes = [dp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp,
+                                                      ctypes.POINTER(ctypes.c_float)]
         for f in ("hils_landmark_compress", "hils_chunk_score_topk", "hils_attn_prefill", "hils_attn_prefill_timed",
                   "hils_attn_decode", "hils_attn_decode_timed", "hils_dense_attention", "hils_landmark_compress_paged",
-                  "hils_attn_decode_paged", "hils_attn_prefill_backward", "hils_attn_decode_noalloc"):
+                  "hils_attn_decode_paged", "hils_attn_prefill_backward", "hils_attn_decode_noalloc",
+                  "hils_landmark_mirror", "hils_attn_decode_mirror", "hils_attn_decode_mirror_timed"):
             getattr(lib, f).restype = ctypes.c_int
         lib.hils_last_error.argtypes = []
         lib.hils_last_error.restype = ctypes.c_char_p
@@ -222,9 +227,26 @@ def attn_prefill_backward(dm: Dims, q, k, v, lmk_q, kc, sel_idx, sel_score, o, d
                                               _p(dv), _p(dlmk), _p(dD), _p(dU), _p(ws), ws.numel(), _stream()))
 
 
+def mirror_shape(dm: Dims):
+    """Shape of the landmark mirror: a flat int16 tensor of B*Hlmk*C*(d + 4) elements, the
+    bf16 rows of k' [B, Hlmk, C, d], then per row (b', an upper bound of ||k'||) as fp32."""
+    return (dm.B * dm.Hlmk * (dm.N // dm.S) * (dm.d + 4),)
+
+
+def landmark_mirror(dm: Dims, kc, bc, kc_mirror, c_begin=0, c_end=None):
+    """hils_landmark_mirror: rows [c_begin, c_end) of the bf16 landmark mirror from kc/bc."""
+    C = dm.N // dm.S
+    c_end = C if c_end is None else c_end
+    _req(kc, "kc", (dm.B, dm.Hlmk, C, dm.d), torch.float32)
+    _req(bc, "bc", (dm.B, dm.Hlmk, C), torch.float32)
+    _req(kc_mirror, "kc_mirror", mirror_shape(dm), torch.int16)
+    _check(load().hils_landmark_mirror(ctypes.byref(dm), _p(kc), _p(bc), c_begin, c_end, _p(kc_mirror), _stream()))
+
+
 def attn_decode(dm: Dims, q, k_cache, v_cache, seq_lens, kc, bc, o, ws, qcal_D=None, qcal_U=None, sel_idx=None,
-                timed=False):
-    """hils_attn_decode (timed=True: hils_attn_decode_timed, returns {stage: ms})."""
+                timed=False, kc_mirror=None):
+    """hils_attn_decode (timed=True: hils_attn_decode_timed, returns {stage: ms}); with
+    kc_mirror (the landmark mirror), hils_attn_decode_mirror / hils_attn_decode_mirror_timed."""
     C = dm.N // dm.S
     dt = torch.float32 if dm.io == F32 else torch.bfloat16
     _req(q, "q", (dm.B, dm.Hq, dm.d), dt)
@@ -240,6 +262,16 @@ def attn_decode(dm: Dims, q, k_cache, v_cache, seq_lens, kc, bc, o, ws, qcal_D=N
         _req(qcal_U, "qcal_U", (dm.Hq, dm.d, dm.qcal_rank), dt)
     if sel_idx is not None:
         _req(sel_idx, "sel_idx", (dm.B, dm.Hq, dm.K), torch.int32)
+    if kc_mirror is not None:
+        _req(kc_mirror, "kc_mirror", mirror_shape(dm), torch.int16)
+        args = (ctypes.byref(dm), _p(q), _p(k_cache), _p(v_cache), _p(seq_lens), _p(kc), _p(bc), _p(kc_mirror),
+                _p(qcal_D), _p(qcal_U), _p(sel_idx), _p(o), _p(ws), ws.numel(), _stream())
+        if timed:
+            ms = (ctypes.c_float * len(DECODE_STAGES))()
+            _check(load().hils_attn_decode_mirror_timed(*args, ms))
+            return dict(zip(DECODE_STAGES, [float(x) for x in ms]))
+        _check(load().hils_attn_decode_mirror(*args))
+        return None
     args = (ctypes.byref(dm), _p(q), _p(k_cache), _p(v_cache), _p(seq_lens), _p(kc), _p(bc), _p(qcal_D), _p(qcal_U),
             _p(sel_idx), _p(o), _p(ws), ws.numel(), _stream())
     if timed:

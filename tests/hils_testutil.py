@@ -183,7 +183,9 @@ def check_selection(w, x, kc_o, bc_o, rows, ref, gpu_sel, gpu_score, label=""):
     return {"rows": n, "exact_rows": int(exact.sum()), "near_tie_rows": int((~exact).sum())}
 
 
-def gpu_decode(w, x, kc=None, bc=None):
+def gpu_decode(w, x, kc=None, bc=None, mirror=False):
+    """One decode step through hils_attn_decode (mirror=True: the landmark mirror is built
+    with hils_landmark_mirror and the step runs through hils_attn_decode_mirror)."""
     dm = dims_of(w)
     k, v = upload(x["k"], w.io), upload(x["v"], w.io)
     if kc is None:
@@ -197,6 +199,11 @@ def gpu_decode(w, x, kc=None, bc=None):
     ws = hils.workspace(dm, hils.OP_DECODE)
     D = upload(x["D"], w.io) if w.qcal_rank else None
     U = upload(x["U"], w.io) if w.qcal_rank else None
-    hils.attn_decode(dm, q, k, v, lens, kc, bc, o, ws, qcal_D=D, qcal_U=U, sel_idx=sel)
+    kcm = None
+    if mirror:
+        kcm = torch.zeros(hils.mirror_shape(dm), dtype=torch.int16, device="cuda")
+        hils.landmark_mirror(dm, kc, bc, kcm)
+    hils.attn_decode(dm, q, k, v, lens, kc, bc, o, ws, qcal_D=D, qcal_U=U, sel_idx=sel, kc_mirror=kcm)
     torch.cuda.synchronize()
-    return {"o": download_f32(o), "sel_idx": sel.cpu().numpy(), "kc": kc, "bc": bc}
+    return {"o": download_f32(o), "o_bits": o.view(torch.int16 if w.io == synth.BF16 else torch.int32).cpu().numpy(),
+            "sel_idx": sel.cpu().numpy(), "kc": kc, "bc": bc, "kcm": kcm}

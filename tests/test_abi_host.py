@@ -248,3 +248,40 @@ def test_score_topk_block_arguments():
     # no query: nothing to do, NULL arrays allowed, nothing enqueued
     assert lib.hils_chunk_score_topk(ctypes.byref(d), 0, None, None, None, None, None, None, None, None, None, 0,
                                      None) == hils.OK
+
+
+def test_mirror_entry_points_validation():
+    """hils_landmark_mirror and hils_attn_decode_mirror(_timed) validate on the host: the
+    chunk range, NULL buffers (the mirror may be NULL only without a complete chunk), and
+    the decode's own checks; an empty range does nothing."""
+    lib = hils.load()
+    fake = ctypes.c_void_p(0x1000)   # never dereferenced: validation fails first
+    d = hils.dims(2, 8, 2, 128, 4096, 16)
+    C = 4096 // 64
+    assert lib.hils_landmark_mirror(ctypes.byref(d), fake, fake, 0, C + 1, fake, None) == hils.E_INVAL
+    assert lib.hils_landmark_mirror(ctypes.byref(d), fake, fake, 5, 4, fake, None) == hils.E_INVAL
+    assert lib.hils_landmark_mirror(ctypes.byref(d), fake, fake, -1, 4, fake, None) == hils.E_INVAL
+    assert lib.hils_landmark_mirror(ctypes.byref(d), None, fake, 0, 4, fake, None) == hils.E_INVAL
+    assert lib.hils_landmark_mirror(ctypes.byref(d), fake, fake, 0, 4, None, None) == hils.E_INVAL
+    assert lib.hils_landmark_mirror(ctypes.byref(d), None, None, 3, 3, None, None) == hils.OK
+    bad = hils.dims(2, 8, 2, 96, 4096, 16)
+    assert lib.hils_landmark_mirror(ctypes.byref(bad), fake, fake, 0, 4, fake, None) == hils.E_UNSUPPORTED
+    ws_need = hils.workspace_bytes(d, hils.OP_DECODE)
+    args = [fake, fake, fake, fake, fake, fake]
+    rc = lib.hils_attn_decode_mirror(ctypes.byref(d), *args, None, None, None, None, fake, fake, ws_need, None)
+    assert rc == hils.E_INVAL and b"kc_mirror" in lib.hils_last_error()
+    rc = lib.hils_attn_decode_mirror(ctypes.byref(d), *args, fake, None, None, None, fake, fake, ws_need - 1, None)
+    assert rc == hils.E_WORKSPACE
+    rc = lib.hils_attn_decode_mirror(ctypes.byref(bad), *args, fake, None, None, None, fake, fake, 1 << 40, None)
+    assert rc == hils.E_UNSUPPORTED
+    ms = (ctypes.c_float * len(hils.DECODE_STAGES))()
+    rc = lib.hils_attn_decode_mirror_timed(ctypes.byref(d), *args, fake, None, None, None, fake, fake, ws_need, None,
+                                           None)
+    assert rc == hils.E_INVAL and b"stage_ms" in lib.hils_last_error()
+    rc = lib.hils_attn_decode_mirror_timed(ctypes.byref(d), *args, None, None, None, None, fake, fake, ws_need, None,
+                                           ms)
+    assert rc == hils.E_INVAL
+    short = hils.dims(2, 8, 2, 128, 48, 16)   # N < S: no chunk, the mirror may be NULL
+    rc = lib.hils_attn_decode_mirror(ctypes.byref(short), fake, fake, fake, fake, None, None, None, None, None, None,
+                                     None, fake, 1 << 40, None)
+    assert rc == hils.E_INVAL and b"o must" in lib.hils_last_error()
