@@ -413,8 +413,8 @@ def run_decode(wd, steps, warmup, seed, dense=False):
     e1.record()
     torch.cuda.synchronize()
     comp_ms = e0.elapsed_time(e1)
-    # the bf16 landmark mirror (built once per chunk, like k' and b'): the scan reads it
-    kcm = torch.empty(hils.mirror_shape(dm), dtype=torch.int16, device="cuda")
+    # the 8-bit landmark mirror (built once per chunk, like k' and b'): the scan reads it
+    kcm = torch.empty(hils.mirror_shape(dm), dtype=torch.uint8, device="cuda")
     e0.record()
     hils.landmark_mirror(dm, kc, bc, kcm)
     e1.record()
@@ -466,7 +466,7 @@ def run_decode(wd, steps, warmup, seed, dense=False):
             kv_bytes += (len(u) * wd.S + (L - own * wd.S) + min(nw - 1, own) * wd.S) * wd.d * 2 * 2
     Ps = [min(wd.C, max(0, (int(L) - 1) // wd.S - nw + 1)) for L in x["seq_lens"]]
     scan_bytes_f = sum(P * wd.Hlmk * (wd.d + 1) * 4 for P in Ps)          # fp32 k' and b'
-    scan_bytes = sum(P * wd.Hlmk * (wd.d * 2 + 8) for P in Ps)   # mirror: bf16 k', fp32 b' and norm bound
+    scan_bytes = sum(P * wd.Hlmk * (wd.d + 8) for P in Ps)   # mirror: 8-bit codes of k', fp32 b' and scale
     total_bytes = scan_bytes + kv_bytes + 2 * 2 * wd.B * wd.Hq * wd.d
     step_gbs = total_bytes / (us * 1e-6) / 1e9
     scan_gbs = scan_bytes / (stages["scan"] * 1e-3) / 1e9
@@ -482,7 +482,7 @@ def run_decode(wd, steps, warmup, seed, dense=False):
         "workload": wd.name, "B": wd.B, "Hq": wd.Hq, "Hkv": wd.Hkv, "d": wd.d, "ctx": int(max(x["seq_lens"])),
         "K": wd.K, "window": wd.window, "us_per_step": us, "us_per_step_dist": dist,
         "stages_us": {k_: v_ * 1e3 for k_, v_ in stages.items()},
-        "scan": "bf16 landmark mirror + exact fp32 rescoring (hils_attn_decode_mirror)",
+        "scan": "8-bit landmark mirror + exact fp32 rescoring (hils_attn_decode_mirror)",
         "one_off_compress_ms": comp_ms, "one_off_mirror_ms": mirror_ms,
         "roofline": {"bound": "hbm", "achieved": scan_gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s",
                      "frac": scan_gbs / PEAK_HBM_GBS, "kernel": "decode_scan_m",

@@ -192,42 +192,45 @@ int hils_attn_decode_timed(const hils_dims_t* dims, const void* q, const void* k
                            void* stream, float* stage_ms);
 
 /*
- * The landmark mirror: a bf16 copy of the landmark cache that halves the bytes the
- * decode scan streams (a decode step reads every past chunk's compressed key for
- * step (2): aitrends.kr "Technical details" on the decode cost; "Methodology" for
- * the score).  kc_mirror: B*Hlmk*floor(N/S)*(d + 4) uint16 (device, caller-owned), two
- * planes: first bf16(kc) [B, Hlmk, floor(N/S), d] (round to nearest even), then for
- * each (b, l, c) the pair (bc[b,l,c], an upper bound of ||kc[b,l,c]||_2) as fp32
- * [B, Hlmk, floor(N/S), 2].
+ * The landmark mirror: an 8-bit copy of the landmark cache that cuts the bytes the
+ * decode scan streams to about a quarter (a decode step reads every past chunk's
+ * compressed key for step (2): aitrends.kr "Technical details" on the decode cost;
+ * "Methodology" for the score).  kc_mirror: B*Hlmk*floor(N/S)*(d + 8) bytes (device,
+ * caller-owned), two planes.  First the codes [B, Hlmk, floor(N/S), d] uint8: with
+ * m = max_e |kc[b,l,c,e]|, code_e = rint(kc[b,l,c,e] * fl(127 / m)) + 128 (128 when
+ * m = 0; rint rounds half to even).  Then for each (b, l, c) the pair
+ * (bc[b,l,c], fl(m / 127)) as fp32 [B, Hlmk, floor(N/S), 2].
  *
- * hils_landmark_mirror writes the rows of chunks c_begin <= c < c_end from kc/bc
+ * hils_landmark_mirror writes the mirror of chunks c_begin <= c < c_end from kc/bc
  * (call it wherever kc/bc of those chunks change, e.g. after hils_landmark_compress
- * of the chunk a decode step completes); other rows are untouched.  Same range rules
+ * of the chunk a decode step completes); other chunks are untouched.  Same range rules
  * as hils_landmark_compress; no workspace; asynchronous on `stream`.
  *
  * hils_attn_decode_mirror: hils_attn_decode with the scan over kc_mirror.  Its result
- * is the same as hils_attn_decode's, bit for bit (selection, scores and o): from the
- * mirror the scan takes, for every chunk, a lower and an upper bound of the exact fp32
- * score (the bf16 rounding error of q^ . k' is at most 2^-8 ||q^|| ||k'||, plus a
- * margin for the fp32 sums); every chunk whose upper bound reaches the K-th largest
- * lower bound is rescored exactly from kc/bc in hils_attn_decode's arithmetic, and the
- * top K is taken from those.  kc_mirror must hold the rows of every chunk that
- * hils_attn_decode would score (c < floor((seq_lens[b]-1)/S), as kc/bc); it may be
- * NULL only when N < S.  Workspace and limits as hils_attn_decode (HILS_OP_DECODE).
- * When many scores lie within the bounds' width of the K-th one (e.g. all equal),
- * the rescoring reads more of kc: the result stays exact, the step gets slower.
+ * is the same as hils_attn_decode's, bit for bit (selection, scores and o): from a
+ * chunk's codes the scan takes a lower and an upper bound of its exact fp32 score
+ * (the codes' error is at most s/2 per element, so the dot product's is at most
+ * (s/2) ||q^||_1, plus a margin for the fp32 sums); within each split of 1024 chunks,
+ * every chunk whose upper bound reaches the split's K-th largest lower bound is
+ * rescored exactly from kc/bc in hils_attn_decode's arithmetic, and the top K is taken
+ * from those.  kc_mirror must hold every chunk that hils_attn_decode would score
+ * (c < floor((seq_lens[b]-1)/S), as kc/bc); it may be NULL only when N < S.
+ * Workspace and limits as hils_attn_decode (HILS_OP_DECODE).  When many scores lie
+ * within the bounds' width of the K-th one (e.g. all equal), the rescoring reads more
+ * of kc: the result stays exact, the step gets slower.
  * hils_attn_decode_mirror_timed: the same with stage times as hils_attn_decode_timed
- * ([0] the mirror scan, [1] rescoring and top-K, [2] attention and fusion).
+ * ([0] the mirror scan with the rescoring, [1] the top-K merge, [2] attention and
+ * fusion).
  */
 int hils_landmark_mirror(const hils_dims_t* dims, const float* kc, const float* bc, int32_t c_begin, int32_t c_end,
-                         uint16_t* kc_mirror, void* stream);
+                         uint8_t* kc_mirror, void* stream);
 int hils_attn_decode_mirror(const hils_dims_t* dims, const void* q, const void* k_cache, const void* v_cache,
-                            const int32_t* seq_lens, const float* kc, const float* bc, const uint16_t* kc_mirror,
+                            const int32_t* seq_lens, const float* kc, const float* bc, const uint8_t* kc_mirror,
                             const void* qcal_D, const void* qcal_U, int32_t* sel_idx_out, void* o, void* ws,
                             size_t ws_bytes, void* stream);
 int hils_attn_decode_mirror_timed(const hils_dims_t* dims, const void* q, const void* k_cache, const void* v_cache,
                                   const int32_t* seq_lens, const float* kc, const float* bc,
-                                  const uint16_t* kc_mirror, const void* qcal_D, const void* qcal_U,
+                                  const uint8_t* kc_mirror, const void* qcal_D, const void* qcal_U,
                                   int32_t* sel_idx_out, void* o, void* ws, size_t ws_bytes, void* stream,
                                   float* stage_ms);
 

@@ -235,7 +235,7 @@ int run_prefill(const hils_dims_t* dims, const void* q, const void* k, const voi
 int run_decode(const hils_dims_t* dims, const void* q, const void* k_cache, const void* v_cache,
                const int32_t* seq_lens, const float* kc, const float* bc, const void* qcal_D, const void* qcal_U,
                int32_t* sel_idx_out, void* o, void* ws, size_t ws_bytes, void* stream, float* stage_ms,
-               hils::KvPages pg = hils::KvPages(), const uint16_t* kcm = nullptr) {
+               hils::KvPages pg = hils::KvPages(), const uint8_t* kcm = nullptr) {
   hils::Geom g;
   int rc = check_dims(dims, g);
   if (rc) return rc;
@@ -268,7 +268,7 @@ int run_decode(const hils_dims_t* dims, const void* q, const void* k_cache, cons
 }
 
 // The mirror decode calls need the mirror whenever the cache has a complete chunk.
-int check_mirror(const hils_dims_t* dims, const uint16_t* kcm) {
+int check_mirror(const hils_dims_t* dims, const uint8_t* kcm) {
   hils::Geom g;
   int rc = check_dims(dims, g);
   if (rc) return rc;
@@ -340,7 +340,7 @@ int hils_attn_decode_timed(const hils_dims_t* dims, const void* q, const void* k
 }
 
 int hils_landmark_mirror(const hils_dims_t* dims, const float* kc, const float* bc, int32_t c_begin, int32_t c_end,
-                         uint16_t* kc_mirror, void* stream) {
+                         uint8_t* kc_mirror, void* stream) {
   hils::Geom g;
   int rc = check_dims(dims, g);
   if (rc) return rc;
@@ -358,7 +358,7 @@ int hils_landmark_mirror(const hils_dims_t* dims, const float* kc, const float* 
 }
 
 int hils_attn_decode_mirror(const hils_dims_t* dims, const void* q, const void* k_cache, const void* v_cache,
-                            const int32_t* seq_lens, const float* kc, const float* bc, const uint16_t* kc_mirror,
+                            const int32_t* seq_lens, const float* kc, const float* bc, const uint8_t* kc_mirror,
                             const void* qcal_D, const void* qcal_U, int32_t* sel_idx_out, void* o, void* ws,
                             size_t ws_bytes, void* stream) {
   int rc;
@@ -369,7 +369,7 @@ int hils_attn_decode_mirror(const hils_dims_t* dims, const void* q, const void* 
 
 int hils_attn_decode_mirror_timed(const hils_dims_t* dims, const void* q, const void* k_cache, const void* v_cache,
                                   const int32_t* seq_lens, const float* kc, const float* bc,
-                                  const uint16_t* kc_mirror, const void* qcal_D, const void* qcal_U,
+                                  const uint8_t* kc_mirror, const void* qcal_D, const void* qcal_U,
                                   int32_t* sel_idx_out, void* o, void* ws, size_t ws_bytes, void* stream,
                                   float* stage_ms) {
   if (!stage_ms) return fail(HILS_E_INVAL, "stage_ms must be non-NULL");

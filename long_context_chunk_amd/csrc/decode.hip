@@ -516,12 +516,14 @@ __global__ void __launch_bounds__(256) decode_combine(const float* __restrict__ 
 }
 
 // ---------------------------------------------------------------- landmark mirror
-// A bf16 mirror of the landmark cache for the decode scan, in two planes: the rows
-// bf16(k'_c) [B*Hlmk*C, d] (each row 128 or 256 bytes, so the scan reads whole cache
-// lines), then per row the pair (b'_c, an upper bound of ||k'_c||_2) as fp32 [B*Hlmk*C, 2].
+// An 8-bit mirror of the landmark cache for the decode scan, in two planes: per row
+// (b, l, c) the codes u_e = rint(k'_e * (127 / m)) + 128 with m = max_e |k'_e| (d bytes,
+// so a row is one or two whole cache lines), then per row the pair (b'_c, s_c = m / 127)
+// as fp32 [B*Hlmk*C, 2].  |k'_e - s_c (u_e - 128)| <= s_c (1/2 + 2^-16): the rounding to
+// an integer, plus the fp32 roundings of 127 / m and of the product.
 template <int D>
 __global__ void __launch_bounds__(256) mirror_build(const float* __restrict__ kc, const float* __restrict__ bc,
-                                                    uint16_t* __restrict__ kcm, int C, int c_begin, int n,
+                                                    uint8_t* __restrict__ kcm, int C, int c_begin, int n,
                                                     int64_t rows, int64_t all_rows) {
   constexpr int TPR = D / 8;        // threads per row, 8 elements each
   constexpr int RPB = 256 / TPR;    // rows per workgroup pass
@@ -539,24 +541,22 @@ __global__ void __launch_bounds__(256) mirror_build(const float* __restrict__ kc
 #pragma unroll
       for (int m = 0; m < 8; ++m) x[m] = 0.f;
     }
-    float s2 = 0.f;
+    float mx = 0.f;
 #pragma unroll
-    for (int m = 0; m < 8; ++m) s2 = fmaf(x[m], x[m], s2);
+    for (int m = 0; m < 8; ++m) mx = fmaxf(mx, fabsf(x[m]));
 #pragma unroll
-    for (int o = TPR / 2; o >= 1; o >>= 1) s2 += __shfl_xor(s2, o);
+    for (int o = TPR / 2; o >= 1; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o));
     if (ok) {
-      uint16_t* dst = kcm + r * D;
-      u32x4_t v;
-      v.x = pack_bf16x2(x[0], x[1]);
-      v.y = pack_bf16x2(x[2], x[3]);
-      v.z = pack_bf16x2(x[4], x[5]);
-      v.w = pack_bf16x2(x[6], x[7]);
-      *reinterpret_cast<u32x4_t*>(dst + 8 * sub) = v;
-      if (sub == 0) {
-        // the fp32 sum of squares errs by at most D 2^-24 relative; the margin covers it
-        const float nrm = sqrtf(s2) * (1.0f + 1.0f / 4096.0f) + 1e-30f;
-        reinterpret_cast<u32x2_t*>(kcm + all_rows * D)[r] = u32x2_t{__float_as_uint(bc[r]), __float_as_uint(nrm)};
+      const float inv = mx > 0.f ? 127.0f / mx : 0.f;
+      uint32_t wd[2] = {0u, 0u};
+#pragma unroll
+      for (int m = 0; m < 8; ++m) {
+        const int code = (int)rintf(x[m] * inv) + 128;   // |x * inv| <= 127 (1 + 2^-23)
+        wd[m >> 2] |= (uint32_t)code << (8 * (m & 3));
       }
+      *reinterpret_cast<u32x2_t*>(kcm + r * D + 8 * sub) = u32x2_t{wd[0], wd[1]};
+      if (sub == 0)
+        reinterpret_cast<u32x2_t*>(kcm + all_rows * D)[r] = u32x2_t{__float_as_uint(bc[r]), __float_as_uint(mx / 127.0f)};
     }
   }
 }
@@ -572,19 +572,19 @@ __global__ void __launch_bounds__(256) mirror_build(const float* __restrict__ kc
 // other chunks, or empty) rank below them, so decode_merge takes the same top K.
 template <typename IO, int D, bool KB, int UNR>
 __global__ void __launch_bounds__(256) decode_scan_m(const IO* __restrict__ q, const IO* __restrict__ Dw,
-                                                     const IO* __restrict__ Uw, const uint16_t* __restrict__ kcm,
+                                                     const IO* __restrict__ Uw, const uint8_t* __restrict__ kcm,
                                                      const float* __restrict__ kc, const float* __restrict__ bc,
                                                      const int32_t* __restrict__ seq_lens, uint64_t* __restrict__ cand,
                                                      int Hq, int Hl, int C, int K, int r, int nsplit, int nw,
                                                      int64_t mrows) {
-  constexpr int TPM = D / 16;       // mirror: threads per chunk, 16 dims (two 16-byte loads) each
+  constexpr int TPM = D / 16;       // mirror: threads per chunk, 16 codes (one 16-byte load) each
   constexpr int CPM = 256 / TPM;    // mirror: chunks per pass
   constexpr int STEP = CPM * UNR;
   constexpr int TPC = D / 16;       // exact rescoring: decode_scan's arrangement
   constexpr int CPP = 256 / TPC;
   __shared__ __align__(16) float qs[D];
   __shared__ float ts[32];
-  __shared__ float qn_s, theta_s;
+  __shared__ float q1_s, l1_s, theta_s;
   __shared__ uint64_t keys[DS_CHUNKS];   // lower-bound keys, then the survivors' exact keys
   __shared__ float ubs[DS_CHUNKS];       // upper bounds
   __shared__ int16_t surv[DS_CHUNKS];    // survivors (offsets in the workgroup's range)
@@ -603,69 +603,66 @@ __global__ void __launch_bounds__(256) decode_scan_m(const IO* __restrict__ q, c
     return;
   }
   qhat_to_lds<IO, D>(q + (int64_t)bh * D, Dw, Uw, h, r, qs, ts);
-  if (w == 0) {
-    float a = 0.f;
-    for (int e = lane; e < D; e += 64) a = fmaf(qs[e], qs[e], a);
+  if (w == 0) {   // sum_e q^_e and an upper bound of sum_e |q^_e|
+    float a = 0.f, ab = 0.f;
+    for (int e = lane; e < D; e += 64) {
+      a += qs[e];
+      ab += fabsf(qs[e]);
+    }
     a = wave_sum(a);
-    if (lane == 0) qn_s = sqrtf(a) * (1.0f + 1.0f / 4096.0f);
+    ab = wave_sum(ab);
+    if (lane == 0) {
+      q1_s = a;
+      l1_s = ab * (1.0f + 1.0f / 4096.0f);
+    }
   }
   __syncthreads();
   const int msub = t % TPM, mgrp = t / TPM;
-  // q^ rounded to bf16 pairs: dims 8 (msub + TPM x) + 2 y + {0, 1}, x = 0, 1, y = 0..3
-  bf16x2_t qp[8];
+  float qv[16];   // dims 16 msub + i
 #pragma unroll
-  for (int x = 0; x < 2; ++x)
-#pragma unroll
-    for (int y = 0; y < 4; ++y) {
-      const int e = 8 * (msub + TPM * x) + 2 * y;
-      qp[4 * x + y] = __builtin_bit_cast(bf16x2_t, pack_bf16x2(qs[e], qs[e + 1]));
-    }
+  for (int i = 0; i < 16; ++i) qv[i] = qs[16 * msub + i];
   const float tau = 1.0f / sqrtf((float)D);
-  // The mirror score sums bf16(q^_e) bf16(k'_e) (products exact in fp32, bf16 rounding
-  // at most 2^-8 relative each): it differs from sum q^_e k'_e by at most
-  // (2 2^-8 + 2^-16) sum |q^_e| |k'_e| <= (2^-7 + 2^-16) ||q^|| ||k'||.  2^-9 more covers
-  // the roundings of both sums (at most about D 2^-24 relative) and of the norms many
-  // times over; a tiny absolute term covers values below the normal range.
-  const float dfac = tau * qn_s * (1.0f / 128.0f + 1.0f / 512.0f);
-  const float dabs = 0x1p-110f * (qn_s + 1.0f);
+  const float q1x128 = 128.0f * q1_s;
+  // Per chunk, with s its scale: |s sum_e q^_e (u_e - 128) - q^ . k'| <= s ||q^||_1 (1/2 +
+  // 2^-16).  The fp32 sums (the codes' sum, 128 sum q^_e, the product with s, and the exact
+  // path's own dot product) add at most about 510 D 2^-24 s ||q^||_1 < 0.004 s ||q^||_1 for
+  // D <= 128: the factor 1/2 + 2^-5 covers all of it.  The roundings of the last fma
+  // (s tau + b') on both sides are covered by 2^-20 (|s| + |b'|), values below the normal
+  // range by a tiny absolute term.
+  const float dfac = tau * l1_s * (0.5f + 1.0f / 32.0f);
+  const float dabs = 0x1p-110f * (l1_s + 1.0f);
   const int64_t lrow = (int64_t)b * Hl + h / (Hq / Hl);
-  const uint16_t* mb = kcm + lrow * C * D;   // this head's bf16 rows
-  const u32x2_t* mt = reinterpret_cast<const u32x2_t*>(kcm + mrows * D) + lrow * C;   // (b', bound)
-  u32x4_t ka[UNR][2], kb2[UNR][2];
+  const uint8_t* mb = kcm + lrow * C * D;   // this head's code rows
+  const u32x2_t* mt = reinterpret_cast<const u32x2_t*>(kcm + mrows * D) + lrow * C;   // (b', s)
+  u32x4_t ka[UNR], kb2[UNR];
   u32x2_t ta[UNR], tb[UNR];
-  auto load = [&](int c0, u32x4_t(&kv)[UNR][2], u32x2_t(&tv)[UNR]) {
+  auto load = [&](int c0, u32x4_t(&kv)[UNR], u32x2_t(&tv)[UNR]) {
 #pragma unroll
     for (int u = 0; u < UNR; ++u) {
       const int c = min(c0 + u * CPM + mgrp, c_end - 1);
-      const uint16_t* row = mb + (int64_t)c * D;
-#pragma unroll
-      for (int x = 0; x < 2; ++x)   // the TPM lanes of a chunk read a whole 128-byte line per load
-        kv[u][x] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(row + 8 * (msub + TPM * x)));
+      // the TPM lanes of a chunk read its whole row (64 or 128 bytes) in one load
+      kv[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(mb + (int64_t)c * D + 16 * msub));
       // every lane loads the pair (the lanes of a chunk share it): a load under a lane mask
       // would make the compiler wait for all loads in flight
       tv[u] = __builtin_nontemporal_load(mt + c);
     }
   };
-  auto bound = [&](int c0, const u32x4_t(&kv)[UNR][2], const u32x2_t(&tv)[UNR]) {
+  auto bound = [&](int c0, const u32x4_t(&kv)[UNR], const u32x2_t(&tv)[UNR]) {
 #pragma unroll
     for (int u = 0; u < UNR; ++u) {
-      float s = 0.f;
+      const uint32_t wd[4] = {kv[u].x, kv[u].y, kv[u].z, kv[u].w};
+      float acc = 0.f;
 #pragma unroll
-      for (int x = 0; x < 2; ++x) {
-        // the words go through scalars: a bit cast of a vector element (v.y) is compiled
-        // as a cast of element 0 by this toolchain
-        const uint32_t wd[4] = {kv[u][x].x, kv[u][x].y, kv[u][x].z, kv[u][x].w};
+      for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int y = 0; y < 4; ++y)
-          s = __builtin_amdgcn_fdot2_f32_bf16(qp[4 * x + y], __builtin_bit_cast(bf16x2_t, wd[y]), s, false);
-      }
+        for (int y = 0; y < 4; ++y) acc = fmaf(qv[4 * i + y], (float)((wd[i] >> (8 * y)) & 0xffu), acc);
 #pragma unroll
-      for (int o = TPM / 2; o >= 1; o >>= 1) s += __shfl_xor(s, o);
+      for (int o = TPM / 2; o >= 1; o >>= 1) acc += __shfl_xor(acc, o);
       const int c = c0 + u * CPM + mgrp;
       if (msub == 0) {
-        const float bv = __uint_as_float(tv[u].x), nrm = __uint_as_float(tv[u].y);
-        const float sh = fmaf(s, tau, bv);
-        const float dl = fmaf(dfac, nrm, fmaf(0x1p-20f, fabsf(sh) + fabsf(bv), dabs * (nrm + 1.0f)));
+        const float bv = __uint_as_float(tv[u].x), sc = __uint_as_float(tv[u].y);
+        const float sh = fmaf(sc * (acc - q1x128), tau, bv);
+        const float dl = fmaf(dfac, sc, fmaf(0x1p-20f, fabsf(sh) + fabsf(bv), dabs));
         const bool live = c < c_end;
         keys[c - c_beg] = live ? make_key(sh - dl, c) : 0ull;
         ubs[c - c_beg] = live ? sh + dl : -INFINITY;
@@ -782,7 +779,7 @@ __global__ void __launch_bounds__(256) decode_scan_m(const IO* __restrict__ q, c
 }
 
 template <int D>
-static hipError_t launch_mirror_d(const float* kc, const float* bc, uint16_t* kcm, int BL, int C, int c_begin, int n,
+static hipError_t launch_mirror_d(const float* kc, const float* bc, uint8_t* kcm, int BL, int C, int c_begin, int n,
                                   hipStream_t st) {
   const int64_t rows = (int64_t)BL * n;
   const int64_t rpb = 256 / (D / 8);
@@ -792,7 +789,7 @@ static hipError_t launch_mirror_d(const float* kc, const float* bc, uint16_t* kc
   return hipGetLastError();
 }
 
-hipError_t launch_mirror(const Geom& g, const float* kc, const float* bc, uint16_t* kcm, int c_begin, int c_end,
+hipError_t launch_mirror(const Geom& g, const float* kc, const float* bc, uint8_t* kcm, int c_begin, int c_end,
                          hipStream_t st) {
   const int n = c_end - c_begin;
   if (n <= 0) return hipSuccess;
@@ -802,7 +799,7 @@ hipError_t launch_mirror(const Geom& g, const float* kc, const float* bc, uint16
 
 template <typename IO, int D>
 static hipError_t launch_decode_t(const Geom& g, const void* q, const void* kcache, const void* vcache,
-                                  const int32_t* seq_lens, const float* kc, const float* bc, const uint16_t* kcm,
+                                  const int32_t* seq_lens, const float* kc, const float* bc, const uint8_t* kcm,
                                   const void* Dw, const void* Uw, int32_t* sel_user, void* o, char* ws, hipStream_t st,
                                   hipEvent_t* ev, KvPages pg) {
   const DecodeWs w = decode_ws(g);
@@ -861,7 +858,7 @@ static hipError_t launch_decode_t(const Geom& g, const void* q, const void* kcac
 }
 
 hipError_t launch_decode(const Geom& g, const void* q, const void* kcache, const void* vcache, const int32_t* seq_lens,
-                         const float* kc, const float* bc, const uint16_t* kcm, const void* Dw, const void* Uw,
+                         const float* kc, const float* bc, const uint8_t* kcm, const void* Dw, const void* Uw,
                          int32_t* sel_idx_out, void* o, void* ws, size_t ws_bytes, hipStream_t st, hipEvent_t* ev,
                          KvPages pg) {
   if (ws_bytes < decode_workspace_bytes(g)) return hipErrorInvalidValue;

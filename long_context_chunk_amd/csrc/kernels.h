@@ -73,17 +73,17 @@ hipError_t launch_prefill_attend(const Geom& g, const void* q, const void* k, co
 
 // One decode step.
 size_t decode_workspace_bytes(const Geom& g);
-// kcm (nullable): the bf16 mirror of kc/bc (launch_mirror); when given, the scan reads it
+// kcm (nullable): the 8-bit mirror of kc/bc (launch_mirror); when given, the scan reads it
 // and the survivors of its score bounds are rescored exactly from kc/bc.
 // ev (nullable): four events recorded before the scan, after it, after the top-K merge, and
 // after chunk attention and fusion.
 hipError_t launch_decode(const Geom& g, const void* q, const void* kcache, const void* vcache, const int32_t* seq_lens,
-                         const float* kc, const float* bc, const uint16_t* kcm, const void* D, const void* U,
+                         const float* kc, const float* bc, const uint8_t* kcm, const void* D, const void* U,
                          int32_t* sel_idx_out, void* o, void* ws, size_t ws_bytes, hipStream_t st,
                          hipEvent_t* ev = nullptr, KvPages pg = KvPages());
-// The mirror of chunks [c_begin, c_end): in a buffer of B*Hlmk*C*(d + 4) uint16, the bf16
-// rows of k' [B*Hlmk*C, d], then per row b' and an upper bound of ||k'|| as fp32 pairs.
-hipError_t launch_mirror(const Geom& g, const float* kc, const float* bc, uint16_t* kcm, int c_begin, int c_end,
+// The mirror of chunks [c_begin, c_end): in a buffer of B*Hlmk*C*(d + 8) bytes, the 8-bit
+// codes of k' [B*Hlmk*C, d], then per row b' and the codes' scale as fp32 pairs.
+hipError_t launch_mirror(const Geom& g, const float* kc, const float* bc, uint8_t* kcm, int c_begin, int c_end,
                          hipStream_t st);
 
 // Dense causal attention (the baseline).

@@ -228,9 +228,9 @@ def attn_prefill_backward(dm: Dims, q, k, v, lmk_q, kc, sel_idx, sel_score, o, d
 
 
 def mirror_shape(dm: Dims):
-    """Shape of the landmark mirror: a flat int16 tensor of B*Hlmk*C*(d + 4) elements, the
-    bf16 rows of k' [B, Hlmk, C, d], then per row (b', an upper bound of ||k'||) as fp32."""
-    return (dm.B * dm.Hlmk * (dm.N // dm.S) * (dm.d + 4),)
+    """Shape of the landmark mirror: a flat uint8 tensor of B*Hlmk*C*(d + 8) bytes, the 8-bit
+    codes of k' [B, Hlmk, C, d], then per row (b', the codes' scale) as fp32 pairs."""
+    return (dm.B * dm.Hlmk * (dm.N // dm.S) * (dm.d + 8),)
 
 
 def landmark_mirror(dm: Dims, kc, bc, kc_mirror, c_begin=0, c_end=None):
@@ -239,7 +239,7 @@ def landmark_mirror(dm: Dims, kc, bc, kc_mirror, c_begin=0, c_end=None):
     c_end = C if c_end is None else c_end
     _req(kc, "kc", (dm.B, dm.Hlmk, C, dm.d), torch.float32)
     _req(bc, "bc", (dm.B, dm.Hlmk, C), torch.float32)
-    _req(kc_mirror, "kc_mirror", mirror_shape(dm), torch.int16)
+    _req(kc_mirror, "kc_mirror", mirror_shape(dm), torch.uint8)
     _check(load().hils_landmark_mirror(ctypes.byref(dm), _p(kc), _p(bc), c_begin, c_end, _p(kc_mirror), _stream()))
 
 
@@ -263,7 +263,7 @@ def attn_decode(dm: Dims, q, k_cache, v_cache, seq_lens, kc, bc, o, ws, qcal_D=N
     if sel_idx is not None:
         _req(sel_idx, "sel_idx", (dm.B, dm.Hq, dm.K), torch.int32)
     if kc_mirror is not None:
-        _req(kc_mirror, "kc_mirror", mirror_shape(dm), torch.int16)
+        _req(kc_mirror, "kc_mirror", mirror_shape(dm), torch.uint8)
         args = (ctypes.byref(dm), _p(q), _p(k_cache), _p(v_cache), _p(seq_lens), _p(kc), _p(bc), _p(kc_mirror),
                 _p(qcal_D), _p(qcal_U), _p(sel_idx), _p(o), _p(ws), ws.numel(), _stream())
         if timed:

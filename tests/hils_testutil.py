@@ -201,7 +201,7 @@ def gpu_decode(w, x, kc=None, bc=None, mirror=False):
     U = upload(x["U"], w.io) if w.qcal_rank else None
     kcm = None
     if mirror:
-        kcm = torch.zeros(hils.mirror_shape(dm), dtype=torch.int16, device="cuda")
+        kcm = torch.zeros(hils.mirror_shape(dm), dtype=torch.uint8, device="cuda")
         hils.landmark_mirror(dm, kc, bc, kcm)
     hils.attn_decode(dm, q, k, v, lens, kc, bc, o, ws, qcal_D=D, qcal_U=U, sel_idx=sel, kc_mirror=kcm)
     torch.cuda.synchronize()

@@ -2,11 +2,12 @@
 (hils_attn_decode_mirror).
 
 The mirror decode promises the result of hils_attn_decode bit for bit: its scan only
-bounds every chunk's score from the bf16 copy of k', and every chunk that can reach the
-top K is rescored exactly.  So each case here runs both calls on the same inputs and
+bounds every chunk's score from the 8-bit codes of k', and every chunk that can reach
+the top K is rescored exactly.  So each case here runs both calls on the same inputs and
 compares the selections and outputs bit for bit, and checks the mirror decode against
-the fp64 oracle as the other decode tests do.  The mirror's rows are checked against
-their definition (bf16 rounding to nearest even of k', b' bits, an upper bound of ||k'||).
+the fp64 oracle as the other decode tests do.  The mirror itself is checked against its
+definition (codes rint(k' * fl(127 / m)) + 128, scale fl(m / 127), b' bit for bit) and
+against the error bound the scan relies on, |k'_e - s (code_e - 128)| <= s (1/2 + 2^-16).
 """
 import sys
 
@@ -28,12 +29,6 @@ SEED = synth.BASE_SEED
 def _say(*a):
     print(*a, flush=True)
     sys.stdout.flush()
-
-
-def _bf16_rne_bits(x: np.ndarray) -> np.ndarray:
-    """bf16 bit pattern of fp32 values, rounded to nearest, ties to even (finite inputs)."""
-    b = np.ascontiguousarray(x, np.float32).view(np.uint32).astype(np.uint64)
-    return ((b + 0x7FFF + ((b >> 16) & 1)) >> 16).astype(np.uint16)
 
 
 def _decode_rows(w, x):
@@ -79,35 +74,43 @@ MIRROR_ROWS = [
 
 @pytest.mark.parametrize("name,w", MIRROR_ROWS, ids=[n for n, _ in MIRROR_ROWS])
 def test_mirror_rows(name, w):
-    """The mirror's bf16 plane holds bf16(k') (nearest even); its pair plane b' bit for bit
-    and an upper bound of ||k'||_2 within 2^-10 of it; a chunk range leaves the other
-    rows of both planes alone."""
+    """The code plane and the (b', scale) plane against their definition and the bound;
+    a chunk range leaves the other chunks of both planes alone; chunk 0 of every head is
+    all zeros (code 128, scale 0)."""
     _say("mirror rows", name)
     x = synth.make_inputs(w, SEED + 5)
     dm = dims_of(w)
     kc, bc = gpu_compress(w, x)
-    sentinel = 0x1357
-    kcm = torch.full(hils.mirror_shape(dm), sentinel, dtype=torch.int16, device="cuda")
+    kc[:, :, 4] = 0.0
+    torch.cuda.synchronize()
+    sentinel = 0x5A
+    kcm = torch.full(hils.mirror_shape(dm), sentinel, dtype=torch.uint8, device="cuda")
     c0, c1 = 3, w.C - 5
     hils.landmark_mirror(dm, kc, bc, kcm, c0, c1)
     torch.cuda.synchronize()
-    m = kcm.cpu().numpy().view(np.uint16)
+    m = kcm.cpu().numpy()
     kcn, bcn = kc.cpu().numpy(), bc.cpu().numpy()
     d, R = w.d, w.B * w.Hlmk * w.C
-    body = m[:R * d].reshape(w.B, w.Hlmk, w.C, d)
+    codes = m[:R * d].reshape(w.B, w.Hlmk, w.C, d)
     pairs = m[R * d:].view(np.uint32).reshape(w.B, w.Hlmk, w.C, 2)
-    for plane, fill in ((body, sentinel), (pairs, sentinel * 0x10001)):
-        assert np.all(plane[:, :, :c0] == fill) and np.all(plane[:, :, c1:] == fill), "rows outside the range changed"
-    np.testing.assert_array_equal(body[:, :, c0:c1], _bf16_rne_bits(kcn[:, :, c0:c1]))
+    for plane, fill in ((codes, sentinel), (pairs, sentinel * 0x01010101)):
+        assert np.all(plane[:, :, :c0] == fill) and np.all(plane[:, :, c1:] == fill), "chunks outside the range changed"
+    k = kcn[:, :, c0:c1]
+    mx = np.max(np.abs(k), axis=-1)
+    with np.errstate(divide="ignore"):
+        inv = np.where(mx > 0, np.float32(127.0) / mx, np.float32(0.0)).astype(np.float32)
+    want = (np.rint(k * inv[..., None]) + 128).astype(np.int64)
+    np.testing.assert_array_equal(codes[:, :, c0:c1].astype(np.int64), want)
     np.testing.assert_array_equal(pairs[:, :, c0:c1, 0], bcn[:, :, c0:c1].view(np.uint32))
-    nrm = pairs[:, :, c0:c1, 1].view(np.float32).astype(np.float64)
-    exact = np.sqrt(np.sum(kcn[:, :, c0:c1].astype(np.float64) ** 2, axis=-1))
-    assert np.all(nrm >= exact), "the norm bound is below ||k'||"
-    assert np.all(nrm <= exact * (1 + 2.0 ** -10) + 1e-29), "the norm bound is loose"
+    sc = pairs[:, :, c0:c1, 1].view(np.float32)
+    np.testing.assert_array_equal(sc, (mx / np.float32(127.0)).astype(np.float32))
+    assert np.all(codes[:, :, 4] == 128) and np.all(sc[:, :, 4 - c0] == 0)
+    err = np.abs(k.astype(np.float64) - sc[..., None].astype(np.float64) * (codes[:, :, c0:c1] - 128.0))
+    assert np.all(err <= sc[..., None] * (0.5 + 2.0 ** -16)), "a code misses its bound"
     # the empty range writes nothing
     hils.landmark_mirror(dm, kc, bc, kcm, 7, 7)
     torch.cuda.synchronize()
-    assert np.array_equal(kcm.cpu().numpy().view(np.uint16), m)
+    assert np.array_equal(kcm.cpu().numpy(), m)
 
 
 MIRROR_DECODE = DECODE_SMALL + DECODE_WINDOW + [
@@ -160,9 +163,9 @@ def test_decode_mirror_all_chunks_identical(K):
     assert np.array_equal(got, np.broadcast_to(np.arange(K), got.shape))
 
 
-def test_decode_mirror_near_ties_below_bf16_resolution():
-    """Chunks whose keys differ by far less than bf16 resolves: their mirror scores agree,
-    their exact scores do not; the exact ones decide."""
+def test_decode_mirror_near_ties_below_mirror_resolution():
+    """Chunks whose keys differ by far less than the 8-bit codes resolve: their mirror
+    bounds agree, their exact scores do not; the exact ones decide."""
     w = synth.Workload("mir_near", B=2, Hq=4, Hkv=2, d=128, N=8192, K=16, io=synth.F32, decode=True,
                        seq_lens=[8192, 6000], planted=False)
     _say("mirror decode near ties")
