@@ -196,10 +196,10 @@ int hils_attn_decode_timed(const hils_dims_t* dims, const void* q, const void* k
  * decode scan streams to about a quarter (a decode step reads every past chunk's
  * compressed key for step (2): aitrends.kr "Technical details" on the decode cost;
  * "Methodology" for the score).  kc_mirror: B*Hlmk*floor(N/S)*(d + 8) bytes (device,
- * caller-owned), two planes.  First the codes [B, Hlmk, floor(N/S), d] uint8: with
- * m = max_e |kc[b,l,c,e]|, code_e = rint(kc[b,l,c,e] * fl(127 / m)) + 128 (128 when
- * m = 0; rint rounds half to even).  Then for each (b, l, c) the pair
- * (bc[b,l,c], fl(m / 127)) as fp32 [B, Hlmk, floor(N/S), 2].
+ * caller-owned, 16-byte aligned), two planes.  First the codes [B, Hlmk, floor(N/S), d]
+ * int8: with m = max_e |kc[b,l,c,e]|, code_e = rint(kc[b,l,c,e] * fl(127 / m)) in
+ * [-127, 127] (0 when m = 0; rint rounds half to even).  Then for each (b, l, c) the
+ * pair (bc[b,l,c], fl(m / 127)) as fp32 [B, Hlmk, floor(N/S), 2].
  *
  * hils_landmark_mirror writes the mirror of chunks c_begin <= c < c_end from kc/bc
  * (call it wherever kc/bc of those chunks change, e.g. after hils_landmark_compress
@@ -210,7 +210,8 @@ int hils_attn_decode_timed(const hils_dims_t* dims, const void* q, const void* k
  * is the same as hils_attn_decode's, bit for bit (selection, scores and o): from a
  * chunk's codes the scan takes a lower and an upper bound of its exact fp32 score
  * (the codes' error is at most s/2 per element, so the dot product's is at most
- * (s/2) ||q^||_1, plus a margin for the fp32 sums); within each split of 1024 chunks,
+ * (s/2) ||q^||_1; q^ enters as two 8-bit parts, hi + lo/254, whose error adds about
+ * 1%, and a margin covers the fp32 sums); within each split of 1024 chunks,
  * every chunk whose upper bound reaches the split's K-th largest lower bound is
  * rescored exactly from kc/bc in hils_attn_decode's arithmetic, and the top K is taken
  * from those.  kc_mirror must hold every chunk that hils_attn_decode would score

@@ -206,7 +206,6 @@ __global__ void __launch_bounds__(256) decode_scan(const IO* __restrict__ q, con
   const int P = candidate_chunks(L - 1, C, nw);
   const int c_beg = sp * DS_CHUNKS, c_end = min(P, c_beg + DS_CHUNKS);
   const int t = threadIdx.x, lane = t & 63, w = t >> 6;
-  qhat_to_lds<IO, D>(q + (int64_t)bh * D, Dw, Uw, h, r, qs, ts);
   // TPC threads per chunk, each holding 16 of the D head dims as 4 float4 spread so
   // that the TPC lanes of a chunk read 128 contiguous bytes per load
   constexpr int TPC = D / 16;
@@ -214,9 +213,6 @@ __global__ void __launch_bounds__(256) decode_scan(const IO* __restrict__ q, con
   constexpr int UNR = 2;            // passes per register buffer
   constexpr int STEP = CPP * UNR;
   const int sub = t % TPC, grp = t / TPC;
-  f32x4_t qv[4];
-#pragma unroll
-  for (int j = 0; j < 4; ++j) qv[j] = *reinterpret_cast<const f32x4_t*>(&qs[4 * (sub + TPC * j)]);
   const float tau = 1.0f / sqrtf((float)D);
   const int64_t lrow = (int64_t)b * Hl + h / (Hq / Hl);   // the query head's landmark head
   const float* kb = kc + lrow * C * D;
@@ -236,6 +232,12 @@ __global__ void __launch_bounds__(256) decode_scan(const IO* __restrict__ q, con
       bv[u] = bb[c];
     }
   };
+  // the first buffer's loads go out before q^ is prepared (they do not depend on it)
+  if (c_beg < c_end) load(c_beg, ka, ba);
+  qhat_to_lds<IO, D>(q + (int64_t)bh * D, Dw, Uw, h, r, qs, ts);
+  f32x4_t qv[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) qv[j] = *reinterpret_cast<const f32x4_t*>(&qs[4 * (sub + TPC * j)]);
   auto score = [&](int c0, const f32x4_t(&kv)[UNR][4], const float(&bv)[UNR]) {
 #pragma unroll
     for (int u = 0; u < UNR; ++u) {
@@ -258,7 +260,6 @@ __global__ void __launch_bounds__(256) decode_scan(const IO* __restrict__ q, con
   static_assert(DS_CHUNKS % (2 * STEP) == 0, "");
   constexpr int NIT = DS_CHUNKS / (2 * STEP);
   if (c_beg < c_end) {   // uniform
-    load(c_beg, ka, ba);
     for (int it = 0; it < NIT - 1; ++it) {
       const int c0 = c_beg + it * 2 * STEP;
       load(c0 + STEP, kb2, bb2);
@@ -517,10 +518,10 @@ __global__ void __launch_bounds__(256) decode_combine(const float* __restrict__ 
 
 // ---------------------------------------------------------------- landmark mirror
 // An 8-bit mirror of the landmark cache for the decode scan, in two planes: per row
-// (b, l, c) the codes u_e = rint(k'_e * (127 / m)) + 128 with m = max_e |k'_e| (d bytes,
-// so a row is one or two whole cache lines), then per row the pair (b'_c, s_c = m / 127)
-// as fp32 [B*Hlmk*C, 2].  |k'_e - s_c (u_e - 128)| <= s_c (1/2 + 2^-16): the rounding to
-// an integer, plus the fp32 roundings of 127 / m and of the product.
+// (b, l, c) the signed codes u_e = rint(k'_e * (127 / m)) in [-127, 127], m = max_e |k'_e|
+// (d bytes, so a row is one or two whole cache lines), then per row the pair
+// (b'_c, s_c = m / 127) as fp32 [B*Hlmk*C, 2].  |k'_e - s_c u_e| <= s_c (1/2 + 2^-16): the
+// rounding to an integer, plus the fp32 roundings of 127 / m and of the product.
 template <int D>
 __global__ void __launch_bounds__(256) mirror_build(const float* __restrict__ kc, const float* __restrict__ bc,
                                                     uint8_t* __restrict__ kcm, int C, int c_begin, int n,
@@ -551,8 +552,8 @@ __global__ void __launch_bounds__(256) mirror_build(const float* __restrict__ kc
       uint32_t wd[2] = {0u, 0u};
 #pragma unroll
       for (int m = 0; m < 8; ++m) {
-        const int code = (int)rintf(x[m] * inv) + 128;   // |x * inv| <= 127 (1 + 2^-23)
-        wd[m >> 2] |= (uint32_t)code << (8 * (m & 3));
+        const int code = (int)rintf(x[m] * inv);   // |x * inv| <= 127 (1 + 2^-23)
+        wd[m >> 2] |= ((uint32_t)code & 0xffu) << (8 * (m & 3));
       }
       *reinterpret_cast<u32x2_t*>(kcm + r * D + 8 * sub) = u32x2_t{wd[0], wd[1]};
       if (sub == 0)
@@ -563,9 +564,10 @@ __global__ void __launch_bounds__(256) mirror_build(const float* __restrict__ kc
 
 // The decode scan over the mirror.  Per chunk, from the mirror row, a lower and an upper
 // bound of the exact score, L <= s <= U with s = fmaf(q^ . k', tau, b') as decode_scan
-// computes it in fp32.  Within the workgroup's chunks, theta = the n-th largest L (n =
-// min(K, chunks)) is at most the n-th best exact score there, so every chunk among the
-// workgroup's exact best n has U >= theta: those survivors are rescored exactly from the
+// computes it in fp32.  Within the workgroup's chunks, theta = the n-th largest of a
+// subset of the L (n = min(K, chunks)) is at most the n-th largest L there, hence at most
+// the n-th best exact score, so every chunk among the workgroup's exact best n has
+// U >= theta: those survivors are rescored exactly from the
 // fp32 k' and b' in decode_scan's arithmetic (same lanes, same order of sums, so the
 // same bits), and the best of their exact keys are written as decode_scan writes its
 // list.  The list's first n entries equal decode_scan's; further entries (exact keys of
@@ -584,8 +586,17 @@ __global__ void __launch_bounds__(256) decode_scan_m(const IO* __restrict__ q, c
   constexpr int CPP = 256 / TPC;
   __shared__ __align__(16) float qs[D];
   __shared__ float ts[32];
-  __shared__ float q1_s, l1_s, theta_s;
-  __shared__ uint64_t keys[DS_CHUNKS];   // lower-bound keys, then the survivors' exact keys
+  __shared__ float mq_s, l1_s;
+  // theta comes from the T largest lower bounds of each chunk lane (NCL lanes, each
+  // bounding every NCL-th chunk): the n-th largest of a subset is at most the n-th largest
+  // of all, and with T = 2..4 it loses almost nothing (the survivors grow by about 2%)
+  constexpr int NCL = 256 / TPM;
+  constexpr int T = NCL == 32 ? (KB ? 4 : 3) : (KB ? 3 : 2);
+  constexpr int NV = NCL * T;
+  static_assert(NV <= 256 && NV % 4 == 0, "");
+  __shared__ __align__(16) float lb_s[NV];   // each chunk lane's T largest lower bounds
+  __shared__ float thw[4];
+  __shared__ uint64_t keys[DS_CHUNKS];   // the survivors' exact keys
   __shared__ float ubs[DS_CHUNKS];       // upper bounds
   __shared__ int16_t surv[DS_CHUNKS];    // survivors (offsets in the workgroup's range)
   __shared__ uint64_t wl[4][64];
@@ -602,35 +613,7 @@ __global__ void __launch_bounds__(256) decode_scan_m(const IO* __restrict__ q, c
     if (t < DS_KEEP) out[t] = 0ull;
     return;
   }
-  qhat_to_lds<IO, D>(q + (int64_t)bh * D, Dw, Uw, h, r, qs, ts);
-  if (w == 0) {   // sum_e q^_e and an upper bound of sum_e |q^_e|
-    float a = 0.f, ab = 0.f;
-    for (int e = lane; e < D; e += 64) {
-      a += qs[e];
-      ab += fabsf(qs[e]);
-    }
-    a = wave_sum(a);
-    ab = wave_sum(ab);
-    if (lane == 0) {
-      q1_s = a;
-      l1_s = ab * (1.0f + 1.0f / 4096.0f);
-    }
-  }
-  __syncthreads();
   const int msub = t % TPM, mgrp = t / TPM;
-  float qv[16];   // dims 16 msub + i
-#pragma unroll
-  for (int i = 0; i < 16; ++i) qv[i] = qs[16 * msub + i];
-  const float tau = 1.0f / sqrtf((float)D);
-  const float q1x128 = 128.0f * q1_s;
-  // Per chunk, with s its scale: |s sum_e q^_e (u_e - 128) - q^ . k'| <= s ||q^||_1 (1/2 +
-  // 2^-16).  The fp32 sums (the codes' sum, 128 sum q^_e, the product with s, and the exact
-  // path's own dot product) add at most about 510 D 2^-24 s ||q^||_1 < 0.004 s ||q^||_1 for
-  // D <= 128: the factor 1/2 + 2^-5 covers all of it.  The roundings of the last fma
-  // (s tau + b') on both sides are covered by 2^-20 (|s| + |b'|), values below the normal
-  // range by a tiny absolute term.
-  const float dfac = tau * l1_s * (0.5f + 1.0f / 32.0f);
-  const float dabs = 0x1p-110f * (l1_s + 1.0f);
   const int64_t lrow = (int64_t)b * Hl + h / (Hq / Hl);
   const uint8_t* mb = kcm + lrow * C * D;   // this head's code rows
   const u32x2_t* mt = reinterpret_cast<const u32x2_t*>(kcm + mrows * D) + lrow * C;   // (b', s)
@@ -647,25 +630,82 @@ __global__ void __launch_bounds__(256) decode_scan_m(const IO* __restrict__ q, c
       tv[u] = __builtin_nontemporal_load(mt + c);
     }
   };
+  // the first buffer's loads go out before q^ is prepared (they do not depend on it)
+  load(c_beg, ka, ta);
+  qhat_to_lds<IO, D>(q + (int64_t)bh * D, Dw, Uw, h, r, qs, ts);
+  if (w == 0) {   // an upper bound of sum_e |q^_e|, and max_e |q^_e|
+    float ab = 0.f, mq = 0.f;
+    for (int e = lane; e < D; e += 64) {
+      ab += fabsf(qs[e]);
+      mq = fmaxf(mq, fabsf(qs[e]));
+    }
+    ab = wave_sum(ab);
+    mq = wave_max(mq);
+    if (lane == 0) {
+      l1_s = ab * (1.0f + 1.0f / 4096.0f);
+      mq_s = mq;
+    }
+  }
+  __syncthreads();
+  // q^ in two 8-bit parts: x_e = q^_e * fl(127 / max|q^|), hi_e = rint(x_e),
+  // lo_e = rint((x_e - hi_e) * 254), so q^_e = s_q (hi_e + lo_e / 254) within
+  // s_q (0.5 + 2^-17) / 254 + s_q 127 2^-21 < 0.0021 s_q, s_q = fl(max|q^| / 127).
+  // Lane msub holds dims 16 msub + 4 i + y as byte y of word i.
+  const float mq = mq_s;
+  const float invq = mq > 0.f ? 127.0f / mq : 0.f, sq = mq / 127.0f;
+  int qhi[4], qlo[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    uint32_t h4 = 0u, l4 = 0u;
+#pragma unroll
+    for (int y = 0; y < 4; ++y) {
+      const float x = qs[16 * msub + 4 * i + y] * invq;
+      const float hf = rintf(x);
+      const int lo = (int)rintf((x - hf) * 254.0f);
+      h4 |= ((uint32_t)(int)hf & 0xffu) << (8 * y);
+      l4 |= ((uint32_t)lo & 0xffu) << (8 * y);
+    }
+    qhi[i] = (int)h4;
+    qlo[i] = (int)l4;
+  }
+  const float tau = 1.0f / sqrtf((float)D);
+  // Per chunk, with s its scale and u its codes: the mirror's dot product is
+  // s s_q (sum hi_e u_e + (sum lo_e u_e) / 254) (integer sums, exact), and
+  //   |q^ . k' - that| <= s (1/2 + 2^-16) ||q^||_1 + 0.0021 s_q s sum_e |u_e|
+  //                    <= s (||q^||_1 (1/2 + 2^-16) + 0.27 D s_q).
+  // The fp32 steps (the lanes' sums, the products with s and s_q, and the exact path's own
+  // dot product, at most about 127 D 2^-24 s ||q^||_1) take far less than the 2^-5 margin
+  // on the first term.  The roundings of the last fma (s tau + b') on both sides are covered
+  // by 2^-20 (|s| + |b'|), values below the normal range by a tiny absolute term.
+  const float dfac = tau * (l1_s * (0.5f + 1.0f / 32.0f) + 0.27f * (float)D * sq);
+  const float dabs = 0x1p-110f * (l1_s + 1.0f);
+  float top[T];   // this chunk lane's largest lower bounds, descending
+#pragma unroll
+  for (int k = 0; k < T; ++k) top[k] = -INFINITY;
   auto bound = [&](int c0, const u32x4_t(&kv)[UNR], const u32x2_t(&tv)[UNR]) {
 #pragma unroll
     for (int u = 0; u < UNR; ++u) {
-      const uint32_t wd[4] = {kv[u].x, kv[u].y, kv[u].z, kv[u].w};
-      float acc = 0.f;
+      const int wd[4] = {(int)kv[u].x, (int)kv[u].y, (int)kv[u].z, (int)kv[u].w};
+      int ih = 0, il = 0;
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int y = 0; y < 4; ++y) acc = fmaf(qv[4 * i + y], (float)((wd[i] >> (8 * y)) & 0xffu), acc);
+      for (int i = 0; i < 4; ++i) {
+        ih = __builtin_amdgcn_sdot4(qhi[i], wd[i], ih, false);
+        il = __builtin_amdgcn_sdot4(qlo[i], wd[i], il, false);
+      }
+      float acc = fmaf((float)il, 1.0f / 254.0f, (float)ih);
 #pragma unroll
       for (int o = TPM / 2; o >= 1; o >>= 1) acc += __shfl_xor(acc, o);
       const int c = c0 + u * CPM + mgrp;
       if (msub == 0) {
         const float bv = __uint_as_float(tv[u].x), sc = __uint_as_float(tv[u].y);
-        const float sh = fmaf(sc * (acc - q1x128), tau, bv);
+        const float sh = fmaf((sc * sq) * acc, tau, bv);
         const float dl = fmaf(dfac, sc, fmaf(0x1p-20f, fabsf(sh) + fabsf(bv), dabs));
         const bool live = c < c_end;
-        keys[c - c_beg] = live ? make_key(sh - dl, c) : 0ull;
+        const float lv = live ? sh - dl : -INFINITY;
         ubs[c - c_beg] = live ? sh + dl : -INFINITY;
+#pragma unroll
+        for (int k = T - 1; k >= 1; --k) top[k] = fmaxf(top[k], fminf(top[k - 1], lv));
+        top[0] = fmaxf(top[0], lv);
       }
     }
   };
@@ -674,7 +714,6 @@ __global__ void __launch_bounds__(256) decode_scan_m(const IO* __restrict__ q, c
   // loads in flight the compiler waits for exactly the buffer it is about to use.
   static_assert(DS_CHUNKS % (2 * STEP) == 0, "");
   constexpr int NIT = DS_CHUNKS / (2 * STEP);
-  load(c_beg, ka, ta);
   for (int it = 0; it < NIT - 1; ++it) {
     const int c0 = c_beg + it * 2 * STEP;
     load(c0 + STEP, kb2, tb);
@@ -688,20 +727,28 @@ __global__ void __launch_bounds__(256) decode_scan_m(const IO* __restrict__ q, c
     bound(c0, ka, ta);
     bound(c0 + STEP, kb2, tb);
   }
+  if (msub == 0)
+#pragma unroll
+    for (int k = 0; k < T; ++k) lb_s[mgrp * T + k] = top[k];
   __syncthreads();
-  // theta: rank n - 1 of the lower bounds
-  if constexpr (KB) {
-    uint64_t hi, lo;
-    best64_of_1024(keys, wl, hi, lo);
-    const uint64_t kk = kl::rank_key(hi, lo, n - 1, lane);
-    if (t == 0) theta_s = key_score(kk);
-  } else {
-    const uint64_t lk = best32_of_1024(keys, wl);
-    const uint64_t kk = __shfl(lk, n - 1);
-    if (t == 0) theta_s = key_score(kk);
+  // theta: the largest of those lower bounds that at least n of them reach
+  {
+    float cand = -INFINITY;
+    if (t < NV) {
+      const float v = lb_s[t];
+      int cnt = 0;
+#pragma unroll 8
+      for (int x = 0; x < NV; x += 4) {
+        const f32x4_t y = *reinterpret_cast<const f32x4_t*>(&lb_s[x]);
+        cnt += (int)(y.x >= v) + (int)(y.y >= v) + (int)(y.z >= v) + (int)(y.w >= v);
+      }
+      cand = cnt >= n ? v : -INFINITY;
+    }
+    cand = wave_max(cand);
+    if (lane == 0) thw[w] = cand;
   }
   __syncthreads();
-  const float theta = theta_s;
+  const float theta = fmaxf(fmaxf(thw[0], thw[1]), fmaxf(thw[2], thw[3]));
   // survivors U >= theta, in chunk order
   int ns = 0;
 #pragma unroll
@@ -732,25 +779,34 @@ __global__ void __launch_bounds__(256) decode_scan_m(const IO* __restrict__ q, c
     for (int y = 0; y < 4; ++y) qe[y] = *reinterpret_cast<const f32x4_t*>(&qs[4 * (sub + TPC * y)]);
     const float* kb = kc + lrow * C * D;
     const float* bb = bc + lrow * C;
-    for (int p0 = 0; p0 < ns; p0 += CPP) {
-      const int x = p0 + grp;
-      const int c = c_beg + surv[min(x, ns - 1)];
-      const f32x4_t* row = reinterpret_cast<const f32x4_t*>(kb + (int64_t)c * D);
-      f32x4_t kv[4];
+    // two survivors per thread group at a time, both rows' loads issued before either sum
+    for (int p0 = 0; p0 < ns; p0 += 2 * CPP) {
+      int xs[2], cs[2];
+      f32x4_t kv[2][4];
+      float bv[2];
 #pragma unroll
-      for (int y = 0; y < 4; ++y) kv[y] = row[sub + TPC * y];
-      const float bv = bb[c];
-      float s = 0.f;
+      for (int v = 0; v < 2; ++v) {
+        xs[v] = p0 + v * CPP + grp;
+        cs[v] = c_beg + surv[min(xs[v], ns - 1)];
+        const f32x4_t* row = reinterpret_cast<const f32x4_t*>(kb + (int64_t)cs[v] * D);
 #pragma unroll
-      for (int y = 0; y < 4; ++y) {
-        s = fmaf(qe[y].x, kv[y].x, s);
-        s = fmaf(qe[y].y, kv[y].y, s);
-        s = fmaf(qe[y].z, kv[y].z, s);
-        s = fmaf(qe[y].w, kv[y].w, s);
+        for (int y = 0; y < 4; ++y) kv[v][y] = row[sub + TPC * y];
+        bv[v] = bb[cs[v]];
       }
 #pragma unroll
-      for (int o = TPC / 2; o >= 1; o >>= 1) s += __shfl_xor(s, o);
-      if (sub == 0 && x < ns) keys[x] = make_key(fmaf(s, tau, bv), c);
+      for (int v = 0; v < 2; ++v) {
+        float s = 0.f;
+#pragma unroll
+        for (int y = 0; y < 4; ++y) {
+          s = fmaf(qe[y].x, kv[v][y].x, s);
+          s = fmaf(qe[y].y, kv[v][y].y, s);
+          s = fmaf(qe[y].z, kv[v][y].z, s);
+          s = fmaf(qe[y].w, kv[v][y].w, s);
+        }
+#pragma unroll
+        for (int o = TPC / 2; o >= 1; o >>= 1) s += __shfl_xor(s, o);
+        if (sub == 0 && xs[v] < ns) keys[xs[v]] = make_key(fmaf(s, tau, bv[v]), cs[v]);
+      }
     }
   }
   __syncthreads();

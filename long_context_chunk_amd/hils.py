@@ -228,8 +228,8 @@ def attn_prefill_backward(dm: Dims, q, k, v, lmk_q, kc, sel_idx, sel_score, o, d
 
 
 def mirror_shape(dm: Dims):
-    """Shape of the landmark mirror: a flat uint8 tensor of B*Hlmk*C*(d + 8) bytes, the 8-bit
-    codes of k' [B, Hlmk, C, d], then per row (b', the codes' scale) as fp32 pairs."""
+    """Shape of the landmark mirror: a flat uint8 tensor of B*Hlmk*C*(d + 8) bytes, the signed
+    8-bit codes of k' [B, Hlmk, C, d], then per row (b', the codes' scale) as fp32 pairs."""
     return (dm.B * dm.Hlmk * (dm.N // dm.S) * (dm.d + 8),)
 
 

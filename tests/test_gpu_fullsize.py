@@ -99,6 +99,12 @@ def test_decode_full_size():
     _say("full-size decode", w.name)
     x = synth.make_inputs(w, SEED + 1)
     g = gpu_decode(w, x)
+    # the step the benchmark times: the scan over the 8-bit landmark mirror, whose result
+    # must be hils_attn_decode's bit for bit (so the oracle comparison below covers both)
+    gm = gpu_decode(w, x, kc=g["kc"], bc=g["bc"], mirror=True)
+    np.testing.assert_array_equal(gm["sel_idx"], g["sel_idx"])
+    np.testing.assert_array_equal(gm["o_bits"], g["o_bits"])
+    del gm
     kc_g = g["kc"].cpu().numpy()
     rows_b = [b for b in range(w.B) for h in range(w.Hq)]
     rows_h = [h for b in range(w.B) for h in range(w.Hq)]

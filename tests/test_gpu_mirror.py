@@ -6,8 +6,8 @@ bounds every chunk's score from the 8-bit codes of k', and every chunk that can 
 the top K is rescored exactly.  So each case here runs both calls on the same inputs and
 compares the selections and outputs bit for bit, and checks the mirror decode against
 the fp64 oracle as the other decode tests do.  The mirror itself is checked against its
-definition (codes rint(k' * fl(127 / m)) + 128, scale fl(m / 127), b' bit for bit) and
-against the error bound the scan relies on, |k'_e - s (code_e - 128)| <= s (1/2 + 2^-16).
+definition (signed codes rint(k' * fl(127 / m)), scale fl(m / 127), b' bit for bit) and
+against the error bound the scan relies on, |k'_e - s code_e| <= s (1/2 + 2^-16).
 """
 import sys
 
@@ -75,8 +75,8 @@ MIRROR_ROWS = [
 @pytest.mark.parametrize("name,w", MIRROR_ROWS, ids=[n for n, _ in MIRROR_ROWS])
 def test_mirror_rows(name, w):
     """The code plane and the (b', scale) plane against their definition and the bound;
-    a chunk range leaves the other chunks of both planes alone; chunk 0 of every head is
-    all zeros (code 128, scale 0)."""
+    a chunk range leaves the other chunks of both planes alone; an all-zero chunk gets
+    codes 0 and scale 0."""
     _say("mirror rows", name)
     x = synth.make_inputs(w, SEED + 5)
     dm = dims_of(w)
@@ -91,21 +91,21 @@ def test_mirror_rows(name, w):
     m = kcm.cpu().numpy()
     kcn, bcn = kc.cpu().numpy(), bc.cpu().numpy()
     d, R = w.d, w.B * w.Hlmk * w.C
-    codes = m[:R * d].reshape(w.B, w.Hlmk, w.C, d)
+    codes = m[:R * d].view(np.int8).reshape(w.B, w.Hlmk, w.C, d)
     pairs = m[R * d:].view(np.uint32).reshape(w.B, w.Hlmk, w.C, 2)
-    for plane, fill in ((codes, sentinel), (pairs, sentinel * 0x01010101)):
+    for plane, fill in ((codes, sentinel), (pairs, sentinel * 0x01010101)):   # 0x5A < 128: the same as int8
         assert np.all(plane[:, :, :c0] == fill) and np.all(plane[:, :, c1:] == fill), "chunks outside the range changed"
     k = kcn[:, :, c0:c1]
     mx = np.max(np.abs(k), axis=-1)
     with np.errstate(divide="ignore"):
         inv = np.where(mx > 0, np.float32(127.0) / mx, np.float32(0.0)).astype(np.float32)
-    want = (np.rint(k * inv[..., None]) + 128).astype(np.int64)
+    want = np.rint(k * inv[..., None]).astype(np.int64)
     np.testing.assert_array_equal(codes[:, :, c0:c1].astype(np.int64), want)
     np.testing.assert_array_equal(pairs[:, :, c0:c1, 0], bcn[:, :, c0:c1].view(np.uint32))
     sc = pairs[:, :, c0:c1, 1].view(np.float32)
     np.testing.assert_array_equal(sc, (mx / np.float32(127.0)).astype(np.float32))
-    assert np.all(codes[:, :, 4] == 128) and np.all(sc[:, :, 4 - c0] == 0)
-    err = np.abs(k.astype(np.float64) - sc[..., None].astype(np.float64) * (codes[:, :, c0:c1] - 128.0))
+    assert np.all(codes[:, :, 4] == 0) and np.all(sc[:, :, 4 - c0] == 0)
+    err = np.abs(k.astype(np.float64) - sc[..., None].astype(np.float64) * codes[:, :, c0:c1])
     assert np.all(err <= sc[..., None] * (0.5 + 2.0 ** -16)), "a code misses its bound"
     # the empty range writes nothing
     hils.landmark_mirror(dm, kc, bc, kcm, 7, 7)
