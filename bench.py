@@ -415,6 +415,7 @@ def run_decode(wd, steps, warmup, seed, dense=False):
     comp_ms = e0.elapsed_time(e1)
     # the 8-bit landmark mirror (built once per chunk, like k' and b'): the scan reads it
     kcm = torch.empty(hils.mirror_shape(dm), dtype=torch.uint8, device="cuda")
+    hils.landmark_mirror(dm, kc, bc, kcm)   # the first launch also loads the kernel: time the second
     e0.record()
     hils.landmark_mirror(dm, kc, bc, kcm)
     e1.record()
