@@ -22,6 +22,10 @@
 #include "hils_common.h"
 #include "keylists.h"
 #include "kernels.h"
+#include <atomic>
+#include <type_traits>
+#include <atomic>
+#include <type_traits>
 
 namespace hils {
 
@@ -473,6 +477,169 @@ __global__ void __launch_bounds__(256) decode_attend(const IO* __restrict__ q, c
 // selected chunks and the window's chunks from the own one back to chunk 0 (at most nw).
 // Lane s of every wave holds slot s's weight (MAXS = 128: slot 64 + s's too); the live
 // slot rows are all loaded at once.
+// Chunk attention and fusion of one (b, h) in one workgroup of four groups of 256 threads
+// (bf16 I/O).  Slots are the same as decode_attend's; group g takes slots g, g + 4, ...
+// Per slot a group computes what decode_attend computes (the chunk's softmax output o_c
+// and its score: the selection score, or the window chunk's exact log-sum-exp) and folds
+// it into a running fusion (m, z, acc) with an online softmax; the next slot's K and V
+// rows are loaded while the current one is computed.  At the end the four groups' running
+// fusions are merged.  It gives decode_combine's result up to the order of the fp32 sums.
+template <int D>
+__global__ void __launch_bounds__(1024) decode_attend_fused(const bf16_t* __restrict__ q,
+                                                            const bf16_t* __restrict__ kcache,
+                                                            const bf16_t* __restrict__ vcache,
+                                                            const int32_t* __restrict__ seq_lens,
+                                                            const int32_t* __restrict__ sel_i,
+                                                            const float* __restrict__ sel_s,
+                                                            const int32_t* __restrict__ nsel, bf16_t* __restrict__ out,
+                                                            int Hq, int Hkv, int N, int K, int nw, KvPages pg) {
+  constexpr int KJ = D / 32;        // logits: 4 threads per key, KJ runs of 8 dims each
+  constexpr int TPR = D / 8;        // values: threads per row (8 dims each)
+  constexpr int NG = 256 / TPR;     // key groups
+  constexpr int KPG = 64 / NG;      // keys per group
+  constexpr int MAXSL = 96;         // K + nw <= 64 + 32
+  __shared__ float z[4][64];
+  __shared__ float ml[4][2];
+  __shared__ float red[4][NG][D];
+  __shared__ int s_c[MAXSL], s_nk[MAXSL];
+  __shared__ int64_t s_row[MAXSL];   // first K/V row of the slot's chunk (row 0 when none)
+  __shared__ float s_sc[MAXSL];
+  __shared__ float f_m[4], f_z[4];
+  __shared__ float f_acc[4][D];
+  __shared__ __align__(16) bf16_t qsh[D];   // the query (read per slot, not held in registers)
+  const int bh = blockIdx.x, b = bh / Hq, h = bh % Hq, kvh = h / (Hq / Hkv);
+  const int t = threadIdx.x, g = t >> 8, tg = t & 255, lane = t & 63;
+  const int L = seq_lens[b];
+  const int NSL = K + nw;
+  if (t < NSL) {   // slot table: chunk (-1: nothing), keys, score (selected slots)
+    int c = -1, nk = 64;
+    float sc = 0.f;
+    if (t >= K) {
+      c = (L - 1) / 64 - (t - K);
+      if (t == K) nk = L - c * 64;
+      if (c < 0) c = -1;
+    } else if (t < nsel[bh]) {
+      c = sel_i[(int64_t)bh * K + t];
+      sc = sel_s[(int64_t)bh * K + t];
+      if (c < 0) c = -1;
+    }
+    s_c[t] = c;
+    s_nk[t] = c >= 0 ? nk : 1;
+    s_sc[t] = sc;
+    s_row[t] = pg.chunk_row(b, kvh, Hkv, N, max(c, 0));
+  }
+  const int key = tg >> 2, qd = tg & 3;
+  const int e8 = (tg % TPR) * 8, kg = tg / TPR;
+  if (t < D / 8) *reinterpret_cast<u32x4_t*>(&qsh[8 * t]) = *reinterpret_cast<const u32x4_t*>(q + (int64_t)bh * D + 8 * t);
+  __syncthreads();
+  const int nit = (NSL + 3) / 4;
+  // K and V rows of slot s into a register buffer; slots with no chunk load row 0 of the
+  // (b, kv head) (in bounds) and are skipped
+  auto load = [&](int s, raw8<bf16_t>(&kr)[KJ], raw8<bf16_t>(&vr)[KPG]) {
+    const int sl = min(s, NSL - 1);   // slots past the table load a real slot's rows (in bounds)
+    const int nk = s_nk[sl];
+    const int64_t row0 = s_row[sl];
+    const bf16_t* krow = kcache + (row0 + min(key, nk - 1)) * D;
+#pragma unroll
+    for (int j = 0; j < KJ; ++j) kr[j].load(krow + 8 * (qd + 4 * j));
+#pragma unroll
+    for (int u = 0; u < KPG; ++u) vr[u].load(vcache + (row0 + min(kg * KPG + u, nk - 1)) * D + e8);
+  };
+  const float tau = 1.0f / sqrtf((float)D);
+  float run_m = -INFINITY, run_z = 0.f, acc = 0.f;   // the group's running fusion (acc: dim tg)
+  raw8<bf16_t> ka[KJ], va[KPG], kb2[KJ], vb2[KPG];
+  auto step = [&](int s, const raw8<bf16_t>(&kr)[KJ], const raw8<bf16_t>(&vr)[KPG]) {
+    const int c = s < NSL ? s_c[s] : -1;   // uniform in the group
+    const int nk = s_nk[min(s, NSL - 1)];
+    {
+      float sv = 0.f;
+#pragma unroll
+      for (int j = 0; j < KJ; ++j) {
+        raw8<bf16_t> qr;
+        qr.load(&qsh[8 * (qd + 4 * j)]);
+#pragma unroll
+        for (int m = 0; m < 8; ++m) sv = fmaf(qr[m], kr[j][m], sv);
+      }
+      sv += __shfl_xor(sv, 1);
+      sv += __shfl_xor(sv, 2);
+      if (qd == 0) z[g][key] = key < nk ? sv * tau : -INFINITY;
+    }
+    __syncthreads();
+    if ((tg >> 6) == 0) {
+      const float zz = z[g][lane];
+      const float m = wave_max(zz);
+      const float p = zz == -INFINITY ? 0.f : __expf(zz - m);
+      const float l = wave_sum(p);
+      z[g][lane] = p;
+      if (lane == 0) {
+        ml[g][0] = m;
+        ml[g][1] = l;
+      }
+    }
+    __syncthreads();
+    {
+      float a[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int u = 0; u < KPG; ++u) {
+        const float pj = z[g][kg * KPG + u];
+#pragma unroll
+        for (int m = 0; m < 8; ++m) a[m] = fmaf(pj, vr[u][m], a[m]);
+      }
+#pragma unroll
+      for (int m = 0; m < 8; ++m) red[g][kg][e8 + m] = a[m];
+    }
+    __syncthreads();
+    if (c >= 0 && tg < D) {
+      float o = 0.f;
+#pragma unroll
+      for (int g2 = 0; g2 < NG; ++g2) o += red[g][g2][tg];
+      const float l = ml[g][1];
+      const float sig = s >= K ? ml[g][0] + logf(l) : s_sc[s];
+      const float mn = fmaxf(run_m, sig);
+      const float a1 = __expf(run_m - mn), a2 = __expf(sig - mn);
+      run_z = fmaf(run_z, a1, a2);
+      acc = fmaf(acc, a1, (o / l) * a2);
+      run_m = mn;
+    }
+  };
+  // double buffer over the group's slots (every group runs nit iterations: the barriers
+  // inside step are workgroup-wide)
+  load(g, ka, va);
+  int it = 0;
+  for (; it + 2 < nit; it += 2) {
+    load(4 * (it + 1) + g, kb2, vb2);
+    step(4 * it + g, ka, va);
+    load(4 * (it + 2) + g, ka, va);
+    step(4 * (it + 1) + g, kb2, vb2);
+  }
+  if (it + 1 < nit) {   // two iterations left
+    load(4 * (it + 1) + g, kb2, vb2);
+    step(4 * it + g, ka, va);
+    step(4 * (it + 1) + g, kb2, vb2);
+  } else {              // one left
+    step(4 * it + g, ka, va);
+  }
+  if (tg < D) {
+    f_acc[g][tg] = acc;
+    if (tg == 0) {
+      f_m[g] = run_m;
+      f_z[g] = run_z;
+    }
+  }
+  __syncthreads();
+  if (t < D) {
+    const float M = fmaxf(fmaxf(f_m[0], f_m[1]), fmaxf(f_m[2], f_m[3]));
+    float zs = 0.f, o = 0.f;
+#pragma unroll
+    for (int g2 = 0; g2 < 4; ++g2) {
+      const float w = f_m[g2] == -INFINITY ? 0.f : __expf(f_m[g2] - M);
+      zs = fmaf(f_z[g2], w, zs);
+      o = fmaf(f_acc[g2][t], w, o);
+    }
+    io_traits<bf16_t>::store(out, (int64_t)bh * D + t, o / zs);
+  }
+}
+
 template <typename IO, int D, int MAXS>
 __global__ void __launch_bounds__(256) decode_combine(const float* __restrict__ part, const float* __restrict__ sig,
                                                       const int32_t* __restrict__ nsel,
@@ -853,6 +1020,19 @@ hipError_t launch_mirror(const Geom& g, const float* kc, const float* bc, uint8_
                    : launch_mirror_d<128>(kc, bc, kcm, g.B * g.Hl, g.C(), c_begin, n, st);
 }
 
+// compute units of the current device (cached per device)
+static int device_cus() {
+  static std::atomic<int> cus[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 1 << 30;
+  int n = cus[dev].load(std::memory_order_relaxed);
+  if (n == 0) {
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 1 << 30;
+    cus[dev].store(n, std::memory_order_relaxed);
+  }
+  return n;
+}
+
 template <typename IO, int D>
 static hipError_t launch_decode_t(const Geom& g, const void* q, const void* kcache, const void* vcache,
                                   const int32_t* seq_lens, const float* kc, const float* bc, const uint8_t* kcm,
@@ -900,15 +1080,24 @@ static hipError_t launch_decode_t(const Geom& g, const void* q, const void* kcac
                        sel_s, nsel, sel_user, g.Hq, C, g.K, nsplit, g.nw);
   }
   if (ev) (void)hipEventRecord(ev[2], st);
-  hipLaunchKernelGGL((decode_attend<IO, D>), dim3(BH * (g.K + g.nw)), dim3(256), 0, st, (const IO*)q,
-                     (const IO*)kcache, (const IO*)vcache, seq_lens, sel_i, sel_s, nsel, part, sig, g.Hq, g.Hkv, g.N,
-                     g.K, g.nw, pg);
-  if (g.K + g.nw > 64)
-    hipLaunchKernelGGL((decode_combine<IO, D, 128>), dim3(BH), dim3(256), 0, st, (const float*)part,
-                       (const float*)sig, (const int32_t*)nsel, seq_lens, (IO*)o, g.Hq, g.K, g.nw);
-  else
-    hipLaunchKernelGGL((decode_combine<IO, D, 64>), dim3(BH), dim3(256), 0, st, (const float*)part,
-                       (const float*)sig, (const int32_t*)nsel, seq_lens, (IO*)o, g.Hq, g.K, g.nw);
+  bool fused = false;
+  if constexpr (std::is_same<IO, bf16_t>::value) fused = BH >= device_cus();
+  if (fused) {   // one workgroup per (b, h) fills the chip: attention and fusion in one kernel
+    if constexpr (std::is_same<IO, bf16_t>::value)
+      hipLaunchKernelGGL((decode_attend_fused<D>), dim3(BH), dim3(1024), 0, st, (const bf16_t*)q,
+                         (const bf16_t*)kcache, (const bf16_t*)vcache, seq_lens, sel_i, sel_s, nsel, (bf16_t*)o, g.Hq,
+                         g.Hkv, g.N, g.K, g.nw, pg);
+  } else {
+    hipLaunchKernelGGL((decode_attend<IO, D>), dim3(BH * (g.K + g.nw)), dim3(256), 0, st, (const IO*)q,
+                       (const IO*)kcache, (const IO*)vcache, seq_lens, sel_i, sel_s, nsel, part, sig, g.Hq, g.Hkv, g.N,
+                       g.K, g.nw, pg);
+    if (g.K + g.nw > 64)
+      hipLaunchKernelGGL((decode_combine<IO, D, 128>), dim3(BH), dim3(256), 0, st, (const float*)part,
+                         (const float*)sig, (const int32_t*)nsel, seq_lens, (IO*)o, g.Hq, g.K, g.nw);
+    else
+      hipLaunchKernelGGL((decode_combine<IO, D, 64>), dim3(BH), dim3(256), 0, st, (const float*)part,
+                         (const float*)sig, (const int32_t*)nsel, seq_lens, (IO*)o, g.Hq, g.K, g.nw);
+  }
   if (ev) (void)hipEventRecord(ev[3], st);
   return hipGetLastError();
 }

@@ -226,6 +226,23 @@ def test_decode(name, w):
     _say(name, summ)
 
 
+# 256 (sequence, head) pairs or more: on MI355X's 256 CUs the step runs attention and fusion
+# in one workgroup per pair (decode_attend_fused) instead of one per chunk plus a combine
+DECODE_FUSED = [
+    ("bf16_d128_B8_H32", synth.Workload("decf_a", B=8, Hq=32, Hkv=8, d=128, N=4096, K=16, decode=True,
+                                        seq_lens=[4096, 1, 64, 65, 1000, 3000, 2049, 4095], needle_frac=0.05)),
+    ("bf16_d64_B16_H16_qcal", synth.Workload("decf_b", B=16, Hq=16, Hkv=4, d=64, N=2048, K=8, decode=True,
+                                             seq_lens=[2048 - 97 * i for i in range(16)], qcal_rank=8, planted_seqs=3)),
+    ("bf16_d128_H64_K64_w1024", synth.Workload("decf_c", B=4, Hq=64, Hkv=8, d=128, N=8192, K=64, decode=True,
+                                               seq_lens=[8192, 5000, 1100, 300], needle_frac=0.02, window=1024)),
+]
+
+
+@pytest.mark.parametrize("name,w", DECODE_FUSED, ids=[n for n, _ in DECODE_FUSED])
+def test_decode_fused_attention(name, w):
+    test_decode(name, w)
+
+
 def test_decode_matches_prefill_row():
     """A decode step at cache length L reproduces prefill row L-1 (same kernels' inputs)."""
     L = 1000
