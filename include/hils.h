@@ -266,7 +266,9 @@ int hils_attn_decode_noalloc(const hils_dims_t* dims, const void* q, const void*
  * [c_begin, c_end) of every sequence, reading keys from the pages; call it for
  * the chunk that a decode step completes (incremental compression).
  * hils_attn_decode_paged: hils_attn_decode on the paged cache (same workspace,
- * HILS_OP_DECODE).  Both are asynchronous on `stream`.
+ * HILS_OP_DECODE).  hils_attn_decode_paged_mirror: the same step scanning the landmark
+ * mirror (hils_landmark_mirror, built from the contiguous kc/bc), with
+ * hils_attn_decode_paged's result bit for bit.  All are asynchronous on `stream`.
  */
 int hils_landmark_compress_paged(const hils_dims_t* dims, const void* k_pages, const int32_t* block_table,
                                  int32_t max_blocks, int32_t num_pages, const void* lmk_q, int32_t c_begin,
@@ -275,6 +277,11 @@ int hils_attn_decode_paged(const hils_dims_t* dims, const void* q, const void* k
                            const int32_t* block_table, int32_t max_blocks, int32_t num_pages, const int32_t* seq_lens,
                            const float* kc, const float* bc, const void* qcal_D, const void* qcal_U,
                            int32_t* sel_idx_out, void* o, void* ws, size_t ws_bytes, void* stream);
+int hils_attn_decode_paged_mirror(const hils_dims_t* dims, const void* q, const void* k_pages, const void* v_pages,
+                                  const int32_t* block_table, int32_t max_blocks, int32_t num_pages,
+                                  const int32_t* seq_lens, const float* kc, const float* bc, const uint8_t* kc_mirror,
+                                  const void* qcal_D, const void* qcal_U, int32_t* sel_idx_out, void* o, void* ws,
+                                  size_t ws_bytes, void* stream);
 
 /*
  * Backward pass of hils_attn_prefill (end-to-end retrieval learning: the training

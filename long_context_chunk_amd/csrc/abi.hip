@@ -433,6 +433,21 @@ int hils_attn_decode_paged(const hils_dims_t* dims, const void* q, const void* k
                     nullptr, pg);
 }
 
+int hils_attn_decode_paged_mirror(const hils_dims_t* dims, const void* q, const void* k_pages, const void* v_pages,
+                                  const int32_t* block_table, int32_t max_blocks, int32_t num_pages,
+                                  const int32_t* seq_lens, const float* kc, const float* bc, const uint8_t* kc_mirror,
+                                  const void* qcal_D, const void* qcal_U, int32_t* sel_idx_out, void* o, void* ws,
+                                  size_t ws_bytes, void* stream) {
+  hils::Geom g;
+  int rc = check_dims(dims, g);
+  if (rc) return rc;
+  if ((rc = check_mirror(dims, kc_mirror))) return rc;
+  hils::KvPages pg;
+  if ((rc = check_pages(g, block_table, max_blocks, num_pages, pg))) return rc;
+  return run_decode(dims, q, k_pages, v_pages, seq_lens, kc, bc, qcal_D, qcal_U, sel_idx_out, o, ws, ws_bytes, stream,
+                    nullptr, pg, kc_mirror);
+}
+
 int hils_dense_attention(const hils_dims_t* dims, const void* q, const void* k, const void* v, void* o,
                          void* stream) {
   hils::Geom g;

@@ -22,7 +22,8 @@ OK, E_INVAL, E_UNSUPPORTED, E_WORKSPACE, E_HIP = 0, -1, -2, -3, -4
 SYMBOLS = ("hils_workspace_bytes", "hils_landmark_compress", "hils_chunk_score_topk", "hils_attn_prefill",
            "hils_attn_prefill_timed", "hils_attn_decode", "hils_attn_decode_timed", "hils_landmark_compress_paged",
            "hils_attn_decode_paged", "hils_dense_attention", "hils_attn_prefill_backward", "hils_attn_decode_noalloc",
-           "hils_landmark_mirror", "hils_attn_decode_mirror", "hils_attn_decode_mirror_timed", "hils_last_error")
+           "hils_landmark_mirror", "hils_attn_decode_mirror", "hils_attn_decode_mirror_timed",
+           "hils_attn_decode_paged_mirror", "hils_last_error")
 NOALLOC_SCRATCH_BYTES = 16 << 20   # HILS_NOALLOC_SCRATCH_BYTES of include/hils.h
 STAGES = ("compress", "score_threshold", "score_select", "bucket", "chunk_attend", "own_attend", "fuse")
 DECODE_STAGES = ("scan", "merge", "attend_fuse")
@@ -68,6 +69,8 @@ def load():
         lib.hils_attn_decode_noalloc.argtypes = [dp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
         lib.hils_landmark_compress_paged.argtypes = [dp, vp, vp, i32, i32, vp, i32, i32, vp, vp, vp]
         lib.hils_attn_decode_paged.argtypes = [dp, vp, vp, vp, vp, i32, i32, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+        lib.hils_attn_decode_paged_mirror.argtypes = [dp, vp, vp, vp, vp, i32, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp,
+                                                      sz, vp]
         lib.hils_attn_prefill_backward.argtypes = [dp] + [vp] * 18 + [sz, vp]
         lib.hils_landmark_mirror.argtypes = [dp, vp, vp, i32, i32, vp, vp]
         lib.hils_attn_decode_mirror.argtypes = [dp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
@@ -76,7 +79,8 @@ def load():
         for f in ("hils_landmark_compress", "hils_chunk_score_topk", "hils_attn_prefill", "hils_attn_prefill_timed",
                   "hils_attn_decode", "hils_attn_decode_timed", "hils_dense_attention", "hils_landmark_compress_paged",
                   "hils_attn_decode_paged", "hils_attn_prefill_backward", "hils_attn_decode_noalloc",
-                  "hils_landmark_mirror", "hils_attn_decode_mirror", "hils_attn_decode_mirror_timed"):
+                  "hils_landmark_mirror", "hils_attn_decode_mirror", "hils_attn_decode_mirror_timed",
+                  "hils_attn_decode_paged_mirror"):
             getattr(lib, f).restype = ctypes.c_int
         lib.hils_last_error.argtypes = []
         lib.hils_last_error.restype = ctypes.c_char_p
@@ -326,8 +330,9 @@ def landmark_compress_paged(dm: Dims, k_pages, block_table, lmk_q, kc, bc, c_beg
 
 
 def attn_decode_paged(dm: Dims, q, k_pages, v_pages, block_table, seq_lens, kc, bc, o, ws, qcal_D=None, qcal_U=None,
-                      sel_idx=None):
-    """hils_attn_decode_paged: hils_attn_decode on a chunk-paged KV cache."""
+                      sel_idx=None, kc_mirror=None):
+    """hils_attn_decode_paged: hils_attn_decode on a chunk-paged KV cache (with kc_mirror, the
+    landmark mirror: hils_attn_decode_paged_mirror)."""
     C = dm.N // dm.S
     dt = torch.float32 if dm.io == F32 else torch.bfloat16
     _req(q, "q", (dm.B, dm.Hq, dm.d), dt)
@@ -346,6 +351,13 @@ def attn_decode_paged(dm: Dims, q, k_pages, v_pages, block_table, seq_lens, kc, 
         _req(qcal_U, "qcal_U", (dm.Hq, dm.d, dm.qcal_rank), dt)
     if sel_idx is not None:
         _req(sel_idx, "sel_idx", (dm.B, dm.Hq, dm.K), torch.int32)
+    if kc_mirror is not None:
+        _req(kc_mirror, "kc_mirror", mirror_shape(dm), torch.uint8)
+        _check(load().hils_attn_decode_paged_mirror(ctypes.byref(dm), _p(q), _p(k_pages), _p(v_pages), _p(block_table),
+                                                    C, k_pages.shape[0], _p(seq_lens), _p(kc), _p(bc), _p(kc_mirror),
+                                                    _p(qcal_D), _p(qcal_U), _p(sel_idx), _p(o), _p(ws), ws.numel(),
+                                                    _stream()))
+        return
     _check(load().hils_attn_decode_paged(ctypes.byref(dm), _p(q), _p(k_pages), _p(v_pages), _p(block_table), C,
                                          k_pages.shape[0], _p(seq_lens), _p(kc), _p(bc), _p(qcal_D), _p(qcal_U),
                                          _p(sel_idx), _p(o), _p(ws), ws.numel(), _stream()))

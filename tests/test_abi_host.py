@@ -285,3 +285,25 @@ def test_mirror_entry_points_validation():
     rc = lib.hils_attn_decode_mirror(ctypes.byref(short), fake, fake, fake, fake, None, None, None, None, None, None,
                                      None, fake, 1 << 40, None)
     assert rc == hils.E_INVAL and b"o must" in lib.hils_last_error()
+
+
+def test_paged_mirror_entry_point_validation():
+    """hils_attn_decode_paged_mirror checks the mirror, the page table and the decode
+    arguments on the host."""
+    lib = hils.load()
+    fake = ctypes.c_void_p(0x1000)
+    d = hils.dims(2, 8, 2, 128, 4096, 16)
+    C = 4096 // 64
+    need = hils.workspace_bytes(d, hils.OP_DECODE)
+    rc = lib.hils_attn_decode_paged_mirror(ctypes.byref(d), fake, fake, fake, fake, C, 4 * C, fake, fake, fake, None,
+                                           None, None, None, fake, fake, need, None)
+    assert rc == hils.E_INVAL and b"kc_mirror" in lib.hils_last_error()
+    rc = lib.hils_attn_decode_paged_mirror(ctypes.byref(d), fake, fake, fake, None, C, 4 * C, fake, fake, fake, fake,
+                                           None, None, None, fake, fake, need, None)
+    assert rc == hils.E_INVAL
+    rc = lib.hils_attn_decode_paged_mirror(ctypes.byref(d), fake, fake, fake, fake, C + 1, 4 * C, fake, fake, fake,
+                                           fake, None, None, None, fake, fake, need, None)
+    assert rc == hils.E_INVAL
+    rc = lib.hils_attn_decode_paged_mirror(ctypes.byref(d), fake, fake, fake, fake, C, 4 * C, fake, fake, fake, fake,
+                                           None, None, None, fake, fake, need - 1, None)
+    assert rc == hils.E_WORKSPACE

@@ -479,9 +479,21 @@ PAGED = [
 def test_paged_decode_against_oracle(name, qcal, window):
     """The paged path on its own: landmark compression one chunk at a time from shuffled
     pages against the oracle's compression, then the paged decode step against the oracle's
-    forward pass on the contiguous cache (selection and output, the usual bar)."""
+    forward pass on the contiguous cache (selection and output, the usual bar), and the
+    paged step over the landmark mirror bit-equal to it."""
     w = synth.Workload("paged_" + name, B=3, Hq=4, Hkv=2, d=128, N=2048, K=8, decode=True,
                        seq_lens=[2048, 1000, 70], qcal_rank=qcal, window=window, needle_frac=0.05)
+    _paged_decode_case(w, name)
+
+
+def test_paged_decode_fused_attention_against_oracle():
+    """The same at 256 (sequence, head) pairs, where attention and fusion run in one kernel."""
+    w = synth.Workload("paged_fused", B=8, Hq=32, Hkv=8, d=128, N=2048, K=16, decode=True,
+                       seq_lens=[2048, 1000, 70, 1, 65, 640, 1999, 2047], qcal_rank=8, window=256, needle_frac=0.05)
+    _paged_decode_case(w, "fused")
+
+
+def _paged_decode_case(w, name):
     _say("paged decode vs oracle", name)
     x = synth.make_inputs(w, SEED + 31)
     kp, vp, table = _paginate(w, x, 17)
@@ -503,9 +515,19 @@ def test_paged_decode_against_oracle(name, qcal, window):
     ws = hils.workspace(dm, hils.OP_DECODE)
     D = upload(x["D"], w.io) if w.qcal_rank else None
     U = upload(x["U"], w.io) if w.qcal_rank else None
-    hils.attn_decode_paged(dm, q, kpt, vpt, tab, torch.from_numpy(x["seq_lens"]).cuda(), kc, bc, o, ws, qcal_D=D,
-                           qcal_U=U, sel_idx=sel)
+    lens = torch.from_numpy(x["seq_lens"]).cuda()
+    hils.attn_decode_paged(dm, q, kpt, vpt, tab, lens, kc, bc, o, ws, qcal_D=D, qcal_U=U, sel_idx=sel)
+    # the same step over the landmark mirror (built chunk by chunk too)
+    kcm = torch.zeros(hils.mirror_shape(dm), dtype=torch.uint8, device="cuda")
+    for c in range(w.C):
+        hils.landmark_mirror(dm, kc, bc, kcm, c, c + 1)
+    om = torch.full_like(q, float("nan"))
+    selm = torch.empty_like(sel)
+    hils.attn_decode_paged(dm, q, kpt, vpt, tab, lens, kc, bc, om, ws, qcal_D=D, qcal_U=U, sel_idx=selm,
+                           kc_mirror=kcm)
     torch.cuda.synchronize()
+    np.testing.assert_array_equal(selm.cpu().numpy(), sel.cpu().numpy())
+    np.testing.assert_array_equal(om.view(torch.int16).cpu().numpy(), o.view(torch.int16).cpu().numpy())
     rows_b = [b for b in range(w.B) for h in range(w.Hq)]
     rows_h = [h for b in range(w.B) for h in range(w.Hq)]
     pos = [int(x["seq_lens"][b]) - 1 for b in rows_b]
