@@ -431,20 +431,30 @@ def run_decode(wd, steps, warmup, seed, dense=False):
     flush_out = torch.empty((), dtype=torch.float32, device="cuda")
 
     def timed_steps(mirror):
+        """Per-step times of plain calls (one HIP event pair per step on the launch stream, the
+        caches evicted before each), then the stage times of as many timed calls (their own
+        events between the stages add a few microseconds, so they are not the step time)."""
         for _ in range(warmup):
             hils.attn_decode(dm, q, kcache, vcache, lens, kc, bc, o, ws, sel_idx=sel, kc_mirror=mirror)
         torch.cuda.synchronize()
-        stages, per = {s: 0.0 for s in hils.DECODE_STAGES}, []
-        for _ in range(steps):
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+        for ea, eb in evs:
             torch.sum(flush, dim=0, out=flush_out)   # evict k' and the KV chunks (untimed)
+            ea.record()
+            hils.attn_decode(dm, q, kcache, vcache, lens, kc, bc, o, ws, sel_idx=sel, kc_mirror=mirror)
+            eb.record()
+        torch.cuda.synchronize()
+        per = [ea.elapsed_time(eb) * 1e3 for ea, eb in evs]
+        stages = {s: 0.0 for s in hils.DECODE_STAGES}
+        for _ in range(steps):
+            torch.sum(flush, dim=0, out=flush_out)
             r = hils.attn_decode(dm, q, kcache, vcache, lens, kc, bc, o, ws, sel_idx=sel, timed=True,
                                  kc_mirror=mirror)
             for s_ in stages:
                 stages[s_] += r[s_] / steps
-            per.append(sum(r.values()) * 1e3)
         dist = {"median": float(np.median(per)), "p10": float(np.percentile(per, 10)),
                 "p90": float(np.percentile(per, 90))}
-        return sum(stages.values()) * 1e3, stages, dist
+        return float(np.mean(per)), stages, dist
 
     # the exact fp32 scan (hils_attn_decode), then the mirror scan (hils_attn_decode_mirror):
     # the same step, bit for bit

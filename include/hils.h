@@ -182,8 +182,10 @@ int hils_attn_decode(const hils_dims_t* dims, const void* q, const void* k_cache
  * hils_attn_decode for measurement: the same work, plus the GPU time of each
  * stage in milliseconds (HIP events on `stream`) in stage_ms[HILS_DECODE_STAGES]
  * (a HOST array): [0] chunk scoring scan (with each split's best chunks), [1]
- * the merge into the top-K, [2] chunk gather-attention and fusion.  Synchronises
- * with the stream before returning.
+ * the merge into the top-K, [2] chunk gather-attention and fusion.  With bf16 I/O and
+ * B*Hq at least the device's compute-unit count the merge runs inside the attention
+ * kernel: [1] is then 0 and [2] includes it.  Synchronises with the stream before
+ * returning.
  */
 #define HILS_DECODE_STAGES 3
 int hils_attn_decode_timed(const hils_dims_t* dims, const void* q, const void* k_cache, const void* v_cache,

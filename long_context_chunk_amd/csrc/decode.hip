@@ -296,65 +296,77 @@ __global__ void __launch_bounds__(256) decode_scan(const IO* __restrict__ q, con
   }
 }
 
-// exact top-K of one (b, h) from the sorted candidate lists of its splits, rank order.
-// Half-wave x of wave w takes lists 2w + x and 2w + x + 8, the halves of each wave
-// merge, then wave 0 merges the four wave lists.
+// exact top-K of one (b, h) from the sorted candidate lists of its splits (cb: the first
+// list), rank order, ties to the lowest id; n = min(K, candidate chunks).  Every thread of
+// the block calls it (it has a block-wide barrier); the first four waves do the work:
+// half-wave x of wave w takes lists 2w + x and 2w + x + 8, the halves of each wave merge,
+// then wave 0 merges the four wave lists and writes ranks < K to out_i / out_s (and sel_user
+// when given): chunk ids, -1 past n.
 template <bool KB>
-__global__ void __launch_bounds__(256) decode_merge(const uint64_t* __restrict__ cand,
-                                                    const int32_t* __restrict__ seq_lens, int32_t* __restrict__ sel_i,
-                                                    float* __restrict__ sel_s, int32_t* __restrict__ nsel_out,
-                                                    int32_t* __restrict__ sel_user, int Hq, int C, int K, int nsplit,
-                                                    int nw) {
+HILS_DEV void merge_splits(const uint64_t* __restrict__ cb, int nsplit, int K, int n, uint64_t (*wl)[64],
+                           int32_t* out_i, float* out_s, int32_t* __restrict__ sel_user) {
   static_assert(DS_MAX_SPLIT == 16, "two lists per half-wave");
-  __shared__ uint64_t wl[4][64];
-  const int bh = blockIdx.x, t = threadIdx.x, lane = t & 63, w = t >> 6;
+  const int t = threadIdx.x, lane = t & 63, w = t >> 6;
   const int j = lane & 31;
   const int li = 2 * w + (lane >> 5);
-  const uint64_t* cb = cand + (int64_t)bh * nsplit * DS_KEEP + j;
-  // the best 32 (KB: 64) of all splits, sorted, in half 0 of wave 0 (half 1 ends up
-  // with a list merged with itself); key of rank `lane`: hi of lane j < 32, lo of lane
-  // j of half 0 for ranks 32 + j
-  uint64_t hi, lo = 0;
-  auto ld = [&](int l, int off) { return l < nsplit ? cb[l * DS_KEEP + off] : 0ull; };  // empty lists: zero keys
+  // the best 32 (KB: 64) of all splits, sorted, in half 0 of wave 0 (half 1 ends up with a
+  // list merged with itself); key of rank `lane`: hi of lane j < 32, lo of lane j of half 0
+  // for ranks 32 + j
+  uint64_t hi = 0, lo = 0;
+  auto ld = [&](int l, int off) { return l < nsplit ? cb[l * DS_KEEP + off + j] : 0ull; };  // empty lists: zero keys
+  if (w < 4) {
+    if constexpr (!KB) {
+      hi = ld(li, 0);
+      dmerge_sorted(hi, ld(li + 8, 0));
+      dmerge_sorted(hi, __shfl(hi, j + 32));
+      if (lane < 32) wl[w][lane] = hi;
+    } else {
+      hi = ld(li, 0);
+      lo = ld(li, 32);
+      kl::merge64(hi, lo, ld(li + 8, 0), ld(li + 8, 32), j);
+      kl::merge64(hi, lo, __shfl(hi, j + 32), __shfl(lo, j + 32), j);
+      if (lane < 32) {
+        wl[w][lane] = hi;
+        wl[w][32 + lane] = lo;
+      }
+    }
+  }
+  __syncthreads();
+  if (w != 0) return;
   if constexpr (!KB) {
-    hi = ld(li, 0);
-    dmerge_sorted(hi, ld(li + 8, 0));
-    dmerge_sorted(hi, __shfl(hi, j + 32));
-    if (lane < 32) wl[w][lane] = hi;
-    __syncthreads();
-    if (w != 0) return;
     hi = wl[(lane >> 5) * 2][j];
     dmerge_sorted(hi, wl[(lane >> 5) * 2 + 1][j]);
     dmerge_sorted(hi, __shfl(hi, j + 32));
   } else {
-    hi = ld(li, 0);
-    lo = ld(li, 32);
-    kl::merge64(hi, lo, ld(li + 8, 0), ld(li + 8, 32), j);
-    kl::merge64(hi, lo, __shfl(hi, j + 32), __shfl(lo, j + 32), j);
-    if (lane < 32) {
-      wl[w][lane] = hi;
-      wl[w][32 + lane] = lo;
-    }
-    __syncthreads();
-    if (w != 0) return;
     const int a = (lane >> 5) * 2;
     hi = wl[a][j];
     lo = wl[a][32 + j];
     kl::merge64(hi, lo, wl[a + 1][j], wl[a + 1][32 + j], j);
     kl::merge64(hi, lo, __shfl(hi, j + 32), __shfl(lo, j + 32), j);
   }
-  const int L = seq_lens[bh / Hq];
-  const int n = min(K, candidate_chunks(L - 1, C, nw));
   const uint64_t lo0 = __shfl(lo, j);   // half 0's ranks 32 + j
   const uint64_t lk = lane < 32 ? hi : lo0;
   if (lane < K) {
     const bool ok = lane < n && lk != 0;
     const int32_t ci = ok ? key_chunk(lk) : -1;
-    sel_i[(int64_t)bh * K + lane] = ci;
-    sel_s[(int64_t)bh * K + lane] = ok ? key_score(lk) : -INFINITY;
-    if (sel_user) sel_user[(int64_t)bh * K + lane] = ci;
+    out_i[lane] = ci;
+    out_s[lane] = ok ? key_score(lk) : -INFINITY;
+    if (sel_user) sel_user[lane] = ci;
   }
-  if (lane == 0) nsel_out[bh] = n;
+}
+
+template <bool KB>
+__global__ void __launch_bounds__(256) decode_merge(const uint64_t* __restrict__ cand,
+                                                    const int32_t* __restrict__ seq_lens, int32_t* __restrict__ sel_i,
+                                                    float* __restrict__ sel_s, int32_t* __restrict__ nsel_out,
+                                                    int32_t* __restrict__ sel_user, int Hq, int C, int K, int nsplit,
+                                                    int nw) {
+  __shared__ uint64_t wl[4][64];
+  const int bh = blockIdx.x;
+  const int n = min(K, candidate_chunks(seq_lens[bh / Hq] - 1, C, nw));
+  merge_splits<KB>(cand + (int64_t)bh * nsplit * DS_KEEP, nsplit, K, n, wl, sel_i + (int64_t)bh * K,
+                   sel_s + (int64_t)bh * K, sel_user ? sel_user + (int64_t)bh * K : nullptr);
+  if (threadIdx.x == 0) nsel_out[bh] = n;
 }
 
 // eight consecutive elements of a row, kept raw until used
@@ -477,22 +489,24 @@ __global__ void __launch_bounds__(256) decode_attend(const IO* __restrict__ q, c
 // selected chunks and the window's chunks from the own one back to chunk 0 (at most nw).
 // Lane s of every wave holds slot s's weight (MAXS = 128: slot 64 + s's too); the live
 // slot rows are all loaded at once.
-// Chunk attention and fusion of one (b, h) in one workgroup of four groups of 256 threads
-// (bf16 I/O).  Slots are the same as decode_attend's; group g takes slots g, g + 4, ...
+// The top-K merge, chunk attention and fusion of one (b, h) in one workgroup of four groups
+// of 256 threads (bf16 I/O).  The first four waves merge the splits' candidate lists into the
+// selection (merge_splits, as decode_merge).  Slots are then decode_attend's; group g takes
+// slots g, g + 4, ...
 // Per slot a group computes what decode_attend computes (the chunk's softmax output o_c
 // and its score: the selection score, or the window chunk's exact log-sum-exp) and folds
 // it into a running fusion (m, z, acc) with an online softmax; the next slot's K and V
 // rows are loaded while the current one is computed.  At the end the four groups' running
 // fusions are merged.  It gives decode_combine's result up to the order of the fp32 sums.
-template <int D>
+template <int D, bool KB>
 __global__ void __launch_bounds__(1024) decode_attend_fused(const bf16_t* __restrict__ q,
                                                             const bf16_t* __restrict__ kcache,
                                                             const bf16_t* __restrict__ vcache,
                                                             const int32_t* __restrict__ seq_lens,
-                                                            const int32_t* __restrict__ sel_i,
-                                                            const float* __restrict__ sel_s,
-                                                            const int32_t* __restrict__ nsel, bf16_t* __restrict__ out,
-                                                            int Hq, int Hkv, int N, int K, int nw, KvPages pg) {
+                                                            const uint64_t* __restrict__ cand,
+                                                            int32_t* __restrict__ sel_user, bf16_t* __restrict__ out,
+                                                            int Hq, int Hkv, int N, int C, int K, int nsplit, int nw,
+                                                            KvPages pg) {
   constexpr int KJ = D / 32;        // logits: 4 threads per key, KJ runs of 8 dims each
   constexpr int TPR = D / 8;        // values: threads per row (8 dims each)
   constexpr int NG = 256 / TPR;     // key groups
@@ -507,10 +521,18 @@ __global__ void __launch_bounds__(1024) decode_attend_fused(const bf16_t* __rest
   __shared__ float f_m[4], f_z[4];
   __shared__ float f_acc[4][D];
   __shared__ __align__(16) bf16_t qsh[D];   // the query (read per slot, not held in registers)
+  __shared__ uint64_t wl[4][64];
+  __shared__ int32_t m_i[64];
+  __shared__ float m_s[64];
   const int bh = blockIdx.x, b = bh / Hq, h = bh % Hq, kvh = h / (Hq / Hkv);
   const int t = threadIdx.x, g = t >> 8, tg = t & 255, lane = t & 63;
   const int L = seq_lens[b];
   const int NSL = K + nw;
+  const int nsel = min(K, candidate_chunks(L - 1, C, nw));
+  if (t < D / 8) *reinterpret_cast<u32x4_t*>(&qsh[8 * t]) = *reinterpret_cast<const u32x4_t*>(q + (int64_t)bh * D + 8 * t);
+  merge_splits<KB>(cand + (int64_t)bh * nsplit * DS_KEEP, nsplit, K, nsel, wl, m_i, m_s,
+                   sel_user ? sel_user + (int64_t)bh * K : nullptr);
+  __syncthreads();
   if (t < NSL) {   // slot table: chunk (-1: nothing), keys, score (selected slots)
     int c = -1, nk = 64;
     float sc = 0.f;
@@ -518,9 +540,9 @@ __global__ void __launch_bounds__(1024) decode_attend_fused(const bf16_t* __rest
       c = (L - 1) / 64 - (t - K);
       if (t == K) nk = L - c * 64;
       if (c < 0) c = -1;
-    } else if (t < nsel[bh]) {
-      c = sel_i[(int64_t)bh * K + t];
-      sc = sel_s[(int64_t)bh * K + t];
+    } else if (t < nsel) {
+      c = m_i[t];
+      sc = m_s[t];
       if (c < 0) c = -1;
     }
     s_c[t] = c;
@@ -530,7 +552,6 @@ __global__ void __launch_bounds__(1024) decode_attend_fused(const bf16_t* __rest
   }
   const int key = tg >> 2, qd = tg & 3;
   const int e8 = (tg % TPR) * 8, kg = tg / TPR;
-  if (t < D / 8) *reinterpret_cast<u32x4_t*>(&qsh[8 * t]) = *reinterpret_cast<const u32x4_t*>(q + (int64_t)bh * D + 8 * t);
   __syncthreads();
   const int nit = (NSL + 3) / 4;
   // K and V rows of slot s into a register buffer; slots with no chunk load row 0 of the
@@ -1050,7 +1071,9 @@ static hipError_t launch_decode_t(const Geom& g, const void* q, const void* kcac
   if (nsplit > DS_MAX_SPLIT) return hipErrorInvalidValue;  // N/S > 16384, rejected by the ABI first
   if (ev) (void)hipEventRecord(ev[0], st);
   const bool kb = g.K > 32;   // keep 64 candidates per split
-  if (kcm) {   // the scan over the bf16 mirror, exact rescoring of each split's survivors
+  bool fused = false;   // one workgroup per (b, h) fills the chip: merge, attention and fusion in one kernel
+  if constexpr (std::is_same<IO, bf16_t>::value) fused = BH >= device_cus();
+  if (kcm) {   // the scan over the 8-bit mirror, exact rescoring of each split's survivors
     if (kb)
       hipLaunchKernelGGL((decode_scan_m<IO, D, true, DSM_UNR>), dim3(BH * nsplit), dim3(256), 0, st, (const IO*)q,
                          (const IO*)Dw, (const IO*)Uw, kcm, kc, bc, seq_lens, cand, g.Hq, g.Hl, C, g.K, g.r, nsplit,
@@ -1059,35 +1082,34 @@ static hipError_t launch_decode_t(const Geom& g, const void* q, const void* kcac
       hipLaunchKernelGGL((decode_scan_m<IO, D, false, DSM_UNR>), dim3(BH * nsplit), dim3(256), 0, st, (const IO*)q,
                          (const IO*)Dw, (const IO*)Uw, kcm, kc, bc, seq_lens, cand, g.Hq, g.Hl, C, g.K, g.r, nsplit,
                          g.nw, (int64_t)g.B * g.Hl * C);
-    if (ev) (void)hipEventRecord(ev[1], st);
+  } else if (kb) {
+    hipLaunchKernelGGL((decode_scan<IO, D, true>), dim3(BH * nsplit), dim3(256), 0, st, (const IO*)q, (const IO*)Dw,
+                       (const IO*)Uw, kc, bc, seq_lens, cand, g.Hq, g.Hl, C, g.r, nsplit, g.nw);
+  } else {
+    hipLaunchKernelGGL((decode_scan<IO, D, false>), dim3(BH * nsplit), dim3(256), 0, st, (const IO*)q,
+                       (const IO*)Dw, (const IO*)Uw, kc, bc, seq_lens, cand, g.Hq, g.Hl, C, g.r, nsplit, g.nw);
+  }
+  if (ev) (void)hipEventRecord(ev[1], st);
+  if (fused) {
+    if (ev) (void)hipEventRecord(ev[2], st);   // the merge runs inside the fused kernel
+    if constexpr (std::is_same<IO, bf16_t>::value) {
+      if (kb)
+        hipLaunchKernelGGL((decode_attend_fused<D, true>), dim3(BH), dim3(1024), 0, st, (const bf16_t*)q,
+                           (const bf16_t*)kcache, (const bf16_t*)vcache, seq_lens, (const uint64_t*)cand, sel_user,
+                           (bf16_t*)o, g.Hq, g.Hkv, g.N, C, g.K, nsplit, g.nw, pg);
+      else
+        hipLaunchKernelGGL((decode_attend_fused<D, false>), dim3(BH), dim3(1024), 0, st, (const bf16_t*)q,
+                           (const bf16_t*)kcache, (const bf16_t*)vcache, seq_lens, (const uint64_t*)cand, sel_user,
+                           (bf16_t*)o, g.Hq, g.Hkv, g.N, C, g.K, nsplit, g.nw, pg);
+    }
+  } else {
     if (kb)
       hipLaunchKernelGGL(decode_merge<true>, dim3(BH), dim3(256), 0, st, (const uint64_t*)cand, seq_lens, sel_i,
                          sel_s, nsel, sel_user, g.Hq, C, g.K, nsplit, g.nw);
     else
       hipLaunchKernelGGL(decode_merge<false>, dim3(BH), dim3(256), 0, st, (const uint64_t*)cand, seq_lens, sel_i,
                          sel_s, nsel, sel_user, g.Hq, C, g.K, nsplit, g.nw);
-  } else if (kb) {
-    hipLaunchKernelGGL((decode_scan<IO, D, true>), dim3(BH * nsplit), dim3(256), 0, st, (const IO*)q, (const IO*)Dw,
-                       (const IO*)Uw, kc, bc, seq_lens, cand, g.Hq, g.Hl, C, g.r, nsplit, g.nw);
-    if (ev) (void)hipEventRecord(ev[1], st);
-    hipLaunchKernelGGL(decode_merge<true>, dim3(BH), dim3(256), 0, st, (const uint64_t*)cand, seq_lens, sel_i, sel_s,
-                       nsel, sel_user, g.Hq, C, g.K, nsplit, g.nw);
-  } else {
-    hipLaunchKernelGGL((decode_scan<IO, D, false>), dim3(BH * nsplit), dim3(256), 0, st, (const IO*)q,
-                       (const IO*)Dw, (const IO*)Uw, kc, bc, seq_lens, cand, g.Hq, g.Hl, C, g.r, nsplit, g.nw);
-    if (ev) (void)hipEventRecord(ev[1], st);
-    hipLaunchKernelGGL(decode_merge<false>, dim3(BH), dim3(256), 0, st, (const uint64_t*)cand, seq_lens, sel_i,
-                       sel_s, nsel, sel_user, g.Hq, C, g.K, nsplit, g.nw);
-  }
-  if (ev) (void)hipEventRecord(ev[2], st);
-  bool fused = false;
-  if constexpr (std::is_same<IO, bf16_t>::value) fused = BH >= device_cus();
-  if (fused) {   // one workgroup per (b, h) fills the chip: attention and fusion in one kernel
-    if constexpr (std::is_same<IO, bf16_t>::value)
-      hipLaunchKernelGGL((decode_attend_fused<D>), dim3(BH), dim3(1024), 0, st, (const bf16_t*)q,
-                         (const bf16_t*)kcache, (const bf16_t*)vcache, seq_lens, sel_i, sel_s, nsel, (bf16_t*)o, g.Hq,
-                         g.Hkv, g.N, g.K, g.nw, pg);
-  } else {
+    if (ev) (void)hipEventRecord(ev[2], st);
     hipLaunchKernelGGL((decode_attend<IO, D>), dim3(BH * (g.K + g.nw)), dim3(256), 0, st, (const IO*)q,
                        (const IO*)kcache, (const IO*)vcache, seq_lens, sel_i, sel_s, nsel, part, sig, g.Hq, g.Hkv, g.N,
                        g.K, g.nw, pg);
