@@ -423,7 +423,7 @@ def run_decode(wd, steps, warmup, seed, dense=False):
     mirror_ms = e0.elapsed_time(e1)
     o = torch.empty_like(q)
     sel = torch.empty((wd.B, wd.Hq, wd.K), dtype=torch.int32, device="cuda")
-    ws = hils.workspace(dm, hils.OP_DECODE)
+    ws = hils.workspace(dm, hils.OP_DECODE_MIRROR)   # covers both steps
     # evicting by a READ of 512 MB of unrelated data leaves the 256 MB Infinity Cache and the
     # L2s holding clean lines: a write-flush would leave dirty lines whose write-back the
     # next step's first cache-allocating kernel pays for

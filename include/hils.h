@@ -76,7 +76,14 @@ enum {
 };
 
 /* op codes of hils_workspace_bytes */
-enum { HILS_OP_COMPRESS = 0, HILS_OP_SCORE_TOPK = 1, HILS_OP_PREFILL = 2, HILS_OP_DECODE = 3, HILS_OP_BACKWARD = 4 };
+enum {
+  HILS_OP_COMPRESS = 0,
+  HILS_OP_SCORE_TOPK = 1,
+  HILS_OP_PREFILL = 2,
+  HILS_OP_DECODE = 3,
+  HILS_OP_BACKWARD = 4,
+  HILS_OP_DECODE_MIRROR = 5 /* the decode calls over the landmark mirror */
+};
 
 typedef struct {
   int32_t B;         /* batch (sequences)                                              */
@@ -213,12 +220,14 @@ int hils_attn_decode_timed(const hils_dims_t* dims, const void* q, const void* k
  * chunk's codes the scan takes a lower and an upper bound of its exact fp32 score
  * (the codes' error is at most s/2 per element, so the dot product's is at most
  * (s/2) ||q^||_1; q^ enters as two 8-bit parts, hi + lo/254, whose error adds about
- * 1%, and a margin covers the fp32 sums); within each split of 1024 chunks,
- * every chunk whose upper bound reaches the split's K-th largest lower bound is
- * rescored exactly from kc/bc in hils_attn_decode's arithmetic, and the top K is taken
+ * 1%, and a margin covers the fp32 sums); each split of 1024 chunks keeps the chunks
+ * whose upper bound reaches its own K-th largest lower bound, and per (sequence, head)
+ * every kept chunk whose upper bound reaches the K-th largest kept lower bound is
+ * rescored exactly from kc/bc in hils_attn_decode's arithmetic; the top K is taken
  * from those.  kc_mirror must hold every chunk that hils_attn_decode would score
  * (c < floor((seq_lens[b]-1)/S), as kc/bc); it may be NULL only when N < S.
- * Workspace and limits as hils_attn_decode (HILS_OP_DECODE).  When many scores lie
+ * Workspace: hils_workspace_bytes(dims, HILS_OP_DECODE_MIRROR) (the decode workspace plus
+ * the scan's survivor lists); limits as hils_attn_decode.  When many scores lie
  * within the bounds' width of the K-th one (e.g. all equal), the rescoring reads more
  * of kc: the result stays exact, the step gets slower.
  * hils_attn_decode_mirror_timed: the same with stage times as hils_attn_decode_timed

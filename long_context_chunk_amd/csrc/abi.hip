@@ -129,6 +129,12 @@ size_t hils_workspace_bytes(const hils_dims_t* dims, int op) {
         return (size_t)-1;
       }
       return hils::decode_workspace_bytes(g);
+    case HILS_OP_DECODE_MIRROR:
+      if (g.C() > 16384) {
+        fail(HILS_E_UNSUPPORTED, "decode needs N/S <= 16384 (N=%d)", g.N);
+        return (size_t)-1;
+      }
+      return hils::decode_workspace_bytes(g, true);
     default:
       fail(HILS_E_INVAL, "unknown op %d", op);
       return (size_t)-1;
@@ -244,7 +250,7 @@ int run_decode(const hils_dims_t* dims, const void* q, const void* k_cache, cons
   if (g.C() > 0 && (!kc || !bc)) return fail(HILS_E_INVAL, "kc and bc must be non-NULL");
   if (g.C() > 16384) return fail(HILS_E_UNSUPPORTED, "decode needs N/S <= 16384 (N=%d)", g.N);
   if (g.r > 0 && (!qcal_D || !qcal_U)) return fail(HILS_E_INVAL, "qcal_rank > 0 needs qcal_D and qcal_U");
-  const size_t need = hils::decode_workspace_bytes(g);
+  const size_t need = hils::decode_workspace_bytes(g, kcm != nullptr);
   if (!ws && need > 0) return fail(HILS_E_WORKSPACE, "workspace is NULL (%zu bytes needed)", need);
   if (ws_bytes < need) return fail(HILS_E_WORKSPACE, "workspace too small: %zu < %zu", ws_bytes, need);
   hipStream_t st = (hipStream_t)stream;

@@ -37,11 +37,16 @@ constexpr int DS_KEEP = 64;      // candidate slots per workgroup (K <= 32 fills
 #endif
 
 struct DecodeWs {
-  size_t cand, sel_i, sel_s, nsel, part, sig, total;
+  size_t cand, sel_i, sel_s, nsel, part, sig, mcnt, ment, total;
+};
+// a survivor of the mirror scan: chunk, lower and upper bound of its exact score
+struct MirrorEnt {
+  int32_t c;
+  float lo, up;
 };
 static size_t al2(size_t x) { return (x + 255) / 256 * 256; }
 static int nsplit_of(const Geom& g) { return (g.C() + DS_CHUNKS - 1) / DS_CHUNKS; }
-static DecodeWs decode_ws(const Geom& g) {
+static DecodeWs decode_ws(const Geom& g, bool mirror = false) {
   DecodeWs w;
   const size_t bh = (size_t)g.B * g.Hq;
   size_t off = 0;
@@ -57,10 +62,16 @@ static DecodeWs decode_ws(const Geom& g) {
   off += al2(bh * (g.K + g.nw) * g.d * 4);
   w.sig = off;
   off += al2(bh * (g.K + g.nw) * 4);
+  w.mcnt = w.ment = off;
+  if (mirror) {   // the mirror scan's survivor lists: a count and up to DS_CHUNKS entries per split
+    off += al2(bh * std::max(1, nsplit_of(g)) * 4);
+    w.ment = off;
+    off += al2(bh * std::max(1, nsplit_of(g)) * (size_t)DS_CHUNKS * sizeof(MirrorEnt));
+  }
   w.total = off;
   return w;
 }
-size_t decode_workspace_bytes(const Geom& g) { return decode_ws(g).total; }
+size_t decode_workspace_bytes(const Geom& g, bool mirror) { return decode_ws(g, mirror).total; }
 
 // 64-bit selection keys (make_key: larger = better, ties to the lower chunk; 0 = none)
 // exchanged with lane j ^ X of the same 32-lane half
@@ -138,11 +149,12 @@ HILS_DEV uint64_t best32_of_1024(const uint64_t* keys, uint64_t (*wl)[64]) {
 }
 
 // The best 64 of the 1024 keys in LDS, as a sorted 64-list (hi, lo) in half 0 of wave 0
-// (256 threads; every thread calls it): each half-wave sorts 4 x 32 keys into a 64-list,
-// the halves of a wave and then the four waves are merged.
+// (every thread of the block calls it; the first four waves do the work): each half-wave
+// sorts 4 x 32 keys into a 64-list, the halves of a wave and then the four waves are merged.
 HILS_DEV void best64_of_1024(const uint64_t* keys, uint64_t (*wl)[64], uint64_t& hi, uint64_t& lo) {
   const int t = threadIdx.x, lane = t & 63, w = t >> 6, j = lane & 31;
-  {
+  hi = lo = 0ull;
+  if (w < 4) {
     const int base = w * 256 + (lane >> 5) * 128 + j;
     hi = keys[base];
     lo = keys[base + 32];
@@ -162,11 +174,13 @@ HILS_DEV void best64_of_1024(const uint64_t* keys, uint64_t (*wl)[64], uint64_t&
     }
   }
   __syncthreads();
-  const int a = (lane >> 5) * 2;   // wave 0: halves merge waves 0+1 and 2+3, then each other
-  hi = wl[a][j];
-  lo = wl[a][32 + j];
-  kl::merge64(hi, lo, wl[a + 1][j], wl[a + 1][32 + j], j);
-  kl::merge64(hi, lo, __shfl(hi, j + 32), __shfl(lo, j + 32), j);
+  if (w < 4) {
+    const int a = (lane >> 5) * 2;   // wave 0: halves merge waves 0+1 and 2+3, then each other
+    hi = wl[a][j];
+    lo = wl[a][32 + j];
+    kl::merge64(hi, lo, wl[a + 1][j], wl[a + 1][32 + j], j);
+    kl::merge64(hi, lo, __shfl(hi, j + 32), __shfl(lo, j + 32), j);
+  }
   __syncthreads();   // wl may be reused
 }
 
@@ -369,6 +383,250 @@ __global__ void __launch_bounds__(256) decode_merge(const uint64_t* __restrict__
   if (threadIdx.x == 0) nsel_out[bh] = n;
 }
 
+// Per-head selection over the mirror scan's survivor lists (1024 threads; every thread of
+// the block calls it).  Every split's list holds its chunks with U >= its own threshold,
+// which include its n chunks with the largest L; so the n-th largest L over all lists is
+// at most the n-th largest L of the head, hence at most its n-th best exact score (taken
+// over the first 1024 entries only when the lists hold more: a subset gives a smaller, still
+// valid threshold).  Every chunk of the exact top n has U >= theta; those entries are
+// rescored exactly from kc/bc in decode_scan's arrangement and arithmetic (same lanes, same
+// order of sums, so decode_scan's bits), in batches of 1024 entries, and the best 64 exact
+// keys are kept.  Writes ranks < K (chunk ids, -1 past n, and their scores).
+struct MirrorSelSmem {
+  float qs[128];
+  float ts[32];
+  int cnt[DS_MAX_SPLIT], off[DS_MAX_SPLIT + 1], tot;
+  float thw[16];
+  int wcnt[16];
+  int hist[256];
+  int sel_b, sel_above;
+  __align__(16) float eL[DS_CHUNKS];
+  float eU[DS_CHUNKS];
+  int eC[DS_CHUNKS], surv[DS_CHUNKS];
+  uint64_t keys[DS_CHUNKS];
+  uint64_t wl[4][64];
+  uint64_t run[64];
+};
+
+template <typename IO, int D>
+HILS_DEV void mirror_select(const IO* __restrict__ qv, const IO* __restrict__ Dw, const IO* __restrict__ Uw, int h,
+                            int r, const float* __restrict__ kb, const float* __restrict__ bb,
+                            const int32_t* __restrict__ cnts, const MirrorEnt* __restrict__ ents, int nsplit, int K,
+                            int n, MirrorSelSmem& sm, int32_t* out_i, float* out_s, int32_t* __restrict__ sel_user) {
+  constexpr int NT = 1024;
+  static_assert(NT == DS_CHUNKS, "one entry per thread in a batch");
+  const int t = threadIdx.x, lane = t & 63, w = t >> 6, j = lane & 31;
+  // the counts and the first 64 entries of every list are loaded together, before the
+  // counts are known (thread t: list t / 64, entry t % 64; lists hold up to 1024 entries)
+  const int32_t cnt_t = t < nsplit ? cnts[t] : 0;
+  const MirrorEnt pre = t / 64 < nsplit ? ents[(int64_t)(t / 64) * DS_CHUNKS + (t % 64)] : MirrorEnt{0, 0.f, 0.f};
+  qhat_to_lds<IO, D>(qv, Dw, Uw, h, r, sm.qs, sm.ts);   // block-wide barriers inside
+  if (t < nsplit) sm.cnt[t] = cnt_t;
+  if (t < 64) sm.run[t] = 0ull;
+  __syncthreads();
+  if (t == 0) {
+    int o = 0;
+    for (int s2 = 0; s2 < nsplit; ++s2) {
+      sm.off[s2] = o;
+      o += sm.cnt[s2];
+    }
+    sm.off[nsplit] = o;
+    sm.tot = o;
+  }
+  __syncthreads();
+  const int tot = sm.tot;
+  auto entry = [&](int x) {   // entry x of the lists laid end to end
+    int s2 = 0;
+    while (x >= sm.off[s2 + 1]) ++s2;
+    return ents[(int64_t)s2 * DS_CHUNKS + (x - sm.off[s2])];
+  };
+  // theta over the first batch: the preloaded entries go to their place in it; the
+  // (rare) entries past 64 of a list are loaded now
+  const int m1 = min(tot, DS_CHUNKS);
+  sm.eL[t] = -INFINITY;
+  __syncthreads();
+  {
+    const int l = t / 64, i = t % 64;
+    if (l < nsplit && i < sm.cnt[l]) {
+      const int x = sm.off[l] + i;
+      if (x < m1) {
+        sm.eL[x] = pre.lo;
+        sm.eU[x] = pre.up;
+        sm.eC[x] = pre.c;
+      }
+    }
+    for (int x = t; x < m1; x += 1024) {
+      int s2 = 0;
+      while (x >= sm.off[s2 + 1]) ++s2;
+      const int i2 = x - sm.off[s2];
+      if (i2 >= 64) {
+        const MirrorEnt e = ents[(int64_t)s2 * DS_CHUNKS + i2];
+        sm.eL[x] = e.lo;
+        sm.eU[x] = e.up;
+        sm.eC[x] = e.c;
+      }
+    }
+  }
+  __syncthreads();
+  // theta: a radix select of the n-th largest L over the first batch on order_f32(L),
+  // 8 bits at a time for the top 16: the smallest value with the 16 bits found has at
+  // least n entries at or above it, so it is at most the n-th largest L
+  float theta = -INFINITY;
+  if (n > 0) {   // uniform
+    const uint32_t key = t < m1 ? order_f32(sm.eL[t]) : 0u;
+    uint32_t found = 0u;
+    int above = 0;
+#pragma unroll
+    for (int pass = 0; pass < 2; ++pass) {
+      const int shift = 24 - 8 * pass;
+      if (t < 256) sm.hist[t] = 0;
+      __syncthreads();
+      if (t < m1 && (pass == 0 || (key >> 24) == (found >> 24))) atomicAdd(&sm.hist[(key >> shift) & 255u], 1);
+      __syncthreads();
+      if (w == 0) {   // the largest bucket whose count from the top reaches n
+        int c4 = 0;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) c4 += sm.hist[4 * lane + i];
+        int suf = c4;   // sum over lanes >= lane
+#pragma unroll
+        for (int o = 1; o < 64; o <<= 1) {
+          const int v = __shfl_down(suf, o);
+          suf += lane + o < 64 ? v : 0;
+        }
+        // within the lane's 4 buckets, from the top
+        int run = suf - c4 + above, bk = -1;
+#pragma unroll
+        for (int i = 3; i >= 0; --i) {
+          const int hv = sm.hist[4 * lane + i];
+          if (bk < 0 && run + hv >= n) bk = 4 * lane + i;
+          if (bk < 0) run += hv;
+        }
+        // the highest lane that found one holds the answer
+        const uint64_t bal = __ballot(bk >= 0);
+        const int src = bal ? 63 - __builtin_clzll(bal) : 0;
+        // no bucket (fewer than n entries, which the lists rule out): bucket 0, theta tiny
+        const int bsel = bal ? __shfl(bk, src) : 0, asel = bal ? __shfl(run, src) : 0;
+        if (lane == 0) {
+          sm.sel_b = bsel;
+          sm.sel_above = asel;
+        }
+      }
+      __syncthreads();
+      found |= (uint32_t)sm.sel_b << shift;
+      above = sm.sel_above;
+      __syncthreads();   // hist and sel_* are rewritten next pass
+    }
+    theta = unorder_f32(found);
+  }
+  constexpr int TPC = D / 16;       // decode_scan's arrangement
+  constexpr int CPP = NT / TPC;
+  const int sub = t % TPC, grp = t / TPC;
+  f32x4_t qe[4];
+#pragma unroll
+  for (int y = 0; y < 4; ++y) qe[y] = *reinterpret_cast<const f32x4_t*>(&sm.qs[4 * (sub + TPC * y)]);
+  const float tau = 1.0f / sqrtf((float)D);
+  for (int bs = 0; bs < tot; bs += DS_CHUNKS) {   // uniform
+    const int mb = min(DS_CHUNKS, tot - bs);
+    if (bs > 0) {
+      __syncthreads();   // the previous batch's reads of eU / eC are done
+      if (t < mb) {
+        const MirrorEnt e = entry(bs + t);
+        sm.eU[t] = e.up;
+        sm.eC[t] = e.c;
+      }
+      __syncthreads();
+    }
+    const bool sv = t < mb && sm.eU[t] >= theta;
+    const uint64_t bal = __ballot(sv);
+    if (lane == 0) sm.wcnt[w] = __popcll(bal);
+    sm.keys[t] = 0ull;
+    __syncthreads();
+    int before = 0, ns = 0;
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+      before += v < w ? sm.wcnt[v] : 0;
+      ns += sm.wcnt[v];
+    }
+    if (sv) sm.surv[before + __popcll(bal & ((1ull << lane) - 1ull))] = sm.eC[t];
+    __syncthreads();
+    for (int p0 = 0; p0 < ns; p0 += CPP) {
+      const int x = p0 + grp;
+      const int c = sm.surv[min(x, ns - 1)];
+      const f32x4_t* row = reinterpret_cast<const f32x4_t*>(kb + (int64_t)c * D);
+      f32x4_t kv[4];
+#pragma unroll
+      for (int y = 0; y < 4; ++y) kv[y] = row[sub + TPC * y];
+      const float bv = bb[c];
+      float s = 0.f;
+#pragma unroll
+      for (int y = 0; y < 4; ++y) {
+        s = fmaf(qe[y].x, kv[y].x, s);
+        s = fmaf(qe[y].y, kv[y].y, s);
+        s = fmaf(qe[y].z, kv[y].z, s);
+        s = fmaf(qe[y].w, kv[y].w, s);
+      }
+#pragma unroll
+      for (int o = TPC / 2; o >= 1; o >>= 1) s += __shfl_xor(s, o);
+      if (sub == 0 && x < ns) sm.keys[x] = make_key(fmaf(s, tau, bv), c);
+    }
+    __syncthreads();
+    if (ns <= 64) {   // one sorted 64-list, merged into the running best (wave 0)
+      if (w == 0) {
+        uint64_t hi = j < ns ? sm.keys[j] : 0ull, lo = 32 + j < ns ? sm.keys[32 + j] : 0ull;
+        kl::sort(hi, j);
+        kl::sort(lo, j);
+        kl::split(hi, lo, j);
+        uint64_t rh = sm.run[j], rl = sm.run[32 + j];
+        kl::merge64(rh, rl, hi, lo, j);
+        if (lane < 32) {
+          sm.run[lane] = rh;
+          sm.run[32 + lane] = rl;
+        }
+      }
+    } else {
+      uint64_t hi, lo;
+      best64_of_1024(sm.keys, sm.wl, hi, lo);
+      if (w == 0) {
+        uint64_t rh = sm.run[j], rl = sm.run[32 + j];
+        kl::merge64(rh, rl, hi, lo, j);
+        if (lane < 32) {
+          sm.run[lane] = rh;
+          sm.run[32 + lane] = rl;
+        }
+      }
+    }
+    __syncthreads();
+  }
+  if (w == 0 && lane < K) {
+    const uint64_t lk = sm.run[lane];
+    const bool ok = lane < n && lk != 0;
+    const int32_t ci = ok ? key_chunk(lk) : -1;
+    out_i[lane] = ci;
+    out_s[lane] = ok ? key_score(lk) : -INFINITY;
+    if (sel_user) sel_user[lane] = ci;
+  }
+}
+
+// mirror_select as a kernel, one workgroup per (b, h), for the steps that do not fuse it
+template <typename IO, int D>
+__global__ void __launch_bounds__(1024) decode_merge_m(const IO* __restrict__ q, const IO* __restrict__ Dw,
+                                                       const IO* __restrict__ Uw, const float* __restrict__ kc,
+                                                       const float* __restrict__ bc, const int32_t* __restrict__ mcnt,
+                                                       const MirrorEnt* __restrict__ ment,
+                                                       const int32_t* __restrict__ seq_lens, int32_t* __restrict__ sel_i,
+                                                       float* __restrict__ sel_s, int32_t* __restrict__ nsel_out,
+                                                       int32_t* __restrict__ sel_user, int Hq, int Hl, int C, int K,
+                                                       int r, int nsplit, int nw) {
+  __shared__ MirrorSelSmem sm;
+  const int bh = blockIdx.x, b = bh / Hq, h = bh % Hq;
+  const int n = min(K, candidate_chunks(seq_lens[b] - 1, C, nw));
+  const int64_t lrow = (int64_t)b * Hl + h / (Hq / Hl);
+  mirror_select<IO, D>(q + (int64_t)bh * D, Dw, Uw, h, r, kc + lrow * C * D, bc + lrow * C,
+                       mcnt + (int64_t)bh * nsplit, ment + (int64_t)bh * nsplit * DS_CHUNKS, nsplit, K, n, sm,
+                       sel_i + (int64_t)bh * K, sel_s + (int64_t)bh * K, sel_user ? sel_user + (int64_t)bh * K : nullptr);
+  if (threadIdx.x == 0) nsel_out[bh] = n;
+}
+
 // eight consecutive elements of a row, kept raw until used
 template <typename IO>
 struct raw8;
@@ -490,15 +748,16 @@ __global__ void __launch_bounds__(256) decode_attend(const IO* __restrict__ q, c
 // Lane s of every wave holds slot s's weight (MAXS = 128: slot 64 + s's too); the live
 // slot rows are all loaded at once.
 // The top-K merge, chunk attention and fusion of one (b, h) in one workgroup of four groups
-// of 256 threads (bf16 I/O).  The first four waves merge the splits' candidate lists into the
-// selection (merge_splits, as decode_merge).  Slots are then decode_attend's; group g takes
+// of 256 threads (bf16 I/O).  First the selection: the first four waves merge the splits'
+// candidate lists (merge_splits, as decode_merge), or, after the mirror scan, the block runs
+// mirror_select on its survivor lists.  Slots are then decode_attend's; group g takes
 // slots g, g + 4, ...
 // Per slot a group computes what decode_attend computes (the chunk's softmax output o_c
 // and its score: the selection score, or the window chunk's exact log-sum-exp) and folds
 // it into a running fusion (m, z, acc) with an online softmax; the next slot's K and V
 // rows are loaded while the current one is computed.  At the end the four groups' running
 // fusions are merged.  It gives decode_combine's result up to the order of the fp32 sums.
-template <int D, bool KB>
+template <int D, bool KB, bool MIR>
 __global__ void __launch_bounds__(1024) decode_attend_fused(const bf16_t* __restrict__ q,
                                                             const bf16_t* __restrict__ kcache,
                                                             const bf16_t* __restrict__ vcache,
@@ -506,7 +765,11 @@ __global__ void __launch_bounds__(1024) decode_attend_fused(const bf16_t* __rest
                                                             const uint64_t* __restrict__ cand,
                                                             int32_t* __restrict__ sel_user, bf16_t* __restrict__ out,
                                                             int Hq, int Hkv, int N, int C, int K, int nsplit, int nw,
-                                                            KvPages pg) {
+                                                            KvPages pg, const bf16_t* __restrict__ Dw,
+                                                            const bf16_t* __restrict__ Uw, const float* __restrict__ kc,
+                                                            const float* __restrict__ bc,
+                                                            const int32_t* __restrict__ mcnt,
+                                                            const MirrorEnt* __restrict__ ment, int Hl, int r) {
   constexpr int KJ = D / 32;        // logits: 4 threads per key, KJ runs of 8 dims each
   constexpr int TPR = D / 8;        // values: threads per row (8 dims each)
   constexpr int NG = 256 / TPR;     // key groups
@@ -530,8 +793,16 @@ __global__ void __launch_bounds__(1024) decode_attend_fused(const bf16_t* __rest
   const int NSL = K + nw;
   const int nsel = min(K, candidate_chunks(L - 1, C, nw));
   if (t < D / 8) *reinterpret_cast<u32x4_t*>(&qsh[8 * t]) = *reinterpret_cast<const u32x4_t*>(q + (int64_t)bh * D + 8 * t);
-  merge_splits<KB>(cand + (int64_t)bh * nsplit * DS_KEEP, nsplit, K, nsel, wl, m_i, m_s,
-                   sel_user ? sel_user + (int64_t)bh * K : nullptr);
+  if constexpr (MIR) {   // the selection from the mirror scan's survivor lists
+    __shared__ MirrorSelSmem msm;
+    const int64_t lrow = (int64_t)b * Hl + h / (Hq / Hl);
+    mirror_select<bf16_t, D>(q + (int64_t)bh * D, Dw, Uw, h, r, kc + lrow * C * D, bc + lrow * C,
+                             mcnt + (int64_t)bh * nsplit, ment + (int64_t)bh * nsplit * DS_CHUNKS, nsplit, K, nsel, msm,
+                             m_i, m_s, sel_user ? sel_user + (int64_t)bh * K : nullptr);
+  } else {
+    merge_splits<KB>(cand + (int64_t)bh * nsplit * DS_KEEP, nsplit, K, nsel, wl, m_i, m_s,
+                     sel_user ? sel_user + (int64_t)bh * K : nullptr);
+  }
   __syncthreads();
   if (t < NSL) {   // slot table: chunk (-1: nothing), keys, score (selected slots)
     int c = -1, nk = 64;
@@ -763,15 +1034,12 @@ __global__ void __launch_bounds__(256) mirror_build(const float* __restrict__ kc
 template <typename IO, int D, bool KB, int UNR>
 __global__ void __launch_bounds__(256) decode_scan_m(const IO* __restrict__ q, const IO* __restrict__ Dw,
                                                      const IO* __restrict__ Uw, const uint8_t* __restrict__ kcm,
-                                                     const float* __restrict__ kc, const float* __restrict__ bc,
-                                                     const int32_t* __restrict__ seq_lens, uint64_t* __restrict__ cand,
-                                                     int Hq, int Hl, int C, int K, int r, int nsplit, int nw,
-                                                     int64_t mrows) {
+                                                     const int32_t* __restrict__ seq_lens, int32_t* __restrict__ mcnt,
+                                                     MirrorEnt* __restrict__ ment, int Hq, int Hl, int C, int K, int r,
+                                                     int nsplit, int nw, int64_t mrows) {
   constexpr int TPM = D / 16;       // mirror: threads per chunk, 16 codes (one 16-byte load) each
   constexpr int CPM = 256 / TPM;    // mirror: chunks per pass
   constexpr int STEP = CPM * UNR;
-  constexpr int TPC = D / 16;       // exact rescoring: decode_scan's arrangement
-  constexpr int CPP = 256 / TPC;
   __shared__ __align__(16) float qs[D];
   __shared__ float ts[32];
   __shared__ float mq_s, l1_s;
@@ -784,10 +1052,8 @@ __global__ void __launch_bounds__(256) decode_scan_m(const IO* __restrict__ q, c
   static_assert(NV <= 256 && NV % 4 == 0, "");
   __shared__ __align__(16) float lb_s[NV];   // each chunk lane's T largest lower bounds
   __shared__ float thw[4];
-  __shared__ uint64_t keys[DS_CHUNKS];   // the survivors' exact keys
-  __shared__ float ubs[DS_CHUNKS];       // upper bounds
+  __shared__ float lbs[DS_CHUNKS], ubs[DS_CHUNKS];   // lower and upper bounds
   __shared__ int16_t surv[DS_CHUNKS];    // survivors (offsets in the workgroup's range)
-  __shared__ uint64_t wl[4][64];
   __shared__ int wcnt[4];
   const int sp = blockIdx.x % nsplit, bh = blockIdx.x / nsplit;
   const int b = bh / Hq, h = bh % Hq;
@@ -795,10 +1061,11 @@ __global__ void __launch_bounds__(256) decode_scan_m(const IO* __restrict__ q, c
   const int P = candidate_chunks(L - 1, C, nw);
   const int c_beg = sp * DS_CHUNKS, c_end = min(P, c_beg + DS_CHUNKS);
   const int nloc = max(0, c_end - c_beg), n = min(K, nloc);
-  const int t = threadIdx.x, lane = t & 63, w = t >> 6, j = lane & 31;
-  uint64_t* out = cand + ((int64_t)bh * nsplit + sp) * DS_KEEP;
+  const int t = threadIdx.x, lane = t & 63, w = t >> 6;
+  int32_t* cnt_out = mcnt + (int64_t)bh * nsplit + sp;
+  MirrorEnt* ent_out = ment + ((int64_t)bh * nsplit + sp) * DS_CHUNKS;
   if (n == 0) {   // no chunk here (uniform): an empty list
-    if (t < DS_KEEP) out[t] = 0ull;
+    if (t == 0) *cnt_out = 0;
     return;
   }
   const int msub = t % TPM, mgrp = t / TPM;
@@ -890,6 +1157,7 @@ __global__ void __launch_bounds__(256) decode_scan_m(const IO* __restrict__ q, c
         const float dl = fmaf(dfac, sc, fmaf(0x1p-20f, fabsf(sh) + fabsf(bv), dabs));
         const bool live = c < c_end;
         const float lv = live ? sh - dl : -INFINITY;
+        lbs[c - c_beg] = lv;
         ubs[c - c_beg] = live ? sh + dl : -INFINITY;
 #pragma unroll
         for (int k = T - 1; k >= 1; --k) top[k] = fmaxf(top[k], fminf(top[k - 1], lv));
@@ -956,70 +1224,13 @@ __global__ void __launch_bounds__(256) decode_scan_m(const IO* __restrict__ q, c
     ns = total;
     __syncthreads();   // wcnt is rewritten next round
   }
-  // exact keys of the survivors in decode_scan's arrangement: dims 4 (sub + TPC y) .. + 3
-  const bool small = ns <= 64;
-  if (!small)
-    for (int x = ns + t; x < DS_CHUNKS; x += 256) keys[x] = 0ull;
-  {
-    const int sub = t % TPC, grp = t / TPC;
-    f32x4_t qe[4];
-#pragma unroll
-    for (int y = 0; y < 4; ++y) qe[y] = *reinterpret_cast<const f32x4_t*>(&qs[4 * (sub + TPC * y)]);
-    const float* kb = kc + lrow * C * D;
-    const float* bb = bc + lrow * C;
-    // two survivors per thread group at a time, both rows' loads issued before either sum
-    for (int p0 = 0; p0 < ns; p0 += 2 * CPP) {
-      int xs[2], cs[2];
-      f32x4_t kv[2][4];
-      float bv[2];
-#pragma unroll
-      for (int v = 0; v < 2; ++v) {
-        xs[v] = p0 + v * CPP + grp;
-        cs[v] = c_beg + surv[min(xs[v], ns - 1)];
-        const f32x4_t* row = reinterpret_cast<const f32x4_t*>(kb + (int64_t)cs[v] * D);
-#pragma unroll
-        for (int y = 0; y < 4; ++y) kv[v][y] = row[sub + TPC * y];
-        bv[v] = bb[cs[v]];
-      }
-#pragma unroll
-      for (int v = 0; v < 2; ++v) {
-        float s = 0.f;
-#pragma unroll
-        for (int y = 0; y < 4; ++y) {
-          s = fmaf(qe[y].x, kv[v][y].x, s);
-          s = fmaf(qe[y].y, kv[v][y].y, s);
-          s = fmaf(qe[y].z, kv[v][y].z, s);
-          s = fmaf(qe[y].w, kv[v][y].w, s);
-        }
-#pragma unroll
-        for (int o = TPC / 2; o >= 1; o >>= 1) s += __shfl_xor(s, o);
-        if (sub == 0 && xs[v] < ns) keys[xs[v]] = make_key(fmaf(s, tau, bv[v]), cs[v]);
-      }
-    }
+  // the survivors go to this split's list; the per-head selection (mirror_select) takes
+  // the threshold over all splits' lists and rescores what reaches it
+  for (int x = t; x < ns; x += 256) {
+    const int o = surv[x];
+    ent_out[x] = MirrorEnt{c_beg + o, lbs[o], ubs[o]};
   }
-  __syncthreads();
-  if (small) {   // at most 64 survivors: one sorted 64-list (both halves of wave 0 build it)
-    if (w == 0) {
-      uint64_t hi = j < ns ? keys[j] : 0ull, lo = 32 + j < ns ? keys[32 + j] : 0ull;
-      kl::sort(hi, j);
-      kl::sort(lo, j);
-      kl::split(hi, lo, j);
-      if (lane < 32) {
-        out[lane] = hi;
-        if constexpr (KB) out[32 + lane] = lo;
-      }
-    }
-  } else if constexpr (KB) {
-    uint64_t hi, lo;
-    best64_of_1024(keys, wl, hi, lo);
-    if (lane < 32 && w == 0) {
-      out[lane] = hi;
-      out[32 + lane] = lo;
-    }
-  } else {
-    const uint64_t lk = best32_of_1024(keys, wl);
-    if (lane < 32 && w == 0) out[lane] = lk;
-  }
+  if (t == 0) *cnt_out = ns;
 }
 
 template <int D>
@@ -1059,13 +1270,15 @@ static hipError_t launch_decode_t(const Geom& g, const void* q, const void* kcac
                                   const int32_t* seq_lens, const float* kc, const float* bc, const uint8_t* kcm,
                                   const void* Dw, const void* Uw, int32_t* sel_user, void* o, char* ws, hipStream_t st,
                                   hipEvent_t* ev, KvPages pg) {
-  const DecodeWs w = decode_ws(g);
+  const DecodeWs w = decode_ws(g, kcm != nullptr);
   uint64_t* cand = (uint64_t*)(ws + w.cand);
   int32_t* sel_i = (int32_t*)(ws + w.sel_i);
   float* sel_s = (float*)(ws + w.sel_s);
   int32_t* nsel = (int32_t*)(ws + w.nsel);
   float* part = (float*)(ws + w.part);
   float* sig = (float*)(ws + w.sig);
+  int32_t* mcnt = (int32_t*)(ws + w.mcnt);
+  MirrorEnt* ment = (MirrorEnt*)(ws + w.ment);
   const int C = g.C(), BH = g.B * g.Hq;
   const int nsplit = std::max(1, nsplit_of(g));  // one (empty) split still writes the selection
   if (nsplit > DS_MAX_SPLIT) return hipErrorInvalidValue;  // N/S > 16384, rejected by the ABI first
@@ -1073,14 +1286,14 @@ static hipError_t launch_decode_t(const Geom& g, const void* q, const void* kcac
   const bool kb = g.K > 32;   // keep 64 candidates per split
   bool fused = false;   // one workgroup per (b, h) fills the chip: merge, attention and fusion in one kernel
   if constexpr (std::is_same<IO, bf16_t>::value) fused = BH >= device_cus();
-  if (kcm) {   // the scan over the 8-bit mirror, exact rescoring of each split's survivors
+  if (kcm) {   // the scan over the 8-bit mirror: each split's survivors of its bounds
     if (kb)
       hipLaunchKernelGGL((decode_scan_m<IO, D, true, DSM_UNR>), dim3(BH * nsplit), dim3(256), 0, st, (const IO*)q,
-                         (const IO*)Dw, (const IO*)Uw, kcm, kc, bc, seq_lens, cand, g.Hq, g.Hl, C, g.K, g.r, nsplit,
+                         (const IO*)Dw, (const IO*)Uw, kcm, seq_lens, mcnt, ment, g.Hq, g.Hl, C, g.K, g.r, nsplit,
                          g.nw, (int64_t)g.B * g.Hl * C);
     else
       hipLaunchKernelGGL((decode_scan_m<IO, D, false, DSM_UNR>), dim3(BH * nsplit), dim3(256), 0, st, (const IO*)q,
-                         (const IO*)Dw, (const IO*)Uw, kcm, kc, bc, seq_lens, cand, g.Hq, g.Hl, C, g.K, g.r, nsplit,
+                         (const IO*)Dw, (const IO*)Uw, kcm, seq_lens, mcnt, ment, g.Hq, g.Hl, C, g.K, g.r, nsplit,
                          g.nw, (int64_t)g.B * g.Hl * C);
   } else if (kb) {
     hipLaunchKernelGGL((decode_scan<IO, D, true>), dim3(BH * nsplit), dim3(256), 0, st, (const IO*)q, (const IO*)Dw,
@@ -1093,17 +1306,27 @@ static hipError_t launch_decode_t(const Geom& g, const void* q, const void* kcac
   if (fused) {
     if (ev) (void)hipEventRecord(ev[2], st);   // the merge runs inside the fused kernel
     if constexpr (std::is_same<IO, bf16_t>::value) {
-      if (kb)
-        hipLaunchKernelGGL((decode_attend_fused<D, true>), dim3(BH), dim3(1024), 0, st, (const bf16_t*)q,
-                           (const bf16_t*)kcache, (const bf16_t*)vcache, seq_lens, (const uint64_t*)cand, sel_user,
-                           (bf16_t*)o, g.Hq, g.Hkv, g.N, C, g.K, nsplit, g.nw, pg);
+      const bf16_t *qb = (const bf16_t*)q, *kb16 = (const bf16_t*)kcache, *vb16 = (const bf16_t*)vcache;
+      const bf16_t *Db = (const bf16_t*)Dw, *Ub = (const bf16_t*)Uw;
+      if (kcm)
+        hipLaunchKernelGGL((decode_attend_fused<D, false, true>), dim3(BH), dim3(1024), 0, st, qb, kb16, vb16, seq_lens,
+                           (const uint64_t*)cand, sel_user, (bf16_t*)o, g.Hq, g.Hkv, g.N, C, g.K, nsplit, g.nw, pg, Db,
+                           Ub, kc, bc, (const int32_t*)mcnt, (const MirrorEnt*)ment, g.Hl, g.r);
+      else if (kb)
+        hipLaunchKernelGGL((decode_attend_fused<D, true, false>), dim3(BH), dim3(1024), 0, st, qb, kb16, vb16, seq_lens,
+                           (const uint64_t*)cand, sel_user, (bf16_t*)o, g.Hq, g.Hkv, g.N, C, g.K, nsplit, g.nw, pg, Db,
+                           Ub, kc, bc, (const int32_t*)mcnt, (const MirrorEnt*)ment, g.Hl, g.r);
       else
-        hipLaunchKernelGGL((decode_attend_fused<D, false>), dim3(BH), dim3(1024), 0, st, (const bf16_t*)q,
-                           (const bf16_t*)kcache, (const bf16_t*)vcache, seq_lens, (const uint64_t*)cand, sel_user,
-                           (bf16_t*)o, g.Hq, g.Hkv, g.N, C, g.K, nsplit, g.nw, pg);
+        hipLaunchKernelGGL((decode_attend_fused<D, false, false>), dim3(BH), dim3(1024), 0, st, qb, kb16, vb16,
+                           seq_lens, (const uint64_t*)cand, sel_user, (bf16_t*)o, g.Hq, g.Hkv, g.N, C, g.K, nsplit,
+                           g.nw, pg, Db, Ub, kc, bc, (const int32_t*)mcnt, (const MirrorEnt*)ment, g.Hl, g.r);
     }
   } else {
-    if (kb)
+    if (kcm)
+      hipLaunchKernelGGL((decode_merge_m<IO, D>), dim3(BH), dim3(1024), 0, st, (const IO*)q, (const IO*)Dw,
+                         (const IO*)Uw, kc, bc, (const int32_t*)mcnt, (const MirrorEnt*)ment, seq_lens, sel_i, sel_s,
+                         nsel, sel_user, g.Hq, g.Hl, C, g.K, g.r, nsplit, g.nw);
+    else if (kb)
       hipLaunchKernelGGL(decode_merge<true>, dim3(BH), dim3(256), 0, st, (const uint64_t*)cand, seq_lens, sel_i,
                          sel_s, nsel, sel_user, g.Hq, C, g.K, nsplit, g.nw);
     else
@@ -1128,7 +1351,7 @@ hipError_t launch_decode(const Geom& g, const void* q, const void* kcache, const
                          const float* kc, const float* bc, const uint8_t* kcm, const void* Dw, const void* Uw,
                          int32_t* sel_idx_out, void* o, void* ws, size_t ws_bytes, hipStream_t st, hipEvent_t* ev,
                          KvPages pg) {
-  if (ws_bytes < decode_workspace_bytes(g)) return hipErrorInvalidValue;
+  if (ws_bytes < decode_workspace_bytes(g, kcm != nullptr)) return hipErrorInvalidValue;
   char* w = (char*)ws;
   if (g.io == 0)
     return g.d == 64

@@ -72,7 +72,8 @@ hipError_t launch_prefill_attend(const Geom& g, const void* q, const void* k, co
                                  hipEvent_t* ev = nullptr);
 
 // One decode step.
-size_t decode_workspace_bytes(const Geom& g);
+// mirror: the workspace of the step over the landmark mirror (it adds the scan's survivor lists)
+size_t decode_workspace_bytes(const Geom& g, bool mirror = false);
 // kcm (nullable): the 8-bit mirror of kc/bc (launch_mirror); when given, the scan reads it
 // and the survivors of its score bounds are rescored exactly from kc/bc.
 // ev (nullable): four events recorded before the scan, after it, after the top-K merge, and

@@ -16,7 +16,7 @@ _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libhils.so")
 
 F32, BF16 = 0, 1
-OP_COMPRESS, OP_SCORE_TOPK, OP_PREFILL, OP_DECODE, OP_BACKWARD = 0, 1, 2, 3, 4
+OP_COMPRESS, OP_SCORE_TOPK, OP_PREFILL, OP_DECODE, OP_BACKWARD, OP_DECODE_MIRROR = 0, 1, 2, 3, 4, 5
 OK, E_INVAL, E_UNSUPPORTED, E_WORKSPACE, E_HIP = 0, -1, -2, -3, -4
 
 SYMBOLS = ("hils_workspace_bytes", "hils_landmark_compress", "hils_chunk_score_topk", "hils_attn_prefill",

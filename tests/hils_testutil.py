@@ -196,7 +196,7 @@ def gpu_decode(w, x, kc=None, bc=None, mirror=False):
     lens = torch.from_numpy(x["seq_lens"]).cuda()
     o = torch.empty_like(q)
     sel = torch.empty((w.B, w.Hq, w.K), dtype=torch.int32, device="cuda")
-    ws = hils.workspace(dm, hils.OP_DECODE)
+    ws = hils.workspace(dm, hils.OP_DECODE_MIRROR if mirror else hils.OP_DECODE)
     D = upload(x["D"], w.io) if w.qcal_rank else None
     U = upload(x["U"], w.io) if w.qcal_rank else None
     kcm = None

@@ -266,7 +266,8 @@ def test_mirror_entry_points_validation():
     assert lib.hils_landmark_mirror(ctypes.byref(d), None, None, 3, 3, None, None) == hils.OK
     bad = hils.dims(2, 8, 2, 96, 4096, 16)
     assert lib.hils_landmark_mirror(ctypes.byref(bad), fake, fake, 0, 4, fake, None) == hils.E_UNSUPPORTED
-    ws_need = hils.workspace_bytes(d, hils.OP_DECODE)
+    ws_need = hils.workspace_bytes(d, hils.OP_DECODE_MIRROR)
+    assert ws_need > hils.workspace_bytes(d, hils.OP_DECODE)   # plus the scan's survivor lists
     args = [fake, fake, fake, fake, fake, fake]
     rc = lib.hils_attn_decode_mirror(ctypes.byref(d), *args, None, None, None, None, fake, fake, ws_need, None)
     assert rc == hils.E_INVAL and b"kc_mirror" in lib.hils_last_error()
@@ -294,7 +295,7 @@ def test_paged_mirror_entry_point_validation():
     fake = ctypes.c_void_p(0x1000)
     d = hils.dims(2, 8, 2, 128, 4096, 16)
     C = 4096 // 64
-    need = hils.workspace_bytes(d, hils.OP_DECODE)
+    need = hils.workspace_bytes(d, hils.OP_DECODE_MIRROR)
     rc = lib.hils_attn_decode_paged_mirror(ctypes.byref(d), fake, fake, fake, fake, C, 4 * C, fake, fake, fake, None,
                                            None, None, None, fake, fake, need, None)
     assert rc == hils.E_INVAL and b"kc_mirror" in lib.hils_last_error()

@@ -523,7 +523,8 @@ def _paged_decode_case(w, name):
         hils.landmark_mirror(dm, kc, bc, kcm, c, c + 1)
     om = torch.full_like(q, float("nan"))
     selm = torch.empty_like(sel)
-    hils.attn_decode_paged(dm, q, kpt, vpt, tab, lens, kc, bc, om, ws, qcal_D=D, qcal_U=U, sel_idx=selm,
+    wsm = hils.workspace(dm, hils.OP_DECODE_MIRROR)
+    hils.attn_decode_paged(dm, q, kpt, vpt, tab, lens, kc, bc, om, wsm, qcal_D=D, qcal_U=U, sel_idx=selm,
                            kc_mirror=kcm)
     torch.cuda.synchronize()
     np.testing.assert_array_equal(selm.cpu().numpy(), sel.cpu().numpy())
