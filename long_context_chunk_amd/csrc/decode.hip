@@ -1021,16 +1021,12 @@ __global__ void __launch_bounds__(256) mirror_build(const float* __restrict__ kc
   }
 }
 
-// The decode scan over the mirror.  Per chunk, from the mirror row, a lower and an upper
-// bound of the exact score, L <= s <= U with s = fmaf(q^ . k', tau, b') as decode_scan
-// computes it in fp32.  Within the workgroup's chunks, theta = the n-th largest of a
-// subset of the L (n = min(K, chunks)) is at most the n-th largest L there, hence at most
-// the n-th best exact score, so every chunk among the workgroup's exact best n has
-// U >= theta: those survivors are rescored exactly from the
-// fp32 k' and b' in decode_scan's arithmetic (same lanes, same order of sums, so the
-// same bits), and the best of their exact keys are written as decode_scan writes its
-// list.  The list's first n entries equal decode_scan's; further entries (exact keys of
-// other chunks, or empty) rank below them, so decode_merge takes the same top K.
+// The decode scan over the mirror.  Per chunk, from its codes, a lower and an upper bound of
+// the exact score, L <= s <= U with s = fmaf(q^ . k', tau, b') as decode_scan computes it
+// in fp32.  Within the workgroup's chunks, theta = the n-th largest of a subset of the L
+// (n = min(K, chunks)) is at most the n-th largest L there; the chunks with U >= theta (the
+// survivors) therefore include the workgroup's n chunks of largest L and every chunk of its
+// exact best n.  They go to the split's list (chunk, L, U) for mirror_select.
 template <typename IO, int D, bool KB, int UNR>
 __global__ void __launch_bounds__(256) decode_scan_m(const IO* __restrict__ q, const IO* __restrict__ Dw,
                                                      const IO* __restrict__ Uw, const uint8_t* __restrict__ kcm,
