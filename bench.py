@@ -142,7 +142,8 @@ def stage_roofline(w, cnt, stage_ms):
 KERNEL_SOURCES = {
     "compress": "compress.hip", "score_threshold": "score_topk.hip", "score_select": "score_topk.hip",
     "bucket": "attend.hip", "chunk_attend": "attend.hip", "own_attend": "attend.hip", "fuse": "attend.hip",
-    "decode_scan": "decode.hip", "decode_merge": "decode.hip", "decode_scan_m": "decode.hip", "decode_attend": "decode.hip", "decode_combine": "decode.hip",
+    "decode_scan": "decode.hip", "decode_merge": "decode.hip", "decode_scan_m": "decode.hip",
+    "decode_merge_m": "decode.hip", "decode_attend_fused": "decode.hip", "decode_attend_fused_mirror": "decode.hip", "decode_attend": "decode.hip", "decode_combine": "decode.hip",
 }
 
 
