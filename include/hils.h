@@ -177,7 +177,8 @@ int hils_attn_prefill_timed(const hils_dims_t* dims, const void* q, const void* 
  * kc/bc [B,Hlmk,floor(N/S),d] must hold the compressed keys of every complete
  * chunk c < floor((seq_lens[b]-1)/S) (see hils_landmark_compress).
  * Writes o [B,Hq,d]; sel_idx_out (nullable) [B,Hq,K].
- * Limits of the library: N/S <= 16384 (decode and prefill); prefill also needs
+ * Limits of the library: N/S <= 65536 for decode (4M tokens at S = 64), N/S <= 16384
+ * for prefill and hils_chunk_score_topk; prefill also needs
  * B*Hq*N*K < 2^32 and N*K < 2^26 (the latter only binds for K > 32).
  */
 int hils_attn_decode(const hils_dims_t* dims, const void* q, const void* k_cache, const void* v_cache,

@@ -124,14 +124,14 @@ size_t hils_workspace_bytes(const hils_dims_t* dims, int op) {
       if (check_prefill(g) != HILS_OK) return (size_t)-1;
       return hils::backward_workspace_bytes(g);
     case HILS_OP_DECODE:
-      if (g.C() > 16384) {
-        fail(HILS_E_UNSUPPORTED, "decode needs N/S <= 16384 (N=%d)", g.N);
+      if (g.C() > 65536) {
+        fail(HILS_E_UNSUPPORTED, "decode needs N/S <= 65536 (N=%d)", g.N);
         return (size_t)-1;
       }
       return hils::decode_workspace_bytes(g);
     case HILS_OP_DECODE_MIRROR:
-      if (g.C() > 16384) {
-        fail(HILS_E_UNSUPPORTED, "decode needs N/S <= 16384 (N=%d)", g.N);
+      if (g.C() > 65536) {
+        fail(HILS_E_UNSUPPORTED, "decode needs N/S <= 65536 (N=%d)", g.N);
         return (size_t)-1;
       }
       return hils::decode_workspace_bytes(g, true);
@@ -248,7 +248,7 @@ int run_decode(const hils_dims_t* dims, const void* q, const void* k_cache, cons
   if (!q || !k_cache || !v_cache || !seq_lens || !o)
     return fail(HILS_E_INVAL, "q, k_cache, v_cache, seq_lens and o must be non-NULL");
   if (g.C() > 0 && (!kc || !bc)) return fail(HILS_E_INVAL, "kc and bc must be non-NULL");
-  if (g.C() > 16384) return fail(HILS_E_UNSUPPORTED, "decode needs N/S <= 16384 (N=%d)", g.N);
+  if (g.C() > 65536) return fail(HILS_E_UNSUPPORTED, "decode needs N/S <= 65536 (N=%d)", g.N);
   if (g.r > 0 && (!qcal_D || !qcal_U)) return fail(HILS_E_INVAL, "qcal_rank > 0 needs qcal_D and qcal_U");
   const size_t need = hils::decode_workspace_bytes(g, kcm != nullptr);
   if (!ws && need > 0) return fail(HILS_E_WORKSPACE, "workspace is NULL (%zu bytes needed)", need);
@@ -391,7 +391,7 @@ int hils_attn_decode_noalloc(const hils_dims_t* dims, const void* q, const void*
   hils::Geom g;
   int rc = check_dims(dims, g);
   if (rc) return rc;
-  if (g.C() > 16384) return fail(HILS_E_UNSUPPORTED, "decode needs N/S <= 16384 (N=%d)", g.N);
+  if (g.C() > 65536) return fail(HILS_E_UNSUPPORTED, "decode needs N/S <= 65536 (N=%d)", g.N);
   const size_t need = hils::decode_workspace_bytes(g);
   if (need > (size_t)HILS_NOALLOC_SCRATCH_BYTES)
     return fail(HILS_E_UNSUPPORTED, "hils_attn_decode_noalloc: these dims need %zu bytes of scratch, above its %zu",

@@ -30,7 +30,7 @@
 namespace hils {
 
 constexpr int DS_CHUNKS = 1024;  // chunks scored per decode_scan workgroup
-constexpr int DS_MAX_SPLIT = 16;  // scan workgroups per (b, h): N/S <= 16384
+constexpr int DS_MAX_SPLIT = 64;  // scan workgroups per (b, h): N/S <= 65536
 constexpr int DS_KEEP = 64;      // candidate slots per workgroup (K <= 32 fills 32 of them)
 #ifndef DSM_UNR
 #define DSM_UNR 2                // chunk passes per register buffer of the mirror scan
@@ -313,13 +313,12 @@ __global__ void __launch_bounds__(256) decode_scan(const IO* __restrict__ q, con
 // exact top-K of one (b, h) from the sorted candidate lists of its splits (cb: the first
 // list), rank order, ties to the lowest id; n = min(K, candidate chunks).  Every thread of
 // the block calls it (it has a block-wide barrier); the first four waves do the work:
-// half-wave x of wave w takes lists 2w + x and 2w + x + 8, the halves of each wave merge,
-// then wave 0 merges the four wave lists and writes ranks < K to out_i / out_s (and sel_user
-// when given): chunk ids, -1 past n.
+// half-wave x of wave w takes lists 2w + x, 2w + x + 8, 2w + x + 16, ..., the halves of each
+// wave merge, then wave 0 merges the four wave lists and writes ranks < K to out_i / out_s
+// (and sel_user when given): chunk ids, -1 past n.
 template <bool KB>
 HILS_DEV void merge_splits(const uint64_t* __restrict__ cb, int nsplit, int K, int n, uint64_t (*wl)[64],
                            int32_t* out_i, float* out_s, int32_t* __restrict__ sel_user) {
-  static_assert(DS_MAX_SPLIT == 16, "two lists per half-wave");
   const int t = threadIdx.x, lane = t & 63, w = t >> 6;
   const int j = lane & 31;
   const int li = 2 * w + (lane >> 5);
@@ -329,15 +328,16 @@ HILS_DEV void merge_splits(const uint64_t* __restrict__ cb, int nsplit, int K, i
   uint64_t hi = 0, lo = 0;
   auto ld = [&](int l, int off) { return l < nsplit ? cb[l * DS_KEEP + off + j] : 0ull; };  // empty lists: zero keys
   if (w < 4) {
+    // the same number of lists in every half-wave (empty ones are zero keys)
     if constexpr (!KB) {
       hi = ld(li, 0);
-      dmerge_sorted(hi, ld(li + 8, 0));
+      for (int l0 = 8; l0 < nsplit; l0 += 8) dmerge_sorted(hi, ld(li + l0, 0));
       dmerge_sorted(hi, __shfl(hi, j + 32));
       if (lane < 32) wl[w][lane] = hi;
     } else {
       hi = ld(li, 0);
       lo = ld(li, 32);
-      kl::merge64(hi, lo, ld(li + 8, 0), ld(li + 8, 32), j);
+      for (int l0 = 8; l0 < nsplit; l0 += 8) kl::merge64(hi, lo, ld(li + l0, 0), ld(li + l0, 32), j);
       kl::merge64(hi, lo, __shfl(hi, j + 32), __shfl(lo, j + 32), j);
       if (lane < 32) {
         wl[w][lane] = hi;
@@ -416,8 +416,8 @@ HILS_DEV void mirror_select(const IO* __restrict__ qv, const IO* __restrict__ Dw
   constexpr int NT = 1024;
   static_assert(NT == DS_CHUNKS, "one entry per thread in a batch");
   const int t = threadIdx.x, lane = t & 63, w = t >> 6, j = lane & 31;
-  // the counts and the first 64 entries of every list are loaded together, before the
-  // counts are known (thread t: list t / 64, entry t % 64; lists hold up to 1024 entries)
+  // the counts and the first 64 entries of the first 16 lists are loaded together, before
+  // the counts are known (thread t: list t / 64, entry t % 64; lists hold up to 1024 entries)
   const int32_t cnt_t = t < nsplit ? cnts[t] : 0;
   const MirrorEnt pre = t / 64 < nsplit ? ents[(int64_t)(t / 64) * DS_CHUNKS + (t % 64)] : MirrorEnt{0, 0.f, 0.f};
   qhat_to_lds<IO, D>(qv, Dw, Uw, h, r, sm.qs, sm.ts);   // block-wide barriers inside
@@ -459,7 +459,7 @@ HILS_DEV void mirror_select(const IO* __restrict__ qv, const IO* __restrict__ Dw
       int s2 = 0;
       while (x >= sm.off[s2 + 1]) ++s2;
       const int i2 = x - sm.off[s2];
-      if (i2 >= 64) {
+      if (i2 >= 64 || s2 >= NT / 64) {   // not preloaded
         const MirrorEnt e = ents[(int64_t)s2 * DS_CHUNKS + i2];
         sm.eL[x] = e.lo;
         sm.eU[x] = e.up;

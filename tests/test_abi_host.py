@@ -308,3 +308,15 @@ def test_paged_mirror_entry_point_validation():
     rc = lib.hils_attn_decode_paged_mirror(ctypes.byref(d), fake, fake, fake, fake, C, 4 * C, fake, fake, fake, fake,
                                            None, None, None, fake, fake, need - 1, None)
     assert rc == hils.E_WORKSPACE
+
+
+def test_decode_chunk_limit():
+    """Decode takes up to 65536 chunks (4M tokens at S = 64); prefill and scoring 16384."""
+    ok = hils.dims(1, 2, 1, 64, 65536 * 64, 16)
+    assert hils.workspace_bytes(ok, hils.OP_DECODE) > 0
+    assert hils.workspace_bytes(ok, hils.OP_DECODE_MIRROR) > hils.workspace_bytes(ok, hils.OP_DECODE)
+    for op in (hils.OP_DECODE, hils.OP_DECODE_MIRROR):
+        with pytest.raises(hils.HilsError):
+            hils.workspace_bytes(hils.dims(1, 2, 1, 64, 65537 * 64, 16), op)
+    with pytest.raises(hils.HilsError):
+        hils.workspace_bytes(hils.dims(1, 2, 1, 64, 16385 * 64, 16), hils.OP_PREFILL)

@@ -19,7 +19,7 @@ import oracle
 import synth
 from hils_testutil import check_selection_and_output, dims_of, gpu_compress, gpu_decode, oracle_compress, shape_of
 from long_context_chunk_amd import hils
-from test_gpu_parity import DECODE_FUSED, DECODE_SMALL, DECODE_WINDOW, TIE_DECODE, _assert_tie_rows, _twin_inputs
+from test_gpu_parity import DECODE_FUSED, DECODE_LONG, DECODE_SMALL, DECODE_WINDOW, TIE_DECODE, _assert_tie_rows, _twin_inputs
 
 pytestmark = pytest.mark.gpu
 
@@ -113,7 +113,7 @@ def test_mirror_rows(name, w):
     assert np.array_equal(kcm.cpu().numpy(), m)
 
 
-MIRROR_DECODE = DECODE_SMALL + DECODE_WINDOW + DECODE_FUSED + [
+MIRROR_DECODE = DECODE_SMALL + DECODE_WINDOW + DECODE_FUSED + DECODE_LONG + [
     ("bf16_d128_shared_lmk_qcal", synth.Workload("mir_shl", B=3, Hq=8, Hkv=2, d=128, N=4096, K=16, decode=True,
                                                  seq_lens=[4096, 2222, 65], qcal_rank=8, Hlmk=2, needle_frac=0.05)),
     # three splits of 1024 chunks, K = 32

@@ -243,6 +243,21 @@ def test_decode_fused_attention(name, w):
     test_decode(name, w)
 
 
+# caches of more than 16384 chunks (over 1M tokens): more than 16 scan splits per (b, h)
+DECODE_LONG = [
+    ("bf16_d64_1.2M", synth.Workload("declong_a", B=1, Hq=2, Hkv=1, d=64, N=1200000, K=16, decode=True,
+                                     seq_lens=[1200000], needle_frac=0.002)),
+    ("bf16_d128_K48_1.1M", synth.Workload("declong_b", B=1, Hq=2, Hkv=1, d=128, N=1100000, K=48, decode=True,
+                                          seq_lens=[1048700], needle_frac=0.002, qcal_rank=8)),
+]
+
+
+@pytest.mark.timeout(300)
+@pytest.mark.parametrize("name,w", DECODE_LONG, ids=[n for n, _ in DECODE_LONG])
+def test_decode_beyond_16384_chunks(name, w):
+    test_decode(name, w)
+
+
 def test_decode_matches_prefill_row():
     """A decode step at cache length L reproduces prefill row L-1 (same kernels' inputs)."""
     L = 1000
