@@ -191,3 +191,23 @@ def test_decode_mirror_sequences_below_one_chunk():
     b = gpu_decode(w, x, kc=a["kc"], bc=a["bc"], mirror=True)
     _assert_same_step(a, b, "short")
     _check_against_oracle(w, x, b, "mirror short")
+
+
+def test_decode_mirror_timed_matches_untimed():
+    """hils_attn_decode_mirror_timed: the same result, and a positive time per stage."""
+    w = synth.Workload("mir_timed", B=8, Hq=32, Hkv=8, d=128, N=4096, K=16, decode=True,
+                       seq_lens=[4096, 3000, 65, 1, 2048, 4095, 100, 700], needle_frac=0.05)
+    x = synth.make_inputs(w, SEED + 3)
+    a = gpu_decode(w, x, mirror=True)
+    dm = dims_of(w)
+    q = torch.from_numpy(x["q"].view(np.int16)).cuda().view(torch.bfloat16)
+    k = torch.from_numpy(x["k"].view(np.int16)).cuda().view(torch.bfloat16)
+    v = torch.from_numpy(x["v"].view(np.int16)).cuda().view(torch.bfloat16)
+    lens = torch.from_numpy(x["seq_lens"]).cuda()
+    o = torch.empty_like(q)
+    sel = torch.empty((w.B, w.Hq, w.K), dtype=torch.int32, device="cuda")
+    ws = hils.workspace(dm, hils.OP_DECODE_MIRROR)
+    ms = hils.attn_decode(dm, q, k, v, lens, a["kc"], a["bc"], o, ws, sel_idx=sel, timed=True, kc_mirror=a["kcm"])
+    assert set(ms) == set(hils.DECODE_STAGES) and all(t_ > 0 for t_ in ms.values()), ms
+    np.testing.assert_array_equal(sel.cpu().numpy(), a["sel_idx"])
+    np.testing.assert_array_equal(o.view(torch.int16).cpu().numpy(), a["o_bits"])
