@@ -40,8 +40,9 @@ constexpr int AT_ROWS = 128;        // gathered rows per chunk_attend tile (4 wa
 constexpr int AT_TILES = 8;         // tiles per chunk_attend work item (one K/V staging)
 constexpr int ITEM_ROWS = AT_ROWS * AT_TILES;
 static_assert(ITEM_ROWS == BUCKET_ITEM_ROWS, "one work-item size for every user of the bucketing");
-constexpr int HIST_SLICE = 1 << 17; // selection entries per bucket_count / bucket_part1 workgroup
-constexpr int P2_SPLIT = 4;         // workgroups sharing one 64-chunk range in bucket_part2
+constexpr int HIST_SLICE = 1 << 17; // largest slice of selection entries per bucket_count / bucket_part1 workgroup
+constexpr int P2_SPLIT = 4;         // fewest workgroups sharing one 64-chunk range in bucket_part2
+constexpr int BK_FILL = 512;        // workgroups the bucketing passes aim for (two per CU)
 constexpr int BK_TILE = 8192;       // entries sorted in LDS at a time by bucket_part1/2
 constexpr int BK_PER = BK_TILE / 256;
 constexpr int FINE_BITS = 6;        // chunks per first-pass range: 64
@@ -93,12 +94,12 @@ __global__ void __launch_bounds__(256) zero_u32(uint32_t* p, int64_t n) {
 // Buckets are (b, h, chunk), numbered head-major; the selection entries of one
 // (b, h) group (all rows, all K slots) are contiguous in sel_idx.
 __global__ void __launch_bounds__(256) bucket_count(const int32_t* __restrict__ sel, uint32_t* __restrict__ counts,
-                                                    int64_t group_len, int slices_per_group, int C) {
+                                                    int64_t group_len, int64_t slice, int slices_per_group, int C) {
   __shared__ uint32_t hist[MAX_C];
   const int grp = blockIdx.x / slices_per_group, sl = blockIdx.x % slices_per_group;
   for (int i = threadIdx.x; i < C; i += 256) hist[i] = 0;
   __syncthreads();
-  const int64_t beg = (int64_t)sl * HIST_SLICE, end = min(group_len, beg + HIST_SLICE);
+  const int64_t beg = (int64_t)sl * slice, end = min(group_len, beg + slice);
   const int32_t* s = sel + (int64_t)grp * group_len;
   for (int64_t t0 = beg; t0 < end; t0 += BK_TILE) {
     int32_t c[BK_PER];  // every load of the tile in flight at once
@@ -310,13 +311,14 @@ HILS_DEV uint32_t block_exscan256(uint32_t v, uint32_t& excl, uint32_t* wsum) {
 // in-group entry index.
 __global__ void __launch_bounds__(256) bucket_part1(const int32_t* __restrict__ sel, const uint32_t* __restrict__ boff,
                                                     uint32_t* __restrict__ rcur, uint32_t* __restrict__ tmp,
-                                                    int64_t group_len, int slices_per_group, int C, int nrg) {
+                                                    int64_t group_len, int64_t slice, int slices_per_group, int C,
+                                                    int nrg) {
   __shared__ uint32_t skey[BK_TILE];
   __shared__ uint8_t srg[BK_TILE];
   __shared__ uint32_t hist[256], loff[256], gpos[256], wsum[4];
   const int grp = blockIdx.x / slices_per_group, sl = blockIdx.x % slices_per_group;
   const int t = threadIdx.x;
-  const int64_t beg = (int64_t)sl * HIST_SLICE, end = min(group_len, beg + HIST_SLICE);
+  const int64_t beg = (int64_t)sl * slice, end = min(group_len, beg + slice);
   const int32_t* s = sel + (int64_t)grp * group_len;
   for (int64_t t0 = beg; t0 < end; t0 += BK_TILE) {
     hist[t] = 0;
@@ -360,17 +362,17 @@ __global__ void __launch_bounds__(256) bucket_part1(const int32_t* __restrict__ 
   }
 }
 
-// Second pass: P2_SPLIT workgroups per (group, 64-chunk range) sort the range's region by
+// Second pass: `split` workgroups per (group, 64-chunk range) sort the range's region by
 // chunk, LDS tile by LDS tile (tiles dealt round-robin), reserving each chunk's run with
 // one atomic per (tile, chunk) on that bucket's cursor.
 __global__ void __launch_bounds__(256) bucket_part2(const uint32_t* __restrict__ tmp, const uint32_t* __restrict__ boff,
                                                     uint32_t* __restrict__ fcur, uint32_t* __restrict__ pairs,
-                                                    int64_t group_len, int C, int nrg) {
+                                                    int64_t group_len, int C, int nrg, int split) {
   constexpr int NF = 1 << FINE_BITS;
   __shared__ uint32_t skey[BK_TILE];
   __shared__ uint8_t sfb[BK_TILE];
   __shared__ uint32_t hist[NF], loff[NF], gpos[NF];
-  const int sp = blockIdx.x % P2_SPLIT, gr = blockIdx.x / P2_SPLIT;
+  const int sp = blockIdx.x % split, gr = blockIdx.x / split;
   const int grp = gr / nrg, rg = gr % nrg;
   const int t = threadIdx.x, lane = t & 63;
   const int c0 = rg << FINE_BITS;
@@ -378,7 +380,7 @@ __global__ void __launch_bounds__(256) bucket_part2(const uint32_t* __restrict__
   const int64_t bk0 = (int64_t)grp * C + c0;
   const uint32_t R0 = boff[bk0], R1 = boff[bk0 + nf];
   const uint32_t ebase = (uint32_t)(grp * group_len);
-  for (uint32_t t0 = R0 + (uint32_t)sp * BK_TILE; t0 < R1; t0 += (uint32_t)P2_SPLIT * BK_TILE) {
+  for (uint32_t t0 = R0 + (uint32_t)sp * BK_TILE; t0 < R1; t0 += (uint32_t)split * BK_TILE) {
     if (t < NF) hist[t] = 0;
     __syncthreads();
     uint32_t key[BK_PER], rk[BK_PER];
@@ -866,9 +868,14 @@ void launch_bucket_pairs(const Geom& g, const int32_t* sel, BucketBufs bb, hipSt
                        bb.counts, nz);
   if (nbk == 0) return;
   const int64_t group_len = (int64_t)g.N * g.K;
-  const int spg = (int)((group_len + HIST_SLICE - 1) / HIST_SLICE);
   const int ngrp = g.B * g.Hq;
-  hipLaunchKernelGGL(bucket_count, dim3(ngrp * spg), dim3(256), 0, st, sel, bb.counts, group_len, spg, C);
+  // slices of whole LDS tiles, at most HIST_SLICE entries, small enough that the passes
+  // over them fill the chip when the groups are few (short sequences)
+  const int64_t want = (BK_FILL + ngrp - 1) / ngrp;
+  const int64_t slice =
+      std::min<int64_t>(HIST_SLICE, std::max<int64_t>(BK_TILE, ((group_len + want - 1) / want + BK_TILE - 1) / BK_TILE * BK_TILE));
+  const int spg = (int)((group_len + slice - 1) / slice);
+  hipLaunchKernelGGL(bucket_count, dim3(ngrp * spg), dim3(256), 0, st, sel, bb.counts, group_len, slice, spg, C);
   if (nbk <= 16 * 1024) {  // one workgroup scans up to 16K buckets quickly
     hipLaunchKernelGGL(bucket_scan, dim3(1), dim3(1024), 0, st, bb.counts, bb.boff, bb.toff, nbk);
   } else {
@@ -882,9 +889,10 @@ void launch_bucket_pairs(const Geom& g, const int32_t* sel, BucketBufs bb, hipSt
                      nbk);
   const int nrg = (C + (1 << FINE_BITS) - 1) >> FINE_BITS;
   hipLaunchKernelGGL(bucket_part1, dim3(ngrp * spg), dim3(256), 0, st, sel, bb.boff, bb.cursor, bb.tmp, group_len,
-                     spg, C, nrg);
-  hipLaunchKernelGGL(bucket_part2, dim3(ngrp * nrg * P2_SPLIT), dim3(256), 0, st, (const uint32_t*)bb.tmp, bb.boff,
-                     bb.counts, bb.pairs, group_len, C, nrg);
+                     slice, spg, C, nrg);
+  const int split = std::min(64, std::max(P2_SPLIT, (BK_FILL + ngrp * nrg - 1) / (ngrp * nrg)));
+  hipLaunchKernelGGL(bucket_part2, dim3(ngrp * nrg * split), dim3(256), 0, st, (const uint32_t*)bb.tmp, bb.boff,
+                     bb.counts, bb.pairs, group_len, C, nrg, split);
 }
 
 int64_t bucket_items_bound(const Geom& g) {
