@@ -46,12 +46,10 @@
  *       sel_idx    [B, Hq, N, K] int32  selected chunk ids (decode: [B, Hq, K])
  *       sel_score  [B, Hq, N, K] fp32   their scores s_ic
  *     Query head h uses KV head h / (Hq / Hkv) and landmark head h / (Hq / Hlmk).
- *   - Selection lists are in rank order: best score first, equal scores by
- *     ascending chunk id.  Rows with fewer than K past chunks select all of them
- *     and pad with id -1 and score -inf.  (The fusion does not depend on the order;
- *     rank order is what the selection produces and keeps the ranking, so a caller
- *     can take the best k <= K of a list without re-sorting.  Sorting a list's valid
- *     ids gives the ascending form.)
+ *   - A selection list holds a row's K best chunks (of equal scores the lower chunk
+ *     id is kept) in ascending chunk id order; sel_score holds the score of the
+ *     chunk in the same slot.  Rows with fewer than K past chunks select all of
+ *     them and pad with id -1 and score -inf after them.
  *   - q, k, v, o, lmk_q, qcal_D, qcal_U all have the element type `io`;
  *     kc, bc and sel_score are always fp32.
  */
@@ -127,7 +125,7 @@ int hils_landmark_compress(const hils_dims_t* dims, const void* k, const void* l
  * ([B,Hlmk,floor(N/S),d] / [B,Hlmk,floor(N/S)], N = dims.N) with
  * s_ic = q^_i . kc[c] / sqrt(d) + bc[c], q^ = q + U_h (D_h q) when qcal_rank > 0
  * (qcal_D/qcal_U may be NULL only if qcal_rank == 0), and keeps the K best.
- * Writes sel_idx and sel_score [B,Hq,Nq,K] (rank order, padded).  0 <= Nq <= N;
+ * Writes sel_idx and sel_score [B,Hq,Nq,K] (ascending ids, padded).  0 <= Nq <= N;
  * Nq == 0 does nothing (the arrays may then be NULL).  Needs a workspace of
  * hils_workspace_bytes(dims, HILS_OP_SCORE_TOPK) bytes (sized for Nq = N).
  */

@@ -24,8 +24,6 @@
 #include "kernels.h"
 #include <atomic>
 #include <type_traits>
-#include <atomic>
-#include <type_traits>
 
 namespace hils {
 
@@ -310,12 +308,37 @@ __global__ void __launch_bounds__(256) decode_scan(const IO* __restrict__ q, con
   }
 }
 
+// The caller's copy of a (b, h)'s selection: the chunk ids of the first min(K, n) ranks of
+// the sorted 64-list (hi, lo) of half 0 (ranks 0..31, 32..63) in ascending order, -1 after
+// them.  Called by all 64 lanes of one wave; half 0 writes.
+HILS_DEV void write_sel_ascending(uint64_t hi, uint64_t lo, int K, int n, int lane, int32_t* __restrict__ sel) {
+  const int j = lane & 31, m = min(K, n);
+  // float keys in [1, 2) whose bits hold 0xffff - chunk (chunk < 65536): larger for a lower
+  // chunk; 0 for no chunk, which sorts last
+  auto fkey = [](uint64_t k) { return __uint_as_float(0x3f800000u | ((0xffffu - (uint32_t)key_chunk(k)) << 7)); };
+  auto chunk = [](float f) { return f != 0.f ? (int32_t)(0xffffu - ((__float_as_uint(f) >> 7) & 0xffffu)) : -1; };
+  float a = j < m && hi ? fkey(hi) : 0.f;
+  float b = 32 + j < m && lo ? fkey(lo) : 0.f;
+  float pinf = INFINITY, ninf = -INFINITY;
+  asm volatile("" : "+v"(pinf));
+  asm volatile("" : "+v"(ninf));
+  kl::sortf(a, j, pinf, ninf);
+  if (m > 32) {
+    kl::sortf(b, j, pinf, ninf);
+    kl::splitf(a, b, j, pinf, ninf);
+  }
+  if (lane < 32) {
+    if (j < K) sel[j] = chunk(a);
+    if (32 + j < K) sel[32 + j] = chunk(b);
+  }
+}
+
 // exact top-K of one (b, h) from the sorted candidate lists of its splits (cb: the first
 // list), rank order, ties to the lowest id; n = min(K, candidate chunks).  Every thread of
 // the block calls it (it has a block-wide barrier); the first four waves do the work:
 // half-wave x of wave w takes lists 2w + x, 2w + x + 8, 2w + x + 16, ..., the halves of each
 // wave merge, then wave 0 merges the four wave lists and writes ranks < K to out_i / out_s
-// (and sel_user when given): chunk ids, -1 past n.
+// (chunk ids, -1 past n), and sel_user when given (the same ids in ascending order).
 template <bool KB>
 HILS_DEV void merge_splits(const uint64_t* __restrict__ cb, int nsplit, int K, int n, uint64_t (*wl)[64],
                            int32_t* out_i, float* out_s, int32_t* __restrict__ sel_user) {
@@ -362,11 +385,10 @@ HILS_DEV void merge_splits(const uint64_t* __restrict__ cb, int nsplit, int K, i
   const uint64_t lk = lane < 32 ? hi : lo0;
   if (lane < K) {
     const bool ok = lane < n && lk != 0;
-    const int32_t ci = ok ? key_chunk(lk) : -1;
-    out_i[lane] = ci;
+    out_i[lane] = ok ? key_chunk(lk) : -1;
     out_s[lane] = ok ? key_score(lk) : -INFINITY;
-    if (sel_user) sel_user[lane] = ci;
   }
+  if (sel_user) write_sel_ascending(hi, lo0, K, n, lane, sel_user);
 }
 
 template <bool KB>
@@ -597,13 +619,14 @@ HILS_DEV void mirror_select(const IO* __restrict__ qv, const IO* __restrict__ Dw
     }
     __syncthreads();
   }
-  if (w == 0 && lane < K) {
-    const uint64_t lk = sm.run[lane];
-    const bool ok = lane < n && lk != 0;
-    const int32_t ci = ok ? key_chunk(lk) : -1;
-    out_i[lane] = ci;
-    out_s[lane] = ok ? key_score(lk) : -INFINITY;
-    if (sel_user) sel_user[lane] = ci;
+  if (w == 0) {
+    if (lane < K) {
+      const uint64_t lk = sm.run[lane];
+      const bool ok = lane < n && lk != 0;
+      out_i[lane] = ok ? key_chunk(lk) : -1;
+      out_s[lane] = ok ? key_score(lk) : -INFINITY;
+    }
+    if (sel_user) write_sel_ascending(sm.run[j], sm.run[32 + j], K, n, lane, sel_user);
   }
 }
 

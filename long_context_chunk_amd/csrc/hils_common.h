@@ -192,6 +192,10 @@ HILS_DEV uint64_t make_key(float s, int c) {
 }
 HILS_DEV float key_score(uint64_t k) { return unorder_f32((uint32_t)(k >> 32)); }
 HILS_DEV int key_chunk(uint64_t k) { return (int)(0xffffffffu - (uint32_t)k); }
+// the key with its halves swapped: larger = lower chunk id, whatever the scores (the
+// empty key stays 0); applied twice it gives the key back.  Sorting swapped keys best
+// first orders a list by ascending chunk id.
+HILS_DEV uint64_t key_by_id(uint64_t k) { return (k << 32) | (k >> 32); }
 
 // ------------------------------------------------------------- XCD-aware ordering
 // MI355X dispatches consecutive workgroup ids round-robin over its 8 XCDs (each

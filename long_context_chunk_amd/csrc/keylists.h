@@ -90,6 +90,45 @@ HILS_DEV void merge64(uint64_t& hi, uint64_t& lo, uint64_t hi2, uint64_t lo2, in
   top(hi2, lo2, j);
   lo = hi2;
 }
+// the first m (m <= 64) keys of the sorted 64-list (hi, lo) of this lane's half, reordered
+// by ascending chunk id (hi holds positions 0..31, lo 32..63), zero keys after them
+HILS_DEV void ids_ascending(uint64_t& hi, uint64_t& lo, int m, int j) {
+  hi = j < m ? key_by_id(hi) : 0ull;
+  lo = 32 + j < m ? key_by_id(lo) : 0ull;
+  sort(hi, j);
+  sort(lo, j);
+  split(hi, lo, j);
+  hi = key_by_id(hi);
+  lo = key_by_id(lo);
+}
+// The same networks on float keys with v_med3_f32: bnd = pinf keeps the larger of a pair,
+// ninf the smaller (+-inf hidden from the compiler, so that the med3s stay med3s).
+template <int X>
+HILS_DEV void cxf(float& k, int j, float bnd) {
+  k = __builtin_amdgcn_fmed3f(k, __uint_as_float(x32<X>(__float_as_uint(k), j)), bnd);
+}
+// bitonic sort, largest first
+HILS_DEV void sortf(float& k, int j, float pinf, float ninf) {
+#define HILS_KL_STAGE(K_, X_) cxf<X_>(k, j, (((j & X_) == 0) == (((j & K_) == 0) || K_ == 32)) ? pinf : ninf);
+  HILS_KL_STAGE(2, 1)
+  HILS_KL_STAGE(4, 2) HILS_KL_STAGE(4, 1)
+  HILS_KL_STAGE(8, 4) HILS_KL_STAGE(8, 2) HILS_KL_STAGE(8, 1)
+  HILS_KL_STAGE(16, 8) HILS_KL_STAGE(16, 4) HILS_KL_STAGE(16, 2) HILS_KL_STAGE(16, 1)
+  HILS_KL_STAGE(32, 16) HILS_KL_STAGE(32, 8) HILS_KL_STAGE(32, 4) HILS_KL_STAGE(32, 2) HILS_KL_STAGE(32, 1)
+#undef HILS_KL_STAGE
+}
+// a, b sorted -> a = the largest 32 of both, b = the other 32, both sorted
+HILS_DEV void splitf(float& a, float& b, int j, float pinf, float ninf) {
+  const float r = __uint_as_float(x32<31>(__float_as_uint(b), j));
+  b = __builtin_amdgcn_fmed3f(a, r, ninf);
+  a = __builtin_amdgcn_fmed3f(a, r, pinf);
+#define HILS_KL_CLEAN(X_)                                  \
+  cxf<X_>(a, j, (j & X_) == 0 ? pinf : ninf); \
+  cxf<X_>(b, j, (j & X_) == 0 ? pinf : ninf);
+  HILS_KL_CLEAN(16) HILS_KL_CLEAN(8) HILS_KL_CLEAN(4) HILS_KL_CLEAN(2) HILS_KL_CLEAN(1)
+#undef HILS_KL_CLEAN
+}
+
 // key of rank p (p < 64) of the 64-list (hi, lo) of this lane's half
 HILS_DEV uint64_t rank_key(uint64_t hi, uint64_t lo, int p, int lane) {
   const int src = (lane & 32) + (p & 31);

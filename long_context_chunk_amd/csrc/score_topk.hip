@@ -827,11 +827,15 @@ __global__ void __launch_bounds__(256, KB ? 1 : 2) score_topk_kernel(const IO* _
     acc = an;
   }
 
-  // ---- final selection and output, rank order.  K <= 32: eight row pairs (p, p + 16) at
-  // a time, the two half lists of a row sorted as keys and merged to the best 32; lane j of
-  // each half writes slot j.  KB: one row pair at a time as 64-lists.
+  // ---- final selection and output in ascending chunk id order.  K <= 32: eight row pairs
+  // (p, p + 16) at a time, the two half lists of a row sorted as keys and merged to the best
+  // 32, the best K sorted again by chunk id; lane j of each half writes slot j.  KB: one row
+  // pair at a time as 64-lists.
   if constexpr (!KB) {
     constexpr int FR = NQ * NK > 4 ? 4 : 8;  // fewer at once where the score operands take more registers
+    float pinf = INFINITY, ninf = -INFINITY;  // hidden from the compiler: the sort's med3s stay med3s
+    asm volatile("" : "+v"(pinf));
+    asm volatile("" : "+v"(ninf));
 #pragma unroll 1
     for (int p0r = 0; p0r < 16; p0r += FR) {
       uint64_t x[FR], y[FR];
@@ -850,19 +854,33 @@ __global__ void __launch_bounds__(256, KB ? 1 : 2) score_topk_kernel(const IO* _
         const uint64_t rk = xl64<31>(y[i]);
         x[i] = rk > x[i] ? rk : x[i];
       }
-      cxk_r<16, FR>(x, (n & 16) == 0);
-      cxk_r<8, FR>(x, (n & 8) == 0);
-      cxk_r<4, FR>(x, (n & 4) == 0);
-      cxk_r<2, FR>(x, (n & 2) == 0);
-      cxk_r<1, FR>(x, (n & 1) == 0);
+      if (K < 32) {  // the ranks matter only when fewer than 32 are kept
+        cxk_r<16, FR>(x, (n & 16) == 0);
+        cxk_r<8, FR>(x, (n & 8) == 0);
+        cxk_r<4, FR>(x, (n & 4) == 0);
+        cxk_r<2, FR>(x, (n & 2) == 0);
+        cxk_r<1, FR>(x, (n & 1) == 0);
+      }
+      // the kept keys in ascending chunk order: float keys in [1, 2) whose bits hold
+      // (0x3fff - chunk, lane), larger for a lower chunk (chunk < 16384), 0 for none;
+      // after a descending sort lane j takes the score from the lane its key names
+      float fk[FR];
+#pragma unroll
+      for (int i = 0; i < FR; ++i)
+        fk[i] = x[i] != 0 && n < K
+                    ? __uint_as_float(0x3f800000u | ((0x3fffu - (uint32_t)key_chunk(x[i])) << 5) | (uint32_t)n)
+                    : 0.f;
+      sort32f_r<FR>(fk, n, pinf, ninf);
 #pragma unroll
       for (int i = 0; i < FR; ++i) {
+        const uint32_t fb = __float_as_uint(fk[i]);
+        const float sc = __shfl(key_score(x[i]), (lane & 32) | (int)(fb & 31u));
         const int rw = r0 + 32 * w + (hf ? p0r + i + 16 : p0r + i);
         if (rw < N && n < K) {
           const int64_t o = ((int64_t)bh * N + rw) * K + n;
-          const bool ok = x[i] != 0;
-          sel_idx[o] = ok ? key_chunk(x[i]) : -1;
-          sel_score[o] = ok ? key_score(x[i]) : -INFINITY;
+          const bool ok = fb != 0;
+          sel_idx[o] = ok ? (int)(0x3fffu - ((fb >> 5) & 0x3fffu)) : -1;
+          sel_score[o] = ok ? sc : -INFINITY;
         }
       }
     }
@@ -871,6 +889,7 @@ __global__ void __launch_bounds__(256, KB ? 1 : 2) score_topk_kernel(const IO* _
     for (int p = 0; p < 16; ++p) {
       uint64_t x, y;
       row_list(hf ? p + 16 : p, x, y);
+      kl::ids_ascending(x, y, K, n);
       const int rw = r0 + 32 * w + (hf ? p + 16 : p);
       auto out = [&](int rank, uint64_t kk) {
         if (rw < N && rank < K) {

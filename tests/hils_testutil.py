@@ -87,10 +87,18 @@ def oracle_rows(w, x, kc, bc, rows):
     return oracle.prefill_rows(shape_of(w), x["q"], x["k"], x["v"], kc, bc, rows, D=x.get("D"), U=x.get("U"))
 
 
+def assert_ascending(sel, valid, label=""):
+    """Valid ids (a prefix of each row) strictly ascending."""
+    sel = np.asarray(sel)
+    both = np.asarray(valid)[..., 1:]
+    assert np.all(sel[..., 1:][both] > sel[..., :-1][both]), "%s: selected ids not in ascending order" % label
+
+
 def check_selection_and_output(w, x, kc_o, bc_o, rows, ref, gpu_sel, gpu_score, gpu_o, label=""):
     """Compare the GPU's selection/output on `rows` with the oracle result `ref`.
 
-    gpu_sel / gpu_score: [n, K] in rank order; gpu_o: [n, d] (fp32 view of the io output).
+    gpu_sel / gpu_score: [n, K], ascending chunk ids then padding; gpu_o: [n, d] (fp32 view
+    of the io output).
     Rows whose gap exceeds GAP are checked together (array operations); near-tie rows one
     by one against the oracle's full score list.  Returns a summary dict.
     """
@@ -107,6 +115,7 @@ def check_selection_and_output(w, x, kc_o, bc_o, rows, ref, gpu_sel, gpu_score, 
     assert np.array_equal(valid, slot < ns[:, None]), "%s: padding is not at the end" % label
     srt = np.sort(np.where(valid, gpu_sel, -1 - slot), axis=1)
     assert np.all(np.diff(srt, axis=1) != 0), "%s: duplicate chunk ids in a row" % label
+    assert_ascending(gpu_sel, valid, label)
     o_sel = np.where(slot < ns[:, None], np.asarray(ref["sel_idx"]), -1 - slot)
     exact = np.asarray(ref["gap"]) > GAP
     same = np.all(np.sort(o_sel, axis=1) == srt, axis=1)
@@ -117,10 +126,9 @@ def check_selection_and_output(w, x, kc_o, bc_o, rows, ref, gpu_sel, gpu_score, 
             label, bad.size, rows[t], ref["gap"][t], srt[t][srt[t] >= 0], np.sort(o_sel[t][o_sel[t] >= 0])))
     diffs = np.zeros((n, w.d))
     diffs[exact] = gpu_o[exact] - np.asarray(ref["o"])[exact]
-    if gpu_score is not None and exact.any():  # rank order and scores of the exact rows
+    if gpu_score is not None and exact.any():  # scores of the exact rows, slot by slot (both lists ascending)
         gs = np.asarray(gpu_score).reshape(n, K)[exact]
         rs = np.where(slot < ns[:, None], np.asarray(ref["sel_score"]), -np.inf)[exact]
-        rs = -np.sort(-rs, axis=1)
         live = (slot < ns[exact][:, None])
         assert np.all(np.isfinite(gs[live])), "%s: non-finite selected score" % label
         err = np.abs(gs[live] - rs[live])
@@ -151,8 +159,8 @@ def check_selection_and_output(w, x, kc_o, bc_o, rows, ref, gpu_sel, gpu_score, 
 
 
 def check_selection(w, x, kc_o, bc_o, rows, ref, gpu_sel, gpu_score, label=""):
-    """Selection only (no output): bit-exact sets where the gap exceeds GAP, rank-ordered
-    scores within 2e-5 there, valid top-K sets within GAP on near-tie rows."""
+    """Selection only (no output): bit-exact sets where the gap exceeds GAP, ids ascending,
+    scores within 2e-5 there slot by slot, valid top-K sets within GAP on near-tie rows."""
     s = shape_of(w)
     n, K = len(rows), w.K
     gpu_sel = np.asarray(gpu_sel).reshape(n, K)
@@ -164,11 +172,12 @@ def check_selection(w, x, kc_o, bc_o, rows, ref, gpu_sel, gpu_score, label=""):
     assert np.all(np.isneginf(gpu_score[~valid])) and np.all(np.isfinite(gpu_score[valid]))
     srt = np.sort(np.where(valid, gpu_sel, -1 - slot), axis=1)
     assert np.all(np.diff(srt, axis=1) != 0), "%s: duplicate chunk ids" % label
+    assert_ascending(gpu_sel, valid, label)
     o_sel = np.sort(np.where(slot < ns[:, None], np.asarray(ref["sel_idx"]), -1 - slot), axis=1)
     exact = np.asarray(ref["gap"]) > GAP
     bad = np.flatnonzero(exact & ~np.all(srt == o_sel, axis=1))
     assert bad.size == 0, "%s: %d rows select different chunks (first %s)" % (label, bad.size, rows[int(bad[0])])
-    rs = -np.sort(-np.where(slot < ns[:, None], np.asarray(ref["sel_score"]), -np.inf), axis=1)
+    rs = np.where(slot < ns[:, None], np.asarray(ref["sel_score"]), -np.inf)  # both lists ascending
     live = valid & exact[:, None]
     if live.any():
         err = np.abs(gpu_score[live] - rs[live])

@@ -41,8 +41,8 @@ def _run_prefill(w, x):
 
 
 def _selection_properties(w, sel, scr):
-    """Every row: exactly min(K, P_i) distinct ids, all < P_i, padded with -1/-inf, the
-    selected scores finite and non-increasing (rank order)."""
+    """Every row: exactly min(K, P_i) distinct ids in ascending order, all < P_i, padded
+    with -1/-inf, the selected scores finite."""
     s = sel.cpu().numpy().reshape(-1, w.N, w.K)
     sc = scr.cpu().numpy().reshape(-1, w.N, w.K)
     P = np.minimum(np.arange(w.N) // w.S, w.C)
@@ -57,7 +57,7 @@ def _selection_properties(w, sel, scr):
     assert np.all(np.isneginf(sc[~valid]))
     assert np.all(np.isfinite(sc[valid])), "a selected chunk has a non-finite score"
     both = valid[..., 1:]          # consecutive valid slots (valid slots form a prefix)
-    assert np.all(sc[..., 1:][both] <= sc[..., :-1][both]), "scores not in rank order"
+    assert np.all(s[..., 1:][both] > s[..., :-1][both]), "ids not in ascending order"
 
 
 # rows checked against the oracle: every row of the first and the last head, plus sampled
