@@ -92,7 +92,7 @@ typedef struct {
                      /* heads); the backward pass needs Hlmk == Hq                      */
   int32_t d;         /* head dimension: 64 or 128                                      */
   int32_t S;         /* chunk size: 64                                                 */
-  int32_t K;         /* top-K chunks per query: 1 <= K <= 64 (the backward: K <= 32)    */
+  int32_t K;         /* top-K chunks per query: 1 <= K <= 64                            */
   int32_t N;         /* prefill: tokens; decode: KV-cache capacity (row stride of k/v) */
   int32_t qcal_rank; /* Q-Cal rank r, 0 <= r <= 32 (0: no Q-Cal, q^ = q)                */
   int32_t io;        /* hils_dtype_t of q, k, v, o, lmk_q, qcal_D, qcal_U              */

@@ -464,7 +464,8 @@ __global__ void __launch_bounds__(BP_THREADS) bwd_pairs(const bf16_t* __restrict
   const char* g_head = reinterpret_cast<const char*>(dO + bhq * N * D);
   const uint32_t e_head = (uint32_t)(bhq * N * K);
   // in-head row = index / K as (index * (floor(2^32 / K) + 1)) >> 32: exact for
-  // index < 2^26 and K <= 32 (the multiplier's excess adds less than 2^-6 to index / K)
+  // index < 2^26 and K <= 64 (the multiplier's excess adds less than 2^-6 <= 1/K to
+  // index / K, whose fraction is at most 1 - 1/K)
   const uint64_t kmul = 0x100000000ull / (uint32_t)K + 1u;
   auto row_of = [&](uint32_t x) { return (uint32_t)(((uint64_t)x * kmul) >> 32); };
   for (int x = tid; x < BUCKET_ITEM_ROWS; x += BP_THREADS) ipid[x] = (uint32_t)x < nrows ? pp[x] - e_head : 0u;
@@ -977,8 +978,11 @@ hipError_t launch_bwd_d(const Geom& g, const BwdArgs& a, char* ws, hipStream_t s
     else if (g.K <= 16)
       hipLaunchKernelGGL((bwd_dq_sum<D, 16>), grid, dim3(256), 0, st, a.sel_idx, dqp, (const float*)dq,
                          (bf16_t*)a.dq, g.K, rows);
-    else
+    else if (g.K <= 32)
       hipLaunchKernelGGL((bwd_dq_sum<D, 32>), grid, dim3(256), 0, st, a.sel_idx, dqp, (const float*)dq,
+                         (bf16_t*)a.dq, g.K, rows);
+    else
+      hipLaunchKernelGGL((bwd_dq_sum<D, 64>), grid, dim3(256), 0, st, a.sel_idx, dqp, (const float*)dq,
                          (bf16_t*)a.dq, g.K, rows);
   }
   if (g.r > 0) {

@@ -222,16 +222,20 @@ def test_landmark_heads_per_kv_group_accepted_backward_rejects():
 
 
 def test_k_above_32_limits():
-    """K up to 64 is valid for the forward calls; prefill also needs N*K < 2^26 (its
-    bucketing keys), and the backward pass keeps K <= 32; both say so before touching
-    the device."""
+    """K up to 64 is valid for every call, the backward pass included (it gets as far as
+    the workspace check, with no workspace given); prefill also needs N*K < 2^26 (its
+    bucketing keys) and says so before touching the device."""
     lib = hils.load()
     d = hils.dims(1, 16, 4, 64, 4096, 64)
     assert hils.workspace_bytes(d, hils.OP_PREFILL) > 0
     assert hils.workspace_bytes(d, hils.OP_DECODE) > 0
+    assert hils.workspace_bytes(d, hils.OP_BACKWARD) > 0
     fake = ctypes.c_void_p(0x1000)
-    rc = lib.hils_attn_prefill_backward(ctypes.byref(d), *([fake] * 18), 1 << 40, None)
-    assert rc == hils.E_UNSUPPORTED and b"K <= 32" in lib.hils_last_error()
+    rc = lib.hils_attn_prefill_backward(ctypes.byref(d), *([fake] * 17), None, 0, None)
+    assert rc == hils.E_WORKSPACE, lib.hils_last_error()
+    d65 = hils.dims(1, 16, 4, 64, 4096, 65)
+    with pytest.raises(hils.HilsError):
+        hils.workspace_bytes(d65, hils.OP_BACKWARD)
     big = hils.dims(1, 1, 1, 64, 16384 * 64, 64)   # N*K = 2^26
     with pytest.raises(hils.HilsError):
         hils.workspace_bytes(big, hils.OP_PREFILL)

@@ -31,6 +31,7 @@ CASES = [
     ("d128_window512_K16", synth.Workload("bw_d", B=1, Hq=2, Hkv=1, d=128, N=1100, K=16, window=512)),
     ("one_chunk", synth.Workload("bw_e", B=1, Hq=2, Hkv=1, d=64, N=100, K=2)),
     ("no_complete_chunk", synth.Workload("bw_f", B=1, Hq=2, Hkv=2, d=128, N=40, K=2)),
+    ("d128_qcal_K48", synth.Workload("bw_g", B=1, Hq=2, Hkv=1, d=128, N=3500, K=48, qcal_rank=8)),
 ]
 
 
