@@ -477,9 +477,6 @@ int hils_attn_prefill_backward(const hils_dims_t* dims, const void* q, const voi
   if (rc) return rc;
   if ((rc = check_prefill(g))) return rc;
   if (g.io != HILS_BF16) return fail(HILS_E_UNSUPPORTED, "the backward pass needs bf16 I/O");
-  if (g.Hl != g.Hq)
-    return fail(HILS_E_UNSUPPORTED, "the backward pass needs one landmark head per query head (Hlmk=%d Hq=%d)", g.Hl,
-                g.Hq);
   if (!q || !k || !v || !o || !dO || !dq || !dk || !dv || !sel_idx || !sel_score)
     return fail(HILS_E_INVAL, "q, k, v, o, dO, dq, dk, dv, sel_idx and sel_score must be non-NULL");
   if (g.C() > 0 && (!lmk_q || !kc || !dlmk))

@@ -52,7 +52,7 @@ size_t alb(size_t x) { return (x + 255) / 256 * 256; }
 BwdWs bwd_ws(const Geom& g) {
   BwdWs w;
   const size_t rows = (size_t)g.B * g.Hq * g.N, kvrows = (size_t)g.B * g.Hkv * g.N;
-  const size_t lrows = (size_t)g.B * g.Hl * g.C(), nbk = (size_t)g.B * g.Hq * g.C();
+  const size_t nbk = (size_t)g.B * g.Hq * g.C();
   const size_t ent = rows * g.K, r = (size_t)g.r;
   size_t off = 0;
   auto take = [&](size_t& f, size_t bytes) {
@@ -62,14 +62,14 @@ BwdWs bwd_ws(const Geom& g) {
   take(w.dq, rows * g.d * 4);
   take(w.dk, kvrows * g.d * 4);  // dk .. dU are zeroed together: keep them contiguous
   take(w.dv, kvrows * g.d * 4);
-  take(w.dkc, lrows * g.d * 4);
-  take(w.dbc, lrows * 4);
+  take(w.dkc, nbk * g.d * 4);  // per query head: a shared landmark head sums its query heads' terms
+  take(w.dbc, nbk * 4);
   take(w.G, r > 0 ? (size_t)g.Hq * g.d * g.d * 4 : 0);  // G = tau sum_c k'_c S_c^T per head (S_c = sum dsigma q)
   take(w.lam, rows * 4);
   take(w.dd, rows * 4);
   take(w.dsig, ent * 4);
   take(w.dqp, ent * g.d * 2);  // per (row, slot) dq of the selected chunk's attention (bf16)
-  take(w.kdq, r > 0 ? lrows * g.d * 4 : 0);  // k'_c + D^T U^T k'_c per chunk (Q-Cal)
+  take(w.kdq, r > 0 ? nbk * g.d * 4 : 0);  // k'_c + D_h^T U_h^T k'_c per (query head, chunk) (Q-Cal)
   take(w.counts, nbk * 4);  // counts and cursor contiguous (zeroed together)
   take(w.cursor, nbk * 4);
   take(w.boff, (nbk + 1) * 4);
@@ -428,7 +428,7 @@ __global__ void __launch_bounds__(BP_THREADS) bwd_pairs(const bf16_t* __restrict
                                                         uint16_t* __restrict__ dqp, float* __restrict__ dk,
                                                         float* __restrict__ dv, float* __restrict__ dkc,
                                                         float* __restrict__ dbc, int Hq, int Hkv, int N, int C, int K,
-                                                        int nbk) {
+                                                        int nbk, int Hd) {
   constexpr int LDR = PairLds<D>::LDR;
   constexpr int LDK = KVTile<bf16_t, D, 1, 8>::LDK, LDV = KVTile<bf16_t, D, 1, 8>::LDV;
   constexpr int SEGS = D / 8;       // 16-byte segments of a bf16 row
@@ -469,7 +469,9 @@ __global__ void __launch_bounds__(BP_THREADS) bwd_pairs(const bf16_t* __restrict
   const uint64_t kmul = 0x100000000ull / (uint32_t)K + 1u;
   auto row_of = [&](uint32_t x) { return (uint32_t)(((uint64_t)x * kmul) >> 32); };
   for (int x = tid; x < BUCKET_ITEM_ROWS; x += BP_THREADS) ipid[x] = (uint32_t)x < nrows ? pp[x] - e_head : 0u;
-  if (tid < D) kdq_s[tid] = kdq[(bhq * C + c) * D + tid];  // landmark head = query head
+  // the chunk's score direction: kdq holds Hd heads, one per query head (Q-Cal) or the
+  // landmark heads (k' itself)
+  if (tid < D) kdq_s[tid] = kdq[(((bhq / Hq) * Hd + h / (Hq / Hd)) * C + c) * D + tid];
   const int ntile = (int)((nrows + BW_ROWS - 1) / BW_ROWS);
   __syncthreads();  // ipid
 
@@ -658,7 +660,7 @@ __global__ void __launch_bounds__(BP_THREADS) bwd_pairs(const bf16_t* __restrict
     for (int rr = 0; rr < 16; ++rr)
       atomicAdd(&dst[(kvrow0 + 32 * kt + acc_row(rr, hf)) * D + e], dkv[ib][rr] * scl);
   }
-  const int64_t ci = bhq * C + c;  // landmark head = query head
+  const int64_t ci = bhq * C + c;  // the chunk sums are kept per query head
   if (kq_wave) {
     // column 0 (lanes 0, 32) holds the high terms' sums, column 1 (lanes 1, 33) the low
 #pragma unroll
@@ -720,18 +722,19 @@ constexpr int KDQ_CHUNKS = 8;  // chunks per bwd_kdq workgroup
 
 template <int D>
 __global__ void __launch_bounds__(256) bwd_kdq(const float* __restrict__ kc, const bf16_t* __restrict__ Dw,
-                                               const bf16_t* __restrict__ Uw, float* __restrict__ kdq, int Hl,
-                                               int C, int r) {
+                                               const bf16_t* __restrict__ Uw, float* __restrict__ kdq, int Hq,
+                                               int Hl, int C, int r) {
   __shared__ float kr[D], t[32];
   const int nblk = (C + KDQ_CHUNKS - 1) / KDQ_CHUNKS;
-  const int64_t bh = blockIdx.x / nblk;  // b * Hl + h
-  const int h = (int)(bh % Hl);
+  const int64_t bh = blockIdx.x / nblk;  // b * Hq + h
+  const int h = (int)(bh % Hq);
+  const int64_t lb = bh / Hq * Hl + h / (Hq / Hl);  // b * Hl + the landmark head of h
   const int c0 = (int)(blockIdx.x % nblk) * KDQ_CHUNKS;
   const int tid = threadIdx.x;
   for (int c = c0; c < min(C, c0 + KDQ_CHUNKS); ++c) {
     const int64_t row = (bh * C + c) * D;
     __syncthreads();  // the previous chunk's kr / t consumed
-    if (tid < D) kr[tid] = kc[row + tid];
+    if (tid < D) kr[tid] = kc[(lb * C + c) * D + tid];
     __syncthreads();
     if (tid < r) {  // t = U_h^T k'_c
       float acc = 0.f;
@@ -751,7 +754,7 @@ __global__ void __launch_bounds__(256) bwd_kdq(const float* __restrict__ kc, con
 // 16 rows a, one thread per (e, group of rows).
 template <int D>
 __global__ void __launch_bounds__(256) bwd_qcal_g(const float* __restrict__ kc, const float* __restrict__ S,
-                                                  float* __restrict__ G, int B, int Hq, int C) {
+                                                  float* __restrict__ G, int B, int Hq, int Hl, int C) {
   constexpr int ARB = 16;               // rows a per workgroup
   constexpr int TPE = 256 / D;          // threads per column e
   constexpr int APT = ARB / TPE;        // rows per thread
@@ -761,10 +764,11 @@ __global__ void __launch_bounds__(256) bwd_qcal_g(const float* __restrict__ kc, 
 #pragma unroll
   for (int m = 0; m < APT; ++m) acc[m] = 0.f;
   for (int b = 0; b < B; ++b) {
-    const int64_t base = ((int64_t)b * Hq + h) * C * D;
+    const int64_t base = ((int64_t)b * Hq + h) * C * D;                   // S: per query head
+    const int64_t kbase = ((int64_t)b * Hl + h / (Hq / Hl)) * C * D;     // k': its landmark head
     for (int c = 0; c < C; ++c) {
       const float sv = S[base + (int64_t)c * D + e];
-      const float* kr = kc + base + (int64_t)c * D + a0 + ag * APT;
+      const float* kr = kc + kbase + (int64_t)c * D + a0 + ag * APT;
 #pragma unroll
       for (int m = 0; m < APT; ++m) acc[m] = fmaf(kr[m], sv, acc[m]);
     }
@@ -804,11 +808,11 @@ template <int D>
 __global__ void __launch_bounds__(256) bwd_compress(const bf16_t* __restrict__ k, const bf16_t* __restrict__ lmk,
                                                     const float* __restrict__ dkc, const float* __restrict__ dbc,
                                                     const bf16_t* __restrict__ Dw, const bf16_t* __restrict__ Uw,
-                                                    float* __restrict__ dk, bf16_t* __restrict__ dlmk, int Hl, int Hkv,
-                                                    int N, int C, int r) {
+                                                    float* __restrict__ dk, bf16_t* __restrict__ dlmk, int Hq, int Hl,
+                                                    int Hkv, int N, int C, int r) {
   __shared__ float ks[64][D + 1];
   __shared__ float acc[64][D + 1];
-  __shared__ float Ls[D], gk[D], tr[32];
+  __shared__ float Ls[D], gk[D], gs[D], tr[32];
   __shared__ float zs[64], as[64], das[64];
   const int c = blockIdx.x % C, bkv = blockIdx.x / C;
   const int kvh = bkv % Hkv, b = bkv / Hkv;
@@ -826,41 +830,52 @@ __global__ void __launch_bounds__(256) bwd_compress(const bf16_t* __restrict__ k
 #pragma unroll
     for (int m = 0; m < 8; ++m) acc[x / D][x % D + m] = 0.f;
   }
-  const int lpk = Hl / Hkv;
+  const int lpk = Hl / Hkv, gq = Hq / Hl;
   for (int li = 0; li < lpk; ++li) {
     const int l = kvh * lpk + li;
     const int64_t ci = ((int64_t)b * Hl + l) * C + c;
     __syncthreads();
     for (int e = tid; e < D; e += 256) {
       Ls[e] = bf16_to_f32(lmk[ci * D + e].bits);
-      gk[e] = dkc[ci * D + e];  // sum over the chunk's pairs of dsigma q
+      gs[e] = 0.f;
     }
-    const float gb = dbc[ci];
-    __syncthreads();
-    // dk' = tau (I + U_l D_l) (sum dsigma q): the scores use q^ = q + U (D q)
-    if (r > 0) {
-      {  // t = D_l gk: eight threads per rank index a, each over D / 8 dims
-        const int a = tid >> 3, part = tid & 7;
-        float t = 0.f;
-        if (a < r)
-          for (int e = part; e < D; e += 8) t = fmaf(bf16_to_f32(Dw[((int64_t)l * r + a) * D + e].bits), gk[e], t);
-        t += __shfl_xor(t, 1);
-        t += __shfl_xor(t, 2);
-        t += __shfl_xor(t, 4);
-        if (a < r && part == 0) tr[a] = t;
+    // dk'_c = sum over the query heads h of landmark head l of tau (I + U_h D_h) S_hc, with
+    // S_hc the sum over head h's pairs with chunk c of dsigma q (the scores use
+    // q^ = q + U_h (D_h q)); db'_c = the sum of those pairs' dsigma
+    float gb = 0.f;
+    for (int hi = 0; hi < gq; ++hi) {
+      const int hq = l * gq + hi;
+      const int64_t qi = ((int64_t)b * Hq + hq) * C + c;
+      __syncthreads();  // the previous head's gk consumed
+      for (int e = tid; e < D; e += 256) gk[e] = dkc[qi * D + e];
+      gb += dbc[qi];
+      __syncthreads();
+      if (r > 0) {
+        {  // t = D_h gk: eight threads per rank index a, each over D / 8 dims
+          const int a = tid >> 3, part = tid & 7;
+          float t = 0.f;
+          if (a < r)
+            for (int e = part; e < D; e += 8) t = fmaf(bf16_to_f32(Dw[((int64_t)hq * r + a) * D + e].bits), gk[e], t);
+          t += __shfl_xor(t, 1);
+          t += __shfl_xor(t, 2);
+          t += __shfl_xor(t, 4);
+          if (a < r && part == 0) tr[a] = t;
+        }
+        __syncthreads();
+        {  // gk += U_h t: 256 / D threads per dim, each over a share of the rank
+          constexpr int TPE = 256 / D;
+          const int e = tid / TPE, part = tid % TPE;
+          float acc2 = 0.f;
+          for (int a2 = part; a2 < r; a2 += TPE) acc2 = fmaf(bf16_to_f32(Uw[((int64_t)hq * D + e) * r + a2].bits), tr[a2], acc2);
+          for (int o = 1; o < TPE; o <<= 1) acc2 += __shfl_xor(acc2, o);
+          __syncthreads();  // every thread has read gk (in t) before it is rewritten
+          if (part == 0) gk[e] = (gk[e] + acc2) * tau;
+        }
+      } else {
+        for (int e = tid; e < D; e += 256) gk[e] *= tau;
       }
       __syncthreads();
-      {  // gk += U_l t: 256 / D threads per dim, each over a share of the rank
-        constexpr int TPE = 256 / D;
-        const int e = tid / TPE, part = tid % TPE;
-        float acc2 = 0.f;
-        for (int a2 = part; a2 < r; a2 += TPE) acc2 = fmaf(bf16_to_f32(Uw[((int64_t)l * D + e) * r + a2].bits), tr[a2], acc2);
-        for (int o = 1; o < TPE; o <<= 1) acc2 += __shfl_xor(acc2, o);
-        __syncthreads();  // every thread has read gk (in t) before it is rewritten
-        if (part == 0) gk[e] = (gk[e] + acc2) * tau;
-      }
-    } else {
-      for (int e = tid; e < D; e += 256) gk[e] *= tau;
+      for (int e = tid; e < D; e += 256) gs[e] += gk[e];
     }
     __syncthreads();
     // z_j and dk'.k_j, four threads per key
@@ -869,7 +884,7 @@ __global__ void __launch_bounds__(256) bwd_compress(const bf16_t* __restrict__ k
       float zz = 0.f, gg = 0.f;
       for (int e = part; e < D; e += 4) {
         zz = fmaf(Ls[e], ks[j][e], zz);
-        gg = fmaf(gk[e], ks[j][e], gg);
+        gg = fmaf(gs[e], ks[j][e], gg);
       }
       zz += __shfl_xor(zz, 1);
       zz += __shfl_xor(zz, 2);
@@ -901,7 +916,7 @@ __global__ void __launch_bounds__(256) bwd_compress(const bf16_t* __restrict__ k
     }
     for (int x = tid; x < 64 * D; x += 256) {
       const int j = x / D, e = x % D;
-      acc[j][e] += as[j] * gk[e] + tau * das[j] * Ls[e];
+      acc[j][e] += as[j] * gs[e] + tau * das[j] * Ls[e];
     }
   }
   __syncthreads();
@@ -945,8 +960,8 @@ hipError_t launch_bwd_d(const Geom& g, const BwdArgs& a, char* ws, hipStream_t s
   const float* kdq = a.kc;
   if (g.r > 0 && C > 0) {
     kdq = (const float*)(ws + w.kdq);
-    hipLaunchKernelGGL((bwd_kdq<D>), dim3(g.B * g.Hl * ((C + KDQ_CHUNKS - 1) / KDQ_CHUNKS)), dim3(256), 0, st, a.kc,
-                       Dw, Uw, (float*)(ws + w.kdq), g.Hl, C, g.r);
+    hipLaunchKernelGGL((bwd_kdq<D>), dim3(g.B * g.Hq * ((C + KDQ_CHUNKS - 1) / KDQ_CHUNKS)), dim3(256), 0, st, a.kc,
+                       Dw, Uw, (float*)(ws + w.kdq), g.Hq, g.Hl, C, g.r);
   }
   const int NQC = (g.N + 63) / 64;
   const int ngb = (g.G() + 1) / 2;
@@ -966,8 +981,7 @@ hipError_t launch_bwd_d(const Geom& g, const BwdArgs& a, char* ws, hipStream_t s
                        a.sel_score, (const float*)lam, (const float*)dd, (const uint32_t*)pairs,
                        (const uint32_t*)boff, (const uint32_t*)toff, (const uint32_t*)(ws + w.imap), kdq, dsig,
                        (uint16_t*)(ws + w.dqp), dk, dv, dkc, dbc,
-                       g.Hq, g.Hkv, g.N, C,
-                       g.K, nbk);
+                       g.Hq, g.Hkv, g.N, C, g.K, nbk, g.r > 0 ? g.Hq : g.Hl);
   }
   {
     const dim3 grid((unsigned)std::min<int64_t>((rows + 3) / 4, 1 << 20));
@@ -987,13 +1001,14 @@ hipError_t launch_bwd_d(const Geom& g, const BwdArgs& a, char* ws, hipStream_t s
   }
   if (g.r > 0) {
     hipLaunchKernelGGL((bwd_qcal_g<D>), dim3(g.Hq * (D / 16)), dim3(256), 0, st, a.kc, (const float*)dkc, G, g.B,
-                       g.Hq, C);
+                       g.Hq, g.Hl, C);
     hipLaunchKernelGGL((bwd_qcal_weights<D>), dim3(g.Hq), dim3(256), 0, st, (const float*)G, Dw, Uw, (bf16_t*)a.dD,
                        (bf16_t*)a.dU, g.r);
   }
   if (C > 0)
     hipLaunchKernelGGL((bwd_compress<D>), dim3(g.B * g.Hkv * C), dim3(256), 0, st, k, (const bf16_t*)a.lmk,
-                       (const float*)dkc, (const float*)dbc, Dw, Uw, dk, (bf16_t*)a.dlmk, g.Hl, g.Hkv, g.N, C, g.r);
+                       (const float*)dkc, (const float*)dbc, Dw, Uw, dk, (bf16_t*)a.dlmk, g.Hq, g.Hl, g.Hkv, g.N, C,
+                       g.r);
   const int64_t kvn = (int64_t)g.B * g.Hkv * g.N * D;
   hipLaunchKernelGGL(bwd_convert, dim3(grid_for(kvn)), dim3(256), 0, st, (const float*)dk, (bf16_t*)a.dk, kvn);
   hipLaunchKernelGGL(bwd_convert, dim3(grid_for(kvn)), dim3(256), 0, st, (const float*)dv, (bf16_t*)a.dv, kvn);

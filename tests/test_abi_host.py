@@ -209,16 +209,17 @@ def test_decode_noalloc_rejects_dims_beyond_its_scratch():
     assert rc == hils.E_UNSUPPORTED
 
 
-def test_landmark_heads_per_kv_group_accepted_backward_rejects():
-    """Hlmk = Hkv (one landmark head per KV group) is valid for the forward calls; the
-    backward pass needs Hlmk == Hq and says so before touching the device."""
+def test_landmark_heads_per_kv_group_accepted():
+    """Hlmk = Hkv (one landmark head per KV group) is valid for every call, the backward
+    pass included (it gets as far as the workspace check, with no workspace given)."""
     lib = hils.load()
     d = hils.dims(1, 16, 4, 64, 1024, 16, Hlmk=4)
     assert hils.workspace_bytes(d, hils.OP_PREFILL) > 0
     assert hils.workspace_bytes(d, hils.OP_SCORE_TOPK) >= 4 * 16 * (2 * 64 + 16) * 2   # k' planes of 4 landmark heads
+    assert hils.workspace_bytes(d, hils.OP_BACKWARD) > 0
     fake = ctypes.c_void_p(0x1000)
-    rc = lib.hils_attn_prefill_backward(ctypes.byref(d), *([fake] * 18), 1 << 40, None)
-    assert rc == hils.E_UNSUPPORTED and b"landmark" in lib.hils_last_error()
+    rc = lib.hils_attn_prefill_backward(ctypes.byref(d), *([fake] * 17), None, 0, None)
+    assert rc == hils.E_WORKSPACE, lib.hils_last_error()
 
 
 def test_k_above_32_limits():

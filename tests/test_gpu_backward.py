@@ -32,6 +32,7 @@ CASES = [
     ("one_chunk", synth.Workload("bw_e", B=1, Hq=2, Hkv=1, d=64, N=100, K=2)),
     ("no_complete_chunk", synth.Workload("bw_f", B=1, Hq=2, Hkv=2, d=128, N=40, K=2)),
     ("d128_qcal_K48", synth.Workload("bw_g", B=1, Hq=2, Hkv=1, d=128, N=3500, K=48, qcal_rank=8)),
+    ("d64_qcal_shared_lmk", synth.Workload("bw_h", B=2, Hq=4, Hkv=2, d=64, N=900, K=6, qcal_rank=8, Hlmk=2)),
 ]
 
 

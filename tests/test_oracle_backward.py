@@ -16,15 +16,16 @@ import torch
 import oracle
 
 
-def _case(seed, W, r, N=37, d=8, S=4, K=2, Hq=2, Hkv=1):
+def _case(seed, W, r, N=37, d=8, S=4, K=2, Hq=2, Hkv=1, Hl=None):
     rng = np.random.default_rng(seed)
-    s = oracle.shape(1, Hq, Hkv, d, N=N, S=S, K=K, r=r, W=W)
+    Hl = Hq if Hl is None else Hl
+    s = oracle.shape(1, Hq, Hkv, d, N=N, S=S, K=K, r=r, W=W, Hl=Hl)
     C = N // S
     x = {
         "q": rng.standard_normal((1, Hq, N, d)),
         "k": rng.standard_normal((1, Hkv, N, d)),
         "v": rng.standard_normal((1, Hkv, N, d)),
-        "lmk": rng.standard_normal((1, Hq, C, d)),
+        "lmk": rng.standard_normal((1, Hl, C, d)),
         "D": rng.standard_normal((Hq, r, d)) * 0.3 if r else None,
         "U": rng.standard_normal((Hq, d, r)) * 0.3 if r else None,
     }
@@ -59,11 +60,20 @@ def _grads(s, x, rows, R):
 @pytest.mark.parametrize("W,r", [(0, 0), (8, 2), (12, 0), (4, 3)])
 def test_backward_matches_finite_differences(W, r):
     """Every element of q, k, v, the landmark queries, D, U, k' and b'."""
-    s, x, rows, R = _case(40 + W + r, W, r)
+    _check_finite_differences(*_case(40 + W + r, W, r))
+
+
+def test_backward_shared_landmark_heads_matches_finite_differences():
+    """Two query heads per landmark head, each with its own Q-Cal: the landmark
+    gradients gather both heads' score terms."""
+    _check_finite_differences(*_case(61, 0, 2, Hq=4, Hkv=2, Hl=2))
+
+
+def _check_finite_differences(s, x, rows, R):
     g, sel, kc, bc = _grads(s, x, rows, R)
     eps = 1e-6
     loss = lambda **kw: float(np.sum(R * _forward(s, kw.get("x", x), rows, sel, kw.get("kc"), kw.get("bc"))["o"]))
-    checks = [("q", "dq_full"), ("k", "dk"), ("v", "dv"), ("lmk", "dlmk")] + ([("D", "dD"), ("U", "dU")] if r else [])
+    checks = [("q", "dq_full"), ("k", "dk"), ("v", "dv"), ("lmk", "dlmk")] + ([("D", "dD"), ("U", "dU")] if x["D"] is not None else [])
     for name, gname in checks:
         a = x[name]
         fd = np.zeros_like(a)
