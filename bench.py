@@ -13,7 +13,9 @@ Also reported on the same line:
   * roofline of the dominant prefill kernel from HIP-event stage times;
   * cpu_baseline: the fp64 oracle on a bounded sample of the same workload;
   * dense: this library's dense causal attention kernel (same MFMA tiles) and
-    torch SDPA on the same q/k/v (the pages compare against full attention).
+    torch SDPA on the same q/k/v (the pages compare against full attention);
+    for decode, this library's dense decode kernel and a torch dense step on the
+    same cache.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-decode] [--no-cpu] [--no-dense]
                        [--no-prefill] [--copy-calibration] [--sweep] [--peaks]
@@ -487,9 +489,15 @@ def run_decode(wd, steps, warmup, seed, dense=False):
     dense_kv = sum(int(L) for L in x["seq_lens"]) * wd.Hkv * wd.d * 2 * 2
     dense_meas = None
     if dense and len(set(int(L) for L in x["seq_lens"])) == 1:
-        dense_meas = dense_decode(q, kcache, vcache, int(x["seq_lens"][0]), flush, flush_out)
-        dense_meas["hils_speedup"] = dense_meas["us"] / us
-        log("dense decode (torch): %.1f us" % dense_meas["us"])
+        own, o_own = dense_decode_own(dm, q, kcache, vcache, lens, flush, flush_out)
+        own["hils_speedup"] = own["us"] / us
+        own["achieved_GBs"] = dense_kv / (own["us"] * 1e-6) / 1e9
+        own["frac"] = own["achieved_GBs"] / PEAK_HBM_GBS
+        tq, o_t = dense_decode(q, kcache, vcache, int(x["seq_lens"][0]), flush, flush_out)
+        tq["hils_speedup"] = tq["us"] / us
+        own["max_abs_diff_vs_torch"] = float((o_own.float() - o_t.float().reshape(o_own.shape)).abs().max())
+        dense_meas = {"own": own, "torch": tq}
+        log("dense decode: own %.1f us (%.0f GB/s), torch %.1f us" % (own["us"], own["achieved_GBs"], tq["us"]))
     return {
         "workload": wd.name, "B": wd.B, "Hq": wd.Hq, "Hkv": wd.Hkv, "d": wd.d, "ctx": int(max(x["seq_lens"])),
         "K": wd.K, "window": wd.window, "us_per_step": us, "us_per_step_dist": dist,
@@ -530,7 +538,7 @@ def dense_decode(q, kcache, vcache, L, flush, flush_out, reps=5):
         p = torch.softmax(st, dim=2).to(torch.bfloat16).transpose(-1, -2).contiguous()   # [B, Hkv, G, L]
         return torch.matmul(p, vv)                                     # [B, Hkv, G, d]
 
-    step()
+    out = step()
     per = []
     for _ in range(reps):
         torch.sum(flush, dim=0, out=flush_out)
@@ -540,8 +548,30 @@ def dense_decode(q, kcache, vcache, L, flush, flush_out, reps=5):
         e1.record()
         torch.cuda.synchronize()
         per.append(e0.elapsed_time(e1) * 1e3)
-    return {"impl": "torch: bf16 matmuls K Q^T and P V with an fp32 softmax, per KV head", "us": float(np.median(per)),
-            "us_p10": float(np.percentile(per, 10)), "us_p90": float(np.percentile(per, 90))}
+    return ({"impl": "torch: bf16 matmuls K Q^T and P V with an fp32 softmax, per KV head", "us": float(np.median(per)),
+             "us_p10": float(np.percentile(per, 10)), "us_p90": float(np.percentile(per, 90))}, out)
+
+
+def dense_decode_own(dm, q, kcache, vcache, lens, flush, flush_out, reps=5):
+    """hils_dense_decode over the whole cache (every key read once per KV group), timed per
+    step after the same cache eviction as the sparse step."""
+    import torch
+    from long_context_chunk_amd import hils
+    ws = hils.workspace(dm, hils.OP_DENSE_DECODE)
+    o = torch.empty_like(q)
+    hils.dense_decode(dm, q, kcache, vcache, lens, o, ws)
+    per = []
+    for _ in range(reps):
+        torch.sum(flush, dim=0, out=flush_out)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        hils.dense_decode(dm, q, kcache, vcache, lens, o, ws)
+        e1.record()
+        torch.cuda.synchronize()
+        per.append(e0.elapsed_time(e1) * 1e3)
+    return ({"impl": "hils_dense_decode (splits of 2048 keys, one K/V read per KV group, split merge)",
+             "us": float(np.median(per)), "us_p10": float(np.percentile(per, 10)),
+             "us_p90": float(np.percentile(per, 90))}, o)
 
 
 def backward_flops(w, cnt):

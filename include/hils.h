@@ -80,7 +80,8 @@ enum {
   HILS_OP_PREFILL = 2,
   HILS_OP_DECODE = 3,
   HILS_OP_BACKWARD = 4,
-  HILS_OP_DECODE_MIRROR = 5 /* the decode calls over the landmark mirror */
+  HILS_OP_DECODE_MIRROR = 5, /* the decode calls over the landmark mirror */
+  HILS_OP_DENSE_DECODE = 6   /* hils_dense_decode */
 };
 
 typedef struct {
@@ -328,6 +329,21 @@ int hils_attn_prefill_backward(const hils_dims_t* dims, const void* q, const voi
  */
 int hils_dense_attention(const hils_dims_t* dims, const void* q, const void* k, const void* v, void* o,
                          void* stream);
+
+/*
+ * Dense decode, the baseline of the decode step (the pages compare decode latency with
+ * full attention: hotpaper.ai abstract, ai-papers.net "Results"): for every sequence b
+ * and query head h, o[b,h] = sum_{j < L_b} softmax_j(q[b,h].k[b,kvh,j] / sqrt(d))
+ * v[b,kvh,j], kvh = h / (Hq/Hkv), L_b = seq_lens[b] (clamped to N) -- every cached key,
+ * nothing selected.  q, o [B,Hq,d]; k_cache, v_cache [B,Hkv,N,d]; seq_lens [B] (device).
+ * bf16 I/O and Hq/Hkv in {1, 2, 4, 8} (HILS_E_UNSUPPORTED otherwise); S, K, Hlmk,
+ * qcal_rank and window are not used.  The keys are split into runs of 2048, each read
+ * once for the KV group's query heads; the runs' partial softmax sums are merged per
+ * (b, h).  Workspace: hils_workspace_bytes(dims, HILS_OP_DENSE_DECODE).  Asynchronous on
+ * `stream`.
+ */
+int hils_dense_decode(const hils_dims_t* dims, const void* q, const void* k_cache, const void* v_cache,
+                      const int32_t* seq_lens, void* o, void* ws, size_t ws_bytes, void* stream);
 
 /* Message of the last non-OK return on this thread ("" if none). */
 const char* hils_last_error(void);

@@ -123,6 +123,8 @@ size_t hils_workspace_bytes(const hils_dims_t* dims, int op) {
     case HILS_OP_BACKWARD:
       if (check_prefill(g) != HILS_OK) return (size_t)-1;
       return hils::backward_workspace_bytes(g);
+    case HILS_OP_DENSE_DECODE:
+      return hils::dense_decode_workspace_bytes(g);
     case HILS_OP_DECODE:
       if (g.C() > 65536) {
         fail(HILS_E_UNSUPPORTED, "decode needs N/S <= 65536 (N=%d)", g.N);
@@ -452,6 +454,27 @@ int hils_attn_decode_paged_mirror(const hils_dims_t* dims, const void* q, const 
   if ((rc = check_pages(g, block_table, max_blocks, num_pages, pg))) return rc;
   return run_decode(dims, q, k_pages, v_pages, seq_lens, kc, bc, qcal_D, qcal_U, sel_idx_out, o, ws, ws_bytes, stream,
                     nullptr, pg, kc_mirror);
+}
+
+int hils_dense_decode(const hils_dims_t* dims, const void* q, const void* k_cache, const void* v_cache,
+                      const int32_t* seq_lens, void* o, void* ws, size_t ws_bytes, void* stream) {
+  hils::Geom g;
+  int rc = check_dims(dims, g);
+  if (rc) return rc;
+  if (!q || !k_cache || !v_cache || !seq_lens || !o)
+    return fail(HILS_E_INVAL, "q, k_cache, v_cache, seq_lens and o must be non-NULL");
+  if (g.io != HILS_BF16) return fail(HILS_E_UNSUPPORTED, "the dense decode baseline needs bf16 I/O");
+  const int G = g.Hq / g.Hkv;
+  if (G != 1 && G != 2 && G != 4 && G != 8)
+    return fail(HILS_E_UNSUPPORTED, "the dense decode baseline needs Hq/Hkv in {1, 2, 4, 8} (%d)", G);
+  const size_t need = hils::dense_decode_workspace_bytes(g);
+  if (!ws || ws_bytes < need) return fail(HILS_E_WORKSPACE, "workspace of %zu bytes needed, %zu given", need, ws_bytes);
+  if ((int64_t)g.B * g.Hkv * ((g.N + 2047) / 2048) > 0x7fffffff)
+    return fail(HILS_E_UNSUPPORTED, "B*Hkv*ceil(N/2048) must fit a 31-bit grid");
+  const hipError_t e = hils::launch_dense_decode(g, q, k_cache, v_cache, seq_lens, o, ws, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "hils_dense_decode");
+  g_err[0] = 0;
+  return HILS_OK;
 }
 
 int hils_dense_attention(const hils_dims_t* dims, const void* q, const void* k, const void* v, void* o,

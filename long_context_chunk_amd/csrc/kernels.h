@@ -89,5 +89,8 @@ hipError_t launch_mirror(const Geom& g, const float* kc, const float* bc, uint8_
 
 // Dense causal attention (the baseline).
 hipError_t launch_dense(const Geom& g, const void* q, const void* k, const void* v, void* o, hipStream_t st);
+size_t dense_decode_workspace_bytes(const Geom& g);
+hipError_t launch_dense_decode(const Geom& g, const void* q, const void* k, const void* v, const int32_t* seq_lens,
+                               void* o, void* ws, hipStream_t st);
 
 }  // namespace hils

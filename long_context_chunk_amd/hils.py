@@ -16,14 +16,14 @@ _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libhils.so")
 
 F32, BF16 = 0, 1
-OP_COMPRESS, OP_SCORE_TOPK, OP_PREFILL, OP_DECODE, OP_BACKWARD, OP_DECODE_MIRROR = 0, 1, 2, 3, 4, 5
+OP_COMPRESS, OP_SCORE_TOPK, OP_PREFILL, OP_DECODE, OP_BACKWARD, OP_DECODE_MIRROR, OP_DENSE_DECODE = 0, 1, 2, 3, 4, 5, 6
 OK, E_INVAL, E_UNSUPPORTED, E_WORKSPACE, E_HIP = 0, -1, -2, -3, -4
 
 SYMBOLS = ("hils_workspace_bytes", "hils_landmark_compress", "hils_chunk_score_topk", "hils_attn_prefill",
            "hils_attn_prefill_timed", "hils_attn_decode", "hils_attn_decode_timed", "hils_landmark_compress_paged",
            "hils_attn_decode_paged", "hils_dense_attention", "hils_attn_prefill_backward", "hils_attn_decode_noalloc",
            "hils_landmark_mirror", "hils_attn_decode_mirror", "hils_attn_decode_mirror_timed",
-           "hils_attn_decode_paged_mirror", "hils_last_error")
+           "hils_attn_decode_paged_mirror", "hils_dense_decode", "hils_last_error")
 NOALLOC_SCRATCH_BYTES = 16 << 20   # HILS_NOALLOC_SCRATCH_BYTES of include/hils.h
 STAGES = ("compress", "score_threshold", "score_select", "bucket", "chunk_attend", "own_attend", "fuse")
 DECODE_STAGES = ("scan", "merge", "attend_fuse")
@@ -66,6 +66,7 @@ def load():
         lib.hils_attn_decode_timed.argtypes = [dp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp,
                                                ctypes.POINTER(ctypes.c_float)]
         lib.hils_dense_attention.argtypes = [dp, vp, vp, vp, vp, vp]
+        lib.hils_dense_decode.argtypes = [dp, vp, vp, vp, vp, vp, vp, sz, vp]
         lib.hils_attn_decode_noalloc.argtypes = [dp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
         lib.hils_landmark_compress_paged.argtypes = [dp, vp, vp, i32, i32, vp, i32, i32, vp, vp, vp]
         lib.hils_attn_decode_paged.argtypes = [dp, vp, vp, vp, vp, i32, i32, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
@@ -80,7 +81,7 @@ def load():
                   "hils_attn_decode", "hils_attn_decode_timed", "hils_dense_attention", "hils_landmark_compress_paged",
                   "hils_attn_decode_paged", "hils_attn_prefill_backward", "hils_attn_decode_noalloc",
                   "hils_landmark_mirror", "hils_attn_decode_mirror", "hils_attn_decode_mirror_timed",
-                  "hils_attn_decode_paged_mirror"):
+                  "hils_attn_decode_paged_mirror", "hils_dense_decode"):
             getattr(lib, f).restype = ctypes.c_int
         lib.hils_last_error.argtypes = []
         lib.hils_last_error.restype = ctypes.c_char_p
@@ -313,6 +314,17 @@ def dense_attention(dm: Dims, q, k, v, o):
     _req(v, "v", (dm.B, dm.Hkv, dm.N, dm.d), dt)
     _req(o, "o", (dm.B, dm.Hq, dm.N, dm.d), dt)
     _check(load().hils_dense_attention(ctypes.byref(dm), _p(q), _p(k), _p(v), _p(o), _stream()))
+
+
+def dense_decode(dm: Dims, q, k_cache, v_cache, seq_lens, o, ws):
+    """hils_dense_decode: the dense baseline of a decode step (every cached key, bf16)."""
+    _req(q, "q", (dm.B, dm.Hq, dm.d), torch.bfloat16)
+    _req(k_cache, "k_cache", (dm.B, dm.Hkv, dm.N, dm.d), torch.bfloat16)
+    _req(v_cache, "v_cache", (dm.B, dm.Hkv, dm.N, dm.d), torch.bfloat16)
+    _req(seq_lens, "seq_lens", (dm.B,), torch.int32)
+    _req(o, "o", (dm.B, dm.Hq, dm.d), torch.bfloat16)
+    _check(load().hils_dense_decode(ctypes.byref(dm), _p(q), _p(k_cache), _p(v_cache), _p(seq_lens), _p(o), _p(ws),
+                                    ws.numel() * ws.element_size(), _stream()))
 
 
 def landmark_compress_paged(dm: Dims, k_pages, block_table, lmk_q, kc, bc, c_begin=0, c_end=None):

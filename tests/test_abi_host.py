@@ -325,3 +325,21 @@ def test_decode_chunk_limit():
             hils.workspace_bytes(hils.dims(1, 2, 1, 64, 65537 * 64, 16), op)
     with pytest.raises(hils.HilsError):
         hils.workspace_bytes(hils.dims(1, 2, 1, 64, 16385 * 64, 16), hils.OP_PREFILL)
+
+
+def test_dense_decode_validation():
+    """hils_dense_decode checks its arguments before touching the device: bf16 only,
+    Hq/Hkv in {1, 2, 4, 8}, non-NULL tensors, a workspace of the size it reports."""
+    lib = hils.load()
+    fake = ctypes.c_void_p(0x1000)
+    ok = hils.dims(2, 8, 2, 128, 4096, 8)
+    need = hils.workspace_bytes(ok, hils.OP_DENSE_DECODE)
+    assert need == 2 * 8 * 2 * (128 + 2) * 4          # B * Hq * ceil(N / 2048) partials of d + 2 floats
+    assert lib.hils_dense_decode(ctypes.byref(ok), fake, fake, fake, fake, fake, None, 0, None) == hils.E_WORKSPACE
+    assert lib.hils_dense_decode(ctypes.byref(ok), None, fake, fake, fake, fake, fake, need, None) == hils.E_INVAL
+    g3 = hils.dims(2, 6, 2, 128, 4096, 8)
+    assert lib.hils_dense_decode(ctypes.byref(g3), fake, fake, fake, fake, fake, fake, 1 << 30, None) == \
+        hils.E_UNSUPPORTED
+    f32 = hils.dims(2, 8, 2, 128, 4096, 8, io=hils.F32)
+    assert lib.hils_dense_decode(ctypes.byref(f32), fake, fake, fake, fake, fake, fake, 1 << 30, None) == \
+        hils.E_UNSUPPORTED

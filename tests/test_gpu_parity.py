@@ -300,6 +300,36 @@ def test_dense_baseline(name, w):
     assert err.max() <= mx and err.mean() <= mean, (err.max(), err.mean())
 
 
+DENSE_DECODE = [
+    ("d128_g4", synth.Workload("dd_a", B=4, Hq=8, Hkv=2, d=128, N=6000, K=8, decode=True,
+                               seq_lens=[1, 2047, 2049, 6000])),
+    ("d64_g8", synth.Workload("dd_b", B=2, Hq=8, Hkv=1, d=64, N=5000, K=8, decode=True, seq_lens=[4097, 333])),
+    ("d128_g1", synth.Workload("dd_c", B=2, Hq=2, Hkv=2, d=128, N=3000, K=8, decode=True, seq_lens=[64, 3000])),
+    ("d64_g2", synth.Workload("dd_d", B=3, Hq=4, Hkv=2, d=64, N=4100, K=8, decode=True, seq_lens=[4100, 2048, 65])),
+]
+
+
+@pytest.mark.parametrize("name,w", DENSE_DECODE, ids=[n for n, _ in DENSE_DECODE])
+def test_dense_decode_baseline(name, w):
+    """hils_dense_decode against the oracle's dense causal attention of each sequence's
+    last row (every cached key; splits of 2048 keys, ragged lengths across them)."""
+    _say("dense decode", name)
+    x = synth.make_inputs(w, SEED + 9)
+    dm = dims_of(w)
+    q, k, v = (upload(x[n], w.io) for n in ("q", "k", "v"))
+    lens = torch.from_numpy(x["seq_lens"]).cuda()
+    o = torch.full_like(q, float("nan"))
+    hils.dense_decode(dm, q, k, v, lens, o, hils.workspace(dm, hils.OP_DENSE_DECODE))
+    torch.cuda.synchronize()
+    rows = np.asarray([(b, h, int(x["seq_lens"][b]) - 1) for b in range(w.B) for h in range(w.Hq)])
+    ref = oracle.dense(shape_of(w), rows[:, 0], rows[:, 1], rows[:, 2], x["q"][rows[:, 0], rows[:, 1]], x["k"],
+                       x["v"])
+    got = o.float().cpu().numpy()[rows[:, 0], rows[:, 1]]
+    err = np.abs(got - ref)
+    mx, mean = TOL[w.io]
+    assert np.all(np.isfinite(got)) and err.max() <= mx and err.mean() <= mean, (err.max(), err.mean())
+
+
 # ------------------------------------------ ablation variants of the chunk summary
 # The pages' ablations replace the learned landmark: mean pooling of the chunk's keys
 # (a_j = 1/S, what a zero landmark query gives) and one shared query for every chunk.
