@@ -516,8 +516,15 @@ constexpr int P2_EXT = 16;     // extension elements after plane 0: [b'_hi, b'_m
 // one workgroup per CU.
 constexpr int SEL_HALF_KB = 48;
 
-template <typename IO, int D, int NQ, int NK, bool QCAL, bool KB>
-__global__ void __launch_bounds__(256, KB ? 1 : 2) score_topk_kernel(const IO* __restrict__ q, const IO* __restrict__ Dw,
+// LM, the list mode: 0 for K <= 16 (half lists of SEL_HALF_SMALL slots: with the smaller
+// lists, three workgroups fit a CU where the score operands leave the registers for it),
+// 1 for K <= 32, 2 for K > 32 (KB).
+constexpr int SEL_HALF_SMALL = 16;
+template <int LM, int NQ, int NK>
+constexpr int sel_wgs() { return LM == 2 ? 1 : (LM == 0 && NQ * NK <= 2) ? 3 : 2; }
+
+template <typename IO, int D, int NQ, int NK, bool QCAL, int LM>
+__global__ void __launch_bounds__(256, (sel_wgs<LM, NQ, NK>())) score_topk_kernel(const IO* __restrict__ q, const IO* __restrict__ Dw,
                                                            const IO* __restrict__ Uw, const uint16_t* __restrict__ p2,
                                                            const float* __restrict__ theta,
                                                            int32_t* __restrict__ sel_idx,
@@ -530,7 +537,8 @@ __global__ void __launch_bounds__(256, KB ? 1 : 2) score_topk_kernel(const IO* _
   constexpr int SEGS = DE2 / 8;
   constexpr int NSEG = SEL_CT * SEGS;
   constexpr int PL = (NSEG + 255) / 256;
-  constexpr int SH = KB ? SEL_HALF_KB : SEL_HALF;   // slots per half list
+  constexpr bool KB = LM == 2;
+  constexpr int SH = KB ? SEL_HALF_KB : LM == 0 ? SEL_HALF_SMALL : SEL_HALF;   // slots per half list
   constexpr int HSTR = SH + 1;          // half-list stride: SH slots + a spill slot
   constexpr int LIST = 2 * HSTR;        // slots per row
   constexpr int NPROD = NQ > NK ? NQ : NK;
@@ -1014,11 +1022,15 @@ static void launch_st(const Geom& g, int Nq, const int32_t* pos0, const void* q,
   if (ev) hipEventRecord(ev[0], st);
   if (items > 0) {
     if (g.K > 32)
-      hipLaunchKernelGGL((score_topk_kernel<IO, D, NQ, NK, QCAL, true>), dim3(grid), dim3(256), 0, st, (const IO*)q,
+      hipLaunchKernelGGL((score_topk_kernel<IO, D, NQ, NK, QCAL, 2>), dim3(grid), dim3(256), 0, st, (const IO*)q,
+                         (const IO*)Dw, (const IO*)Uw, planes, (const float*)theta, si, ss, pos0, g.Hq, g.Hl, Nq,
+                         g.C(), g.K, g.r, NB, items, g.nw);
+    else if (g.K > 16)
+      hipLaunchKernelGGL((score_topk_kernel<IO, D, NQ, NK, QCAL, 1>), dim3(grid), dim3(256), 0, st, (const IO*)q,
                          (const IO*)Dw, (const IO*)Uw, planes, (const float*)theta, si, ss, pos0, g.Hq, g.Hl, Nq,
                          g.C(), g.K, g.r, NB, items, g.nw);
     else
-      hipLaunchKernelGGL((score_topk_kernel<IO, D, NQ, NK, QCAL, false>), dim3(grid), dim3(256), 0, st, (const IO*)q,
+      hipLaunchKernelGGL((score_topk_kernel<IO, D, NQ, NK, QCAL, 0>), dim3(grid), dim3(256), 0, st, (const IO*)q,
                          (const IO*)Dw, (const IO*)Uw, planes, (const float*)theta, si, ss, pos0, g.Hq, g.Hl, Nq,
                          g.C(), g.K, g.r, NB, items, g.nw);
   }
