@@ -953,8 +953,11 @@ static hipError_t launch_attend_t(const Geom& g, const void* q, const void* k, c
   if (g.K > 32)
     hipLaunchKernelGGL((fuse<IO, D, 64>), dim3((unsigned)nwg), dim3(256), 0, st, scr, (const float*)lse,
                        (const void*)partial, (IO*)o, g.N, C, g.K, rows, g.nw);
-  else
+  else if (g.K > 16)
     hipLaunchKernelGGL((fuse<IO, D, 32>), dim3((unsigned)nwg), dim3(256), 0, st, scr, (const float*)lse,
+                       (const void*)partial, (IO*)o, g.N, C, g.K, rows, g.nw);
+  else
+    hipLaunchKernelGGL((fuse<IO, D, 16>), dim3((unsigned)nwg), dim3(256), 0, st, scr, (const float*)lse,
                        (const void*)partial, (IO*)o, g.N, C, g.K, rows, g.nw);
   if (ev) hipEventRecord(ev[3], st);
   return hipGetLastError();
