@@ -73,11 +73,17 @@ int main() {
   f32.io = HILS_F32;
   EXPECT(hils_attn_prefill_backward(&f32, f, f, f, f, (float*)f, nullptr, nullptr, (int32_t*)f, (float*)f, f, f, f, f,
                                     f, f, nullptr, nullptr, f, (size_t)1 << 40, nullptr) == HILS_E_UNSUPPORTED);
-  hils_dims_t shared = ok;
+  hils_dims_t shared = ok;  // landmark heads shared by query heads: valid, stopped at the workspace check
   shared.Hlmk = 2;
   EXPECT(hils_attn_prefill_backward(&shared, f, f, f, f, (float*)f, nullptr, nullptr, (int32_t*)f, (float*)f, f, f, f,
-                                    f, f, f, nullptr, nullptr, f, (size_t)1 << 40, nullptr) == HILS_E_UNSUPPORTED);
+                                    f, f, f, nullptr, nullptr, nullptr, 0, nullptr) == HILS_E_WORKSPACE);
   EXPECT(hils_last_error()[0] != 0);
+  // the dense decode baseline: bf16 and Hq/Hkv in {1, 2, 4, 8}, a workspace of the reported size
+  const size_t dd = hils_workspace_bytes(&ok, HILS_OP_DENSE_DECODE);
+  EXPECT(dd != (size_t)-1 && dd > 0);
+  EXPECT(hils_dense_decode(&ok, f, f, f, (const int32_t*)f, f, nullptr, 0, nullptr) == HILS_E_WORKSPACE);
+  EXPECT(hils_dense_decode(&ok, nullptr, f, f, (const int32_t*)f, f, f, dd, nullptr) == HILS_E_INVAL);
+  EXPECT(hils_dense_decode(&f32, f, f, f, (const int32_t*)f, f, f, (size_t)1 << 40, nullptr) == HILS_E_UNSUPPORTED);
   if (!g_fail) printf("host ABI sanitizer run: ok\n");
   return g_fail;
 }
