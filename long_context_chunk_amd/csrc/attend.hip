@@ -320,17 +320,24 @@ __global__ void __launch_bounds__(256) bucket_part1(const int32_t* __restrict__ 
   const int t = threadIdx.x;
   const int64_t beg = (int64_t)sl * slice, end = min(group_len, beg + slice);
   const int32_t* s = sel + (int64_t)grp * group_len;
+  // a tile's entries, loaded during the previous tile's scatter and writes (indices past
+  // the slice read its last entry, in bounds, and are dropped)
+  int32_t nx[BK_PER];
+  auto fetch = [&](int64_t t0n) {
+#pragma unroll
+    for (int u = 0; u < BK_PER; ++u) nx[u] = s[min(t0n + t + 256 * u, end - 1)];
+  };
+  if (beg < end) fetch(beg);
   for (int64_t t0 = beg; t0 < end; t0 += BK_TILE) {
     hist[t] = 0;
-    __syncthreads();
     int32_t c[BK_PER];
     uint32_t rk[BK_PER];
 #pragma unroll
     for (int u = 0; u < BK_PER; ++u) {
       const int64_t i = t0 + t + 256 * u;
-      const int32_t x = i < end ? s[i] : -1;
-      c[u] = (unsigned)x < (unsigned)C ? x : -1;  // the same entries bucket_count counted
+      c[u] = i < end && (unsigned)nx[u] < (unsigned)C ? nx[u] : -1;  // the same entries bucket_count counted
     }
+    __syncthreads();
 #pragma unroll
     for (int u = 0; u < BK_PER; ++u)
       if (c[u] >= 0) rk[u] = atomicAdd(&hist[c[u] >> FINE_BITS], 1u);
@@ -344,6 +351,7 @@ __global__ void __launch_bounds__(256) bucket_part1(const int32_t* __restrict__ 
       gpos[t] = boff[bk0] + atomicAdd(&rcur[(int64_t)grp * nrg + t], h);
     }
     __syncthreads();
+    if (t0 + BK_TILE < end) fetch(t0 + BK_TILE);  // after this tile's global reads, before its writes
 #pragma unroll
     for (int u = 0; u < BK_PER; ++u)
       if (c[u] >= 0) {
@@ -380,15 +388,23 @@ __global__ void __launch_bounds__(256) bucket_part2(const uint32_t* __restrict__
   const int64_t bk0 = (int64_t)grp * C + c0;
   const uint32_t R0 = boff[bk0], R1 = boff[bk0 + nf];
   const uint32_t ebase = (uint32_t)(grp * group_len);
-  for (uint32_t t0 = R0 + (uint32_t)sp * BK_TILE; t0 < R1; t0 += (uint32_t)split * BK_TILE) {
+  const uint32_t stride = (uint32_t)split * BK_TILE;
+  // a tile's keys, loaded during the previous tile's scatter and writes (indices past the
+  // range read its last key, in bounds, and are dropped)
+  uint32_t nx[BK_PER];
+  auto fetch = [&](uint32_t t0n) {
+#pragma unroll
+    for (int u = 0; u < BK_PER; ++u) nx[u] = tmp[min(t0n + t + 256 * u, R1 - 1)];
+  };
+  // 64-bit tile starts: R1 may lie within one stride of 2^32
+  if ((uint64_t)R0 + (uint64_t)sp * BK_TILE < R1) fetch(R0 + (uint32_t)sp * BK_TILE);
+  for (uint64_t t0l = (uint64_t)R0 + (uint64_t)sp * BK_TILE; t0l < R1; t0l += stride) {
+    const uint32_t t0 = (uint32_t)t0l;
     if (t < NF) hist[t] = 0;
-    __syncthreads();
     uint32_t key[BK_PER], rk[BK_PER];
 #pragma unroll
-    for (int u = 0; u < BK_PER; ++u) {
-      const uint32_t i = t0 + t + 256 * u;
-      key[u] = i < R1 ? tmp[i] : 0xffffffffu;
-    }
+    for (int u = 0; u < BK_PER; ++u) key[u] = t0l + t + 256 * u < R1 ? nx[u] : 0xffffffffu;
+    __syncthreads();
 #pragma unroll
     for (int u = 0; u < BK_PER; ++u)
       if (key[u] != 0xffffffffu) rk[u] = atomicAdd(&hist[key[u] >> LOCAL_BITS], 1u);
@@ -405,6 +421,7 @@ __global__ void __launch_bounds__(256) bucket_part2(const uint32_t* __restrict__
       if (lane < nf && h) gpos[lane] = boff[bk0 + lane] + atomicAdd(&fcur[bk0 + lane], h);
     }
     __syncthreads();
+    if (t0l + stride < R1) fetch(t0 + stride);  // after this tile's global reads, before its writes
 #pragma unroll
     for (int u = 0; u < BK_PER; ++u)
       if (key[u] != 0xffffffffu) {
