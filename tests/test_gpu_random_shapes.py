@@ -1,5 +1,5 @@
-"""Parity on seeded random shapes: prefill, decode (plain and over the landmark mirror) and
-the dense decode baseline against the oracle, over head layouts (GQA, MQA, landmark heads
+"""Parity on seeded random shapes: prefill, decode (plain and over the landmark mirror), the
+dense decode baseline and the backward pass against the oracle, over head layouts (GQA, MQA, landmark heads
 shared per KV group), d = 64 / 128, K from 1 to 64 (across the 16- and 32-entry list
 boundaries), Q-Cal ranks, local windows, bf16 and fp32, ragged lengths and decode caches
 of up to four scan splits.  Each case is one pytest item; the shapes come from a fixed
@@ -96,3 +96,42 @@ def test_random_shape(label, w, seed):
         err = np.abs(o.float().cpu().numpy()[rr[:, 0], rr[:, 1]] - dref)
         mx, mean = TOL[w.io]
         assert err.max() <= mx and err.mean() <= mean, (label, "dense decode", err.max(), err.mean())
+
+
+def _backward_cases(seed=2027, n=12):
+    rng = np.random.default_rng(seed)
+    out = []
+    for ci in range(n):
+        d = int(rng.choice([64, 128]))
+        Hkv = int(rng.choice([1, 2]))
+        Hq = Hkv * int(rng.choice([1, 2, 4]))
+        Hlmk = Hq if rng.random() < 0.6 else Hkv
+        K = int(rng.choice([1, 2, 5, 8, 16, 17, 32, 33, 48]))
+        r = int(rng.choice([0, 8, 32]))
+        W = int(rng.choice([0, 0, 128, 512]))
+        B = int(rng.integers(1, 3))
+        N = int(rng.integers(1, 1600))
+        w = synth.Workload("rbw%d" % ci, B=B, Hq=Hq, Hkv=Hkv, d=d, N=N, K=K, qcal_rank=r, Hlmk=Hlmk, window=W)
+        label = "%d_d%d_h%d-%d-%d_K%d_r%d_W%d_N%d_B%d" % (ci, d, Hq, Hkv, Hlmk, K, r, W, N, B)
+        out.append((label, w, 7000 + ci))
+    return out
+
+
+BACKWARD_CASES = _backward_cases()
+
+
+@pytest.mark.parametrize("label,w,seed", BACKWARD_CASES, ids=[c[0] for c in BACKWARD_CASES])
+def test_random_shape_backward(label, w, seed):
+    from test_gpu_backward import T_DO, _compare, gpu_backward, oracle_backward
+    print("random backward shape", label, flush=True)
+    sys.stdout.flush()
+    x = synth.make_inputs(w, seed)
+    g = gpu_prefill(w, x)
+    dO = synth.normal((w.B, w.Hq, w.N, w.d), seed, T_DO, synth.BF16)
+    got = gpu_backward(w, x, g, dO)
+    ref = oracle_backward(w, x, g["sel_idx"], dO)
+    for n in ["dq", "dk", "dv"] + (["dlmk"] if w.C else []) + (["dD", "dU"] if w.qcal_rank else []):
+        if np.abs(ref[n]).max() > 0:   # a gradient that is zero everywhere (no complete chunk) has no scale
+            _compare(n, got[n], ref[n], label)
+        else:
+            assert np.abs(got[n]).max() == 0, (label, n)
