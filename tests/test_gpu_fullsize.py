@@ -94,6 +94,34 @@ def test_prefill_full_size(name, nrows):
     np.testing.assert_allclose(bc.cpu().numpy(), bc_o, rtol=0, atol=1e-5)
 
 
+@pytest.mark.timeout(400)
+def test_prefill_at_the_chunk_limit():
+    """Prefill at the largest supported context, N/S = 16384 chunks (1M tokens, 16/4-style
+    heads reduced to 2/1, d = 64, K = 16): the longest rows (16383 candidate chunks) and
+    sampled rows against the oracle, selection properties over every row, k'/b' of every
+    chunk."""
+    w = synth.Workload("prefill_1m_limit", B=1, Hq=2, Hkv=1, d=64, N=16384 * 64, K=16)
+    _say("prefill at the chunk limit", w.N)
+    x = synth.make_inputs(w, SEED + 2)
+    o, sel, scr, kc, bc = _run_prefill(w, x)
+    _selection_properties(w, sel, scr)
+    assert torch.isfinite(o.float()).all()
+    rng = np.random.default_rng(4)
+    rows = [(0, h, i) for h in range(w.Hq) for i in range(w.N - 64, w.N)]              # the longest rows
+    rows += sorted({(0, int(rng.integers(w.Hq)), int(rng.integers(w.N))) for _ in range(200)})
+    rows += [(0, h, 64 * c + j) for h in range(w.Hq) for c in (1, 16, 8191, 16383) for j in (0, 63)]
+    rows = sorted(set(rows))
+    kc_o, bc_o = oracle.compress(shape_of(w), x["k"], x["lmk"])
+    ref = oracle.prefill_rows(shape_of(w), x["q"], x["k"], x["v"], kc_o, bc_o, rows)
+    rr = np.asarray(rows)
+    sel_h, scr_h, o_h = sel[0].cpu().numpy(), scr[0].cpu().numpy(), o[0].float().cpu().numpy()
+    summ = check_selection_and_output(w, x, kc_o, bc_o, rows, ref, sel_h[rr[:, 1], rr[:, 2]], scr_h[rr[:, 1], rr[:, 2]],
+                                      o_h[rr[:, 1], rr[:, 2]], label=w.name)
+    _say(w.name, summ)
+    np.testing.assert_allclose(kc.cpu().numpy(), kc_o, rtol=0, atol=1e-5 * max(1.0, np.abs(kc_o).max()))
+    np.testing.assert_allclose(bc.cpu().numpy(), bc_o, rtol=0, atol=1e-5)
+
+
 def test_decode_full_size():
     w = synth.WORKLOADS["decode_512k"]
     _say("full-size decode", w.name)
