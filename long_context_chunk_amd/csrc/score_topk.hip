@@ -8,20 +8,27 @@
 // keep the K best (ties -> lower chunk id).  (aitrends.kr article,
 // "Methodology": the score formula, the calculation flow and the Q-Cal module.)
 //
+// Q-Cal is applied on the key side: q^_i . k'_c = q_i . k~_hc with
+//   k~_hc = k'_c + D_h^T (U_h^T k'_c),
+// one fp32 row per (batch, query head, chunk) made once per call by prep_kprime.  The
+// queries then enter as given: a bf16 query is one exact bf16 term, so the selection
+// pass needs two products per score (q . k~_hi + q . k~_lo) instead of three, and
+// neither pass computes q^.
+//
 // Two passes over the past chunks, both on v_mfma_f32_32x32x16_bf16, one workgroup per
 // 128 consecutive queries of one (batch, head) (32 per wave), with k' tiles staged
 // through LDS and shared by the four waves:
 //
 //   1. score_threshold (queries = M, chunks = N: accumulator register r of a lane holds
 //      one chunk's score for one row; the 32 lanes of a half-wave cover 32 chunks of
-//      that row): one bf16 product per score, bf16(q^/sqrt(d)) . bf16(k'_c), with b'_c
+//      that row): one bf16 product per score, bf16(q/sqrt(d)) . bf16(k~_c), with b'_c
 //      and an error allowance e_i |k'_c| folded into one extra MFMA k-step, so every
 //      value is at most the fp32-accurate score of pass 2.  Each lane keeps the two
 //      largest values of its column of chunks; the K-th largest of these 64 values of
 //      distinct chunks is a threshold theta_i that the row's K-th best score can not
 //      be below.
 //   2. score_topk_kernel (chunks = M, queries = N: each lane owns one row's scores):
-//      the scores to ~2^-17 relative (tau k' split into bf16 hi + lo terms, q^ too
+//      the scores to ~2^-17 relative (tau k~ split into bf16 hi + lo terms, q too
 //      when it is not exactly bf16; b' through an extra k-step), tested against the
 //      row's threshold, which starts at theta_i, so only about K candidates per row
 //      are kept.  Each lane appends its row's candidates to its own half of the row's
@@ -203,16 +210,15 @@ HILS_DEV uint16_t bf16_up(float x) {
   return b;
 }
 
-// q^ = q + U_h (D_h q) of this lane's row (zero when !row_ok), delivered one MFMA
-// k-step at a time in the A-operand layout: sink(ks, v) gets v[m] = q^[kperm(ks, hf, m)].
-// Q-Cal runs on the MFMA (T = D q, then U T), chained through the accumulator layout.
-template <typename IO, int D, bool QCAL, typename Sink>
-HILS_DEV void qhat_rows(const IO* __restrict__ q, const IO* __restrict__ Dw, const IO* __restrict__ Uw, int hh, int r,
-                        int64_t qrow, bool row_ok, int lane, Sink&& sink) {
+// This lane's query row (zero when !row_ok), delivered one MFMA k-step at a time in the
+// A-operand layout: sink(ks, v) gets v[m] = q[kperm(ks, hf, m)].  Q-Cal never touches
+// the queries: it is folded into the chunk rows (prep_kprime).
+template <typename IO, int D, typename Sink>
+HILS_DEV void q_rows(const IO* __restrict__ q, int64_t qrow, bool row_ok, int lane, Sink&& sink) {
   constexpr int NKS = D / 16;
-  constexpr int NIO = io_traits<IO>::terms;
   const int hf = lane >> 5;
-  auto load8 = [&](int ks, float(&v)[8]) {
+#pragma unroll
+  for (int ks = 0; ks < NKS; ++ks) {
     float a4[4], b4[4];
     if (row_ok) {
       io_traits<IO>::load4(q, qrow + kperm(ks, hf, 0), a4);
@@ -221,132 +227,31 @@ HILS_DEV void qhat_rows(const IO* __restrict__ q, const IO* __restrict__ Dw, con
 #pragma unroll
       for (int m = 0; m < 4; ++m) a4[m] = b4[m] = 0.f;
     }
+    float v[8];
 #pragma unroll
     for (int m = 0; m < 4; ++m) {
       v[m] = a4[m];
       v[4 + m] = b4[m];
     }
-  };
-  if constexpr (!QCAL) {
-#pragma unroll
-    for (int ks = 0; ks < NKS; ++ks) {
-      float v[8];
-      load8(ks, v);
-      sink(ks, v);
-    }
-  } else {
-    // raw q terms (exact: NIO bf16 terms carry an io value exactly), as B operands
-    bf16x8_t qr[NIO][NKS];
-#pragma unroll
-    for (int ks = 0; ks < NKS; ++ks) {
-      float v[8];
-      load8(ks, v);
-      u32x4_t t[NIO];
-      split8<NIO>(v, t);
-#pragma unroll
-      for (int j = 0; j < NIO; ++j) qr[j][ks] = __builtin_bit_cast(bf16x8_t, t[j]);
-    }
-    // T^T[a][row] = sum_e D[a][e] q[row][e]   (a < r; rows a >= r are zero)
-    f32x16_t T = zero16();
-    const int a_row = lane & 31;
-#pragma unroll
-    for (int ks = 0; ks < NKS; ++ks) {
-      u32x4_t dt[NIO];
-      float dv[8];
-      {
-        float a4[4], b4[4];
-        const int64_t drow = ((int64_t)hh * r + min(a_row, r - 1)) * D;  // clamped: no divergent loads
-        io_traits<IO>::load4(Dw, drow + kperm(ks, hf, 0), a4);
-        io_traits<IO>::load4(Dw, drow + kperm(ks, hf, 4), b4);
-#pragma unroll
-        for (int m = 0; m < 4; ++m) {
-          dv[m] = a_row < r ? a4[m] : 0.f;
-          dv[4 + m] = a_row < r ? b4[m] : 0.f;
-        }
-      }
-      split8<NIO>(dv, dt);
-#pragma unroll
-      for (int i = 0; i < NIO; ++i)
-#pragma unroll
-        for (int j = 0; j < NIO; ++j)
-          if (i + j < NIO) T = mfma32(__builtin_bit_cast(bf16x8_t, dt[i]), qr[j][ks], T);
-    }
-    // T as the B operand of U T: accumulator register 8*ks2 + m -> k-step ks2, element m
-    constexpr int NT = NIO == 1 ? 2 : 3;
-    bf16x8_t tb[NT][2];
-#pragma unroll
-    for (int ks2 = 0; ks2 < 2; ++ks2) {
-      float tv[8];
-#pragma unroll
-      for (int m = 0; m < 8; ++m) tv[m] = T[8 * ks2 + m];
-      u32x4_t t[NT];
-      split8<NT>(tv, t);
-#pragma unroll
-      for (int j = 0; j < NT; ++j) tb[j][ks2] = __builtin_bit_cast(bf16x8_t, t[j]);
-    }
-    constexpr int NP = NIO > NT ? NIO : NT;
-#pragma unroll
-    for (int dt2 = 0; dt2 < D / 32; ++dt2) {
-      f32x16_t Q = zero16();
-      const int e = 32 * dt2 + (lane & 31);
-#pragma unroll
-      for (int ks2 = 0; ks2 < 2; ++ks2) {
-        float uv[8];
-        const int64_t urow = ((int64_t)hh * D + e) * r;
-        if ((r & 3) == 0) {  // 4-aligned rows: two vector loads
-          float a4[4], b4[4];
-          io_traits<IO>::load4(Uw, urow + min(kperm(ks2, hf, 0), r - 4), a4);
-          io_traits<IO>::load4(Uw, urow + min(kperm(ks2, hf, 4), r - 4), b4);
-#pragma unroll
-          for (int m = 0; m < 4; ++m) {
-            uv[m] = kperm(ks2, hf, m) < r ? a4[m] : 0.f;
-            uv[4 + m] = kperm(ks2, hf, 4 + m) < r ? b4[m] : 0.f;
-          }
-        } else {
-#pragma unroll
-          for (int m = 0; m < 8; ++m) {
-            const int a = kperm(ks2, hf, m);
-            const float x = io_traits<IO>::load(Uw, urow + min(a, r - 1));
-            uv[m] = a < r ? x : 0.f;
-          }
-        }
-        u32x4_t ut[NIO];
-        split8<NIO>(uv, ut);
-#pragma unroll
-        for (int i = 0; i < NIO; ++i)
-#pragma unroll
-          for (int j = 0; j < NT; ++j)
-            if (i + j < NP) Q = mfma32(__builtin_bit_cast(bf16x8_t, ut[i]), tb[j][ks2], Q);
-      }
-      // register rr of this tile is head dim 32*dt2 + acc_row(rr, hf) = k-step 2*dt2 + rr/8, element rr%8
-#pragma unroll
-      for (int half = 0; half < 2; ++half) {
-        const int ks = 2 * dt2 + half;
-        float v[8];
-        load8(ks, v);  // reload the raw q slice (cheaper than keeping it live)
-#pragma unroll
-        for (int m = 0; m < 8; ++m) v[m] += Q[8 * half + m];
-        sink(ks, v);
-      }
-    }
+    sink(ks, v);
   }
 }
 
 // ------------------------------------------------------------- threshold pass
 // Error allowance of the one-product scores: with u = 2^-8 (bf16 rounding),
 // |bf(x) bf(y) - x y| <= (2u + u^2) |x y|, so over the head dimension the product
-// error is at most (2u + u^2) |tau q^| |k'| (Cauchy-Schwarz); TH_REL exceeds 2u + u^2
+// error is at most (2u + u^2) |tau q| |k~| (Cauchy-Schwarz); TH_REL exceeds 2u + u^2
 // by enough to cover pass 2's own ~2^-16 relative error and fp32 accumulation, and
 // TH_ABS covers the two-term split of b'.
 constexpr float TH_REL = 0.008f;
 constexpr float TH_ABS = 1.0f / 4096.0f;   // bf16 0x3980
 constexpr int TH_EXT = 16;                  // elements of the extension k-step
 
-template <typename IO, int D, bool QCAL>
-__global__ void __launch_bounds__(256, 3) score_threshold(const IO* __restrict__ q, const IO* __restrict__ Dw,
-                                                          const IO* __restrict__ Uw, const uint16_t* __restrict__ t1,
+// Hl: heads of the chunk rows t1 (the landmark heads, or the query heads under Q-Cal).
+template <typename IO, int D>
+__global__ void __launch_bounds__(256, 3) score_threshold(const IO* __restrict__ q, const uint16_t* __restrict__ t1,
                                                           float* __restrict__ theta, const int32_t* __restrict__ pos0,
-                                                          int H, int Hl, int N, int C, int K, int r, int NB, int items,
+                                                          int H, int Hl, int N, int C, int K, int NB, int items,
                                                           int nw) {
   constexpr int NKS = D / 16;
   constexpr int DE = D + TH_EXT;      // bf16 elements of a chunk row
@@ -375,11 +280,11 @@ __global__ void __launch_bounds__(256, 3) score_threshold(const IO* __restrict__
   const float tau = 1.0f / sqrtf((float)D);
   const int64_t qrow = ((int64_t)bh * N + (row_ok ? row : 0)) * D;
 
-  // A operands: bf16(tau q^), then the extension step [1, 1, -1, -e_i] against the
-  // chunk's [b'_hi, b'_lo, TH_ABS, |k'_c| rounded up], e_i = TH_REL |tau q^_i| rounded up
+  // A operands: bf16(tau q), then the extension step [1, 1, -1, -e_i] against the
+  // chunk's [b'_hi, b'_lo, TH_ABS, |k~_c| rounded up], e_i = TH_REL |tau q_i| rounded up
   bf16x8_t qa[NKS + 1];
   float ss = 0.f;
-  qhat_rows<IO, D, QCAL>(q, Dw, Uw, hh, r, qrow, row_ok, lane, [&](int ks, const float(&v)[8]) {
+  q_rows<IO, D>(q, qrow, row_ok, lane, [&](int ks, const float(&v)[8]) {
     float x[8];
 #pragma unroll
     for (int m = 0; m < 8; ++m) {
@@ -496,7 +401,7 @@ __global__ void __launch_bounds__(256, 3) score_threshold(const IO* __restrict__
 
 
 // ------------------------------------------------------------- selection pass
-// S^T = k' q^T on the MFMA: k' rows (chunks) are the A operand, the queries the B
+// S^T = k~ q^T on the MFMA: k~ rows (chunks) are the A operand, the queries the B
 // operand, so accumulator register r of lane l holds the score of chunk
 // acc_row(r, l >> 5) of the 32-chunk tile for query row l & 31.  Each lane therefore
 // owns one row's scores (half of each tile's chunks) and appends its passing candidates
@@ -523,14 +428,14 @@ constexpr int SEL_HALF_SMALL = 16;
 template <int LM, int NQ, int NK>
 constexpr int sel_wgs() { return LM == 2 ? 1 : (LM == 0 && NQ * NK <= 2) ? 3 : 2; }
 
-template <typename IO, int D, int NQ, int NK, bool QCAL, int LM>
-__global__ void __launch_bounds__(256, (sel_wgs<LM, NQ, NK>())) score_topk_kernel(const IO* __restrict__ q, const IO* __restrict__ Dw,
-                                                           const IO* __restrict__ Uw, const uint16_t* __restrict__ p2,
+template <typename IO, int D, int NQ, int NK, int LM>
+__global__ void __launch_bounds__(256, (sel_wgs<LM, NQ, NK>())) score_topk_kernel(const IO* __restrict__ q,
+                                                           const uint16_t* __restrict__ p2,
                                                            const float* __restrict__ theta,
                                                            int32_t* __restrict__ sel_idx,
                                                            float* __restrict__ sel_score,
                                                            const int32_t* __restrict__ pos0, int H, int Hl, int N,
-                                                           int C, int K, int r, int NB, int items, int nw) {
+                                                           int C, int K, int NB, int items, int nw) {
   constexpr int NKS = D / 16;
   constexpr int DE2 = NK * D + P2_EXT;  // elements of a chunk row: plane 0, extension, planes 1..
   constexpr int LDR = DE2 + 8;          // LDS row stride (16-byte pad)
@@ -573,9 +478,9 @@ __global__ void __launch_bounds__(256, (sel_wgs<LM, NQ, NK>())) score_topk_kerne
   const int prow = row_ok ? candidate_chunks(p0 + row, C, nw) : 0;   // candidate chunks of this lane's row
   const int64_t qrow = ((int64_t)bh * N + (row_ok ? row : 0)) * D;
 
-  // ---- the query's B operands: q^ split into NQ bf16 terms, plus the constant extension
+  // ---- the query's B operands: q split into NQ bf16 terms, plus the constant extension
   bf16x8_t qb[NQ][NKS];
-  qhat_rows<IO, D, QCAL>(q, Dw, Uw, hh, r, qrow, row_ok, lane, [&](int ks, const float(&v)[8]) {
+  q_rows<IO, D>(q, qrow, row_ok, lane, [&](int ks, const float(&v)[8]) {
     float x[8];
 #pragma unroll
     for (int m = 0; m < 8; ++m) x[m] = v[m];
@@ -913,28 +818,49 @@ __global__ void __launch_bounds__(256, (sel_wgs<LM, NQ, NK>())) score_topk_kerne
 }
 
 // ---------------------------------------------------------------- k' preparation
-// k' (fp32) -> (a) the selection pass's rows: tau*k' split into NK bf16 term planes with
-// the extension [b'_hi, b'_mid, b'_lo, 0 ...] after plane 0, and (b) the threshold pass's
-// rows: bf16(k') followed by [b'_hi, b'_lo, TH_ABS, |k'_c| rounded up, 0 ...].  Both hold
-// each 16-element k-block in MFMA operand order: position 16 ks + 8 h + m holds element
-// kperm(ks, h, m).  Each (batch, landmark head) gets kp_rows(C) rows, those past C zero.
-template <int D, int NK>
+// k' (fp32) -> chunk rows k~ for both passes: k~ = k' without Q-Cal, one row per
+// (batch, landmark head, chunk); with Q-Cal (r > 0) k~_hc = k'_c + D_h^T (U_h^T k'_c) in
+// fp32, one row per (batch, query head, chunk), so that q^ . k' = q . k~.  Written as
+// (a) the selection pass's rows: tau*k~ split into NK bf16 term planes with the extension
+// [b'_hi, b'_mid, b'_lo, 0 ...] after plane 0, and (b) the threshold pass's rows: bf16(k~)
+// followed by [b'_hi, b'_lo, TH_ABS, |k~_c| rounded up, 0 ...].  Both hold each 16-element
+// k-block in MFMA operand order: position 16 ks + 8 h + m holds element kperm(ks, h, m).
+// Each (batch, row head) gets kp_rows(C) rows, those past C zero.  Hp: heads of the output
+// rows (Hl, or Hq under Q-Cal).
+constexpr int QC_MAXR = 32;   // largest Q-Cal rank
+
+template <typename IO, int D, int NK>
 __global__ void __launch_bounds__(256) prep_kprime(const float* __restrict__ kc, const float* __restrict__ bc,
+                                                   const IO* __restrict__ Dw, const IO* __restrict__ Uw,
                                                    uint16_t* __restrict__ p2, uint16_t* __restrict__ t1,
-                                                   int64_t rows, int C, int Cp) {
+                                                   int64_t rows, int C, int Cp, int Hp, int Hl, int r) {
   constexpr int SPR = D / 8;        // 16-byte segments (threads) per chunk row
-  constexpr int RPB = 256 / SPR;    // chunk rows per workgroup pass
+  constexpr int RPB = 256 / SPR;    // chunk rows per workgroup pass (one row head: RPB divides Cp)
+  constexpr int APT = QC_MAXR / SPR;   // entries of w per thread
   constexpr int DE = D + TH_EXT;
   constexpr int DE2 = NK * D + P2_EXT;
+  // Q-Cal staging: U_h as [e][a] and D_h as [a][e] (fp32, zero past rank r), the pass's
+  // k' rows and their w = U_h^T k'
+  __shared__ __align__(16) float Us[D * QC_MAXR];
+  __shared__ __align__(16) float Ds[QC_MAXR * D];
+  __shared__ __align__(16) float Ks[RPB * (D + 4)];
+  __shared__ __align__(16) float Ws[RPB * QC_MAXR];
   const float tau = 1.0f / sqrtf((float)D);
   const int tid = threadIdx.x;
-  const int sg = tid % SPR, ks = sg >> 1, h = sg & 1;
-  for (int64_t base = (int64_t)blockIdx.x * RPB; base < rows; base += (int64_t)gridDim.x * RPB) {
-    const int64_t rw = base + tid / SPR;   // output row: (b, landmark head) * Cp + chunk
+  const int sg = tid % SPR, ks = sg >> 1, h = sg & 1, lr = tid / SPR;
+  // each workgroup takes a contiguous range of passes, so the row head rarely changes
+  const int64_t npass = (rows + RPB - 1) / RPB;
+  const int64_t ppw = (npass + gridDim.x - 1) / gridDim.x;
+  const int64_t pbeg = (int64_t)blockIdx.x * ppw, pend = min(npass, pbeg + ppw);
+  int staged = -1;
+  for (int64_t pass = pbeg; pass < pend; ++pass) {
+    const int64_t rw = pass * RPB + lr;    // output row: (b, row head) * Cp + chunk
     const bool ok = rw < rows;
     const int c = (int)(rw % Cp);
     const bool real = ok && c < C;         // rows c >= C are zero padding
-    const int64_t sr = rw / Cp * C + c;    // source row of kc / bc
+    const int64_t bhp = rw / Cp;           // (b, row head)
+    const int hp = (int)(bhp % Hp);
+    const int64_t sr = (bhp / Hp * Hl + hp / (Hp / Hl)) * C + c;   // source row of kc / bc
     float x[8];
     if (real) {
       const float4 a = *reinterpret_cast<const float4*>(kc + sr * D + kperm(ks, h, 0));
@@ -943,6 +869,63 @@ __global__ void __launch_bounds__(256) prep_kprime(const float* __restrict__ kc,
     } else {
 #pragma unroll
       for (int m = 0; m < 8; ++m) x[m] = 0.f;
+    }
+    if (r > 0) {
+      // k~ = k' + D_h^T w with w = U_h^T k'.  The pass's rows share one row head (every
+      // thread agrees on hp0, so the branches and barriers are uniform).
+      const int hp0 = (int)((pass * RPB / Cp) % Hp);
+      if (hp0 != staged) {
+        __syncthreads();
+        for (int i = tid; i < D * QC_MAXR; i += 256) {
+          const int e = i / QC_MAXR, a = i % QC_MAXR;   // Us[e][a] = U_h[e][a]
+          Us[i] = a < r ? io_traits<IO>::load(Uw, ((int64_t)hp0 * D + e) * r + a) : 0.f;
+          const int a2 = i / D, e2 = i % D;             // Ds[a][e] = D_h[a][e]
+          Ds[i] = a2 < r ? io_traits<IO>::load(Dw, ((int64_t)hp0 * r + a2) * D + e2) : 0.f;
+        }
+        staged = hp0;
+      }
+      {
+        float* kr = Ks + lr * (D + 4);
+        *reinterpret_cast<float4*>(kr + kperm(ks, h, 0)) = make_float4(x[0], x[1], x[2], x[3]);
+        *reinterpret_cast<float4*>(kr + kperm(ks, h, 4)) = make_float4(x[4], x[5], x[6], x[7]);
+      }
+      __syncthreads();
+      {
+        // w[lr][a] for a = APT sg + j
+        float wv[APT];
+#pragma unroll
+        for (int j = 0; j < APT; ++j) wv[j] = 0.f;
+        const float* kr = Ks + lr * (D + 4);
+        for (int e = 0; e < D; e += 4) {
+          const float4 kv = *reinterpret_cast<const float4*>(kr + e);
+          const float ke[4] = {kv.x, kv.y, kv.z, kv.w};
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int j = 0; j < APT; ++j) wv[j] = fmaf(Us[(e + i) * QC_MAXR + APT * sg + j], ke[i], wv[j]);
+        }
+#pragma unroll
+        for (int j = 0; j < APT; ++j) Ws[lr * QC_MAXR + APT * sg + j] = wv[j];
+      }
+      __syncthreads();
+      float kt[8];
+#pragma unroll
+      for (int m = 0; m < 8; ++m) kt[m] = x[m];
+      for (int a = 0; a < r; ++a) {
+        const float wa = Ws[lr * QC_MAXR + a];
+        const float4 d0 = *reinterpret_cast<const float4*>(Ds + a * D + kperm(ks, h, 0));
+        const float4 d1 = *reinterpret_cast<const float4*>(Ds + a * D + kperm(ks, h, 4));
+        kt[0] = fmaf(d0.x, wa, kt[0]);
+        kt[1] = fmaf(d0.y, wa, kt[1]);
+        kt[2] = fmaf(d0.z, wa, kt[2]);
+        kt[3] = fmaf(d0.w, wa, kt[3]);
+        kt[4] = fmaf(d1.x, wa, kt[4]);
+        kt[5] = fmaf(d1.y, wa, kt[5]);
+        kt[6] = fmaf(d1.z, wa, kt[6]);
+        kt[7] = fmaf(d1.w, wa, kt[7]);
+      }
+#pragma unroll
+      for (int m = 0; m < 8; ++m) x[m] = real ? kt[m] : 0.f;
     }
     float s2 = 0.f;
 #pragma unroll
@@ -988,12 +971,14 @@ __global__ void __launch_bounds__(256) prep_kprime(const float* __restrict__ kc,
 
 static size_t al3(size_t x) { return (x + 255) / 256 * 256; }
 static int nk_of(const Geom& g) { return g.io == 0 ? 3 : 2; }
+// heads of the chunk rows: the landmark heads, or the query heads when Q-Cal folds into them
+static int row_heads(const Geom& g) { return g.r > 0 ? g.Hq : g.Hl; }
 
 struct ScoreWs {
   size_t planes, t1, theta, total;
 };
 static ScoreWs score_ws(const Geom& g) {
-  const size_t rows = (size_t)g.B * g.Hl * kp_rows(g.C());   // k' rows per (b, landmark head): padded
+  const size_t rows = (size_t)g.B * row_heads(g) * kp_rows(g.C());   // chunk rows per (b, row head): padded
   ScoreWs w;
   size_t off = 0;
   w.planes = off;
@@ -1008,56 +993,53 @@ static ScoreWs score_ws(const Geom& g) {
 
 size_t score_workspace_bytes(const Geom& g) { return score_ws(g).total; }
 
-template <typename IO, int D, int NQ, int NK, bool QCAL>
-static void launch_st(const Geom& g, int Nq, const int32_t* pos0, const void* q, const void* Dw, const void* Uw,
-                      const uint16_t* planes, const uint16_t* t1, float* theta, int32_t* si, float* ss, hipStream_t st,
-                      hipEvent_t* ev) {
+template <typename IO, int D, int NQ, int NK>
+static void launch_st(const Geom& g, int Nq, const int32_t* pos0, const void* q, const uint16_t* planes,
+                      const uint16_t* t1, float* theta, int32_t* si, float* ss, hipStream_t st, hipEvent_t* ev) {
   const int NB = (Nq + ST_ROWS - 1) / ST_ROWS;
   const int items = g.B * g.Hq * NB;
   const int grid = ((items + 7) / 8) * 8;
+  const int Hp = row_heads(g);
   if (items > 0) {
-    hipLaunchKernelGGL((score_threshold<IO, D, QCAL>), dim3(grid), dim3(256), 0, st, (const IO*)q, (const IO*)Dw,
-                       (const IO*)Uw, t1, theta, pos0, g.Hq, g.Hl, Nq, g.C(), g.K, g.r, NB, items, g.nw);
+    hipLaunchKernelGGL((score_threshold<IO, D>), dim3(grid), dim3(256), 0, st, (const IO*)q, t1, theta, pos0, g.Hq,
+                       Hp, Nq, g.C(), g.K, NB, items, g.nw);
   }
   if (ev) hipEventRecord(ev[0], st);
   if (items > 0) {
     if (g.K > 32)
-      hipLaunchKernelGGL((score_topk_kernel<IO, D, NQ, NK, QCAL, 2>), dim3(grid), dim3(256), 0, st, (const IO*)q,
-                         (const IO*)Dw, (const IO*)Uw, planes, (const float*)theta, si, ss, pos0, g.Hq, g.Hl, Nq,
-                         g.C(), g.K, g.r, NB, items, g.nw);
+      hipLaunchKernelGGL((score_topk_kernel<IO, D, NQ, NK, 2>), dim3(grid), dim3(256), 0, st, (const IO*)q, planes,
+                         (const float*)theta, si, ss, pos0, g.Hq, Hp, Nq, g.C(), g.K, NB, items, g.nw);
     else if (g.K > 16)
-      hipLaunchKernelGGL((score_topk_kernel<IO, D, NQ, NK, QCAL, 1>), dim3(grid), dim3(256), 0, st, (const IO*)q,
-                         (const IO*)Dw, (const IO*)Uw, planes, (const float*)theta, si, ss, pos0, g.Hq, g.Hl, Nq,
-                         g.C(), g.K, g.r, NB, items, g.nw);
+      hipLaunchKernelGGL((score_topk_kernel<IO, D, NQ, NK, 1>), dim3(grid), dim3(256), 0, st, (const IO*)q, planes,
+                         (const float*)theta, si, ss, pos0, g.Hq, Hp, Nq, g.C(), g.K, NB, items, g.nw);
     else
-      hipLaunchKernelGGL((score_topk_kernel<IO, D, NQ, NK, QCAL, 0>), dim3(grid), dim3(256), 0, st, (const IO*)q,
-                         (const IO*)Dw, (const IO*)Uw, planes, (const float*)theta, si, ss, pos0, g.Hq, g.Hl, Nq,
-                         g.C(), g.K, g.r, NB, items, g.nw);
+      hipLaunchKernelGGL((score_topk_kernel<IO, D, NQ, NK, 0>), dim3(grid), dim3(256), 0, st, (const IO*)q, planes,
+                         (const float*)theta, si, ss, pos0, g.Hq, Hp, Nq, g.C(), g.K, NB, items, g.nw);
   }
 }
 
 template <typename IO, int D>
-static void launch_st_d(const Geom& g, int Nq, const int32_t* pos0, const void* q, const void* Dw, const void* Uw,
-                        const uint16_t* planes, const uint16_t* t1, float* theta, int32_t* si, float* ss,
-                        hipStream_t st, hipEvent_t* ev) {
-  constexpr bool F32 = io_traits<IO>::terms == 3;
-  if (g.r > 0)
-    launch_st<IO, D, F32 ? 3 : 2, F32 ? 3 : 2, true>(g, Nq, pos0, q, Dw, Uw, planes, t1, theta, si, ss, st, ev);
-  else
-    launch_st<IO, D, F32 ? 3 : 1, F32 ? 3 : 2, false>(g, Nq, pos0, q, Dw, Uw, planes, t1, theta, si, ss, st, ev);
+static void launch_prep(const Geom& g, const float* kc, const float* bc, const void* Dw, const void* Uw,
+                        uint16_t* planes, uint16_t* t1, hipStream_t st) {
+  const int Cp = kp_rows(g.C());
+  const int Hp = row_heads(g);
+  const int64_t rows = (int64_t)g.B * Hp * Cp;
+  const int64_t rpb = 256 / (D / 8);
+  const unsigned gs = (unsigned)std::min<int64_t>((rows + rpb - 1) / rpb, 2048);
+  constexpr int NK = io_traits<IO>::terms == 3 ? 3 : 2;   // nk_of(g)
+  hipLaunchKernelGGL((prep_kprime<IO, D, NK>), dim3(gs), dim3(256), 0, st, kc, bc, (const IO*)Dw, (const IO*)Uw,
+                     planes, t1, rows, g.C(), Cp, Hp, g.Hl, g.r);
 }
 
-template <int D>
-static void launch_prep(const Geom& g, const float* kc, const float* bc, uint16_t* planes, uint16_t* t1,
-                        hipStream_t st) {
-  const int Cp = kp_rows(g.C());
-  const int64_t rows = (int64_t)g.B * g.Hl * Cp;
-  const int64_t rpb = 256 / (D / 8);
-  const unsigned gs = (unsigned)std::min<int64_t>((rows + rpb - 1) / rpb, 16384);
-  if (nk_of(g) == 3)
-    hipLaunchKernelGGL((prep_kprime<D, 3>), dim3(gs), dim3(256), 0, st, kc, bc, planes, t1, rows, g.C(), Cp);
-  else
-    hipLaunchKernelGGL((prep_kprime<D, 2>), dim3(gs), dim3(256), 0, st, kc, bc, planes, t1, rows, g.C(), Cp);
+// q enters the products as NQ exact bf16 terms (one for bf16, three for fp32); the chunk
+// rows as NK terms (hi + lo for bf16 I/O, three for fp32)
+template <typename IO, int D>
+static void launch_all(const Geom& g, int Nq, const int32_t* pos0, const void* q, const void* Dw, const void* Uw,
+                       const float* kc, const float* bc, uint16_t* planes, uint16_t* t1, float* theta, int32_t* si,
+                       float* ss, hipStream_t st, hipEvent_t* ev) {
+  constexpr bool F32 = io_traits<IO>::terms == 3;
+  if (g.C() > 0) launch_prep<IO, D>(g, kc, bc, Dw, Uw, planes, t1, st);
+  launch_st<IO, D, F32 ? 3 : 1, F32 ? 3 : 2>(g, Nq, pos0, q, planes, t1, theta, si, ss, st, ev);
 }
 
 hipError_t launch_score_topk(const Geom& g, int Nq, const int32_t* pos0, const void* q, const void* Dw, const void* Uw,
@@ -1068,22 +1050,16 @@ hipError_t launch_score_topk(const Geom& g, int Nq, const int32_t* pos0, const v
   uint16_t* planes = (uint16_t*)((char*)ws + w.planes);
   uint16_t* t1 = (uint16_t*)((char*)ws + w.t1);
   float* theta = (float*)((char*)ws + w.theta);
-  if (g.C() > 0) {
-    if (g.d == 64)
-      launch_prep<64>(g, kc, bc, planes, t1, st);
-    else
-      launch_prep<128>(g, kc, bc, planes, t1, st);
-  }
   if (g.io == 0) {
     if (g.d == 64)
-      launch_st_d<float, 64>(g, Nq, pos0, q, Dw, Uw, planes, t1, theta, sel_idx, sel_score, st, ev);
+      launch_all<float, 64>(g, Nq, pos0, q, Dw, Uw, kc, bc, planes, t1, theta, sel_idx, sel_score, st, ev);
     else
-      launch_st_d<float, 128>(g, Nq, pos0, q, Dw, Uw, planes, t1, theta, sel_idx, sel_score, st, ev);
+      launch_all<float, 128>(g, Nq, pos0, q, Dw, Uw, kc, bc, planes, t1, theta, sel_idx, sel_score, st, ev);
   } else {
     if (g.d == 64)
-      launch_st_d<bf16_t, 64>(g, Nq, pos0, q, Dw, Uw, planes, t1, theta, sel_idx, sel_score, st, ev);
+      launch_all<bf16_t, 64>(g, Nq, pos0, q, Dw, Uw, kc, bc, planes, t1, theta, sel_idx, sel_score, st, ev);
     else
-      launch_st_d<bf16_t, 128>(g, Nq, pos0, q, Dw, Uw, planes, t1, theta, sel_idx, sel_score, st, ev);
+      launch_all<bf16_t, 128>(g, Nq, pos0, q, Dw, Uw, kc, bc, planes, t1, theta, sel_idx, sel_score, st, ev);
   }
   if (ev) hipEventRecord(ev[1], st);
   return hipGetLastError();
