@@ -21,7 +21,7 @@
 //
 //   1. score_threshold (queries = M, chunks = N: accumulator register r of a lane holds
 //      one chunk's score for one row; the 32 lanes of a half-wave cover 32 chunks of
-//      that row): one bf16 product per score, bf16(q/sqrt(d)) . bf16(k~_c), with b'_c
+//      that row): one bf16 product per score, bf16(q) . bf16(k~_c/sqrt(d)), with b'_c
 //      and an error allowance e_i |k'_c| folded into one extra MFMA k-step, so every
 //      value is at most the fp32-accurate score of pass 2.  Each lane keeps the two
 //      largest values of its column of chunks; the K-th largest of these 64 values of
@@ -238,12 +238,14 @@ HILS_DEV void q_rows(const IO* __restrict__ q, int64_t qrow, bool row_ok, int la
 }
 
 // ------------------------------------------------------------- threshold pass
-// Error allowance of the one-product scores: with u = 2^-8 (bf16 rounding),
-// |bf(x) bf(y) - x y| <= (2u + u^2) |x y|, so over the head dimension the product
-// error is at most (2u + u^2) |tau q| |k~| (Cauchy-Schwarz); TH_REL exceeds 2u + u^2
-// by enough to cover pass 2's own ~2^-16 relative error and fp32 accumulation, and
-// TH_ABS covers the two-term split of b'.
-constexpr float TH_REL = 0.008f;
+// Error allowance of the one-product scores bf(q) . bf(tau k~): with u = 2^-8 (bf16
+// rounding), |bf(x) bf(y) - x y| <= (2u + u^2) |x y|, and <= u |x y| when x is exactly a
+// bf16 value (a bf16 query), so over the head dimension the product error is at most
+// (2u + u^2) |q| |tau k~|, or u |q| |tau k~| (Cauchy-Schwarz).  TH_REL exceeds these by
+// enough to cover pass 2's own ~2^-16 relative error and fp32 accumulation, and TH_ABS
+// covers the two-term split of b'.
+template <typename IO>
+constexpr float th_rel() { return io_traits<IO>::terms == 1 ? 0.0042f : 0.008f; }
 constexpr float TH_ABS = 1.0f / 4096.0f;   // bf16 0x3980
 constexpr int TH_EXT = 16;                  // elements of the extension k-step
 
@@ -277,18 +279,17 @@ __global__ void __launch_bounds__(256, 3) score_threshold(const IO* __restrict__
   const int last = min(r0 + ST_ROWS, N) - 1;
   const int Pmax = candidate_chunks(p0 + last, C, nw);
   const int Pmin = candidate_chunks(p0 + r0, C, nw);
-  const float tau = 1.0f / sqrtf((float)D);
   const int64_t qrow = ((int64_t)bh * N + (row_ok ? row : 0)) * D;
 
-  // A operands: bf16(tau q), then the extension step [1, 1, -1, -e_i] against the
-  // chunk's [b'_hi, b'_lo, TH_ABS, |k~_c| rounded up], e_i = TH_REL |tau q_i| rounded up
+  // A operands: bf16(q), then the extension step [1, 1, -1, -e_i] against the
+  // chunk's [b'_hi, b'_lo, TH_ABS, |tau k~_c| rounded up], e_i = TH_REL |q_i| rounded up
   bf16x8_t qa[NKS + 1];
   float ss = 0.f;
   q_rows<IO, D>(q, qrow, row_ok, lane, [&](int ks, const float(&v)[8]) {
     float x[8];
 #pragma unroll
     for (int m = 0; m < 8; ++m) {
-      x[m] = v[m] * tau;
+      x[m] = v[m];
       ss = fmaf(x[m], x[m], ss);
     }
     u32x4_t t[1];
@@ -301,7 +302,7 @@ __global__ void __launch_bounds__(256, 3) score_threshold(const IO* __restrict__
     if (hf == 0) {
       t[0] = t[1] = 0x3f80;
       t[2] = 0xbf80;
-      t[3] = (uint16_t)(bf16_up(TH_REL * sqrtf(ss)) | 0x8000u);
+      t[3] = (uint16_t)(bf16_up(th_rel<IO>() * sqrtf(ss)) | 0x8000u);
     }
     qa[NKS] = pack8(t);
   }
@@ -822,8 +823,8 @@ __global__ void __launch_bounds__(256, (sel_wgs<LM, NQ, NK>())) score_topk_kerne
 // (batch, landmark head, chunk); with Q-Cal (r > 0) k~_hc = k'_c + D_h^T (U_h^T k'_c) in
 // fp32, one row per (batch, query head, chunk), so that q^ . k' = q . k~.  Written as
 // (a) the selection pass's rows: tau*k~ split into NK bf16 term planes with the extension
-// [b'_hi, b'_mid, b'_lo, 0 ...] after plane 0, and (b) the threshold pass's rows: bf16(k~)
-// followed by [b'_hi, b'_lo, TH_ABS, |k~_c| rounded up, 0 ...].  Both hold each 16-element
+// [b'_hi, b'_mid, b'_lo, 0 ...] after plane 0, and (b) the threshold pass's rows:
+// bf16(tau*k~) followed by [b'_hi, b'_lo, TH_ABS, |tau*k~_c| rounded up, 0 ...].  Both hold each 16-element
 // k-block in MFMA operand order: position 16 ks + 8 h + m holds element kperm(ks, h, m).
 // Each (batch, row head) gets kp_rows(C) rows, those past C zero.  Hp: heads of the output
 // rows (Hl, or Hq under Q-Cal).
@@ -936,7 +937,7 @@ __global__ void __launch_bounds__(256) prep_kprime(const float* __restrict__ kc,
 #pragma unroll
     for (int m = 0; m < 8; ++m) {
       xs[m] = tau * x[m];
-      xh[m] = x[m];
+      xh[m] = tau * x[m];
     }
     u32x4_t tm[NK], hi[1];
     split8<NK>(xs, tm);
@@ -957,7 +958,7 @@ __global__ void __launch_bounds__(256) prep_kprime(const float* __restrict__ kc,
           e[0] = sp2[0];
           e[1] = sp2[1];
           e[2] = f32_to_bf16(TH_ABS);  // 2^-12, exact in bf16 (0x3980)
-          e[3] = bf16_up(sqrtf(s2));
+          e[3] = bf16_up(tau * sqrtf(s2));
           f[0] = sp3[0];
           f[1] = sp3[1];
           f[2] = sp3[2];
