@@ -386,6 +386,36 @@ def test_chunk_size_one_is_dense():
     np.testing.assert_allclose(r["o"], ref, rtol=0, atol=1e-12)
 
 
+def test_qcal_on_the_key_side():
+    """Q-Cal as a transform of the chunk rows: q^ . k' = q . (k' + D_h^T (U_h^T k')), so
+    the score the oracle computes from the calibrated query (aitrends.kr article,
+    "Methodology", Q-Cal module: q^ = q + U_h (D_h q)) equals tau q . k~_hc + b'_c with
+    k~_hc = k'_c + D_h^T (U_h^T k'_c), one row per query head even where query heads share
+    a landmark head.  This is the reading the GPU scoring passes compute."""
+    rng = _rng(29)
+    d, S, C, r_ = 32, 16, 10, 8
+    N = (C + 1) * S
+    s = oracle.shape(1, 4, 2, d, N=N, S=S, K=4, Hl=2, r=r_)
+    k = rng.standard_normal((1, 2, N, d))
+    lmk = rng.standard_normal((1, 2, C + 1, d))
+    q = rng.standard_normal((1, 4, N, d))
+    D = rng.standard_normal((4, r_, d)) * 0.3
+    U = rng.standard_normal((4, d, r_)) * 0.3
+    kc, bc = oracle.compress(s, k, lmk)
+    tau = 1 / math.sqrt(d)
+    for h in range(4):
+        lh = h // 2
+        kt = kc[0, lh] + (kc[0, lh] @ U[h]) @ D[h]      # [C + 1, d]: k~ of query head h
+        for i in (S, 3 * S + 5, N - 1):
+            got = oracle.row_scores(s, 0, h, i, q[0, h, i], kc=kc, bc=bc, D=D, U=U)
+            want = tau * (kt[:len(got)] @ q[0, h, i]) + bc[0, lh, :len(got)]
+            np.testing.assert_allclose(got, want, rtol=0, atol=1e-11)
+            # and the query-side form, for contrast: one calibrated query against k'
+            qh = q[0, h, i] + U[h] @ (D[h] @ q[0, h, i])
+            np.testing.assert_allclose(got, tau * (kc[0, lh, :len(got)] @ qh) + bc[0, lh, :len(got)], rtol=0,
+                                       atol=1e-11)
+
+
 def test_qcal_special_cases():
     rng = _rng(13)
     d, S, C, r_ = 32, 16, 12, 32
