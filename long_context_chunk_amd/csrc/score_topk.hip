@@ -824,10 +824,10 @@ __global__ void __launch_bounds__(256, (sel_wgs<LM, NQ, NK>())) score_topk_kerne
 // fp32, one row per (batch, query head, chunk), so that q^ . k' = q . k~.  Written as
 // (a) the selection pass's rows: tau*k~ split into NK bf16 term planes with the extension
 // [b'_hi, b'_mid, b'_lo, 0 ...] after plane 0, and (b) the threshold pass's rows:
-// bf16(tau*k~) followed by [b'_hi, b'_lo, TH_ABS, |tau*k~_c| rounded up, 0 ...].  Both hold each 16-element
-// k-block in MFMA operand order: position 16 ks + 8 h + m holds element kperm(ks, h, m).
-// Each (batch, row head) gets kp_rows(C) rows, those past C zero.  Hp: heads of the output
-// rows (Hl, or Hq under Q-Cal).
+// bf16(tau*k~) followed by [b'_hi, b'_lo, TH_ABS, |tau*k~_c| rounded up, 0 ...].  Both
+// hold each 16-element k-block in MFMA operand order: position 16 ks + 8 h + m holds
+// element kperm(ks, h, m).  Each (batch, row head) gets kp_rows(C) rows, those past C
+// zero.  Hp: heads of the output rows (Hl, or Hq under Q-Cal).
 constexpr int QC_MAXR = 32;   // largest Q-Cal rank
 
 template <typename IO, int D, int NK>
