@@ -52,6 +52,10 @@
  *     them and pad with id -1 and score -inf after them.
  *   - q, k, v, o, lmk_q, qcal_D, qcal_U all have the element type `io`;
  *     kc, bc and sel_score are always fp32.
+ *   - The tensor arguments (q, k, v, o, the caches, lmk_q, kc, qcal_D, qcal_U and the
+ *     gradients) must be 16-byte aligned, as hipMalloc and torch allocations are: the
+ *     kernels move their rows with 16-byte accesses.  A misaligned one returns
+ *     HILS_E_INVAL.
  */
 #ifndef HILS_H
 #define HILS_H

@@ -3,6 +3,7 @@
 // is valid.
 #include <stdarg.h>
 #include <algorithm>
+#include <initializer_list>
 #include <mutex>
 #include <stdio.h>
 #include <string.h>
@@ -28,6 +29,15 @@ int hip_fail(hipError_t e, const char* where) {
 
 constexpr size_t kAlign = 256;
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+// The kernels move rows of the tensor arguments with 16-byte vector accesses.  NULL (an
+// optional argument left out) passes.
+bool aligned16(std::initializer_list<const void*> ps) {
+  for (const void* p : ps)
+    if (reinterpret_cast<uintptr_t>(p) & 15u) return false;
+  return true;
+}
+int misaligned() { return fail(HILS_E_INVAL, "tensor arguments must be 16-byte aligned device pointers"); }
 
 // Validates dims; on success fills g.  Returns HILS_OK or an error code.
 int check_dims(const hils_dims_t* dims, hils::Geom& g) {
@@ -155,6 +165,7 @@ int hils_landmark_compress(const hils_dims_t* dims, const void* k, const void* l
     return HILS_OK;
   }
   if (!k || !lmk_q || !kc || !bc) return fail(HILS_E_INVAL, "k, lmk_q, kc and bc must be non-NULL");
+  if (!aligned16({k, lmk_q, kc})) return misaligned();
   hipError_t e = hils::launch_compress(g.io, k, lmk_q, kc, bc, g.B, g.Hkv, g.Hl, g.N, g.d, c_begin, c_end,
                                        (hipStream_t)stream);
   if (e != hipSuccess) return hip_fail(e, "hils_landmark_compress");
@@ -176,6 +187,7 @@ int hils_chunk_score_topk(const hils_dims_t* dims, int32_t Nq, const void* q, co
   }
   if (!q || !sel_idx || !sel_score) return fail(HILS_E_INVAL, "q, sel_idx and sel_score must be non-NULL");
   if (g.C() > 0 && (!kc || !bc)) return fail(HILS_E_INVAL, "kc and bc must be non-NULL");
+  if (!aligned16({q, kc, qcal_D, qcal_U})) return misaligned();
   if (g.r > 0 && (!qcal_D || !qcal_U)) return fail(HILS_E_INVAL, "qcal_rank > 0 needs qcal_D and qcal_U");
   const size_t need = hils::score_workspace_bytes(g);
   if (!ws && need > 0) return fail(HILS_E_WORKSPACE, "workspace is NULL (%zu bytes needed)", need);
@@ -201,6 +213,7 @@ int run_prefill(const hils_dims_t* dims, const void* q, const void* k, const voi
   if ((rc = check_prefill(g))) return rc;
   if (!q || !k || !v || !o) return fail(HILS_E_INVAL, "q, k, v and o must be non-NULL");
   if (g.C() > 0 && !lmk_q && (!kc || !bc)) return fail(HILS_E_INVAL, "without lmk_q, kc and bc are required inputs");
+  if (!aligned16({q, k, v, o, lmk_q, kc, qcal_D, qcal_U})) return misaligned();
   if (g.r > 0 && (!qcal_D || !qcal_U)) return fail(HILS_E_INVAL, "qcal_rank > 0 needs qcal_D and qcal_U");
   const PrefillWs w = prefill_ws(g);
   if (!ws && w.total > 0) return fail(HILS_E_WORKSPACE, "workspace is NULL (%zu bytes needed)", w.total);
@@ -250,6 +263,7 @@ int run_decode(const hils_dims_t* dims, const void* q, const void* k_cache, cons
   if (!q || !k_cache || !v_cache || !seq_lens || !o)
     return fail(HILS_E_INVAL, "q, k_cache, v_cache, seq_lens and o must be non-NULL");
   if (g.C() > 0 && (!kc || !bc)) return fail(HILS_E_INVAL, "kc and bc must be non-NULL");
+  if (!aligned16({q, k_cache, v_cache, o, kc, qcal_D, qcal_U, kcm})) return misaligned();
   if (g.C() > 65536) return fail(HILS_E_UNSUPPORTED, "decode needs N/S <= 65536 (N=%d)", g.N);
   if (g.r > 0 && (!qcal_D || !qcal_U)) return fail(HILS_E_INVAL, "qcal_rank > 0 needs qcal_D and qcal_U");
   const size_t need = hils::decode_workspace_bytes(g, kcm != nullptr);
@@ -463,6 +477,7 @@ int hils_dense_decode(const hils_dims_t* dims, const void* q, const void* k_cach
   if (rc) return rc;
   if (!q || !k_cache || !v_cache || !seq_lens || !o)
     return fail(HILS_E_INVAL, "q, k_cache, v_cache, seq_lens and o must be non-NULL");
+  if (!aligned16({q, k_cache, v_cache, o})) return misaligned();
   if (g.io != HILS_BF16) return fail(HILS_E_UNSUPPORTED, "the dense decode baseline needs bf16 I/O");
   const int G = g.Hq / g.Hkv;
   if (G != 1 && G != 2 && G != 4 && G != 8)
@@ -483,6 +498,7 @@ int hils_dense_attention(const hils_dims_t* dims, const void* q, const void* k, 
   int rc = check_dims(dims, g);
   if (rc) return rc;
   if (!q || !k || !v || !o) return fail(HILS_E_INVAL, "q, k, v and o must be non-NULL");
+  if (!aligned16({q, k, v, o})) return misaligned();
   if ((int64_t)g.B * g.Hq * ((g.N + 127) / 128) > 0x7fffffff)
     return fail(HILS_E_UNSUPPORTED, "B*Hq*ceil(N/128) must fit a 31-bit grid");
   const hipError_t e = hils::launch_dense(g, q, k, v, o, (hipStream_t)stream);
@@ -506,6 +522,7 @@ int hils_attn_prefill_backward(const hils_dims_t* dims, const void* q, const voi
     return fail(HILS_E_INVAL, "lmk_q, kc and dlmk must be non-NULL when N >= S");
   if (g.r > 0 && (!qcal_D || !qcal_U || !dD || !dU))
     return fail(HILS_E_INVAL, "qcal_D, qcal_U, dD and dU must be non-NULL when qcal_rank > 0");
+  if (!aligned16({q, k, v, o, dO, dq, dk, dv, lmk_q, kc, dlmk, qcal_D, qcal_U, dD, dU})) return misaligned();
   const size_t need = hils::backward_workspace_bytes(g);
   if (ws_bytes < need || (need > 0 && !ws))
     return fail(HILS_E_WORKSPACE, "workspace of %zu bytes needed, %zu given", need, ws_bytes);

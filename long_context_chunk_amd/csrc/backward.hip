@@ -674,38 +674,60 @@ __global__ void __launch_bounds__(BP_THREADS) bwd_pairs(const bf16_t* __restrict
 }
 
 // ------------------------------------------------------------------ bwd_dq_sum
-// Per row (one wave, lanes over the dims): the output dq (bf16) = the window's dq (fp32) +
-// the selected chunks' dq partials (bf16; each already holds the pair's score term
-// tau dsigma (I + D^T U^T) k'_c).  The row's number of selections comes from one ballot.
-// This is the last step of dq, so the sum is rounded straight into the output.
+// Per row (one wave): the output dq (bf16) = the window's dq (fp32) + the selected chunks'
+// dq partials (bf16; each already holds the pair's score term tau dsigma (I + D^T U^T)
+// k'_c).  The row's number of selections comes from one ballot.  A slot row is read by
+// D/8 lanes with 16-byte loads, 64/(D/8) slots per wave-wide load, every load of the row
+// at once; the lanes' sums over their slots are then added across the slot groups.  This
+// is the last step of dq, so the sum is rounded straight into the output.
 template <int D, int KMAX>
 __global__ void __launch_bounds__(256) bwd_dq_sum(const int32_t* __restrict__ sel, const uint16_t* __restrict__ dqp,
                                                   const float* __restrict__ dq, bf16_t* __restrict__ out, int K,
                                                   int64_t rows) {
-  constexpr int EPL = D / 64;
+  constexpr int LPS = D / 8;                        // lanes per slot row (8 dims each)
+  constexpr int SPL = 64 / LPS;                     // slot rows per wave-wide load
+  constexpr int NSEG = (KMAX + SPL - 1) / SPL;      // loads per lane
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int sl = lane / LPS, dp = (lane % LPS) * 8;
   for (int64_t row = (int64_t)blockIdx.x * 4 + w; row < rows; row += (int64_t)gridDim.x * 4) {
-    const int32_t sl = lane < K ? sel[row * K + lane] : -1;
-    const int n = __popcll(__ballot(sl >= 0));  // valid selections come first
-    const uint16_t* pr = dqp + row * K * D + lane * EPL;
-    // every slot's load at once (slots past n read slot 0, in bounds, and are dropped)
-    uint32_t pv[KMAX];
+    const int32_t sv = lane < K ? sel[row * K + lane] : -1;
+    const int n = __popcll(__ballot(sv >= 0));  // valid selections come first
+    const uint16_t* pr = dqp + row * K * D + dp;
+    // slots t = SPL g + sl; those past n read slot 0 (in bounds) and are dropped
+    u32x4_t pv[NSEG];
 #pragma unroll
-    for (int x = 0; x < KMAX; ++x) {
-      const int xs = x < n ? x : 0;
-      pv[x] = EPL == 2 ? *reinterpret_cast<const uint32_t*>(pr + (int64_t)xs * D) : pr[(int64_t)xs * D];
+    for (int g = 0; g < NSEG; ++g) {
+      const int t = SPL * g + sl;
+      pv[g] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(pr + (int64_t)(t < n ? t : 0) * D));
     }
-    float acc[EPL];
+    float acc[8];
 #pragma unroll
-    for (int u = 0; u < EPL; ++u) acc[u] = 0.f;
+    for (int m = 0; m < 8; ++m) acc[m] = 0.f;
 #pragma unroll
-    for (int x = 0; x < KMAX; ++x) {
-      const bool live = x < n;
-      acc[0] += live ? __uint_as_float(pv[x] << 16) : 0.f;
-      if constexpr (EPL == 2) acc[1] += live ? __uint_as_float(pv[x] & 0xffff0000u) : 0.f;
+    for (int g = 0; g < NSEG; ++g) {
+      if (SPL * g + sl < n) {
+        const uint32_t wd[4] = {pv[g].x, pv[g].y, pv[g].z, pv[g].w};
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+          acc[2 * m] += __uint_as_float(wd[m] << 16);
+          acc[2 * m + 1] += __uint_as_float(wd[m] & 0xffff0000u);
+        }
+      }
     }
 #pragma unroll
-    for (int u = 0; u < EPL; ++u) out[row * D + lane * EPL + u].bits = f32_to_bf16(dq[row * D + lane * EPL + u] + acc[u]);
+    for (int o = LPS; o < 64; o <<= 1)
+#pragma unroll
+      for (int m = 0; m < 8; ++m) acc[m] += __shfl_xor(acc[m], o);
+    if (lane < LPS) {
+      const float4 d0 = *reinterpret_cast<const float4*>(dq + row * D + dp);
+      const float4 d1 = *reinterpret_cast<const float4*>(dq + row * D + dp + 4);
+      u32x4_t pk;
+      pk.x = pack_bf16x2(d0.x + acc[0], d0.y + acc[1]);
+      pk.y = pack_bf16x2(d0.z + acc[2], d0.w + acc[3]);
+      pk.z = pack_bf16x2(d1.x + acc[4], d1.y + acc[5]);
+      pk.w = pack_bf16x2(d1.z + acc[6], d1.w + acc[7]);
+      *reinterpret_cast<u32x4_t*>(out + row * D + dp) = pk;
+    }
   }
 }
 

@@ -190,6 +190,25 @@ def test_backward_validation_and_workspace():
     assert b"bf16" in lib.hils_last_error()
 
 
+def test_misaligned_tensor_pointers_rejected():
+    """Tensor arguments must be 16-byte aligned (the kernels move rows with 16-byte
+    accesses); a misaligned one is rejected on the host, before any HIP call."""
+    lib = hils.load()
+    fake = ctypes.c_void_p(0x1000)     # never dereferenced: validation fails first
+    odd = ctypes.c_void_p(0x1008)      # 8-byte aligned only
+    d = hils.dims(1, 8, 2, 64, 1024, 8)
+    rc = lib.hils_attn_prefill(ctypes.byref(d), odd, fake, fake, fake, fake, fake, None, None, fake, fake, fake,
+                               fake, ctypes.c_size_t(1 << 40), None)
+    assert rc == hils.E_INVAL, (rc, lib.hils_last_error())
+    assert b"16-byte aligned" in lib.hils_last_error()
+    rc = lib.hils_dense_attention(ctypes.byref(d), fake, fake, fake, odd, None)
+    assert rc == hils.E_INVAL and b"16-byte aligned" in lib.hils_last_error()
+    dd = hils.dims(2, 8, 2, 64, 4096, 8)
+    rc = lib.hils_attn_decode(ctypes.byref(dd), fake, odd, fake, fake, fake, fake, None, None, None, fake, fake,
+                              ctypes.c_size_t(1 << 40), None)
+    assert rc == hils.E_INVAL and b"16-byte aligned" in lib.hils_last_error()
+
+
 def test_decode_noalloc_rejects_dims_beyond_its_scratch():
     """hils_attn_decode_noalloc checks its fixed scratch size on the host, before any HIP call."""
     lib = hils.load()
